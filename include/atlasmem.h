@@ -1,0 +1,204 @@
+/*
+ * atlasmem -- the neural-memory test-time update and retrieval (Titans / ATLAS)
+ * on one MI355X (gfx950), behind a plain C ABI.
+ *
+ * What is computed (per memory m = (b, h), all memories independent):
+ *
+ *   memory     M_W(x) = W x                      (LINEAR, W: d_value x d_in)
+ *              M_W(x) = W2 silu(W1 x)            (MLP2_SILU, W1: d_hidden x d_in,
+ *                                                 W2: d_value x d_hidden)
+ *   loss       l(W; x, v) = ||M_W(x) - v||^2      -- "Titans: Learning to Memorize at
+ *              Test Time" (titans-pytorch-mlx README), Core Equations, Eq. 12
+ *   momentum   S_t = eta_t S_{t-1} - theta_t G_t  -- same page, Eq. 14
+ *   forgetting W_t = (1 - alpha_t) W_{t-1} + S_t  -- same page, Eq. 13; titans-torch
+ *              0.1.2 (PyPI), API Reference, inner-loop update rule
+ *   chunks     the sequence is cut into chunks of `chunk` tokens; every gradient of a
+ *              chunk is taken at the chunk-start weights and every query of the chunk
+ *              is answered with them, y_t = M_{W_start}(phi(q_t)) ("ATLAS: Learning to
+ *              Optimally Memorize the Context at Test Time | Summary", section 3.3;
+ *              titans-pytorch-mlx README, MAC Eq. 21)
+ *   Omega      G_t = sum_{i=t-c+1..t} gamma_i grad l(W_start; phi(k_i), v_i) for a
+ *              window c > 1 (gamma_i per token; the window crosses chunk boundaries and
+ *              is clipped only at the start of the sequence); G_t = grad l(...; k_t, v_t)
+ *              for c = 1 (ATLAS summary, section 3.2; Atlas-Torch README, Atlas
+ *              Extensions table, Omega Rule)
+ *   features   phi(x) = [1, x_i, x_i x_j / 2 (i <= j)] in combinations_with_replacement
+ *              order, C(d_key + 2, 2) features, for poly_degree = 2 (Atlas-Torch README,
+ *              Atlas Extensions table, Polynomial Features); identity for poly_degree = 1
+ *   per chunk  (gate_mode = PER_CHUNK) one summed gradient G_c per chunk, optionally
+ *              orthogonalised per weight matrix by ns_steps quintic Newton-Schulz
+ *              iterations X <- aX + (b A + c A^2) X, A = X X^T, on X0 = G/(||G||_F + eps)
+ *              in the orientation with rows <= cols, then S_c = eta_c S - theta_c NS(G_c),
+ *              W_c = (1 - alpha_c) W + S_c (Atlas-Torch README, Atlas Extensions table,
+ *              Muon / Newton-Schulz; Bug Fixes table, no-omega ablation row)
+ *
+ * Conventions for every call:
+ *   - Every array pointer is a DEVICE pointer (HIP device memory on the handle's
+ *     device) unless stated otherwise; the caller owns it.  Arrays are dense and
+ *     row-major with the shapes given below; M = batch * heads, memory m = b*heads + h.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *     enqueued on it asynchronously; a call returns once its work is enqueued.
+ *   - Status codes are returned synchronously.  Argument and shape errors are
+ *     detected before anything is enqueued and leave the handle unchanged.
+ *   - A handle is not re-entrant: calls on one handle must not overlap; distinct
+ *     handles are independent.
+ */
+#ifndef ATLASMEM_H
+#define ATLASMEM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATLASMEM_ABI_VERSION 1
+
+typedef enum {
+  ATLASMEM_OK = 0,
+  ATLASMEM_E_INVALID = 1,      /* null pointer, negative size, bad enum value, wrong abi_version */
+  ATLASMEM_E_SHAPE = 2,        /* T not a multiple of the chunk, sizes beyond the stated limits  */
+  ATLASMEM_E_UNSUPPORTED = 3,  /* a valid but unsupported combination of options                  */
+  ATLASMEM_E_DEVICE = 4,       /* no usable gfx950 device, or a HIP runtime / launch error        */
+  ATLASMEM_E_NOMEM = 5,        /* device allocation failed (create only)                          */
+  ATLASMEM_E_NONFINITE = 6     /* a state element became NaN/Inf (reported by get_state)          */
+} atlasmem_status;
+
+typedef enum { ATLASMEM_LINEAR = 0, ATLASMEM_MLP2_SILU = 1 } atlasmem_memory_kind;
+typedef enum { ATLASMEM_PER_TOKEN = 0, ATLASMEM_PER_CHUNK = 1 } atlasmem_gate_mode;
+typedef enum { ATLASMEM_F32 = 0, ATLASMEM_BF16 = 1 } atlasmem_dtype;
+
+/* Operand precision of the matrix-core products (state and accumulation are fp32 always).
+ * BF16X3 splits every fp32 operand x into hi = bf16(x), lo = bf16(x - hi) and sums
+ * hi*hi + hi*lo + lo*hi (two products where one side is an exact bf16 input).
+ * AUTO = BF16X3.  The linear memory always runs in fp32 FMA. */
+typedef enum {
+  ATLASMEM_PREC_AUTO = 0,
+  ATLASMEM_PREC_BF16 = 1,
+  ATLASMEM_PREC_BF16X3 = 2
+} atlasmem_precision;
+
+typedef struct {
+  int32_t abi_version;   /* ATLASMEM_ABI_VERSION                                           */
+  int32_t memory_kind;   /* atlasmem_memory_kind                                            */
+  int32_t batch;         /* B >= 1                                                          */
+  int32_t heads;         /* H >= 1                                                          */
+  int32_t d_key;         /* raw key/query width, 1..1024                                    */
+  int32_t d_value;       /* value width, 1..1024                                            */
+  int32_t d_hidden;      /* MLP hidden width, 1..4096 (ignored for LINEAR)                  */
+  int32_t poly_degree;   /* 1 (identity) or 2 (degree <= 2 monomials, 1/deg!)               */
+  int32_t chunk;         /* tokens per chunk, 1..1024                                       */
+  int32_t omega_window;  /* c >= 1, c <= 64                                                 */
+  int32_t gate_mode;     /* atlasmem_gate_mode                                              */
+  int32_t ns_steps;      /* 0 (none) or 1..16 Newton-Schulz iterations (PER_CHUNK only)     */
+  float ns_a, ns_b, ns_c;/* quintic coefficients (Muon: 3.4445, -4.7750, 2.0315)            */
+  float ns_eps;          /* added to ||G||_F before normalising (e.g. 1e-7)                 */
+  int32_t input_dtype;   /* atlasmem_dtype of K, Q, V                                       */
+  int32_t output_dtype;  /* atlasmem_dtype of Y                                             */
+  int32_t precision;     /* atlasmem_precision                                              */
+} atlasmem_config;
+
+typedef struct atlasmem_handle_s* atlasmem_handle;
+
+/* Parameter count P per memory: d_value*d_in (LINEAR) or d_hidden*d_in + d_value*d_hidden,
+ * with d_in = d_key (poly_degree 1) or C(d_key + 2, 2) (poly_degree 2).  The state layout
+ * of one memory is W1 (row-major) followed by W2 (row-major); LINEAR: W.  Returns -1 for an
+ * invalid config. */
+int64_t atlasmem_param_count(const atlasmem_config* cfg);
+
+int atlasmem_abi_version(void);
+const char* atlasmem_status_string(int status);
+
+/* Validates `cfg`, selects the device's kernels, allocates every buffer the handle will
+ * need (state, momentum, window history, per-chunk workspace) and copies the initial
+ * state in, ordered on `stream`.
+ *   W0: [M, P] fp32 initial weights, or NULL for zeros.
+ *   S0: [M, P] fp32 initial momentum, or NULL for zeros.
+ * The window history starts empty (start of a sequence).  The handle is bound to the
+ * device current at the call.  On error *out is set to NULL and nothing is leaked. */
+atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, const float* S0,
+                                void* stream, atlasmem_handle* out);
+
+/* Consumes T tokens of every memory: for each chunk, writes the chunk's retrieved rows
+ * Y = M_{W_start}(phi(Q)) and advances (W, S) by the chunk's update.  T must be a multiple
+ * of cfg.chunk (else E_SHAPE); T = 0 is a no-op.  The window history (last c - 1 keys,
+ * values and gammas) and the state carry over to the next call, so one call over T tokens
+ * equals consecutive calls over T1 + T2 tokens (T1 a multiple of the chunk).
+ *   K, Q:  [M, T, d_key]   input_dtype
+ *   V:     [M, T, d_value] input_dtype
+ *   theta, eta, alpha: fp32 [M, T] (PER_TOKEN) or [M, T / chunk] (PER_CHUNK)
+ *   gamma: fp32 [M, T] for omega_window > 1, must be NULL for omega_window == 1
+ *   Y:     [M, T, d_value] output_dtype, or NULL to skip retrieval
+ * Never allocates. */
+atlasmem_status atlasmem_update_chunked(atlasmem_handle h, const void* K, const void* Q, const void* V,
+                                        const float* theta, const float* eta, const float* alpha,
+                                        const float* gamma, int64_t T, void* Y, void* stream);
+
+/* Retrieval with no update (titans-torch 0.1.2, forward(): inference without updating the
+ * memory): Y[m, t] = M_W(phi(Q[m, t])) with the current weights, for T >= 0 tokens.
+ *   Q: [M, T, d_key] input_dtype;  Y: [M, T, d_value] output_dtype.  Never allocates. */
+atlasmem_status atlasmem_retrieve(atlasmem_handle h, const void* Q, int64_t T, void* Y, void* stream);
+
+/* Copies the current weights / momentum out to W, S ([M, P] fp32 device arrays; either may be
+ * NULL).  Synchronises `stream` to read the device's non-finite flag and returns
+ * E_NONFINITE if any update since create / set_state produced a NaN or Inf (the copies are
+ * still made). */
+atlasmem_status atlasmem_get_state(atlasmem_handle h, float* W, float* S, void* stream);
+
+/* Replaces the weights / momentum ([M, P] fp32 device arrays; NULL = zeros) and clears the
+ * non-finite flag.  The window history is left as it is. */
+atlasmem_status atlasmem_set_state(atlasmem_handle h, const float* W, const float* S, void* stream);
+
+/* Forgets the window history (start of a new sequence).  State is unchanged. */
+atlasmem_status atlasmem_reset_history(atlasmem_handle h, void* stream);
+
+/* Waits for the handle's work and frees everything it owns.  NULL is a no-op. */
+void atlasmem_destroy(atlasmem_handle h);
+
+/* ---------------------------------------------------------------------------------------
+ * Stand-alone stages of the path (the same kernels the update runs), for callers that
+ * want one stage and for measuring each against its own roofline.  Device pointers,
+ * asynchronous on `stream`.
+ * ------------------------------------------------------------------------------------- */
+
+/* Gate scan over the chunk-internal recurrence (derived from Eq. 13-14 with all gradients
+ * of a chunk at the chunk-start weights).  For every memory and chunk [s, s+C) of the
+ * per-token gates theta, eta, alpha ([M, T] fp32, T a multiple of C):
+ *   e_j = prod_{l=j+1..C} eta_l,  b_j = prod_{l=j+1..C} (1 - alpha_l),
+ *   w_C = 1, w_j = b_j + eta_{j+1} w_{j+1},
+ *   cS[m, s+j] = theta_j e_j,  cW[m, s+j] = theta_j w_j            ([M, T] fp32)
+ *   chunk_scalars[m, k, 0..2] = (prod eta, prod (1 - alpha), eta_1 w_1)   ([M, T/C, 3])
+ * so that S_end = P S_0 - sum_j cS_j g_j and W_end = beta W_0 + a_S S_0 - sum_j cW_j g_j. */
+atlasmem_status atlasmem_gate_scan(const float* theta, const float* eta, const float* alpha, int64_t M,
+                                   int64_t T, int32_t chunk, float* cW, float* cS, float* chunk_scalars,
+                                   void* stream);
+
+/* Omega window coefficients: for chunk k = [s, s+C) and row r in [0, C + c - 1), token
+ * i = s - (c - 1) + r (ATLAS summary, section 3.2):
+ *   oW[m, k, r] = gamma_i * sum_{t = max(i, s)}^{min(i + c - 1, s + C - 1)} cW[m, t]   (same for oS)
+ * gamma: [M, T]; tokens before 0 take gamma from `gamma_hist` ([M, c-1], the c - 1 tokens
+ * before this T, oldest first; NULL = none, i.e. the start of the sequence, weight 0).
+ * cW, cS: [M, T];  oW, oS: [M, T/C, C + c - 1] fp32. */
+atlasmem_status atlasmem_omega_coeffs(const float* cW, const float* cS, const float* gamma,
+                                      const float* gamma_hist, int64_t M, int64_t T, int32_t chunk,
+                                      int32_t window, float* oW, float* oS, void* stream);
+
+/* Polynomial feature map phi (poly_degree 2) of n vectors of width d (1..1024):
+ *   X: [n, d] (in_dtype),  F: [n, C(d+2, 2)] fp32 (exact: every monomial of bf16 inputs
+ *   is representable in fp32). */
+atlasmem_status atlasmem_poly_features(const void* X, int32_t in_dtype, int64_t n, int32_t d, float* F,
+                                       void* stream);
+
+/* Newton-Schulz orthogonalisation of n_mat independent rows x cols fp32 matrices
+ * (G, out: [n_mat, rows, cols]; out may not alias G), with the handle-free semantics of
+ * the per-chunk path above.  precision as in atlasmem_config.  Never allocates when
+ * rows, cols <= 128 and min(rows, cols) <= 64; larger matrices return E_UNSUPPORTED. */
+atlasmem_status atlasmem_newton_schulz(const float* G, int64_t n_mat, int32_t rows, int32_t cols,
+                                       int32_t steps, float a, float b, float c, float eps,
+                                       int32_t precision, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATLASMEM_H */

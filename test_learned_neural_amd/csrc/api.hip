@@ -1,0 +1,376 @@
+// C ABI of the atlasmem library: validation, the handle and its device arena, dispatch.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "common.h"
+#include "internal.h"
+
+using namespace am;
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    ok = (prev == dev) || (hipSetDevice(dev) == hipSuccess);
+  }
+  ~DeviceGuard() {
+    if (ok && prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+int64_t feature_count(int dk, int poly) { return poly == 1 ? dk : 1 + dk + (int64_t)dk * (dk + 1) / 2; }
+
+atlasmem_status validate(const atlasmem_config* c) {
+  if (!c) return ATLASMEM_E_INVALID;
+  if (c->abi_version != ATLASMEM_ABI_VERSION) return ATLASMEM_E_INVALID;
+  if (c->memory_kind != ATLASMEM_LINEAR && c->memory_kind != ATLASMEM_MLP2_SILU) return ATLASMEM_E_INVALID;
+  if (c->batch < 1 || c->heads < 1 || c->d_key < 1 || c->d_value < 1 || c->chunk < 1 || c->omega_window < 1)
+    return ATLASMEM_E_INVALID;
+  if (c->memory_kind == ATLASMEM_MLP2_SILU && c->d_hidden < 1) return ATLASMEM_E_INVALID;
+  if (c->poly_degree != 1 && c->poly_degree != 2) return ATLASMEM_E_INVALID;
+  if (c->gate_mode != ATLASMEM_PER_TOKEN && c->gate_mode != ATLASMEM_PER_CHUNK) return ATLASMEM_E_INVALID;
+  if (c->ns_steps < 0 || c->ns_steps > 16) return ATLASMEM_E_INVALID;
+  if ((c->input_dtype != ATLASMEM_F32 && c->input_dtype != ATLASMEM_BF16) ||
+      (c->output_dtype != ATLASMEM_F32 && c->output_dtype != ATLASMEM_BF16))
+    return ATLASMEM_E_INVALID;
+  if (c->precision < ATLASMEM_PREC_AUTO || c->precision > ATLASMEM_PREC_BF16X3) return ATLASMEM_E_INVALID;
+  if (c->ns_steps > 0 && !(c->ns_eps >= 0.0f)) return ATLASMEM_E_INVALID;
+  if ((int64_t)c->batch * c->heads > (1 << 20)) return ATLASMEM_E_SHAPE;
+  if (c->d_key > 1024 || c->d_value > 1024 || c->d_hidden > 4096 || c->chunk > 1024 || c->omega_window > 64)
+    return ATLASMEM_E_SHAPE;
+  const int64_t din = feature_count(c->d_key, c->poly_degree);
+  if (din > 16384) return ATLASMEM_E_SHAPE;
+  // valid but not provided
+  if (c->gate_mode == ATLASMEM_PER_CHUNK && c->omega_window > 1) return ATLASMEM_E_UNSUPPORTED;
+  if (c->gate_mode == ATLASMEM_PER_TOKEN && c->ns_steps > 0) return ATLASMEM_E_UNSUPPORTED;
+  if (c->memory_kind == ATLASMEM_LINEAR) {
+    if (din > 64 || c->d_value > 64 || c->omega_window > 8 || c->ns_steps > 0) return ATLASMEM_E_UNSUPPORTED;
+  } else if (c->ns_steps > 0) {
+    if (!ns_supported(c->d_hidden, (int)din) || !ns_supported(c->d_value, c->d_hidden)) return ATLASMEM_E_UNSUPPORTED;
+  }
+  return ATLASMEM_OK;
+}
+
+Dims make_dims(const atlasmem_config* c) {
+  Dims d;
+  d.M = c->batch * c->heads;
+  d.dk = c->d_key;
+  d.dv = c->d_value;
+  d.dh = c->memory_kind == ATLASMEM_MLP2_SILU ? c->d_hidden : 0;
+  d.poly = c->poly_degree;
+  d.din = (int)feature_count(c->d_key, c->poly_degree);
+  d.C = c->chunk;
+  d.c = c->omega_window;
+  d.Rk = d.C + d.c - 1;
+  d.Rt = d.Rk + d.C;
+  d.kind = c->memory_kind;
+  if (d.kind == ATLASMEM_LINEAR) {
+    d.P1 = (int64_t)d.dv * d.din;
+    d.P = d.P1;
+  } else {
+    d.P1 = (int64_t)d.dh * d.din;
+    d.P = d.P1 + (int64_t)d.dv * d.dh;
+  }
+  d.gate_mode = c->gate_mode;
+  d.ns_steps = c->ns_steps;
+  d.ns_a = c->ns_a;
+  d.ns_b = c->ns_b;
+  d.ns_c = c->ns_c;
+  d.ns_eps = c->ns_eps;
+  d.in_bf16 = c->input_dtype == ATLASMEM_BF16;
+  d.out_bf16 = c->output_dtype == ATLASMEM_BF16;
+  d.split = c->precision != ATLASMEM_PREC_BF16;
+  return d;
+}
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  }
+};
+
+bool device_is_gfx950(int dev) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+  return strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+}
+
+hipStream_t S(void* p) { return (hipStream_t)p; }
+
+}  // namespace
+
+extern "C" {
+
+int atlasmem_abi_version(void) { return ATLASMEM_ABI_VERSION; }
+
+const char* atlasmem_status_string(int status) {
+  switch (status) {
+    case ATLASMEM_OK: return "ok";
+    case ATLASMEM_E_INVALID: return "invalid argument";
+    case ATLASMEM_E_SHAPE: return "bad shape";
+    case ATLASMEM_E_UNSUPPORTED: return "unsupported combination";
+    case ATLASMEM_E_DEVICE: return "device or launch error";
+    case ATLASMEM_E_NOMEM: return "out of device memory";
+    case ATLASMEM_E_NONFINITE: return "non-finite state";
+    default: return "unknown status";
+  }
+}
+
+int64_t atlasmem_param_count(const atlasmem_config* cfg) {
+  if (!cfg) return -1;
+  atlasmem_status s = validate(cfg);
+  if (s == ATLASMEM_E_INVALID) return -1;
+  return make_dims(cfg).P;
+}
+
+atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, const float* S0, void* stream,
+                                atlasmem_handle* out) {
+  if (!out) return ATLASMEM_E_INVALID;
+  *out = nullptr;
+  atlasmem_status s = validate(cfg);
+  if (s != ATLASMEM_OK) return s;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return ATLASMEM_E_DEVICE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATLASMEM_E_DEVICE;
+  if (!device_is_gfx950(dev)) return ATLASMEM_E_DEVICE;
+
+  Handle* h = new (std::nothrow) Handle();
+  if (!h) return ATLASMEM_E_NOMEM;
+  h->cfg = *cfg;
+  h->d = make_dims(cfg);
+  h->device = dev;
+  const Dims& d = h->d;
+  const int64_t M = d.M;
+  const int H = d.c - 1 > 0 ? d.c - 1 : 1;
+
+  Carver cv;
+  size_t oW[2], oS[2], ohk[2], ohv[2], ohg[2];
+  for (int i = 0; i < 2; ++i) {
+    oW[i] = cv.take(sizeof(float) * M * d.P);
+    oS[i] = cv.take(sizeof(float) * M * d.P);
+    ohk[i] = cv.take(sizeof(float) * M * H * d.dk);
+    ohv[i] = cv.take(sizeof(float) * M * H * d.dv);
+    ohg[i] = cv.take(sizeof(float) * M * H);
+  }
+  const size_t oflag = cv.take(256);
+  const size_t state_end = cv.off;
+  size_t oZ = 0, oD2 = 0, oD1 = 0, ocW = 0, ocS = 0, ooW = 0, ooS = 0, oscal = 0, oG = 0, oZr = 0;
+  if (d.kind == ATLASMEM_MLP2_SILU) {
+    oZ = cv.take(sizeof(float) * M * d.Rt * d.dh);
+    oD2 = cv.take(sizeof(float) * M * d.Rk * d.dv);
+    oD1 = cv.take(sizeof(float) * M * d.Rk * d.dh);
+    const int64_t per_chunk_floats = M * (2 * (int64_t)d.C + 2 * (int64_t)d.Rk + 3);
+    int64_t ncb = ((int64_t)32 << 20) / 4 / per_chunk_floats;
+    ncb = ncb < 1 ? 1 : (ncb > 4096 ? 4096 : ncb);
+    h->ncb = (int)ncb;
+    if (d.gate_mode == ATLASMEM_PER_TOKEN) {
+      ocW = cv.take(sizeof(float) * M * ncb * d.C);
+      ocS = cv.take(sizeof(float) * M * ncb * d.C);
+      oscal = cv.take(sizeof(float) * M * ncb * 3);
+      if (d.c > 1) {
+        ooW = cv.take(sizeof(float) * M * ncb * d.Rk);
+        ooS = cv.take(sizeof(float) * M * ncb * d.Rk);
+      }
+    }
+    if (d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0) oG = cv.take(sizeof(float) * M * d.P);
+    int64_t rb = 1024;
+    while (rb > 64 && (int64_t)M * rb * d.dh * 4 > ((int64_t)256 << 20)) rb /= 2;
+    h->rb = (int)rb;
+    oZr = cv.take(sizeof(float) * M * rb * d.dh);
+  }
+  h->arena_bytes = cv.off;
+  if (hipMalloc(&h->arena, h->arena_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return ATLASMEM_E_NOMEM;
+  }
+  char* base = (char*)h->arena;
+  for (int i = 0; i < 2; ++i) {
+    h->W[i] = (float*)(base + oW[i]);
+    h->S[i] = (float*)(base + oS[i]);
+    h->hk[i] = (float*)(base + ohk[i]);
+    h->hv[i] = (float*)(base + ohv[i]);
+    h->hg[i] = (float*)(base + ohg[i]);
+  }
+  h->flag = (int*)(base + oflag);
+  if (d.kind == ATLASMEM_MLP2_SILU) {
+    h->Z = (float*)(base + oZ);
+    h->D2 = (float*)(base + oD2);
+    h->D1 = (float*)(base + oD1);
+    h->cW = ocW ? (float*)(base + ocW) : nullptr;
+    h->cS = ocS ? (float*)(base + ocS) : nullptr;
+    h->oW = ooW ? (float*)(base + ooW) : nullptr;
+    h->oS = ooS ? (float*)(base + ooS) : nullptr;
+    h->scal = oscal ? (float*)(base + oscal) : nullptr;
+    h->G = oG ? (float*)(base + oG) : nullptr;
+    h->Zr = (float*)(base + oZr);
+  }
+  h->cur = 0;
+  h->hcur = 0;
+  hipStream_t st = S(stream);
+  bool ok = hipMemsetAsync(h->arena, 0, state_end, st) == hipSuccess;
+  if (ok && W0) ok = hipMemcpyAsync(h->W[0], W0, sizeof(float) * M * d.P, hipMemcpyDeviceToDevice, st) == hipSuccess;
+  if (ok && S0) ok = hipMemcpyAsync(h->S[0], S0, sizeof(float) * M * d.P, hipMemcpyDeviceToDevice, st) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    (void)hipStreamSynchronize(st);
+    (void)hipFree(h->arena);
+    delete h;
+    return ATLASMEM_E_DEVICE;
+  }
+  *out = h;
+  return ATLASMEM_OK;
+}
+
+atlasmem_status atlasmem_update_chunked(atlasmem_handle hh, const void* K, const void* Q, const void* V,
+                                        const float* theta, const float* eta, const float* alpha, const float* gamma,
+                                        int64_t T, void* Y, void* stream) {
+  Handle* h = (Handle*)hh;
+  if (!h || T < 0) return ATLASMEM_E_INVALID;
+  const Dims& d = h->d;
+  if (T % d.C != 0) return ATLASMEM_E_SHAPE;
+  if (T == 0) return ATLASMEM_OK;
+  if (!K || !V || !theta || !eta || !alpha || (Y && !Q)) return ATLASMEM_E_INVALID;
+  if ((d.c > 1) != (gamma != nullptr)) return ATLASMEM_E_INVALID;
+  DeviceGuard g(h->device);
+  if (!g.ok) return ATLASMEM_E_DEVICE;
+  if (d.kind == ATLASMEM_LINEAR) {
+    atlasmem_status s = launch_linear_update(h, K, Q, V, theta, eta, alpha, gamma, T, Y, S(stream));
+    if (s != ATLASMEM_OK) return s;
+    if (d.c > 1) {
+      s = launch_history_update(h, K, V, gamma, T, S(stream));
+      if (s != ATLASMEM_OK) return s;
+      h->hcur = 1 - h->hcur;
+    }
+    return ATLASMEM_OK;
+  }
+  return mlp_update(h, K, Q, V, theta, eta, alpha, gamma, T, Y, S(stream));
+}
+
+atlasmem_status atlasmem_retrieve(atlasmem_handle hh, const void* Q, int64_t T, void* Y, void* stream) {
+  Handle* h = (Handle*)hh;
+  if (!h || T < 0) return ATLASMEM_E_INVALID;
+  if (T == 0) return ATLASMEM_OK;
+  if (!Q || !Y) return ATLASMEM_E_INVALID;
+  DeviceGuard g(h->device);
+  if (!g.ok) return ATLASMEM_E_DEVICE;
+  if (h->d.kind == ATLASMEM_LINEAR) return launch_linear_retrieve(h, Q, T, Y, S(stream));
+  return mlp_retrieve(h, Q, T, Y, S(stream));
+}
+
+atlasmem_status atlasmem_get_state(atlasmem_handle hh, float* W, float* Sm, void* stream) {
+  Handle* h = (Handle*)hh;
+  if (!h) return ATLASMEM_E_INVALID;
+  DeviceGuard g(h->device);
+  if (!g.ok) return ATLASMEM_E_DEVICE;
+  const size_t bytes = sizeof(float) * h->d.M * h->d.P;
+  hipStream_t st = S(stream);
+  if (W && hipMemcpyAsync(W, h->W[h->cur], bytes, hipMemcpyDeviceToDevice, st) != hipSuccess) return ATLASMEM_E_DEVICE;
+  if (Sm && hipMemcpyAsync(Sm, h->S[h->cur], bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return ATLASMEM_E_DEVICE;
+  int flag = 0;
+  if (hipMemcpyAsync(&flag, h->flag, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return ATLASMEM_E_DEVICE;
+  if (hipStreamSynchronize(st) != hipSuccess) return ATLASMEM_E_DEVICE;
+  return flag ? ATLASMEM_E_NONFINITE : ATLASMEM_OK;
+}
+
+atlasmem_status atlasmem_set_state(atlasmem_handle hh, const float* W, const float* Sm, void* stream) {
+  Handle* h = (Handle*)hh;
+  if (!h) return ATLASMEM_E_INVALID;
+  DeviceGuard g(h->device);
+  if (!g.ok) return ATLASMEM_E_DEVICE;
+  const size_t bytes = sizeof(float) * h->d.M * h->d.P;
+  hipStream_t st = S(stream);
+  bool ok = true;
+  ok = ok && (W ? hipMemcpyAsync(h->W[h->cur], W, bytes, hipMemcpyDeviceToDevice, st)
+                : hipMemsetAsync(h->W[h->cur], 0, bytes, st)) == hipSuccess;
+  ok = ok && (Sm ? hipMemcpyAsync(h->S[h->cur], Sm, bytes, hipMemcpyDeviceToDevice, st)
+                 : hipMemsetAsync(h->S[h->cur], 0, bytes, st)) == hipSuccess;
+  ok = ok && hipMemsetAsync(h->flag, 0, sizeof(int), st) == hipSuccess;
+  return ok ? ATLASMEM_OK : ATLASMEM_E_DEVICE;
+}
+
+atlasmem_status atlasmem_reset_history(atlasmem_handle hh, void* stream) {
+  Handle* h = (Handle*)hh;
+  if (!h) return ATLASMEM_E_INVALID;
+  DeviceGuard g(h->device);
+  if (!g.ok) return ATLASMEM_E_DEVICE;
+  const Dims& d = h->d;
+  const int H = d.c - 1 > 0 ? d.c - 1 : 1;
+  hipStream_t st = S(stream);
+  for (int i = 0; i < 2; ++i) {
+    if (hipMemsetAsync(h->hk[i], 0, sizeof(float) * d.M * H * d.dk, st) != hipSuccess ||
+        hipMemsetAsync(h->hv[i], 0, sizeof(float) * d.M * H * d.dv, st) != hipSuccess ||
+        hipMemsetAsync(h->hg[i], 0, sizeof(float) * d.M * H, st) != hipSuccess)
+      return ATLASMEM_E_DEVICE;
+  }
+  return ATLASMEM_OK;
+}
+
+void atlasmem_destroy(atlasmem_handle hh) {
+  Handle* h = (Handle*)hh;
+  if (!h) return;
+  {
+    DeviceGuard g(h->device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(h->arena);
+  }
+  delete h;
+}
+
+atlasmem_status atlasmem_gate_scan(const float* theta, const float* eta, const float* alpha, int64_t M, int64_t T,
+                                   int32_t chunk, float* cW, float* cS, float* chunk_scalars, void* stream) {
+  if (M < 0 || T < 0 || chunk < 1) return ATLASMEM_E_INVALID;
+  if (T % chunk != 0) return ATLASMEM_E_SHAPE;
+  if (M == 0 || T == 0) return ATLASMEM_OK;
+  if (!theta || !eta || !alpha || !cW || !cS || !chunk_scalars) return ATLASMEM_E_INVALID;
+  if (M > INT32_MAX || T / chunk > INT32_MAX) return ATLASMEM_E_SHAPE;
+  return launch_gate_scan(theta, eta, alpha, (int)M, T, 0, (int)(T / chunk), chunk, cW, cS, T, chunk_scalars,
+                          (T / chunk) * 3, S(stream));
+}
+
+atlasmem_status atlasmem_omega_coeffs(const float* cW, const float* cS, const float* gamma, const float* gamma_hist,
+                                      int64_t M, int64_t T, int32_t chunk, int32_t window, float* oW, float* oS,
+                                      void* stream) {
+  if (M < 0 || T < 0 || chunk < 1 || window < 1 || window > 64) return ATLASMEM_E_INVALID;
+  if (T % chunk != 0) return ATLASMEM_E_SHAPE;
+  if (M == 0 || T == 0) return ATLASMEM_OK;
+  if (!cW || !cS || !gamma || !oW || !oS) return ATLASMEM_E_INVALID;
+  if (M > INT32_MAX || T / chunk > INT32_MAX) return ATLASMEM_E_SHAPE;
+  const int Rk = chunk + window - 1;
+  return launch_omega(cW, cS, T, gamma, T, gamma_hist, (int)M, 0, (int)(T / chunk), chunk, window, oW, oS,
+                      (T / chunk) * Rk, S(stream));
+}
+
+atlasmem_status atlasmem_poly_features(const void* X, int32_t in_dtype, int64_t n, int32_t d, float* F,
+                                       void* stream) {
+  if (n < 0 || d < 1 || d > 1024 || (in_dtype != ATLASMEM_F32 && in_dtype != ATLASMEM_BF16))
+    return ATLASMEM_E_INVALID;
+  if (n == 0) return ATLASMEM_OK;
+  if (!X || !F) return ATLASMEM_E_INVALID;
+  return launch_poly(X, in_dtype == ATLASMEM_BF16, n, d, F, S(stream));
+}
+
+atlasmem_status atlasmem_newton_schulz(const float* G, int64_t n_mat, int32_t rows, int32_t cols, int32_t steps,
+                                       float a, float b, float c, float eps, int32_t precision, float* out,
+                                       void* stream) {
+  if (n_mat < 0 || rows < 1 || cols < 1 || steps < 0 || steps > 16 || !(eps >= 0.0f)) return ATLASMEM_E_INVALID;
+  if (precision < ATLASMEM_PREC_AUTO || precision > ATLASMEM_PREC_BF16X3) return ATLASMEM_E_INVALID;
+  if (!ns_supported(rows, cols)) return ATLASMEM_E_UNSUPPORTED;
+  if (n_mat == 0) return ATLASMEM_OK;
+  if (!G || !out || G == out) return ATLASMEM_E_INVALID;
+  if (n_mat > INT32_MAX) return ATLASMEM_E_SHAPE;
+  return launch_ns(G, (int64_t)rows * cols, (int)n_mat, rows, cols, steps, a, b, c, eps,
+                   precision != ATLASMEM_PREC_BF16, out, nullptr, S(stream));
+}
+
+}  // extern "C"

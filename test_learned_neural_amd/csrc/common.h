@@ -1,0 +1,94 @@
+// Shared device helpers for the atlasmem kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace am {
+
+constexpr int kWave = 64;
+
+// Round-to-nearest-even fp32 -> bf16 bit pattern (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// Split x into hi = bf16(x) and lo = bf16(x - hi); hi + lo carries ~16 significant bits.
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = bf16_bits(x);
+  lo = bf16_bits(x - bf16_value(hi));
+}
+
+// Pack eight fp32 values into bf16x8 hi / lo operand words (little-endian pairs).
+__device__ __forceinline__ void pack8(const float* v, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t h0, l0, h1, l1;
+    split_bf16(v[2 * p], h0, l0);
+    split_bf16(v[2 * p + 1], h1, l1);
+    hi[p] = h0 | (h1 << 16);
+    lo[p] = l0 | (l1 << 16);
+  }
+}
+__device__ __forceinline__ void pack8_hi(const float* v, u32x4& hi) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) hi[p] = bf16_bits(v[2 * p]) | (bf16_bits(v[2 * p + 1]) << 16);
+}
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float siluf_(float z) { return z * sigmoidf_(z); }
+__device__ __forceinline__ float silu_primef_(float z) {
+  float s = sigmoidf_(z);
+  return s * (1.0f + z * (1.0f - s));
+}
+
+// Load one input element (bf16 bits or fp32) as float.
+__device__ __forceinline__ float load_in(const void* p, int64_t idx, int is_bf16) {
+  if (is_bf16) return bf16_value(((const uint16_t*)p)[idx]);
+  return ((const float*)p)[idx];
+}
+
+}  // namespace am
+
+// Host-side launch helpers
+#define AM_LAUNCH_CHECK()                                   \
+  do {                                                      \
+    hipError_t e_ = hipGetLastError();                      \
+    if (e_ != hipSuccess) return ATLASMEM_E_DEVICE;         \
+  } while (0)
+
+namespace am {
+
+// Degree-2 feature map phi(x) = [1, x_0..x_{d-1}, x_i x_j / 2 (i <= j, row-major upper
+// triangle = combinations_with_replacement order)], C(d+2, 2) features.  The pair index p of
+// (i, j) is start(i) + (j - i) with start(i) = i d - i (i - 1) / 2.
+__device__ __forceinline__ int pair_start(int i, int d) { return i * d - (i * (i - 1)) / 2; }
+__device__ __forceinline__ void pair_of(int p, int d, int& i, int& j) {
+  const float fd = 2.0f * d + 1.0f;
+  int ii = (int)((fd - sqrtf(fmaxf(fd * fd - 8.0f * (float)p, 0.0f))) * 0.5f);
+  ii = ii < 0 ? 0 : (ii > d - 1 ? d - 1 : ii);
+  while (ii > 0 && pair_start(ii, d) > p) --ii;
+  while (ii + 1 < d && pair_start(ii + 1, d) <= p) ++ii;
+  i = ii;
+  j = ii + (p - pair_start(ii, d));
+}
+__device__ __forceinline__ int poly_count(int d) { return 1 + d + (d * (d + 1)) / 2; }
+
+}  // namespace am

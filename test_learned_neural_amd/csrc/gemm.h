@@ -1,0 +1,160 @@
+// Batched small-GEMM engine on CDNA4 matrix cores (v_mfma_f32_16x16x32_bf16).
+//
+// out[z](i, j) = sum_k A[z](i, k) * B[z](k, j) for every batch index z, with
+//  - A and B produced element-wise by loader functors (so transposes, feature maps,
+//    SiLU and per-row coefficients are applied while staging, never materialised),
+//  - each fp32 operand split into bf16 hi + lo in LDS and the product formed as
+//    hi*hi (+ hi*lo + lo*hi in the split precision; a side known to be an exact bf16
+//    input contributes no lo term),
+//  - fp32 accumulation in the matrix cores and a functor epilogue per output element.
+//
+// Tile 64 x 64 x 32, 256 threads = 4 waves in a 2 x 2 grid, each wave 32 x 32 = 2 x 2
+// MFMA blocks of 16 x 16.  Grid: (ceil(N/64), ceil(M/64), batch).
+#pragma once
+
+#include "common.h"
+
+namespace am {
+
+// Loader contract: load8(z, outer, k0, v) fills v[u] = Op(outer, k0 + u) for u = 0..7, zero
+// outside [0, outer_dim) x [0, K).  For A, outer = row i; for B, outer = column j.
+
+constexpr int GT = 64;       // output tile
+constexpr int GK = 32;       // k step
+constexpr int GLD = GK + 8;  // LDS row stride in bf16 (80 bytes: 16-byte aligned, staggers banks)
+
+template <bool SPLIT, bool A_EXACT, bool B_EXACT, class LA, class LB, class EP>
+__global__ void __launch_bounds__(256) gemm_tile_kernel(int M, int N, int K, LA la, LB lb, EP ep) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ah[GT * GLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bh[GT * GLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Al[SPLIT && !A_EXACT ? GT * GLD : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Bl[SPLIT && !B_EXACT ? GT * GLD : 8];
+
+  const int z = blockIdx.z;
+  const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int srow = t >> 2, sk = (t & 3) * 8;
+  for (int k0 = 0; k0 < K; k0 += GK) {
+    {
+      float v[8];
+      la.load8(z, m0 + srow, k0 + sk, v);
+      u32x4 hi, lo;
+      if (SPLIT && !A_EXACT) {
+        pack8(v, hi, lo);
+        *(u32x4*)&Al[srow * GLD + sk] = lo;
+      } else {
+        pack8_hi(v, hi);
+      }
+      *(u32x4*)&Ah[srow * GLD + sk] = hi;
+    }
+    {
+      float v[8];
+      lb.load8(z, n0 + srow, k0 + sk, v);
+      u32x4 hi, lo;
+      if (SPLIT && !B_EXACT) {
+        pack8(v, hi, lo);
+        *(u32x4*)&Bl[srow * GLD + sk] = lo;
+      } else {
+        pack8_hi(v, hi);
+      }
+      *(u32x4*)&Bh[srow * GLD + sk] = hi;
+    }
+    __syncthreads();
+    u32x4 ah[2], bh[2], al[2], bl[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = (wm * 32 + i * 16 + lr) * GLD + lk;
+      ah[i] = *(const u32x4*)&Ah[r];
+      if (SPLIT && !A_EXACT) al[i] = *(const u32x4*)&Al[r];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = (wn * 32 + j * 16 + lr) * GLD + lk;
+      bh[j] = *(const u32x4*)&Bh[r];
+      if (SPLIT && !B_EXACT) bl[j] = *(const u32x4*)&Bl[r];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = mfma16(ah[i], bh[j], acc[i][j]);
+        if (SPLIT && !B_EXACT) acc[i][j] = mfma16(ah[i], bl[j], acc[i][j]);
+        if (SPLIT && !A_EXACT) acc[i][j] = mfma16(al[i], bh[j], acc[i][j]);
+      }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+        const int col = n0 + wn * 32 + j * 16 + lr;
+        if (row < M && col < N) ep(z, row, col, acc[i][j][r]);
+      }
+}
+
+template <bool A_EXACT, bool B_EXACT, class LA, class LB, class EP>
+inline void launch_gemm(bool split, int M, int N, int K, int batch, const LA& la, const LB& lb, const EP& ep,
+                        hipStream_t st) {
+  if (M <= 0 || N <= 0 || batch <= 0) return;
+  dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch);
+  if (split)
+    hipLaunchKernelGGL((gemm_tile_kernel<true, A_EXACT, B_EXACT, LA, LB, EP>), grid, dim3(256), 0, st, M, N, K, la,
+                       lb, ep);
+  else
+    hipLaunchKernelGGL((gemm_tile_kernel<false, A_EXACT, B_EXACT, LA, LB, EP>), grid, dim3(256), 0, st, M, N, K, la,
+                       lb, ep);
+}
+
+// ---------------------------------------------------------------------------- generic loaders
+
+enum Xform { XF_NONE = 0, XF_SILU = 1, XF_COEF = 2, XF_SCALE = 3 };
+
+// Element (outer, k) = xf(base[zoff(z) + outer * so + k * sk]); zoff(z) = (z / zdiv) * sz.
+// XF_COEF multiplies by coef[(z / zdiv) * cz + csel(z) + k]  (per-k coefficient; csel picks
+// one of two coefficient arrays by z % 2 when `pair` is set).
+// XF_SCALE multiplies by scale[z].
+struct StridedLoader {
+  const float* base;
+  int64_t sz, so, sk;
+  int zdiv;
+  int outer_dim, K;
+  int xf;
+  const float* coef0;
+  const float* coef1;
+  int64_t cz;
+  const float* scale;
+  __device__ __forceinline__ void load8(int z, int outer, int k0, float* v) const {
+    const int zz = z / zdiv;
+    const float* p = base + zz * sz + (int64_t)outer * so;
+    const float* cf = nullptr;
+    if (xf == XF_COEF) cf = ((zdiv == 2 && (z & 1)) ? coef1 : coef0) + zz * cz;
+    const float sc = (xf == XF_SCALE) ? scale[z] : 1.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u;
+      float x = 0.0f;
+      if (outer < outer_dim && k < K) {
+        x = p[(int64_t)k * sk];
+        if (xf == XF_SILU) x = siluf_(x);
+        else if (xf == XF_COEF) x *= cf[k];
+        else if (xf == XF_SCALE) x *= sc;
+      }
+      v[u] = x;
+    }
+  }
+};
+
+}  // namespace am

@@ -1,0 +1,108 @@
+// Internal declarations shared by the atlasmem translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/atlasmem.h"
+
+namespace am {
+
+// Derived sizes of a validated configuration.
+struct Dims {
+  int M;        // memories = batch * heads
+  int dk, dv, dh, din;
+  int poly;
+  int C, c;     // chunk, Omega window
+  int Rk;       // key rows per chunk incl. window history = C + c - 1
+  int Rt;       // key rows + query rows = Rk + C
+  int64_t P;    // parameters per memory
+  int64_t P1;   // size of W1 (MLP) / W (linear)
+  int kind, gate_mode, ns_steps;
+  float ns_a, ns_b, ns_c, ns_eps;
+  int in_bf16, out_bf16;
+  bool split;   // bf16 hi/lo split products
+};
+
+}  // namespace am
+
+// The opaque handle of the C ABI.
+struct atlasmem_handle_s {
+  atlasmem_config cfg;
+  am::Dims d;
+  int device;
+  void* arena;
+  size_t arena_bytes;
+  // state, ping-pong
+  float* W[2];
+  float* S[2];
+  int cur;
+  // window history (raw keys fp32, values fp32, gamma), ping-pong
+  float* hk[2];
+  float* hv[2];
+  float* hg[2];
+  int hcur;
+  // per-chunk workspace (MLP path)
+  float* Z;      // [M][Rt][dh]
+  float* D2;     // [M][Rk][dv]
+  float* D1;     // [M][Rk][dh]
+  // gate coefficients for a batch of up to ncb chunks
+  int ncb;
+  float* cW;     // [M][ncb*C]
+  float* cS;     // [M][ncb*C]
+  float* oW;     // [M][ncb][Rk]  (window > 1)
+  float* oS;
+  float* scal;   // [M][ncb][3]
+  // per-chunk gradient (PER_CHUNK path)
+  float* G;      // [M][P]
+  // retrieval workspace
+  int rb;        // rows per retrieval block
+  float* Zr;     // [M][rb][dh]
+  int* flag;     // non-finite flag (device)
+};
+
+namespace am {
+
+using Handle = ::atlasmem_handle_s;
+
+
+// Launchers (enqueue only; return ATLASMEM_OK or ATLASMEM_E_DEVICE on a launch error).
+atlasmem_status launch_gate_scan(const float* theta, const float* eta, const float* alpha, int M, int64_t ld_gate,
+                                 int64_t t0, int nchunks, int C, float* cW, float* cS, int64_t ld_c, float* scal,
+                                 int64_t ld_s, hipStream_t st);
+atlasmem_status launch_omega(const float* cW, const float* cS, int64_t ld_c, const float* gamma, int64_t ld_g,
+                             const float* ghist, int M, int64_t s0, int nchunks, int C, int c, float* oW, float* oS,
+                             int64_t ld_o, hipStream_t st);
+atlasmem_status launch_history_update(const Handle* h, const void* K, const void* V, const float* gamma, int64_t T,
+                                      hipStream_t st);
+atlasmem_status launch_poly(const void* X, int in_bf16, int64_t n, int d, float* F, hipStream_t st);
+atlasmem_status launch_linear_update(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
+                                     const float* eta, const float* alpha, const float* gamma, int64_t T, void* Y,
+                                     hipStream_t st);
+atlasmem_status launch_linear_retrieve(Handle* h, const void* Q, int64_t T, void* Y, hipStream_t st);
+atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
+                           const float* eta, const float* alpha, const float* gamma, int64_t T, void* Y,
+                           hipStream_t st);
+atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, void* Y, hipStream_t st);
+// Newton-Schulz on [n_mat] matrices of rows x cols, followed by an optional momentum/forgetting
+// epilogue.  When `upd` is null the result is written to `out` ([n_mat, rows, cols]).
+struct NsUpdate {
+  const float* Win;
+  const float* Sin;
+  float* Wout;
+  float* Sout;
+  int64_t P;          // parameters per memory
+  int64_t off;        // offset of this matrix inside a memory's parameters
+  int mats_per_mem;   // matrices in the batch belonging to one memory (1)
+  const float* theta; // per-chunk gates [M][ld_gate] at column k
+  const float* eta;
+  const float* alpha;
+  int64_t ld_gate;
+  int64_t k;
+  int* flag;
+};
+atlasmem_status launch_ns(const float* G, int64_t ldG_mat, int n_mat, int rows, int cols, int steps, float a, float b,
+                          float c, float eps, bool split, float* out, const NsUpdate* upd, hipStream_t st);
+bool ns_supported(int rows, int cols);
+
+}  // namespace am

@@ -1,0 +1,269 @@
+// Newton-Schulz orthogonalisation of the per-chunk surprise (Atlas-Torch README, Atlas
+// Extensions table, Muon / Newton-Schulz; ATLAS summary, section 5), one workgroup per matrix.
+//
+// X0 = G / (||G||_F + eps) in the orientation with rows <= cols (m x n, m <= 64, n <= 128,
+// zero-padded to 64 x 128), then `steps` times
+//     A = X X^T,   B = b A + c A^2,   X = a X + B X
+// on the matrix cores.  X lives in fp32 registers (each wave owns a 64 x 32 column slab of X in
+// the output layout of the X-update product, so the a X term needs no memory traffic); its
+// bf16 hi/lo split is kept in LDS twice, row-major (operand of X X^T) and transposed (B operand
+// of B X); A and B are kept as hi/lo in LDS (A is symmetric, so its rows serve as columns).
+// The result is written back in G's orientation, or consumed by the momentum / forgetting
+// epilogue S = eta_c S - theta_c X, W = (1 - alpha_c) W + S.
+#include "common.h"
+#include "internal.h"
+
+namespace am {
+
+constexpr int NSM = 64, NSN = 128;
+constexpr int LX = NSN + 8;  // row stride of X (bf16)
+constexpr int LT = NSM + 8;  // row stride of X^T, A, B (bf16)
+
+struct NsArgs {
+  const float* G;
+  int64_t ldG;
+  int rows, cols, steps;
+  float a, b, c, eps;
+  float* out;
+  NsUpdate u;
+  int has_upd;
+};
+
+template <bool SPLIT>
+__global__ void __launch_bounds__(256) ns_kernel(NsArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t Xh[NSM * LX];
+  __shared__ __attribute__((aligned(16))) uint16_t Xl[SPLIT ? NSM * LX : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t XTh[NSN * LT];
+  __shared__ __attribute__((aligned(16))) uint16_t XTl[SPLIT ? NSN * LT : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Ah[NSM * LT];
+  __shared__ __attribute__((aligned(16))) uint16_t Al[SPLIT ? NSM * LT : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Bh[NSM * LT];
+  __shared__ __attribute__((aligned(16))) uint16_t Bl[SPLIT ? NSM * LT : 8];
+  __shared__ float red[4];
+
+  const int mat = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
+  const bool tr = p.rows > p.cols;
+  const int m = tr ? p.cols : p.rows;
+  const int n = tr ? p.rows : p.cols;
+  const float* g = p.G + (int64_t)mat * p.ldG;
+
+  // x[ri][cj][r]: X(i, j) with i = 16 ri + 4 lq + r, j = 32 w + 16 cj + lr
+  float x[4][2][4];
+  float ss = 0.0f;
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+    for (int cj = 0; cj < 2; ++cj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ri + 4 * lq + r, j = 32 * w + 16 * cj + lr;
+        float v = 0.0f;
+        if (i < m && j < n) v = tr ? g[(int64_t)j * p.cols + i] : g[(int64_t)i * p.cols + j];
+        x[ri][cj][r] = v;
+        ss = fmaf(v, v, ss);
+      }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  const float inv = 1.0f / (sqrtf(red[0] + red[1] + red[2] + red[3]) + p.eps);
+
+  auto store_x = [&]() {
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+      for (int cj = 0; cj < 2; ++cj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ri + 4 * lq + r, j = 32 * w + 16 * cj + lr;
+          uint32_t hi, lo;
+          split_bf16(x[ri][cj][r], hi, lo);
+          Xh[i * LX + j] = (uint16_t)hi;
+          XTh[j * LT + i] = (uint16_t)hi;
+          if (SPLIT) {
+            Xl[i * LX + j] = (uint16_t)lo;
+            XTl[j * LT + i] = (uint16_t)lo;
+          }
+        }
+  };
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+    for (int cj = 0; cj < 2; ++cj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[ri][cj][r] *= inv;
+  store_x();
+  __syncthreads();
+
+  for (int step = 0; step < p.steps; ++step) {
+    // A = X X^T: wave w owns rows 16w..16w+15, all 64 columns
+    f32x4 accA[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) accA[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NSN / 32; ++kk) {
+      const int ao = (16 * w + lr) * LX + kk * 32 + lk;
+      const u32x4 ah = *(const u32x4*)&Xh[ao];
+      u32x4 al;
+      if (SPLIT) al = *(const u32x4*)&Xl[ao];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int bo = (16 * cb + lr) * LX + kk * 32 + lk;
+        const u32x4 bh = *(const u32x4*)&Xh[bo];
+        accA[cb] = mfma16(ah, bh, accA[cb]);
+        if (SPLIT) {
+          const u32x4 bl = *(const u32x4*)&Xl[bo];
+          accA[cb] = mfma16(ah, bl, accA[cb]);
+          accA[cb] = mfma16(al, bh, accA[cb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * lq + r, j = 16 * cb + lr;
+        uint32_t hi, lo;
+        split_bf16(accA[cb][r], hi, lo);
+        Ah[i * LT + j] = (uint16_t)hi;
+        if (SPLIT) Al[i * LT + j] = (uint16_t)lo;
+      }
+    __syncthreads();
+    // B = b A + c A^2 (same layout as A)
+    f32x4 accB[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) accB[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NSM / 32; ++kk) {
+      const int ao = (16 * w + lr) * LT + kk * 32 + lk;
+      const u32x4 ah = *(const u32x4*)&Ah[ao];
+      u32x4 al;
+      if (SPLIT) al = *(const u32x4*)&Al[ao];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int bo = (16 * cb + lr) * LT + kk * 32 + lk;  // column j of A = row j (symmetric)
+        const u32x4 bh = *(const u32x4*)&Ah[bo];
+        accB[cb] = mfma16(ah, bh, accB[cb]);
+        if (SPLIT) {
+          const u32x4 bl = *(const u32x4*)&Al[bo];
+          accB[cb] = mfma16(ah, bl, accB[cb]);
+          accB[cb] = mfma16(al, bh, accB[cb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * lq + r, j = 16 * cb + lr;
+        const float bv = p.b * accA[cb][r] + p.c * accB[cb][r];
+        uint32_t hi, lo;
+        split_bf16(bv, hi, lo);
+        Bh[i * LT + j] = (uint16_t)hi;
+        if (SPLIT) Bl[i * LT + j] = (uint16_t)lo;
+      }
+    __syncthreads();
+    // X = a X + B X: wave w owns columns 32w..32w+31, all 64 rows
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+      for (int cj = 0; cj < 2; ++cj) acc[ri][cj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NSM / 32; ++kk) {
+      u32x4 bh[2], bl[2];
+#pragma unroll
+      for (int cj = 0; cj < 2; ++cj) {
+        const int bo = (32 * w + 16 * cj + lr) * LT + kk * 32 + lk;
+        bh[cj] = *(const u32x4*)&XTh[bo];
+        if (SPLIT) bl[cj] = *(const u32x4*)&XTl[bo];
+      }
+#pragma unroll
+      for (int ri = 0; ri < 4; ++ri) {
+        const int ao = (16 * ri + lr) * LT + kk * 32 + lk;
+        const u32x4 ah = *(const u32x4*)&Bh[ao];
+        u32x4 al;
+        if (SPLIT) al = *(const u32x4*)&Bl[ao];
+#pragma unroll
+        for (int cj = 0; cj < 2; ++cj) {
+          acc[ri][cj] = mfma16(ah, bh[cj], acc[ri][cj]);
+          if (SPLIT) {
+            acc[ri][cj] = mfma16(ah, bl[cj], acc[ri][cj]);
+            acc[ri][cj] = mfma16(al, bh[cj], acc[ri][cj]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+      for (int cj = 0; cj < 2; ++cj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[ri][cj][r] = p.a * x[ri][cj][r] + acc[ri][cj][r];
+    __syncthreads();  // every wave is done reading X, X^T, B
+    store_x();
+    __syncthreads();
+  }
+
+  // write back in G's orientation, or apply the momentum / forgetting update
+  bool bad = false;
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+    for (int cj = 0; cj < 2; ++cj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ri + 4 * lq + r, j = 32 * w + 16 * cj + lr;
+        if (i < m && j < n) {
+          const int gr = tr ? j : i, gc = tr ? i : j;
+          const float v = x[ri][cj][r];
+          if (!p.has_upd) {
+            p.out[(int64_t)mat * p.rows * p.cols + (int64_t)gr * p.cols + gc] = v;
+          } else {
+            const NsUpdate& u = p.u;
+            const int mem = mat / u.mats_per_mem;
+            const int64_t e = (int64_t)mem * u.P + u.off + (int64_t)gr * p.cols + gc;
+            const int64_t gi = (int64_t)mem * u.ld_gate + u.k;
+            const float s = u.eta[gi] * u.Sin[e] - u.theta[gi] * v;
+            const float wv = (1.0f - u.alpha[gi]) * u.Win[e] + s;
+            u.Sout[e] = s;
+            u.Wout[e] = wv;
+            bad |= !(isfinite(s) && isfinite(wv));
+          }
+        }
+      }
+  if (bad) p.u.flag[0] = 1;
+}
+
+bool ns_supported(int rows, int cols) {
+  const int m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
+  return m >= 1 && m <= NSM && n <= NSN;
+}
+
+atlasmem_status launch_ns(const float* G, int64_t ldG_mat, int n_mat, int rows, int cols, int steps, float a, float b,
+                          float c, float eps, bool split, float* out, const NsUpdate* upd, hipStream_t st) {
+  if (!ns_supported(rows, cols)) return ATLASMEM_E_UNSUPPORTED;
+  if (n_mat == 0) return ATLASMEM_OK;
+  NsArgs p;
+  p.G = G;
+  p.ldG = ldG_mat;
+  p.rows = rows;
+  p.cols = cols;
+  p.steps = steps;
+  p.a = a;
+  p.b = b;
+  p.c = c;
+  p.eps = eps;
+  p.out = out;
+  p.has_upd = upd != nullptr;
+  if (upd) p.u = *upd;
+  else p.u = NsUpdate{};
+  if (split) hipLaunchKernelGGL(ns_kernel<true>, dim3(n_mat), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL(ns_kernel<false>, dim3(n_mat), dim3(256), 0, st, p);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
+}  // namespace am

@@ -1,0 +1,204 @@
+// Gate scan, Omega-window coefficients, window history and the stand-alone feature map.
+//
+// Gate scan.  Inside a chunk every gradient g_j is taken at the chunk-start weights, so the
+// per-token momentum / forgetting recurrence (titans-pytorch-mlx README, Core Equations,
+// Eq. 13-14) unrolls to S_end = P S0 - sum_j cS_j g_j, W_end = beta W0 + a_S S0 - sum_j cW_j g_j.
+// The pair (b_j, w_j) of forgetting product and W-weight obeys
+//   [b_j; w_j] = M_{j+1} [b_{j+1}; w_{j+1}],  M_l = [[1 - alpha_l, 0], [1 - alpha_l, eta_l]],
+// with b_C = w_C = 1, so [b_j; w_j] = L_j [1; 1] where L_j = M_{j+1} ... M_C is a suffix product
+// of 2x2 lower-triangular matrices; e_j = prod_{l>j} eta_l is L_j's lower-right entry.  One wave64
+// computes the suffix products of 64 tokens in six shuffle steps (division free), carrying the
+// product of later 64-token blocks for chunks longer than a wave.
+#include "common.h"
+#include "internal.h"
+
+namespace am {
+
+struct Lt {  // [[a, 0], [c, d]]
+  float a, c, d;
+};
+__device__ __forceinline__ Lt lt_mul(Lt x, Lt y) { return Lt{x.a * y.a, x.c * y.a + x.d * y.c, x.d * y.d}; }
+__device__ __forceinline__ Lt lt_shfl_down(Lt x, int off) {
+  return Lt{__shfl_down(x.a, off, 64), __shfl_down(x.c, off, 64), __shfl_down(x.d, off, 64)};
+}
+
+__global__ void __launch_bounds__(256) gate_scan_kernel(const float* __restrict__ theta, const float* __restrict__ eta,
+                                                        const float* __restrict__ alpha, int M, int64_t ld_gate,
+                                                        int64_t t0, int nchunks, int C, float* __restrict__ cW,
+                                                        float* __restrict__ cS, int64_t ld_c,
+                                                        float* __restrict__ scal, int64_t ld_s) {
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (wave >= (int64_t)M * nchunks) return;  // uniform per wave
+  const int m = (int)(wave / nchunks), kc = (int)(wave % nchunks);
+  const int64_t g0 = (int64_t)m * ld_gate + t0 + (int64_t)kc * C;
+  const int64_t o0 = (int64_t)m * ld_c + (int64_t)kc * C;
+  Lt carry{1.0f, 0.0f, 1.0f};
+  for (int b0 = ((C - 1) / 64) * 64; b0 >= 0; b0 -= 64) {
+    const int j = b0 + lane;
+    const bool valid = j < C;
+    const float et = valid ? eta[g0 + j] : 1.0f;
+    const float al = valid ? alpha[g0 + j] : 0.0f;
+    const float th = valid ? theta[g0 + j] : 0.0f;
+    Lt U = valid ? Lt{1.0f - al, 1.0f - al, et} : Lt{1.0f, 0.0f, 1.0f};
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {  // inclusive suffix product inside the block
+      Lt o = lt_shfl_down(U, off);
+      if (lane + off < 64) U = lt_mul(U, o);
+    }
+    U = lt_mul(U, carry);  // ... times every later block: U_j = M_j ... M_C
+    Lt L = lt_shfl_down(U, 1);
+    if (lane == 63) L = carry;  // L_j = U_{j+1}
+    if (valid) {
+      cS[o0 + j] = th * L.d;
+      cW[o0 + j] = th * (L.c + L.d);
+    }
+    if (b0 == 0 && lane == 0) {
+      float* sc = scal + (int64_t)m * ld_s + (int64_t)kc * 3;
+      sc[0] = U.d;                  // prod eta
+      sc[1] = U.a;                  // prod (1 - alpha)
+      sc[2] = et * (L.c + L.d);     // a_S = eta_1 w_1
+    }
+    carry = Lt{__shfl(U.a, 0, 64), __shfl(U.c, 0, 64), __shfl(U.d, 0, 64)};
+  }
+}
+
+atlasmem_status launch_gate_scan(const float* theta, const float* eta, const float* alpha, int M, int64_t ld_gate,
+                                 int64_t t0, int nchunks, int C, float* cW, float* cS, int64_t ld_c, float* scal,
+                                 int64_t ld_s, hipStream_t st) {
+  const int64_t waves = (int64_t)M * nchunks;
+  if (waves == 0) return ATLASMEM_OK;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL(gate_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, st, theta, eta, alpha, M, ld_gate, t0,
+                     nchunks, C, cW, cS, ld_c, scal, ld_s);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
+// Omega window (ATLAS summary, section 3.2): the step-t gradient sums gamma_i g_i over the last c
+// tokens, so g_i's coefficient in the chunk is gamma_i times the sum of the per-step coefficients
+// c_t over the steps t in [i, i + c - 1] that fall inside the chunk.  Row r of chunk [s, s + C)
+// is token i = s - (c - 1) + r; tokens before the call come from the window history.
+__global__ void __launch_bounds__(256) omega_kernel(const float* __restrict__ cW, const float* __restrict__ cS,
+                                                    int64_t ld_c, const float* __restrict__ gamma, int64_t ld_g,
+                                                    const float* __restrict__ ghist, int M, int64_t s0, int nchunks,
+                                                    int C, int c, float* __restrict__ oW, float* __restrict__ oS,
+                                                    int64_t ld_o) {
+  const int Rk = C + c - 1;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)M * nchunks * Rk;
+  if (idx >= total) return;
+  const int r = (int)(idx % Rk);
+  const int kc = (int)((idx / Rk) % nchunks);
+  const int m = (int)(idx / ((int64_t)Rk * nchunks));
+  const int64_t s = s0 + (int64_t)kc * C;
+  const int64_t i = s - (c - 1) + r;
+  float g = 0.0f;
+  if (i >= 0) g = gamma[(int64_t)m * ld_g + i];
+  else if (ghist) g = ghist[(int64_t)m * (c - 1) + (c - 1) + i];
+  const int64_t t_lo = i > s ? i : s;
+  const int64_t t_hi = (i + c - 1) < (s + C - 1) ? (i + c - 1) : (s + C - 1);
+  float sw = 0.0f, ss = 0.0f;
+  for (int64_t t = t_lo; t <= t_hi; ++t) {
+    sw += cW[(int64_t)m * ld_c + (t - s0)];
+    ss += cS[(int64_t)m * ld_c + (t - s0)];
+  }
+  const int64_t o = (int64_t)m * ld_o + (int64_t)kc * Rk + r;
+  oW[o] = g * sw;
+  oS[o] = g * ss;
+}
+
+atlasmem_status launch_omega(const float* cW, const float* cS, int64_t ld_c, const float* gamma, int64_t ld_g,
+                             const float* ghist, int M, int64_t s0, int nchunks, int C, int c, float* oW, float* oS,
+                             int64_t ld_o, hipStream_t st) {
+  const int64_t total = (int64_t)M * nchunks * (C + c - 1);
+  if (total == 0) return ATLASMEM_OK;
+  hipLaunchKernelGGL(omega_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, cW, cS, ld_c, gamma, ld_g,
+                     ghist, M, s0, nchunks, C, c, oW, oS, ld_o);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
+// Window history: after a call of T tokens, keep the last c - 1 (key, value, gamma) rows of
+// (old history ++ this call), oldest first.  Rows that do not exist (fewer than c - 1 tokens
+// seen since the sequence start) keep gamma = 0 and zero vectors.
+__global__ void history_kernel(const void* __restrict__ K, const void* __restrict__ V,
+                               const float* __restrict__ gamma, int in_bf16, int M, int64_t T, int c, int dk, int dv,
+                               const float* __restrict__ hk, const float* __restrict__ hv,
+                               const float* __restrict__ hg, float* __restrict__ nk, float* __restrict__ nv,
+                               float* __restrict__ ng) {
+  const int H = c - 1;
+  const int width = dk + dv + 1;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * H * width) return;
+  const int e = (int)(idx % width);
+  const int hrow = (int)((idx / width) % H);
+  const int m = (int)(idx / ((int64_t)width * H));
+  const int64_t tau = T - H + hrow;
+  if (e < dk) {
+    float x = (tau >= 0) ? load_in(K, ((int64_t)m * T + tau) * dk + e, in_bf16)
+                         : hk[((int64_t)m * H + hrow + T) * dk + e];
+    nk[((int64_t)m * H + hrow) * dk + e] = x;
+  } else if (e < dk + dv) {
+    const int ev = e - dk;
+    float x = (tau >= 0) ? load_in(V, ((int64_t)m * T + tau) * dv + ev, in_bf16)
+                         : hv[((int64_t)m * H + hrow + T) * dv + ev];
+    nv[((int64_t)m * H + hrow) * dv + ev] = x;
+  } else {
+    float x = (tau >= 0) ? gamma[(int64_t)m * T + tau] : hg[(int64_t)m * H + hrow + T];
+    ng[(int64_t)m * H + hrow] = x;
+  }
+}
+
+atlasmem_status launch_history_update(const Handle* h, const void* K, const void* V, const float* gamma, int64_t T,
+                                      hipStream_t st) {
+  const Dims& d = h->d;
+  if (d.c <= 1 || T == 0) return ATLASMEM_OK;
+  const int64_t total = (int64_t)d.M * (d.c - 1) * (d.dk + d.dv + 1);
+  const int src = h->hcur, dst = 1 - h->hcur;
+  hipLaunchKernelGGL(history_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, K, V, gamma, d.in_bf16,
+                     d.M, T, d.c, d.dk, d.dv, h->hk[src], h->hv[src], h->hg[src], h->hk[dst], h->hv[dst],
+                     h->hg[dst]);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
+// Stand-alone feature map: rows of width d -> C(d+2, 2) fp32 features.  A block stages
+// kRows rows in LDS and writes their features with consecutive threads on consecutive
+// features (coalesced stores; the map is bound by the output bytes).
+constexpr int kPolyRows = 8;
+__global__ void __launch_bounds__(256) poly_kernel(const void* __restrict__ X, int in_bf16, int64_t n, int d,
+                                                   float* __restrict__ F) {
+  extern __shared__ float xs[];  // [kPolyRows][d]
+  const int64_t r0 = (int64_t)blockIdx.x * kPolyRows;
+  const int nr = (int)((n - r0) < kPolyRows ? (n - r0) : kPolyRows);
+  for (int e = threadIdx.x; e < nr * d; e += blockDim.x) xs[e] = load_in(X, r0 * d + e, in_bf16);
+  __syncthreads();
+  const int nf = poly_count(d);
+  for (int rr = 0; rr < nr; ++rr) {
+    const float* x = xs + rr * d;
+    float* out = F + (r0 + rr) * nf;
+    for (int f = threadIdx.x; f < nf; f += blockDim.x) {
+      float v;
+      if (f == 0) v = 1.0f;
+      else if (f <= d) v = x[f - 1];
+      else {
+        int i, j;
+        pair_of(f - 1 - d, d, i, j);
+        v = 0.5f * (x[i] * x[j]);
+      }
+      out[f] = v;
+    }
+  }
+}
+
+atlasmem_status launch_poly(const void* X, int in_bf16, int64_t n, int d, float* F, hipStream_t st) {
+  if (n == 0) return ATLASMEM_OK;
+  const int64_t blocks = (n + kPolyRows - 1) / kPolyRows;
+  hipLaunchKernelGGL(poly_kernel, dim3((unsigned)blocks), dim3(256), kPolyRows * d * sizeof(float), st, X, in_bf16, n,
+                     d, F);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
+}  // namespace am

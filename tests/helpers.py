@@ -1,0 +1,120 @@
+"""Shared helpers of the GPU tests: generator inputs on the device, one library run, error metric."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from test_learned_neural_amd import atlasmem as am
+from test_learned_neural_amd import synth
+
+DEV = "cuda:0"
+BF16_TOL = 2e-2   # max relative error for bf16-input workloads (Y, W, S)
+F32_TOL = 1e-4    # max relative error for fp32 workloads
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def maxrel(x, r) -> float:
+    """max |x - r| / max |r| over a whole tensor (every memory at once)."""
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    den = float(np.max(np.abs(r))) if r.size else 0.0
+    if den == 0.0:
+        return float(np.max(np.abs(x))) if x.size else 0.0
+    return float(np.max(np.abs(x - r)) / den)
+
+
+def config_for(spec, precision=am.PREC_AUTO, output_dtype=am.F32):
+    return am.make_config(kind=spec.kind, batch=spec.batch, heads=spec.heads, d_key=spec.d_key,
+                          d_value=spec.d_value, d_hidden=spec.d_hidden, poly_degree=spec.poly_degree,
+                          chunk=spec.chunk, omega_window=spec.omega_window, gate_mode=spec.gate_mode,
+                          ns_steps=spec.ns_steps, input_dtype=spec.input_dtype, output_dtype=output_dtype,
+                          precision=precision)
+
+
+def to_dev(a: np.ndarray):
+    import torch
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def segment(inp, t0: int, t1: int):
+    """Device tensors of the inputs for tokens [t0, t1) of every memory."""
+    s = inp.spec
+    g0, g1 = (t0, t1) if s.gate_mode == synth.PER_TOKEN else (t0 // s.chunk, t1 // s.chunk)
+    out = dict(K=to_dev(inp.K[:, t0:t1]), Q=to_dev(inp.Q[:, t0:t1]), V=to_dev(inp.V[:, t0:t1]),
+               theta=to_dev(inp.theta[:, g0:g1]), eta=to_dev(inp.eta[:, g0:g1]), alpha=to_dev(inp.alpha[:, g0:g1]),
+               gamma=None if inp.gamma is None else to_dev(inp.gamma[:, t0:t1]))
+    return out
+
+
+def y_to_np(Y):
+    import torch
+    if Y.dtype == torch.int16:
+        u = Y.cpu().numpy().view(np.uint16)
+        return synth.bf16_bits_to_f32(u).astype(np.float64)
+    return Y.cpu().numpy().astype(np.float64)
+
+
+def run_gpu(inp, splits=None, precision=am.PREC_AUTO, output_dtype=am.F32, with_y=True, W0=None, S0=None):
+    """Run the library over the generator inputs, one update call per segment in `splits`
+    (token boundaries, default one call over all of T).  Returns (Y, W, S, status) as float64."""
+    import torch
+    s = inp.spec
+    T = s.T
+    splits = [0, T] if splits is None else splits
+    cfg = config_for(s, precision, output_dtype)
+    W0 = to_dev(inp.W0 if W0 is None else W0)
+    S0 = to_dev(inp.S0 if S0 is None else S0)
+    mem = am.Memory(cfg, W0, S0)
+    if output_dtype == am.BF16:
+        Y = torch.zeros((s.n_mem, T, s.d_value), dtype=torch.int16, device=DEV)
+    else:
+        Y = torch.full((s.n_mem, T, s.d_value), float("nan"), dtype=torch.float32, device=DEV)
+    for a, b in zip(splits[:-1], splits[1:]):
+        seg = segment(inp, a, b)
+        y = torch.empty((s.n_mem, b - a, s.d_value), dtype=Y.dtype, device=DEV) if with_y else None
+        mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], seg["gamma"],
+                           b - a, y)
+        if with_y:
+            Y[:, a:b] = y
+    W = torch.empty((s.n_mem, mem.P), dtype=torch.float32, device=DEV)
+    S = torch.empty_like(W)
+    status = mem.get_state(W, S)
+    torch.cuda.synchronize()
+    mem.close()
+    return y_to_np(Y), W.cpu().numpy().astype(np.float64), S.cpu().numpy().astype(np.float64), status
+
+
+def split_params(spec, flat):
+    """[..., P] -> list of per-matrix arrays [..., n_i] (W1, W2 or W)."""
+    if spec.kind == synth.LINEAR:
+        return [flat]
+    n1 = spec.d_hidden * spec.d_in
+    return [flat[..., :n1], flat[..., n1:]]
+
+
+def compare(name, spec, got, ref, tol, check_state=True):
+    """Print and return the max relative errors of Y and of every weight / momentum matrix."""
+    Yg, Wg, Sg = got[:3]
+    Yr, Wr, Sr = ref[:3]
+    errs = {"Y": maxrel(Yg, Yr)}
+    if check_state:
+        for i, (a, b) in enumerate(zip(split_params(spec, Wg), split_params(spec, Wr))):
+            errs[f"W{i + 1}"] = maxrel(a, b)
+        for i, (a, b) in enumerate(zip(split_params(spec, Sg), split_params(spec, Sr))):
+            errs[f"S{i + 1}"] = maxrel(a, b)
+    log(f"PARITY {name}: " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()) + f" (tol {tol:g})")
+    return errs
+
+
+def oracle_run(inp, mems=None, T=None, processes=1):
+    with np.errstate(all="ignore"):
+        return oracle.run_inputs(inp, mems=mems, T=T, processes=processes)

@@ -1,0 +1,124 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared symbol, validates
+configurations and arguments before touching a device, and reports a missing GPU."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from test_learned_neural_amd import atlasmem as am
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "atlasmem.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(atlasmem_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = am.load()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(am.EXPORTS)
+
+
+def test_abi_version_and_status_strings():
+    assert am.abi_version() == am.ABI_VERSION == 1
+    for s in range(7):
+        assert am.status_string(s) and am.status_string(s) != "unknown status"
+    assert am.status_string(99) == "unknown status"
+
+
+def cfg4(**kw):
+    base = dict(kind=am.MLP2_SILU, batch=8, heads=16, d_key=64, d_value=64, d_hidden=128, chunk=128,
+                gate_mode=am.PER_CHUNK, ns_steps=5)
+    base.update(kw)
+    return am.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,P", [
+    (dict(), 128 * 64 + 64 * 128),
+    (dict(kind=am.LINEAR, d_key=16, d_value=16, d_hidden=0, gate_mode=am.PER_TOKEN, ns_steps=0, chunk=1), 256),
+    (dict(d_key=32, poly_degree=2, d_hidden=128, gate_mode=am.PER_TOKEN, ns_steps=0, omega_window=4, chunk=64),
+     128 * math.comb(34, 2) + 64 * 128),
+    (dict(d_key=384, d_value=384, d_hidden=768, gate_mode=am.PER_TOKEN, ns_steps=0, chunk=64),
+     768 * 384 + 384 * 768),
+])
+def test_param_count(kw, P):
+    assert am.param_count(cfg4(**kw)) == P
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), am.E_INVALID),
+    (dict(d_key=-1), am.E_INVALID),
+    (dict(kind=7), am.E_INVALID),
+    (dict(poly_degree=3), am.E_INVALID),
+    (dict(gate_mode=2), am.E_INVALID),
+    (dict(ns_steps=-1), am.E_INVALID),
+    (dict(input_dtype=5), am.E_INVALID),
+    (dict(precision=9), am.E_INVALID),
+    (dict(d_key=2048), am.E_SHAPE),
+    (dict(chunk=4096), am.E_SHAPE),
+    (dict(omega_window=4), am.E_UNSUPPORTED),                             # window needs per-token gates
+    (dict(gate_mode=am.PER_TOKEN), am.E_UNSUPPORTED),                     # NS needs per-chunk gates
+    (dict(d_hidden=256), am.E_UNSUPPORTED),                               # NS matrix beyond 64 x 128
+    (dict(kind=am.LINEAR, d_key=128, ns_steps=0), am.E_UNSUPPORTED),      # linear kernel: widths <= 64
+])
+def test_create_rejects_bad_configs_before_any_device_call(kw, status):
+    lib = am.load()
+    cfg = cfg4(**kw)
+    h = ctypes.c_void_p(1234)
+    st = lib.atlasmem_create(ctypes.byref(cfg), None, None, None, ctypes.byref(h))
+    assert st == status
+    assert h.value is None
+
+
+def test_wrong_abi_version_and_null_config():
+    lib = am.load()
+    cfg = cfg4()
+    cfg.abi_version = 2
+    h = ctypes.c_void_p()
+    assert lib.atlasmem_create(ctypes.byref(cfg), None, None, None, ctypes.byref(h)) == am.E_INVALID
+    assert lib.atlasmem_create(None, None, None, None, ctypes.byref(h)) == am.E_INVALID
+    assert lib.atlasmem_create(ctypes.byref(cfg4()), None, None, None, None) == am.E_INVALID
+    assert lib.atlasmem_param_count(None) == -1
+
+
+def test_null_handle_calls():
+    lib = am.load()
+    assert lib.atlasmem_update_chunked(None, None, None, None, None, None, None, None, 0, None, None) == am.E_INVALID
+    assert lib.atlasmem_retrieve(None, None, 0, None, None) == am.E_INVALID
+    assert lib.atlasmem_get_state(None, None, None, None) == am.E_INVALID
+    assert lib.atlasmem_set_state(None, None, None, None) == am.E_INVALID
+    assert lib.atlasmem_reset_history(None, None) == am.E_INVALID
+    lib.atlasmem_destroy(None)
+
+
+def test_standalone_entry_argument_checks():
+    lib = am.load()
+    assert lib.atlasmem_gate_scan(None, None, None, 1, 10, 4, None, None, None, None) == am.E_SHAPE
+    assert lib.atlasmem_gate_scan(None, None, None, 1, 8, 0, None, None, None, None) == am.E_INVALID
+    assert lib.atlasmem_gate_scan(None, None, None, 0, 8, 4, None, None, None, None) == am.OK   # nothing to do
+    assert lib.atlasmem_gate_scan(None, None, None, 1, 8, 4, None, None, None, None) == am.E_INVALID
+    assert lib.atlasmem_omega_coeffs(None, None, None, None, 1, 8, 4, 65, None, None, None) == am.E_INVALID
+    assert lib.atlasmem_poly_features(None, 0, 4, 0, None, None) == am.E_INVALID
+    assert lib.atlasmem_poly_features(None, 0, 0, 4, None, None) == am.OK
+    assert lib.atlasmem_newton_schulz(None, 1, 65, 129, 5, 1.0, 1.0, 1.0, 1e-7, 0, None, None) == am.E_UNSUPPORTED
+    assert lib.atlasmem_newton_schulz(None, 1, 64, 128, 5, 1.0, 1.0, 1.0, 1e-7, 0, None, None) == am.E_INVALID
+
+
+def test_create_without_a_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = am.load()
+    h = ctypes.c_void_p()
+    assert lib.atlasmem_create(ctypes.byref(cfg4()), None, None, None, ctypes.byref(h)) == am.E_DEVICE
+    assert h.value is None

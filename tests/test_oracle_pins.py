@@ -289,44 +289,58 @@ def test_recurrence_against_autograd_bruteforce(case):
 
 
 def coefficient_form(cfg, params, momenta, K, V, th, et, al, ga):
-    """Derived closed form of one chunk-wise pass (test-only): with all gradients at the chunk start,
-    S_end = P S0 - sum_j cS_j g_j and W_end = beta W0 + a_S S0 - sum_j cW_j g_j, where
-    e_j = prod_{l>j} eta_l, b_j = prod_{l>j} (1-alpha_l), w_j = b_j + eta_{j+1} w_{j+1} (w_C = 1),
-    cS_j = theta_j e_j, cW_j = theta_j w_j, P = prod eta, beta = prod (1-alpha), a_S = eta_1 w_1.
-    With a window, g_i's coefficient is gamma_i times the sum of c_t over t in [i, i+c-1] in the chunk."""
+    """Chunk-wise closed form built on oracle.coefficients (coefficients written out as products):
+    S_end = P S0 - sum_i oS_i g_i, W_end = beta W0 + a_S S0 - sum_i oW_i g_i, every g_i at the
+    chunk-start weights, i over the chunk and the window - 1 tokens before it."""
+    from oracle.coefficients import chunk_coefficients, omega_coefficients
     W = [p.copy() for p in params]
     S = [m.copy() for m in momenta]
     X = phi_triu(K, cfg.poly_degree)
     T, C, c = K.shape[0], cfg.chunk, cfg.omega_window
+    cW_all = np.zeros(T)
+    cS_all = np.zeros(T)
+    scal = []
     for s in range(0, T, C):
-        th_c, et_c, al_c = th[s:s + C], et[s:s + C], al[s:s + C]
-        e = np.ones(C)
-        b = np.ones(C)
-        w = np.ones(C)
-        for j in range(C - 2, -1, -1):
-            e[j] = e[j + 1] * et_c[j + 1]
-            b[j] = b[j + 1] * (1 - al_c[j + 1])
-            w[j] = b[j] + et_c[j + 1] * w[j + 1]
-        cS, cW = th_c * e, th_c * w
-        P, beta, aS = np.prod(et_c), np.prod(1 - al_c), et_c[0] * w[0]
+        cW_all[s:s + C], cS_all[s:s + C], sc = chunk_coefficients(th[s:s + C], et[s:s + C], al[s:s + C])
+        scal.append(sc)
+    oW, oS = omega_coefficients(cW_all, cS_all, ga if c > 1 else np.ones(T), C, c)
+    for k, s in enumerate(range(0, T, C)):
+        P, beta, aS = scal[k]
         GW = [np.zeros_like(x) for x in W]
         GS = [np.zeros_like(x) for x in W]
-        for i in range(max(0, s - c + 1), s + C):
-            ts = range(max(i, s), min(i + c - 1, s + C - 1) + 1)
-            om = ga[i] if c > 1 else 1.0
-            kw = om * sum(cW[t - s] for t in ts)
-            ks = om * sum(cS[t - s] for t in ts)
+        for r in range(C + c - 1):
+            i = s - (c - 1) + r
+            if i < 0:
+                continue
             g = oracle.loss_grad(W, X[i], V[i])
             for m in range(len(W)):
-                GW[m] += kw * g[m]
-                GS[m] += ks * g[m]
+                GW[m] += oW[k, r] * g[m]
+                GS[m] += oS[k, r] * g[m]
         newS = [P * S[m] - GS[m] for m in range(len(W))]
         W = [beta * W[m] + aS * S[m] - GW[m] for m in range(len(W))]
         S = newS
     return W, S
 
 
-@pytest.mark.parametrize("c", [1, 3])
+def test_chunk_coefficients_backward_recursion():
+    """The product form of the coefficients equals the backward recursion e_j = eta_{j+1} e_{j+1},
+    b_j = (1 - alpha_{j+1}) b_{j+1}, w_j = b_j + eta_{j+1} w_{j+1} (w_C = b_C = e_C = 1)."""
+    from oracle.coefficients import chunk_coefficients
+    r = rng(21)
+    C = 9
+    th, et, al = r.uniform(.01, .1, C), r.uniform(.8, .99, C), r.uniform(0, .05, C)
+    cW, cS, (P, beta, aS) = chunk_coefficients(th, et, al)
+    e, b, w = np.ones(C), np.ones(C), np.ones(C)
+    for j in range(C - 2, -1, -1):
+        e[j] = e[j + 1] * et[j + 1]
+        b[j] = b[j + 1] * (1 - al[j + 1])
+        w[j] = b[j] + et[j + 1] * w[j + 1]
+    np.testing.assert_allclose(cS, th * e, rtol=1e-14)
+    np.testing.assert_allclose(cW, th * w, rtol=1e-14)
+    np.testing.assert_allclose([P, beta, aS], [np.prod(et), np.prod(1 - al), et[0] * w[0]], rtol=1e-14)
+
+
+@pytest.mark.parametrize("c", [1, 3, 6])
 @pytest.mark.parametrize("kind", [LINEAR, MLP2_SILU])
 def test_recurrence_matches_derived_coefficient_form(kind, c):
     cfg, params, momenta, K, Q, V, th, et, al, ga = tiny_problem(12, kind, 12, 3, 2, 4, 1, 4, c, PER_TOKEN)
