@@ -1,0 +1,255 @@
+"""Throughput of the neural-memory update + retrieval on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu]
+
+A step is one atlasmem_update_chunked call over the whole sequence of every memory
+(retrieval of every query at its chunk-start weights, the chunk-wise update with the
+per-chunk Newton-Schulz orthogonalisation), starting from the workload's initial state
+(restored with atlasmem_set_state before each step, inside the timed region).
+Inputs are seeded synthetic tensors already resident in device memory.
+
+Prints one JSON line: tokens/s (B*H*T per second), the roofline of the dominant kernel
+(algorithmic FLOPs or bytes per launch over its average duration, timed with HIP events
+on the stream it runs on) and the fp64 oracle's throughput on a bounded sample on the
+host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix peak (TFLOP/s)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (GB/s)
+METRIC = "memory-update+retrieval tokens/s (B·H·T/s) per config; % of bf16 MFMA peak"
+
+
+def mlp_flops_per_chunk(spec) -> dict:
+    """Algorithmic FLOPs of one chunk of one memory (2 per multiply-add), by stage."""
+    C, din, dh, dv = spec.chunk, spec.d_in, spec.d_hidden, spec.d_value
+    R = C + spec.omega_window - 1
+    f = dict(
+        retrieval=2 * C * din * dh + 2 * C * dh * dv,
+        forward=2 * R * din * dh + 2 * R * dh * dv,
+        backward=2 * R * dv * dh,
+        wgrad=(2 if spec.gate_mode == 0 else 1) * (2 * R * dv * dh + 2 * R * dh * din),
+    )
+    if spec.ns_steps:
+        def ns(r, c):
+            m, n = min(r, c), max(r, c)
+            return spec.ns_steps * (2 * m * m * n + 2 * m * m * m + 2 * m * m * n)
+        f["newton_schulz"] = ns(dh, din) + ns(dv, dh)
+    return f
+
+
+def ns_flops_per_matrix(rows, cols, steps):
+    m, n = min(rows, cols), max(rows, cols)
+    return steps * (2 * m * m * n + 2 * m * m * m + 2 * m * m * n)
+
+
+def event_ms(fn, iters, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def cpu_baseline(inp, seconds_target: float, cores: int):
+    """The fp64 oracle, as it stands, on a bounded sample: `n` memories over their first T_s tokens,
+    one memory per process."""
+    import multiprocessing as mp
+
+    import oracle
+    s = inp.spec
+    # probe the cost of one chunk of one memory (over four chunks)
+    probe_chunks = min(4, s.T // s.chunk)
+    t0 = time.perf_counter()
+    with np.errstate(all="ignore"):
+        oracle.run_inputs(inp, mems=[0], T=probe_chunks * s.chunk)
+    one = max((time.perf_counter() - t0) / probe_chunks, 1e-4)
+    chunks_per_mem = s.T // s.chunk
+    n_mem = min(s.n_mem, cores)
+    budget_chunks = max(1, int(seconds_target * cores / one / n_mem))
+    n_chunks = min(chunks_per_mem, budget_chunks)
+    Ts = n_chunks * s.chunk
+    mems = list(range(n_mem))
+    global _CPU_INPUTS
+    _CPU_INPUTS = inp          # inherited by the forked workers, not pickled
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores, initializer=_limit_threads) as pool:
+        pool.map(_oracle_one, [(m, Ts) for m in mems], chunksize=1)
+    wall = time.perf_counter() - t0
+    return dict(value=n_mem * Ts / wall, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{n_mem} memories x first {Ts} tokens ({n_chunks} of {chunks_per_mem} chunks) of "
+                       f"{s.name}, fp64 NumPy, one memory per process, {wall:.1f} s wall")
+
+
+def _limit_threads():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+_CPU_INPUTS = None
+
+
+def _oracle_one(args):
+    import oracle
+    m, Ts = args
+    with np.errstate(all="ignore"):
+        oracle.run_inputs(_CPU_INPUTS, mems=[m], T=Ts)
+    return m
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--variant", default="literal")
+    ap.add_argument("--precision", type=int, default=0, help="0 auto (split bf16), 1 bf16, 2 split bf16")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-check", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the memories shard over (batch, head) with no exchange, "
+              "and this build runs and reports the single-GPU share. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from test_learned_neural_amd import atlasmem as am
+    from test_learned_neural_amd import synth
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    inp = synth.make_inputs(args.workload, args.variant)
+    s = inp.spec
+
+    def t(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    K, Q, V = t(inp.K), t(inp.Q), t(inp.V)
+    th, et, al = t(inp.theta), t(inp.eta), t(inp.alpha)
+    ga = None if inp.gamma is None else t(inp.gamma)
+    W0, S0 = t(inp.W0), t(inp.S0)
+    cfg = am.make_config(kind=s.kind, batch=s.batch, heads=s.heads, d_key=s.d_key, d_value=s.d_value,
+                         d_hidden=s.d_hidden, poly_degree=s.poly_degree, chunk=s.chunk, omega_window=s.omega_window,
+                         gate_mode=s.gate_mode, ns_steps=s.ns_steps, input_dtype=s.input_dtype,
+                         precision=args.precision)
+    mem = am.Memory(cfg, W0, S0)
+    Y = torch.empty((s.n_mem, s.T, s.d_value), dtype=torch.float32, device=dev)
+
+    def step():
+        mem.set_state(W0, S0)
+        mem.reset_history()
+        mem.update_chunked(K, Q, V, th, et, al, ga, s.T, Y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = event_ms(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    tokens = s.n_mem * s.T
+    value = tokens / (ms * 1e-3)
+
+    # algorithmic FLOPs of the whole step and per stage
+    nchunks = s.T // s.chunk
+    per_chunk = mlp_flops_per_chunk(s)
+    step_flops = sum(per_chunk.values()) * nchunks * s.n_mem
+    path_tflops = step_flops / (ms * 1e-3) / 1e12
+
+    # dominant kernel: the Newton-Schulz launch of one chunk (all memories, W1-shaped gradients),
+    # the same kernel and grid the step launches, timed on the same stream
+    roof = None
+    if s.ns_steps:
+        n_mat = s.n_mem
+        G = torch.randn((n_mat, s.d_hidden, s.d_in), device=dev, dtype=torch.float32)
+        out = torch.empty_like(G)
+        prec = am.PREC_BF16 if args.precision == am.PREC_BF16 else am.PREC_BF16X3
+
+        def ns_call():
+            am.newton_schulz(G, n_mat, s.d_hidden, s.d_in, s.ns_steps, synth.NS_COEFFS, synth.NS_EPS, prec, out)
+        for _ in range(3):
+            ns_call()
+        ns_ms = event_ms(ns_call, 50, stream)
+        flops = n_mat * ns_flops_per_matrix(s.d_hidden, s.d_in, s.ns_steps)
+        ach = flops / (ns_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None, kernel="ns_kernel<split>",
+                    launch=f"{n_mat} workgroups, one {s.d_hidden}x{s.d_in} matrix each",
+                    avg_launch_ms=round(ns_ms, 5))
+
+    check = None
+    if not args.no_check:
+        import oracle
+        Wg = torch.empty((s.n_mem, mem.P), dtype=torch.float32, device=dev)
+        Sg = torch.empty_like(Wg)
+        st = mem.get_state(Wg, Sg)
+        m = s.n_mem // 2
+        Yr, Wr, Sr = oracle.run_inputs(inp, mems=[m])
+
+        def rel(x, r):
+            return float(np.abs(x - r).max() / np.abs(r).max())
+        check = dict(memory=m, status=st, Y=rel(Y[m].cpu().numpy(), Yr[0]), W=rel(Wg[m].cpu().numpy(), Wr[0]),
+                     S=rel(Sg[m].cpu().numpy(), Sr[0]))
+
+    cpu = None
+    if not args.no_cpu:
+        cores = min(os.cpu_count() or 1, 16)
+        cpu = cpu_baseline(inp, args.cpu_seconds, cores)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16x3" if args.precision != 1 else "bf16",
+        "data": "synthetic (seeded, generator inputs resident in HBM)",
+        "config": {"workload": s.name, "batch": s.batch, "heads": s.heads, "T": s.T, "chunk": s.chunk,
+                   "d_key": s.d_key, "d_hidden": s.d_hidden, "d_value": s.d_value, "ns_steps": s.ns_steps,
+                   "gate_mode": "per_chunk" if s.gate_mode else "per_token", "variant": args.variant,
+                   "tokens_per_step": tokens, "parallelism": "single GPU; memories spread over workgroups"},
+        "path_tflops": round(path_tflops, 2),
+        "path_frac_bf16_peak": round(path_tflops / PEAK_BF16_TFLOPS, 5),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "check": check,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
