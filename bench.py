@@ -163,18 +163,32 @@ def main():
     mem = am.Memory(cfg, W0, S0)
     Y = torch.empty((s.n_mem, s.T, s.d_value), dtype=torch.float32, device=dev)
 
-    def step():
+    upd_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    upd_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i=None):
         mem.set_state(W0, S0)
         mem.reset_history()
+        if i is not None:
+            upd_start[i].record(stream)
         mem.update_chunked(K, Q, V, th, et, al, ga, s.T, Y)
+        if i is not None:
+            upd_end[i].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = event_ms(step, args.steps, stream)
-    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    end.synchronize()
+    ms = start.elapsed_time(end) / args.steps
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    upd_ms = sum(a.elapsed_time(b) for a, b in zip(upd_start, upd_end)) / args.steps
     tokens = s.n_mem * s.T
     value = tokens / (ms * 1e-3)
 
@@ -184,26 +198,18 @@ def main():
     step_flops = sum(per_chunk.values()) * nchunks * s.n_mem
     path_tflops = step_flops / (ms * 1e-3) / 1e12
 
-    # dominant kernel: the Newton-Schulz launch of one chunk (all memories, W1-shaped gradients),
-    # the same kernel and grid the step launches, timed on the same stream
-    roof = None
-    if s.ns_steps:
-        n_mat = s.n_mem
-        G = torch.randn((n_mat, s.d_hidden, s.d_in), device=dev, dtype=torch.float32)
-        out = torch.empty_like(G)
-        prec = am.PREC_BF16 if args.precision == am.PREC_BF16 else am.PREC_BF16X3
-
-        def ns_call():
-            am.newton_schulz(G, n_mat, s.d_hidden, s.d_in, s.ns_steps, synth.NS_COEFFS, synth.NS_EPS, prec, out)
-        for _ in range(3):
-            ns_call()
-        ns_ms = event_ms(ns_call, 50, stream)
-        flops = n_mat * ns_flops_per_matrix(s.d_hidden, s.d_in, s.ns_steps)
-        ach = flops / (ns_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None, kernel="ns_kernel<split>",
-                    launch=f"{n_mat} workgroups, one {s.d_hidden}x{s.d_in} matrix each",
-                    avg_launch_ms=round(ns_ms, 5))
+    # dominant kernel: the update call.  On the fused path it is one launch of the whole-call
+    # kernel; on the general path it is the whole per-chunk launch sequence.
+    fused = (s.kind == synth.MLP2_SILU and s.gate_mode == synth.PER_CHUNK and s.ns_steps > 0 and s.d_key == 64
+             and s.d_value == 64 and s.d_hidden == 128 and s.chunk % 32 == 0 and args.precision != am.PREC_BF16)
+    ach = step_flops / (upd_ms * 1e-3) / 1e12
+    roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=round(ach / PEAK_BF16_TFLOPS, 5), traffic=None,
+                kernel="am::fz::fused_ns_kernel" if fused else "update_chunked launch sequence",
+                launch=(f"{s.n_mem} workgroups x 256 threads, one memory each, all {nchunks} chunks"
+                        if fused else "per-chunk launches"),
+                avg_launch_ms=round(upd_ms, 5),
+                algorithmic_flops_per_launch=int(step_flops))
 
     check = None
     if not args.no_check:

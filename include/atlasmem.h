@@ -96,7 +96,13 @@ typedef struct {
   int32_t input_dtype;   /* atlasmem_dtype of K, Q, V                                       */
   int32_t output_dtype;  /* atlasmem_dtype of Y                                             */
   int32_t precision;     /* atlasmem_precision                                              */
+  int32_t flags;         /* bit set of ATLASMEM_FLAG_* (0 = defaults)                       */
 } atlasmem_config;
+
+/* Force the general per-chunk kernel sequence even where a fused whole-call kernel exists
+ * (the fused kernel covers the 64 -> 128 -> 64 MLP memory with per-chunk gates and
+ * Newton-Schulz, bf16 inputs, split precision).  Results agree within rounding. */
+#define ATLASMEM_FLAG_NO_FUSED 1
 
 typedef struct atlasmem_handle_s* atlasmem_handle;
 

@@ -19,6 +19,7 @@ LINEAR, MLP2_SILU = 0, 1
 PER_TOKEN, PER_CHUNK = 0, 1
 F32, BF16 = 0, 1
 PREC_AUTO, PREC_BF16, PREC_BF16X3 = 0, 1, 2
+FLAG_NO_FUSED = 1
 ABI_VERSION = 1
 
 EXPORTS = (
@@ -37,6 +38,7 @@ class Config(ctypes.Structure):
         ("omega_window", ctypes.c_int32), ("gate_mode", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
         ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float), ("ns_eps", ctypes.c_float),
         ("input_dtype", ctypes.c_int32), ("output_dtype", ctypes.c_int32), ("precision", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -115,10 +117,10 @@ def _check(status: int, where: str) -> int:
 
 def make_config(kind, batch, heads, d_key, d_value, d_hidden=0, poly_degree=1, chunk=1, omega_window=1,
                 gate_mode=PER_TOKEN, ns_steps=0, ns_coeffs=(3.4445, -4.7750, 2.0315), ns_eps=1e-7,
-                input_dtype=BF16, output_dtype=F32, precision=PREC_AUTO) -> Config:
+                input_dtype=BF16, output_dtype=F32, precision=PREC_AUTO, flags=0) -> Config:
     return Config(ABI_VERSION, kind, batch, heads, d_key, d_value, d_hidden, poly_degree, chunk, omega_window,
                   gate_mode, ns_steps, ns_coeffs[0], ns_coeffs[1], ns_coeffs[2], ns_eps, input_dtype, output_dtype,
-                  precision)
+                  precision, flags)
 
 
 def abi_version() -> int:

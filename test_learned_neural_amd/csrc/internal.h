@@ -22,6 +22,7 @@ struct Dims {
   float ns_a, ns_b, ns_c, ns_eps;
   int in_bf16, out_bf16;
   bool split;   // bf16 hi/lo split products
+  bool no_fused;
 };
 
 }  // namespace am
@@ -104,5 +105,8 @@ struct NsUpdate {
 atlasmem_status launch_ns(const float* G, int64_t ldG_mat, int n_mat, int rows, int cols, int steps, float a, float b,
                           float c, float eps, bool split, float* out, const NsUpdate* upd, hipStream_t st);
 bool ns_supported(int rows, int cols);
+bool fused_supported(const Dims& d);
+atlasmem_status launch_fused(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
+                             const float* eta, const float* alpha, int64_t T, void* Y, hipStream_t st);
 
 }  // namespace am

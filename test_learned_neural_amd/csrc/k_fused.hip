@@ -1,0 +1,487 @@
+// Fused chunk loop for the 64 -> 128 -> 64 SiLU MLP memory with per-chunk gates and
+// Newton-Schulz orthogonalisation: one 256-thread workgroup per memory runs every chunk of
+// the call, with no launch between chunks and no per-chunk round trip of intermediates
+// through global memory.
+//
+// What each chunk computes (titans-pytorch-mlx README, Core Equations, Eq. 12-14; ATLAS
+// summary, section 3.3 (chunk-start weights) and section 5 (Newton-Schulz); Atlas-Torch
+// README, Atlas Extensions and Bug Fixes tables (one summed gradient per chunk, eta and
+// theta outside the orthogonalisation)):
+//   retrieval   Y = W2 silu(W1 q)                         (chunk-start weights)
+//   forward     Z = X W1^T, H = silu(Z), Yh = H W2^T      (keys X of the chunk)
+//   backward    D2 = 2 (Yh - V), D1 = (D2 W2) * silu'(Z)
+//   gradient    G1^T = X^T D1 (64 x 128), G2 = D2^T H (64 x 128)
+//   NS          X0 = G / (||G||_F + eps); steps x {A = X X^T; B = bA + cA^2; X = aX + BX}
+//   update      S = eta_c S - theta_c NS(G), W = (1 - alpha_c) W + S      (per matrix)
+//
+// Layout on the matrix cores (v_mfma_f32_32x32x16_bf16 unless noted; every fp32 operand is
+// split into bf16 hi + lo and multiplied as hi*hi + hi*lo + lo*hi, exact bf16 inputs as
+// x*hi + x*lo):
+//  - A 32 x 32 output tile leaves lane l with rows 8q + 4(l/32) + u (q, u = 0..3) of column
+//    l % 32.  Read as a k-operand, registers 8kl..8kl+7 of a tile hold the 16 consecutive k of
+//    k-step kl in the fixed order {4h..4h+3, 8+4h..8+4h+3} (h = l/32); the partner operand is
+//    read from memory in the same order.  Chained products therefore take tiles straight
+//    from registers: H and D1 feed the gradient products, the updated weights feed the next
+//    chunk's forward products, the Newton-Schulz iterate feeds B X.
+//  - Wave w owns hidden units [32w, 32w + 32): its slice of W1 (the B operand of X W1^T) lives
+//    in its registers; W2 is kept in LDS in both orientations (B operand of H W2^T, contraction
+//    over hidden units, and of D2 W2, contraction over values).
+//  - A chunk is processed in groups of 32 rows; H, D2 (both orientations) and X^T of a group
+//    go through LDS, the gradients accumulate in registers across groups.
+#include "common.h"
+#include "internal.h"
+
+namespace am {
+namespace fz {
+
+constexpr int D = 64;        // key / value width
+constexpr int HD = 128;      // hidden width
+constexpr int LH = HD + 8;   // LDS row stride (bf16) of [*][128] buffers
+constexpr int LD = D + 8;    // LDS row stride of [*][64] buffers
+constexpr int LR = 32 + 8;   // LDS row stride of [*][32 rows] buffers
+constexpr int GR = 32;       // rows per group
+
+// LDS map in uint16 units
+constexpr int W2H = 0, W2L = W2H + 64 * LH;       // W2 [v][h]   (B operand of H W2^T)
+constexpr int WTH = W2L + 64 * LH, WTL = WTH + HD * LD;  // W2^T [h][v] (B operand of D2 W2)
+constexpr int UREG = WTL + HD * LD;
+// group phase
+constexpr int HBH = UREG, HBL = HBH + GR * LH;
+constexpr int D2H = HBL + GR * LH, D2L = D2H + GR * LD;
+constexpr int DTH = D2L + GR * LD, DTL = DTH + 64 * LR;
+constexpr int XTH = DTL + 64 * LR;
+constexpr int GEND = XTH + 64 * LR;
+// Newton-Schulz phase (aliases the group buffers)
+constexpr int XBH = UREG, XBL = XBH + 64 * LH;
+constexpr int ABH = XBL + 64 * LH, ABL = ABH + 64 * LD;
+constexpr int BBH = ABL + 64 * LD, BBL = BBH + 64 * LD;
+constexpr int NEND = BBL + 64 * LD;
+constexpr int LDS_U16 = (GEND > NEND ? GEND : NEND);
+constexpr int LDS_BYTES = LDS_U16 * 2 + 16 * 4;
+
+struct Args {
+  const uint16_t* K;
+  const uint16_t* Q;
+  const uint16_t* V;
+  const float* theta;
+  const float* eta;
+  const float* alpha;
+  int64_t T;
+  int C;
+  int nchunks;
+  const float* Win;
+  const float* Sin;
+  float* Wout;
+  float* Sout;
+  void* Y;
+  int out_bf16;
+  int ns_steps;
+  float ns_a, ns_b, ns_c, ns_eps;
+  int* flag;
+};
+
+// LDS buffer bases as opaque scalars: the bases lie beyond the 64 KB reach of a ds
+// instruction's immediate offset, so folding them into constants would cost one address
+// register per (buffer, constant) pair; kept opaque, only the small in-buffer constants fold.
+__device__ __forceinline__ int opq(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+struct Bases {
+  int w2h, w2l, wth, wtl, hbh, hbl, d2h, d2l, dth, dtl, xth, xbh, xbl, abh, abl, bbh, bbl;
+  __device__ __forceinline__ void init() {
+    w2h = opq(W2H); w2l = opq(W2L); wth = opq(WTH); wtl = opq(WTL);
+    hbh = opq(HBH); hbl = opq(HBL); d2h = opq(D2H); d2l = opq(D2L);
+    dth = opq(DTH); dtl = opq(DTL); xth = opq(XTH);
+    xbh = opq(XBH); xbl = opq(XBL); abh = opq(ABH); abl = opq(ABL); bbh = opq(BBH); bbl = opq(BBL);
+  }
+};
+
+constexpr int64_t P1 = (int64_t)HD * D;        // W1 size
+constexpr int64_t P = P1 + (int64_t)D * HD;    // parameters per memory
+
+__device__ __forceinline__ u32x4 cat2(uint2 a, uint2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
+__device__ __forceinline__ uint2 lds8(const uint16_t* s, int off) { return *(const uint2*)(s + off); }
+__device__ __forceinline__ u32x4 lds16(const uint16_t* s, int off) { return *(const u32x4*)(s + off); }
+
+// 8 consecutive fp32 of a tile (k-step kl) -> hi / lo operand words
+__device__ __forceinline__ void tile_op(const f32x16& t, int kl, u32x4& hi, u32x4& lo) {
+  float v[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) v[s] = t[8 * kl + s];
+  pack8(v, hi, lo);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+__device__ __forceinline__ f32x16 mma3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x16 c) {
+  c = mfma32(ah, bh, c);
+  c = mfma32(ah, bl, c);
+  c = mfma32(al, bh, c);
+  return c;
+}
+__device__ __forceinline__ f32x4 mma3_16(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+  c = mfma16(ah, bh, c);
+  c = mfma16(ah, bl, c);
+  c = mfma16(al, bh, c);
+  return c;
+}
+
+// Write a 32x32 fp32 tile (rows r0.., cols c0..) transposed into an LDS matrix [col][row] as
+// hi/lo: four consecutive rows of a column are one 8-byte store.
+__device__ __forceinline__ void store_tile_T(uint16_t* sm, int offh, int offl, int ld, const f32x16& t, int r0, int c0,
+                                             int lane) {
+  const int hf = lane >> 5, col = c0 + (lane & 31);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) split_bf16(t[4 * q + u], h[u], l[u]);
+    const int o = col * ld + r0 + 8 * q + 4 * hf;
+    *(uint2*)(sm + offh + o) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    *(uint2*)(sm + offl + o) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+  }
+}
+
+// Write a 32x32 fp32 tile into an LDS matrix [row][col] as hi/lo (2-byte stores).
+__device__ __forceinline__ void store_tile(uint16_t* sm, int offh, int offl, int ld, const f32x16& t, int r0, int c0,
+                                           int lane) {
+  const int hf = lane >> 5, col = c0 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    uint32_t h, l;
+    split_bf16(t[r], h, l);
+    const int row = r0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+    sm[offh + row * ld + col] = (uint16_t)h;
+    sm[offl + row * ld + col] = (uint16_t)l;
+  }
+}
+
+// Newton-Schulz on a 64 x 128 matrix held as two 32 x 32 tiles per wave (wave w: columns
+// 32w..32w+31), in place.
+__device__ void newton_schulz(f32x16 (&x)[2], uint16_t* sm, const Bases& B, float* red, const Args& a, int lane,
+                              int w) {
+  const int hf = lane >> 5, l32 = lane & 31;
+  float ss = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ss = fmaf(x[t][r], x[t][r], ss);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  __syncthreads();  // previous readers of red are done
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  const float inv = 1.0f / (sqrtf(red[0] + red[1] + red[2] + red[3]) + a.ns_eps);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[t][r] *= inv;
+
+  const int rt = w >> 1, ct = w & 1;
+  for (int it = 0; it < a.ns_steps; ++it) {
+    store_tile(sm, B.xbh, B.xbl, LH, x[0], 0, 32 * w, lane);
+    store_tile(sm, B.xbh, B.xbl, LH, x[1], 32, 32 * w, lane);
+    __syncthreads();
+    // A = X X^T, tile (rt, ct)
+    f32x16 A = zero16();
+#pragma unroll
+    for (int ks = 0; ks < HD / 16; ++ks) {
+      const int oa = (32 * rt + l32) * LH + 16 * ks + 8 * hf;
+      const int ob = (32 * ct + l32) * LH + 16 * ks + 8 * hf;
+      A = mma3(lds16(sm, B.xbh + oa), lds16(sm, B.xbl + oa), lds16(sm, B.xbh + ob), lds16(sm, B.xbl + ob), A);
+    }
+    store_tile_T(sm, B.abh, B.abl, LD, A, 32 * rt, 32 * ct, lane);
+    __syncthreads();
+    // A^2, tile (rt, ct); B = b A + c A^2
+    f32x16 A2 = zero16();
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int oa = (32 * rt + l32) * LD + 16 * ks + 8 * hf;
+      const int ob = (32 * ct + l32) * LD + 16 * ks + 8 * hf;
+      A2 = mma3(lds16(sm, B.abh + oa), lds16(sm, B.abl + oa), lds16(sm, B.abh + ob), lds16(sm, B.abl + ob), A2);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) A2[r] = a.ns_b * A[r] + a.ns_c * A2[r];
+    store_tile_T(sm, B.bbh, B.bbl, LD, A2, 32 * rt, 32 * ct, lane);
+    __syncthreads();
+    // X = a X + B X: rows 0..63, columns 32w..32w+31; B X's k-operand X comes from registers
+    f32x16 acc[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 bh, bl;
+      tile_op(x[ks >> 1], ks & 1, bh, bl);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int o0 = (32 * t + l32) * LD + 16 * ks + 4 * hf;
+        const u32x4 ah = cat2(lds8(sm, B.bbh + o0), lds8(sm, B.bbh + o0 + 8));
+        const u32x4 al = cat2(lds8(sm, B.bbl + o0), lds8(sm, B.bbl + o0 + 8));
+        acc[t] = mma3(ah, al, bh, bl, acc[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[t][r] = a.ns_a * x[t][r] + acc[t][r];
+    __syncthreads();  // B and X buffers free for the next iteration
+  }
+}
+
+__global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
+  float* red = (float*)(sm + LDS_U16);
+  Bases B;
+  B.init();
+  const int m = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int h_own = 32 * w + l32;  // hidden unit this lane owns in register slices
+  const int64_t mT = (int64_t)m * a.T;
+  const float* Win = a.Win + (int64_t)m * P;
+  const float* Sin = a.Sin + (int64_t)m * P;
+  float* Wout = a.Wout + (int64_t)m * P;
+  float* Sout = a.Sout + (int64_t)m * P;
+
+  // register slice of W1[h_own][d] (B operand of X W1^T, k = d), four k-steps of 16, hi and lo
+  u32x4 w1h[4], w1l[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    float v[8];
+    const float4 p0 = *(const float4*)(Win + (int64_t)h_own * D + 16 * ks + 4 * hf);
+    const float4 p1 = *(const float4*)(Win + (int64_t)h_own * D + 16 * ks + 8 + 4 * hf);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+    v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+    pack8(v, w1h[ks], w1l[ks]);
+  }
+  // W2 in LDS as [v][h] (for H W2^T) and [h][v] (for D2 W2)
+  for (int e = t; e < D * HD; e += 256) {
+    const int vv = e / HD, hh = e % HD;
+    uint32_t hi, lo;
+    split_bf16(Win[P1 + e], hi, lo);
+    sm[B.w2h + vv * LH + hh] = (uint16_t)hi;
+    sm[B.w2l + vv * LH + hh] = (uint16_t)lo;
+    sm[B.wth + hh * LD + vv] = (uint16_t)hi;
+    sm[B.wtl + hh * LD + vv] = (uint16_t)lo;
+  }
+  __syncthreads();
+
+  bool bad = false;
+  for (int k = 0; k < a.nchunks; ++k) {
+    const int64_t s0 = (int64_t)k * a.C;
+    f32x16 g1[2] = {zero16(), zero16()};  // G1^T tiles (d rows 0..31 / 32..63, h_own)
+    f32x16 g2[2] = {zero16(), zero16()};  // G2 tiles (v rows 0..31 / 32..63, h_own)
+    const int ngroups = a.C / GR;
+    for (int gi = 0; gi < 2 * ngroups; ++gi) {
+      const bool query = gi < ngroups;
+      if (query && !a.Y) continue;
+      const int g = query ? gi : gi - ngroups;
+      const int64_t row0 = mT + s0 + (int64_t)g * GR;  // token row of the group's first row
+      const uint16_t* Xg = (query ? a.Q : a.K) + row0 * D;
+      if (!query) {  // X^T of the group for the G1 product
+        const int r = t >> 3, d0 = (t & 7) * 8;
+        const u32x4 xv = *(const u32x4*)(Xg + (int64_t)r * D + d0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sm[B.xth + (d0 + 2 * i) * LR + r] = (uint16_t)(xv[i] & 0xFFFFu);
+          sm[B.xth + (d0 + 2 * i + 1) * LR + r] = (uint16_t)(xv[i] >> 16);
+        }
+      }
+      // Z = X W1^T: rows 0..31 of the group, hidden units of this wave
+      f32x16 z = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint16_t* xr = Xg + (int64_t)l32 * D + 16 * ks + 4 * hf;
+        const u32x4 xa = cat2(*(const uint2*)xr, *(const uint2*)(xr + 8));
+        z = mfma32(xa, w1h[ks], z);
+        z = mfma32(xa, w1l[ks], z);
+      }
+      f32x16 hz, zp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float sg = sigmoidf_(z[r]);
+        hz[r] = z[r] * sg;
+        zp[r] = sg * (1.0f + z[r] * (1.0f - sg));
+      }
+      store_tile(sm, B.hbh, B.hbl, LH, hz, 0, 32 * w, lane);
+      __syncthreads();
+      // Yh = H W2^T: 16x16 tiles, wave w owns values [16w, 16w+16), both row halves
+      f32x4 yh[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < HD / 32; ++ks) {
+          const int oa = (16 * rt + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
+          const int ob = (16 * w + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
+          acc = mma3_16(lds16(sm, B.hbh + oa), lds16(sm, B.hbl + oa), lds16(sm, B.w2h + ob), lds16(sm, B.w2l + ob), acc);
+        }
+        yh[rt] = acc;
+      }
+      const int vcol = 16 * w + (lane & 15);
+      if (query) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int64_t yo = (row0 + 16 * rt + 4 * (lane >> 4) + u) * D + vcol;
+            if (a.out_bf16) ((uint16_t*)a.Y)[yo] = (uint16_t)bf16_bits(yh[rt][u]);
+            else ((float*)a.Y)[yo] = yh[rt][u];
+          }
+        __syncthreads();  // H buffer is rewritten by the next group
+        continue;
+      }
+      // D2 = 2 (Yh - V): to LDS as [row][v] (operand of D2 W2) and [v][row] (operand of D2^T H)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int rb = 16 * rt + 4 * (lane >> 4);
+        uint32_t hh[4], ll[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float vv = bf16_value(a.V[(row0 + rb + u) * D + vcol]);
+          const float d2 = 2.0f * (yh[rt][u] - vv);
+          split_bf16(d2, hh[u], ll[u]);
+          sm[B.d2h + (rb + u) * LD + vcol] = (uint16_t)hh[u];
+          sm[B.d2l + (rb + u) * LD + vcol] = (uint16_t)ll[u];
+        }
+        *(uint2*)(sm + B.dth + vcol * LR + rb) = uint2{hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16)};
+        *(uint2*)(sm + B.dtl + vcol * LR + rb) = uint2{ll[0] | (ll[1] << 16), ll[2] | (ll[3] << 16)};
+      }
+      __syncthreads();
+      // Pm = D2 W2 (k = v), D1 = Pm * silu'(Z)
+      f32x16 p = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int o0 = l32 * LD + 16 * ks + 4 * hf;
+        const u32x4 ah = cat2(lds8(sm, B.d2h + o0), lds8(sm, B.d2h + o0 + 8));
+        const u32x4 al = cat2(lds8(sm, B.d2l + o0), lds8(sm, B.d2l + o0 + 8));
+        const int ob = h_own * LD + 16 * ks + 4 * hf;
+        const u32x4 bh = cat2(lds8(sm, B.wth + ob), lds8(sm, B.wth + ob + 8));
+        const u32x4 bl = cat2(lds8(sm, B.wtl + ob), lds8(sm, B.wtl + ob + 8));
+        p = mma3(ah, al, bh, bl, p);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] *= zp[r];
+      // G1^T += X^T D1 and G2 += D2^T H (k = the group's rows, B operands from registers)
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl) {
+        u32x4 dh, dl, hh, hl;
+        tile_op(p, kl, dh, dl);
+        tile_op(hz, kl, hh, hl);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int o0 = (32 * tt + l32) * LR + 16 * kl + 4 * hf;
+          const u32x4 xa = cat2(lds8(sm, B.xth + o0), lds8(sm, B.xth + o0 + 8));
+          g1[tt] = mfma32(xa, dh, g1[tt]);
+          g1[tt] = mfma32(xa, dl, g1[tt]);
+          const u32x4 ah = cat2(lds8(sm, B.dth + o0), lds8(sm, B.dth + o0 + 8));
+          const u32x4 al = cat2(lds8(sm, B.dtl + o0), lds8(sm, B.dtl + o0 + 8));
+          g2[tt] = mma3(ah, al, hh, hl, g2[tt]);
+        }
+      }
+      __syncthreads();  // group buffers are rewritten by the next group
+    }
+
+    const int64_t gk = (int64_t)m * a.nchunks + k;
+    const float th = a.theta[gk], et = a.eta[gk], om = 1.0f - a.alpha[gk];
+    const float* Wsrc = (k == 0) ? Win : Wout;
+    const float* Ssrc = (k == 0) ? Sin : Sout;
+
+    // W1: G1^T tile element (d, h_own) <-> W1[h_own][d]
+    newton_schulz(g1, sm, B, red, a, lane, w);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t e = (int64_t)h_own * D + 32 * tt + 8 * q + 4 * hf;
+        const float4 so = *(const float4*)(Ssrc + e);
+        const float4 wo = *(const float4*)(Wsrc + e);
+        const float sv[4] = {so.x, so.y, so.z, so.w}, wv[4] = {wo.x, wo.y, wo.z, wo.w};
+        float sn[4], wn[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          sn[u] = et * sv[u] - th * g1[tt][4 * q + u];
+          wn[u] = om * wv[u] + sn[u];
+          g1[tt][4 * q + u] = wn[u];
+          bad |= !(isfinite(sn[u]) && isfinite(wn[u]));
+        }
+        *(float4*)(Sout + e) = float4{sn[0], sn[1], sn[2], sn[3]};
+        *(float4*)(Wout + e) = float4{wn[0], wn[1], wn[2], wn[3]};
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) tile_op(g1[ks >> 1], ks & 1, w1h[ks], w1l[ks]);
+
+    // W2: G2 tile element (v, h_own) <-> W2[v][h_own]
+    newton_schulz(g2, sm, B, red + 4, a, lane, w);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int vv = 32 * tt + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int64_t e = P1 + (int64_t)vv * HD + h_own;
+        const float sn = et * Ssrc[e] - th * g2[tt][r];
+        const float wn = om * Wsrc[e] + sn;
+        Sout[e] = sn;
+        Wout[e] = wn;
+        g2[tt][r] = wn;
+        bad |= !(isfinite(sn) && isfinite(wn));
+      }
+    store_tile(sm, B.w2h, B.w2l, LH, g2[0], 0, 32 * w, lane);
+    store_tile(sm, B.w2h, B.w2l, LH, g2[1], 32, 32 * w, lane);
+    store_tile_T(sm, B.wth, B.wtl, LD, g2[0], 0, 32 * w, lane);
+    store_tile_T(sm, B.wth, B.wtl, LD, g2[1], 32, 32 * w, lane);
+    __syncthreads();
+  }
+  if (bad) a.flag[0] = 1;
+}
+
+}  // namespace fz
+
+bool fused_supported(const Dims& d) {
+  return d.kind == ATLASMEM_MLP2_SILU && d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0 && d.dk == fz::D &&
+         d.din == fz::D && d.dv == fz::D && d.dh == fz::HD && d.c == 1 && d.C % fz::GR == 0 && d.in_bf16 && d.split;
+}
+
+atlasmem_status launch_fused(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
+                             const float* eta, const float* alpha, int64_t T, void* Y, hipStream_t st) {
+  const Dims& d = h->d;
+  fz::Args a;
+  a.K = (const uint16_t*)K;
+  a.Q = (const uint16_t*)Q;
+  a.V = (const uint16_t*)V;
+  a.theta = theta;
+  a.eta = eta;
+  a.alpha = alpha;
+  a.T = T;
+  a.C = d.C;
+  a.nchunks = (int)(T / d.C);
+  a.Win = h->W[h->cur];
+  a.Sin = h->S[h->cur];
+  a.Wout = h->W[1 - h->cur];
+  a.Sout = h->S[1 - h->cur];
+  a.Y = Y;
+  a.out_bf16 = d.out_bf16;
+  a.ns_steps = d.ns_steps;
+  a.ns_a = d.ns_a;
+  a.ns_b = d.ns_b;
+  a.ns_c = d.ns_c;
+  a.ns_eps = d.ns_eps;
+  a.flag = h->flag;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)fz::fused_ns_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            fz::LDS_BYTES) != hipSuccess)
+      return ATLASMEM_E_DEVICE;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(fz::fused_ns_kernel, dim3(d.M), dim3(256), fz::LDS_BYTES, st, a);
+  AM_LAUNCH_CHECK();
+  h->cur = 1 - h->cur;
+  return ATLASMEM_OK;
+}
+
+}  // namespace am

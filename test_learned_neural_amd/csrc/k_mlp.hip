@@ -265,6 +265,7 @@ atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* 
   const int64_t zsz = (int64_t)d.Rt * dh;
   const bool per_token = d.gate_mode == ATLASMEM_PER_TOKEN;
   atlasmem_status stt;
+  if (!d.no_fused && fused_supported(d)) return launch_fused(h, K, Q, V, theta, eta, alpha, T, Y, st);
 
   for (int64_t kb0 = 0; kb0 < nchunks; kb0 += h->ncb) {
     const int nb = (int)((nchunks - kb0) < h->ncb ? (nchunks - kb0) : h->ncb);

@@ -30,12 +30,12 @@ def maxrel(x, r) -> float:
     return float(np.max(np.abs(x - r)) / den)
 
 
-def config_for(spec, precision=am.PREC_AUTO, output_dtype=am.F32):
+def config_for(spec, precision=am.PREC_AUTO, output_dtype=am.F32, flags=0):
     return am.make_config(kind=spec.kind, batch=spec.batch, heads=spec.heads, d_key=spec.d_key,
                           d_value=spec.d_value, d_hidden=spec.d_hidden, poly_degree=spec.poly_degree,
                           chunk=spec.chunk, omega_window=spec.omega_window, gate_mode=spec.gate_mode,
                           ns_steps=spec.ns_steps, input_dtype=spec.input_dtype, output_dtype=output_dtype,
-                          precision=precision)
+                          precision=precision, flags=flags)
 
 
 def to_dev(a: np.ndarray):
@@ -63,14 +63,14 @@ def y_to_np(Y):
     return Y.cpu().numpy().astype(np.float64)
 
 
-def run_gpu(inp, splits=None, precision=am.PREC_AUTO, output_dtype=am.F32, with_y=True, W0=None, S0=None):
+def run_gpu(inp, splits=None, precision=am.PREC_AUTO, output_dtype=am.F32, with_y=True, W0=None, S0=None, flags=0):
     """Run the library over the generator inputs, one update call per segment in `splits`
     (token boundaries, default one call over all of T).  Returns (Y, W, S, status) as float64."""
     import torch
     s = inp.spec
     T = s.T
     splits = [0, T] if splits is None else splits
-    cfg = config_for(s, precision, output_dtype)
+    cfg = config_for(s, precision, output_dtype, flags)
     W0 = to_dev(inp.W0 if W0 is None else W0)
     S0 = to_dev(inp.S0 if S0 is None else S0)
     mem = am.Memory(cfg, W0, S0)

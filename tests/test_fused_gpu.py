@@ -1,0 +1,53 @@
+"""The fused whole-call kernel (64 -> 128 -> 64 MLP memory, per-chunk gates, Newton-Schulz) against
+the fp64 oracle and against the general per-chunk kernel sequence, through the C ABI."""
+
+import numpy as np
+import pytest
+
+from helpers import BF16_TOL, compare, log, maxrel, oracle_run, run_gpu
+from test_learned_neural_amd import atlasmem as am
+from test_learned_neural_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("ov", [dict(batch=2, heads=4, T=512), dict(batch=1, heads=3, T=384, chunk=64),
+                                dict(batch=1, heads=2, T=256, chunk=32), dict(batch=1, heads=2, T=384, chunk=96)],
+                         ids=["C128", "C64", "C32", "C96"])
+def test_fused_matches_oracle_and_general_path(ov):
+    inp = synth.make_inputs(4, "literal", **ov)
+    ref = oracle_run(inp)
+    fused = run_gpu(inp)
+    general = run_gpu(inp, flags=am.FLAG_NO_FUSED)
+    e1 = compare(f"fused_{inp.spec.chunk}", inp.spec, fused, ref, BF16_TOL)
+    e2 = compare(f"general_{inp.spec.chunk}", inp.spec, general, ref, BF16_TOL)
+    assert fused[3] == am.OK and general[3] == am.OK
+    assert all(v <= BF16_TOL for v in e1.values()), e1
+    assert all(v <= BF16_TOL for v in e2.values()), e2
+    d = max(maxrel(a, b) for a, b in zip(fused[:3], general[:3]))
+    log(f"PARITY fused_vs_general_{inp.spec.chunk}: {d:.3e}")
+
+
+def test_fused_streaming_and_no_retrieval():
+    inp = synth.make_inputs(4, "literal", batch=1, heads=2, T=512)
+    one = run_gpu(inp)
+    parts = run_gpu(inp, splits=[0, 128, 384, 512])
+    for a, b in zip(one[:3], parts[:3]):
+        assert np.array_equal(a, b)
+    no_y = run_gpu(inp, with_y=False)
+    assert np.array_equal(no_y[1], one[1]) and np.array_equal(no_y[2], one[2])
+    bf = run_gpu(inp, output_dtype=am.BF16)
+    assert maxrel(bf[0], one[0]) < 8e-3
+
+
+def test_fused_full_size_sampled():
+    """The full workload (B=8, H=16, T=32768, chunk 128) in one call, as the benchmark runs it; the
+    oracle recomputes two sampled memories over the whole sequence."""
+    inp = synth.make_inputs(4, "literal")
+    got = run_gpu(inp)
+    assert got[3] == am.OK
+    mems = [5, 101]
+    ref = oracle_run(inp, mems=mems)
+    sub = (got[0][mems], got[1][mems], got[2][mems])
+    errs = compare("fused_full_size_memories_5_101", inp.spec, sub, ref, BF16_TOL)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
