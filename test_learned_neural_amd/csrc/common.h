@@ -13,34 +13,43 @@ namespace am {
 
 constexpr int kWave = 64;
 
-// Round-to-nearest-even fp32 -> bf16 bit pattern (finite inputs).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair (round to nearest even, one hardware conversion).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
+// Round-to-nearest-even fp32 -> bf16 bit pattern.
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return cvt_pk_bf16(x, 0.0f) & 0xFFFFu; }
 __device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
 
-// Split x into hi = bf16(x) and lo = bf16(x - hi); hi + lo carries ~16 significant bits.
+// Split a pair into hi = bf16(x), lo = bf16(x - hi), both packed; hi + lo carries ~16
+// significant bits of each value.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = cvt_pk_bf16(a, b);
+  lo = cvt_pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
+// Single-value split (bit patterns in the low half).
 __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
-  hi = bf16_bits(x);
-  lo = bf16_bits(x - bf16_value(hi));
+  const uint32_t h = cvt_pk_bf16(x, 0.0f) & 0xFFFFu;
+  hi = h;
+  lo = cvt_pk_bf16(x - __uint_as_float(h << 16), 0.0f) & 0xFFFFu;
 }
 
 // Pack eight fp32 values into bf16x8 hi / lo operand words (little-endian pairs).
 __device__ __forceinline__ void pack8(const float* v, u32x4& hi, u32x4& lo) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    uint32_t h0, l0, h1, l1;
-    split_bf16(v[2 * p], h0, l0);
-    split_bf16(v[2 * p + 1], h1, l1);
-    hi[p] = h0 | (h1 << 16);
-    lo[p] = l0 | (l1 << 16);
+    uint32_t h, l;
+    split2(v[2 * p], v[2 * p + 1], h, l);
+    hi[p] = h;
+    lo[p] = l;
   }
 }
 __device__ __forceinline__ void pack8_hi(const float* v, u32x4& hi) {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) hi[p] = bf16_bits(v[2 * p]) | (bf16_bits(v[2 * p + 1]) << 16);
+  for (int p = 0; p < 4; ++p) hi[p] = cvt_pk_bf16(v[2 * p], v[2 * p + 1]);
 }
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -52,7 +61,8 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// sigma(z) with the hardware exponential and reciprocal (about 1 ulp each)
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 __device__ __forceinline__ float siluf_(float z) { return z * sigmoidf_(z); }
 __device__ __forceinline__ float silu_primef_(float z) {
   float s = sigmoidf_(z);

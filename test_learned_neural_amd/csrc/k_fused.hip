@@ -36,26 +36,32 @@ namespace fz {
 
 constexpr int D = 64;        // key / value width
 constexpr int HD = 128;      // hidden width
-constexpr int LH = HD + 8;   // LDS row stride (bf16) of [*][128] buffers
-constexpr int LD = D + 8;    // LDS row stride of [*][64] buffers
-constexpr int LR = 32 + 8;   // LDS row stride of [*][32 rows] buffers
+// LDS row strides (bf16 units).  Rows read 16 bytes per lane by 16 consecutive lanes want a
+// byte stride of 16 (mod 256) times an odd number, rows read 8 bytes per lane by 32
+// consecutive lanes want 8 (mod 256) times an odd number: either way every lane of a pass
+// lands on its own banks.
+constexpr int LH = HD + 8;   // [*][128], 16-byte row reads (272 B)
+constexpr int LD = D + 8;    // [*][64],  16-byte row reads (144 B)
+constexpr int LE = D + 4;    // [*][64],  8-byte row reads (136 B)
+constexpr int LR = 32 + 4;   // [*][32 rows], 8-byte row reads (72 B)
 constexpr int GR = 32;       // rows per group
 
 // LDS map in uint16 units
 constexpr int W2H = 0, W2L = W2H + 64 * LH;       // W2 [v][h]   (B operand of H W2^T)
-constexpr int WTH = W2L + 64 * LH, WTL = WTH + HD * LD;  // W2^T [h][v] (B operand of D2 W2)
-constexpr int UREG = WTL + HD * LD;
+constexpr int WTH = W2L + 64 * LH, WTL = WTH + HD * LE;  // W2^T [h][v] (B operand of D2 W2)
+constexpr int UREG = WTL + HD * LE;
 // group phase
-constexpr int HBH = UREG, HBL = HBH + GR * LH;
-constexpr int D2H = HBL + GR * LH, D2L = D2H + GR * LD;
-constexpr int DTH = D2L + GR * LD, DTL = DTH + 64 * LR;
+constexpr int HBH = UREG, HBL = HBH + GR * LH;        // H of the group, two buffers
+constexpr int HB2 = HBL + GR * LH;                     // offset of the second H buffer
+constexpr int D2H = HB2 + 2 * GR * LH, D2L = D2H + GR * LE;
+constexpr int DTH = D2L + GR * LE, DTL = DTH + 64 * LR;
 constexpr int XTH = DTL + 64 * LR;
 constexpr int GEND = XTH + 64 * LR;
 // Newton-Schulz phase (aliases the group buffers)
 constexpr int XBH = UREG, XBL = XBH + 64 * LH;
 constexpr int ABH = XBL + 64 * LH, ABL = ABH + 64 * LD;
-constexpr int BBH = ABL + 64 * LD, BBL = BBH + 64 * LD;
-constexpr int NEND = BBL + 64 * LD;
+constexpr int BBH = ABL + 64 * LD, BBL = BBH + 64 * LE;
+constexpr int NEND = BBL + 64 * LE;
 constexpr int LDS_U16 = (GEND > NEND ? GEND : NEND);
 constexpr int LDS_BYTES = LDS_U16 * 2 + 16 * 4;
 
@@ -139,12 +145,12 @@ __device__ __forceinline__ void store_tile_T(uint16_t* sm, int offh, int offl, i
   const int hf = lane >> 5, col = c0 + (lane & 31);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) split_bf16(t[4 * q + u], h[u], l[u]);
+    uint32_t h0, l0, h1, l1;
+    split2(t[4 * q], t[4 * q + 1], h0, l0);
+    split2(t[4 * q + 2], t[4 * q + 3], h1, l1);
     const int o = col * ld + r0 + 8 * q + 4 * hf;
-    *(uint2*)(sm + offh + o) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-    *(uint2*)(sm + offl + o) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    *(uint2*)(sm + offh + o) = uint2{h0, h1};
+    *(uint2*)(sm + offl + o) = uint2{l0, l1};
   }
 }
 
@@ -160,6 +166,29 @@ __device__ __forceinline__ void store_tile(uint16_t* sm, int offh, int offl, int
     sm[offh + row * ld + col] = (uint16_t)h;
     sm[offl + row * ld + col] = (uint16_t)l;
   }
+}
+
+// Store the packed operand words of one k-step (16 rows starting at r0, one column) into a
+// row-major LDS matrix [row][col]: word p holds rows r0 + 8(p/2) + 4h + 2(p%2) and the next.
+__device__ __forceinline__ void store_rows(uint16_t* sm, int offh, int offl, int ld, const u32x4& hi, const u32x4& lo,
+                                           int r0, int col, int hf) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = r0 + 8 * (p >> 1) + 4 * hf + 2 * (p & 1);
+    sm[offh + r * ld + col] = (uint16_t)hi[p];
+    sm[offh + (r + 1) * ld + col] = (uint16_t)(hi[p] >> 16);
+    sm[offl + r * ld + col] = (uint16_t)lo[p];
+    sm[offl + (r + 1) * ld + col] = (uint16_t)(lo[p] >> 16);
+  }
+}
+// The same k-step words into a transposed LDS matrix [col][row] (two 8-byte stores each).
+__device__ __forceinline__ void store_rows_T(uint16_t* sm, int offh, int offl, int ld, const u32x4& hi,
+                                             const u32x4& lo, int r0, int col, int hf) {
+  const int o = col * ld + r0 + 4 * hf;
+  *(uint2*)(sm + offh + o) = uint2{hi[0], hi[1]};
+  *(uint2*)(sm + offh + o + 8) = uint2{hi[2], hi[3]};
+  *(uint2*)(sm + offl + o) = uint2{lo[0], lo[1]};
+  *(uint2*)(sm + offl + o + 8) = uint2{lo[2], lo[3]};
 }
 
 // Newton-Schulz on a 64 x 128 matrix held as two 32 x 32 tiles per wave (wave w: columns
@@ -185,8 +214,13 @@ __device__ void newton_schulz(f32x16 (&x)[2], uint16_t* sm, const Bases& B, floa
 
   const int rt = w >> 1, ct = w & 1;
   for (int it = 0; it < a.ns_steps; ++it) {
-    store_tile(sm, B.xbh, B.xbl, LH, x[0], 0, 32 * w, lane);
-    store_tile(sm, B.xbh, B.xbl, LH, x[1], 32, 32 * w, lane);
+    // hi/lo words of X, k-step ks = rows 16ks..16ks+15 (operand of B X and the LDS copy)
+    u32x4 xh[4], xl[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      tile_op(x[ks >> 1], ks & 1, xh[ks], xl[ks]);
+      store_rows(sm, B.xbh, B.xbl, LH, xh[ks], xl[ks], 16 * ks, 32 * w + l32, hf);
+    }
     __syncthreads();
     // A = X X^T, tile (rt, ct)
     f32x16 A = zero16();
@@ -208,27 +242,26 @@ __device__ void newton_schulz(f32x16 (&x)[2], uint16_t* sm, const Bases& B, floa
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) A2[r] = a.ns_b * A[r] + a.ns_c * A2[r];
-    store_tile_T(sm, B.bbh, B.bbl, LD, A2, 32 * rt, 32 * ct, lane);
+    store_tile_T(sm, B.bbh, B.bbl, LE, A2, 32 * rt, 32 * ct, lane);
     __syncthreads();
     // X = a X + B X: rows 0..63, columns 32w..32w+31; B X's k-operand X comes from registers
     f32x16 acc[2] = {zero16(), zero16()};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 bh, bl;
-      tile_op(x[ks >> 1], ks & 1, bh, bl);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int o0 = (32 * t + l32) * LD + 16 * ks + 4 * hf;
+        const int o0 = (32 * t + l32) * LE + 16 * ks + 4 * hf;
         const u32x4 ah = cat2(lds8(sm, B.bbh + o0), lds8(sm, B.bbh + o0 + 8));
         const u32x4 al = cat2(lds8(sm, B.bbl + o0), lds8(sm, B.bbl + o0 + 8));
-        acc[t] = mma3(ah, al, bh, bl, acc[t]);
+        acc[t] = mma3(ah, al, xh[ks], xl[ks], acc[t]);
       }
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[t][r] = a.ns_a * x[t][r] + acc[t][r];
-    __syncthreads();  // B and X buffers free for the next iteration
+    // No barrier here: the next iteration's X stores only overwrite what its A X^T read before
+    // barrier 2 of this iteration, and its A / B stores come after its own first barrier.
   }
 }
 
@@ -265,40 +298,61 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
     split_bf16(Win[P1 + e], hi, lo);
     sm[B.w2h + vv * LH + hh] = (uint16_t)hi;
     sm[B.w2l + vv * LH + hh] = (uint16_t)lo;
-    sm[B.wth + hh * LD + vv] = (uint16_t)hi;
-    sm[B.wtl + hh * LD + vv] = (uint16_t)lo;
+    sm[B.wth + hh * LE + vv] = (uint16_t)hi;
+    sm[B.wtl + hh * LE + vv] = (uint16_t)lo;
   }
   __syncthreads();
+
+  // The X operand of the next row group's X W1^T is loaded one group ahead (software
+  // pipelining); the group's values and X^T staging words are loaded at the group's start and
+  // used only after its first barrier.
+  const int ngroups = a.C / GR;
+  const int gpc = a.Y ? 2 * ngroups : ngroups;  // groups per chunk: queries first, then keys
+  const int vcol = 16 * w + (lane & 15);
+  auto load_x = [&](int k, int gi, u32x4 (&px)[4]) {
+    if (k >= a.nchunks) return;
+    const bool query = a.Y && gi < ngroups;
+    const int g = query ? gi : (a.Y ? gi - ngroups : gi);
+    const int64_t row0 = mT + (int64_t)k * a.C + (int64_t)g * GR;
+    const uint16_t* xr0 = (query ? a.Q : a.K) + (row0 + l32) * D + 4 * hf;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      px[ks] = cat2(*(const uint2*)(xr0 + 16 * ks), *(const uint2*)(xr0 + 16 * ks + 8));
+  };
+  u32x4 px[4];
+  load_x(0, 0, px);
 
   bool bad = false;
   for (int k = 0; k < a.nchunks; ++k) {
     const int64_t s0 = (int64_t)k * a.C;
     f32x16 g1[2] = {zero16(), zero16()};  // G1^T tiles (d rows 0..31 / 32..63, h_own)
     f32x16 g2[2] = {zero16(), zero16()};  // G2 tiles (v rows 0..31 / 32..63, h_own)
-    const int ngroups = a.C / GR;
-    for (int gi = 0; gi < 2 * ngroups; ++gi) {
-      const bool query = gi < ngroups;
-      if (query && !a.Y) continue;
-      const int g = query ? gi : gi - ngroups;
+    for (int gi = 0; gi < gpc; ++gi) {
+      const bool query = a.Y && gi < ngroups;
+      const int g = query ? gi : (a.Y ? gi - ngroups : gi);
       const int64_t row0 = mT + s0 + (int64_t)g * GR;  // token row of the group's first row
-      const uint16_t* Xg = (query ? a.Q : a.K) + row0 * D;
-      if (!query) {  // X^T of the group for the G1 product
-        const int r = t >> 3, d0 = (t & 7) * 8;
-        const u32x4 xv = *(const u32x4*)(Xg + (int64_t)r * D + d0);
+      // this group's values and X^T words first: the next group's loads are issued after them,
+      // so waiting for these (loads return in order) never waits for the prefetch
+      u32x4 xt;
+      uint32_t vv[8];
+      if (!query) {
+        xt = *(const u32x4*)(a.K + (row0 + (t >> 3)) * D + (t & 7) * 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sm[B.xth + (d0 + 2 * i) * LR + r] = (uint16_t)(xv[i] & 0xFFFFu);
-          sm[B.xth + (d0 + 2 * i + 1) * LR + r] = (uint16_t)(xv[i] >> 16);
-        }
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) vv[4 * rt + u] = a.V[(row0 + 16 * rt + 4 * (lane >> 4) + u) * D + vcol];
       }
+      u32x4 xa[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) xa[ks] = px[ks];
+      if (gi + 1 < gpc) load_x(k, gi + 1, px);
+      else load_x(k + 1, 0, px);
       // Z = X W1^T: rows 0..31 of the group, hidden units of this wave
       f32x16 z = zero16();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint16_t* xr = Xg + (int64_t)l32 * D + 16 * ks + 4 * hf;
-        const u32x4 xa = cat2(*(const uint2*)xr, *(const uint2*)(xr + 8));
-        z = mfma32(xa, w1h[ks], z);
-        z = mfma32(xa, w1l[ks], z);
+        z = mfma32(xa[ks], w1h[ks], z);
+        z = mfma32(xa[ks], w1l[ks], z);
       }
       f32x16 hz, zp;
 #pragma unroll
@@ -307,7 +361,15 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
         hz[r] = z[r] * sg;
         zp[r] = sg * (1.0f + z[r] * (1.0f - sg));
       }
-      store_tile(sm, B.hbh, B.hbl, LH, hz, 0, 32 * w, lane);
+      // H buffers alternate between groups, so a group never waits for the previous group's
+      // readers before writing
+      const int hoff = (gi & 1) ? (HB2 - HBH) : 0;
+      u32x4 hph[2], hpl[2];  // hi/lo words of H, k-steps over the group's rows
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl) {
+        tile_op(hz, kl, hph[kl], hpl[kl]);
+        store_rows(sm, B.hbh + hoff, B.hbl + hoff, LH, hph[kl], hpl[kl], 16 * kl, h_own, hf);
+      }
       __syncthreads();
       // Yh = H W2^T: 16x16 tiles, wave w owns values [16w, 16w+16), both row halves
       f32x4 yh[2];
@@ -318,11 +380,11 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
         for (int ks = 0; ks < HD / 32; ++ks) {
           const int oa = (16 * rt + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
           const int ob = (16 * w + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
-          acc = mma3_16(lds16(sm, B.hbh + oa), lds16(sm, B.hbl + oa), lds16(sm, B.w2h + ob), lds16(sm, B.w2l + ob), acc);
+          acc = mma3_16(lds16(sm, B.hbh + hoff + oa), lds16(sm, B.hbl + hoff + oa), lds16(sm, B.w2h + ob),
+                        lds16(sm, B.w2l + ob), acc);
         }
         yh[rt] = acc;
       }
-      const int vcol = 16 * w + (lane & 15);
       if (query) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -332,34 +394,45 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
             if (a.out_bf16) ((uint16_t*)a.Y)[yo] = (uint16_t)bf16_bits(yh[rt][u]);
             else ((float*)a.Y)[yo] = yh[rt][u];
           }
-        __syncthreads();  // H buffer is rewritten by the next group
         continue;
       }
       // D2 = 2 (Yh - V): to LDS as [row][v] (operand of D2 W2) and [v][row] (operand of D2^T H)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int rb = 16 * rt + 4 * (lane >> 4);
-        uint32_t hh[4], ll[4];
+        float d2[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) d2[u] = 2.0f * (yh[rt][u] - bf16_value(vv[4 * rt + u]));
+        uint32_t h0, l0, h1, l1;
+        split2(d2[0], d2[1], h0, l0);
+        split2(d2[2], d2[3], h1, l1);
+        const uint32_t hh[4] = {h0 & 0xFFFFu, h0 >> 16, h1 & 0xFFFFu, h1 >> 16};
+        const uint32_t ll[4] = {l0 & 0xFFFFu, l0 >> 16, l1 & 0xFFFFu, l1 >> 16};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float vv = bf16_value(a.V[(row0 + rb + u) * D + vcol]);
-          const float d2 = 2.0f * (yh[rt][u] - vv);
-          split_bf16(d2, hh[u], ll[u]);
-          sm[B.d2h + (rb + u) * LD + vcol] = (uint16_t)hh[u];
-          sm[B.d2l + (rb + u) * LD + vcol] = (uint16_t)ll[u];
+          sm[B.d2h + (rb + u) * LE + vcol] = (uint16_t)hh[u];
+          sm[B.d2l + (rb + u) * LE + vcol] = (uint16_t)ll[u];
         }
-        *(uint2*)(sm + B.dth + vcol * LR + rb) = uint2{hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16)};
-        *(uint2*)(sm + B.dtl + vcol * LR + rb) = uint2{ll[0] | (ll[1] << 16), ll[2] | (ll[3] << 16)};
+        *(uint2*)(sm + B.dth + vcol * LR + rb) = uint2{h0, h1};
+        *(uint2*)(sm + B.dtl + vcol * LR + rb) = uint2{l0, l1};
+      }
+      {  // X^T of the group for the G1 product
+        const int r = t >> 3, d0 = (t & 7) * 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sm[B.xth + (d0 + 2 * i) * LR + r] = (uint16_t)(xt[i] & 0xFFFFu);
+          sm[B.xth + (d0 + 2 * i + 1) * LR + r] = (uint16_t)(xt[i] >> 16);
+        }
       }
       __syncthreads();
       // Pm = D2 W2 (k = v), D1 = Pm * silu'(Z)
       f32x16 p = zero16();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int o0 = l32 * LD + 16 * ks + 4 * hf;
+        const int o0 = l32 * LE + 16 * ks + 4 * hf;
         const u32x4 ah = cat2(lds8(sm, B.d2h + o0), lds8(sm, B.d2h + o0 + 8));
         const u32x4 al = cat2(lds8(sm, B.d2l + o0), lds8(sm, B.d2l + o0 + 8));
-        const int ob = h_own * LD + 16 * ks + 4 * hf;
+        const int ob = h_own * LE + 16 * ks + 4 * hf;
         const u32x4 bh = cat2(lds8(sm, B.wth + ob), lds8(sm, B.wth + ob + 8));
         const u32x4 bl = cat2(lds8(sm, B.wtl + ob), lds8(sm, B.wtl + ob + 8));
         p = mma3(ah, al, bh, bl, p);
@@ -369,9 +442,9 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
       // G1^T += X^T D1 and G2 += D2^T H (k = the group's rows, B operands from registers)
 #pragma unroll
       for (int kl = 0; kl < 2; ++kl) {
-        u32x4 dh, dl, hh, hl;
+        u32x4 dh, dl;
         tile_op(p, kl, dh, dl);
-        tile_op(hz, kl, hh, hl);
+        const u32x4 hh = hph[kl], hl = hpl[kl];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int o0 = (32 * tt + l32) * LR + 16 * kl + 4 * hf;
@@ -383,7 +456,8 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
           g2[tt] = mma3(ah, al, hh, hl, g2[tt]);
         }
       }
-      __syncthreads();  // group buffers are rewritten by the next group
+      // No barrier here: the next group rewrites D2, D2^T and X^T only after its first barrier,
+      // which every wave reaches after finishing these reads; H alternates buffers.
     }
 
     const int64_t gk = (int64_t)m * a.nchunks + k;
@@ -391,15 +465,24 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
     const float* Wsrc = (k == 0) ? Win : Wout;
     const float* Ssrc = (k == 0) ? Sin : Sout;
 
-    // W1: G1^T tile element (d, h_own) <-> W1[h_own][d]
+    // W1: G1^T tile element (d, h_own) <-> W1[h_own][d]; state loads issued before NS
+    float4 so1[2][4], wo1[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t e = (int64_t)h_own * D + 32 * tt + 8 * q + 4 * hf;
+        so1[tt][q] = *(const float4*)(Ssrc + e);
+        wo1[tt][q] = *(const float4*)(Wsrc + e);
+      }
     newton_schulz(g1, sm, B, red, a, lane, w);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t e = (int64_t)h_own * D + 32 * tt + 8 * q + 4 * hf;
-        const float4 so = *(const float4*)(Ssrc + e);
-        const float4 wo = *(const float4*)(Wsrc + e);
+        const float4 so = so1[tt][q];
+        const float4 wo = wo1[tt][q];
         const float sv[4] = {so.x, so.y, so.z, so.w}, wv[4] = {wo.x, wo.y, wo.z, wo.w};
         float sn[4], wn[4];
 #pragma unroll
@@ -415,7 +498,17 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) tile_op(g1[ks >> 1], ks & 1, w1h[ks], w1l[ks]);
 
-    // W2: G2 tile element (v, h_own) <-> W2[v][h_own]
+    // W2: G2 tile element (v, h_own) <-> W2[v][h_own]; state loads issued before NS
+    float so2[2][16], wo2[2][16];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int vv = 32 * tt + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int64_t e = P1 + (int64_t)vv * HD + h_own;
+        so2[tt][r] = Ssrc[e];
+        wo2[tt][r] = Wsrc[e];
+      }
     newton_schulz(g2, sm, B, red + 4, a, lane, w);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -423,17 +516,20 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
       for (int r = 0; r < 16; ++r) {
         const int vv = 32 * tt + 8 * (r >> 2) + 4 * hf + (r & 3);
         const int64_t e = P1 + (int64_t)vv * HD + h_own;
-        const float sn = et * Ssrc[e] - th * g2[tt][r];
-        const float wn = om * Wsrc[e] + sn;
+        const float sn = et * so2[tt][r] - th * g2[tt][r];
+        const float wn = om * wo2[tt][r] + sn;
         Sout[e] = sn;
         Wout[e] = wn;
         g2[tt][r] = wn;
         bad |= !(isfinite(sn) && isfinite(wn));
       }
-    store_tile(sm, B.w2h, B.w2l, LH, g2[0], 0, 32 * w, lane);
-    store_tile(sm, B.w2h, B.w2l, LH, g2[1], 32, 32 * w, lane);
-    store_tile_T(sm, B.wth, B.wtl, LD, g2[0], 0, 32 * w, lane);
-    store_tile_T(sm, B.wth, B.wtl, LD, g2[1], 32, 32 * w, lane);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 wh, wl;
+      tile_op(g2[ks >> 1], ks & 1, wh, wl);
+      store_rows(sm, B.w2h, B.w2l, LH, wh, wl, 16 * ks, h_own, hf);
+      store_rows_T(sm, B.wth, B.wtl, LE, wh, wl, 16 * ks, h_own, hf);
+    }
     __syncthreads();
   }
   if (bad) a.flag[0] = 1;
