@@ -57,6 +57,30 @@ def ns_flops_per_matrix(rows, cols, steps):
     return steps * (2 * m * m * n + 2 * m * m * m + 2 * m * m * n)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns5_B8H16_T32768_fused_kernel_traffic.txt")
+FUSED_SOURCES = [os.path.join(ROOT, "test_learned_neural_amd", "csrc", f) for f in ("k_fused.hip", "common.h")]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused kernel from the committed counter summary, or None when
+    the kernel's sources have changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for ln in open(TRAFFIC_FILE):
+            if "=" in ln and not ln.startswith("#"):
+                k, v = ln.split("=", 1)
+                kv[k.strip()] = v.strip()
+        m = hashlib.sha256()
+        for f in FUSED_SOURCES:
+            m.update(open(f, "rb").read())
+        if m.hexdigest()[:16] != kv["kernel_sources_sha256_16"]:
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def event_ms(fn, iters, stream):
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -130,6 +154,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the memories shard over (batch, head) with no exchange, "
@@ -162,6 +188,13 @@ def main():
                          precision=args.precision)
     mem = am.Memory(cfg, W0, S0)
     Y = torch.empty((s.n_mem, s.T, s.d_value), dtype=torch.float32, device=dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     upd_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     upd_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -204,7 +237,8 @@ def main():
              and s.d_value == 64 and s.d_hidden == 128 and s.chunk % 32 == 0 and args.precision != am.PREC_BF16)
     ach = step_flops / (upd_ms * 1e-3) / 1e12
     roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                frac=round(ach / PEAK_BF16_TFLOPS, 5), traffic=None,
+                frac=round(ach / PEAK_BF16_TFLOPS, 5),
+                traffic=(measured_traffic() if fused and s.T == 32768 and s.n_mem == 128 else None),
                 kernel="am::fz::fused_ns_kernel" if fused else "update_chunked launch sequence",
                 launch=(f"{s.n_mem} workgroups x 256 threads, one memory each, all {nchunks} chunks"
                         if fused else "per-chunk launches"),

@@ -57,11 +57,12 @@ constexpr int D2H = HB2 + 2 * GR * LH, D2L = D2H + GR * LE;
 constexpr int DTH = D2L + GR * LE, DTL = DTH + 64 * LR;
 constexpr int XTH = DTL + 64 * LR;
 constexpr int GEND = XTH + 64 * LR;
-// Newton-Schulz phase (aliases the group buffers)
-constexpr int XBH = UREG, XBL = XBH + 64 * LH;
-constexpr int ABH = XBL + 64 * LH, ABL = ABH + 64 * LD;
-constexpr int BBH = ABL + 64 * LD, BBL = BBH + 64 * LE;
-constexpr int NEND = BBL + 64 * LE;
+// Newton-Schulz phase: both gradients at once, over the whole region (the weight copies and
+// group buffers are dead until the update rewrites W2 / W2^T)
+constexpr int NXH = 0, NXS = 2 * 64 * LH;          // X hi of matrix j at NXH + j*NXS, lo at +64*LH
+constexpr int NAH = 2 * NXS, NAS = 2 * 64 * LD;    // A
+constexpr int NBH = NAH + 2 * NAS, NBS = 2 * 64 * LE;  // B
+constexpr int NEND = NBH + 2 * NBS;
 constexpr int LDS_U16 = (GEND > NEND ? GEND : NEND);
 constexpr int LDS_BYTES = LDS_U16 * 2 + 16 * 4;
 
@@ -93,13 +94,25 @@ __device__ __forceinline__ int opq(int x) {
   asm volatile("" : "+s"(x));
   return x;
 }
+// A per-lane value made opaque where it is used, so that the compiler recomputes it there
+// instead of keeping many such addresses alive across the whole kernel.
+__device__ __forceinline__ int opv(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 struct Bases {
-  int w2h, w2l, wth, wtl, hbh, hbl, d2h, d2l, dth, dtl, xth, xbh, xbl, abh, abl, bbh, bbl;
+  int w2h, w2l, wth, wtl, hbh, hbl, d2h, d2l, dth, dtl, xth;
+  int xh[2], xl[2], ah[2], al[2], bh[2], bl[2];  // Newton-Schulz buffers of the two matrices
   __device__ __forceinline__ void init() {
     w2h = opq(W2H); w2l = opq(W2L); wth = opq(WTH); wtl = opq(WTL);
     hbh = opq(HBH); hbl = opq(HBL); d2h = opq(D2H); d2l = opq(D2L);
     dth = opq(DTH); dtl = opq(DTL); xth = opq(XTH);
-    xbh = opq(XBH); xbl = opq(XBL); abh = opq(ABH); abl = opq(ABL); bbh = opq(BBH); bbl = opq(BBL);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      xh[j] = opq(NXH + j * NXS); xl[j] = opq(NXH + j * NXS + 64 * LH);
+      ah[j] = opq(NAH + j * NAS); al[j] = opq(NAH + j * NAS + 64 * LD);
+      bh[j] = opq(NBH + j * NBS); bl[j] = opq(NBH + j * NBS + 64 * LE);
+    }
   }
 };
 
@@ -191,75 +204,107 @@ __device__ __forceinline__ void store_rows_T(uint16_t* sm, int offh, int offl, i
   *(uint2*)(sm + offl + o + 8) = uint2{lo[2], lo[3]};
 }
 
-// Newton-Schulz on a 64 x 128 matrix held as two 32 x 32 tiles per wave (wave w: columns
-// 32w..32w+31), in place.
-__device__ void newton_schulz(f32x16 (&x)[2], uint16_t* sm, const Bases& B, float* red, const Args& a, int lane,
-                              int w) {
+// Newton-Schulz on two 64 x 128 matrices at once (the two weight gradients of a chunk are
+// independent), each held as two 32 x 32 tiles per wave (wave w: columns 32w..32w+31), in
+// place.  Stepping both in lockstep gives every phase two independent chains of matrix-core,
+// LDS and vector work and halves the barriers.
+__device__ void newton_schulz2(f32x16 (&x)[2][2], uint16_t* sm, const Bases& B, float* red, const Args& a, int lane,
+                               int w) {
   const int hf = lane >> 5, l32 = lane & 31;
-  float ss = 0.0f;
+  float ss[2] = {0.0f, 0.0f};
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ss = fmaf(x[t][r], x[t][r], ss);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  __syncthreads();  // previous readers of red are done
-  if (lane == 0) red[w] = ss;
-  __syncthreads();
-  const float inv = 1.0f / (sqrtf(red[0] + red[1] + red[2] + red[3]) + a.ns_eps);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[t][r] *= inv;
-
-  const int rt = w >> 1, ct = w & 1;
-  for (int it = 0; it < a.ns_steps; ++it) {
-    // hi/lo words of X, k-step ks = rows 16ks..16ks+15 (operand of B X and the LDS copy)
-    u32x4 xh[4], xl[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      tile_op(x[ks >> 1], ks & 1, xh[ks], xl[ks]);
-      store_rows(sm, B.xbh, B.xbl, LH, xh[ks], xl[ks], 16 * ks, 32 * w + l32, hf);
-    }
-    __syncthreads();
-    // A = X X^T, tile (rt, ct)
-    f32x16 A = zero16();
-#pragma unroll
-    for (int ks = 0; ks < HD / 16; ++ks) {
-      const int oa = (32 * rt + l32) * LH + 16 * ks + 8 * hf;
-      const int ob = (32 * ct + l32) * LH + 16 * ks + 8 * hf;
-      A = mma3(lds16(sm, B.xbh + oa), lds16(sm, B.xbl + oa), lds16(sm, B.xbh + ob), lds16(sm, B.xbl + ob), A);
-    }
-    store_tile_T(sm, B.abh, B.abl, LD, A, 32 * rt, 32 * ct, lane);
-    __syncthreads();
-    // A^2, tile (rt, ct); B = b A + c A^2
-    f32x16 A2 = zero16();
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const int oa = (32 * rt + l32) * LD + 16 * ks + 8 * hf;
-      const int ob = (32 * ct + l32) * LD + 16 * ks + 8 * hf;
-      A2 = mma3(lds16(sm, B.abh + oa), lds16(sm, B.abl + oa), lds16(sm, B.abh + ob), lds16(sm, B.abl + ob), A2);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) A2[r] = a.ns_b * A[r] + a.ns_c * A2[r];
-    store_tile_T(sm, B.bbh, B.bbl, LE, A2, 32 * rt, 32 * ct, lane);
-    __syncthreads();
-    // X = a X + B X: rows 0..63, columns 32w..32w+31; B X's k-operand X comes from registers
-    f32x16 acc[2] = {zero16(), zero16()};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int o0 = (32 * t + l32) * LE + 16 * ks + 4 * hf;
-        const u32x4 ah = cat2(lds8(sm, B.bbh + o0), lds8(sm, B.bbh + o0 + 8));
-        const u32x4 al = cat2(lds8(sm, B.bbl + o0), lds8(sm, B.bbl + o0 + 8));
-        acc[t] = mma3(ah, al, xh[ks], xl[ks], acc[t]);
-      }
-    }
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[t][r] = a.ns_a * x[t][r] + acc[t][r];
+      for (int r = 0; r < 16; ++r) ss[j] = fmaf(x[j][t][r], x[j][t][r], ss[j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss[j] += __shfl_xor(ss[j], off, 64);
+  __syncthreads();  // previous readers of red (and of the group buffers) are done
+  if (lane == 0) {
+    red[w] = ss[0];
+    red[4 + w] = ss[1];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float inv =
+        1.0f / (sqrtf(red[4 * j] + red[4 * j + 1] + red[4 * j + 2] + red[4 * j + 3]) + a.ns_eps);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[j][t][r] *= inv;
+  }
+
+  const int rt = w >> 1, ct = w & 1;
+  for (int it = 0; it < a.ns_steps; ++it) {
+    const int xcol = opv(32 * w + l32);
+    const int xra = opv((32 * rt + l32) * LH + 8 * hf), xrb = opv((32 * ct + l32) * LH + 8 * hf);
+    // hi/lo words of X, k-step ks = rows 16ks..16ks+15 (operand of B X and the LDS copy)
+    u32x4 xh[2][4], xl[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        tile_op(x[j][ks >> 1], ks & 1, xh[j][ks], xl[j][ks]);
+        store_rows(sm, B.xh[j], B.xl[j], LH, xh[j][ks], xl[j][ks], 16 * ks, xcol, hf);
+      }
+    __syncthreads();
+    // A = X X^T, tile (rt, ct)
+    f32x16 A[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int ks = 0; ks < HD / 16; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int oa = xra + 16 * ks;
+        const int ob = xrb + 16 * ks;
+        A[j] = mma3(lds16(sm, B.xh[j] + oa), lds16(sm, B.xl[j] + oa), lds16(sm, B.xh[j] + ob),
+                    lds16(sm, B.xl[j] + ob), A[j]);
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) store_tile_T(sm, B.ah[j], B.al[j], LD, A[j], 32 * rt, 32 * ct, lane);
+    __syncthreads();
+    // A^2, tile (rt, ct); B = b A + c A^2
+    const int ara = opv((32 * rt + l32) * LD + 8 * hf), arb = opv((32 * ct + l32) * LD + 8 * hf);
+    f32x16 A2[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int oa = ara + 16 * ks;
+        const int ob = arb + 16 * ks;
+        A2[j] = mma3(lds16(sm, B.ah[j] + oa), lds16(sm, B.al[j] + oa), lds16(sm, B.ah[j] + ob),
+                     lds16(sm, B.al[j] + ob), A2[j]);
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) A2[j][r] = a.ns_b * A[j][r] + a.ns_c * A2[j][r];
+      store_tile_T(sm, B.bh[j], B.bl[j], LE, A2[j], 32 * rt, 32 * ct, lane);
+    }
+    __syncthreads();
+    // X = a X + B X: rows 0..63, columns 32w..32w+31; B X's k-operand X comes from registers
+    const int brow = opv(l32 * LE + 4 * hf);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f32x16 acc[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int o0 = brow + 32 * t * LE + 16 * ks;
+          const u32x4 ah = cat2(lds8(sm, B.bh[j] + o0), lds8(sm, B.bh[j] + o0 + 8));
+          const u32x4 al = cat2(lds8(sm, B.bl[j] + o0), lds8(sm, B.bl[j] + o0 + 8));
+          acc[t] = mma3(ah, al, xh[j][ks], xl[j][ks], acc[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[j][t][r] = a.ns_a * x[j][t][r] + acc[t][r];
+    }
     // No barrier here: the next iteration's X stores only overwrite what its A X^T read before
     // barrier 2 of this iteration, and its A / B stores come after its own first barrier.
   }
@@ -325,8 +370,8 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
   bool bad = false;
   for (int k = 0; k < a.nchunks; ++k) {
     const int64_t s0 = (int64_t)k * a.C;
-    f32x16 g1[2] = {zero16(), zero16()};  // G1^T tiles (d rows 0..31 / 32..63, h_own)
-    f32x16 g2[2] = {zero16(), zero16()};  // G2 tiles (v rows 0..31 / 32..63, h_own)
+    // gr[0]: G1^T tiles (d rows 0..31 / 32..63, h_own); gr[1]: G2 tiles (v rows 0..31 / 32..63, h_own)
+    f32x16 gr[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
     for (int gi = 0; gi < gpc; ++gi) {
       const bool query = a.Y && gi < ngroups;
       const int g = query ? gi : (a.Y ? gi - ngroups : gi);
@@ -449,11 +494,11 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
         for (int tt = 0; tt < 2; ++tt) {
           const int o0 = (32 * tt + l32) * LR + 16 * kl + 4 * hf;
           const u32x4 xa = cat2(lds8(sm, B.xth + o0), lds8(sm, B.xth + o0 + 8));
-          g1[tt] = mfma32(xa, dh, g1[tt]);
-          g1[tt] = mfma32(xa, dl, g1[tt]);
+          gr[0][tt] = mfma32(xa, dh, gr[0][tt]);
+          gr[0][tt] = mfma32(xa, dl, gr[0][tt]);
           const u32x4 ah = cat2(lds8(sm, B.dth + o0), lds8(sm, B.dth + o0 + 8));
           const u32x4 al = cat2(lds8(sm, B.dtl + o0), lds8(sm, B.dtl + o0 + 8));
-          g2[tt] = mma3(ah, al, hh, hl, g2[tt]);
+          gr[1][tt] = mma3(ah, al, hh, hl, gr[1][tt]);
         }
       }
       // No barrier here: the next group rewrites D2, D2^T and X^T only after its first barrier,
@@ -465,68 +510,68 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
     const float* Wsrc = (k == 0) ? Win : Wout;
     const float* Ssrc = (k == 0) ? Sin : Sout;
 
-    // W1: G1^T tile element (d, h_own) <-> W1[h_own][d]; state loads issued before NS
+    newton_schulz2(gr, sm, B, red, a, lane, w);
+    // state of both matrices (W1 element (h_own, d), W2 element (v, h_own)), loaded together;
+    // addressed as 32-bit offsets from the memory's uniform base
+    const int o1 = h_own * D + 4 * hf;                // W1 row h_own, d = 4hf + ...
+    const int o2 = (int)P1 + 4 * hf * HD + h_own;     // W2 column h_own, v = 4hf + ...
     float4 so1[2][4], wo1[2][4];
+    float so2[2][16], wo2[2][16];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t e = (int64_t)h_own * D + 32 * tt + 8 * q + 4 * hf;
-        so1[tt][q] = *(const float4*)(Ssrc + e);
-        wo1[tt][q] = *(const float4*)(Wsrc + e);
+        so1[tt][q] = *(const float4*)(Ssrc + o1 + 32 * tt + 8 * q);
+        wo1[tt][q] = *(const float4*)(Wsrc + o1 + 32 * tt + 8 * q);
       }
-    newton_schulz(g1, sm, B, red, a, lane, w);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ov = o2 + (32 * tt + 8 * (r >> 2) + (r & 3)) * HD;
+        so2[tt][r] = Ssrc[ov];
+        wo2[tt][r] = Wsrc[ov];
+      }
+    // W1: G1^T tile element (d, h_own) <-> W1[h_own][d]
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t e = (int64_t)h_own * D + 32 * tt + 8 * q + 4 * hf;
         const float4 so = so1[tt][q];
         const float4 wo = wo1[tt][q];
         const float sv[4] = {so.x, so.y, so.z, so.w}, wv[4] = {wo.x, wo.y, wo.z, wo.w};
         float sn[4], wn[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          sn[u] = et * sv[u] - th * g1[tt][4 * q + u];
+          sn[u] = et * sv[u] - th * gr[0][tt][4 * q + u];
           wn[u] = om * wv[u] + sn[u];
-          g1[tt][4 * q + u] = wn[u];
+          gr[0][tt][4 * q + u] = wn[u];
           bad |= !(isfinite(sn[u]) && isfinite(wn[u]));
         }
-        *(float4*)(Sout + e) = float4{sn[0], sn[1], sn[2], sn[3]};
-        *(float4*)(Wout + e) = float4{wn[0], wn[1], wn[2], wn[3]};
+        *(float4*)(Sout + o1 + 32 * tt + 8 * q) = float4{sn[0], sn[1], sn[2], sn[3]};
+        *(float4*)(Wout + o1 + 32 * tt + 8 * q) = float4{wn[0], wn[1], wn[2], wn[3]};
       }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) tile_op(g1[ks >> 1], ks & 1, w1h[ks], w1l[ks]);
-
-    // W2: G2 tile element (v, h_own) <-> W2[v][h_own]; state loads issued before NS
-    float so2[2][16], wo2[2][16];
+    for (int ks = 0; ks < 4; ++ks) tile_op(gr[0][ks >> 1], ks & 1, w1h[ks], w1l[ks]);
+    // W2: G2 tile element (v, h_own) <-> W2[v][h_own]
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int vv = 32 * tt + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const int64_t e = P1 + (int64_t)vv * HD + h_own;
-        so2[tt][r] = Ssrc[e];
-        wo2[tt][r] = Wsrc[e];
-      }
-    newton_schulz(g2, sm, B, red + 4, a, lane, w);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int vv = 32 * tt + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const int64_t e = P1 + (int64_t)vv * HD + h_own;
-        const float sn = et * so2[tt][r] - th * g2[tt][r];
+        const int ov = o2 + (32 * tt + 8 * (r >> 2) + (r & 3)) * HD;
+        const float sn = et * so2[tt][r] - th * gr[1][tt][r];
         const float wn = om * wo2[tt][r] + sn;
-        Sout[e] = sn;
-        Wout[e] = wn;
-        g2[tt][r] = wn;
+        Sout[ov] = sn;
+        Wout[ov] = wn;
+        gr[1][tt][r] = wn;
         bad |= !(isfinite(sn) && isfinite(wn));
       }
+    // the weight copies overwrite the Newton-Schulz X buffers, which nobody reads after the
+    // last iteration's second barrier
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       u32x4 wh, wl;
-      tile_op(g2[ks >> 1], ks & 1, wh, wl);
+      tile_op(gr[1][ks >> 1], ks & 1, wh, wl);
       store_rows(sm, B.w2h, B.w2l, LH, wh, wl, 16 * ks, h_own, hf);
       store_rows_T(sm, B.wth, B.wtl, LE, wh, wl, 16 * ks, h_own, hf);
     }
