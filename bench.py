@@ -93,6 +93,53 @@ def event_ms(fn, iters, stream):
     return start.elapsed_time(end) / iters
 
 
+def stage_rooflines(torch, am, synth, dev, stream):
+    """Stand-alone stages at the workloads' sizes, each against its own roofline: the gate scan,
+    Omega coefficients and feature map against HBM bandwidth (algorithmic bytes), Newton-Schulz
+    against the bf16 matrix peak (algorithmic FLOPs)."""
+    out = {}
+    M, T, C, c, d = 32, 8192, 64, 4, 32            # the Omega / feature-map workload's sizes
+    th = torch.rand((M, T), device=dev)
+    et = torch.rand((M, T), device=dev)
+    al = torch.rand((M, T), device=dev)
+    ga = torch.rand((M, T), device=dev)
+    cW = torch.empty((M, T), device=dev)
+    cS = torch.empty((M, T), device=dev)
+    sc = torch.empty((M, T // C, 3), device=dev)
+    R = C + c - 1
+    oW = torch.empty((M, T // C, R), device=dev)
+    oS = torch.empty((M, T // C, R), device=dev)
+    X = torch.randn((M * T, d), device=dev).to(torch.bfloat16).view(torch.int16)
+    F = torch.empty((M * T, (d + 1) * (d + 2) // 2), device=dev)
+    G = torch.randn((256, 128, 64), device=dev)
+    Gout = torch.empty_like(G)
+    cases = [
+        ("gate_scan", lambda: am.gate_scan(th, et, al, M, T, C, cW, cS, sc),
+         M * T * (12 + 8) + M * (T // C) * 12, "hbm", f"{M} memories x {T} tokens, chunk {C}"),
+        ("omega_coeffs", lambda: am.omega_coeffs(cW, cS, ga, None, M, T, C, c, oW, oS),
+         M * T * 12 + M * (T // C) * R * 8, "hbm", f"{M} memories x {T} tokens, chunk {C}, window {c}"),
+        ("poly_features", lambda: am.poly_features(X, synth.BF16, M * T, d, F),
+         M * T * (2 * d + 4 * F.shape[1]), "hbm", f"{M * T} bf16 vectors of width {d} -> {F.shape[1]} fp32"),
+        ("newton_schulz", lambda: am.newton_schulz(G, 256, 128, 64, 5, synth.NS_COEFFS, synth.NS_EPS,
+                                                   am.PREC_BF16X3, Gout),
+         256 * ns_flops_per_matrix(128, 64, 5), "mfma", "256 matrices 128x64, 5 steps, split bf16"),
+    ]
+    for name, fn, work, bound, shape in cases:
+        for _ in range(3):
+            fn()
+        t = event_ms(fn, 20, stream)
+        if bound == "hbm":
+            ach = work / (t * 1e-3) / 1e9
+            out[name] = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                             frac=round(ach / PEAK_HBM_GBS, 4), algorithmic_bytes=int(work), ms=round(t, 5), shape=shape)
+        else:
+            ach = work / (t * 1e-3) / 1e12
+            out[name] = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                             frac=round(ach / PEAK_BF16_TFLOPS, 5), algorithmic_flops=int(work), ms=round(t, 5),
+                             shape=shape)
+    return out
+
+
 def cpu_baseline(inp, seconds_target: float, cores: int):
     """The fp64 oracle, as it stands, on a bounded sample: `n` memories over their first T_s tokens,
     one memory per process."""
@@ -154,6 +201,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-stages", action="store_true", help="skip the stand-alone stage rooflines")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -259,6 +307,8 @@ def main():
         check = dict(memory=m, status=st, Y=rel(Y[m].cpu().numpy(), Yr[0]), W=rel(Wg[m].cpu().numpy(), Wr[0]),
                      S=rel(Sg[m].cpu().numpy(), Sr[0]))
 
+    stages = None if args.no_stages else stage_rooflines(torch, am, synth, dev, stream)
+
     cpu = None
     if not args.no_cpu:
         cores = min(os.cpu_count() or 1, 16)
@@ -287,6 +337,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "check": check,
+        "stages": stages,
     }
     print(json.dumps(out))
 
