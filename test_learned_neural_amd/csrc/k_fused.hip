@@ -23,11 +23,17 @@
 //    read from memory in the same order.  Chained products therefore take tiles straight
 //    from registers: H and D1 feed the gradient products, the updated weights feed the next
 //    chunk's forward products, the Newton-Schulz iterate feeds B X.
-//  - Wave w owns hidden units [32w, 32w + 32): its slice of W1 (the B operand of X W1^T) lives
-//    in its registers; W2 is kept in LDS in both orientations (B operand of H W2^T, contraction
-//    over hidden units, and of D2 W2, contraction over values).
-//  - A chunk is processed in groups of 32 rows; H, D2 (both orientations) and X^T of a group
-//    go through LDS, the gradients accumulate in registers across groups.
+//  - 512 threads = two sets of four waves, two waves per SIMD, so that one wave's vector and
+//    LDS work overlaps the other's matrix-core work.  Wave w of either set owns hidden units
+//    [32w, 32w + 32): its slice of W1 (the B operand of X W1^T) lives in its registers; W2 is
+//    kept in LDS in both orientations (B operand of H W2^T, contraction over hidden units, and
+//    of D2 W2, contraction over values).
+//  - A chunk is processed in groups of 64 rows, set s taking rows [32s, 32s + 32); H, D2 (both
+//    orientations) and X^T of a group go through LDS, and each wave accumulates its partial
+//    gradients over its set's rows in registers.  At the end of the chunk the sets swap
+//    partials through LDS, so that set 0 holds all of G1 and set 1 all of G2; each set then
+//    orthogonalises and applies its own matrix, and the new W1 slices pass from set 0 to set 1
+//    through LDS.
 #include "common.h"
 #include "internal.h"
 
@@ -36,35 +42,53 @@ namespace fz {
 
 constexpr int D = 64;        // key / value width
 constexpr int HD = 128;      // hidden width
+constexpr int NT = 512;      // threads per workgroup: two sets of four waves
+constexpr int GR = 32;       // rows per set in a group
+constexpr int GROWS = 64;    // rows per group
 // LDS row strides (bf16 units).  Rows read 16 bytes per lane by 16 consecutive lanes want a
 // byte stride of 16 (mod 256) times an odd number, rows read 8 bytes per lane by 32
 // consecutive lanes want 8 (mod 256) times an odd number: either way every lane of a pass
 // lands on its own banks.
-constexpr int LH = HD + 8;   // [*][128], 16-byte row reads (272 B)
-constexpr int LD = D + 8;    // [*][64],  16-byte row reads (144 B)
-constexpr int LE = D + 4;    // [*][64],  8-byte row reads (136 B)
-constexpr int LR = 32 + 4;   // [*][32 rows], 8-byte row reads (72 B)
-constexpr int GR = 32;       // rows per group
+constexpr int LH = HD + 8;      // [*][128], 16-byte row reads (272 B)
+constexpr int LD = D + 8;       // [*][64],  16-byte row reads (144 B)
+constexpr int LE = D + 4;       // [*][64],  8-byte row reads (136 B)
+constexpr int LR = GROWS + 4;   // [*][64 rows], 8-byte row reads (136 B)
 
-// LDS map in uint16 units
-constexpr int W2H = 0, W2L = W2H + 64 * LH;       // W2 [v][h]   (B operand of H W2^T)
-constexpr int WTH = W2L + 64 * LH, WTL = WTH + HD * LE;  // W2^T [h][v] (B operand of D2 W2)
-constexpr int UREG = WTL + HD * LE;
-// group phase
-constexpr int HBH = UREG, HBL = HBH + GR * LH;        // H of the group, two buffers
-constexpr int HB2 = HBL + GR * LH;                     // offset of the second H buffer
-constexpr int D2H = HB2 + 2 * GR * LH, D2L = D2H + GR * LE;
-constexpr int DTH = D2L + GR * LE, DTL = DTH + 64 * LR;
-constexpr int XTH = DTL + 64 * LR;
-constexpr int GEND = XTH + 64 * LR;
-// Newton-Schulz phase: both gradients at once, over the whole region (the weight copies and
-// group buffers are dead until the update rewrites W2 / W2^T)
-constexpr int NXH = 0, NXS = 2 * 64 * LH;          // X hi of matrix j at NXH + j*NXS, lo at +64*LH
-constexpr int NAH = 2 * NXS, NAS = 2 * 64 * LD;    // A
-constexpr int NBH = NAH + 2 * NAS, NBS = 2 * 64 * LE;  // B
-constexpr int NEND = NBH + 2 * NBS;
+// LDS map in uint16 units.
+// Weights: W2 [v][h] (B operand of H W2^T) and W2^T [h][v] (B operand of D2 W2), hi and lo.
+constexpr int W2H = 0, W2L = W2H + 64 * LH;
+constexpr int WTH = W2L + 64 * LH, WTL = WTH + HD * LE;
+// Group buffers: region A holds D2 [row][v], D2^T [v][row] and X^T [d][row] of a key group, or
+// the H of every second query group; region B holds H [row][h] (hi, then lo).
+constexpr int RA = WTL + HD * LE;
+constexpr int D2H = RA, D2L = D2H + GROWS * LE;
+constexpr int DTH = D2L + GROWS * LE, DTL = DTH + D * LR;
+constexpr int XTH = DTL + D * LR;
+constexpr int RA_END = XTH + D * LR;
+constexpr int HSZ = GROWS * LH;                  // one of H hi / H lo
+constexpr int RB = RA_END;
+constexpr int GEND = RB + 2 * HSZ;
+static_assert(RA_END - RA >= 2 * HSZ, "region A must also hold an H");
+// Newton-Schulz phase, matrix j (set j): X [row][col] hi/lo, A and B [64][64] hi/lo.  The X
+// buffers lie under the weight copies, which the update rewrites after the last read of X.
+constexpr int NX = 0, NXS = 2 * 64 * LH;
+constexpr int NA = 2 * NXS, NAS = 2 * 64 * LD;
+constexpr int NB = NA + 2 * NAS, NBS = 2 * 64 * LE;
+constexpr int NEND = NB + 2 * NBS;
+// Partial-gradient exchange at the end of a chunk (fp32, [wave][tile][quad][lane] float4):
+// G2 partials of set 0 under W2 (read last by the group's H W2^T), G1 partials of set 1 in
+// region B (read last by the same product).
+constexpr int XG2 = 0, XG1 = RB;
+constexpr int XG_U16 = 4 * 2 * 4 * 64 * 4 * 2;
+static_assert(XG_U16 <= 2 * 64 * LH && XG_U16 <= 2 * HSZ, "exchange slots");
+// New W1 operand words from set 0 to set 1 ([wave][k-step word][lane] u32x4), over the
+// Newton-Schulz A buffers, which are dead after the last A^2 product.
+constexpr int HOFF = NA;
+constexpr int HOFF_U16 = 4 * 8 * 64 * 8;
+static_assert(HOFF + HOFF_U16 <= NB, "handoff must not overlap the B buffers");
 constexpr int LDS_U16 = (GEND > NEND ? GEND : NEND);
 constexpr int LDS_BYTES = LDS_U16 * 2 + 16 * 4;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
 struct Args {
   const uint16_t* K;
@@ -100,21 +124,6 @@ __device__ __forceinline__ int opv(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }
-struct Bases {
-  int w2h, w2l, wth, wtl, hbh, hbl, d2h, d2l, dth, dtl, xth;
-  int xh[2], xl[2], ah[2], al[2], bh[2], bl[2];  // Newton-Schulz buffers of the two matrices
-  __device__ __forceinline__ void init() {
-    w2h = opq(W2H); w2l = opq(W2L); wth = opq(WTH); wtl = opq(WTL);
-    hbh = opq(HBH); hbl = opq(HBL); d2h = opq(D2H); d2l = opq(D2L);
-    dth = opq(DTH); dtl = opq(DTL); xth = opq(XTH);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      xh[j] = opq(NXH + j * NXS); xl[j] = opq(NXH + j * NXS + 64 * LH);
-      ah[j] = opq(NAH + j * NAS); al[j] = opq(NAH + j * NAS + 64 * LD);
-      bh[j] = opq(NBH + j * NBS); bl[j] = opq(NBH + j * NBS + 64 * LE);
-    }
-  }
-};
 
 constexpr int64_t P1 = (int64_t)HD * D;        // W1 size
 constexpr int64_t P = P1 + (int64_t)D * HD;    // parameters per memory
@@ -204,126 +213,101 @@ __device__ __forceinline__ void store_rows_T(uint16_t* sm, int offh, int offl, i
   *(uint2*)(sm + offl + o + 8) = uint2{lo[2], lo[3]};
 }
 
-// Newton-Schulz on two 64 x 128 matrices at once (the two weight gradients of a chunk are
-// independent), each held as two 32 x 32 tiles per wave (wave w: columns 32w..32w+31), in
-// place.  Stepping both in lockstep gives every phase two independent chains of matrix-core,
-// LDS and vector work and halves the barriers.
-__device__ void newton_schulz2(f32x16 (&x)[2][2], uint16_t* sm, const Bases& B, float* red, const Args& a, int lane,
-                               int w) {
+// Newton-Schulz on one 64 x 128 matrix held by the four waves of a set as two 32 x 32 tiles
+// per wave (wave w: columns 32w..32w+31), in place.  xh/xl/ah/al/bh/bl: the set's LDS buffers;
+// red: the set's four partial sums of squares.
+__device__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int bxh, int bxl, int bah, int bal, int bbh, int bbl,
+                               float* red, const Args& a, int lane, int w) {
   const int hf = lane >> 5, l32 = lane & 31;
-  float ss[2] = {0.0f, 0.0f};
+  float ss = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int r = 0; r < 16; ++r) ss = fmaf(x[t][r], x[t][r], ss);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ss[j] = fmaf(x[j][t][r], x[j][t][r], ss[j]);
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss[j] += __shfl_xor(ss[j], off, 64);
-  __syncthreads();  // previous readers of red (and of the group buffers) are done
-  if (lane == 0) {
-    red[w] = ss[0];
-    red[4 + w] = ss[1];
-  }
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) red[w] = ss;
   __syncthreads();
+  const float inv = 1.0f / (sqrtf(red[0] + red[1] + red[2] + red[3]) + a.ns_eps);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float inv =
-        1.0f / (sqrtf(red[4 * j] + red[4 * j + 1] + red[4 * j + 2] + red[4 * j + 3]) + a.ns_eps);
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[j][t][r] *= inv;
-  }
+    for (int r = 0; r < 16; ++r) x[t][r] *= inv;
 
   const int rt = w >> 1, ct = w & 1;
   for (int it = 0; it < a.ns_steps; ++it) {
     const int xcol = opv(32 * w + l32);
     const int xra = opv((32 * rt + l32) * LH + 8 * hf), xrb = opv((32 * ct + l32) * LH + 8 * hf);
     // hi/lo words of X, k-step ks = rows 16ks..16ks+15 (operand of B X and the LDS copy)
-    u32x4 xh[2][4], xl[2][4];
+    u32x4 xh[4], xl[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        tile_op(x[j][ks >> 1], ks & 1, xh[j][ks], xl[j][ks]);
-        store_rows(sm, B.xh[j], B.xl[j], LH, xh[j][ks], xl[j][ks], 16 * ks, xcol, hf);
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      tile_op(x[ks >> 1], ks & 1, xh[ks], xl[ks]);
+      store_rows(sm, bxh, bxl, LH, xh[ks], xl[ks], 16 * ks, xcol, hf);
+    }
     __syncthreads();
     // A = X X^T, tile (rt, ct)
-    f32x16 A[2] = {zero16(), zero16()};
+    f32x16 A = zero16();
 #pragma unroll
-    for (int ks = 0; ks < HD / 16; ++ks)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int oa = xra + 16 * ks;
-        const int ob = xrb + 16 * ks;
-        A[j] = mma3(lds16(sm, B.xh[j] + oa), lds16(sm, B.xl[j] + oa), lds16(sm, B.xh[j] + ob),
-                    lds16(sm, B.xl[j] + ob), A[j]);
-      }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) store_tile_T(sm, B.ah[j], B.al[j], LD, A[j], 32 * rt, 32 * ct, lane);
+    for (int ks = 0; ks < HD / 16; ++ks) {
+      const int oa = xra + 16 * ks;
+      const int ob = xrb + 16 * ks;
+      A = mma3(lds16(sm, bxh + oa), lds16(sm, bxl + oa), lds16(sm, bxh + ob), lds16(sm, bxl + ob), A);
+    }
+    store_tile_T(sm, bah, bal, LD, A, 32 * rt, 32 * ct, lane);
     __syncthreads();
     // A^2, tile (rt, ct); B = b A + c A^2
     const int ara = opv((32 * rt + l32) * LD + 8 * hf), arb = opv((32 * ct + l32) * LD + 8 * hf);
-    f32x16 A2[2] = {zero16(), zero16()};
+    f32x16 A2 = zero16();
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int oa = ara + 16 * ks;
-        const int ob = arb + 16 * ks;
-        A2[j] = mma3(lds16(sm, B.ah[j] + oa), lds16(sm, B.al[j] + oa), lds16(sm, B.ah[j] + ob),
-                     lds16(sm, B.al[j] + ob), A2[j]);
-      }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) A2[j][r] = a.ns_b * A[j][r] + a.ns_c * A2[j][r];
-      store_tile_T(sm, B.bh[j], B.bl[j], LE, A2[j], 32 * rt, 32 * ct, lane);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int oa = ara + 16 * ks;
+      const int ob = arb + 16 * ks;
+      A2 = mma3(lds16(sm, bah + oa), lds16(sm, bal + oa), lds16(sm, bah + ob), lds16(sm, bal + ob), A2);
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) A2[r] = a.ns_b * A[r] + a.ns_c * A2[r];
+    store_tile_T(sm, bbh, bbl, LE, A2, 32 * rt, 32 * ct, lane);
     __syncthreads();
     // X = a X + B X: rows 0..63, columns 32w..32w+31; B X's k-operand X comes from registers
     const int brow = opv(l32 * LE + 4 * hf);
+    f32x16 acc[2] = {zero16(), zero16()};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      f32x16 acc[2] = {zero16(), zero16()};
+    for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int o0 = brow + 32 * t * LE + 16 * ks;
-          const u32x4 ah = cat2(lds8(sm, B.bh[j] + o0), lds8(sm, B.bh[j] + o0 + 8));
-          const u32x4 al = cat2(lds8(sm, B.bl[j] + o0), lds8(sm, B.bl[j] + o0 + 8));
-          acc[t] = mma3(ah, al, xh[j][ks], xl[j][ks], acc[t]);
-        }
+      for (int t = 0; t < 2; ++t) {
+        const int o0 = brow + 32 * t * LE + 16 * ks;
+        const u32x4 ah = cat2(lds8(sm, bbh + o0), lds8(sm, bbh + o0 + 8));
+        const u32x4 al = cat2(lds8(sm, bbl + o0), lds8(sm, bbl + o0 + 8));
+        acc[t] = mma3(ah, al, xh[ks], xl[ks], acc[t]);
       }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[j][t][r] = a.ns_a * x[j][t][r] + acc[t][r];
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[t][r] = a.ns_a * x[t][r] + acc[t][r];
     // No barrier here: the next iteration's X stores only overwrite what its A X^T read before
     // barrier 2 of this iteration, and its A / B stores come after its own first barrier.
   }
 }
 
-__global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
+__global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
   float* red = (float*)(sm + LDS_U16);
-  Bases B;
-  B.init();
   const int m = blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w8 = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int s = w8 >> 2, w = w8 & 3;  // row set, hidden-unit slice
   const int hf = lane >> 5, l32 = lane & 31;
-  const int h_own = 32 * w + l32;  // hidden unit this lane owns in register slices
+  const int h_own = 32 * w + l32;     // hidden unit this lane owns in register slices
   const int64_t mT = (int64_t)m * a.T;
   const float* Win = a.Win + (int64_t)m * P;
   const float* Sin = a.Sin + (int64_t)m * P;
   float* Wout = a.Wout + (int64_t)m * P;
   float* Sout = a.Sout + (int64_t)m * P;
+  const int w2h = opq(W2H), w2l = opq(W2L), wth = opq(WTH), wtl = opq(WTL);
+  const int d2h = opq(D2H), d2l = opq(D2L), dth = opq(DTH), dtl = opq(DTL), xth = opq(XTH);
+  const int ra = opq(RA), rb = opq(RB);
 
   // register slice of W1[h_own][d] (B operand of X W1^T, k = d), four k-steps of 16, hi and lo
   u32x4 w1h[4], w1l[4];
@@ -337,29 +321,30 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
     pack8(v, w1h[ks], w1l[ks]);
   }
   // W2 in LDS as [v][h] (for H W2^T) and [h][v] (for D2 W2)
-  for (int e = t; e < D * HD; e += 256) {
+  for (int e = t; e < D * HD; e += NT) {
     const int vv = e / HD, hh = e % HD;
     uint32_t hi, lo;
     split_bf16(Win[P1 + e], hi, lo);
-    sm[B.w2h + vv * LH + hh] = (uint16_t)hi;
-    sm[B.w2l + vv * LH + hh] = (uint16_t)lo;
-    sm[B.wth + hh * LE + vv] = (uint16_t)hi;
-    sm[B.wtl + hh * LE + vv] = (uint16_t)lo;
+    sm[w2h + vv * LH + hh] = (uint16_t)hi;
+    sm[w2l + vv * LH + hh] = (uint16_t)lo;
+    sm[wth + hh * LE + vv] = (uint16_t)hi;
+    sm[wtl + hh * LE + vv] = (uint16_t)lo;
   }
   __syncthreads();
 
   // The X operand of the next row group's X W1^T is loaded one group ahead (software
   // pipelining); the group's values and X^T staging words are loaded at the group's start and
   // used only after its first barrier.
-  const int ngroups = a.C / GR;
-  const int gpc = a.Y ? 2 * ngroups : ngroups;  // groups per chunk: queries first, then keys
+  const int ngroups = a.C / GROWS;
+  const int nq = a.Y ? ngroups : 0;     // query groups come first in a chunk, then key groups
+  const int gpc = nq + ngroups;
   const int vcol = 16 * w + (lane & 15);
   auto load_x = [&](int k, int gi, u32x4 (&px)[4]) {
     if (k >= a.nchunks) return;
-    const bool query = a.Y && gi < ngroups;
-    const int g = query ? gi : (a.Y ? gi - ngroups : gi);
-    const int64_t row0 = mT + (int64_t)k * a.C + (int64_t)g * GR;
-    const uint16_t* xr0 = (query ? a.Q : a.K) + (row0 + l32) * D + 4 * hf;
+    const bool query = gi < nq;
+    const int g = query ? gi : gi - nq;
+    const int64_t row = mT + (int64_t)k * a.C + (int64_t)g * GROWS + GR * s;
+    const uint16_t* xr0 = (query ? a.Q : a.K) + (row + l32) * D + 4 * hf;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       px[ks] = cat2(*(const uint2*)(xr0 + 16 * ks), *(const uint2*)(xr0 + 16 * ks + 8));
@@ -370,12 +355,14 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
   bool bad = false;
   for (int k = 0; k < a.nchunks; ++k) {
     const int64_t s0 = (int64_t)k * a.C;
-    // gr[0]: G1^T tiles (d rows 0..31 / 32..63, h_own); gr[1]: G2 tiles (v rows 0..31 / 32..63, h_own)
+    // partial gradients over this set's rows: gr[0] = G1^T tiles (d rows 0..31 / 32..63,
+    // h_own), gr[1] = G2 tiles (v rows 0..31 / 32..63, h_own)
     f32x16 gr[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
     for (int gi = 0; gi < gpc; ++gi) {
-      const bool query = a.Y && gi < ngroups;
-      const int g = query ? gi : (a.Y ? gi - ngroups : gi);
-      const int64_t row0 = mT + s0 + (int64_t)g * GR;  // token row of the group's first row
+      const bool query = gi < nq;
+      const int g = query ? gi : gi - nq;
+      const int64_t row0 = mT + s0 + (int64_t)g * GROWS;  // token row of the group's first row
+      const int64_t rset = row0 + GR * s;                  // ... and of this set's first row
       // this group's values and X^T words first: the next group's loads are issued after them,
       // so waiting for these (loads return in order) never waits for the prefetch
       u32x4 xt;
@@ -385,14 +372,19 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) vv[4 * rt + u] = a.V[(row0 + 16 * rt + 4 * (lane >> 4) + u) * D + vcol];
+          for (int u = 0; u < 4; ++u) vv[4 * rt + u] = a.V[(rset + 16 * rt + 4 * (lane >> 4) + u) * D + vcol];
       }
       u32x4 xa[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) xa[ks] = px[ks];
       if (gi + 1 < gpc) load_x(k, gi + 1, px);
       else load_x(k + 1, 0, px);
-      // Z = X W1^T: rows 0..31 of the group, hidden units of this wave
+      // H of query groups alternates between regions B and A, so a query group never waits for
+      // the previous one's readers; a key group writes H to B and D2 / X^T to A.  With an odd
+      // number of query groups the last one used B, whose readers the first key group waits for.
+      const int hb = (query && (gi & 1)) ? ra : rb;
+      if (!query && gi == nq && (nq & 1)) __syncthreads();
+      // Z = X W1^T: this set's 32 rows, hidden units of this wave
       f32x16 z = zero16();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -400,33 +392,35 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
         z = mfma32(xa[ks], w1l[ks], z);
       }
       f32x16 hz, zp;
+      if (query) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float sg = sigmoidf_(z[r]);
-        hz[r] = z[r] * sg;
-        zp[r] = sg * (1.0f + z[r] * (1.0f - sg));
+        for (int r = 0; r < 16; ++r) hz[r] = z[r] * sigmoidf_(z[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float sg = sigmoidf_(z[r]);
+          hz[r] = z[r] * sg;
+          zp[r] = sg * (1.0f + z[r] * (1.0f - sg));
+        }
       }
-      // H buffers alternate between groups, so a group never waits for the previous group's
-      // readers before writing
-      const int hoff = (gi & 1) ? (HB2 - HBH) : 0;
-      u32x4 hph[2], hpl[2];  // hi/lo words of H, k-steps over the group's rows
+      u32x4 hph[2], hpl[2];  // hi/lo words of H, k-steps over the set's rows
 #pragma unroll
       for (int kl = 0; kl < 2; ++kl) {
         tile_op(hz, kl, hph[kl], hpl[kl]);
-        store_rows(sm, B.hbh + hoff, B.hbl + hoff, LH, hph[kl], hpl[kl], 16 * kl, h_own, hf);
+        store_rows(sm, hb, hb + HSZ, LH, hph[kl], hpl[kl], GR * s + 16 * kl, h_own, hf);
       }
       __syncthreads();
-      // Yh = H W2^T: 16x16 tiles, wave w owns values [16w, 16w+16), both row halves
+      // Yh = H W2^T: 16x16 tiles, wave w owns values [16w, 16w+16), both row halves of the set
       f32x4 yh[2];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < HD / 32; ++ks) {
-          const int oa = (16 * rt + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
+          const int oa = (GR * s + 16 * rt + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
           const int ob = (16 * w + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
-          acc = mma3_16(lds16(sm, B.hbh + hoff + oa), lds16(sm, B.hbl + hoff + oa), lds16(sm, B.w2h + ob),
-                        lds16(sm, B.w2l + ob), acc);
+          acc = mma3_16(lds16(sm, hb + oa), lds16(sm, hb + HSZ + oa), lds16(sm, w2h + ob), lds16(sm, w2l + ob),
+                        acc);
         }
         yh[rt] = acc;
       }
@@ -435,7 +429,7 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int64_t yo = (row0 + 16 * rt + 4 * (lane >> 4) + u) * D + vcol;
+            const int64_t yo = (rset + 16 * rt + 4 * (lane >> 4) + u) * D + vcol;
             if (a.out_bf16) ((uint16_t*)a.Y)[yo] = (uint16_t)bf16_bits(yh[rt][u]);
             else ((float*)a.Y)[yo] = yh[rt][u];
           }
@@ -444,7 +438,7 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
       // D2 = 2 (Yh - V): to LDS as [row][v] (operand of D2 W2) and [v][row] (operand of D2^T H)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const int rb = 16 * rt + 4 * (lane >> 4);
+        const int rr = GR * s + 16 * rt + 4 * (lane >> 4);
         float d2[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) d2[u] = 2.0f * (yh[rt][u] - bf16_value(vv[4 * rt + u]));
@@ -455,18 +449,18 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
         const uint32_t ll[4] = {l0 & 0xFFFFu, l0 >> 16, l1 & 0xFFFFu, l1 >> 16};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          sm[B.d2h + (rb + u) * LE + vcol] = (uint16_t)hh[u];
-          sm[B.d2l + (rb + u) * LE + vcol] = (uint16_t)ll[u];
+          sm[d2h + (rr + u) * LE + vcol] = (uint16_t)hh[u];
+          sm[d2l + (rr + u) * LE + vcol] = (uint16_t)ll[u];
         }
-        *(uint2*)(sm + B.dth + vcol * LR + rb) = uint2{h0, h1};
-        *(uint2*)(sm + B.dtl + vcol * LR + rb) = uint2{l0, l1};
+        *(uint2*)(sm + dth + vcol * LR + rr) = uint2{h0, h1};
+        *(uint2*)(sm + dtl + vcol * LR + rr) = uint2{l0, l1};
       }
       {  // X^T of the group for the G1 product
         const int r = t >> 3, d0 = (t & 7) * 8;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sm[B.xth + (d0 + 2 * i) * LR + r] = (uint16_t)(xt[i] & 0xFFFFu);
-          sm[B.xth + (d0 + 2 * i + 1) * LR + r] = (uint16_t)(xt[i] >> 16);
+          sm[xth + (d0 + 2 * i) * LR + r] = (uint16_t)(xt[i] & 0xFFFFu);
+          sm[xth + (d0 + 2 * i + 1) * LR + r] = (uint16_t)(xt[i] >> 16);
         }
       }
       __syncthreads();
@@ -474,17 +468,17 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
       f32x16 p = zero16();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int o0 = l32 * LE + 16 * ks + 4 * hf;
-        const u32x4 ah = cat2(lds8(sm, B.d2h + o0), lds8(sm, B.d2h + o0 + 8));
-        const u32x4 al = cat2(lds8(sm, B.d2l + o0), lds8(sm, B.d2l + o0 + 8));
+        const int o0 = (GR * s + l32) * LE + 16 * ks + 4 * hf;
+        const u32x4 ah = cat2(lds8(sm, d2h + o0), lds8(sm, d2h + o0 + 8));
+        const u32x4 al = cat2(lds8(sm, d2l + o0), lds8(sm, d2l + o0 + 8));
         const int ob = h_own * LE + 16 * ks + 4 * hf;
-        const u32x4 bh = cat2(lds8(sm, B.wth + ob), lds8(sm, B.wth + ob + 8));
-        const u32x4 bl = cat2(lds8(sm, B.wtl + ob), lds8(sm, B.wtl + ob + 8));
+        const u32x4 bh = cat2(lds8(sm, wth + ob), lds8(sm, wth + ob + 8));
+        const u32x4 bl = cat2(lds8(sm, wtl + ob), lds8(sm, wtl + ob + 8));
         p = mma3(ah, al, bh, bl, p);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[r] *= zp[r];
-      // G1^T += X^T D1 and G2 += D2^T H (k = the group's rows, B operands from registers)
+      // G1^T += X^T D1 and G2 += D2^T H (k = the set's rows, B operands from registers)
 #pragma unroll
       for (int kl = 0; kl < 2; ++kl) {
         u32x4 dh, dl;
@@ -492,17 +486,51 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
         const u32x4 hh = hph[kl], hl = hpl[kl];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const int o0 = (32 * tt + l32) * LR + 16 * kl + 4 * hf;
-          const u32x4 xa = cat2(lds8(sm, B.xth + o0), lds8(sm, B.xth + o0 + 8));
+          const int o0 = (32 * tt + l32) * LR + GR * s + 16 * kl + 4 * hf;
+          const u32x4 xa = cat2(lds8(sm, xth + o0), lds8(sm, xth + o0 + 8));
           gr[0][tt] = mfma32(xa, dh, gr[0][tt]);
           gr[0][tt] = mfma32(xa, dl, gr[0][tt]);
-          const u32x4 ah = cat2(lds8(sm, B.dth + o0), lds8(sm, B.dth + o0 + 8));
-          const u32x4 al = cat2(lds8(sm, B.dtl + o0), lds8(sm, B.dtl + o0 + 8));
+          const u32x4 ah = cat2(lds8(sm, dth + o0), lds8(sm, dth + o0 + 8));
+          const u32x4 al = cat2(lds8(sm, dtl + o0), lds8(sm, dtl + o0 + 8));
           gr[1][tt] = mma3(ah, al, hh, hl, gr[1][tt]);
         }
       }
       // No barrier here: the next group rewrites D2, D2^T and X^T only after its first barrier,
-      // which every wave reaches after finishing these reads; H alternates buffers.
+      // which every wave reaches after finishing these reads.
+    }
+
+    // Swap partial gradients: set 0 keeps G1 and passes its G2 partial, set 1 the reverse.
+    // The slots were last read by the final group's H W2^T, before its second barrier.
+    f32x16 x[2];
+    {
+      float* xg1 = (float*)(sm + opq(XG1));
+      float* xg2 = (float*)(sm + opq(XG2));
+      if (s == 0) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(float4*)(xg2 + (((w * 2 + tt) * 4 + q) * 64 + lane) * 4) =
+                float4{gr[1][tt][4 * q], gr[1][tt][4 * q + 1], gr[1][tt][4 * q + 2], gr[1][tt][4 * q + 3]};
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(float4*)(xg1 + (((w * 2 + tt) * 4 + q) * 64 + lane) * 4) =
+                float4{gr[0][tt][4 * q], gr[0][tt][4 * q + 1], gr[0][tt][4 * q + 2], gr[0][tt][4 * q + 3]};
+      }
+      __syncthreads();
+      const float* src = s ? xg2 : xg1;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = *(const float4*)(src + (((w * 2 + tt) * 4 + q) * 64 + lane) * 4);
+          const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[tt][4 * q + u] = (s ? gr[1][tt][4 * q + u] : gr[0][tt][4 * q + u]) + fv[u];
+        }
     }
 
     const int64_t gk = (int64_t)m * a.nchunks + k;
@@ -510,72 +538,91 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
     const float* Wsrc = (k == 0) ? Win : Wout;
     const float* Ssrc = (k == 0) ? Sin : Sout;
 
-    newton_schulz2(gr, sm, B, red, a, lane, w);
-    // state of both matrices (W1 element (h_own, d), W2 element (v, h_own)), loaded together;
-    // addressed as 32-bit offsets from the memory's uniform base
-    const int o1 = h_own * D + 4 * hf;                // W1 row h_own, d = 4hf + ...
-    const int o2 = (int)P1 + 4 * hf * HD + h_own;     // W2 column h_own, v = 4hf + ...
-    float4 so1[2][4], wo1[2][4];
-    float so2[2][16], wo2[2][16];
+    {
+      const int bxh = opq(NX + s * NXS), bah = opq(NA + s * NAS), bbh = opq(NB + s * NBS);
+      newton_schulz1(x, sm, bxh, bxh + 64 * LH, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red + 4 * s, a, lane, w);
+    }
+    // Update of this set's matrix; state addressed as 32-bit offsets from the memory's base.
+    // The weight copies overwrite the Newton-Schulz X buffers, which nobody reads after the
+    // last iteration's second barrier; the W1 handoff overwrites the A buffers, dead after its
+    // third.
+    u32x4* ho = (u32x4*)(sm + opq(HOFF));
+    if (s == 0) {
+      // W1: G1^T tile element (d, h_own) <-> W1[h_own][d]
+      const int o1 = opv(h_own * D + 4 * hf);
+      float4 so1[2][4], wo1[2][4];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        so1[tt][q] = *(const float4*)(Ssrc + o1 + 32 * tt + 8 * q);
-        wo1[tt][q] = *(const float4*)(Wsrc + o1 + 32 * tt + 8 * q);
-      }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ov = o2 + (32 * tt + 8 * (r >> 2) + (r & 3)) * HD;
-        so2[tt][r] = Ssrc[ov];
-        wo2[tt][r] = Wsrc[ov];
-      }
-    // W1: G1^T tile element (d, h_own) <-> W1[h_own][d]
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 so = so1[tt][q];
-        const float4 wo = wo1[tt][q];
-        const float sv[4] = {so.x, so.y, so.z, so.w}, wv[4] = {wo.x, wo.y, wo.z, wo.w};
-        float sn[4], wn[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          sn[u] = et * sv[u] - th * gr[0][tt][4 * q + u];
-          wn[u] = om * wv[u] + sn[u];
-          gr[0][tt][4 * q + u] = wn[u];
-          bad |= !(isfinite(sn[u]) && isfinite(wn[u]));
+        for (int q = 0; q < 4; ++q) {
+          so1[tt][q] = *(const float4*)(Ssrc + o1 + 32 * tt + 8 * q);
+          wo1[tt][q] = *(const float4*)(Wsrc + o1 + 32 * tt + 8 * q);
         }
-        *(float4*)(Sout + o1 + 32 * tt + 8 * q) = float4{sn[0], sn[1], sn[2], sn[3]};
-        *(float4*)(Wout + o1 + 32 * tt + 8 * q) = float4{wn[0], wn[1], wn[2], wn[3]};
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 so = so1[tt][q];
+          const float4 wo = wo1[tt][q];
+          const float sv[4] = {so.x, so.y, so.z, so.w}, wv[4] = {wo.x, wo.y, wo.z, wo.w};
+          float sn[4], wn[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            sn[u] = et * sv[u] - th * x[tt][4 * q + u];
+            wn[u] = om * wv[u] + sn[u];
+            x[tt][4 * q + u] = wn[u];
+            bad |= !(isfinite(sn[u]) && isfinite(wn[u]));
+          }
+          *(float4*)(Sout + o1 + 32 * tt + 8 * q) = float4{sn[0], sn[1], sn[2], sn[3]};
+          *(float4*)(Wout + o1 + 32 * tt + 8 * q) = float4{wn[0], wn[1], wn[2], wn[3]};
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 wh, wl;
+        tile_op(x[ks >> 1], ks & 1, wh, wl);
+        ho[(w * 8 + ks) * 64 + lane] = wh;
+        ho[(w * 8 + 4 + ks) * 64 + lane] = wl;
       }
+    } else {
+      // W2: G2 tile element (v, h_own) <-> W2[v][h_own]
+      const int o2 = opv((int)P1 + 4 * hf * HD + h_own);
+      float so2[2][16], wo2[2][16];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) tile_op(gr[0][ks >> 1], ks & 1, w1h[ks], w1l[ks]);
-    // W2: G2 tile element (v, h_own) <-> W2[v][h_own]
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+        for (int r = 0; r < 16; ++r) {
+          const int ov = o2 + (32 * tt + 8 * (r >> 2) + (r & 3)) * HD;
+          so2[tt][r] = Ssrc[ov];
+          wo2[tt][r] = Wsrc[ov];
+        }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ov = o2 + (32 * tt + 8 * (r >> 2) + (r & 3)) * HD;
-        const float sn = et * so2[tt][r] - th * gr[1][tt][r];
-        const float wn = om * wo2[tt][r] + sn;
-        Sout[ov] = sn;
-        Wout[ov] = wn;
-        gr[1][tt][r] = wn;
-        bad |= !(isfinite(sn) && isfinite(wn));
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ov = o2 + (32 * tt + 8 * (r >> 2) + (r & 3)) * HD;
+          const float sn = et * so2[tt][r] - th * x[tt][r];
+          const float wn = om * wo2[tt][r] + sn;
+          Sout[ov] = sn;
+          Wout[ov] = wn;
+          x[tt][r] = wn;
+          bad |= !(isfinite(sn) && isfinite(wn));
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 wh, wl;
+        tile_op(x[ks >> 1], ks & 1, wh, wl);
+        store_rows(sm, w2h, w2l, LH, wh, wl, 16 * ks, h_own, hf);
+        store_rows_T(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
       }
-    // the weight copies overwrite the Newton-Schulz X buffers, which nobody reads after the
-    // last iteration's second barrier
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 wh, wl;
-      tile_op(gr[1][ks >> 1], ks & 1, wh, wl);
-      store_rows(sm, B.w2h, B.w2l, LH, wh, wl, 16 * ks, h_own, hf);
-      store_rows_T(sm, B.wth, B.wtl, LE, wh, wl, 16 * ks, h_own, hf);
     }
     __syncthreads();
+    // both sets take the new W1 slices from LDS (the registers then hold nothing across the
+    // Newton-Schulz phase)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      w1h[ks] = ho[(w * 8 + ks) * 64 + lane];
+      w1l[ks] = ho[(w * 8 + 4 + ks) * 64 + lane];
+    }
   }
   if (bad) a.flag[0] = 1;
 }
@@ -584,7 +631,8 @@ __global__ void __launch_bounds__(256) fused_ns_kernel(Args a) {
 
 bool fused_supported(const Dims& d) {
   return d.kind == ATLASMEM_MLP2_SILU && d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0 && d.dk == fz::D &&
-         d.din == fz::D && d.dv == fz::D && d.dh == fz::HD && d.c == 1 && d.C % fz::GR == 0 && d.in_bf16 && d.split;
+         d.din == fz::D && d.dv == fz::D && d.dh == fz::HD && d.c == 1 && d.C % fz::GROWS == 0 && d.in_bf16 &&
+         d.split;
 }
 
 atlasmem_status launch_fused(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
@@ -612,14 +660,10 @@ atlasmem_status launch_fused(Handle* h, const void* K, const void* Q, const void
   a.ns_c = d.ns_c;
   a.ns_eps = d.ns_eps;
   a.flag = h->flag;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)fz::fused_ns_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            fz::LDS_BYTES) != hipSuccess)
-      return ATLASMEM_E_DEVICE;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(fz::fused_ns_kernel, dim3(d.M), dim3(256), fz::LDS_BYTES, st, a);
+  if (hipFuncSetAttribute((const void*)fz::fused_ns_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          fz::LDS_BYTES) != hipSuccess)
+    return ATLASMEM_E_DEVICE;
+  hipLaunchKernelGGL(fz::fused_ns_kernel, dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
   AM_LAUNCH_CHECK();
   h->cur = 1 - h->cur;
   return ATLASMEM_OK;

@@ -12,8 +12,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("ov", [dict(batch=2, heads=4, T=512), dict(batch=1, heads=3, T=384, chunk=64),
-                                dict(batch=1, heads=2, T=256, chunk=32), dict(batch=1, heads=2, T=384, chunk=96)],
-                         ids=["C128", "C64", "C32", "C96"])
+                                dict(batch=1, heads=2, T=384, chunk=192), dict(batch=1, heads=2, T=384, chunk=96)],
+                         ids=["C128", "C64", "C192", "C96_general"])
 def test_fused_matches_oracle_and_general_path(ov):
     inp = synth.make_inputs(4, "literal", **ov)
     ref = oracle_run(inp)
