@@ -69,6 +69,42 @@ __device__ __forceinline__ float silu_primef_(float z) {
   return s * (1.0f + z * (1.0f - s));
 }
 
+// Raw buffer access: a uniform base in a buffer resource plus a 32-bit per-lane byte offset and
+// a uniform byte offset, so that per-element addresses cost no 64-bit vector arithmetic.
+// Accesses at or beyond `bytes` read 0 / are dropped by the hardware range check.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float buf_ld(rsrc_t r, int voff, int soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ float4 buf_ld4(rsrc_t r, int voff, int soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return float4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+}
+__device__ __forceinline__ uint2 buf_ld8(rsrc_t r, int voff, int soff) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return uint2{v[0], v[1]};
+}
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_ld_u16(rsrc_t r, int voff, int soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st_u16(rsrc_t r, int voff, int soff, uint32_t x) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)x, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st(rsrc_t r, int voff, int soff, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st4(rsrc_t r, int voff, int soff, float4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      u32x4{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)}, r, voff, soff, 0);
+}
+
 // Load one input element (bf16 bits or fp32) as float.
 __device__ __forceinline__ float load_in(const void* p, int64_t idx, int is_bf16) {
   if (is_bf16) return bf16_value(((const uint16_t*)p)[idx]);

@@ -69,9 +69,10 @@ constexpr int HSZ = GROWS * LH;                  // one of H hi / H lo
 constexpr int RB = RA_END;
 constexpr int GEND = RB + 2 * HSZ;
 static_assert(RA_END - RA >= 2 * HSZ, "region A must also hold an H");
-// Newton-Schulz phase, matrix j (set j): X [row][col] hi/lo, A and B [64][64] hi/lo.  The X
-// buffers lie under the weight copies, which the update rewrites after the last read of X.
-constexpr int NX = 0, NXS = 2 * 64 * LH;
+// Newton-Schulz phase, matrix j (set j): X^T [col][row] hi/lo (128 x 64, rows of 128 bytes, 8-byte
+// chunks swizzled), A and B [64][64] hi/lo.  The X buffers lie under the weight copies, which
+// the update rewrites after the last read of X.
+constexpr int NX = 0, NXS = 2 * HD * 64;
 constexpr int NA = 2 * NXS, NAS = 2 * 64 * LD;
 constexpr int NB = NA + 2 * NAS, NBS = 2 * 64 * LE;
 constexpr int NEND = NB + 2 * NBS;
@@ -83,27 +84,29 @@ constexpr int XG_U16 = 4 * 2 * 4 * 64 * 4 * 2;
 static_assert(XG_U16 <= 2 * 64 * LH && XG_U16 <= 2 * HSZ, "exchange slots");
 // New W1 operand words from set 0 to set 1 ([wave][k-step word][lane] u32x4), over the
 // Newton-Schulz A buffers, which are dead after the last A^2 product.
-constexpr int HOFF = NA;
+constexpr int HOFF = RA;
 constexpr int HOFF_U16 = 4 * 8 * 64 * 8;
-static_assert(HOFF + HOFF_U16 <= NB, "handoff must not overlap the B buffers");
+static_assert(HOFF >= NA && HOFF + HOFF_U16 <= NB, "handoff must lie in the A buffers");
 constexpr int LDS_U16 = (GEND > NEND ? GEND : NEND);
 constexpr int LDS_BYTES = LDS_U16 * 2 + 16 * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
 struct Args {
-  const uint16_t* K;
+  const uint16_t* K;     // token 0 of this launch, memory 0; memory m at + m * ldT * D
   const uint16_t* Q;
   const uint16_t* V;
-  const float* theta;
+  const float* theta;    // chunk 0 of this launch, memory 0; memory m at + m * ld_gate
   const float* eta;
   const float* alpha;
-  int64_t T;
+  int64_t ldT;           // tokens per memory in the caller's arrays
+  int64_t ld_gate;       // chunks per memory in the caller's gate arrays
   int C;
-  int nchunks;
+  int nchunks;           // chunks of this launch
   const float* Win;
   const float* Sin;
   float* Wout;
   float* Sout;
+  float* T2;   // per memory [W2^T (h, v) | S2^T (h, v)]: the W2 state between chunks of a launch
   void* Y;
   int out_bf16;
   int ns_steps;
@@ -127,6 +130,7 @@ __device__ __forceinline__ int opv(int x) {
 
 constexpr int64_t P1 = (int64_t)HD * D;        // W1 size
 constexpr int64_t P = P1 + (int64_t)D * HD;    // parameters per memory
+constexpr int P2 = D * HD;                     // W2 size
 
 __device__ __forceinline__ u32x4 cat2(uint2 a, uint2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
 __device__ __forceinline__ uint2 lds8(const uint16_t* s, int off) { return *(const uint2*)(s + off); }
@@ -213,11 +217,35 @@ __device__ __forceinline__ void store_rows_T(uint16_t* sm, int offh, int offl, i
   *(uint2*)(sm + offl + o + 8) = uint2{lo[2], lo[3]};
 }
 
+// X^T element (c, r) of the Newton-Schulz buffer lives at c * 64 + (r ^ swz(c)): the XOR moves
+// whole 8-byte chunks so that the 8-byte stores and reads along c and the transposing reads
+// across four consecutive c all land on distinct banks.
+__device__ __forceinline__ int swz(int c) {
+  const int x = (c >> 1) & 15;
+  return 4 * (((x & 1) << 3) | (x >> 1));
+}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4e + q names an 8-byte chunk (row e, four
+// consecutive columns 4q..4q+3 of a 4 x 16 block); lane i receives column i of the four rows.
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // Newton-Schulz on one 64 x 128 matrix held by the four waves of a set as two 32 x 32 tiles
 // per wave (wave w: columns 32w..32w+31), in place.  xh/xl/ah/al/bh/bl: the set's LDS buffers;
 // red: the set's four partial sums of squares.
-__device__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int bxh, int bxl, int bah, int bal, int bbh, int bbl,
-                               float* red, const Args& a, int lane, int w) {
+template <int P>
+struct Part {
+  static constexpr int value = P;
+};
+// pre(Part<p>) (p = 0..3) is called before iteration p: it issues the p-th quarter of the state
+// loads, so that they stream in under the matrix work instead of stalling the vector memory path
+// all at once.
+template <class Pre>
+__device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int bxh, int bxl, int bah, int bal,
+                                               int bbh, int bbl, float* red, const Args& a, int lane, int w,
+                                               Pre&& pre) {
   const int hf = lane >> 5, l32 = lane & 31;
   float ss = 0.0f;
 #pragma unroll
@@ -235,72 +263,126 @@ __device__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int bxh, int bxl, i
     for (int r = 0; r < 16; ++r) x[t][r] *= inv;
 
   const int rt = w >> 1, ct = w & 1;
-  for (int it = 0; it < a.ns_steps; ++it) {
-    const int xcol = opv(32 * w + l32);
-    const int xra = opv((32 * rt + l32) * LH + 8 * hf), xrb = opv((32 * ct + l32) * LH + 8 * hf);
-    // hi/lo words of X, k-step ks = rows 16ks..16ks+15 (operand of B X and the LDS copy)
-    u32x4 xh[4], xl[4];
+  // this lane's column c = 32w + l32 of X: X^T row base and swizzle
+  const int cx = opv(32 * w + l32);
+  const int xrow = cx * 64, xsw = swz(cx) ^ (4 * hf);
+  // operands of A = X X^T by transposing reads: lane (g, e, q) of 16-lane group g reads the
+  // chunk of X^T row c = 16ks + 8(g/2) + e (+4 for the second half of the k-step) at rows
+  // rb + 16(g%2) + 4q; the swizzle of c + 16 differs from that of c by 16 (XOR).
+  const int ln = opv(lane);
+  const int g = ln >> 4, e = (ln >> 2) & 3, q4 = 4 * (ln & 3);
+  const int c1 = 8 * (g >> 1) + e, c2 = c1 + 4;
+  const int ra = 32 * rt + 16 * (g & 1) + q4, rb = 32 * ct + 16 * (g & 1) + q4;
+  const int ta1 = c1 * 64 + (ra ^ swz(c1)), ta2 = c2 * 64 + (ra ^ swz(c2));
+  const int tb1 = c1 * 64 + (rb ^ swz(c1)), tb2 = c2 * 64 + (rb ^ swz(c2));
+  auto iteration = [&]() __attribute__((always_inline)) {
+    // X^T to LDS: tile t, quad q of this lane = rows 32t + 8q + 4hf .. +3 of column cx
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      tile_op(x[ks >> 1], ks & 1, xh[ks], xl[ks]);
-      store_rows(sm, bxh, bxl, LH, xh[ks], xl[ks], 16 * ks, xcol, hf);
-    }
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t h0, l0, h1, l1;
+        split2(x[t][4 * q], x[t][4 * q + 1], h0, l0);
+        split2(x[t][4 * q + 2], x[t][4 * q + 3], h1, l1);
+        const int o = opv(xrow + ((32 * t + 8 * q) ^ xsw));
+        *(uint2*)(sm + bxh + o) = uint2{h0, h1};
+        *(uint2*)(sm + bxl + o) = uint2{l0, l1};
+      }
     __syncthreads();
-    // A = X X^T, tile (rt, ct)
+    // A = X X^T, tile (rt, ct), k = the 128 columns in steps of 16 (natural order)
     f32x16 A = zero16();
+    {
+      const int pa1 = opv(ta1), pa2 = opv(ta2), pb1 = opv(tb1), pb2 = opv(tb2);
 #pragma unroll
-    for (int ks = 0; ks < HD / 16; ++ks) {
-      const int oa = xra + 16 * ks;
-      const int ob = xrb + 16 * ks;
-      A = mma3(lds16(sm, bxh + oa), lds16(sm, bxl + oa), lds16(sm, bxh + ob), lds16(sm, bxl + ob), A);
+      for (int ks = 0; ks < HD / 16; ++ks) {
+        const int f = (ks & 1) ? 16 : 0, kb = ks * 16 * 64;
+        const u32x4 ah = cat2(lds_tr16(sm + bxh + kb + (pa1 ^ f)), lds_tr16(sm + bxh + kb + (pa2 ^ f)));
+        const u32x4 al = cat2(lds_tr16(sm + bxl + kb + (pa1 ^ f)), lds_tr16(sm + bxl + kb + (pa2 ^ f)));
+        const u32x4 bh = cat2(lds_tr16(sm + bxh + kb + (pb1 ^ f)), lds_tr16(sm + bxh + kb + (pb2 ^ f)));
+        const u32x4 bl = cat2(lds_tr16(sm + bxl + kb + (pb1 ^ f)), lds_tr16(sm + bxl + kb + (pb2 ^ f)));
+        A = mma3(ah, al, bh, bl, A);
+      }
     }
     store_tile_T(sm, bah, bal, LD, A, 32 * rt, 32 * ct, lane);
     __syncthreads();
-    // A^2, tile (rt, ct); B = b A + c A^2
-    const int ara = opv((32 * rt + l32) * LD + 8 * hf), arb = opv((32 * ct + l32) * LD + 8 * hf);
-    f32x16 A2 = zero16();
+    // B = b A + c A^2, tile (rt, ct), accumulated in place of A as c (A^2 + (b/c) A)
+    if (a.ns_c != 0.0f) {
+      const float r_bc = a.ns_b / a.ns_c;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const int oa = ara + 16 * ks;
-      const int ob = arb + 16 * ks;
-      A2 = mma3(lds16(sm, bah + oa), lds16(sm, bal + oa), lds16(sm, bah + ob), lds16(sm, bal + ob), A2);
+      for (int r = 0; r < 16; ++r) A[r] *= r_bc;
+      const int ara = opv((32 * rt + l32) * LD + 8 * hf), arb = opv((32 * ct + l32) * LD + 8 * hf);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int oa = ara + 16 * ks;
+        const int ob = arb + 16 * ks;
+        A = mma3(lds16(sm, bah + oa), lds16(sm, bal + oa), lds16(sm, bah + ob), lds16(sm, bal + ob), A);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) A[r] *= a.ns_c;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) A[r] *= a.ns_b;
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) A2[r] = a.ns_b * A[r] + a.ns_c * A2[r];
-    store_tile_T(sm, bbh, bbl, LE, A2, 32 * rt, 32 * ct, lane);
+    store_tile_T(sm, bbh, bbl, LE, A, 32 * rt, 32 * ct, lane);
     __syncthreads();
-    // X = a X + B X: rows 0..63, columns 32w..32w+31; B X's k-operand X comes from registers
+    // X = a X + B X: rows 0..63, columns 32w..32w+31; B X's k-operand X (rows of column cx in
+    // the order 4hf..4hf+3, 8+4hf..8+4hf+3 of each k-step) comes back from X^T
+    // (accumulated onto a X in place)
     const int brow = opv(l32 * LE + 4 * hf);
-    f32x16 acc[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[t][r] *= a.ns_a;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
+      const int o1 = opv(xrow + ((16 * ks) ^ xsw)), o2 = opv(xrow + ((16 * ks + 8) ^ xsw));
+      const u32x4 xh = cat2(lds8(sm, bxh + o1), lds8(sm, bxh + o2));
+      const u32x4 xl = cat2(lds8(sm, bxl + o1), lds8(sm, bxl + o2));
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int o0 = brow + 32 * t * LE + 16 * ks;
         const u32x4 ah = cat2(lds8(sm, bbh + o0), lds8(sm, bbh + o0 + 8));
         const u32x4 al = cat2(lds8(sm, bbl + o0), lds8(sm, bbl + o0 + 8));
-        acc[t] = mma3(ah, al, xh[ks], xl[ks], acc[t]);
+        x[t] = mma3(ah, al, xh, xl, x[t]);
       }
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[t][r] = a.ns_a * x[t][r] + acc[t][r];
-    // No barrier here: the next iteration's X stores only overwrite what its A X^T read before
-    // barrier 2 of this iteration, and its A / B stores come after its own first barrier.
-  }
+    // No barrier here: B X reads only the X^T rows of this lane's own column, which this lane
+    // wrote, and the other waves read X^T only in A X^T, which every wave finished before
+    // barrier 2; the A / B stores of the next iteration come after its own first barrier.
+  };
+  pre(Part<0>());
+  if (a.ns_steps > 0) iteration();
+  pre(Part<1>());
+  if (a.ns_steps > 1) iteration();
+  pre(Part<2>());
+  if (a.ns_steps > 2) iteration();
+  pre(Part<3>());
+  for (int it = 3; it < a.ns_steps; ++it) iteration();
 }
 
 __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
   float* red = (float*)(sm + LDS_U16);
   const int m = blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63;
-  const int w8 = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int t0 = threadIdx.x;
+  const int w8 = __builtin_amdgcn_readfirstlane(t0 >> 6);
   const int s = w8 >> 2, w = w8 & 3;  // row set, hidden-unit slice
-  const int hf = lane >> 5, l32 = lane & 31;
-  const int h_own = 32 * w + l32;     // hidden unit this lane owns in register slices
-  const int64_t mT = (int64_t)m * a.T;
+  // Lane-dependent values are re-derived in each phase from an opaque copy of the thread index,
+  // so that the compiler does not keep them (and every address made from them) live across the
+  // whole chunk loop.  h_own: the hidden unit this lane owns in register slices.
+#define AM_LANE_VARS                                                                \
+  const int t = opv(t0), lane = t & 63, hf = lane >> 5, l32 = lane & 31;          \
+  const int h_own = 32 * w + l32;                                                 \
+  (void)hf; (void)l32; (void)h_own
+  // this memory's token rows as buffer resources (byte offsets fit in 32 bits: a launch covers
+  // at most 2^22 tokens)
+  const int nT = a.nchunks * a.C;
+  const rsrc_t rK = make_rsrc(a.K + (int64_t)m * a.ldT * D, (uint32_t)nT * D * 2);
+  const rsrc_t rQ = make_rsrc(a.Q + (int64_t)m * a.ldT * D, (uint32_t)nT * D * 2);
+  const rsrc_t rV = make_rsrc(a.V + (int64_t)m * a.ldT * D, (uint32_t)nT * D * 2);
+  const int ysz = a.out_bf16 ? 2 : 4;  // bytes per output element
+  const rsrc_t rY = make_rsrc(a.Y ? (const char*)a.Y + (int64_t)m * a.ldT * D * ysz : nullptr,
+                              a.Y ? (uint32_t)nT * D * ysz : 0u);
   const float* Win = a.Win + (int64_t)m * P;
   const float* Sin = a.Sin + (int64_t)m * P;
   float* Wout = a.Wout + (int64_t)m * P;
@@ -311,6 +393,8 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
 
   // register slice of W1[h_own][d] (B operand of X W1^T, k = d), four k-steps of 16, hi and lo
   u32x4 w1h[4], w1l[4];
+  {
+  AM_LANE_VARS;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     float v[8];
@@ -330,6 +414,27 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
     sm[wth + hh * LE + vv] = (uint16_t)hi;
     sm[wtl + hh * LE + vv] = (uint16_t)lo;
   }
+  // set 1 keeps the W2 part of the state transposed in T2 between chunks (16-byte accesses for
+  // its register layout, see the update); each lane writes exactly the elements it reads later
+  if (s == 1) {
+    const rsrc_t rt2 = make_rsrc(a.T2 + (int64_t)m * 2 * P2, (uint32_t)(2 * P2 * 4));
+    const int vt = (h_own * D + 4 * hf) * 4;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float wv4[4], sv4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t o = P1 + (int64_t)(32 * tt + 8 * q + 4 * hf + u) * HD + h_own;
+          wv4[u] = Win[o];
+          sv4[u] = Sin[o];
+        }
+        buf_st4(rt2, vt, (32 * tt + 8 * q) * 4, float4{wv4[0], wv4[1], wv4[2], wv4[3]});
+        buf_st4(rt2, vt + P2 * 4, (32 * tt + 8 * q) * 4, float4{sv4[0], sv4[1], sv4[2], sv4[3]});
+      }
+  }
+  }
   __syncthreads();
 
   // The X operand of the next row group's X W1^T is loaded one group ahead (software
@@ -338,59 +443,57 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
   const int ngroups = a.C / GROWS;
   const int nq = a.Y ? ngroups : 0;     // query groups come first in a chunk, then key groups
   const int gpc = nq + ngroups;
-  const int vcol = 16 * w + (lane & 15);
-  auto load_x = [&](int k, int gi, u32x4 (&px)[4]) {
-    if (k >= a.nchunks) return;
+  // The X operand rows of a row group (this set's rows) are loaded by the previous group
+  // (software pipelining), right after its own X W1^T has consumed the registers they land in.
+  auto load_x = [&](int k, int gi, u32x4 (&px)[4]) __attribute__((always_inline)) {
+    AM_LANE_VARS;
+    if (k >= a.nchunks) {  // past the end of the launch: repeat the last group's loads, so that
+      k = a.nchunks - 1;   // every group issues the same loads and every wait count is fixed
+      gi = gpc - 1;
+    }
     const bool query = gi < nq;
     const int g = query ? gi : gi - nq;
-    const int64_t row = mT + (int64_t)k * a.C + (int64_t)g * GROWS + GR * s;
-    const uint16_t* xr0 = (query ? a.Q : a.K) + (row + l32) * D + 4 * hf;
+    const int rset = k * a.C + g * GROWS + GR * s;
+    const int vx = (l32 * D + 4 * hf) * 2;
+    const rsrc_t rx = query ? rQ : rK;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      px[ks] = cat2(*(const uint2*)(xr0 + 16 * ks), *(const uint2*)(xr0 + 16 * ks + 8));
+      px[ks] = cat2(buf_ld8(rx, vx + 32 * ks, rset * D * 2), buf_ld8(rx, vx + 32 * ks + 16, rset * D * 2));
   };
-  u32x4 px[4];
-  load_x(0, 0, px);
 
   bool bad = false;
-  for (int k = 0; k < a.nchunks; ++k) {
-    const int64_t s0 = (int64_t)k * a.C;
-    // partial gradients over this set's rows: gr[0] = G1^T tiles (d rows 0..31 / 32..63,
-    // h_own), gr[1] = G2 tiles (v rows 0..31 / 32..63, h_own)
-    f32x16 gr[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
-    for (int gi = 0; gi < gpc; ++gi) {
+  f32x16 gr[2][2];
+  // One row group: Z, H, Yh (queries: Y), then D2, D1 and the gradient accumulation (keys).
+  auto run_group = [&](int k, int gi, u32x4 (&px)[4]) __attribute__((always_inline)) {
+      AM_LANE_VARS;
+      const int vcol = 16 * w + (lane & 15);
       const bool query = gi < nq;
       const int g = query ? gi : gi - nq;
-      const int64_t row0 = mT + s0 + (int64_t)g * GROWS;  // token row of the group's first row
-      const int64_t rset = row0 + GR * s;                  // ... and of this set's first row
-      // this group's values and X^T words first: the next group's loads are issued after them,
-      // so waiting for these (loads return in order) never waits for the prefetch
-      u32x4 xt;
-      uint32_t vv[8];
-      if (!query) {
-        xt = *(const u32x4*)(a.K + (row0 + (t >> 3)) * D + (t & 7) * 8);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) vv[4 * rt + u] = a.V[(rset + 16 * rt + 4 * (lane >> 4) + u) * D + vcol];
-      }
-      u32x4 xa[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) xa[ks] = px[ks];
-      if (gi + 1 < gpc) load_x(k, gi + 1, px);
-      else load_x(k + 1, 0, px);
+      const int row0 = k * a.C + g * GROWS;  // the group's first row in this launch
+      const int rset = row0 + GR * s;        // ... and this set's first row
       // H of query groups alternates between regions B and A, so a query group never waits for
       // the previous one's readers; a key group writes H to B and D2 / X^T to A.  With an odd
       // number of query groups the last one used B, whose readers the first key group waits for.
       const int hb = (query && (gi & 1)) ? ra : rb;
       if (!query && gi == nq && (nq & 1)) __syncthreads();
+      // The group's X^T staging words and values (used by key groups after their first barrier),
+      // issued by every group so that the wait for px below always has nine younger loads.
+      const u32x4 xt = buf_ld16(rK, ((t >> 3) * D + (t & 7) * 8) * 2, row0 * D * 2);
+      uint32_t vv[8];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          vv[4 * rt + u] = buf_ld_u16(rV, (4 * (lane >> 4) * D + vcol) * 2 + u * D * 2, (rset + 16 * rt) * D * 2);
       // Z = X W1^T: this set's 32 rows, hidden units of this wave
       f32x16 z = zero16();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        z = mfma32(xa[ks], w1h[ks], z);
-        z = mfma32(xa[ks], w1l[ks], z);
+        z = mfma32(px[ks], w1h[ks], z);
+        z = mfma32(px[ks], w1l[ks], z);
       }
+      if (gi + 1 < gpc) load_x(k, gi + 1, px);
+      else load_x(k + 1, 0, px);
       f32x16 hz, zp;
       if (query) {
 #pragma unroll
@@ -425,15 +528,20 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
         yh[rt] = acc;
       }
       if (query) {
+        const int vy = 4 * (lane >> 4) * D + vcol;  // element offset of this lane's first output
+        if (a.out_bf16) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+          for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int64_t yo = (rset + 16 * rt + 4 * (lane >> 4) + u) * D + vcol;
-            if (a.out_bf16) ((uint16_t*)a.Y)[yo] = (uint16_t)bf16_bits(yh[rt][u]);
-            else ((float*)a.Y)[yo] = yh[rt][u];
-          }
-        continue;
+            for (int u = 0; u < 4; ++u)
+              buf_st_u16(rY, vy * 2 + u * D * 2, (rset + 16 * rt) * D * 2, bf16_bits(yh[rt][u]));
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) buf_st(rY, vy * 4 + u * D * 4, (rset + 16 * rt) * D * 4, yh[rt][u]);
+        }
+        return;
       }
       // D2 = 2 (Yh - V): to LDS as [row][v] (operand of D2 W2) and [v][row] (operand of D2^T H)
 #pragma unroll
@@ -497,12 +605,24 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
       }
       // No barrier here: the next group rewrites D2, D2^T and X^T only after its first barrier,
       // which every wave reaches after finishing these reads.
-    }
+  };
+
+  u32x4 px[4];
+  load_x(0, 0, px);
+  for (int k = 0; k < a.nchunks; ++k) {
+    // partial gradients over this set's rows: gr[0] = G1^T tiles (d rows 0..31 / 32..63,
+    // h_own), gr[1] = G2 tiles (v rows 0..31 / 32..63, h_own)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) gr[i][j] = zero16();
+    for (int gi = 0; gi < gpc; ++gi) run_group(k, gi, px);
 
     // Swap partial gradients: set 0 keeps G1 and passes its G2 partial, set 1 the reverse.
     // The slots were last read by the final group's H W2^T, before its second barrier.
     f32x16 x[2];
     {
+      AM_LANE_VARS;
       float* xg1 = (float*)(sm + opq(XG1));
       float* xg2 = (float*)(sm + opq(XG2));
       if (s == 0) {
@@ -533,49 +653,81 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
         }
     }
 
-    const int64_t gk = (int64_t)m * a.nchunks + k;
+    const int64_t gk = (int64_t)m * a.ld_gate + k;
     const float th = a.theta[gk], et = a.eta[gk], om = 1.0f - a.alpha[gk];
     const float* Wsrc = (k == 0) ? Win : Wout;
     const float* Ssrc = (k == 0) ? Sin : Sout;
+    // This set's state, loaded in quarters during the Newton-Schulz phase so that the loads
+    // complete under it: register r of tile tt holds the element of row 32tt + 8(r/4) + 4hf + r%4
+    // of G1^T (set 0: W1[h_own][d]) or of G2 (set 1: W2[v][h_own], kept transposed in T2 within
+    // a launch).  Buffer accesses: one per-lane byte offset, per-register offsets are constants.
+    const rsrc_t rt2 = make_rsrc(a.T2 + (int64_t)m * 2 * P2, (uint32_t)(2 * P2 * 4));
+    const rsrc_t rs = s ? rt2 : make_rsrc(Ssrc, (uint32_t)(P * 4));
+    const rsrc_t rw = s ? rt2 : make_rsrc(Wsrc, (uint32_t)(P * 4));
+    float sv[2][16], wv[2][16];
+    auto pre = [&](auto part) __attribute__((always_inline)) {
+      constexpr int tt = decltype(part)::value >> 1, q0 = 2 * (decltype(part)::value & 1);
+      AM_LANE_VARS;
+      const int vo1 = (h_own * D + 4 * hf) * 4;  // W1[h_own][4hf], W2^T[h_own][4hf]
+      const int vs = vo1 + (s ? P2 * 4 : 0);
+#pragma unroll
+      for (int q = q0; q < q0 + 2; ++q) {
+        const float4 so = buf_ld4(rs, vs, (32 * tt + 8 * q) * 4);
+        const float4 wo = buf_ld4(rw, vo1, (32 * tt + 8 * q) * 4);
+        sv[tt][4 * q] = so.x; sv[tt][4 * q + 1] = so.y; sv[tt][4 * q + 2] = so.z; sv[tt][4 * q + 3] = so.w;
+        wv[tt][4 * q] = wo.x; wv[tt][4 * q + 1] = wo.y; wv[tt][4 * q + 2] = wo.z; wv[tt][4 * q + 3] = wo.w;
+      }
+    };
 
     {
+      AM_LANE_VARS;
       const int bxh = opq(NX + s * NXS), bah = opq(NA + s * NAS), bbh = opq(NB + s * NBS);
-      newton_schulz1(x, sm, bxh, bxh + 64 * LH, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red + 4 * s, a, lane, w);
+      newton_schulz1(x, sm, bxh, bxh + HD * 64, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red + 4 * s, a, lane, w,
+                     pre);
     }
-    // Update of this set's matrix; state addressed as 32-bit offsets from the memory's base.
+    // S = eta S - theta NS(G), W = (1 - alpha) W + S for this set's matrix
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float sn = et * sv[tt][r] - th * x[tt][r];
+        const float wn = om * wv[tt][r] + sn;
+        sv[tt][r] = sn;
+        x[tt][r] = wn;
+        bad |= !(isfinite(sn) && isfinite(wn));
+      }
     // The weight copies overwrite the Newton-Schulz X buffers, which nobody reads after the
     // last iteration's second barrier; the W1 handoff overwrites the A buffers, dead after its
     // third.
     u32x4* ho = (u32x4*)(sm + opq(HOFF));
+    {
+    AM_LANE_VARS;
+    const rsrc_t rs_out = make_rsrc(Sout, (uint32_t)(P * 4)), rw_out = make_rsrc(Wout, (uint32_t)(P * 4));
+    const bool last = k + 1 == a.nchunks;
+    const int wo1 = (h_own * D + 4 * hf) * 4, wo2 = ((int)P1 + 4 * hf * HD + h_own) * 4;
+    if (s == 0 || !last) {
+      const rsrc_t rs = s ? rt2 : rs_out, rw = s ? rt2 : rw_out;
+      const int vs = wo1 + (s ? P2 * 4 : 0);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          buf_st4(rs, vs, (32 * tt + 8 * q) * 4,
+                  float4{sv[tt][4 * q], sv[tt][4 * q + 1], sv[tt][4 * q + 2], sv[tt][4 * q + 3]});
+          buf_st4(rw, wo1, (32 * tt + 8 * q) * 4,
+                  float4{x[tt][4 * q], x[tt][4 * q + 1], x[tt][4 * q + 2], x[tt][4 * q + 3]});
+        }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int so = (32 * tt + 8 * (r >> 2) + (r & 3)) * HD * 4;
+          buf_st(rs_out, wo2, so, sv[tt][r]);
+          buf_st(rw_out, wo2, so, x[tt][r]);
+        }
+    }
     if (s == 0) {
-      // W1: G1^T tile element (d, h_own) <-> W1[h_own][d]
-      const int o1 = opv(h_own * D + 4 * hf);
-      float4 so1[2][4], wo1[2][4];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          so1[tt][q] = *(const float4*)(Ssrc + o1 + 32 * tt + 8 * q);
-          wo1[tt][q] = *(const float4*)(Wsrc + o1 + 32 * tt + 8 * q);
-        }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 so = so1[tt][q];
-          const float4 wo = wo1[tt][q];
-          const float sv[4] = {so.x, so.y, so.z, so.w}, wv[4] = {wo.x, wo.y, wo.z, wo.w};
-          float sn[4], wn[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            sn[u] = et * sv[u] - th * x[tt][4 * q + u];
-            wn[u] = om * wv[u] + sn[u];
-            x[tt][4 * q + u] = wn[u];
-            bad |= !(isfinite(sn[u]) && isfinite(wn[u]));
-          }
-          *(float4*)(Sout + o1 + 32 * tt + 8 * q) = float4{sn[0], sn[1], sn[2], sn[3]};
-          *(float4*)(Wout + o1 + 32 * tt + 8 * q) = float4{wn[0], wn[1], wn[2], wn[3]};
-        }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         u32x4 wh, wl;
@@ -584,29 +736,6 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
         ho[(w * 8 + 4 + ks) * 64 + lane] = wl;
       }
     } else {
-      // W2: G2 tile element (v, h_own) <-> W2[v][h_own]
-      const int o2 = opv((int)P1 + 4 * hf * HD + h_own);
-      float so2[2][16], wo2[2][16];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ov = o2 + (32 * tt + 8 * (r >> 2) + (r & 3)) * HD;
-          so2[tt][r] = Ssrc[ov];
-          wo2[tt][r] = Wsrc[ov];
-        }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ov = o2 + (32 * tt + 8 * (r >> 2) + (r & 3)) * HD;
-          const float sn = et * so2[tt][r] - th * x[tt][r];
-          const float wn = om * wo2[tt][r] + sn;
-          Sout[ov] = sn;
-          Wout[ov] = wn;
-          x[tt][r] = wn;
-          bad |= !(isfinite(sn) && isfinite(wn));
-        }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         u32x4 wh, wl;
@@ -615,16 +744,21 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
         store_rows_T(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
       }
     }
+    }
     __syncthreads();
     // both sets take the new W1 slices from LDS (the registers then hold nothing across the
     // Newton-Schulz phase)
+    {
+      AM_LANE_VARS;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      w1h[ks] = ho[(w * 8 + ks) * 64 + lane];
-      w1l[ks] = ho[(w * 8 + 4 + ks) * 64 + lane];
+      for (int ks = 0; ks < 4; ++ks) {
+        w1h[ks] = ho[(w * 8 + ks) * 64 + lane];
+        w1l[ks] = ho[(w * 8 + 4 + ks) * 64 + lane];
+      }
     }
   }
   if (bad) a.flag[0] = 1;
+#undef AM_LANE_VARS
 }
 
 }  // namespace fz
@@ -638,34 +772,44 @@ bool fused_supported(const Dims& d) {
 atlasmem_status launch_fused(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
                              const float* eta, const float* alpha, int64_t T, void* Y, hipStream_t st) {
   const Dims& d = h->d;
-  fz::Args a;
-  a.K = (const uint16_t*)K;
-  a.Q = (const uint16_t*)Q;
-  a.V = (const uint16_t*)V;
-  a.theta = theta;
-  a.eta = eta;
-  a.alpha = alpha;
-  a.T = T;
-  a.C = d.C;
-  a.nchunks = (int)(T / d.C);
-  a.Win = h->W[h->cur];
-  a.Sin = h->S[h->cur];
-  a.Wout = h->W[1 - h->cur];
-  a.Sout = h->S[1 - h->cur];
-  a.Y = Y;
-  a.out_bf16 = d.out_bf16;
-  a.ns_steps = d.ns_steps;
-  a.ns_a = d.ns_a;
-  a.ns_b = d.ns_b;
-  a.ns_c = d.ns_c;
-  a.ns_eps = d.ns_eps;
-  a.flag = h->flag;
   if (hipFuncSetAttribute((const void*)fz::fused_ns_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                           fz::LDS_BYTES) != hipSuccess)
     return ATLASMEM_E_DEVICE;
-  hipLaunchKernelGGL(fz::fused_ns_kernel, dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
-  AM_LAUNCH_CHECK();
-  h->cur = 1 - h->cur;
+  // one launch per segment of at most 2^22 tokens, so that per-memory byte offsets fit 32 bits
+  const int64_t nchunks = T / d.C;
+  const int64_t seg = ((int64_t)1 << 22) / d.C;
+  const int ysz = d.out_bf16 ? 2 : 4;
+  for (int64_t c0 = 0; c0 < nchunks; c0 += seg) {
+    const int64_t nc = nchunks - c0 < seg ? nchunks - c0 : seg;
+    const int64_t t0 = c0 * d.C;
+    fz::Args a;
+    a.K = (const uint16_t*)K + t0 * fz::D;
+    a.Q = (const uint16_t*)Q + t0 * fz::D;
+    a.V = (const uint16_t*)V + t0 * fz::D;
+    a.theta = theta + c0;
+    a.eta = eta + c0;
+    a.alpha = alpha + c0;
+    a.ldT = T;
+    a.ld_gate = nchunks;
+    a.C = d.C;
+    a.nchunks = (int)nc;
+    a.Win = h->W[h->cur];
+    a.Sin = h->S[h->cur];
+    a.Wout = h->W[1 - h->cur];
+    a.Sout = h->S[1 - h->cur];
+    a.T2 = h->G;
+    a.Y = Y ? (void*)((char*)Y + t0 * fz::D * ysz) : nullptr;
+    a.out_bf16 = d.out_bf16;
+    a.ns_steps = d.ns_steps;
+    a.ns_a = d.ns_a;
+    a.ns_b = d.ns_b;
+    a.ns_c = d.ns_c;
+    a.ns_eps = d.ns_eps;
+    a.flag = h->flag;
+    hipLaunchKernelGGL(fz::fused_ns_kernel, dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+    AM_LAUNCH_CHECK();
+    h->cur = 1 - h->cur;
+  }
   return ATLASMEM_OK;
 }
 
