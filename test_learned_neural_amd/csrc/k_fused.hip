@@ -58,8 +58,9 @@ constexpr int LR = GROWS + 4;   // [*][64 rows], 8-byte row reads (136 B)
 // Weights: W2 [v][h] (B operand of H W2^T) and W2^T [h][v] (B operand of D2 W2), hi and lo.
 constexpr int W2H = 0, W2L = W2H + 64 * LH;
 constexpr int WTH = W2L + 64 * LH, WTL = WTH + HD * LE;
-// Group buffers: region A holds D2 [row][v], D2^T [v][row] and X^T [d][row] of a key group, or
-// the H of every second query group; region B holds H [row][h] (hi, then lo).
+// Group buffers: region A holds D2 [row][v], D2^T [v][row] and X^T [d][row] of the key rows,
+// region B their H [row][h] (hi, then lo), HQ the H of the query rows (where W2 [v][h] would be:
+// H W2^T reads W2 from W2^T).
 constexpr int RA = WTL + HD * LE;
 constexpr int D2H = RA, D2L = D2H + GROWS * LE;
 constexpr int DTH = D2L + GROWS * LE, DTL = DTH + D * LR;
@@ -68,7 +69,8 @@ constexpr int RA_END = XTH + D * LR;
 constexpr int HSZ = GROWS * LH;                  // one of H hi / H lo
 constexpr int RB = RA_END;
 constexpr int GEND = RB + 2 * HSZ;
-static_assert(RA_END - RA >= 2 * HSZ, "region A must also hold an H");
+constexpr int HQ = 0;
+static_assert(HQ + 2 * HSZ <= WTH, "query H below W2^T");
 // Newton-Schulz phase, matrix j (set j): X^T [col][row] hi/lo (128 x 64, rows of 128 bytes, 8-byte
 // chunks swizzled), A and B [64][64] hi/lo.  The X buffers lie under the weight copies, which
 // the update rewrites after the last read of X.
@@ -378,7 +380,7 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
   // at most 2^22 tokens)
   const int nT = a.nchunks * a.C;
   const rsrc_t rK = make_rsrc(a.K + (int64_t)m * a.ldT * D, (uint32_t)nT * D * 2);
-  const rsrc_t rQ = make_rsrc(a.Q + (int64_t)m * a.ldT * D, (uint32_t)nT * D * 2);
+  const rsrc_t rQ = (a.Y && a.Q) ? make_rsrc(a.Q + (int64_t)m * a.ldT * D, (uint32_t)nT * D * 2) : rK;
   const rsrc_t rV = make_rsrc(a.V + (int64_t)m * a.ldT * D, (uint32_t)nT * D * 2);
   const int ysz = a.out_bf16 ? 2 : 4;  // bytes per output element
   const rsrc_t rY = make_rsrc(a.Y ? (const char*)a.Y + (int64_t)m * a.ldT * D * ysz : nullptr,
@@ -387,9 +389,9 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
   const float* Sin = a.Sin + (int64_t)m * P;
   float* Wout = a.Wout + (int64_t)m * P;
   float* Sout = a.Sout + (int64_t)m * P;
-  const int w2h = opq(W2H), w2l = opq(W2L), wth = opq(WTH), wtl = opq(WTL);
+  const int wth = opq(WTH), wtl = opq(WTL);
   const int d2h = opq(D2H), d2l = opq(D2L), dth = opq(DTH), dtl = opq(DTL), xth = opq(XTH);
-  const int ra = opq(RA), rb = opq(RB);
+  const int rb = opq(RB);
 
   // register slice of W1[h_own][d] (B operand of X W1^T, k = d), four k-steps of 16, hi and lo
   u32x4 w1h[4], w1l[4];
@@ -404,13 +406,11 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
     v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
     pack8(v, w1h[ks], w1l[ks]);
   }
-  // W2 in LDS as [v][h] (for H W2^T) and [h][v] (for D2 W2)
+  // W2 in LDS as [h][v]: B operand of D2 W2 (direct reads) and of H W2^T (transposing reads)
   for (int e = t; e < D * HD; e += NT) {
     const int vv = e / HD, hh = e % HD;
     uint32_t hi, lo;
     split_bf16(Win[P1 + e], hi, lo);
-    sm[w2h + vv * LH + hh] = (uint16_t)hi;
-    sm[w2l + vv * LH + hh] = (uint16_t)lo;
     sm[wth + hh * LE + vv] = (uint16_t)hi;
     sm[wtl + hh * LE + vv] = (uint16_t)lo;
   }
@@ -437,178 +437,194 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
   }
   __syncthreads();
 
-  // The X operand of the next row group's X W1^T is loaded one group ahead (software
-  // pipelining); the group's values and X^T staging words are loaded at the group's start and
-  // used only after its first barrier.
+  // A chunk is processed in double groups: the query rows and the key rows [64g, 64g + 64)
+  // together (only the key rows when nothing is retrieved), so that the two X W1^T and H W2^T
+  // products run as independent chains between the same barriers.
   const int ngroups = a.C / GROWS;
-  const int nq = a.Y ? ngroups : 0;     // query groups come first in a chunk, then key groups
-  const int gpc = nq + ngroups;
-  // The X operand rows of a row group (this set's rows) are loaded by the previous group
-  // (software pipelining), right after its own X W1^T has consumed the registers they land in.
-  auto load_x = [&](int k, int gi, u32x4 (&px)[4]) __attribute__((always_inline)) {
+  const bool withq = a.Y != nullptr;
+  // The X operand rows of a double group (this set's rows) are loaded by the previous one
+  // (software pipelining), right after its own X W1^T has consumed the registers they land in;
+  // the query operand is loaded (from the key rows when nothing is retrieved) in every case, so
+  // that every wait for these loads has a fixed count of younger loads.
+  auto load_x = [&](int k, int g, u32x4 (&pq)[4], u32x4 (&pk)[4]) __attribute__((always_inline)) {
     AM_LANE_VARS;
-    if (k >= a.nchunks) {  // past the end of the launch: repeat the last group's loads, so that
-      k = a.nchunks - 1;   // every group issues the same loads and every wait count is fixed
-      gi = gpc - 1;
+    if (k >= a.nchunks) {  // past the end of the launch: repeat the last group's loads
+      k = a.nchunks - 1;
+      g = ngroups - 1;
     }
-    const bool query = gi < nq;
-    const int g = query ? gi : gi - nq;
-    const int rset = k * a.C + g * GROWS + GR * s;
+    const int rset = (k * a.C + g * GROWS + GR * s) * D * 2;
     const int vx = (l32 * D + 4 * hf) * 2;
-    const rsrc_t rx = query ? rQ : rK;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      px[ks] = cat2(buf_ld8(rx, vx + 32 * ks, rset * D * 2), buf_ld8(rx, vx + 32 * ks + 16, rset * D * 2));
+      pk[ks] = cat2(buf_ld8(rK, vx + 32 * ks, rset), buf_ld8(rK, vx + 32 * ks + 16, rset));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      pq[ks] = cat2(buf_ld8(rQ, vx + 32 * ks, rset), buf_ld8(rQ, vx + 32 * ks + 16, rset));
   };
 
   bool bad = false;
   f32x16 gr[2][2];
-  // One row group: Z, H, Yh (queries: Y), then D2, D1 and the gradient accumulation (keys).
-  auto run_group = [&](int k, int gi, u32x4 (&px)[4]) __attribute__((always_inline)) {
-      AM_LANE_VARS;
-      const int vcol = 16 * w + (lane & 15);
-      const bool query = gi < nq;
-      const int g = query ? gi : gi - nq;
-      const int row0 = k * a.C + g * GROWS;  // the group's first row in this launch
-      const int rset = row0 + GR * s;        // ... and this set's first row
-      // H of query groups alternates between regions B and A, so a query group never waits for
-      // the previous one's readers; a key group writes H to B and D2 / X^T to A.  With an odd
-      // number of query groups the last one used B, whose readers the first key group waits for.
-      const int hb = (query && (gi & 1)) ? ra : rb;
-      if (!query && gi == nq && (nq & 1)) __syncthreads();
-      // The group's X^T staging words and values (used by key groups after their first barrier),
-      // issued by every group so that the wait for px below always has nine younger loads.
-      const u32x4 xt = buf_ld16(rK, ((t >> 3) * D + (t & 7) * 8) * 2, row0 * D * 2);
-      uint32_t vv[8];
+  const int hq = opq(HQ);
+  // One double group: Z, H and Yh of queries and keys, Y of the queries, then D2, D1 and the
+  // gradient accumulation of the keys.
+  auto run_group = [&](int k, int g, u32x4 (&pq)[4], u32x4 (&pk)[4]) __attribute__((always_inline)) {
+    AM_LANE_VARS;
+    const int vcol = 16 * w + (lane & 15);
+    const int row0 = k * a.C + g * GROWS;  // the group's first row in this launch
+    const int rset = row0 + GR * s;        // ... and this set's first row
+    // the key rows' X^T staging words and values, used after the first barrier (issued before
+    // the X operands are consumed: the wait for those then has exactly nine younger loads)
+    const u32x4 xt = buf_ld16(rK, ((t >> 3) * D + (t & 7) * 8) * 2, row0 * D * 2);
+    uint32_t vv[8];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          vv[4 * rt + u] = buf_ld_u16(rV, (4 * (lane >> 4) * D + vcol) * 2 + u * D * 2, (rset + 16 * rt) * D * 2);
-      // Z = X W1^T: this set's 32 rows, hidden units of this wave
-      f32x16 z = zero16();
+      for (int u = 0; u < 4; ++u)
+        vv[4 * rt + u] = buf_ld_u16(rV, (4 * (lane >> 4) * D + vcol) * 2 + u * D * 2, (rset + 16 * rt) * D * 2);
+    // Z = X W1^T of keys and queries: this set's 32 rows, hidden units of this wave
+    f32x16 zk = zero16(), zq = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      zk = mfma32(pk[ks], w1h[ks], zk);
+      zk = mfma32(pk[ks], w1l[ks], zk);
+    }
+    if (withq) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        z = mfma32(px[ks], w1h[ks], z);
-        z = mfma32(px[ks], w1l[ks], z);
+        zq = mfma32(pq[ks], w1h[ks], zq);
+        zq = mfma32(pq[ks], w1l[ks], zq);
       }
-      if (gi + 1 < gpc) load_x(k, gi + 1, px);
-      else load_x(k + 1, 0, px);
-      f32x16 hz, zp;
-      if (query) {
+    }
+    if (g + 1 < ngroups) load_x(k, g + 1, pq, pk);
+    else load_x(k + 1, 0, pq, pk);
+    // H = silu(Z) to LDS (keys: region B, queries: HQ), silu'(Z) of the keys kept for D1
+    f32x16 hz, zp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) hz[r] = z[r] * sigmoidf_(z[r]);
+    for (int r = 0; r < 16; ++r) {
+      const float sg = sigmoidf_(zk[r]);
+      hz[r] = zk[r] * sg;
+      zp[r] = sg * (1.0f + zk[r] * (1.0f - sg));
+    }
+    u32x4 hph[2], hpl[2];  // hi/lo words of the keys' H, k-steps over the set's rows
+#pragma unroll
+    for (int kl = 0; kl < 2; ++kl) {
+      tile_op(hz, kl, hph[kl], hpl[kl]);
+      store_rows(sm, rb, rb + HSZ, LH, hph[kl], hpl[kl], GR * s + 16 * kl, h_own, hf);
+    }
+    if (withq) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hz[r] = zq[r] * sigmoidf_(zq[r]);
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl) {
+        u32x4 qh, ql;
+        tile_op(hz, kl, qh, ql);
+        store_rows(sm, hq, hq + HSZ, LH, qh, ql, GR * s + 16 * kl, h_own, hf);
+      }
+    }
+    __syncthreads();
+    // Yh = H W2^T: 16x16 tiles, wave w owns values [16w, 16w+16), both row halves of the set;
+    // the B operand (k = h, n = v) comes from W2^T [h][v] by transposing reads: lane 4e + q of
+    // 16-lane group g names row 32ks + 8g + e (+4), columns 16w + 4q .. +3
+    f32x4 yk[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 yq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      const int ob = ((lane >> 4) * 8 + ((lane >> 2) & 3)) * LE + 16 * w + 4 * (lane & 3);
+#pragma unroll
+      for (int ks = 0; ks < HD / 32; ++ks) {
+        const int o1 = ob + 32 * ks * LE, o2 = o1 + 4 * LE;
+        const u32x4 bh = cat2(lds_tr16(sm + wth + o1), lds_tr16(sm + wth + o2));
+        const u32x4 bl = cat2(lds_tr16(sm + wtl + o1), lds_tr16(sm + wtl + o2));
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const int oa = (GR * s + 16 * rt + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
+          yk[rt] = mma3_16(lds16(sm, rb + oa), lds16(sm, rb + HSZ + oa), bh, bl, yk[rt]);
+          if (withq) yq[rt] = mma3_16(lds16(sm, hq + oa), lds16(sm, hq + HSZ + oa), bh, bl, yq[rt]);
+        }
+      }
+    }
+    // D2 = 2 (Yh - V): to LDS as [row][v] (operand of D2 W2) and [v][row] (operand of D2^T H)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int rr = GR * s + 16 * rt + 4 * (lane >> 4);
+      float d2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) d2[u] = 2.0f * (yk[rt][u] - bf16_value(vv[4 * rt + u]));
+      uint32_t h0, l0, h1, l1;
+      split2(d2[0], d2[1], h0, l0);
+      split2(d2[2], d2[3], h1, l1);
+      const uint32_t hh[4] = {h0 & 0xFFFFu, h0 >> 16, h1 & 0xFFFFu, h1 >> 16};
+      const uint32_t ll[4] = {l0 & 0xFFFFu, l0 >> 16, l1 & 0xFFFFu, l1 >> 16};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sm[d2h + (rr + u) * LE + vcol] = (uint16_t)hh[u];
+        sm[d2l + (rr + u) * LE + vcol] = (uint16_t)ll[u];
+      }
+      *(uint2*)(sm + dth + vcol * LR + rr) = uint2{h0, h1};
+      *(uint2*)(sm + dtl + vcol * LR + rr) = uint2{l0, l1};
+    }
+    {  // X^T of the group for the G1 product
+      const int r = t >> 3, d0 = (t & 7) * 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sm[xth + (d0 + 2 * i) * LR + r] = (uint16_t)(xt[i] & 0xFFFFu);
+        sm[xth + (d0 + 2 * i + 1) * LR + r] = (uint16_t)(xt[i] >> 16);
+      }
+    }
+    // Y of the queries (after the loads above have been waited for)
+    if (withq) {
+      const int vy = 4 * (lane >> 4) * D + vcol;  // element offset of this lane's first output
+      if (a.out_bf16) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            buf_st_u16(rY, vy * 2 + u * D * 2, (rset + 16 * rt) * D * 2, bf16_bits(yq[rt][u]));
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float sg = sigmoidf_(z[r]);
-          hz[r] = z[r] * sg;
-          zp[r] = sg * (1.0f + z[r] * (1.0f - sg));
-        }
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) buf_st(rY, vy * 4 + u * D * 4, (rset + 16 * rt) * D * 4, yq[rt][u]);
       }
-      u32x4 hph[2], hpl[2];  // hi/lo words of H, k-steps over the set's rows
+    }
+    __syncthreads();
+    // Pm = D2 W2 (k = v), D1 = Pm * silu'(Z)
+    f32x16 p = zero16();
 #pragma unroll
-      for (int kl = 0; kl < 2; ++kl) {
-        tile_op(hz, kl, hph[kl], hpl[kl]);
-        store_rows(sm, hb, hb + HSZ, LH, hph[kl], hpl[kl], GR * s + 16 * kl, h_own, hf);
+    for (int ks = 0; ks < 4; ++ks) {
+      const int o0 = (GR * s + l32) * LE + 16 * ks + 4 * hf;
+      const u32x4 ah = cat2(lds8(sm, d2h + o0), lds8(sm, d2h + o0 + 8));
+      const u32x4 al = cat2(lds8(sm, d2l + o0), lds8(sm, d2l + o0 + 8));
+      const int ob = h_own * LE + 16 * ks + 4 * hf;
+      const u32x4 bh = cat2(lds8(sm, wth + ob), lds8(sm, wth + ob + 8));
+      const u32x4 bl = cat2(lds8(sm, wtl + ob), lds8(sm, wtl + ob + 8));
+      p = mma3(ah, al, bh, bl, p);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] *= zp[r];
+    // G1^T += X^T D1 and G2 += D2^T H (k = the set's rows, B operands from registers)
+#pragma unroll
+    for (int kl = 0; kl < 2; ++kl) {
+      u32x4 dh, dl;
+      tile_op(p, kl, dh, dl);
+      const u32x4 hh = hph[kl], hl = hpl[kl];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int o0 = (32 * tt + l32) * LR + GR * s + 16 * kl + 4 * hf;
+        const u32x4 xa = cat2(lds8(sm, xth + o0), lds8(sm, xth + o0 + 8));
+        gr[0][tt] = mfma32(xa, dh, gr[0][tt]);
+        gr[0][tt] = mfma32(xa, dl, gr[0][tt]);
+        const u32x4 ah = cat2(lds8(sm, dth + o0), lds8(sm, dth + o0 + 8));
+        const u32x4 al = cat2(lds8(sm, dtl + o0), lds8(sm, dtl + o0 + 8));
+        gr[1][tt] = mma3(ah, al, hh, hl, gr[1][tt]);
       }
-      __syncthreads();
-      // Yh = H W2^T: 16x16 tiles, wave w owns values [16w, 16w+16), both row halves of the set
-      f32x4 yh[2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < HD / 32; ++ks) {
-          const int oa = (GR * s + 16 * rt + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
-          const int ob = (16 * w + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
-          acc = mma3_16(lds16(sm, hb + oa), lds16(sm, hb + HSZ + oa), lds16(sm, w2h + ob), lds16(sm, w2l + ob),
-                        acc);
-        }
-        yh[rt] = acc;
-      }
-      if (query) {
-        const int vy = 4 * (lane >> 4) * D + vcol;  // element offset of this lane's first output
-        if (a.out_bf16) {
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              buf_st_u16(rY, vy * 2 + u * D * 2, (rset + 16 * rt) * D * 2, bf16_bits(yh[rt][u]));
-        } else {
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) buf_st(rY, vy * 4 + u * D * 4, (rset + 16 * rt) * D * 4, yh[rt][u]);
-        }
-        return;
-      }
-      // D2 = 2 (Yh - V): to LDS as [row][v] (operand of D2 W2) and [v][row] (operand of D2^T H)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int rr = GR * s + 16 * rt + 4 * (lane >> 4);
-        float d2[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) d2[u] = 2.0f * (yh[rt][u] - bf16_value(vv[4 * rt + u]));
-        uint32_t h0, l0, h1, l1;
-        split2(d2[0], d2[1], h0, l0);
-        split2(d2[2], d2[3], h1, l1);
-        const uint32_t hh[4] = {h0 & 0xFFFFu, h0 >> 16, h1 & 0xFFFFu, h1 >> 16};
-        const uint32_t ll[4] = {l0 & 0xFFFFu, l0 >> 16, l1 & 0xFFFFu, l1 >> 16};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          sm[d2h + (rr + u) * LE + vcol] = (uint16_t)hh[u];
-          sm[d2l + (rr + u) * LE + vcol] = (uint16_t)ll[u];
-        }
-        *(uint2*)(sm + dth + vcol * LR + rr) = uint2{h0, h1};
-        *(uint2*)(sm + dtl + vcol * LR + rr) = uint2{l0, l1};
-      }
-      {  // X^T of the group for the G1 product
-        const int r = t >> 3, d0 = (t & 7) * 8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sm[xth + (d0 + 2 * i) * LR + r] = (uint16_t)(xt[i] & 0xFFFFu);
-          sm[xth + (d0 + 2 * i + 1) * LR + r] = (uint16_t)(xt[i] >> 16);
-        }
-      }
-      __syncthreads();
-      // Pm = D2 W2 (k = v), D1 = Pm * silu'(Z)
-      f32x16 p = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int o0 = (GR * s + l32) * LE + 16 * ks + 4 * hf;
-        const u32x4 ah = cat2(lds8(sm, d2h + o0), lds8(sm, d2h + o0 + 8));
-        const u32x4 al = cat2(lds8(sm, d2l + o0), lds8(sm, d2l + o0 + 8));
-        const int ob = h_own * LE + 16 * ks + 4 * hf;
-        const u32x4 bh = cat2(lds8(sm, wth + ob), lds8(sm, wth + ob + 8));
-        const u32x4 bl = cat2(lds8(sm, wtl + ob), lds8(sm, wtl + ob + 8));
-        p = mma3(ah, al, bh, bl, p);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] *= zp[r];
-      // G1^T += X^T D1 and G2 += D2^T H (k = the set's rows, B operands from registers)
-#pragma unroll
-      for (int kl = 0; kl < 2; ++kl) {
-        u32x4 dh, dl;
-        tile_op(p, kl, dh, dl);
-        const u32x4 hh = hph[kl], hl = hpl[kl];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int o0 = (32 * tt + l32) * LR + GR * s + 16 * kl + 4 * hf;
-          const u32x4 xa = cat2(lds8(sm, xth + o0), lds8(sm, xth + o0 + 8));
-          gr[0][tt] = mfma32(xa, dh, gr[0][tt]);
-          gr[0][tt] = mfma32(xa, dl, gr[0][tt]);
-          const u32x4 ah = cat2(lds8(sm, dth + o0), lds8(sm, dth + o0 + 8));
-          const u32x4 al = cat2(lds8(sm, dtl + o0), lds8(sm, dtl + o0 + 8));
-          gr[1][tt] = mma3(ah, al, hh, hl, gr[1][tt]);
-        }
-      }
-      // No barrier here: the next group rewrites D2, D2^T and X^T only after its first barrier,
-      // which every wave reaches after finishing these reads.
+    }
+    // No barrier here: the next group writes H after its X W1^T (every wave is past this
+    // group's second barrier, so done with H W2^T) and D2, D2^T, X^T after its first barrier,
+    // which every wave reaches after finishing these reads.
   };
 
-  u32x4 px[4];
-  load_x(0, 0, px);
+  u32x4 pq[4], pk[4];
+  load_x(0, 0, pq, pk);
   for (int k = 0; k < a.nchunks; ++k) {
     // partial gradients over this set's rows: gr[0] = G1^T tiles (d rows 0..31 / 32..63,
     // h_own), gr[1] = G2 tiles (v rows 0..31 / 32..63, h_own)
@@ -616,7 +632,7 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) gr[i][j] = zero16();
-    for (int gi = 0; gi < gpc; ++gi) run_group(k, gi, px);
+    for (int g = 0; g < ngroups; ++g) run_group(k, g, pq, pk);
 
     // Swap partial gradients: set 0 keeps G1 and passes its G2 partial, set 1 the reverse.
     // The slots were last read by the final group's H W2^T, before its second barrier.
@@ -694,8 +710,16 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
         const float wn = om * wv[tt][r] + sn;
         sv[tt][r] = sn;
         x[tt][r] = wn;
-        bad |= !(isfinite(sn) && isfinite(wn));
       }
+    // A non-finite value never becomes finite again under the momentum, forgetting and
+    // Newton-Schulz steps (its row and column turn NaN or stay infinite), so checking the state
+    // after the last chunk of the launch flags every launch that produced one.
+    if (k + 1 == a.nchunks) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bad |= !(isfinite(sv[tt][r]) && isfinite(x[tt][r]));
+    }
     // The weight copies overwrite the Newton-Schulz X buffers, which nobody reads after the
     // last iteration's second barrier; the W1 handoff overwrites the A buffers, dead after its
     // third.
@@ -740,7 +764,6 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
       for (int ks = 0; ks < 4; ++ks) {
         u32x4 wh, wl;
         tile_op(x[ks >> 1], ks & 1, wh, wl);
-        store_rows(sm, w2h, w2l, LH, wh, wl, 16 * ks, h_own, hf);
         store_rows_T(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
       }
     }
