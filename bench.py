@@ -94,11 +94,14 @@ def event_ms(fn, iters, stream):
 
 
 def stage_rooflines(torch, am, synth, dev, stream):
-    """Stand-alone stages at the workloads' sizes, each against its own roofline: the gate scan,
-    Omega coefficients and feature map against HBM bandwidth (algorithmic bytes), Newton-Schulz
-    against the bf16 matrix peak (algorithmic FLOPs)."""
+    """Stand-alone stages, each against its own roofline: the gate scan, Omega coefficients and
+    feature map against HBM bandwidth (algorithmic bytes), Newton-Schulz against the bf16 matrix
+    peak (algorithmic FLOPs).  Sizes are large enough for the launch to be bandwidth- or
+    compute-bound (the per-chunk sizes inside a workload are far smaller): the scans over 256
+    memories x 32768 tokens in chunks of 64, the feature map over the Omega workload's 262144 keys
+    (width 32 -> 561), Newton-Schulz over 4096 gradient matrices of 128 x 64."""
     out = {}
-    M, T, C, c, d = 32, 8192, 64, 4, 32            # the Omega / feature-map workload's sizes
+    M, T, C, c, d = 256, 32768, 64, 4, 32
     th = torch.rand((M, T), device=dev)
     et = torch.rand((M, T), device=dev)
     al = torch.rand((M, T), device=dev)
@@ -109,20 +112,22 @@ def stage_rooflines(torch, am, synth, dev, stream):
     R = C + c - 1
     oW = torch.empty((M, T // C, R), device=dev)
     oS = torch.empty((M, T // C, R), device=dev)
-    X = torch.randn((M * T, d), device=dev).to(torch.bfloat16).view(torch.int16)
-    F = torch.empty((M * T, (d + 1) * (d + 2) // 2), device=dev)
-    G = torch.randn((256, 128, 64), device=dev)
+    NP = 262144
+    X = torch.randn((NP, d), device=dev).to(torch.bfloat16).view(torch.int16)
+    F = torch.empty((NP, (d + 1) * (d + 2) // 2), device=dev)
+    NM = 4096
+    G = torch.randn((NM, 128, 64), device=dev)
     Gout = torch.empty_like(G)
     cases = [
         ("gate_scan", lambda: am.gate_scan(th, et, al, M, T, C, cW, cS, sc),
          M * T * (12 + 8) + M * (T // C) * 12, "hbm", f"{M} memories x {T} tokens, chunk {C}"),
         ("omega_coeffs", lambda: am.omega_coeffs(cW, cS, ga, None, M, T, C, c, oW, oS),
          M * T * 12 + M * (T // C) * R * 8, "hbm", f"{M} memories x {T} tokens, chunk {C}, window {c}"),
-        ("poly_features", lambda: am.poly_features(X, synth.BF16, M * T, d, F),
-         M * T * (2 * d + 4 * F.shape[1]), "hbm", f"{M * T} bf16 vectors of width {d} -> {F.shape[1]} fp32"),
-        ("newton_schulz", lambda: am.newton_schulz(G, 256, 128, 64, 5, synth.NS_COEFFS, synth.NS_EPS,
+        ("poly_features", lambda: am.poly_features(X, synth.BF16, NP, d, F),
+         NP * (2 * d + 4 * F.shape[1]), "hbm", f"{NP} bf16 vectors of width {d} -> {F.shape[1]} fp32"),
+        ("newton_schulz", lambda: am.newton_schulz(G, NM, 128, 64, 5, synth.NS_COEFFS, synth.NS_EPS,
                                                    am.PREC_BF16X3, Gout),
-         256 * ns_flops_per_matrix(128, 64, 5), "mfma", "256 matrices 128x64, 5 steps, split bf16"),
+         NM * ns_flops_per_matrix(128, 64, 5), "mfma", f"{NM} matrices 128x64, 5 steps, split bf16"),
     ]
     for name, fn, work, bound, shape in cases:
         for _ in range(3):

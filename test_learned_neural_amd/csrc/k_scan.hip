@@ -163,40 +163,65 @@ atlasmem_status launch_history_update(const Handle* h, const void* K, const void
   return ATLASMEM_OK;
 }
 
-// Stand-alone feature map: rows of width d -> C(d+2, 2) fp32 features.  A block stages
-// kRows rows in LDS and writes their features with consecutive threads on consecutive
-// features (coalesced stores; the map is bound by the output bytes).
-constexpr int kPolyRows = 8;
+// Stand-alone feature map: rows of width d -> C(d+2, 2) fp32 features.  The map is bound by the
+// output bytes (C(d+2, 2) / (d / 2) times the input), so a block writes the contiguous feature
+// rows of kPolyRows input rows as one stream of 16-byte stores: each store's four features are
+// looked up in an LDS table of (i, j) index pairs built once per block (constant: both 0xFFFF,
+// linear x_i: j = 0xFFFF, quadratic x_i x_j / 2: both set).  For widths whose table does not fit
+// in LDS (TAB = false) the pair is recomputed per feature.
+constexpr int kPolyRows = 32;  // a multiple of 4: each block's output starts 16-byte aligned
+template <bool TAB>
 __global__ void __launch_bounds__(256) poly_kernel(const void* __restrict__ X, int in_bf16, int64_t n, int d,
                                                    float* __restrict__ F) {
-  extern __shared__ float xs[];  // [kPolyRows][d]
+  extern __shared__ float xs[];  // [kPolyRows][d] inputs, then the pair table [nf]
+  const int nf = poly_count(d);
+  uint32_t* tab = (uint32_t*)(xs + kPolyRows * d);
   const int64_t r0 = (int64_t)blockIdx.x * kPolyRows;
   const int nr = (int)((n - r0) < kPolyRows ? (n - r0) : kPolyRows);
   for (int e = threadIdx.x; e < nr * d; e += blockDim.x) xs[e] = load_in(X, r0 * d + e, in_bf16);
+  auto code_of = [&](int f) -> uint32_t {
+    if (f == 0) return 0xFFFFFFFFu;
+    if (f <= d) return 0xFFFF0000u | (uint32_t)(f - 1);
+    int i, j;
+    pair_of(f - 1 - d, d, i, j);
+    return ((uint32_t)j << 16) | (uint32_t)i;
+  };
+  if (TAB)
+    for (int f = threadIdx.x; f < nf; f += blockDim.x) tab[f] = code_of(f);
   __syncthreads();
-  const int nf = poly_count(d);
-  for (int rr = 0; rr < nr; ++rr) {
-    const float* x = xs + rr * d;
-    float* out = F + (r0 + rr) * nf;
-    for (int f = threadIdx.x; f < nf; f += blockDim.x) {
-      float v;
-      if (f == 0) v = 1.0f;
-      else if (f <= d) v = x[f - 1];
-      else {
-        int i, j;
-        pair_of(f - 1 - d, d, i, j);
-        v = 0.5f * (x[i] * x[j]);
-      }
-      out[f] = v;
-    }
+  auto feature = [&](int e) -> float {  // element e of the block's contiguous output
+    const int r = e / nf, f = e - r * nf;
+    const uint32_t code = TAB ? tab[f] : code_of(f);
+    const uint32_t i = code & 0xFFFFu, j = code >> 16;
+    const float* x = xs + r * d;
+    if (i == 0xFFFFu) return 1.0f;
+    if (j == 0xFFFFu) return x[i];
+    return 0.5f * (x[i] * x[j]);
+  };
+  float* out = F + r0 * nf;
+  const int total = nr * nf;
+  const int n4 = ((uintptr_t)out & 15) ? 0 : total >> 2;  // scalar stores for a misaligned F
+  for (int e4 = threadIdx.x; e4 < n4; e4 += blockDim.x) {
+    const int e = 4 * e4;
+    *(float4*)(out + e) = float4{feature(e), feature(e + 1), feature(e + 2), feature(e + 3)};
   }
+  for (int e = 4 * n4 + threadIdx.x; e < total; e += blockDim.x) out[e] = feature(e);
 }
 
 atlasmem_status launch_poly(const void* X, int in_bf16, int64_t n, int d, float* F, hipStream_t st) {
   if (n == 0) return ATLASMEM_OK;
   const int64_t blocks = (n + kPolyRows - 1) / kPolyRows;
-  hipLaunchKernelGGL(poly_kernel, dim3((unsigned)blocks), dim3(256), kPolyRows * d * sizeof(float), st, X, in_bf16, n,
-                     d, F);
+  const size_t lds_x = (size_t)kPolyRows * d * sizeof(float);
+  const size_t lds_t = lds_x + (size_t)(1 + d + (d * (d + 1)) / 2) * sizeof(uint32_t);
+  const bool tab = lds_t <= 64 * 1024;
+  const size_t lds = tab ? lds_t : lds_x;
+  const void* fn = tab ? (const void*)poly_kernel<true> : (const void*)poly_kernel<false>;
+  if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return ATLASMEM_E_DEVICE;
+  if (tab)
+    hipLaunchKernelGGL(poly_kernel<true>, dim3((unsigned)blocks), dim3(256), lds, st, X, in_bf16, n, d, F);
+  else
+    hipLaunchKernelGGL(poly_kernel<false>, dim3((unsigned)blocks), dim3(256), lds, st, X, in_bf16, n, d, F);
   AM_LAUNCH_CHECK();
   return ATLASMEM_OK;
 }

@@ -56,15 +56,21 @@ def test_omega_coeffs(T, C, c, hist):
         assert e < 1e-6
 
 
-@pytest.mark.parametrize("n,d,dtype", [(1000, 32, synth.BF16), (37, 5, synth.F32), (3, 1, synth.BF16),
-                                       (130, 64, synth.F32)])
-def test_poly_features_exact(n, d, dtype):
+@pytest.mark.parametrize("n,d,dtype,shift", [(1000, 32, synth.BF16, 0), (37, 5, synth.F32, 0), (3, 1, synth.BF16, 0),
+                                             (130, 64, synth.F32, 0), (45, 7, synth.F32, 1), (70, 200, synth.BF16, 0),
+                                             (33, 200, synth.F32, 3)],
+                         ids=["d32", "d5", "d1", "d64", "ragged_misaligned", "wide_no_table", "wide_misaligned"])
+def test_poly_features_exact(n, d, dtype, shift):
+    """The feature map against the oracle's, exact for bf16 inputs; also with an output that is not
+    16-byte aligned (shift floats into the buffer) and for widths whose pair table exceeds LDS."""
     import torch
     r = np.random.default_rng(n + d)
     x32 = r.normal(size=(n, d)).astype(np.float32)
     xin = synth.f32_to_bf16_bits(x32) if dtype == synth.BF16 else x32
     xv = synth.bf16_bits_to_f32(xin).astype(np.float64) if dtype == synth.BF16 else x32.astype(np.float64)
-    F = torch.empty((n, math.comb(d + 2, 2)), device=DEV)
+    nf = math.comb(d + 2, 2)
+    buf = torch.full((n * nf + shift,), float("nan"), device=DEV)
+    F = buf[shift:].view(n, nf)
     am.poly_features(to_dev(xin), dtype, n, d, F)
     ref = oracle.poly_features(xv, 2)
     got = F.cpu().numpy().astype(np.float64)
