@@ -125,20 +125,36 @@ const char* atlasmem_status_string(int status);
 atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, const float* S0,
                                 void* stream, atlasmem_handle* out);
 
-/* Consumes T tokens of every memory: for each chunk, writes the chunk's retrieved rows
- * Y = M_{W_start}(phi(Q)) and advances (W, S) by the chunk's update.  T must be a multiple
- * of cfg.chunk (else E_SHAPE); T = 0 is a no-op.  The window history (last c - 1 keys,
- * values and gammas) and the state carry over to the next call, so one call over T tokens
- * equals consecutive calls over T1 + T2 tokens (T1 a multiple of the chunk).
+/* Consumes T >= 0 tokens of every memory.  Tokens are grouped into chunks of cfg.chunk in
+ * stream order across calls (titans-pytorch-mlx README, Core Equations, Eq. 12-14 with the
+ * gradients of a chunk at its start weights; ATLAS summary, section 3.3): every token's
+ * retrieved row Y = M_{W_start}(phi(Q)) uses the weights at the start of its chunk, and (W, S)
+ * advance each time a chunk is complete.  The tokens of an unfinished chunk are buffered by the
+ * handle (their Y is written by this call), so the result does not depend on how a sequence is
+ * cut into calls: token-by-token decoding equals one call over the whole sequence.  A final
+ * partial chunk is applied by atlasmem_flush.  The window history (last c - 1 keys, values and
+ * gammas) carries over likewise.
  *   K, Q:  [M, T, d_key]   input_dtype
  *   V:     [M, T, d_value] input_dtype
- *   theta, eta, alpha: fp32 [M, T] (PER_TOKEN) or [M, T / chunk] (PER_CHUNK)
+ *   theta, eta, alpha: fp32 [M, T] (PER_TOKEN), or [M, n] (PER_CHUNK) with n the number of
+ *          chunks this call completes, (pending + T) / chunk; may be NULL when n = 0
  *   gamma: fp32 [M, T] for omega_window > 1, must be NULL for omega_window == 1
  *   Y:     [M, T, d_value] output_dtype, or NULL to skip retrieval
  * Never allocates. */
 atlasmem_status atlasmem_update_chunked(atlasmem_handle h, const void* K, const void* Q, const void* V,
                                         const float* theta, const float* eta, const float* alpha,
                                         const float* gamma, int64_t T, void* Y, void* stream);
+
+/* Applies the buffered tokens of an unfinished chunk (r = atlasmem_pending(h) > 0 of them) as
+ * one final chunk of r tokens, e.g. at the end of a sequence; no-op when none are buffered.
+ *   theta, eta, alpha: PER_CHUNK: fp32 [M, 1], the gates of that chunk; PER_TOKEN: ignored (the
+ *   buffered per-token gates are used), may be NULL.
+ * Never allocates. */
+atlasmem_status atlasmem_flush(atlasmem_handle h, const float* theta, const float* eta, const float* alpha,
+                               void* stream);
+
+/* Tokens of the unfinished chunk buffered by the handle (0 .. chunk - 1); -1 for NULL. */
+int64_t atlasmem_pending(atlasmem_handle h);
 
 /* Retrieval with no update (titans-torch 0.1.2, forward(): inference without updating the
  * memory): Y[m, t] = M_W(phi(Q[m, t])) with the current weights, for T >= 0 tokens.
@@ -152,10 +168,11 @@ atlasmem_status atlasmem_retrieve(atlasmem_handle h, const void* Q, int64_t T, v
 atlasmem_status atlasmem_get_state(atlasmem_handle h, float* W, float* S, void* stream);
 
 /* Replaces the weights / momentum ([M, P] fp32 device arrays; NULL = zeros) and clears the
- * non-finite flag.  The window history is left as it is. */
+ * non-finite flag.  The window history and any buffered tokens are left as they are. */
 atlasmem_status atlasmem_set_state(atlasmem_handle h, const float* W, const float* S, void* stream);
 
-/* Forgets the window history (start of a new sequence).  State is unchanged. */
+/* Forgets the window history and any buffered tokens of an unfinished chunk (start of a new
+ * sequence).  State is unchanged. */
 atlasmem_status atlasmem_reset_history(atlasmem_handle h, void* stream);
 
 /* Waits for the handle's work and frees everything it owns.  NULL is a no-op. */

@@ -27,7 +27,7 @@ def run_inputs(inputs, mems=None, T=None, processes: int = 1):
     cfg = config_from(s)
     mems = list(range(s.n_mem)) if mems is None else list(mems)
     T = s.T if T is None else T
-    ng = T if s.gate_mode == PER_TOKEN else T // s.chunk
+    ng = T if s.gate_mode == PER_TOKEN else -(-T // s.chunk)
     K = inputs.values("K", mems)[:, :T]
     Q = inputs.values("Q", mems)[:, :T]
     V = inputs.values("V", mems)[:, :T]

@@ -172,10 +172,13 @@ class MemoryResult:
 
 def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, gamma=None,
                history=None, keep_boundaries: bool = False) -> MemoryResult:
-    """The literal recurrence for one memory over T tokens (T a multiple of the chunk).
+    """The literal recurrence for one memory over T tokens, in chunks of cfg.chunk tokens; when T
+    is not a multiple of the chunk, the last chunk holds the remaining T mod chunk tokens (a
+    sequence's final partial chunk: its gradients are taken at its own start weights, like any
+    chunk's).
 
     params / momenta: weight and momentum matrices at the start of the call.
-    K, Q: [T, d_key]; V: [T, d_value]; theta/eta/alpha: [T] (per token) or [T / chunk]
+    K, Q: [T, d_key]; V: [T, d_value]; theta/eta/alpha: [T] (per token) or [ceil(T / chunk)]
     (per chunk); gamma: [T] (used only when the window is > 1).
     history: the previous call's last (window - 1) tokens as (phi(k), v, gamma); empty at the
     start of a sequence, where the window is clipped.
@@ -185,8 +188,6 @@ def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, g
     T = int(K.shape[0])
     C = cfg.chunk
     c = cfg.omega_window
-    if T % C != 0:
-        raise ValueError("T must be a multiple of the chunk")
     X = poly_features(K, cfg.poly_degree)
     Xq = poly_features(Q, cfg.poly_degree)
     V = np.asarray(V, dtype=np.float64)
@@ -203,10 +204,11 @@ def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, g
     bounds = []
     health = []
     for s in range(0, T, C):
+        e = min(s + C, T)                                  # the chunk is tokens [s, e)
         if keep_boundaries:
             bounds.append(([w.copy() for w in W], [m.copy() for m in S]))
         w_bar = [w.copy() for w in W]                     # chunk-start weights
-        for t in range(s, s + C):                          # retrieval at the chunk-start weights
+        for t in range(s, e):                              # retrieval at the chunk-start weights
             Y[t] = memory_apply(w_bar, Xq[t])
         if cfg.gate_mode == PER_TOKEN:
             cache = {}
@@ -217,7 +219,7 @@ def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, g
                     cache[i] = None if tok is None else (loss_grad(w_bar, tok[0], tok[1]), tok[2])
                 return cache[i]
 
-            for t in range(s, s + C):
+            for t in range(s, e):
                 G = [np.zeros_like(w) for w in W]
                 for i in range(t - c + 1, t + 1):
                     gi = grad_at(i)
@@ -231,7 +233,7 @@ def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, g
                     W[m] = (1.0 - alpha[t]) * W[m] + S[m]
         else:
             G = [np.zeros_like(w) for w in W]
-            for t in range(s, s + C):
+            for t in range(s, e):
                 for G_m, g_m in zip(G, loss_grad(w_bar, X[t], V[t])):
                     G_m += g_m
             if cfg.ns_steps > 0:

@@ -24,7 +24,8 @@ ABI_VERSION = 1
 
 EXPORTS = (
     "atlasmem_abi_version", "atlasmem_status_string", "atlasmem_param_count", "atlasmem_create",
-    "atlasmem_update_chunked", "atlasmem_retrieve", "atlasmem_get_state", "atlasmem_set_state",
+    "atlasmem_update_chunked", "atlasmem_flush", "atlasmem_pending", "atlasmem_retrieve", "atlasmem_get_state",
+    "atlasmem_set_state",
     "atlasmem_reset_history", "atlasmem_destroy", "atlasmem_gate_scan", "atlasmem_omega_coeffs",
     "atlasmem_poly_features", "atlasmem_newton_schulz",
 )
@@ -69,6 +70,8 @@ def load():
         "atlasmem_param_count": ([ctypes.POINTER(Config)], _i64),
         "atlasmem_create": ([ctypes.POINTER(Config), _vp, _vp, _vp, ctypes.POINTER(_vp)], ctypes.c_int),
         "atlasmem_update_chunked": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp], ctypes.c_int),
+        "atlasmem_flush": ([_vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+        "atlasmem_pending": ([_vp], _i64),
         "atlasmem_retrieve": ([_vp, _vp, _i64, _vp, _vp], ctypes.c_int),
         "atlasmem_get_state": ([_vp, _vp, _vp, _vp], ctypes.c_int),
         "atlasmem_set_state": ([_vp, _vp, _vp, _vp], ctypes.c_int),
@@ -147,6 +150,13 @@ class Memory:
         _check(load().atlasmem_update_chunked(self._h, _ptr(K), _ptr(Q), _ptr(V), _ptr(theta), _ptr(eta),
                                               _ptr(alpha), _ptr(gamma), int(T), _ptr(Y), _stream(stream)),
                "atlasmem_update_chunked")
+
+    def flush(self, theta=None, eta=None, alpha=None, stream=None):
+        _check(load().atlasmem_flush(self._h, _ptr(theta), _ptr(eta), _ptr(alpha), _stream(stream)), "atlasmem_flush")
+
+    @property
+    def pending(self) -> int:
+        return int(load().atlasmem_pending(self._h))
 
     def retrieve(self, Q, T: int, Y, stream=None):
         _check(load().atlasmem_retrieve(self._h, _ptr(Q), int(T), _ptr(Y), _stream(stream)), "atlasmem_retrieve")

@@ -164,6 +164,11 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
     ohg[i] = cv.take(sizeof(float) * M * H);
   }
   const size_t oflag = cv.take(256);
+  // the tokens of an unfinished chunk (streaming calls)
+  const size_t esz = d.in_bf16 ? 2 : 4;
+  const size_t opK = cv.take(esz * M * d.C * d.dk), opV = cv.take(esz * M * d.C * d.dv);
+  const size_t opg = cv.take(sizeof(float) * M * d.C), opth = cv.take(sizeof(float) * M * d.C);
+  const size_t opet = cv.take(sizeof(float) * M * d.C), opal = cv.take(sizeof(float) * M * d.C);
   const size_t state_end = cv.off;
   size_t oZ = 0, oD2 = 0, oD1 = 0, ocW = 0, ocS = 0, ooW = 0, ooS = 0, oscal = 0, oG = 0, oZr = 0;
   if (d.kind == ATLASMEM_MLP2_SILU) {
@@ -204,6 +209,13 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
     h->hg[i] = (float*)(base + ohg[i]);
   }
   h->flag = (int*)(base + oflag);
+  h->pK = base + opK;
+  h->pV = base + opV;
+  h->pg = (float*)(base + opg);
+  h->pth = (float*)(base + opth);
+  h->pet = (float*)(base + opet);
+  h->pal = (float*)(base + opal);
+  h->pending = 0;
   if (d.kind == ATLASMEM_MLP2_SILU) {
     h->Z = (float*)(base + oZ);
     h->D2 = (float*)(base + oD2);
@@ -233,29 +245,160 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
   return ATLASMEM_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// One launch sequence of the update over sp.T tokens (a multiple of d.C), then the window
+// history of those tokens.
+atlasmem_status run_update(Handle* h, const Dims& d, const void* K, const void* Q, const void* V, const float* theta,
+                           const float* eta, const float* alpha, const float* gamma, const Span& sp, void* Y,
+                           hipStream_t st) {
+  if (sp.T == 0) return ATLASMEM_OK;
+  if (d.kind == ATLASMEM_MLP2_SILU) return mlp_update(h, d, K, Q, V, theta, eta, alpha, gamma, sp, Y, st);
+  atlasmem_status s = launch_linear_update(h, d, K, Q, V, theta, eta, alpha, gamma, sp, Y, st);
+  if (s != ATLASMEM_OK) return s;
+  if (d.c > 1) {
+    s = launch_history_update(h, K, V, gamma, sp.T, sp.ld, st);
+    if (s != ATLASMEM_OK) return s;
+    h->hcur = 1 - h->hcur;
+  }
+  return ATLASMEM_OK;
+}
+
+atlasmem_status retrieve_rows(Handle* h, const void* Q, int64_t T, int64_t ld, void* Y, hipStream_t st) {
+  if (T == 0) return ATLASMEM_OK;
+  if (h->d.kind == ATLASMEM_LINEAR) return launch_linear_retrieve(h, Q, T, ld, Y, st);
+  return mlp_retrieve(h, Q, T, ld, Y, st);
+}
+
+// Copies tokens [0, n) of every memory of a row array (token stride ld, `row` bytes per token)
+// to rows [r0, r0 + n) of the matching pending buffer.
+bool to_pending(void* dst, const void* src, int64_t ld, int64_t r0, int64_t n, size_t row, const Dims& d,
+                hipStream_t st) {
+  if (n == 0 || !src) return true;
+  return hipMemcpy2DAsync((char*)dst + r0 * row, (size_t)d.C * row, src, (size_t)ld * row, (size_t)n * row, d.M,
+                          hipMemcpyDeviceToDevice, st) == hipSuccess;
+}
+
+bool append_pending(Handle* h, const void* K, const void* V, const float* theta, const float* eta, const float* alpha,
+                    const float* gamma, int64_t ld, int64_t n, hipStream_t st) {
+  const Dims& d = h->d;
+  const size_t esz = d.in_bf16 ? 2 : 4;
+  const int64_t r0 = h->pending;
+  bool ok = to_pending(h->pK, K, ld, r0, n, esz * d.dk, d, st) && to_pending(h->pV, V, ld, r0, n, esz * d.dv, d, st);
+  if (ok && d.c > 1) ok = to_pending(h->pg, gamma, ld, r0, n, sizeof(float), d, st);
+  if (ok && d.gate_mode == ATLASMEM_PER_TOKEN)
+    ok = to_pending(h->pth, theta, ld, r0, n, sizeof(float), d, st) &&
+         to_pending(h->pet, eta, ld, r0, n, sizeof(float), d, st) &&
+         to_pending(h->pal, alpha, ld, r0, n, sizeof(float), d, st);
+  if (!ok) {
+    (void)hipGetLastError();
+    return false;
+  }
+  h->pending += n;
+  return true;
+}
+
+const char* at_token(const void* base, int64_t t, size_t row) { return base ? (const char*)base + t * row : nullptr; }
+
+}  // namespace
+
+extern "C" {
+
 atlasmem_status atlasmem_update_chunked(atlasmem_handle hh, const void* K, const void* Q, const void* V,
                                         const float* theta, const float* eta, const float* alpha, const float* gamma,
                                         int64_t T, void* Y, void* stream) {
   Handle* h = (Handle*)hh;
   if (!h || T < 0) return ATLASMEM_E_INVALID;
   const Dims& d = h->d;
-  if (T % d.C != 0) return ATLASMEM_E_SHAPE;
   if (T == 0) return ATLASMEM_OK;
-  if (!K || !V || !theta || !eta || !alpha || (Y && !Q)) return ATLASMEM_E_INVALID;
+  const int64_t C = d.C;
+  const bool per_token = d.gate_mode == ATLASMEM_PER_TOKEN;
+  const int64_t p0 = h->pending;
+  const int64_t ncomp = (p0 + T) / C;  // chunks this call completes
+  if (!K || !V || (Y && !Q)) return ATLASMEM_E_INVALID;
+  if ((per_token || ncomp > 0) && (!theta || !eta || !alpha)) return ATLASMEM_E_INVALID;
   if ((d.c > 1) != (gamma != nullptr)) return ATLASMEM_E_INVALID;
   DeviceGuard g(h->device);
   if (!g.ok) return ATLASMEM_E_DEVICE;
-  if (d.kind == ATLASMEM_LINEAR) {
-    atlasmem_status s = launch_linear_update(h, K, Q, V, theta, eta, alpha, gamma, T, Y, S(stream));
-    if (s != ATLASMEM_OK) return s;
-    if (d.c > 1) {
-      s = launch_history_update(h, K, V, gamma, T, S(stream));
+  hipStream_t st = S(stream);
+  const int64_t ldg = per_token ? T : ncomp;
+  if (p0 == 0 && T % C == 0)
+    return run_update(h, d, K, Q, V, theta, eta, alpha, gamma, Span{T, T, ldg}, Y, st);
+
+  const size_t ek = (d.in_bf16 ? 2 : 4) * (size_t)d.dk, ev = (d.in_bf16 ? 2 : 4) * (size_t)d.dv;
+  const size_t ey = (d.out_bf16 ? 2 : 4) * (size_t)d.dv;
+  atlasmem_status s;
+  int64_t pos = 0, gpos = 0;  // tokens and (per-chunk) gates consumed
+  if (p0 > 0) {
+    // tokens of the unfinished chunk: retrieved now, at its start weights (the current state),
+    // and buffered until the chunk is complete
+    const int64_t a = T < C - p0 ? T : C - p0;
+    if (Y && (s = retrieve_rows(h, Q, a, T, Y, st)) != ATLASMEM_OK) return s;
+    if (!append_pending(h, K, V, theta, eta, alpha, gamma, T, a, st)) return ATLASMEM_E_DEVICE;
+    pos = a;
+    if (h->pending == C) {
+      const float* th = per_token ? h->pth : theta;
+      const float* et = per_token ? h->pet : eta;
+      const float* al = per_token ? h->pal : alpha;
+      s = run_update(h, d, h->pK, nullptr, h->pV, th, et, al, d.c > 1 ? h->pg : nullptr,
+                     Span{C, C, per_token ? C : ldg}, nullptr, st);
       if (s != ATLASMEM_OK) return s;
-      h->hcur = 1 - h->hcur;
+      h->pending = 0;
+      gpos = 1;
     }
-    return ATLASMEM_OK;
   }
-  return mlp_update(h, K, Q, V, theta, eta, alpha, gamma, T, Y, S(stream));
+  // whole chunks straight from the caller's arrays
+  const int64_t nfull = (T - pos) / C * C;
+  if (nfull > 0) {
+    const int64_t go = per_token ? pos : gpos;
+    s = run_update(h, d, at_token(K, pos, ek), at_token(Q, pos, ek), at_token(V, pos, ev), theta + go, eta + go,
+                   alpha + go, gamma ? gamma + pos : nullptr, Span{nfull, T, ldg}, Y ? (void*)at_token(Y, pos, ey) : nullptr,
+                   st);
+    if (s != ATLASMEM_OK) return s;
+    pos += nfull;
+  }
+  // the rest starts a new chunk
+  const int64_t r = T - pos;
+  if (r > 0) {
+    if (Y && (s = retrieve_rows(h, at_token(Q, pos, ek), r, T, (void*)at_token(Y, pos, ey), st)) != ATLASMEM_OK)
+      return s;
+    if (!append_pending(h, at_token(K, pos, ek), at_token(V, pos, ev), per_token ? theta + pos : nullptr,
+                        per_token ? eta + pos : nullptr, per_token ? alpha + pos : nullptr,
+                        gamma ? gamma + pos : nullptr, T, r, st))
+      return ATLASMEM_E_DEVICE;
+  }
+  return ATLASMEM_OK;
+}
+
+atlasmem_status atlasmem_flush(atlasmem_handle hh, const float* theta, const float* eta, const float* alpha,
+                               void* stream) {
+  Handle* h = (Handle*)hh;
+  if (!h) return ATLASMEM_E_INVALID;
+  const int64_t r = h->pending;
+  if (r == 0) return ATLASMEM_OK;
+  const bool per_token = h->d.gate_mode == ATLASMEM_PER_TOKEN;
+  if (!per_token && (!theta || !eta || !alpha)) return ATLASMEM_E_INVALID;
+  DeviceGuard g(h->device);
+  if (!g.ok) return ATLASMEM_E_DEVICE;
+  // the buffered tokens form one final chunk of r tokens
+  Dims dr = h->d;
+  dr.C = (int)r;
+  dr.Rk = dr.C + dr.c - 1;
+  dr.Rt = dr.Rk + dr.C;
+  const atlasmem_status s =
+      run_update(h, dr, h->pK, nullptr, h->pV, per_token ? h->pth : theta, per_token ? h->pet : eta,
+                 per_token ? h->pal : alpha, dr.c > 1 ? h->pg : nullptr, Span{r, h->d.C, per_token ? h->d.C : 1},
+                 nullptr, S(stream));
+  if (s != ATLASMEM_OK) return s;
+  h->pending = 0;
+  return ATLASMEM_OK;
+}
+
+int64_t atlasmem_pending(atlasmem_handle hh) {
+  const Handle* h = (const Handle*)hh;
+  return h ? h->pending : -1;
 }
 
 atlasmem_status atlasmem_retrieve(atlasmem_handle hh, const void* Q, int64_t T, void* Y, void* stream) {
@@ -265,8 +408,7 @@ atlasmem_status atlasmem_retrieve(atlasmem_handle hh, const void* Q, int64_t T, 
   if (!Q || !Y) return ATLASMEM_E_INVALID;
   DeviceGuard g(h->device);
   if (!g.ok) return ATLASMEM_E_DEVICE;
-  if (h->d.kind == ATLASMEM_LINEAR) return launch_linear_retrieve(h, Q, T, Y, S(stream));
-  return mlp_retrieve(h, Q, T, Y, S(stream));
+  return retrieve_rows(h, Q, T, T, Y, S(stream));
 }
 
 atlasmem_status atlasmem_get_state(atlasmem_handle hh, float* W, float* Sm, void* stream) {
@@ -315,6 +457,7 @@ atlasmem_status atlasmem_reset_history(atlasmem_handle hh, void* stream) {
         hipMemsetAsync(h->hg[i], 0, sizeof(float) * d.M * H, st) != hipSuccess)
       return ATLASMEM_E_DEVICE;
   }
+  h->pending = 0;  // a new sequence starts with a new chunk
   return ATLASMEM_OK;
 }
 

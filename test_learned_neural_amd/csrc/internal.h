@@ -25,6 +25,12 @@ struct Dims {
   bool no_fused;
 };
 
+// The token arrays of one launch sequence: T tokens; per memory, token stride `ld` of K, Q, V, Y,
+// gamma and per-token gates, and stride `ldg` of per-chunk gates.
+struct Span {
+  int64_t T, ld, ldg;
+};
+
 }  // namespace am
 
 // The opaque handle of the C ABI.
@@ -60,6 +66,15 @@ struct atlasmem_handle_s {
   int rb;        // rows per retrieval block
   float* Zr;     // [M][rb][dh]
   int* flag;     // non-finite flag (device)
+  // tokens of the current, unfinished chunk (streaming calls): input rows of K and V (input
+  // dtype), gamma and per-token gates, [M][C] each; `pending` of them are filled
+  void* pK;
+  void* pV;
+  float* pg;
+  float* pth;
+  float* pet;
+  float* pal;
+  int64_t pending;
 };
 
 namespace am {
@@ -75,16 +90,18 @@ atlasmem_status launch_omega(const float* cW, const float* cS, int64_t ld_c, con
                              const float* ghist, int M, int64_t s0, int nchunks, int C, int c, float* oW, float* oS,
                              int64_t ld_o, hipStream_t st);
 atlasmem_status launch_history_update(const Handle* h, const void* K, const void* V, const float* gamma, int64_t T,
-                                      hipStream_t st);
+                                      int64_t ld, hipStream_t st);
 atlasmem_status launch_poly(const void* X, int in_bf16, int64_t n, int d, float* F, hipStream_t st);
-atlasmem_status launch_linear_update(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
-                                     const float* eta, const float* alpha, const float* gamma, int64_t T, void* Y,
-                                     hipStream_t st);
-atlasmem_status launch_linear_retrieve(Handle* h, const void* Q, int64_t T, void* Y, hipStream_t st);
-atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
-                           const float* eta, const float* alpha, const float* gamma, int64_t T, void* Y,
+// The update launchers take the sizes from `d` (the handle's, or a copy with a shorter chunk for
+// a final partial chunk) and advance the handle's state over sp.T tokens (a multiple of d.C).
+atlasmem_status launch_linear_update(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
+                                     const float* theta, const float* eta, const float* alpha, const float* gamma,
+                                     const Span& sp, void* Y, hipStream_t st);
+atlasmem_status launch_linear_retrieve(Handle* h, const void* Q, int64_t T, int64_t ld, void* Y, hipStream_t st);
+atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* Q, const void* V, const float* theta,
+                           const float* eta, const float* alpha, const float* gamma, const Span& sp, void* Y,
                            hipStream_t st);
-atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, void* Y, hipStream_t st);
+atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, int64_t ld, void* Y, hipStream_t st);
 // Newton-Schulz on [n_mat] matrices of rows x cols, followed by an optional momentum/forgetting
 // epilogue.  When `upd` is null the result is written to `out` ([n_mat, rows, cols]).
 struct NsUpdate {
@@ -106,7 +123,8 @@ atlasmem_status launch_ns(const float* G, int64_t ldG_mat, int n_mat, int rows, 
                           float c, float eps, bool split, float* out, const NsUpdate* upd, hipStream_t st);
 bool ns_supported(int rows, int cols);
 bool fused_supported(const Dims& d);
-atlasmem_status launch_fused(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
-                             const float* eta, const float* alpha, int64_t T, void* Y, hipStream_t st);
+atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
+                             const float* theta, const float* eta, const float* alpha, const Span& sp, void* Y,
+                             hipStream_t st);
 
 }  // namespace am

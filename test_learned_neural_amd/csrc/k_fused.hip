@@ -792,14 +792,14 @@ bool fused_supported(const Dims& d) {
          d.split;
 }
 
-atlasmem_status launch_fused(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
-                             const float* eta, const float* alpha, int64_t T, void* Y, hipStream_t st) {
-  const Dims& d = h->d;
+atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
+                             const float* theta, const float* eta, const float* alpha, const Span& sp, void* Y,
+                             hipStream_t st) {
   if (hipFuncSetAttribute((const void*)fz::fused_ns_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                           fz::LDS_BYTES) != hipSuccess)
     return ATLASMEM_E_DEVICE;
   // one launch per segment of at most 2^22 tokens, so that per-memory byte offsets fit 32 bits
-  const int64_t nchunks = T / d.C;
+  const int64_t nchunks = sp.T / d.C;
   const int64_t seg = ((int64_t)1 << 22) / d.C;
   const int ysz = d.out_bf16 ? 2 : 4;
   for (int64_t c0 = 0; c0 < nchunks; c0 += seg) {
@@ -812,8 +812,8 @@ atlasmem_status launch_fused(Handle* h, const void* K, const void* Q, const void
     a.theta = theta + c0;
     a.eta = eta + c0;
     a.alpha = alpha + c0;
-    a.ldT = T;
-    a.ld_gate = nchunks;
+    a.ldT = sp.ld;
+    a.ld_gate = sp.ldg;
     a.C = d.C;
     a.nchunks = (int)nc;
     a.Win = h->W[h->cur];

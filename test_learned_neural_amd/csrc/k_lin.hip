@@ -27,7 +27,8 @@ struct LinArgs {
   const float* alpha;
   const float* gamma;
   int per_chunk;
-  int64_t T;
+  int64_t T;         // tokens
+  int64_t ld, ldg;   // per memory: token stride of the row arrays, stride of per-chunk gates
   int C, c, dk, din, dv, poly;
   const float* Win;
   const float* Sin;
@@ -113,18 +114,19 @@ __global__ void __launch_bounds__(64) lin_kernel(LinArgs a) {
       const int j = idx / D, f = idx % D;
       const int64_t tau = b0 + j;
       const int slot = (int)(tau & (kRing - 1));
-      const int64_t krow = ((int64_t)m * a.T + tau) * a.dk;
+      const int64_t krow = ((int64_t)m * a.ld + tau) * a.dk;
       Xr[slot * D + f] = f < a.din ? feature_of(a.K, krow, a.in_bf16, f, a.dk, a.poly) : 0.0f;
-      Qb[j * D + f] = f < a.din ? feature_of(a.Q, krow, a.in_bf16, f, a.dk, a.poly) : 0.0f;
-      Vr[slot * D + f] = f < a.dv ? load_in(a.V, ((int64_t)m * a.T + tau) * a.dv + f, a.in_bf16) : 0.0f;
+      // queries are read only when Y is asked for (Q may be null otherwise)
+      Qb[j * D + f] = (a.Y && f < a.din) ? feature_of(a.Q, krow, a.in_bf16, f, a.dk, a.poly) : 0.0f;
+      Vr[slot * D + f] = f < a.dv ? load_in(a.V, ((int64_t)m * a.ld + tau) * a.dv + f, a.in_bf16) : 0.0f;
     }
     for (int j = r; j < nb; j += 64) {
       const int64_t tau = b0 + j;
-      Gr[tau & (kRing - 1)] = a.c > 1 ? a.gamma[(int64_t)m * a.T + tau] : 1.0f;
+      Gr[tau & (kRing - 1)] = a.c > 1 ? a.gamma[(int64_t)m * a.ld + tau] : 1.0f;
       if (!a.per_chunk) {
-        Th[j] = a.theta[(int64_t)m * a.T + tau];
-        Et[j] = a.eta[(int64_t)m * a.T + tau];
-        Al[j] = a.alpha[(int64_t)m * a.T + tau];
+        Th[j] = a.theta[(int64_t)m * a.ld + tau];
+        Et[j] = a.eta[(int64_t)m * a.ld + tau];
+        Al[j] = a.alpha[(int64_t)m * a.ld + tau];
       }
     }
     __syncthreads();
@@ -146,9 +148,9 @@ __global__ void __launch_bounds__(64) lin_kernel(LinArgs a) {
         }
       }
       const int slot = (int)(t & (kRing - 1));
-      const float y = dot_row<D>(Wb, Qb + j * D);
       if (own && a.Y) {
-        const int64_t yo = ((int64_t)m * a.T + t) * a.dv + r;
+        const float y = dot_row<D>(Wb, Qb + j * D);
+        const int64_t yo = ((int64_t)m * a.ld + t) * a.dv + r;
         if (a.out_bf16) ((uint16_t*)a.Y)[yo] = (uint16_t)bf16_bits(y);
         else ((float*)a.Y)[yo] = y;
       }
@@ -179,7 +181,7 @@ __global__ void __launch_bounds__(64) lin_kernel(LinArgs a) {
         for (int l = 0; l < D; ++l) G[l] = fmaf(e, Xr[slot * D + l], G[l]);
         if ((t + 1) % a.C == 0) {
           const int64_t k = t / a.C;
-          const int64_t go = (int64_t)m * (a.T / a.C) + k;
+          const int64_t go = (int64_t)m * a.ldg + k;
           const float th = a.theta[go], et = a.eta[go], om = 1.0f - a.alpha[go];
 #pragma unroll
           for (int l = 0; l < D; ++l) {
@@ -222,10 +224,9 @@ static atlasmem_status lin_launch(const LinArgs& a, int M, hipStream_t st) {
   return ATLASMEM_OK;
 }
 
-atlasmem_status launch_linear_update(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
-                                     const float* eta, const float* alpha, const float* gamma, int64_t T, void* Y,
-                                     hipStream_t st) {
-  const Dims& d = h->d;
+atlasmem_status launch_linear_update(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
+                                     const float* theta, const float* eta, const float* alpha, const float* gamma,
+                                     const Span& sp, void* Y, hipStream_t st) {
   LinArgs a;
   a.K = K;
   a.Q = Q;
@@ -236,7 +237,9 @@ atlasmem_status launch_linear_update(Handle* h, const void* K, const void* Q, co
   a.alpha = alpha;
   a.gamma = gamma;
   a.per_chunk = d.gate_mode == ATLASMEM_PER_CHUNK;
-  a.T = T;
+  a.T = sp.T;
+  a.ld = sp.ld;
+  a.ldg = sp.ldg;
   a.C = d.C;
   a.c = d.c;
   a.dk = d.dk;
@@ -266,14 +269,14 @@ atlasmem_status launch_linear_update(Handle* h, const void* K, const void* Q, co
 // Retrieval with the current weights: one wave per (memory, block of 64 tokens), lane r
 // owns row r of W.
 __global__ void __launch_bounds__(64) lin_retrieve_kernel(const float* __restrict__ W, int64_t P, const void* Q,
-                                                          int in_bf16, int64_t T, int dk, int din, int dv, int poly,
-                                                          void* Y, int out_bf16) {
+                                                          int in_bf16, int64_t T, int64_t ld, int dk, int din,
+                                                          int dv, int poly, void* Y, int out_bf16) {
   extern __shared__ float qs[];  // [din]
   const int m = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
   const int r = threadIdx.x;
   for (int64_t t = t0; t < t0 + 64 && t < T; ++t) {
-    const int64_t qrow = ((int64_t)m * T + t) * dk;
+    const int64_t qrow = ((int64_t)m * ld + t) * dk;
     __syncthreads();
     for (int f = r; f < din; f += 64) qs[f] = feature_of(Q, qrow, in_bf16, f, dk, poly);
     __syncthreads();
@@ -281,19 +284,19 @@ __global__ void __launch_bounds__(64) lin_retrieve_kernel(const float* __restric
       const float* w = W + (int64_t)m * P + (int64_t)r * din;
       float acc = 0.0f;
       for (int l = 0; l < din; ++l) acc = fmaf(w[l], qs[l], acc);
-      const int64_t yo = ((int64_t)m * T + t) * dv + r;
+      const int64_t yo = ((int64_t)m * ld + t) * dv + r;
       if (out_bf16) ((uint16_t*)Y)[yo] = (uint16_t)bf16_bits(acc);
       else ((float*)Y)[yo] = acc;
     }
   }
 }
 
-atlasmem_status launch_linear_retrieve(Handle* h, const void* Q, int64_t T, void* Y, hipStream_t st) {
+atlasmem_status launch_linear_retrieve(Handle* h, const void* Q, int64_t T, int64_t ld, void* Y, hipStream_t st) {
   const Dims& d = h->d;
   if (T == 0) return ATLASMEM_OK;
   dim3 grid((unsigned)((T + 63) / 64), d.M);
   hipLaunchKernelGGL(lin_retrieve_kernel, grid, dim3(64), d.din * sizeof(float), st, h->W[h->cur], d.P, Q, d.in_bf16,
-                     T, d.dk, d.din, d.dv, d.poly, Y, d.out_bf16);
+                     T, ld, d.dk, d.din, d.dv, d.poly, Y, d.out_bf16);
   AM_LAUNCH_CHECK();
   return ATLASMEM_OK;
 }

@@ -29,7 +29,7 @@ struct FeatRows {
   const void* Q;
   int in_bf16;
   const float* hk;  // [M][c-1][dk] fp32
-  int64_t T, s;
+  int64_t T, s;  // T: token stride per memory of the row arrays
   int Rk, nrows;
   int c, dk, din, poly;
   int zdiv;
@@ -121,7 +121,7 @@ struct EpiY {
   const void* V;
   int in_bf16;
   const float* hv;
-  int64_t T, s;
+  int64_t T, s;  // T: token stride per memory of the row arrays
   int Rk, c, dv;
   void* Y;
   int out_bf16;
@@ -230,7 +230,7 @@ static void gemm_any(bool split, bool a_exact, bool b_exact, int M, int N, int K
   else launch_gemm<false, false>(split, M, N, K, batch, la, lb, ep, st);
 }
 
-static FeatRows feat_rows(const Handle* h, const void* K, const void* Q, int64_t T, int64_t s, int Rk, int nrows,
+static FeatRows feat_rows(const Handle* h, const void* K, const void* Q, int64_t ld, int64_t s, int Rk, int nrows,
                           int zdiv) {
   const Dims& d = h->d;
   FeatRows fr;
@@ -238,7 +238,7 @@ static FeatRows feat_rows(const Handle* h, const void* K, const void* Q, int64_t
   fr.Q = Q;
   fr.in_bf16 = d.in_bf16;
   fr.hk = h->hk[h->hcur];
-  fr.T = T;
+  fr.T = ld;
   fr.s = s;
   fr.Rk = Rk;
   fr.nrows = nrows;
@@ -252,10 +252,10 @@ static FeatRows feat_rows(const Handle* h, const void* K, const void* Q, int64_t
 
 // ---------------------------------------------------------------------------- one call
 
-atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* V, const float* theta,
-                           const float* eta, const float* alpha, const float* gamma, int64_t T, void* Y,
+atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* Q, const void* V, const float* theta,
+                           const float* eta, const float* alpha, const float* gamma, const Span& sp, void* Y,
                            hipStream_t st) {
-  const Dims& d = h->d;
+  const int64_t T = sp.T, ld = sp.ld;
   const int M = d.M, C = d.C, c = d.c, Rk = d.Rk, dh = d.dh, dv = d.dv, din = d.din;
   const bool split = d.split;
   const bool feat_exact = d.poly == 1 && d.in_bf16;
@@ -265,16 +265,16 @@ atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* 
   const int64_t zsz = (int64_t)d.Rt * dh;
   const bool per_token = d.gate_mode == ATLASMEM_PER_TOKEN;
   atlasmem_status stt;
-  if (!d.no_fused && fused_supported(d)) return launch_fused(h, K, Q, V, theta, eta, alpha, T, Y, st);
+  if (!d.no_fused && fused_supported(d)) return launch_fused(h, d, K, Q, V, theta, eta, alpha, sp, Y, st);
 
   for (int64_t kb0 = 0; kb0 < nchunks; kb0 += h->ncb) {
     const int nb = (int)((nchunks - kb0) < h->ncb ? (nchunks - kb0) : h->ncb);
     if (per_token) {
-      stt = launch_gate_scan(theta, eta, alpha, M, T, kb0 * C, nb, C, h->cW, h->cS, (int64_t)h->ncb * C, h->scal,
+      stt = launch_gate_scan(theta, eta, alpha, M, ld, kb0 * C, nb, C, h->cW, h->cS, (int64_t)h->ncb * C, h->scal,
                              (int64_t)h->ncb * 3, st);
       if (stt != ATLASMEM_OK) return stt;
       if (c > 1) {
-        stt = launch_omega(h->cW, h->cS, (int64_t)h->ncb * C, gamma, T, h->hg[h->hcur], M, kb0 * C, nb, C, c, h->oW,
+        stt = launch_omega(h->cW, h->cS, (int64_t)h->ncb * C, gamma, ld, h->hg[h->hcur], M, kb0 * C, nb, C, c, h->oW,
                            h->oS, (int64_t)h->ncb * Rk, st);
         if (stt != ATLASMEM_OK) return stt;
       }
@@ -291,7 +291,7 @@ atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* 
 
       // Z = X W1^T over key rows (+ query rows)
       {
-        FeatA la{feat_rows(h, K, Q, T, s, Rk, nrows, 1)};
+        FeatA la{feat_rows(h, K, Q, ld, s, Rk, nrows, 1)};
         StridedLoader lb = strided(W1, d.P, din, 1, 1, dh, din);  // B(k=f, j=h) = W1[h][f]
         EpiStore ep{h->Z, zsz, dh, 1};
         gemm_any(split, feat_exact, false, nrows, dh, din, M, la, lb, ep, st);
@@ -300,7 +300,7 @@ atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* 
       {
         StridedLoader la = strided(h->Z, zsz, dh, 1, 1, nrows, dh, XF_SILU);
         StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);  // B(k=h, j=v) = W2[v][h]
-        EpiY ep{h->D2, (int64_t)Rk * dv, V, d.in_bf16, h->hv[h->hcur], T, s, Rk, c, dv, Y, d.out_bf16};
+        EpiY ep{h->D2, (int64_t)Rk * dv, V, d.in_bf16, h->hv[h->hcur], ld, s, Rk, c, dv, Y, d.out_bf16};
         gemm_any(split, false, false, nrows, dv, dh, M, la, lb, ep, st);
       }
       // Pm = D2 W2 -> D1 = Pm * silu'(Z)
@@ -331,7 +331,7 @@ atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* 
           la.coef0 = c0;
           la.coef1 = c1;
           la.cz = cz;
-          FeatB lb{feat_rows(h, K, Q, T, s, Rk, Rk, 2)};
+          FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 2)};
           EpiUpdPair ep{Win, Sin, Wout, Sout, d.P, 0, din, sc, (int64_t)h->ncb * 3, h->flag};
           gemm_any(split, false, feat_exact, dh, din, Rk, 2 * M, la, lb, ep, st);
         }
@@ -339,13 +339,13 @@ atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* 
         {
           StridedLoader la = strided(h->D2, (int64_t)Rk * dv, 1, dv, 1, dv, Rk);
           StridedLoader lb = strided(h->Z, zsz, 1, dh, 1, dh, Rk, XF_SILU);
-          EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, d.P1, dh, theta, eta, alpha, nchunks, k, h->flag};
+          EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, d.P1, dh, theta, eta, alpha, sp.ldg, k, h->flag};
           gemm_any(split, false, false, dv, dh, Rk, M, la, lb, ep, st);
         }
         {
           StridedLoader la = strided(h->D1, (int64_t)Rk * dh, 1, dh, 1, dh, Rk);
-          FeatB lb{feat_rows(h, K, Q, T, s, Rk, Rk, 1)};
-          EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, 0, din, theta, eta, alpha, nchunks, k, h->flag};
+          FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)};
+          EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, 0, din, theta, eta, alpha, sp.ldg, k, h->flag};
           gemm_any(split, false, feat_exact, dh, din, Rk, M, la, lb, ep, st);
         }
       } else {
@@ -357,14 +357,14 @@ atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* 
         }
         {
           StridedLoader la = strided(h->D1, (int64_t)Rk * dh, 1, dh, 1, dh, Rk);
-          FeatB lb{feat_rows(h, K, Q, T, s, Rk, Rk, 1)};
+          FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)};
           EpiStore ep{h->G, d.P, din, 1};
           gemm_any(split, false, feat_exact, dh, din, Rk, M, la, lb, ep, st);
         }
-        NsUpdate u1{Win, Sin, Wout, Sout, d.P, 0, 1, theta, eta, alpha, nchunks, k, h->flag};
+        NsUpdate u1{Win, Sin, Wout, Sout, d.P, 0, 1, theta, eta, alpha, sp.ldg, k, h->flag};
         stt = launch_ns(h->G, d.P, M, dh, din, d.ns_steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, split, nullptr, &u1, st);
         if (stt != ATLASMEM_OK) return stt;
-        NsUpdate u2{Win, Sin, Wout, Sout, d.P, d.P1, 1, theta, eta, alpha, nchunks, k, h->flag};
+        NsUpdate u2{Win, Sin, Wout, Sout, d.P, d.P1, 1, theta, eta, alpha, sp.ldg, k, h->flag};
         stt = launch_ns(h->G + d.P1, d.P, M, dv, dh, d.ns_steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, split, nullptr,
                         &u2, st);
         if (stt != ATLASMEM_OK) return stt;
@@ -373,13 +373,13 @@ atlasmem_status mlp_update(Handle* h, const void* K, const void* Q, const void* 
       h->cur = 1 - h->cur;
     }
   }
-  stt = launch_history_update(h, K, V, gamma, T, st);
+  stt = launch_history_update(h, K, V, gamma, T, ld, st);
   if (stt != ATLASMEM_OK) return stt;
   if (c > 1 && T > 0) h->hcur = 1 - h->hcur;
   return ATLASMEM_OK;
 }
 
-atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, void* Y, hipStream_t st) {
+atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, int64_t ld, void* Y, hipStream_t st) {
   const Dims& d = h->d;
   const int M = d.M, dh = d.dh, dv = d.dv, din = d.din;
   const bool feat_exact = d.poly == 1 && d.in_bf16;
@@ -389,7 +389,7 @@ atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, void* Y, hipSt
   for (int64_t s = 0; s < T; s += h->rb) {
     const int rows = (int)((T - s) < h->rb ? (T - s) : h->rb);
     {
-      FeatA la{feat_rows(h, nullptr, Q, T, s, 0, rows, 1)};
+      FeatA la{feat_rows(h, nullptr, Q, ld, s, 0, rows, 1)};
       StridedLoader lb = strided(W1, d.P, din, 1, 1, dh, din);
       EpiStore ep{h->Zr, zsz, dh, 1};
       gemm_any(d.split, feat_exact, false, rows, dh, din, M, la, lb, ep, st);
@@ -397,7 +397,7 @@ atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, void* Y, hipSt
     {
       StridedLoader la = strided(h->Zr, zsz, dh, 1, 1, rows, dh, XF_SILU);
       StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);
-      EpiY ep{nullptr, 0, nullptr, d.in_bf16, nullptr, T, s, 0, d.c, dv, Y, d.out_bf16};
+      EpiY ep{nullptr, 0, nullptr, d.in_bf16, nullptr, ld, s, 0, d.c, dv, Y, d.out_bf16};
       gemm_any(d.split, false, false, rows, dv, dh, M, la, lb, ep, st);
     }
     AM_LAUNCH_CHECK();

@@ -123,7 +123,8 @@ atlasmem_status launch_omega(const float* cW, const float* cS, int64_t ld_c, con
 // (old history ++ this call), oldest first.  Rows that do not exist (fewer than c - 1 tokens
 // seen since the sequence start) keep gamma = 0 and zero vectors.
 __global__ void history_kernel(const void* __restrict__ K, const void* __restrict__ V,
-                               const float* __restrict__ gamma, int in_bf16, int M, int64_t T, int c, int dk, int dv,
+                               const float* __restrict__ gamma, int in_bf16, int M, int64_t T, int64_t ld, int c,
+                               int dk, int dv,
                                const float* __restrict__ hk, const float* __restrict__ hv,
                                const float* __restrict__ hg, float* __restrict__ nk, float* __restrict__ nv,
                                float* __restrict__ ng) {
@@ -136,28 +137,28 @@ __global__ void history_kernel(const void* __restrict__ K, const void* __restric
   const int m = (int)(idx / ((int64_t)width * H));
   const int64_t tau = T - H + hrow;
   if (e < dk) {
-    float x = (tau >= 0) ? load_in(K, ((int64_t)m * T + tau) * dk + e, in_bf16)
+    float x = (tau >= 0) ? load_in(K, ((int64_t)m * ld + tau) * dk + e, in_bf16)
                          : hk[((int64_t)m * H + hrow + T) * dk + e];
     nk[((int64_t)m * H + hrow) * dk + e] = x;
   } else if (e < dk + dv) {
     const int ev = e - dk;
-    float x = (tau >= 0) ? load_in(V, ((int64_t)m * T + tau) * dv + ev, in_bf16)
+    float x = (tau >= 0) ? load_in(V, ((int64_t)m * ld + tau) * dv + ev, in_bf16)
                          : hv[((int64_t)m * H + hrow + T) * dv + ev];
     nv[((int64_t)m * H + hrow) * dv + ev] = x;
   } else {
-    float x = (tau >= 0) ? gamma[(int64_t)m * T + tau] : hg[(int64_t)m * H + hrow + T];
+    float x = (tau >= 0) ? gamma[(int64_t)m * ld + tau] : hg[(int64_t)m * H + hrow + T];
     ng[(int64_t)m * H + hrow] = x;
   }
 }
 
 atlasmem_status launch_history_update(const Handle* h, const void* K, const void* V, const float* gamma, int64_t T,
-                                      hipStream_t st) {
+                                      int64_t ld, hipStream_t st) {
   const Dims& d = h->d;
   if (d.c <= 1 || T == 0) return ATLASMEM_OK;
   const int64_t total = (int64_t)d.M * (d.c - 1) * (d.dk + d.dv + 1);
   const int src = h->hcur, dst = 1 - h->hcur;
   hipLaunchKernelGGL(history_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, K, V, gamma, d.in_bf16,
-                     d.M, T, d.c, d.dk, d.dv, h->hk[src], h->hv[src], h->hg[src], h->hk[dst], h->hv[dst],
+                     d.M, T, ld, d.c, d.dk, d.dv, h->hk[src], h->hv[src], h->hg[src], h->hk[dst], h->hv[dst],
                      h->hg[dst]);
   AM_LAUNCH_CHECK();
   return ATLASMEM_OK;

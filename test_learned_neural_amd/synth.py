@@ -155,7 +155,7 @@ class Inputs:
     """Host arrays for all memories, in the device layouts.
 
     K, Q: [M, T, d_key]; V: [M, T, d_value] -- uint16 bf16 bits for bf16 workloads, float32 otherwise.
-    theta, eta, alpha: [M, T] (per token) or [M, T / chunk] (per chunk), float32.
+    theta, eta, alpha: [M, T] (per token) or [M, ceil(T / chunk)] (per chunk), float32.
     gamma: [M, T] float32 or None (window 1).
     W0: [M, P] float32 (W1 row-major then W2 row-major; linear: W), S0: zeros [M, P].
     """
@@ -198,7 +198,7 @@ def _draw_memory(s: Spec, index: int, b: int, h: int):
     k = rng.standard_normal((T, s.d_key))
     q = rng.standard_normal((T, s.d_key))
     v = rng.standard_normal((T, s.d_value))
-    n_g = T if s.gate_mode == PER_TOKEN else T // s.chunk
+    n_g = T if s.gate_mode == PER_TOKEN else -(-T // s.chunk)
     theta = rng.uniform(*s.theta_range, size=n_g)
     eta = rng.uniform(*s.eta_range, size=n_g)
     alpha = rng.uniform(*s.alpha_range, size=n_g)
@@ -225,14 +225,12 @@ def _prepare(x: np.ndarray, normalise: bool, dtype: int) -> np.ndarray:
 def make_inputs(index: int, variant: str = "literal", **overrides) -> Inputs:
     """All memories' inputs for workload `index` (optionally with overridden sizes)."""
     s = spec(index, variant, **overrides)
-    if s.T % s.chunk != 0 and s.gate_mode == PER_CHUNK:
-        raise ValueError("per-chunk gates need T to be a multiple of the chunk")
     M, T = s.n_mem, s.T
     in_dt = np.uint16 if s.input_dtype == BF16 else np.float32
     K = np.empty((M, T, s.d_key), in_dt)
     Q = np.empty((M, T, s.d_key), in_dt)
     V = np.empty((M, T, s.d_value), in_dt)
-    n_g = T if s.gate_mode == PER_TOKEN else T // s.chunk
+    n_g = T if s.gate_mode == PER_TOKEN else -(-T // s.chunk)
     theta = np.empty((M, n_g), np.float32)
     eta = np.empty((M, n_g), np.float32)
     alpha = np.empty((M, n_g), np.float32)

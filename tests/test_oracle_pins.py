@@ -84,12 +84,13 @@ def bruteforce_run(cfg, params, momenta, K, Q, V, th, et, al, ga):
     T, C, c = K.shape[0], cfg.chunk, cfg.omega_window
     Y = np.zeros((T, cfg.d_value))
     for s in range(0, T, C):
+        e = min(s + C, T)  # a final partial chunk holds the rest
         wb = [w.copy() for w in W]
         tw = [torch.tensor(w) for w in wb]
-        for t in range(s, s + C):
+        for t in range(s, e):
             Y[t] = torch_memory(tw, torch.tensor(Xq[t])).numpy()
         if cfg.gate_mode == PER_TOKEN:
-            for t in range(s, s + C):
+            for t in range(s, e):
                 idx = [i for i in range(t - c + 1, t + 1) if i >= 0]
                 ws = [(ga[i] if c > 1 else 1.0) for i in idx]
                 G = autograd_window_grad(wb, [X[i] for i in idx], [V[i] for i in idx], ws)
@@ -97,8 +98,8 @@ def bruteforce_run(cfg, params, momenta, K, Q, V, th, et, al, ga):
                     S[m] = et[t] * S[m] - th[t] * G[m]
                     W[m] = (1 - al[t]) * W[m] + S[m]
         else:
-            idx = list(range(s, s + C))
-            G = autograd_window_grad(wb, [X[i] for i in idx], [V[i] for i in idx], [1.0] * C)
+            idx = list(range(s, e))
+            G = autograd_window_grad(wb, [X[i] for i in idx], [V[i] for i in idx], [1.0] * len(idx))
             if cfg.ns_steps:
                 G = [ns5_svd(g, cfg.ns_steps) for g in G]
             k = s // C
@@ -117,7 +118,7 @@ def tiny_problem(seed, kind, T, d_k, d_v, d_h, poly, C, c, mode, ns=0, gate_scal
     K = r.normal(0, 1, (T, d_k)) / math.sqrt(d_k)
     Q = r.normal(0, 1, (T, d_k)) / math.sqrt(d_k)
     V = r.normal(0, 1, (T, d_v))
-    ng = T if mode == PER_TOKEN else T // C
+    ng = T if mode == PER_TOKEN else -(-T // C)
     th = r.uniform(0.01, 0.1, ng) * gate_scale
     et = r.uniform(0.8, 0.99, ng)
     al = r.uniform(0.0, 0.05, ng)
@@ -269,6 +270,11 @@ CASES = [
     (MLP2_SILU, 12, 3, 2, 5, 1, 4, 1, PER_CHUNK, 5),
     (MLP2_SILU, 12, 3, 4, 6, 2, 6, 1, PER_CHUNK, 5),
     (LINEAR, 12, 4, 3, 0, 1, 4, 1, PER_CHUNK, 5),
+    # a final partial chunk (T not a multiple of the chunk)
+    (MLP2_SILU, 14, 3, 2, 5, 1, 4, 3, PER_TOKEN, 0),
+    (MLP2_SILU, 13, 3, 2, 5, 2, 5, 2, PER_TOKEN, 0),
+    (MLP2_SILU, 10, 3, 2, 5, 1, 4, 1, PER_CHUNK, 5),
+    (LINEAR, 7, 4, 3, 0, 1, 3, 1, PER_CHUNK, 0),
 ]
 
 

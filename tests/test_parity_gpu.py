@@ -150,17 +150,48 @@ def test_retrieve_with_generator_weights():
 
 
 def test_argument_errors_on_device():
+    """Bad arguments are reported as errors and change nothing; a call of fewer tokens than a
+    chunk (or a non-multiple) is valid and leaves the tail pending."""
     import torch
     inp = synth.make_inputs(3, "stabilised", batch=1, heads=1, T=128)
     s = inp.spec
     mem = am.Memory(config_for(s))
     seg = segment(inp, 0, 128)
     with pytest.raises(am.AtlasMemError) as e:
-        mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], seg["gamma"], 100)
-    assert e.value.status == am.E_SHAPE
-    with pytest.raises(am.AtlasMemError) as e:
-        mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], None, 128)
+        mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], None, 100)
     assert e.value.status == am.E_INVALID
+    with pytest.raises(am.AtlasMemError) as e:
+        mem.update_chunked(seg["K"], seg["Q"], seg["V"], None, seg["eta"], seg["alpha"], seg["gamma"], 100)
+    assert e.value.status == am.E_INVALID
+    with pytest.raises(am.AtlasMemError) as e:
+        mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], seg["gamma"], -1)
+    assert e.value.status == am.E_INVALID
+    assert mem.pending == 0
     mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], seg["gamma"], 0)
+    assert mem.pending == 0
+    mem.update_chunked(seg["K"], None, seg["V"], seg["theta"], seg["eta"], seg["alpha"], seg["gamma"], 100)
+    assert mem.pending == 100 - s.chunk
+    mem.flush()
+    assert mem.pending == 0
+    torch.cuda.synchronize()
+    mem.close()
+
+    # per-chunk gates: needed only by calls that complete a chunk, and by a flush
+    inp = synth.make_inputs(4, "literal", batch=1, heads=2, T=256)
+    s = inp.spec
+    mem = am.Memory(config_for(s))
+    seg = segment(inp, 0, 256)
+    mem.update_chunked(seg["K"], None, seg["V"], None, None, None, None, 100)
+    assert mem.pending == 100
+    with pytest.raises(am.AtlasMemError) as e:
+        mem.update_chunked(seg["K"], None, seg["V"], None, None, None, None, 100)
+    assert e.value.status == am.E_INVALID
+    assert mem.pending == 100
+    with pytest.raises(am.AtlasMemError) as e:
+        mem.flush()
+    assert e.value.status == am.E_INVALID
+    assert mem.pending == 100
+    mem.reset_history()
+    assert mem.pending == 0
     torch.cuda.synchronize()
     mem.close()
