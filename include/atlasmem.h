@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
   ATLASMEM_OK = 0,
   ATLASMEM_E_INVALID = 1,      /* null pointer, negative size, bad enum value, wrong abi_version */
-  ATLASMEM_E_SHAPE = 2,        /* T not a multiple of the chunk, sizes beyond the stated limits  */
+  ATLASMEM_E_SHAPE = 2,        /* sizes beyond the stated limits; stand-alone stages: T % chunk */
   ATLASMEM_E_UNSUPPORTED = 3,  /* a valid but unsupported combination of options                  */
   ATLASMEM_E_DEVICE = 4,       /* no usable gfx950 device, or a HIP runtime / launch error        */
   ATLASMEM_E_NOMEM = 5,        /* device allocation failed (create only)                          */
