@@ -220,6 +220,47 @@ atlasmem_status atlasmem_newton_schulz(const float* G, int64_t n_mat, int32_t ro
                                        int32_t steps, float a, float b, float c, float eps,
                                        int32_t precision, float* out, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Input prologue: the steps just before the update, producing its K, Q, V and gates.
+ * ------------------------------------------------------------------------------------- */
+
+/* Causal depthwise short convolution, kernel 4, along the token axis, one filter per (head,
+ * channel), for keys, queries or values (Atlas-Torch README, Atlas Extensions table, "Short
+ * Convolution"; titans-pytorch-mlx README, Configuration table, use_conv / conv_kernel_size 4):
+ *   out[m, t, i] = bias[h, i] + sum_{j=0..3} taps[h, i, j] * X[m, t - 3 + j, i],  h = m % heads
+ * then, with l2norm = 1, each output row divided by max(its L2 norm, 1e-12) (keys, queries).
+ *   X:     [M, T, d] in_dtype (d 1..512); memory m = b * heads + h
+ *   taps:  fp32 [heads, d, 4];  bias: fp32 [heads, d] or NULL (zero)
+ *   hist:  [M, 3, d] in_dtype, the three rows before token 0 (oldest first), or NULL (the
+ *          start of a sequence: zeros)
+ *   out:   [M, T, d] out_dtype (fp32 arithmetic, one rounding to bf16); must not overlap X
+ *   hist_out: [M, 3, d] in_dtype or NULL: the three rows before the next call's first token (the
+ *          last three of hist ++ X), for streaming; must not overlap X or hist
+ * T = 0 is valid (only hist_out is written).  Errors: E_INVALID for bad sizes, enums, null or
+ * overlapping pointers; E_SHAPE for d > 512. */
+atlasmem_status atlasmem_short_conv(const void* X, int32_t in_dtype, int64_t M, int64_t T, int32_t d,
+                                    int32_t heads, const float* taps, const float* bias, const void* hist,
+                                    int32_t l2norm, void* out, int32_t out_dtype, void* hist_out, void* stream);
+
+/* Data-dependent gates (titans-pytorch-mlx README, Key Innovations item 4, and the
+ * Configuration table: memory_lr 0.1, memory_momentum 0.9, memory_decay 0.01, each scaled by a
+ * gate; titans-torch 0.1.2, "Inner-loop update rule"): for gate g (e.g. theta, eta, alpha and
+ * the Omega gamma), head h and token t of sequence b,
+ *   out[g, b, h, t] = scale[g] * sigmoid(Wg[g, h, :] . U[b, t, :] + bg[g, h])        (chunk = 1)
+ * and with chunk > 1 (the per-chunk path) one value per chunk, the gate of the chunk's
+ * mean-pooled input: sigmoid of the mean of its tokens' logits (Atlas-Torch README, Bug Fixes
+ * table, "no-omega ablation" row); a final short chunk pools its own tokens.
+ *   U:  [B, T, d_model] bf16 (d_model a multiple of 16, at most 512)
+ *   Wg: fp32 [n_gates, heads, d_model];  bg: fp32 [n_gates, heads];  scale: fp32 [n_gates]
+ *   chunk: 1, or a multiple of 32
+ *   out: fp32 [n_gates, B, heads, n], n = T or ceil(T / chunk): row (g, b, h) is memory
+ *        b * heads + h's gate array as atlasmem_update_chunked takes it
+ * Errors: E_INVALID for bad sizes or null pointers; E_UNSUPPORTED for other d_model / chunk;
+ * E_SHAPE for (T + 32) * d_model * 2 > 2^31 - 1. */
+atlasmem_status atlasmem_gates(const void* U, int64_t B, int64_t T, int32_t d_model, int32_t heads,
+                               int32_t n_gates, const float* Wg, const float* bg, const float* scale,
+                               int32_t chunk, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

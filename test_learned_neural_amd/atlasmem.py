@@ -27,7 +27,7 @@ EXPORTS = (
     "atlasmem_update_chunked", "atlasmem_flush", "atlasmem_pending", "atlasmem_retrieve", "atlasmem_get_state",
     "atlasmem_set_state",
     "atlasmem_reset_history", "atlasmem_destroy", "atlasmem_gate_scan", "atlasmem_omega_coeffs",
-    "atlasmem_poly_features", "atlasmem_newton_schulz",
+    "atlasmem_poly_features", "atlasmem_newton_schulz", "atlasmem_short_conv", "atlasmem_gates",
 )
 
 
@@ -81,6 +81,9 @@ def load():
         "atlasmem_omega_coeffs": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
         "atlasmem_poly_features": ([_vp, _i32, _i64, _i32, _vp, _vp], ctypes.c_int),
         "atlasmem_newton_schulz": ([_vp, _i64, _i32, _i32, _i32, _f, _f, _f, _f, _i32, _vp, _vp], ctypes.c_int),
+        "atlasmem_short_conv": ([_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp],
+                                ctypes.c_int),
+        "atlasmem_gates": ([_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -206,3 +209,15 @@ def newton_schulz(G, n_mat: int, rows: int, cols: int, steps: int, coeffs, eps: 
     a, b, c = coeffs
     _check(load().atlasmem_newton_schulz(_ptr(G), n_mat, rows, cols, steps, a, b, c, eps, precision, _ptr(out),
                                          _stream(stream)), "atlasmem_newton_schulz")
+
+
+def short_conv(X, in_dtype: int, M: int, T: int, d: int, heads: int, taps, bias, hist, l2norm: bool, out,
+               out_dtype: int, hist_out=None, stream=None):
+    _check(load().atlasmem_short_conv(_ptr(X), in_dtype, M, T, d, heads, _ptr(taps), _ptr(bias), _ptr(hist),
+                                      int(l2norm), _ptr(out), out_dtype, _ptr(hist_out), _stream(stream)),
+           "atlasmem_short_conv")
+
+
+def gates(U, B: int, T: int, d_model: int, heads: int, n_gates: int, Wg, bg, scale, chunk: int, out, stream=None):
+    _check(load().atlasmem_gates(_ptr(U), B, T, d_model, heads, n_gates, _ptr(Wg), _ptr(bg), _ptr(scale), chunk,
+                                 _ptr(out), _stream(stream)), "atlasmem_gates")

@@ -518,4 +518,32 @@ atlasmem_status atlasmem_newton_schulz(const float* G, int64_t n_mat, int32_t ro
                    precision != ATLASMEM_PREC_BF16, out, nullptr, S(stream));
 }
 
+atlasmem_status atlasmem_short_conv(const void* X, int32_t in_dtype, int64_t M, int64_t T, int32_t d, int32_t heads,
+                                    const float* taps, const float* bias, const void* hist, int32_t l2norm, void* out,
+                                    int32_t out_dtype, void* hist_out, void* stream) {
+  const bool dt_ok = (in_dtype == ATLASMEM_F32 || in_dtype == ATLASMEM_BF16) &&
+                     (out_dtype == ATLASMEM_F32 || out_dtype == ATLASMEM_BF16);
+  if (M < 0 || T < 0 || d < 1 || heads < 1 || !dt_ok || (l2norm != 0 && l2norm != 1)) return ATLASMEM_E_INVALID;
+  if (d > 512) return ATLASMEM_E_SHAPE;
+  if (M == 0 || (T == 0 && !hist_out)) return ATLASMEM_OK;
+  if (!taps || (T > 0 && (!X || !out)) || (hist_out && (!X && T > 0))) return ATLASMEM_E_INVALID;
+  // the output and the carried rows must not overlap what is still being read
+  if ((out && out == X) || (hist_out && (hist_out == hist || hist_out == X))) return ATLASMEM_E_INVALID;
+  return launch_short_conv(X, in_dtype == ATLASMEM_BF16, M, T, d, heads, taps, bias, hist, l2norm != 0, out,
+                           out_dtype == ATLASMEM_BF16, hist_out, S(stream));
+}
+
+atlasmem_status atlasmem_gates(const void* U, int64_t B, int64_t T, int32_t d_model, int32_t heads, int32_t n_gates,
+                               const float* Wg, const float* bg, const float* scale, int32_t chunk, float* out,
+                               void* stream) {
+  if (B < 0 || T < 0 || d_model < 1 || heads < 1 || n_gates < 1 || chunk < 1) return ATLASMEM_E_INVALID;
+  if (!gates_supported(d_model, chunk)) return ATLASMEM_E_UNSUPPORTED;
+  if ((int64_t)n_gates * heads > (1 << 20)) return ATLASMEM_E_SHAPE;
+  // per-sequence byte offsets of U (plus one 32-row block past the end) stay within 32 bits
+  if ((T + 32) * (int64_t)d_model * 2 > INT32_MAX) return ATLASMEM_E_SHAPE;
+  if (B == 0 || T == 0) return ATLASMEM_OK;
+  if (!U || !Wg || !bg || !scale || !out) return ATLASMEM_E_INVALID;
+  return launch_gates(U, B, T, d_model, heads, n_gates, Wg, bg, scale, chunk, out, S(stream));
+}
+
 }  // extern "C"

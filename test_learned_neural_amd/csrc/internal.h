@@ -31,6 +31,14 @@ struct Span {
   int64_t T, ld, ldg;
 };
 
+// Input prologue (k_prologue.hip)
+atlasmem_status launch_short_conv(const void* X, bool in_bf16, int64_t M, int64_t T, int d, int heads,
+                                  const float* taps, const float* bias, const void* hist, bool l2norm, void* out,
+                                  bool out_bf16, void* hist_out, hipStream_t st);
+bool gates_supported(int dm, int chunk);
+atlasmem_status launch_gates(const void* U, int64_t B, int64_t T, int dm, int H, int n_gates, const float* Wg,
+                             const float* bg, const float* scale, int chunk, float* out, hipStream_t st);
+
 }  // namespace am
 
 // The opaque handle of the C ABI.
@@ -126,5 +134,13 @@ bool fused_supported(const Dims& d);
 atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
                              const float* theta, const float* eta, const float* alpha, const Span& sp, void* Y,
                              hipStream_t st);
+
+// Input prologue (k_prologue.hip)
+atlasmem_status launch_short_conv(const void* X, bool in_bf16, int64_t M, int64_t T, int d, int heads,
+                                  const float* taps, const float* bias, const void* hist, bool l2norm, void* out,
+                                  bool out_bf16, void* hist_out, hipStream_t st);
+bool gates_supported(int dm, int chunk);
+atlasmem_status launch_gates(const void* U, int64_t B, int64_t T, int dm, int H, int n_gates, const float* Wg,
+                             const float* bg, const float* scale, int chunk, float* out, hipStream_t st);
 
 }  // namespace am

@@ -251,3 +251,48 @@ def make_inputs(index: int, variant: str = "literal", **overrides) -> Inputs:
             if not s.zero_init:
                 W0[m] = np.concatenate([p.astype(np.float32).ravel() for p in params])
     return Inputs(s, index, variant, K, Q, V, theta, eta, alpha, gamma, W0, np.zeros_like(W0))
+
+
+# ----------------------------------------------------------------------------- prologue inputs
+
+GATE_SCALES = (0.1, 0.9, 0.01, 1.0)  # theta, eta, alpha maxima and gamma's
+
+
+@dataclasses.dataclass
+class PrologueInputs:
+    """Host arrays for the input prologue (short convolution and gates).
+
+    X: [B*H, T, d] raw key / query / value rows (bf16 bits or fp32), hist: [B*H, 3, d] rows
+    before token 0 (same dtype); taps: [H, d, 4], bias: [H, d] fp32;
+    U: [B, T, d_model] bf16 bits; Wg: [n_gates, H, d_model], bg: [n_gates, H], scale: [n_gates]."""
+
+    X: np.ndarray
+    hist: np.ndarray
+    taps: np.ndarray
+    bias: np.ndarray
+    U: np.ndarray
+    Wg: np.ndarray
+    bg: np.ndarray
+    scale: np.ndarray
+
+
+def make_prologue_inputs(seed: int, B: int, H: int, T: int, d: int, d_model: int, n_gates: int = 3,
+                         in_dtype: int = BF16) -> PrologueInputs:
+    """Seeded draws: X, hist, U ~ N(0, 1); taps ~ N(0, 0.5^2); bias ~ N(0, 0.1^2);
+    Wg ~ N(0, 1/d_model); bg ~ N(0, 1); scale = the first n_gates of GATE_SCALES.
+    Rows are rounded to bf16 once where bf16 is asked for (U always)."""
+    rng = np.random.default_rng(np.random.SeedSequence([1000 + seed, B, H, T, d, d_model]))
+    M = B * H
+    X = rng.standard_normal((M, T, d)).astype(np.float32)
+    hist = rng.standard_normal((M, 3, d)).astype(np.float32)
+    taps = (0.5 * rng.standard_normal((H, d, 4))).astype(np.float32)
+    bias = (0.1 * rng.standard_normal((H, d))).astype(np.float32)
+    U = rng.standard_normal((B, T, d_model)).astype(np.float32)
+    Wg = (rng.standard_normal((n_gates, H, d_model)) / math.sqrt(d_model)).astype(np.float32)
+    bg = rng.standard_normal((n_gates, H)).astype(np.float32)
+    scale = np.array(GATE_SCALES[:n_gates], dtype=np.float32)
+    if in_dtype == BF16:
+        X = f32_to_bf16_bits(X)
+        hist = f32_to_bf16_bits(hist)
+    return PrologueInputs(X=X, hist=hist, taps=taps, bias=bias, U=f32_to_bf16_bits(U), Wg=Wg, bg=bg, scale=scale)
+
