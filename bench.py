@@ -99,7 +99,10 @@ def stage_rooflines(torch, am, synth, dev, stream):
     peak (algorithmic FLOPs).  Sizes are large enough for the launch to be bandwidth- or
     compute-bound (the per-chunk sizes inside a workload are far smaller): the scans over 256
     memories x 32768 tokens in chunks of 64, the feature map over the Omega workload's 262144 keys
-    (width 32 -> 561), Newton-Schulz over 4096 gradient matrices of 128 x 64."""
+    (width 32 -> 561), Newton-Schulz over 4096 gradient matrices of 128 x 64; the input prologue at
+    the Newton-Schulz workload's shape: the keys' short convolution (128 memories x 32768 tokens x
+    64, bf16 in and out, L2-normalised) and the gates of 8 x 32768 token inputs of width 512 for 16
+    heads (per token: theta, eta, alpha, gamma; per chunk of 128: theta, eta, alpha)."""
     out = {}
     M, T, C, c, d = 256, 32768, 64, 4, 32
     th = torch.rand((M, T), device=dev)
@@ -118,6 +121,19 @@ def stage_rooflines(torch, am, synth, dev, stream):
     NM = 4096
     G = torch.randn((NM, 128, 64), device=dev)
     Gout = torch.empty_like(G)
+    CM, CT, CD, CH = 128, 32768, 64, 16
+    KX = torch.randn((CM, CT, CD), device=dev).to(torch.bfloat16).view(torch.int16)
+    KO = torch.empty_like(KX)
+    Khist = torch.zeros((CM, 3, CD), dtype=torch.int16, device=dev)
+    taps = 0.5 * torch.randn((CH, CD, 4), device=dev)
+    cbias = 0.1 * torch.randn((CH, CD), device=dev)
+    GB, DM = 8, 512
+    U = torch.randn((GB, CT, DM), device=dev).to(torch.bfloat16).view(torch.int16)
+    Wg = torch.randn((4, CH, DM), device=dev) / DM ** 0.5
+    bg = torch.randn((4, CH), device=dev)
+    gsc = torch.tensor(synth.GATE_SCALES, device=dev)
+    gout = torch.empty((4, GB, CH, CT), device=dev)
+    gout_c = torch.empty((3, GB, CH, CT // 128), device=dev)
     cases = [
         ("gate_scan", lambda: am.gate_scan(th, et, al, M, T, C, cW, cS, sc),
          M * T * (12 + 8) + M * (T // C) * 12, "hbm", f"{M} memories x {T} tokens, chunk {C}"),
@@ -128,6 +144,13 @@ def stage_rooflines(torch, am, synth, dev, stream):
         ("newton_schulz", lambda: am.newton_schulz(G, NM, 128, 64, 5, synth.NS_COEFFS, synth.NS_EPS,
                                                    am.PREC_BF16X3, Gout),
          NM * ns_flops_per_matrix(128, 64, 5), "mfma", f"{NM} matrices 128x64, 5 steps, split bf16"),
+        ("short_conv", lambda: am.short_conv(KX, synth.BF16, CM, CT, CD, CH, taps, cbias, Khist, True, KO, synth.BF16),
+         CM * CT * CD * (2 + 2), "hbm", f"{CM} memories x {CT} tokens x {CD}, bf16 in/out, L2-normalised"),
+        ("gates_per_token", lambda: am.gates(U, GB, CT, DM, CH, 4, Wg, bg, gsc, 1, gout),
+         GB * CT * DM * 2 + 4 * GB * CH * CT * 4, "hbm", f"{GB} x {CT} inputs of width {DM}, 4 gates x {CH} heads"),
+        ("gates_per_chunk", lambda: am.gates(U, GB, CT, DM, CH, 3, Wg[:3], bg[:3], gsc[:3], 128, gout_c),
+         GB * CT * DM * 2 + 3 * GB * CH * (CT // 128) * 4, "hbm",
+         f"{GB} x {CT} inputs of width {DM}, 3 gates x {CH} heads, pooled per chunk of 128"),
     ]
     for name, fn, work, bound, shape in cases:
         for _ in range(3):

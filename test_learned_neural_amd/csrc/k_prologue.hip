@@ -20,7 +20,7 @@ namespace am {
 // ------------------------------------------------------------------------ short convolution
 
 constexpr int kConvCh = 8;    // channels per lane (16 bytes of bf16)
-constexpr int kConvSeg = 32;  // consecutive tokens per lane
+constexpr int kConvSeg = 64;  // consecutive tokens per lane
 
 struct ConvArgs {
   const void* X;      // [M, T, d]
@@ -35,27 +35,52 @@ struct ConvArgs {
   void* out;          // [M, T, d]
 };
 
-template <bool IN_BF16, bool OUT_BF16, bool VEC>
-__device__ __forceinline__ void conv_load(const void* base, int64_t off, int c0, int d, float (&v)[kConvCh]) {
-  if (VEC) {  // d % 8 == 0: the lane's 8 channels are one aligned 16-byte (bf16) or 32-byte (fp32) run
+// One row's 8 channels as loaded: packed bf16 pairs (4 words) or fp32 (8 words).  Loads are
+// issued into these raw words and converted only where they are used, so that a whole batch of
+// rows is in flight at once.
+template <bool IN_BF16>
+struct RawRow {
+  static constexpr int N = IN_BF16 ? 4 : 8;
+  uint32_t w[N];
+};
+
+template <bool IN_BF16, bool VEC>
+__device__ __forceinline__ void conv_load(const void* base, int64_t off, int c0, int d, RawRow<IN_BF16>& r) {
+  if (VEC) {  // d % 8 == 0 and aligned bases: one 16-byte (bf16) or two 16-byte (fp32) loads
     if (IN_BF16) {
-      const u32x4 w = *(const u32x4*)((const uint16_t*)base + off + c0);
+      const u32x4 v = *(const u32x4*)((const uint16_t*)base + off + c0);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) r.w[p] = v[p];
+    } else {
+      const u32x4 a = *(const u32x4*)((const float*)base + off + c0);
+      const u32x4 b = *(const u32x4*)((const float*)base + off + c0 + 4);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        v[2 * p] = __uint_as_float(w[p] << 16);
-        v[2 * p + 1] = __uint_as_float(w[p] & 0xFFFF0000u);
+        r.w[p] = a[p];
+        r.w[4 + p] = b[p];
       }
-    } else {
-      const float4 a = *(const float4*)((const float*)base + off + c0);
-      const float4 b = *(const float4*)((const float*)base + off + c0 + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kConvCh; ++i) v[i] = (c0 + i < d) ? load_in(base, off + c0 + i, IN_BF16) : 0.0f;
+    for (int i = 0; i < kConvCh; ++i) {
+      const int c = c0 + i < d ? c0 + i : d - 1;  // in-bounds address; the value is masked below
+      const uint32_t v = IN_BF16 ? (uint32_t)((const uint16_t*)base)[off + c] : ((const uint32_t*)base)[off + c];
+      const uint32_t m = c0 + i < d ? v : 0u;
+      if (IN_BF16) r.w[i >> 1] = (i & 1) ? (r.w[i >> 1] | (m << 16)) : m;
+      else r.w[i] = m;
+    }
   }
 }
+
+template <bool IN_BF16>
+__device__ __forceinline__ void conv_unpack(const RawRow<IN_BF16>& r, float (&v)[kConvCh]) {
+#pragma unroll
+  for (int i = 0; i < kConvCh; ++i)
+    v[i] = IN_BF16 ? __uint_as_float((i & 1) ? (r.w[i >> 1] & 0xFFFF0000u) : (r.w[i >> 1] << 16))
+                   : __uint_as_float(r.w[i]);
+}
+
+constexpr int kConvBatch = 8;  // rows loaded together
 
 template <bool IN_BF16, bool OUT_BF16, bool VEC>
 __global__ void __launch_bounds__(256) conv_kernel(ConvArgs a) {
@@ -64,22 +89,46 @@ __global__ void __launch_bounds__(256) conv_kernel(ConvArgs a) {
   const int g = (int)(gid & (lpr - 1));
   const int64_t row_group = gid >> a.log_lpr;  // (memory, segment)
   // Lanes past the last segment still take part in the row reductions (whole groups are either
-  // valid or not, and a group never straddles a wave), but read and write nothing.
+  // valid or not, and a group never straddles a wave), but write nothing.  Every lane loads from
+  // a clamped, in-bounds address, so the loads need no branches.
   const bool valid = row_group < a.M * a.nseg;
   const int64_t m = valid ? row_group / a.nseg : 0;
   const int64_t seg = valid ? row_group % a.nseg : 0;
   const int h = (int)(m % a.heads);
   const int c0 = g * kConvCh;
   const bool lane_on = valid && c0 < a.d;
+  const int cl = lane_on ? c0 : 0;
 
   float w[4][kConvCh], bs[kConvCh];
+  if (VEC) {  // the lane's 8 channels' taps are 32 consecutive floats, its biases 8
+    const float4* tp = (const float4*)(a.taps + ((int64_t)h * a.d + cl) * 4);
 #pragma unroll
-  for (int i = 0; i < kConvCh; ++i) {
-    const bool in = lane_on && c0 + i < a.d;
-    const float* tp = a.taps + ((int64_t)h * a.d + c0 + i) * 4;
+    for (int i = 0; i < kConvCh; ++i) {
+      const float4 v = tp[i];
+      w[0][i] = lane_on ? v.x : 0.0f;
+      w[1][i] = lane_on ? v.y : 0.0f;
+      w[2][i] = lane_on ? v.z : 0.0f;
+      w[3][i] = lane_on ? v.w : 0.0f;
+    }
+    if (a.bias) {
+      const float4* bp = (const float4*)(a.bias + (int64_t)h * a.d + cl);
+      const float4 b0 = bp[0], b1 = bp[1];
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j][i] = in ? tp[j] : 0.0f;
-    bs[i] = (in && a.bias) ? a.bias[(int64_t)h * a.d + c0 + i] : 0.0f;
+      for (int i = 0; i < kConvCh; ++i) bs[i] = lane_on ? bv[i] : 0.0f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kConvCh; ++i) bs[i] = 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kConvCh; ++i) {
+      const bool in = lane_on && c0 + i < a.d;
+      const float* tp = a.taps + ((int64_t)h * a.d + (in ? c0 + i : 0)) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j][i] = in ? tp[j] : 0.0f;
+      bs[i] = (in && a.bias) ? a.bias[(int64_t)h * a.d + c0 + i] : 0.0f;
+    }
   }
 
   const int64_t t0 = seg * kConvSeg;
@@ -91,67 +140,76 @@ __global__ void __launch_bounds__(256) conv_kernel(ConvArgs a) {
     if (!lane_on || (t < 0 && !a.hist)) {
 #pragma unroll
       for (int i = 0; i < kConvCh; ++i) v[i] = 0.0f;
-    } else if (t >= 0) {
-      conv_load<IN_BF16, OUT_BF16, VEC>(a.X, (rowbase + t) * a.d, c0, a.d, v);
     } else {
-      conv_load<IN_BF16, OUT_BF16, VEC>(a.hist, (m * 3 + 3 + t) * a.d, c0, a.d, v);
+      RawRow<IN_BF16> r;
+      if (t >= 0) conv_load<IN_BF16, VEC>(a.X, (rowbase + t) * a.d, c0, a.d, r);
+      else conv_load<IN_BF16, VEC>(a.hist, (m * 3 + 3 + t) * a.d, c0, a.d, r);
+      conv_unpack<IN_BF16>(r, v);
     }
   };
   prev_row(t0 - 3, p3);
   prev_row(t0 - 2, p2);
   prev_row(t0 - 1, p1);
 
-  for (int64_t t = t0; t < t0 + kConvSeg; ++t) {
-    const bool tok = lane_on && t < t1;
-    float x[kConvCh];
-    if (tok) {
-      conv_load<IN_BF16, OUT_BF16, VEC>(a.X, (rowbase + t) * a.d, c0, a.d, x);
-    } else {
 #pragma unroll
-      for (int i = 0; i < kConvCh; ++i) x[i] = 0.0f;
+  for (int bt = 0; bt < kConvSeg / kConvBatch; ++bt) {
+    RawRow<IN_BF16> raw[kConvBatch];
+#pragma unroll
+    for (int i = 0; i < kConvBatch; ++i) {
+      const int64_t t = t0 + bt * kConvBatch + i;
+      const int64_t tc = t < t1 ? t : t1 - 1;
+      conv_load<IN_BF16, VEC>(a.X, (rowbase + tc) * a.d, cl, a.d, raw[i]);
     }
-    float y[kConvCh];
-    float ss = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kConvCh; ++i) {
-      float acc = bs[i];
-      acc = fmaf(w[0][i], p3[i], acc);
-      acc = fmaf(w[1][i], p2[i], acc);
-      acc = fmaf(w[2][i], p1[i], acc);
-      acc = fmaf(w[3][i], x[i], acc);
-      y[i] = acc;
-      ss = fmaf(acc, acc, ss);
-      p3[i] = p2[i];
-      p2[i] = p1[i];
-      p1[i] = x[i];
-    }
-    if (a.l2norm) {  // uniform branch: every lane of the wave takes it
-      for (int off = 1; off < lpr; off <<= 1) ss += __shfl_xor(ss, off, 64);
-      const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    for (int i = 0; i < kConvBatch; ++i) {
+      const int64_t t = t0 + bt * kConvBatch + i;
+      const bool tok = lane_on && t < t1;
+      float x[kConvCh];
+      conv_unpack<IN_BF16>(raw[i], x);
+      float y[kConvCh];
+      float ss = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kConvCh; ++i) y[i] *= inv;
-    }
-    if (!tok) continue;
-    const int64_t o = (rowbase + t) * a.d + c0;
-    if (OUT_BF16) {
-      uint16_t* dst = (uint16_t*)a.out + o;
-      if (VEC) {
-        *(u32x4*)dst = u32x4{cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3]), cvt_pk_bf16(y[4], y[5]),
-                             cvt_pk_bf16(y[6], y[7])};
-      } else {
-#pragma unroll
-        for (int i = 0; i < kConvCh; ++i)
-          if (c0 + i < a.d) dst[i] = (uint16_t)bf16_bits(y[i]);
+      for (int k = 0; k < kConvCh; ++k) {
+        const float xv = tok ? x[k] : 0.0f;
+        float acc = bs[k];
+        acc = fmaf(w[0][k], p3[k], acc);
+        acc = fmaf(w[1][k], p2[k], acc);
+        acc = fmaf(w[2][k], p1[k], acc);
+        acc = fmaf(w[3][k], xv, acc);
+        y[k] = acc;
+        ss = fmaf(acc, acc, ss);
+        p3[k] = p2[k];
+        p2[k] = p1[k];
+        p1[k] = xv;
       }
-    } else {
-      float* dst = (float*)a.out + o;
-      if (VEC) {
-        *(float4*)dst = float4{y[0], y[1], y[2], y[3]};
-        *(float4*)(dst + 4) = float4{y[4], y[5], y[6], y[7]};
-      } else {
+      if (a.l2norm) {  // uniform branch: every lane of the wave takes it
+        for (int off = 1; off < lpr; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
 #pragma unroll
-        for (int i = 0; i < kConvCh; ++i)
-          if (c0 + i < a.d) dst[i] = y[i];
+        for (int k = 0; k < kConvCh; ++k) y[k] *= inv;
+      }
+      if (!tok) continue;
+      const int64_t o = (rowbase + t) * a.d + c0;
+      if (OUT_BF16) {
+        uint16_t* dst = (uint16_t*)a.out + o;
+        if (VEC) {
+          *(u32x4*)dst = u32x4{cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3]), cvt_pk_bf16(y[4], y[5]),
+                               cvt_pk_bf16(y[6], y[7])};
+        } else {
+#pragma unroll
+          for (int k = 0; k < kConvCh; ++k)
+            if (c0 + k < a.d) dst[k] = (uint16_t)bf16_bits(y[k]);
+        }
+      } else {
+        float* dst = (float*)a.out + o;
+        if (VEC) {
+          *(float4*)dst = float4{y[0], y[1], y[2], y[3]};
+          *(float4*)(dst + 4) = float4{y[4], y[5], y[6], y[7]};
+        } else {
+#pragma unroll
+          for (int k = 0; k < kConvCh; ++k)
+            if (c0 + k < a.d) dst[k] = y[k];
+        }
       }
     }
   }
@@ -199,8 +257,9 @@ atlasmem_status launch_short_conv(const void* X, bool in_bf16, int64_t M, int64_
     const int64_t lanes = M * a.nseg * lpr;
     const int64_t blocks = (lanes + 255) / 256;
     if (blocks > INT32_MAX) return ATLASMEM_E_SHAPE;
-    // 16-byte row accesses need whole 8-channel runs and aligned bases
-    const bool vec = d % kConvCh == 0 && (((uintptr_t)X | (uintptr_t)out | (uintptr_t)hist) & 15) == 0;
+    // 16-byte row, tap and bias accesses need whole 8-channel runs and aligned bases
+    const bool vec = d % kConvCh == 0 &&
+                     (((uintptr_t)X | (uintptr_t)out | (uintptr_t)hist | (uintptr_t)taps | (uintptr_t)bias) & 15) == 0;
 #define AM_CONV(IB, OB, V) hipLaunchKernelGGL((conv_kernel<IB, OB, V>), dim3((unsigned)blocks), dim3(256), 0, st, a)
     if (in_bf16 && out_bf16) { if (vec) AM_CONV(true, true, true); else AM_CONV(true, true, false); }
     else if (in_bf16) { if (vec) AM_CONV(true, false, true); else AM_CONV(true, false, false); }
@@ -224,7 +283,7 @@ atlasmem_status launch_short_conv(const void* X, bool in_bf16, int64_t M, int64_
 
 constexpr int kGateCols = 64;    // output columns (gate, head) per pass
 constexpr int kGateRows = 32;    // tokens per MFMA block
-constexpr int kGateWaves = 8;
+constexpr int kGateWaves = 16;  // at most: one workgroup per CU (LDS), four waves per SIMD
 constexpr int kGateMaxDm = 512;
 
 struct GateArgs {
@@ -260,7 +319,7 @@ __global__ void __launch_bounds__(kGateWaves * 64) gates_kernel(GateArgs a) {
   __syncthreads();
 
   const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int ksteps = a.dm / 16;
   // this lane's two output columns and their constants
   float bias[2], sc[2];
@@ -279,7 +338,7 @@ __global__ void __launch_bounds__(kGateWaves * 64) gates_kernel(GateArgs a) {
   const int64_t per_seq = a.units / a.B;
   const int blocks_per_unit = POOL ? a.chunk / kGateRows : 1;
 
-  for (int64_t u = (int64_t)blockIdx.x * kGateWaves + wave; u < a.units; u += (int64_t)gridDim.x * kGateWaves) {
+  for (int64_t u = (int64_t)blockIdx.x * nwaves + wave; u < a.units; u += (int64_t)gridDim.x * nwaves) {
     const int64_t b = u / per_seq, c = u - b * per_seq;
     const rsrc_t rU = make_rsrc(a.U + b * a.T * a.dm, (uint32_t)(a.T * a.dm * 2));
     float colsum[2] = {0.0f, 0.0f};
@@ -322,9 +381,19 @@ __global__ void __launch_bounds__(kGateWaves * 64) gates_kernel(GateArgs a) {
           if (!col_ok[j]) continue;
           float* row = a.out + (((int64_t)gi[j] * a.B + b) * a.H + hi_[j]) * a.nout;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t t = t0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (t < a.T) row[t] = sc[j] * sigmoidf_(acc[j][r] + bias[j]);
+          for (int q = 0; q < 4; ++q) {
+            // four consecutive tokens per register quad: one 16-byte store when whole and aligned
+            const int64_t t = t0 + 8 * q + 4 * hf;
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = sc[j] * sigmoidf_(acc[j][4 * q + u] + bias[j]);
+            if (a.nout % 4 == 0 && t + 3 < a.T) {
+              *(float4*)(row + t) = float4{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (t + u < a.T) row[t + u] = v[u];
+            }
           }
         }
       }
@@ -369,7 +438,10 @@ atlasmem_status launch_gates(const void* U, int64_t B, int64_t T, int dm, int H,
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
                                               hipSuccess)
     return ATLASMEM_E_DEVICE;
-  const int64_t want = (a.units + kGateWaves - 1) / kGateWaves;
+  // one workgroup per CU (the weights fill most of the LDS); as many waves as the units keep busy
+  const int64_t per_cu = (a.units + ncu - 1) / ncu;
+  const int nw = per_cu < 4 ? 4 : (per_cu > kGateWaves ? kGateWaves : (int)per_cu);
+  const int64_t want = (a.units + nw - 1) / nw;
   const unsigned grid = (unsigned)(want < ncu ? want : ncu);
   for (int n0 = 0; n0 < a.ncol; n0 += kGateCols) {
     a.n0 = n0;
@@ -377,12 +449,12 @@ atlasmem_status launch_gates(const void* U, int64_t B, int64_t T, int dm, int H,
       if (hipFuncSetAttribute((const void*)gates_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
           hipSuccess)
         return ATLASMEM_E_DEVICE;
-      hipLaunchKernelGGL(gates_kernel<true>, dim3(grid), dim3(kGateWaves * 64), lds, st, a);
+      hipLaunchKernelGGL(gates_kernel<true>, dim3(grid), dim3(nw * 64), lds, st, a);
     } else {
       if (hipFuncSetAttribute((const void*)gates_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds) != hipSuccess)
         return ATLASMEM_E_DEVICE;
-      hipLaunchKernelGGL(gates_kernel<false>, dim3(grid), dim3(kGateWaves * 64), lds, st, a);
+      hipLaunchKernelGGL(gates_kernel<false>, dim3(grid), dim3(nw * 64), lds, st, a);
     }
     AM_LAUNCH_CHECK();
   }
