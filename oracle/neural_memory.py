@@ -9,7 +9,10 @@ What it computes, and where the pages define it
 * Memory M_W: a linear map (M(x) = W x) or a 2-layer SiLU MLP
   (M(x) = W2 silu(W1 x)).  Deep memory: "Titans: Learning to Memorize at Test
   Time" (titans-pytorch-mlx README), Key Innovations item 3; titans-torch 0.1.2
-  (PyPI), API Reference, NeuralLongTermMemory (num_layers = 2).
+  (PyPI), API Reference, NeuralLongTermMemory (num_layers = 2).  The residual
+  2-layer memory M(x) = x + W2 silu(W1 x) (d_in == d_value) is ATLAS's default
+  memory ("ATLAS ... | Summary", section 5.1; the pages give no formula, the
+  residual adds the memory's input to its output).
 * Associative loss l(M; x_t) = ||M(k_t) - v_t||^2 (sum of squares, no 1/d):
   titans-pytorch-mlx README, Core Equations, Eq. 12.  For a linear memory its
   gradient is (prediction error) x (key), the delta rule: Atlas-Torch README,
@@ -57,13 +60,14 @@ from scipy.special import expit
 
 LINEAR = 0
 MLP2_SILU = 1
+MLP2_SILU_RESIDUAL = 2      # x + W2 silu(W1 x): the default memory of ATLAS (d_in == d_value)
 PER_TOKEN = 0
 PER_CHUNK = 1
 
 
 @dataclasses.dataclass(frozen=True)
 class MemoryConfig:
-    kind: int                 # LINEAR or MLP2_SILU
+    kind: int                 # LINEAR, MLP2_SILU or MLP2_SILU_RESIDUAL
     d_key: int
     d_value: int
     d_hidden: int = 0
@@ -110,29 +114,36 @@ def silu_prime(z):
     return s * (1.0 + z * (1.0 - s))
 
 
-def memory_apply(params, x):
-    """M_W(x) for one input vector."""
+def memory_apply(params, x, residual: bool = False):
+    """M_W(x) for one input vector; with `residual` the 2-layer memory adds its input,
+    M(x) = x + W2 silu(W1 x) ("ATLAS ... | Summary", section 5.1: the default memory is a
+    two-layer residual MLP)."""
     if len(params) == 1:
         return params[0] @ x
     w1, w2 = params
-    return w2 @ silu(w1 @ x)
+    y = w2 @ silu(w1 @ x)
+    return x + y if residual else y
 
 
-def loss(params, x, v) -> float:
+def loss(params, x, v, residual: bool = False) -> float:
     """l = ||M_W(x) - v||^2 (titans-pytorch-mlx README, Eq. 12)."""
-    r = memory_apply(params, x) - v
+    r = memory_apply(params, x, residual) - v
     return float(r @ r)
 
 
-def loss_grad(params, x, v):
-    """Gradient of ||M_W(x) - v||^2 with respect to each weight matrix, by the chain rule."""
+def loss_grad(params, x, v, residual: bool = False):
+    """Gradient of ||M_W(x) - v||^2 with respect to each weight matrix, by the chain rule.  The
+    residual input x does not depend on the weights: it only shifts the prediction error."""
     if len(params) == 1:
         w = params[0]
         return [np.outer(2.0 * (w @ x - v), x)]
     w1, w2 = params
     z = w1 @ x
     h = silu(z)
-    e = 2.0 * (w2 @ h - v)                       # dl/dy
+    y = w2 @ h
+    if residual:
+        y = x + y
+    e = 2.0 * (y - v)                            # dl/dy
     g2 = np.outer(e, h)                          # dl/dW2
     g1 = np.outer((w2.T @ e) * silu_prime(z), x)  # dl/dW1
     return [g1, g2]
@@ -191,6 +202,9 @@ def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, g
     X = poly_features(K, cfg.poly_degree)
     Xq = poly_features(Q, cfg.poly_degree)
     V = np.asarray(V, dtype=np.float64)
+    res = cfg.kind == MLP2_SILU_RESIDUAL
+    if res and X.shape[1] != cfg.d_value:
+        raise ValueError("a residual memory needs d_in == d_value")
     hist = list(history or [])[-(c - 1):] if c > 1 else []
 
     def token(i):
@@ -209,14 +223,14 @@ def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, g
             bounds.append(([w.copy() for w in W], [m.copy() for m in S]))
         w_bar = [w.copy() for w in W]                     # chunk-start weights
         for t in range(s, e):                              # retrieval at the chunk-start weights
-            Y[t] = memory_apply(w_bar, Xq[t])
+            Y[t] = memory_apply(w_bar, Xq[t], res)
         if cfg.gate_mode == PER_TOKEN:
             cache = {}
 
             def grad_at(i):
                 if i not in cache:
                     tok = token(i)
-                    cache[i] = None if tok is None else (loss_grad(w_bar, tok[0], tok[1]), tok[2])
+                    cache[i] = None if tok is None else (loss_grad(w_bar, tok[0], tok[1], res), tok[2])
                 return cache[i]
 
             for t in range(s, e):
@@ -234,7 +248,7 @@ def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, g
         else:
             G = [np.zeros_like(w) for w in W]
             for t in range(s, e):
-                for G_m, g_m in zip(G, loss_grad(w_bar, X[t], V[t])):
+                for G_m, g_m in zip(G, loss_grad(w_bar, X[t], V[t], res)):
                     G_m += g_m
             if cfg.ns_steps > 0:
                 G = [newton_schulz(g, cfg.ns_steps, cfg.ns_coeffs, cfg.ns_eps) for g in G]

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from oracle import MemoryConfig, LINEAR, MLP2_SILU, PER_TOKEN, PER_CHUNK
+from oracle import MemoryConfig, LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, PER_TOKEN, PER_CHUNK
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 NS = (3.4445, -4.7750, 2.0315)
@@ -33,11 +33,13 @@ def rand_params(r, kind, d_in, d_v, d_h, scale=0.5):
     return [r.normal(0, scale, (d_h, d_in)), r.normal(0, scale, (d_v, d_h))]
 
 
-def torch_memory(params, x):
-    """M_W(x) written with torch primitives (silu from torch.nn.functional)."""
+def torch_memory(params, x, residual=False):
+    """M_W(x) written with torch primitives (silu from torch.nn.functional); the residual memory
+    adds its input."""
     if len(params) == 1:
         return params[0] @ x
-    return params[1] @ torch.nn.functional.silu(params[0] @ x)
+    y = params[1] @ torch.nn.functional.silu(params[0] @ x)
+    return x + y if residual else y
 
 
 def phi_triu(x, degree):
@@ -50,12 +52,12 @@ def phi_triu(x, degree):
     return np.concatenate([np.ones(x.shape[:-1] + (1,)), x, 0.5 * x[..., iu] * x[..., ju]], axis=-1)
 
 
-def autograd_window_grad(params_np, xs, vs, ws):
+def autograd_window_grad(params_np, xs, vs, ws, residual=False):
     """Gradient of sum_i w_i ||M_W(x_i) - v_i||^2 with respect to every weight matrix, by autograd."""
     params = [torch.tensor(p, dtype=torch.float64, requires_grad=True) for p in params_np]
     L = torch.zeros((), dtype=torch.float64)
     for x, v, w in zip(xs, vs, ws):
-        r = torch_memory(params, torch.tensor(x)) - torch.tensor(v)
+        r = torch_memory(params, torch.tensor(x), residual) - torch.tensor(v)
         L = L + w * (r * r).sum()
     if not L.requires_grad:
         return [np.zeros_like(p) for p in params_np]
@@ -82,24 +84,25 @@ def bruteforce_run(cfg, params, momenta, K, Q, V, th, et, al, ga):
     X = phi_triu(K, cfg.poly_degree)
     Xq = phi_triu(Q, cfg.poly_degree)
     T, C, c = K.shape[0], cfg.chunk, cfg.omega_window
+    res = cfg.kind == MLP2_SILU_RESIDUAL
     Y = np.zeros((T, cfg.d_value))
     for s in range(0, T, C):
         e = min(s + C, T)  # a final partial chunk holds the rest
         wb = [w.copy() for w in W]
         tw = [torch.tensor(w) for w in wb]
         for t in range(s, e):
-            Y[t] = torch_memory(tw, torch.tensor(Xq[t])).numpy()
+            Y[t] = torch_memory(tw, torch.tensor(Xq[t]), res).numpy()
         if cfg.gate_mode == PER_TOKEN:
             for t in range(s, e):
                 idx = [i for i in range(t - c + 1, t + 1) if i >= 0]
                 ws = [(ga[i] if c > 1 else 1.0) for i in idx]
-                G = autograd_window_grad(wb, [X[i] for i in idx], [V[i] for i in idx], ws)
+                G = autograd_window_grad(wb, [X[i] for i in idx], [V[i] for i in idx], ws, res)
                 for m in range(len(W)):
                     S[m] = et[t] * S[m] - th[t] * G[m]
                     W[m] = (1 - al[t]) * W[m] + S[m]
         else:
             idx = list(range(s, e))
-            G = autograd_window_grad(wb, [X[i] for i in idx], [V[i] for i in idx], [1.0] * len(idx))
+            G = autograd_window_grad(wb, [X[i] for i in idx], [V[i] for i in idx], [1.0] * len(idx), res)
             if cfg.ns_steps:
                 G = [ns5_svd(g, cfg.ns_steps) for g in G]
             k = s // C
@@ -134,16 +137,36 @@ def maxrel(a, b):
 # ----------------------------------------------------------------------------- gradients
 
 
-@pytest.mark.parametrize("kind", [LINEAR, MLP2_SILU])
+@pytest.mark.parametrize("kind", [LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL])
 def test_loss_gradient_matches_autograd(kind):
     r = rng(1)
-    params = rand_params(r, kind, 7, 5, 9)
-    x, v = r.normal(size=7), r.normal(size=5)
-    got = oracle.loss_grad(params, x, v)
-    ref = autograd_window_grad(params, [x], [v], [1.0])
+    res = kind == MLP2_SILU_RESIDUAL
+    d_in, d_v = (6, 6) if res else (7, 5)
+    params = rand_params(r, kind, d_in, d_v, 9)
+    x, v = r.normal(size=d_in), r.normal(size=d_v)
+    got = oracle.loss_grad(params, x, v, res)
+    ref = autograd_window_grad(params, [x], [v], [1.0], res)
     for g, h in zip(got, ref):
         assert g.shape == h.shape
         np.testing.assert_allclose(g, h, rtol=1e-13, atol=1e-13)
+
+
+def test_residual_memory_identity_and_shifted_target():
+    """With W2 = 0 the residual memory is the identity; its gradient equals the plain memory's
+    for the target v - x (the residual only shifts the prediction error)."""
+    r = rng(2)
+    w1, w2 = rand_params(r, MLP2_SILU, 6, 6, 8)
+    x, v = r.normal(size=6), r.normal(size=6)
+    assert np.array_equal(oracle.memory_apply([w1, np.zeros_like(w2)], x, True), x)
+    g_res = oracle.loss_grad([w1, w2], x, v, True)
+    g_plain = oracle.loss_grad([w1, w2], x, v - x)
+    for a, b in zip(g_res, g_plain):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+    with pytest.raises(ValueError):
+        cfg = MemoryConfig(MLP2_SILU_RESIDUAL, 4, 3, 5)
+        oracle.run_memory(cfg, rand_params(r, MLP2_SILU, 4, 3, 5), rand_params(r, MLP2_SILU, 4, 3, 5),
+                          r.normal(size=(4, 4)), r.normal(size=(4, 4)), r.normal(size=(4, 3)), np.ones(4),
+                          np.ones(4), np.zeros(4))
 
 
 def test_linear_gradient_is_delta_rule_outer_product():
@@ -275,6 +298,10 @@ CASES = [
     (MLP2_SILU, 13, 3, 2, 5, 2, 5, 2, PER_TOKEN, 0),
     (MLP2_SILU, 10, 3, 2, 5, 1, 4, 1, PER_CHUNK, 5),
     (LINEAR, 7, 4, 3, 0, 1, 3, 1, PER_CHUNK, 0),
+    # the residual memory x + W2 silu(W1 x) (d_in == d_v; poly 2 on d_k = 2 gives d_in = 6)
+    (MLP2_SILU_RESIDUAL, 12, 3, 3, 5, 1, 4, 3, PER_TOKEN, 0),
+    (MLP2_SILU_RESIDUAL, 12, 2, 6, 5, 2, 4, 2, PER_TOKEN, 0),
+    (MLP2_SILU_RESIDUAL, 13, 4, 4, 6, 1, 4, 1, PER_CHUNK, 5),
 ]
 
 
