@@ -28,10 +28,13 @@ int64_t feature_count(int dk, int poly) { return poly == 1 ? dk : 1 + dk + (int6
 atlasmem_status validate(const atlasmem_config* c) {
   if (!c) return ATLASMEM_E_INVALID;
   if (c->abi_version != ATLASMEM_ABI_VERSION) return ATLASMEM_E_INVALID;
-  if (c->memory_kind != ATLASMEM_LINEAR && c->memory_kind != ATLASMEM_MLP2_SILU) return ATLASMEM_E_INVALID;
+  if (c->memory_kind != ATLASMEM_LINEAR && c->memory_kind != ATLASMEM_MLP2_SILU &&
+      c->memory_kind != ATLASMEM_MLP2_SILU_RESIDUAL)
+    return ATLASMEM_E_INVALID;
+  const bool mlp = c->memory_kind != ATLASMEM_LINEAR;
   if (c->batch < 1 || c->heads < 1 || c->d_key < 1 || c->d_value < 1 || c->chunk < 1 || c->omega_window < 1)
     return ATLASMEM_E_INVALID;
-  if (c->memory_kind == ATLASMEM_MLP2_SILU && c->d_hidden < 1) return ATLASMEM_E_INVALID;
+  if (mlp && c->d_hidden < 1) return ATLASMEM_E_INVALID;
   if (c->poly_degree != 1 && c->poly_degree != 2) return ATLASMEM_E_INVALID;
   if (c->gate_mode != ATLASMEM_PER_TOKEN && c->gate_mode != ATLASMEM_PER_CHUNK) return ATLASMEM_E_INVALID;
   if (c->ns_steps < 0 || c->ns_steps > 16) return ATLASMEM_E_INVALID;
@@ -46,6 +49,8 @@ atlasmem_status validate(const atlasmem_config* c) {
     return ATLASMEM_E_SHAPE;
   const int64_t din = feature_count(c->d_key, c->poly_degree);
   if (din > 16384) return ATLASMEM_E_SHAPE;
+  // the residual memory adds its input to its output
+  if (c->memory_kind == ATLASMEM_MLP2_SILU_RESIDUAL && din != c->d_value) return ATLASMEM_E_INVALID;
   // valid but not provided
   if (c->gate_mode == ATLASMEM_PER_CHUNK && c->omega_window > 1) return ATLASMEM_E_UNSUPPORTED;
   if (c->gate_mode == ATLASMEM_PER_TOKEN && c->ns_steps > 0) return ATLASMEM_E_UNSUPPORTED;
@@ -62,14 +67,16 @@ Dims make_dims(const atlasmem_config* c) {
   d.M = c->batch * c->heads;
   d.dk = c->d_key;
   d.dv = c->d_value;
-  d.dh = c->memory_kind == ATLASMEM_MLP2_SILU ? c->d_hidden : 0;
+  d.dh = c->memory_kind != ATLASMEM_LINEAR ? c->d_hidden : 0;
   d.poly = c->poly_degree;
   d.din = (int)feature_count(c->d_key, c->poly_degree);
   d.C = c->chunk;
   d.c = c->omega_window;
   d.Rk = d.C + d.c - 1;
   d.Rt = d.Rk + d.C;
-  d.kind = c->memory_kind;
+  // both 2-layer memories run the MLP path; the residual one adds its input in the epilogues
+  d.kind = c->memory_kind == ATLASMEM_LINEAR ? ATLASMEM_LINEAR : ATLASMEM_MLP2_SILU;
+  d.residual = c->memory_kind == ATLASMEM_MLP2_SILU_RESIDUAL;
   if (d.kind == ATLASMEM_LINEAR) {
     d.P1 = (int64_t)d.dv * d.din;
     d.P = d.P1;

@@ -18,7 +18,8 @@ struct Dims {
   int Rt;       // key rows + query rows = Rk + C
   int64_t P;    // parameters per memory
   int64_t P1;   // size of W1 (MLP) / W (linear)
-  int kind, gate_mode, ns_steps;
+  int kind, gate_mode, ns_steps;  // kind: LINEAR or MLP2_SILU (also for the residual memory)
+  bool residual;                  // M(x) = x + W2 silu(W1 x)
   float ns_a, ns_b, ns_c, ns_eps;
   int in_bf16, out_bf16;
   bool split;   // bf16 hi/lo split products

@@ -125,7 +125,10 @@ struct EpiY {
   int Rk, c, dv;
   void* Y;
   int out_bf16;
+  int residual;  // the residual memory adds its input: feature `col` of the same row
+  FeatRows fr;   // the rows of the product (keys, then queries), for the residual input
   __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    if (residual) v += fr.feat(z, row, col);
     if (row < Rk) {
       const int64_t tau = s - (c - 1) + row;
       const float vv = (tau >= 0) ? load_in(V, ((int64_t)z * T + tau) * dv + col, in_bf16)
@@ -300,7 +303,8 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
       {
         StridedLoader la = strided(h->Z, zsz, dh, 1, 1, nrows, dh, XF_SILU);
         StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);  // B(k=h, j=v) = W2[v][h]
-        EpiY ep{h->D2, (int64_t)Rk * dv, V, d.in_bf16, h->hv[h->hcur], ld, s, Rk, c, dv, Y, d.out_bf16};
+        EpiY ep{h->D2, (int64_t)Rk * dv, V, d.in_bf16, h->hv[h->hcur], ld, s, Rk, c, dv, Y, d.out_bf16,
+                d.residual, feat_rows(h, K, Q, ld, s, Rk, nrows, 1)};
         gemm_any(split, false, false, nrows, dv, dh, M, la, lb, ep, st);
       }
       // Pm = D2 W2 -> D1 = Pm * silu'(Z)
@@ -397,7 +401,8 @@ atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, int64_t ld, vo
     {
       StridedLoader la = strided(h->Zr, zsz, dh, 1, 1, rows, dh, XF_SILU);
       StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);
-      EpiY ep{nullptr, 0, nullptr, d.in_bf16, nullptr, ld, s, 0, d.c, dv, Y, d.out_bf16};
+      EpiY ep{nullptr, 0, nullptr, d.in_bf16, nullptr, ld, s, 0, d.c, dv, Y, d.out_bf16, d.residual,
+              feat_rows(h, nullptr, Q, ld, s, 0, rows, 1)};
       gemm_any(d.split, false, false, rows, dv, dh, M, la, lb, ep, st);
     }
     AM_LAUNCH_CHECK();

@@ -42,6 +42,7 @@ import numpy as np
 
 LINEAR = 0
 MLP2_SILU = 1
+MLP2_SILU_RESIDUAL = 2
 PER_TOKEN = 0
 PER_CHUNK = 1
 F32 = 0

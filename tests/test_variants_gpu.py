@@ -1,0 +1,69 @@
+"""GPU parity of the memory variants against the fp64 oracle, through the C ABI.
+
+The residual 2-layer memory M(x) = x + W2 silu(W1 x) (ATLAS's default memory) runs the general
+MLP path with its input added in the prediction and retrieval epilogues.  Tolerances as for the
+plain memory: max |x - r| / max |r| per tensor within 2e-2 for bf16 inputs.
+"""
+
+import numpy as np
+import pytest
+
+from helpers import BF16_TOL, DEV, compare, config_for, log, maxrel, oracle_run, run_gpu, segment, to_dev
+from test_learned_neural_amd import atlasmem as am
+from test_learned_neural_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+R = synth.MLP2_SILU_RESIDUAL
+
+RESIDUAL = [
+    # (name, workload, variant, overrides, call boundaries or None)
+    ("mlp64_T256", 1, "stabilised", dict(kind=R, batch=1, heads=4, T=256), None),
+    ("window3_d40_history_rows", 3, "stabilised",
+     dict(kind=R, batch=1, heads=3, T=144, d_key=40, poly_degree=1, d_value=40, d_hidden=72, chunk=48,
+          omega_window=3), [0, 48, 96, 144]),
+    ("poly2_d4_to_15_window2", 3, "stabilised",
+     dict(kind=R, batch=2, heads=1, T=96, d_key=4, d_value=15, d_hidden=24, chunk=24, omega_window=2), None),
+    ("ns5_per_chunk_general_path", 4, "literal", dict(kind=R, batch=1, heads=3, T=512), None),
+    ("streamed_uneven_calls", 1, "stabilised", dict(kind=R, batch=1, heads=2, T=192),
+     [0, 1, 2, 3, 70, 71, 150, 192]),
+]
+
+
+@pytest.mark.parametrize("case", RESIDUAL, ids=[c[0] for c in RESIDUAL])
+def test_residual_memory_parity(case):
+    name, idx, variant, ov, splits = case
+    log(f"CASE residual {name}")
+    inp = synth.make_inputs(idx, variant, **ov)
+    got = run_gpu(inp, splits=splits)
+    ref = oracle_run(inp)
+    errs = compare(f"residual_{name}", inp.spec, got, ref, BF16_TOL)
+    assert got[3] == am.OK
+    assert all(v <= BF16_TOL for v in errs.values()), errs
+
+
+def test_residual_retrieve_and_shape_error():
+    """Retrieval alone adds the query's features too; a residual memory whose input width
+    differs from its output width is refused."""
+    import torch
+    import oracle
+    inp = synth.make_inputs(1, "stabilised", kind=R, batch=1, heads=2, T=64)
+    s = inp.spec
+    log("CASE residual_retrieve")
+    mem = am.Memory(config_for(s), to_dev(inp.W0))
+    seg = segment(inp, 0, 64)
+    Y = torch.empty((s.n_mem, 64, s.d_value), dtype=torch.float32, device=DEV)
+    mem.retrieve(seg["Q"], 64, Y)
+    torch.cuda.synchronize()
+    mem.close()
+    cfg = oracle.config_from(s)
+    Qf = synth.bf16_bits_to_f32(inp.Q).astype(np.float64) if s.input_dtype == synth.BF16 else inp.Q
+    ref = np.stack([np.stack([oracle.memory_apply(oracle.unflatten(cfg, inp.W0[m]), Qf[m, t], True)
+                              for t in range(64)]) for m in range(s.n_mem)])
+    err = maxrel(Y.cpu().numpy(), ref)
+    log(f"PARITY residual_retrieve: Y={err:.3e}")
+    assert err <= BF16_TOL
+    bad = synth.spec(1, "stabilised", kind=R, d_value=32)
+    with pytest.raises(am.AtlasMemError) as e:
+        am.Memory(config_for(bad))
+    assert e.value.status == am.E_INVALID
