@@ -5,7 +5,7 @@ import this package; the library itself never does.
 """
 
 from .neural_memory import (  # noqa: F401
-    LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, PER_TOKEN, PER_CHUNK, MemoryConfig, MemoryResult, flatten, loss, loss_grad,
+    LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, MLP2_GATED, PER_TOKEN, PER_CHUNK, MemoryConfig, MemoryResult, flatten, loss, loss_grad,
     memory_apply, newton_schulz, poly_feature_count, poly_features, run_many, run_memory, silu,
     silu_prime, unflatten,
 )

@@ -12,7 +12,9 @@ What it computes, and where the pages define it
   (PyPI), API Reference, NeuralLongTermMemory (num_layers = 2).  The residual
   2-layer memory M(x) = x + W2 silu(W1 x) (d_in == d_value) is ATLAS's default
   memory ("ATLAS ... | Summary", section 5.1; the pages give no formula, the
-  residual adds the memory's input to its output).
+  residual adds the memory's input to its output).  ATLAS++ uses a gated MLP
+  (same section); reading taken: M(x) = W2 (silu(W1 x) * (W3 x)), a SiLU branch
+  gating a linear one elementwise, weights [W1, W3, W2].
 * Associative loss l(M; x_t) = ||M(k_t) - v_t||^2 (sum of squares, no 1/d):
   titans-pytorch-mlx README, Core Equations, Eq. 12.  For a linear memory its
   gradient is (prediction error) x (key), the delta rule: Atlas-Torch README,
@@ -61,13 +63,14 @@ from scipy.special import expit
 LINEAR = 0
 MLP2_SILU = 1
 MLP2_SILU_RESIDUAL = 2      # x + W2 silu(W1 x): the default memory of ATLAS (d_in == d_value)
+MLP2_GATED = 3              # W2 (silu(W1 x) * (W3 x)): the gated memory of ATLAS++
 PER_TOKEN = 0
 PER_CHUNK = 1
 
 
 @dataclasses.dataclass(frozen=True)
 class MemoryConfig:
-    kind: int                 # LINEAR, MLP2_SILU or MLP2_SILU_RESIDUAL
+    kind: int                 # LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL or MLP2_GATED
     d_key: int
     d_value: int
     d_hidden: int = 0
@@ -117,9 +120,13 @@ def silu_prime(z):
 def memory_apply(params, x, residual: bool = False):
     """M_W(x) for one input vector; with `residual` the 2-layer memory adds its input,
     M(x) = x + W2 silu(W1 x) ("ATLAS ... | Summary", section 5.1: the default memory is a
-    two-layer residual MLP)."""
+    two-layer residual MLP).  Three matrices [W1, W3, W2] are the gated memory
+    W2 (silu(W1 x) * (W3 x)) (same section: ATLAS++)."""
     if len(params) == 1:
         return params[0] @ x
+    if len(params) == 3:
+        w1, w3, w2 = params
+        return w2 @ (silu(w1 @ x) * (w3 @ x))
     w1, w2 = params
     y = w2 @ silu(w1 @ x)
     return x + y if residual else y
@@ -137,6 +144,14 @@ def loss_grad(params, x, v, residual: bool = False):
     if len(params) == 1:
         w = params[0]
         return [np.outer(2.0 * (w @ x - v), x)]
+    if len(params) == 3:
+        w1, w3, w2 = params
+        z1, z3 = w1 @ x, w3 @ x
+        a = silu(z1)
+        hg = a * z3                                  # gated hidden activation
+        e = 2.0 * (w2 @ hg - v)                      # dl/dy
+        back = w2.T @ e                              # dl/dhg
+        return [np.outer(back * z3 * silu_prime(z1), x), np.outer(back * a, x), np.outer(e, hg)]
     w1, w2 = params
     z = w1 @ x
     h = silu(z)
@@ -279,6 +294,9 @@ def unflatten(cfg: MemoryConfig, flat) -> list:
     if cfg.kind == LINEAR:
         return [flat.reshape(cfg.d_value, d_in)]
     n1 = cfg.d_hidden * d_in
+    if cfg.kind == MLP2_GATED:
+        return [flat[:n1].reshape(cfg.d_hidden, d_in), flat[n1:2 * n1].reshape(cfg.d_hidden, d_in),
+                flat[2 * n1:].reshape(cfg.d_value, cfg.d_hidden)]
     return [flat[:n1].reshape(cfg.d_hidden, d_in), flat[n1:].reshape(cfg.d_value, cfg.d_hidden)]
 
 

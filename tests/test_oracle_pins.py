@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from oracle import MemoryConfig, LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, PER_TOKEN, PER_CHUNK
+from oracle import MemoryConfig, LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, MLP2_GATED, PER_TOKEN, PER_CHUNK
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 NS = (3.4445, -4.7750, 2.0315)
@@ -30,6 +30,8 @@ def rng(seed):
 def rand_params(r, kind, d_in, d_v, d_h, scale=0.5):
     if kind == LINEAR:
         return [r.normal(0, scale, (d_v, d_in))]
+    if kind == MLP2_GATED:
+        return [r.normal(0, scale, (d_h, d_in)), r.normal(0, scale, (d_h, d_in)), r.normal(0, scale, (d_v, d_h))]
     return [r.normal(0, scale, (d_h, d_in)), r.normal(0, scale, (d_v, d_h))]
 
 
@@ -38,6 +40,8 @@ def torch_memory(params, x, residual=False):
     adds its input."""
     if len(params) == 1:
         return params[0] @ x
+    if len(params) == 3:  # gated: W2 (silu(W1 x) * (W3 x))
+        return params[2] @ (torch.nn.functional.silu(params[0] @ x) * (params[1] @ x))
     y = params[1] @ torch.nn.functional.silu(params[0] @ x)
     return x + y if residual else y
 
@@ -137,7 +141,7 @@ def maxrel(a, b):
 # ----------------------------------------------------------------------------- gradients
 
 
-@pytest.mark.parametrize("kind", [LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL])
+@pytest.mark.parametrize("kind", [LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, MLP2_GATED])
 def test_loss_gradient_matches_autograd(kind):
     r = rng(1)
     res = kind == MLP2_SILU_RESIDUAL
@@ -167,6 +171,25 @@ def test_residual_memory_identity_and_shifted_target():
         oracle.run_memory(cfg, rand_params(r, MLP2_SILU, 4, 3, 5), rand_params(r, MLP2_SILU, 4, 3, 5),
                           r.normal(size=(4, 4)), r.normal(size=(4, 4)), r.normal(size=(4, 3)), np.ones(4),
                           np.ones(4), np.zeros(4))
+
+
+def test_gated_memory_reduces_to_plain_when_gate_is_one():
+    """If W3 x = 1 for every hidden unit, the gated memory is the plain one and its W1 and W2
+    gradients are the plain memory's; its W3 gradient is (W2^T e) * silu(W1 x) times x^T."""
+    r = rng(3)
+    w1, w2 = rand_params(r, MLP2_SILU, 5, 3, 7)
+    x = np.zeros(5)
+    x[0] = 1.0
+    w3 = r.normal(size=(7, 5))
+    w3[:, 0] = 1.0
+    v = r.normal(size=3)
+    np.testing.assert_allclose(oracle.memory_apply([w1, w3, w2], x), oracle.memory_apply([w1, w2], x), rtol=1e-15)
+    g1, g3, g2 = oracle.loss_grad([w1, w3, w2], x, v)
+    p1, p2 = oracle.loss_grad([w1, w2], x, v)
+    np.testing.assert_allclose(g1, p1, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(g2, p2, rtol=1e-14, atol=1e-15)
+    e = 2.0 * (oracle.memory_apply([w1, w2], x) - v)
+    np.testing.assert_allclose(g3, np.outer((w2.T @ e) * oracle.silu(w1 @ x), x), rtol=1e-14, atol=1e-15)
 
 
 def test_linear_gradient_is_delta_rule_outer_product():
@@ -302,6 +325,10 @@ CASES = [
     (MLP2_SILU_RESIDUAL, 12, 3, 3, 5, 1, 4, 3, PER_TOKEN, 0),
     (MLP2_SILU_RESIDUAL, 12, 2, 6, 5, 2, 4, 2, PER_TOKEN, 0),
     (MLP2_SILU_RESIDUAL, 13, 4, 4, 6, 1, 4, 1, PER_CHUNK, 5),
+    # the gated memory W2 (silu(W1 x) * (W3 x))
+    (MLP2_GATED, 12, 3, 2, 5, 1, 4, 3, PER_TOKEN, 0),
+    (MLP2_GATED, 12, 3, 2, 5, 2, 4, 1, PER_TOKEN, 0),
+    (MLP2_GATED, 13, 3, 4, 6, 1, 4, 1, PER_CHUNK, 5),
 ]
 
 
