@@ -10,6 +10,9 @@
  *              M_W(x) = x + W2 silu(W1 x)        (MLP2_SILU_RESIDUAL, d_in == d_value: the
  *                                                 default memory of ATLAS, "ATLAS ... |
  *                                                 Summary", section 5.1)
+ *              M_W(x) = W2 (silu(W1 x) * (W3 x)) (MLP2_GATED, W3 like W1: the gated memory
+ *                                                 of ATLAS++, same section; parameters
+ *                                                 [W1 | W3 | W2])
  *   loss       l(W; x, v) = ||M_W(x) - v||^2      -- "Titans: Learning to Memorize at
  *              Test Time" (titans-pytorch-mlx README), Core Equations, Eq. 12
  *   momentum   S_t = eta_t S_{t-1} - theta_t G_t  -- same page, Eq. 14
@@ -67,7 +70,12 @@ typedef enum {
   ATLASMEM_E_NONFINITE = 6     /* a state element became NaN/Inf (reported by get_state)          */
 } atlasmem_status;
 
-typedef enum { ATLASMEM_LINEAR = 0, ATLASMEM_MLP2_SILU = 1, ATLASMEM_MLP2_SILU_RESIDUAL = 2 } atlasmem_memory_kind;
+typedef enum {
+  ATLASMEM_LINEAR = 0,
+  ATLASMEM_MLP2_SILU = 1,
+  ATLASMEM_MLP2_SILU_RESIDUAL = 2,
+  ATLASMEM_MLP2_GATED = 3
+} atlasmem_memory_kind;
 typedef enum { ATLASMEM_PER_TOKEN = 0, ATLASMEM_PER_CHUNK = 1 } atlasmem_gate_mode;
 typedef enum { ATLASMEM_F32 = 0, ATLASMEM_BF16 = 1 } atlasmem_dtype;
 

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libatlasmem.so")
 
 OK, E_INVALID, E_SHAPE, E_UNSUPPORTED, E_DEVICE, E_NOMEM, E_NONFINITE = range(7)
-LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL = 0, 1, 2
+LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, MLP2_GATED = 0, 1, 2, 3
 PER_TOKEN, PER_CHUNK = 0, 1
 F32, BF16 = 0, 1
 PREC_AUTO, PREC_BF16, PREC_BF16X3 = 0, 1, 2

@@ -28,9 +28,7 @@ int64_t feature_count(int dk, int poly) { return poly == 1 ? dk : 1 + dk + (int6
 atlasmem_status validate(const atlasmem_config* c) {
   if (!c) return ATLASMEM_E_INVALID;
   if (c->abi_version != ATLASMEM_ABI_VERSION) return ATLASMEM_E_INVALID;
-  if (c->memory_kind != ATLASMEM_LINEAR && c->memory_kind != ATLASMEM_MLP2_SILU &&
-      c->memory_kind != ATLASMEM_MLP2_SILU_RESIDUAL)
-    return ATLASMEM_E_INVALID;
+  if (c->memory_kind < ATLASMEM_LINEAR || c->memory_kind > ATLASMEM_MLP2_GATED) return ATLASMEM_E_INVALID;
   const bool mlp = c->memory_kind != ATLASMEM_LINEAR;
   if (c->batch < 1 || c->heads < 1 || c->d_key < 1 || c->d_value < 1 || c->chunk < 1 || c->omega_window < 1)
     return ATLASMEM_E_INVALID;
@@ -77,11 +75,14 @@ Dims make_dims(const atlasmem_config* c) {
   // both 2-layer memories run the MLP path; the residual one adds its input in the epilogues
   d.kind = c->memory_kind == ATLASMEM_LINEAR ? ATLASMEM_LINEAR : ATLASMEM_MLP2_SILU;
   d.residual = c->memory_kind == ATLASMEM_MLP2_SILU_RESIDUAL;
+  d.gated = c->memory_kind == ATLASMEM_MLP2_GATED;
+  // first-layer rows: W1 (and W3 below it, gated); the hidden buffers hold [Z1 | Z3] per row
+  d.dz = d.gated ? 2 * d.dh : d.dh;
   if (d.kind == ATLASMEM_LINEAR) {
     d.P1 = (int64_t)d.dv * d.din;
     d.P = d.P1;
   } else {
-    d.P1 = (int64_t)d.dh * d.din;
+    d.P1 = (int64_t)d.dz * d.din;
     d.P = d.P1 + (int64_t)d.dv * d.dh;
   }
   d.gate_mode = c->gate_mode;
@@ -179,9 +180,9 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
   const size_t state_end = cv.off;
   size_t oZ = 0, oD2 = 0, oD1 = 0, ocW = 0, ocS = 0, ooW = 0, ooS = 0, oscal = 0, oG = 0, oZr = 0;
   if (d.kind == ATLASMEM_MLP2_SILU) {
-    oZ = cv.take(sizeof(float) * M * d.Rt * d.dh);
+    oZ = cv.take(sizeof(float) * M * d.Rt * d.dz);
     oD2 = cv.take(sizeof(float) * M * d.Rk * d.dv);
-    oD1 = cv.take(sizeof(float) * M * d.Rk * d.dh);
+    oD1 = cv.take(sizeof(float) * M * d.Rk * d.dz);
     const int64_t per_chunk_floats = M * (2 * (int64_t)d.C + 2 * (int64_t)d.Rk + 3);
     int64_t ncb = ((int64_t)32 << 20) / 4 / per_chunk_floats;
     ncb = ncb < 1 ? 1 : (ncb > 4096 ? 4096 : ncb);
@@ -197,9 +198,9 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
     }
     if (d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0) oG = cv.take(sizeof(float) * M * d.P);
     int64_t rb = 1024;
-    while (rb > 64 && (int64_t)M * rb * d.dh * 4 > ((int64_t)256 << 20)) rb /= 2;
+    while (rb > 64 && (int64_t)M * rb * d.dz * 4 > ((int64_t)256 << 20)) rb /= 2;
     h->rb = (int)rb;
-    oZr = cv.take(sizeof(float) * M * rb * d.dh);
+    oZr = cv.take(sizeof(float) * M * rb * d.dz);
   }
   h->arena_bytes = cv.off;
   if (hipMalloc(&h->arena, h->arena_bytes) != hipSuccess) {

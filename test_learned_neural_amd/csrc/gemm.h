@@ -120,12 +120,14 @@ inline void launch_gemm(bool split, int M, int N, int K, int batch, const LA& la
 
 // ---------------------------------------------------------------------------- generic loaders
 
-enum Xform { XF_NONE = 0, XF_SILU = 1, XF_COEF = 2, XF_SCALE = 3 };
+enum Xform { XF_NONE = 0, XF_SILU = 1, XF_COEF = 2, XF_SCALE = 3, XF_GATED = 4 };
 
 // Element (outer, k) = xf(base[zoff(z) + outer * so + k * sk]); zoff(z) = (z / zdiv) * sz.
 // XF_COEF multiplies by coef[(z / zdiv) * cz + csel(z) + k]  (per-k coefficient; csel picks
 // one of two coefficient arrays by z % 2 when `pair` is set).
 // XF_SCALE multiplies by scale[z].
+// XF_GATED is silu(x) times the element `gofs` further on (the gated memory's activation
+// silu(Z1) * Z3, with Z3 stored beside Z1).
 struct StridedLoader {
   const float* base;
   int64_t sz, so, sk;
@@ -136,6 +138,7 @@ struct StridedLoader {
   const float* coef1;
   int64_t cz;
   const float* scale;
+  int64_t gofs;
   __device__ __forceinline__ void load8(int z, int outer, int k0, float* v) const {
     const int zz = z / zdiv;
     const float* p = base + zz * sz + (int64_t)outer * so;
@@ -149,6 +152,7 @@ struct StridedLoader {
       if (outer < outer_dim && k < K) {
         x = p[(int64_t)k * sk];
         if (xf == XF_SILU) x = siluf_(x);
+        else if (xf == XF_GATED) x = siluf_(x) * p[(int64_t)k * sk + gofs];
         else if (xf == XF_COEF) x *= cf[k];
         else if (xf == XF_SCALE) x *= sc;
       }

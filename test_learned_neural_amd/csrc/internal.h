@@ -20,6 +20,8 @@ struct Dims {
   int64_t P1;   // size of W1 (MLP) / W (linear)
   int kind, gate_mode, ns_steps;  // kind: LINEAR or MLP2_SILU (also for the residual memory)
   bool residual;                  // M(x) = x + W2 silu(W1 x)
+  bool gated;                     // M(x) = W2 (silu(W1 x) * (W3 x)), W3 stored after W1
+  int dz;                         // first-layer rows: d_hidden, or 2 d_hidden when gated
   float ns_a, ns_b, ns_c, ns_eps;
   int in_bf16, out_bf16;
   bool split;   // bf16 hi/lo split products

@@ -787,7 +787,7 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
 }  // namespace fz
 
 bool fused_supported(const Dims& d) {
-  return d.kind == ATLASMEM_MLP2_SILU && !d.residual && d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0 && d.dk == fz::D &&
+  return d.kind == ATLASMEM_MLP2_SILU && !d.residual && !d.gated && d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0 && d.dk == fz::D &&
          d.din == fz::D && d.dv == fz::D && d.dh == fz::HD && d.c == 1 && d.C % fz::GROWS == 0 && d.in_bf16 &&
          d.split;
 }

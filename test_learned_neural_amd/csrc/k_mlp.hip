@@ -142,15 +142,24 @@ struct EpiY {
   }
 };
 
-// D1 = Pm * silu'(Z)
+// D1 = Pm * silu'(Z).  Gated memory (rows of Z and D1 hold [Z1 | Z3] and [D1 | D3]):
+// D1 = Pm * Z3 * silu'(Z1), D3 = Pm * silu(Z1).
 struct EpiP {
   float* D1;
   const float* Z;
   int64_t d1z, zz;
-  int dh;
+  int dh, dz, gated;
   __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    const float zv = Z[(int64_t)z * zz + (int64_t)row * dh + col];
-    D1[(int64_t)z * d1z + (int64_t)row * dh + col] = v * silu_primef_(zv);
+    const float* zr = Z + (int64_t)z * zz + (int64_t)row * dz;
+    float* dr = D1 + (int64_t)z * d1z + (int64_t)row * dz;
+    const float z1 = zr[col];
+    if (gated) {
+      const float z3 = zr[dh + col];
+      dr[col] = v * z3 * silu_primef_(z1);
+      dr[dh + col] = v * siluf_(z1);
+    } else {
+      dr[col] = v * silu_primef_(z1);
+    }
   }
 };
 
@@ -221,6 +230,16 @@ static StridedLoader strided(const float* base, int64_t sz, int64_t so, int64_t 
   l.coef0 = l.coef1 = nullptr;
   l.cz = 0;
   l.scale = nullptr;
+  l.gofs = 0;
+  return l;
+}
+
+// The hidden activation H of the memory from the stored first-layer outputs: silu(Z) or, for the
+// gated memory, silu(Z1) * Z3 with Z3 d_hidden elements after Z1.
+static StridedLoader hidden(const Dims& d, const float* Z, int64_t sz, int64_t so, int64_t sk, int zdiv, int outer_dim,
+                            int K) {
+  StridedLoader l = strided(Z, sz, so, sk, zdiv, outer_dim, K, d.gated ? XF_GATED : XF_SILU);
+  l.gofs = d.dh;
   return l;
 }
 
@@ -259,13 +278,13 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
                            const float* eta, const float* alpha, const float* gamma, const Span& sp, void* Y,
                            hipStream_t st) {
   const int64_t T = sp.T, ld = sp.ld;
-  const int M = d.M, C = d.C, c = d.c, Rk = d.Rk, dh = d.dh, dv = d.dv, din = d.din;
+  const int M = d.M, C = d.C, c = d.c, Rk = d.Rk, dh = d.dh, dv = d.dv, din = d.din, dz = d.dz;
   const bool split = d.split;
   const bool feat_exact = d.poly == 1 && d.in_bf16;
   const int64_t nchunks = T / C;
   const int nq = Y ? C : 0;
   const int nrows = Rk + nq;
-  const int64_t zsz = (int64_t)d.Rt * dh;
+  const int64_t zsz = (int64_t)d.Rt * dz;
   const bool per_token = d.gate_mode == ATLASMEM_PER_TOKEN;
   atlasmem_status stt;
   if (!d.no_fused && fused_supported(d)) return launch_fused(h, d, K, Q, V, theta, eta, alpha, sp, Y, st);
@@ -292,16 +311,16 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
       const float* W1 = Win;
       const float* W2 = Win + d.P1;
 
-      // Z = X W1^T over key rows (+ query rows)
+      // Z = X W1^T over key rows (+ query rows); gated: [Z1 | Z3] = X [W1; W3]^T
       {
         FeatA la{feat_rows(h, K, Q, ld, s, Rk, nrows, 1)};
-        StridedLoader lb = strided(W1, d.P, din, 1, 1, dh, din);  // B(k=f, j=h) = W1[h][f]
-        EpiStore ep{h->Z, zsz, dh, 1};
-        gemm_any(split, feat_exact, false, nrows, dh, din, M, la, lb, ep, st);
+        StridedLoader lb = strided(W1, d.P, din, 1, 1, dz, din);  // B(k=f, j=h) = W1[h][f]
+        EpiStore ep{h->Z, zsz, dz, 1};
+        gemm_any(split, feat_exact, false, nrows, dz, din, M, la, lb, ep, st);
       }
-      // Yh = silu(Z) W2^T -> D2 (key rows), Y (query rows)
+      // Yh = H W2^T -> D2 (key rows), Y (query rows)
       {
-        StridedLoader la = strided(h->Z, zsz, dh, 1, 1, nrows, dh, XF_SILU);
+        StridedLoader la = hidden(d, h->Z, zsz, dz, 1, 1, nrows, dh);
         StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);  // B(k=h, j=v) = W2[v][h]
         EpiY ep{h->D2, (int64_t)Rk * dv, V, d.in_bf16, h->hv[h->hcur], ld, s, Rk, c, dv, Y, d.out_bf16,
                 d.residual, feat_rows(h, K, Q, ld, s, Rk, nrows, 1)};
@@ -311,7 +330,7 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
       {
         StridedLoader la = strided(h->D2, (int64_t)Rk * dv, dv, 1, 1, Rk, dv);
         StridedLoader lb = strided(W2, d.P, 1, dh, 1, dh, dv);  // B(k=v, j=h) = W2[v][h]
-        EpiP ep{h->D1, h->Z, (int64_t)Rk * dh, zsz, dh};
+        EpiP ep{h->D1, h->Z, (int64_t)Rk * dz, zsz, dh, dz, d.gated};
         gemm_any(split, false, false, Rk, dh, dv, M, la, lb, ep, st);
       }
       if (per_token) {
@@ -319,55 +338,64 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
         const float* c1 = (c > 1) ? h->oS + (int64_t)kb * Rk : h->cS + (int64_t)kb * C;
         const int64_t cz = (c > 1) ? (int64_t)h->ncb * Rk : (int64_t)h->ncb * C;
         const float* sc = h->scal + (int64_t)kb * 3;
-        // W2 pair: A(i=v, k=row) = D2[row][v] * coef[row], B(k=row, j=h) = silu(Z[row][h])
+        // W2 pair: A(i=v, k=row) = D2[row][v] * coef[row], B(k=row, j=h) = H[row][h]
         {
           StridedLoader la = strided(h->D2, (int64_t)Rk * dv, 1, dv, 2, dv, Rk, XF_COEF);
           la.coef0 = c0;
           la.coef1 = c1;
           la.cz = cz;
-          StridedLoader lb = strided(h->Z, zsz, 1, dh, 2, dh, Rk, XF_SILU);
+          StridedLoader lb = hidden(d, h->Z, zsz, 1, dz, 2, dh, Rk);
           EpiUpdPair ep{Win, Sin, Wout, Sout, d.P, d.P1, dh, sc, (int64_t)h->ncb * 3, h->flag};
           gemm_any(split, false, false, dv, dh, Rk, 2 * M, la, lb, ep, st);
         }
-        // W1 pair: A(i=h, k=row) = D1[row][h] * coef[row], B(k=row, j=f) = X[row][f]
+        // W1 pair (gated: W1 and W3 as one block of 2 d_hidden rows): A(i=h, k=row) =
+        // D1[row][h] * coef[row], B(k=row, j=f) = X[row][f]
         {
-          StridedLoader la = strided(h->D1, (int64_t)Rk * dh, 1, dh, 2, dh, Rk, XF_COEF);
+          StridedLoader la = strided(h->D1, (int64_t)Rk * dz, 1, dz, 2, dz, Rk, XF_COEF);
           la.coef0 = c0;
           la.coef1 = c1;
           la.cz = cz;
           FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 2)};
           EpiUpdPair ep{Win, Sin, Wout, Sout, d.P, 0, din, sc, (int64_t)h->ncb * 3, h->flag};
-          gemm_any(split, false, feat_exact, dh, din, Rk, 2 * M, la, lb, ep, st);
+          gemm_any(split, false, feat_exact, dz, din, Rk, 2 * M, la, lb, ep, st);
         }
       } else if (d.ns_steps == 0) {
         {
           StridedLoader la = strided(h->D2, (int64_t)Rk * dv, 1, dv, 1, dv, Rk);
-          StridedLoader lb = strided(h->Z, zsz, 1, dh, 1, dh, Rk, XF_SILU);
+          StridedLoader lb = hidden(d, h->Z, zsz, 1, dz, 1, dh, Rk);
           EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, d.P1, dh, theta, eta, alpha, sp.ldg, k, h->flag};
           gemm_any(split, false, false, dv, dh, Rk, M, la, lb, ep, st);
         }
         {
-          StridedLoader la = strided(h->D1, (int64_t)Rk * dh, 1, dh, 1, dh, Rk);
+          StridedLoader la = strided(h->D1, (int64_t)Rk * dz, 1, dz, 1, dz, Rk);
           FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)};
           EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, 0, din, theta, eta, alpha, sp.ldg, k, h->flag};
-          gemm_any(split, false, feat_exact, dh, din, Rk, M, la, lb, ep, st);
+          gemm_any(split, false, feat_exact, dz, din, Rk, M, la, lb, ep, st);
         }
       } else {
         {
           StridedLoader la = strided(h->D2, (int64_t)Rk * dv, 1, dv, 1, dv, Rk);
-          StridedLoader lb = strided(h->Z, zsz, 1, dh, 1, dh, Rk, XF_SILU);
+          StridedLoader lb = hidden(d, h->Z, zsz, 1, dz, 1, dh, Rk);
           EpiStore ep{h->G + d.P1, d.P, dh, 1};
           gemm_any(split, false, false, dv, dh, Rk, M, la, lb, ep, st);
         }
         {
-          StridedLoader la = strided(h->D1, (int64_t)Rk * dh, 1, dh, 1, dh, Rk);
+          StridedLoader la = strided(h->D1, (int64_t)Rk * dz, 1, dz, 1, dz, Rk);
           FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)};
           EpiStore ep{h->G, d.P, din, 1};
-          gemm_any(split, false, feat_exact, dh, din, Rk, M, la, lb, ep, st);
+          gemm_any(split, false, feat_exact, dz, din, Rk, M, la, lb, ep, st);
         }
+        // each weight matrix separately: W1, (W3,) W2
         NsUpdate u1{Win, Sin, Wout, Sout, d.P, 0, 1, theta, eta, alpha, sp.ldg, k, h->flag};
         stt = launch_ns(h->G, d.P, M, dh, din, d.ns_steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, split, nullptr, &u1, st);
         if (stt != ATLASMEM_OK) return stt;
+        if (d.gated) {
+          const int64_t o3 = (int64_t)dh * din;
+          NsUpdate u3{Win, Sin, Wout, Sout, d.P, o3, 1, theta, eta, alpha, sp.ldg, k, h->flag};
+          stt = launch_ns(h->G + o3, d.P, M, dh, din, d.ns_steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, split, nullptr,
+                          &u3, st);
+          if (stt != ATLASMEM_OK) return stt;
+        }
         NsUpdate u2{Win, Sin, Wout, Sout, d.P, d.P1, 1, theta, eta, alpha, sp.ldg, k, h->flag};
         stt = launch_ns(h->G + d.P1, d.P, M, dv, dh, d.ns_steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, split, nullptr,
                         &u2, st);
@@ -385,21 +413,21 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
 
 atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, int64_t ld, void* Y, hipStream_t st) {
   const Dims& d = h->d;
-  const int M = d.M, dh = d.dh, dv = d.dv, din = d.din;
+  const int M = d.M, dh = d.dh, dv = d.dv, din = d.din, dz = d.dz;
   const bool feat_exact = d.poly == 1 && d.in_bf16;
   const float* W1 = h->W[h->cur];
   const float* W2 = W1 + d.P1;
-  const int64_t zsz = (int64_t)h->rb * dh;
+  const int64_t zsz = (int64_t)h->rb * dz;
   for (int64_t s = 0; s < T; s += h->rb) {
     const int rows = (int)((T - s) < h->rb ? (T - s) : h->rb);
     {
       FeatA la{feat_rows(h, nullptr, Q, ld, s, 0, rows, 1)};
-      StridedLoader lb = strided(W1, d.P, din, 1, 1, dh, din);
-      EpiStore ep{h->Zr, zsz, dh, 1};
-      gemm_any(d.split, feat_exact, false, rows, dh, din, M, la, lb, ep, st);
+      StridedLoader lb = strided(W1, d.P, din, 1, 1, dz, din);
+      EpiStore ep{h->Zr, zsz, dz, 1};
+      gemm_any(d.split, feat_exact, false, rows, dz, din, M, la, lb, ep, st);
     }
     {
-      StridedLoader la = strided(h->Zr, zsz, dh, 1, 1, rows, dh, XF_SILU);
+      StridedLoader la = hidden(d, h->Zr, zsz, dz, 1, 1, rows, dh);
       StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);
       EpiY ep{nullptr, 0, nullptr, d.in_bf16, nullptr, ld, s, 0, d.c, dv, Y, d.out_bf16, d.residual,
               feat_rows(h, nullptr, Q, ld, s, 0, rows, 1)};

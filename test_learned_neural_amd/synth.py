@@ -28,7 +28,8 @@ workload 3 L2-normalises K, Q, V and scales theta by 0.1.
 
 Random stream: numpy default_rng(SeedSequence([workload, b, h])), drawn in the
 order K, Q, V (N(0,1) fp64), theta, eta, alpha (uniform), gamma (U(0,1), only
-for an Omega window > 1), then W1 (or W), then W2 (N(0, 1/fan_in)).
+for an Omega window > 1), then W1 (or W), then W2, then (gated memory) W3
+(N(0, 1/fan_in)).
 Preparation: cast to fp32, L2-normalise in fp32 where the workload says so,
 round to bf16 once (round-to-nearest-even) for bf16 workloads.
 """
@@ -43,6 +44,7 @@ import numpy as np
 LINEAR = 0
 MLP2_SILU = 1
 MLP2_SILU_RESIDUAL = 2
+MLP2_GATED = 3
 PER_TOKEN = 0
 PER_CHUNK = 1
 F32 = 0
@@ -94,6 +96,8 @@ class Spec:
     def param_count(self) -> int:
         if self.kind == LINEAR:
             return self.d_value * self.d_in
+        if self.kind == MLP2_GATED:
+            return 2 * self.d_hidden * self.d_in + self.d_value * self.d_hidden
         return self.d_hidden * self.d_in + self.d_value * self.d_hidden
 
 
@@ -184,12 +188,15 @@ class Inputs:
         return a.astype(np.float64)
 
     def split_params(self, flat: np.ndarray):
-        """Split one memory's flat parameter vector into its matrices (W) or (W1, W2)."""
+        """Split one memory's flat parameter vector into its matrices (W), (W1, W2) or (W1, W3, W2)."""
         s = self.spec
         flat = np.asarray(flat, dtype=np.float64)
         if s.kind == LINEAR:
             return [flat.reshape(s.d_value, s.d_in)]
         n1 = s.d_hidden * s.d_in
+        if s.kind == MLP2_GATED:
+            return [flat[:n1].reshape(s.d_hidden, s.d_in), flat[n1:2 * n1].reshape(s.d_hidden, s.d_in),
+                    flat[2 * n1:].reshape(s.d_value, s.d_hidden)]
         return [flat[:n1].reshape(s.d_hidden, s.d_in), flat[n1:].reshape(s.d_value, s.d_hidden)]
 
 
@@ -211,6 +218,9 @@ def _draw_memory(s: Spec, index: int, b: int, h: int):
         w1 = rng.normal(0.0, 1.0 / math.sqrt(s.d_in), size=(s.d_hidden, s.d_in))
         w2 = rng.normal(0.0, 1.0 / math.sqrt(s.d_hidden), size=(s.d_value, s.d_hidden))
         params = [w1, w2]
+        if s.kind == MLP2_GATED:  # drawn last, so the other draws match the plain memory's
+            w3 = rng.normal(0.0, 1.0 / math.sqrt(s.d_in), size=(s.d_hidden, s.d_in))
+            params = [w1, w3, w2]
     return k, q, v, theta, eta, alpha, gamma, params
 
 

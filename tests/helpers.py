@@ -98,6 +98,8 @@ def split_params(spec, flat):
     if spec.kind == synth.LINEAR:
         return [flat]
     n1 = spec.d_hidden * spec.d_in
+    if spec.kind == synth.MLP2_GATED:
+        return [flat[..., :n1], flat[..., n1:2 * n1], flat[..., 2 * n1:]]
     return [flat[..., :n1], flat[..., n1:]]
 
 
@@ -106,11 +108,12 @@ def compare(name, spec, got, ref, tol, check_state=True):
     Yg, Wg, Sg = got[:3]
     Yr, Wr, Sr = ref[:3]
     errs = {"Y": maxrel(Yg, Yr)}
+    names = ["1", "3", "2"] if spec.kind == synth.MLP2_GATED else ["1", "2"]  # storage order of the matrices
     if check_state:
         for i, (a, b) in enumerate(zip(split_params(spec, Wg), split_params(spec, Wr))):
-            errs[f"W{i + 1}"] = maxrel(a, b)
+            errs[f"W{names[i]}"] = maxrel(a, b)
         for i, (a, b) in enumerate(zip(split_params(spec, Sg), split_params(spec, Sr))):
-            errs[f"S{i + 1}"] = maxrel(a, b)
+            errs[f"S{names[i]}"] = maxrel(a, b)
     log(f"PARITY {name}: " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()) + f" (tol {tol:g})")
     return errs
 

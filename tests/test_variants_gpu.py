@@ -67,3 +67,54 @@ def test_residual_retrieve_and_shape_error():
     with pytest.raises(am.AtlasMemError) as e:
         am.Memory(config_for(bad))
     assert e.value.status == am.E_INVALID
+
+
+G = synth.MLP2_GATED
+
+GATED = [
+    # (name, workload, variant, overrides, call boundaries or None)
+    ("mlp64_T256", 1, "stabilised", dict(kind=G, batch=1, heads=4, T=256), None),
+    ("window3_ragged_widths", 3, "stabilised",
+     dict(kind=G, batch=1, heads=3, T=144, d_key=40, poly_degree=1, d_value=24, d_hidden=72, chunk=48,
+          omega_window=3), [0, 48, 96, 144]),
+    ("poly2_window2", 3, "stabilised",
+     dict(kind=G, batch=2, heads=1, T=96, d_key=11, d_value=20, d_hidden=37, chunk=24, omega_window=2), None),
+    ("ns5_per_chunk_three_matrices", 4, "literal", dict(kind=G, batch=1, heads=3, T=512), None),
+    ("per_chunk_no_ns", 4, "literal", dict(kind=G, batch=1, heads=2, T=256, ns_steps=0), None),
+    ("streamed_uneven_calls", 1, "stabilised", dict(kind=G, batch=1, heads=2, T=192),
+     [0, 1, 2, 3, 70, 71, 150, 192]),
+]
+
+
+@pytest.mark.parametrize("case", GATED, ids=[c[0] for c in GATED])
+def test_gated_memory_parity(case):
+    name, idx, variant, ov, splits = case
+    log(f"CASE gated {name}")
+    inp = synth.make_inputs(idx, variant, **ov)
+    got = run_gpu(inp, splits=splits)
+    ref = oracle_run(inp)
+    errs = compare(f"gated_{name}", inp.spec, got, ref, BF16_TOL)
+    assert got[3] == am.OK
+    assert all(v <= BF16_TOL for v in errs.values()), errs
+
+
+def test_gated_retrieve():
+    import torch
+    import oracle
+    inp = synth.make_inputs(1, "stabilised", kind=G, batch=1, heads=2, T=64)
+    s = inp.spec
+    log("CASE gated_retrieve")
+    mem = am.Memory(config_for(s), to_dev(inp.W0))
+    assert mem.P == s.param_count
+    seg = segment(inp, 0, 64)
+    Y = torch.empty((s.n_mem, 64, s.d_value), dtype=torch.float32, device=DEV)
+    mem.retrieve(seg["Q"], 64, Y)
+    torch.cuda.synchronize()
+    mem.close()
+    cfg = oracle.config_from(s)
+    Qf = synth.bf16_bits_to_f32(inp.Q).astype(np.float64)
+    ref = np.stack([np.stack([oracle.memory_apply(oracle.unflatten(cfg, inp.W0[m]), Qf[m, t])
+                              for t in range(64)]) for m in range(s.n_mem)])
+    err = maxrel(Y.cpu().numpy(), ref)
+    log(f"PARITY gated_retrieve: Y={err:.3e}")
+    assert err <= BF16_TOL
