@@ -15,7 +15,8 @@ def config_from(spec) -> MemoryConfig:
     """MemoryConfig from any object carrying the workload fields (kind, d_key, ...)."""
     return MemoryConfig(kind=spec.kind, d_key=spec.d_key, d_value=spec.d_value, d_hidden=spec.d_hidden,
                         poly_degree=spec.poly_degree, chunk=spec.chunk, omega_window=spec.omega_window,
-                        gate_mode=spec.gate_mode, ns_steps=spec.ns_steps)
+                        gate_mode=spec.gate_mode, ns_steps=spec.ns_steps,
+                        per_token_retrieve=getattr(spec, "per_token_retrieve", False))
 
 
 def run_inputs(inputs, mems=None, T=None, processes: int = 1):

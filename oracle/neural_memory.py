@@ -15,6 +15,11 @@ What it computes, and where the pages define it
   residual adds the memory's input to its output).  ATLAS++ uses a gated MLP
   (same section); reading taken: M(x) = W2 (silu(W1 x) * (W3 x)), a SiLU branch
   gating a linear one elementwise, weights [W1, W3, W2].
+* Per-token retrieval (optional, per-token gates): y_t = M_{W_t}(phi(q_t)) with
+  W_t the state right after token t's update, the Atlas configuration's
+  retrieve (Atlas-Torch README, "Known deviations from the paper's MAC": the
+  post-update per-token state; Bug Fixes table, "no-omega ablation" row:
+  per-token retrieve on the per-token path).
 * Associative loss l(M; x_t) = ||M(k_t) - v_t||^2 (sum of squares, no 1/d):
   titans-pytorch-mlx README, Core Equations, Eq. 12.  For a linear memory its
   gradient is (prediction error) x (key), the delta rule: Atlas-Torch README,
@@ -81,6 +86,7 @@ class MemoryConfig:
     ns_steps: int = 0
     ns_coeffs: tuple = (3.4445, -4.7750, 2.0315)
     ns_eps: float = 1e-7
+    per_token_retrieve: bool = False   # y_t read after token t's update (per-token gates only)
 
 
 # ----------------------------------------------------------------------------- feature map
@@ -218,6 +224,9 @@ def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, g
     Xq = poly_features(Q, cfg.poly_degree)
     V = np.asarray(V, dtype=np.float64)
     res = cfg.kind == MLP2_SILU_RESIDUAL
+    ptr = cfg.per_token_retrieve
+    if ptr and cfg.gate_mode != PER_TOKEN:
+        raise ValueError("per-token retrieval needs per-token gates")
     if res and X.shape[1] != cfg.d_value:
         raise ValueError("a residual memory needs d_in == d_value")
     hist = list(history or [])[-(c - 1):] if c > 1 else []
@@ -237,8 +246,9 @@ def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, g
         if keep_boundaries:
             bounds.append(([w.copy() for w in W], [m.copy() for m in S]))
         w_bar = [w.copy() for w in W]                     # chunk-start weights
-        for t in range(s, e):                              # retrieval at the chunk-start weights
-            Y[t] = memory_apply(w_bar, Xq[t], res)
+        if not ptr:
+            for t in range(s, e):                          # retrieval at the chunk-start weights
+                Y[t] = memory_apply(w_bar, Xq[t], res)
         if cfg.gate_mode == PER_TOKEN:
             cache = {}
 
@@ -260,6 +270,8 @@ def run_memory(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, g
                 for m in range(len(W)):
                     S[m] = eta[t] * S[m] - theta[t] * G[m]
                     W[m] = (1.0 - alpha[t]) * W[m] + S[m]
+                if ptr:                                    # the state right after token t's update
+                    Y[t] = memory_apply(W, Xq[t], res)
         else:
             G = [np.zeros_like(w) for w in W]
             for t in range(s, e):

@@ -80,6 +80,7 @@ class Spec:
     norm_v: bool
     theta_scale: float = 1.0
     zero_init: bool = False
+    per_token_retrieve: bool = False   # retrieval after each token's update (per-token gates)
 
     @property
     def n_mem(self) -> int:

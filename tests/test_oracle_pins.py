@@ -82,7 +82,8 @@ def ns5_svd(G, steps=5, coeffs=NS, eps=1e-7):
 
 def bruteforce_run(cfg, params, momenta, K, Q, V, th, et, al, ga):
     """Per-step gradient of the windowed loss at the chunk-start weights by autograd, features by
-    phi_triu, retrieval by torch; the momentum / forgetting updates applied step by step."""
+    phi_triu, retrieval by torch (at the chunk start, or right after each step for per-token
+    retrieval); the momentum / forgetting updates applied step by step."""
     W = [p.copy() for p in params]
     S = [m.copy() for m in momenta]
     X = phi_triu(K, cfg.poly_degree)
@@ -104,6 +105,8 @@ def bruteforce_run(cfg, params, momenta, K, Q, V, th, et, al, ga):
                 for m in range(len(W)):
                     S[m] = et[t] * S[m] - th[t] * G[m]
                     W[m] = (1 - al[t]) * W[m] + S[m]
+                if cfg.per_token_retrieve:
+                    Y[t] = torch_memory([torch.tensor(w) for w in W], torch.tensor(Xq[t]), res).numpy()
         else:
             idx = list(range(s, e))
             G = autograd_window_grad(wb, [X[i] for i in idx], [V[i] for i in idx], [1.0] * len(idx), res)
@@ -346,6 +349,38 @@ def test_recurrence_against_autograd_bruteforce(case):
         assert maxrel(a, b) < 1e-11
     for a, b in zip(res.momenta, S):
         assert maxrel(a, b) < 1e-11
+
+
+PTR_CASES = [
+    # kind, T, d_k, d_v, d_h, poly, C, c
+    (LINEAR, 12, 4, 3, 0, 1, 4, 3),
+    (MLP2_SILU, 12, 3, 2, 5, 1, 4, 1),
+    (MLP2_SILU, 14, 3, 2, 5, 2, 4, 3),
+    (MLP2_SILU_RESIDUAL, 12, 3, 3, 5, 1, 5, 2),
+    (MLP2_GATED, 12, 3, 2, 5, 1, 4, 3),
+]
+
+
+@pytest.mark.parametrize("case", PTR_CASES)
+def test_per_token_retrieve_against_bruteforce(case):
+    """Per-token retrieval (each query answered right after its token's update) against the
+    autograd brute force; the chunk-start retrieval of the same run differs from it."""
+    import dataclasses
+    kind, T, d_k, d_v, d_h, poly, C, c = case
+    cfg, params, momenta, K, Q, V, th, et, al, ga = tiny_problem(13, kind, T, d_k, d_v, d_h, poly, C, c, PER_TOKEN)
+    cfg = dataclasses.replace(cfg, per_token_retrieve=True)
+    res = oracle.run_memory(cfg, params, momenta, K, Q, V, th, et, al, ga)
+    Y, W, S = bruteforce_run(cfg, params, momenta, K, Q, V, th, et, al, ga)
+    assert maxrel(res.Y, Y) < 1e-11
+    for a, b in zip(res.params, W):
+        assert maxrel(a, b) < 1e-11
+    plain = oracle.run_memory(dataclasses.replace(cfg, per_token_retrieve=False), params, momenta, K, Q, V, th,
+                              et, al, ga)
+    for a, b in zip(plain.params, res.params):
+        assert np.array_equal(a, b)  # retrieval does not touch the state
+    assert maxrel(plain.Y, res.Y) > 1e-6
+    with pytest.raises(ValueError):
+        oracle.run_memory(dataclasses.replace(cfg, gate_mode=PER_CHUNK), params, momenta, K, Q, V, th, et, al, ga)
 
 
 def coefficient_form(cfg, params, momenta, K, V, th, et, al, ga):
