@@ -114,6 +114,14 @@ typedef struct {
  * (the fused kernel covers the 64 -> 128 -> 64 MLP memory with per-chunk gates and
  * Newton-Schulz, bf16 inputs, split precision).  Results agree within rounding. */
 #define ATLASMEM_FLAG_NO_FUSED 1
+/* Per-token retrieval: Y[t] = M_{W_t}(phi(Q[t])) with W_t the state right after token t's
+ * update, instead of the chunk-start weights (Atlas-Torch README, "Known deviations from the
+ * paper's MAC": the Atlas configuration reads the post-update per-token state).  Per-token gates
+ * only (E_UNSUPPORTED otherwise); update calls must then cover whole chunks with nothing pending
+ * (E_UNSUPPORTED otherwise).  No per-token weights are formed: inside a chunk W_t is the
+ * chunk-start state plus a masked sum of the chunk's rank-one gradients, so the queries are
+ * answered through query-key score products. */
+#define ATLASMEM_FLAG_PER_TOKEN_RETRIEVE 2
 
 typedef struct atlasmem_handle_s* atlasmem_handle;
 

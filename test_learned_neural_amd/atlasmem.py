@@ -20,6 +20,7 @@ PER_TOKEN, PER_CHUNK = 0, 1
 F32, BF16 = 0, 1
 PREC_AUTO, PREC_BF16, PREC_BF16X3 = 0, 1, 2
 FLAG_NO_FUSED = 1
+FLAG_PER_TOKEN_RETRIEVE = 2
 ABI_VERSION = 1
 
 EXPORTS = (

@@ -41,7 +41,7 @@ atlasmem_status validate(const atlasmem_config* c) {
     return ATLASMEM_E_INVALID;
   if (c->precision < ATLASMEM_PREC_AUTO || c->precision > ATLASMEM_PREC_BF16X3) return ATLASMEM_E_INVALID;
   if (c->ns_steps > 0 && !(c->ns_eps >= 0.0f)) return ATLASMEM_E_INVALID;
-  if (c->flags & ~ATLASMEM_FLAG_NO_FUSED) return ATLASMEM_E_INVALID;
+  if (c->flags & ~(ATLASMEM_FLAG_NO_FUSED | ATLASMEM_FLAG_PER_TOKEN_RETRIEVE)) return ATLASMEM_E_INVALID;
   if ((int64_t)c->batch * c->heads > (1 << 20)) return ATLASMEM_E_SHAPE;
   if (c->d_key > 1024 || c->d_value > 1024 || c->d_hidden > 4096 || c->chunk > 1024 || c->omega_window > 64)
     return ATLASMEM_E_SHAPE;
@@ -52,6 +52,8 @@ atlasmem_status validate(const atlasmem_config* c) {
   // valid but not provided
   if (c->gate_mode == ATLASMEM_PER_CHUNK && c->omega_window > 1) return ATLASMEM_E_UNSUPPORTED;
   if (c->gate_mode == ATLASMEM_PER_TOKEN && c->ns_steps > 0) return ATLASMEM_E_UNSUPPORTED;
+  if ((c->flags & ATLASMEM_FLAG_PER_TOKEN_RETRIEVE) && c->gate_mode != ATLASMEM_PER_TOKEN)
+    return ATLASMEM_E_UNSUPPORTED;
   if (c->memory_kind == ATLASMEM_LINEAR) {
     if (din > 64 || c->d_value > 64 || c->omega_window > 8 || c->ns_steps > 0) return ATLASMEM_E_UNSUPPORTED;
   } else if (c->ns_steps > 0) {
@@ -95,6 +97,7 @@ Dims make_dims(const atlasmem_config* c) {
   d.out_bf16 = c->output_dtype == ATLASMEM_BF16;
   d.split = c->precision != ATLASMEM_PREC_BF16;
   d.no_fused = (c->flags & ATLASMEM_FLAG_NO_FUSED) != 0;
+  d.ptr = (c->flags & ATLASMEM_FLAG_PER_TOKEN_RETRIEVE) != 0;
   return d;
 }
 
@@ -179,6 +182,7 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
   const size_t opet = cv.take(sizeof(float) * M * d.C), opal = cv.take(sizeof(float) * M * d.C);
   const size_t state_end = cv.off;
   size_t oZ = 0, oD2 = 0, oD1 = 0, ocW = 0, ocS = 0, ooW = 0, ooS = 0, oscal = 0, oG = 0, oZr = 0;
+  size_t opZS = 0, opA1 = 0, opYB = 0, opbA = 0, opOm = 0;
   if (d.kind == ATLASMEM_MLP2_SILU) {
     oZ = cv.take(sizeof(float) * M * d.Rt * d.dz);
     oD2 = cv.take(sizeof(float) * M * d.Rk * d.dv);
@@ -201,6 +205,13 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
     while (rb > 64 && (int64_t)M * rb * d.dz * 4 > ((int64_t)256 << 20)) rb /= 2;
     h->rb = (int)rb;
     oZr = cv.take(sizeof(float) * M * rb * d.dz);
+    if (d.ptr) {
+      opZS = cv.take(sizeof(float) * M * d.C * d.dz);
+      opA1 = cv.take(sizeof(float) * M * d.C * d.Rk);
+      opYB = cv.take(sizeof(float) * M * d.C * d.dv);
+      opbA = cv.take(sizeof(float) * M * d.C * 2);
+      opOm = cv.take(sizeof(float) * M * d.C * d.Rk);
+    }
   }
   h->arena_bytes = cv.off;
   if (hipMalloc(&h->arena, h->arena_bytes) != hipSuccess) {
@@ -235,6 +246,11 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
     h->scal = oscal ? (float*)(base + oscal) : nullptr;
     h->G = oG ? (float*)(base + oG) : nullptr;
     h->Zr = (float*)(base + oZr);
+    h->pZS = d.ptr ? (float*)(base + opZS) : nullptr;
+    h->pA1 = d.ptr ? (float*)(base + opA1) : nullptr;
+    h->pYB = d.ptr ? (float*)(base + opYB) : nullptr;
+    h->pbA = d.ptr ? (float*)(base + opbA) : nullptr;
+    h->pOm = d.ptr ? (float*)(base + opOm) : nullptr;
   }
   h->cur = 0;
   h->hcur = 0;
@@ -332,6 +348,8 @@ atlasmem_status atlasmem_update_chunked(atlasmem_handle hh, const void* K, const
   if (!g.ok) return ATLASMEM_E_DEVICE;
   hipStream_t st = S(stream);
   const int64_t ldg = per_token ? T : ncomp;
+  // per-token retrieval answers a chunk's queries once its last token is known
+  if (d.ptr && (p0 != 0 || T % C != 0)) return ATLASMEM_E_UNSUPPORTED;
   if (p0 == 0 && T % C == 0)
     return run_update(h, d, K, Q, V, theta, eta, alpha, gamma, Span{T, T, ldg}, Y, st);
 

@@ -120,7 +120,7 @@ inline void launch_gemm(bool split, int M, int N, int K, int batch, const LA& la
 
 // ---------------------------------------------------------------------------- generic loaders
 
-enum Xform { XF_NONE = 0, XF_SILU = 1, XF_COEF = 2, XF_SCALE = 3, XF_GATED = 4 };
+enum Xform { XF_NONE = 0, XF_SILU = 1, XF_COEF = 2, XF_SCALE = 3, XF_GATED = 4, XF_MAT = 5 };
 
 // Element (outer, k) = xf(base[zoff(z) + outer * so + k * sk]); zoff(z) = (z / zdiv) * sz.
 // XF_COEF multiplies by coef[(z / zdiv) * cz + csel(z) + k]  (per-k coefficient; csel picks
@@ -128,6 +128,8 @@ enum Xform { XF_NONE = 0, XF_SILU = 1, XF_COEF = 2, XF_SCALE = 3, XF_GATED = 4 }
 // XF_SCALE multiplies by scale[z].
 // XF_GATED is silu(x) times the element `gofs` further on (the gated memory's activation
 // silu(Z1) * Z3, with Z3 stored beside Z1).
+// XF_MAT multiplies element (outer, k) by coef0[(z / zdiv) * cz + outer * cld + k] (a per-element
+// coefficient matrix).
 struct StridedLoader {
   const float* base;
   int64_t sz, so, sk;
@@ -139,11 +141,13 @@ struct StridedLoader {
   int64_t cz;
   const float* scale;
   int64_t gofs;
+  int64_t cld;
   __device__ __forceinline__ void load8(int z, int outer, int k0, float* v) const {
     const int zz = z / zdiv;
     const float* p = base + zz * sz + (int64_t)outer * so;
     const float* cf = nullptr;
     if (xf == XF_COEF) cf = ((zdiv == 2 && (z & 1)) ? coef1 : coef0) + zz * cz;
+    if (xf == XF_MAT) cf = coef0 + zz * cz + (int64_t)outer * cld;
     const float sc = (xf == XF_SCALE) ? scale[z] : 1.0f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -153,7 +157,7 @@ struct StridedLoader {
         x = p[(int64_t)k * sk];
         if (xf == XF_SILU) x = siluf_(x);
         else if (xf == XF_GATED) x = siluf_(x) * p[(int64_t)k * sk + gofs];
-        else if (xf == XF_COEF) x *= cf[k];
+        else if (xf == XF_COEF || xf == XF_MAT) x *= cf[k];
         else if (xf == XF_SCALE) x *= sc;
       }
       v[u] = x;

@@ -22,6 +22,7 @@ struct Dims {
   bool residual;                  // M(x) = x + W2 silu(W1 x)
   bool gated;                     // M(x) = W2 (silu(W1 x) * (W3 x)), W3 stored after W1
   int dz;                         // first-layer rows: d_hidden, or 2 d_hidden when gated
+  bool ptr;                       // per-token retrieval: y_t from the state right after token t
   float ns_a, ns_b, ns_c, ns_eps;
   int in_bf16, out_bf16;
   bool split;   // bf16 hi/lo split products
@@ -33,6 +34,13 @@ struct Dims {
 struct Span {
   int64_t T, ld, ldg;
 };
+
+// Per-token retrieval coefficients of one chunk (k_scan.hip): for query t of the chunk starting at
+// token s0, beta_t and a_t of W_t = beta_t W0 + a_t S0 - sum_i Om[t][r] g_i (key row r <-> token
+// i = s0 - (c - 1) + r).
+atlasmem_status launch_ptr_coeffs(const float* theta, const float* eta, const float* alpha, const float* gamma,
+                                  int64_t ld, const float* ghist, int M, int64_t s0, int C, int c, float* bA,
+                                  float* Om, hipStream_t st);
 
 // Input prologue (k_prologue.hip)
 atlasmem_status launch_short_conv(const void* X, bool in_bf16, int64_t M, int64_t T, int d, int heads,
@@ -77,6 +85,13 @@ struct atlasmem_handle_s {
   int rb;        // rows per retrieval block
   float* Zr;     // [M][rb][dh]
   int* flag;     // non-finite flag (device)
+  // per-token retrieval workspace (one chunk): [Zq | ...] [M][C][dz], scores [M][C][Rk], Y
+  // accumulator [M][C][dv], per-token (beta, a) [M][C][2] and window coefficients [M][C][Rk]
+  float* pZS;
+  float* pA1;
+  float* pYB;
+  float* pbA;
+  float* pOm;
   // tokens of the current, unfinished chunk (streaming calls): input rows of K and V (input
   // dtype), gamma and per-token gates, [M][C] each; `pending` of them are filled
   void* pK;
@@ -137,6 +152,13 @@ bool fused_supported(const Dims& d);
 atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
                              const float* theta, const float* eta, const float* alpha, const Span& sp, void* Y,
                              hipStream_t st);
+
+// Per-token retrieval coefficients of one chunk (k_scan.hip): for query t of the chunk starting at
+// token s0, beta_t and a_t of W_t = beta_t W0 + a_t S0 - sum_i Om[t][r] g_i (key row r <-> token
+// i = s0 - (c - 1) + r).
+atlasmem_status launch_ptr_coeffs(const float* theta, const float* eta, const float* alpha, const float* gamma,
+                                  int64_t ld, const float* ghist, int M, int64_t s0, int C, int c, float* bA,
+                                  float* Om, hipStream_t st);
 
 // Input prologue (k_prologue.hip)
 atlasmem_status launch_short_conv(const void* X, bool in_bf16, int64_t M, int64_t T, int d, int heads,

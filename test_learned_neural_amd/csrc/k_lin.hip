@@ -40,6 +40,7 @@ struct LinArgs {
   const float* hg;
   void* Y;
   int out_bf16;
+  int ptr;           // per-token retrieval: y_t from the state right after token t's update
   int* flag;
 };
 
@@ -148,7 +149,7 @@ __global__ void __launch_bounds__(64) lin_kernel(LinArgs a) {
         }
       }
       const int slot = (int)(t & (kRing - 1));
-      if (own && a.Y) {
+      if (own && a.Y && !a.ptr) {
         const float y = dot_row<D>(Wb, Qb + j * D);
         const int64_t yo = ((int64_t)m * a.ld + t) * a.dv + r;
         if (a.out_bf16) ((uint16_t*)a.Y)[yo] = (uint16_t)bf16_bits(y);
@@ -175,6 +176,12 @@ __global__ void __launch_bounds__(64) lin_kernel(LinArgs a) {
             if (u < a.c) g = fmaf(coef[u], Xr[sl[u] * D + l], g);
           S[l] = et * S[l] - th * g;
           W[l] = om * W[l] + S[l];
+        }
+        if (own && a.Y && a.ptr) {  // the state right after this token's update
+          const float y = dot_row<D>(W, Qb + j * D);
+          const int64_t yo = ((int64_t)m * a.ld + t) * a.dv + r;
+          if (a.out_bf16) ((uint16_t*)a.Y)[yo] = (uint16_t)bf16_bits(y);
+          else ((float*)a.Y)[yo] = y;
         }
       } else {
 #pragma unroll
@@ -256,6 +263,7 @@ atlasmem_status launch_linear_update(Handle* h, const Dims& d, const void* K, co
   a.hg = h->hg[h->hcur];
   a.Y = Y;
   a.out_bf16 = d.out_bf16;
+  a.ptr = d.ptr;
   a.flag = h->flag;
   const int D = d.din > d.dv ? d.din : d.dv;
   atlasmem_status s;

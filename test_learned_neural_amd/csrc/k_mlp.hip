@@ -142,6 +142,53 @@ struct EpiY {
   }
 };
 
+// Per-token retrieval epilogues (rows = the chunk's queries t; bA = (beta_t, a_t)).
+// Zq = beta_t Z0 + a_t ZS - acc, in place in ZS: Z0 = the chunk-start first-layer product of the
+// queries (rows zr0.. of Z), ZS = their product with the chunk-start momentum.
+struct EpiZq {
+  float* ZS;
+  const float* Z;
+  const float* bA;
+  int64_t zs_z, z_z, zr0;
+  int dz, C;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    float* o = ZS + (int64_t)z * zs_z + (int64_t)row * dz + col;
+    const float* b = bA + ((int64_t)z * C + row) * 2;
+    *o = b[0] * Z[(int64_t)z * z_z + (zr0 + row) * dz + col] + b[1] * *o - v;
+  }
+};
+// out = which-th coefficient of the row times acc (acc = 0) or added to out (acc = 1)
+struct EpiRowMix {
+  float* out;
+  const float* bA;
+  int64_t oz;
+  int ld, C, which, add;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    float* o = out + (int64_t)z * oz + (int64_t)row * ld + col;
+    const float x = bA[((int64_t)z * C + row) * 2 + which] * v;
+    *o = add ? *o + x : x;
+  }
+};
+// Y of the chunk's queries: the accumulated beta/a terms minus acc (plus the query's features for
+// the residual memory)
+struct EpiYptr {
+  const float* YB;
+  int64_t yb_z;
+  int dv;
+  int64_t ld, s;  // token stride of Y per memory, first token of the chunk
+  void* Y;
+  int out_bf16;
+  int residual;
+  FeatRows fr;    // the queries, for the residual input
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    float y = YB[(int64_t)z * yb_z + (int64_t)row * dv + col] - v;
+    if (residual) y += fr.feat(z, row, col);
+    const int64_t yo = ((int64_t)z * ld + s + row) * dv + col;
+    if (out_bf16) ((uint16_t*)Y)[yo] = (uint16_t)bf16_bits(y);
+    else ((float*)Y)[yo] = y;
+  }
+};
+
 // D1 = Pm * silu'(Z).  Gated memory (rows of Z and D1 hold [Z1 | Z3] and [D1 | D3]):
 // D1 = Pm * Z3 * silu'(Z1), D3 = Pm * silu(Z1).
 struct EpiP {
@@ -231,6 +278,7 @@ static StridedLoader strided(const float* base, int64_t sz, int64_t so, int64_t 
   l.cz = 0;
   l.scale = nullptr;
   l.gofs = 0;
+  l.cld = 0;
   return l;
 }
 
@@ -270,6 +318,78 @@ static FeatRows feat_rows(const Handle* h, const void* K, const void* Q, int64_t
   fr.poly = d.poly;
   fr.zdiv = zdiv;
   return fr;
+}
+
+// ---------------------------------------------------------------------------- per-token retrieval
+
+// Queries of the chunk starting at token s answered from W_t, the state right after token t's
+// update (Atlas-Torch README, "Known deviations from the paper's MAC": the post-update per-token
+// state), without forming any W_t.  With W_t = beta_t W0 + a_t S0 - sum_i Om[t][i] g_i (the
+// coefficients of launch_ptr_coeffs) and the MLP gradients g_i = (D1_i x_i^T, D2_i h_i^T) that the
+// update has just formed at the chunk-start weights:
+//   Zq_t = beta_t (W0_1 q_t) + a_t (S0_1 q_t) - sum_i Om[t][i] (x_i . q_t) D1_i
+//   y_t  = beta_t (W0_2 Hq_t) + a_t (S0_2 Hq_t) - sum_i Om[t][i] (h_i . Hq_t) D2_i,  Hq = H(Zq)
+// i.e. masked query-key score products, as in attention.  The gated memory's first layer is the
+// [W1; W3] block throughout.
+static atlasmem_status ptr_retrieve(Handle* h, const Dims& d, const void* K, const void* Q, const float* theta,
+                                    const float* eta, const float* alpha, const float* gamma, int64_t ld, int64_t s,
+                                    const float* Win, const float* Sin, void* Y, hipStream_t st) {
+  const int M = d.M, C = d.C, Rk = d.Rk, dh = d.dh, dv = d.dv, din = d.din, dz = d.dz;
+  const bool split = d.split, feat_exact = d.poly == 1 && d.in_bf16;
+  const int64_t zsz = (int64_t)d.Rt * dz, qz = (int64_t)C * dz, az = (int64_t)C * Rk, yz = (int64_t)C * dv;
+  atlasmem_status stt = launch_ptr_coeffs(theta, eta, alpha, gamma, ld, h->hg[h->hcur], M, s, C, d.c, h->pbA,
+                                          h->pOm, st);
+  if (stt != ATLASMEM_OK) return stt;
+  const FeatRows qrows = feat_rows(h, nullptr, Q, ld, s, 0, C, 1);
+  // ZS = Q S0_1^T
+  {
+    FeatA la{qrows};
+    StridedLoader lb = strided(Sin, d.P, din, 1, 1, dz, din);
+    EpiStore ep{h->pZS, qz, dz, 1};
+    gemm_any(split, feat_exact, false, C, dz, din, M, la, lb, ep, st);
+  }
+  // scores A1[t][r] = q_t . x_r over the key rows (window history included)
+  {
+    FeatA la{qrows};
+    FeatA lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)};
+    EpiStore ep{h->pA1, az, Rk, 1};
+    gemm_any(split, feat_exact, feat_exact, C, Rk, din, M, la, lb, ep, st);
+  }
+  // Zq = beta Z0 + a ZS - (Om * A1) D1
+  {
+    StridedLoader la = strided(h->pA1, az, Rk, 1, 1, C, Rk, XF_MAT);
+    la.coef0 = h->pOm;
+    la.cz = az;
+    la.cld = Rk;
+    StridedLoader lb = strided(h->D1, (int64_t)Rk * dz, 1, dz, 1, dz, Rk);  // B(k=r, j) = D1[r][j]
+    EpiZq ep{h->pZS, h->Z, h->pbA, qz, zsz, (int64_t)Rk, dz, C};
+    gemm_any(split, false, false, C, dz, Rk, M, la, lb, ep, st);
+  }
+  // scores A2[t][r] = Hq_t . h_r
+  {
+    StridedLoader la = hidden(d, h->pZS, qz, dz, 1, 1, C, dh);
+    StridedLoader lb = hidden(d, h->Z, zsz, dz, 1, 1, Rk, dh);  // B(k=h, j=r) = H[r][h]
+    EpiStore ep{h->pA1, az, Rk, 1};
+    gemm_any(split, false, false, C, Rk, dh, M, la, lb, ep, st);
+  }
+  // YB = beta Hq W0_2^T + a Hq S0_2^T
+  for (int which = 0; which < 2; ++which) {
+    StridedLoader la = hidden(d, h->pZS, qz, dz, 1, 1, C, dh);
+    StridedLoader lb = strided((which ? Sin : Win) + d.P1, d.P, dh, 1, 1, dv, dh);  // B(k=h, j=v) = W2[v][h]
+    EpiRowMix ep{h->pYB, h->pbA, yz, dv, C, which, which};
+    gemm_any(split, false, false, C, dv, dh, M, la, lb, ep, st);
+  }
+  // Y = YB - (Om * A2) D2 (+ the query's features for the residual memory)
+  {
+    StridedLoader la = strided(h->pA1, az, Rk, 1, 1, C, Rk, XF_MAT);
+    la.coef0 = h->pOm;
+    la.cz = az;
+    la.cld = Rk;
+    StridedLoader lb = strided(h->D2, (int64_t)Rk * dv, 1, dv, 1, dv, Rk);  // B(k=r, j=v) = D2[r][v]
+    EpiYptr ep{h->pYB, yz, dv, ld, s, Y, d.out_bf16, d.residual, qrows};
+    gemm_any(split, false, false, C, dv, Rk, M, la, lb, ep, st);
+  }
+  return ATLASMEM_OK;
 }
 
 // ---------------------------------------------------------------------------- one call
@@ -318,13 +438,15 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
         EpiStore ep{h->Z, zsz, dz, 1};
         gemm_any(split, feat_exact, false, nrows, dz, din, M, la, lb, ep, st);
       }
-      // Yh = H W2^T -> D2 (key rows), Y (query rows)
+      // Yh = H W2^T -> D2 (key rows), Y (query rows; with per-token retrieval they are answered
+      // below from the per-token states instead)
+      const int yrows = d.ptr ? Rk : nrows;
       {
-        StridedLoader la = hidden(d, h->Z, zsz, dz, 1, 1, nrows, dh);
+        StridedLoader la = hidden(d, h->Z, zsz, dz, 1, 1, yrows, dh);
         StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);  // B(k=h, j=v) = W2[v][h]
         EpiY ep{h->D2, (int64_t)Rk * dv, V, d.in_bf16, h->hv[h->hcur], ld, s, Rk, c, dv, Y, d.out_bf16,
                 d.residual, feat_rows(h, K, Q, ld, s, Rk, nrows, 1)};
-        gemm_any(split, false, false, nrows, dv, dh, M, la, lb, ep, st);
+        gemm_any(split, false, false, yrows, dv, dh, M, la, lb, ep, st);
       }
       // Pm = D2 W2 -> D1 = Pm * silu'(Z)
       {
@@ -399,6 +521,10 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
         NsUpdate u2{Win, Sin, Wout, Sout, d.P, d.P1, 1, theta, eta, alpha, sp.ldg, k, h->flag};
         stt = launch_ns(h->G + d.P1, d.P, M, dv, dh, d.ns_steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, split, nullptr,
                         &u2, st);
+        if (stt != ATLASMEM_OK) return stt;
+      }
+      if (d.ptr && Y) {
+        stt = ptr_retrieve(h, d, K, Q, theta, eta, alpha, gamma, ld, s, Win, Sin, Y, st);
         if (stt != ATLASMEM_OK) return stt;
       }
       AM_LAUNCH_CHECK();

@@ -119,6 +119,83 @@ atlasmem_status launch_omega(const float* cW, const float* cS, int64_t ld_c, con
   return ATLASMEM_OK;
 }
 
+// Per-token retrieval reads W_t, the state right after token t's update.  Inside a chunk that
+// starts from (W0, S0) with per-token gates (titans-pytorch-mlx README, Eq. 13-14), every
+// gradient taken at the chunk-start weights,
+//   S_t = P_t S0 - sum_{l<=t} E_{t,l} theta_l G_l,  E_{t,l} = prod_{n=l+1..t} eta_n, P_t = prod_{n<=t} eta_n
+//   W_t = beta_t W0 + a_t S0 - sum_{l<=t} w_{t,l} theta_l G_l,  beta_t = prod_{l<=t} (1 - alpha_l),
+// with a_t = (1 - alpha_t) a_{t-1} + P_t and w_{t,l} = (1 - alpha_t) w_{t-1,l} + E_{t,l}, w_{l,l} = 1.
+// With the Omega window G_l = sum_{i=l-c+1..l} gamma_i g_i (ATLAS summary, section 3.2), so g_i
+// enters W_t with Om_{t,i} = gamma_i sum_{l in [max(i, s), min(i + c - 1, t)]} w_{t,l} theta_l.
+// One block per memory walks the chunk's tokens in order; w and E live in LDS, one column per l.
+__global__ void ptr_coeff_kernel(const float* __restrict__ theta, const float* __restrict__ eta,
+                                 const float* __restrict__ alpha, const float* __restrict__ gamma, int64_t ld,
+                                 const float* __restrict__ ghist, int64_t s0, int C, int c, float* __restrict__ bA,
+                                 float* __restrict__ Om) {
+  extern __shared__ float pc[];  // w[C], E[C], tw[C]
+  float* w = pc;
+  float* E = pc + C;
+  float* tw = pc + 2 * C;
+  const int m = blockIdx.x;
+  const int Rk = C + c - 1;
+  const float* th = theta + (int64_t)m * ld + s0;
+  const float* et = eta + (int64_t)m * ld + s0;
+  const float* al = alpha + (int64_t)m * ld + s0;
+  float beta = 1.0f, a = 0.0f, P = 1.0f;
+  for (int t = 0; t < C; ++t) {
+    const float om = 1.0f - al[t], e = et[t];
+    for (int l = threadIdx.x; l < C; l += blockDim.x) {
+      float wl, El;
+      if (l < t) {
+        El = e * E[l];
+        wl = om * w[l] + El;
+      } else {
+        El = 1.0f;
+        wl = 1.0f;
+      }
+      if (l <= t) {
+        E[l] = El;
+        w[l] = wl;
+      }
+      tw[l] = (l <= t) ? th[l] * wl : 0.0f;
+    }
+    P *= e;
+    a = om * a + P;
+    beta *= om;
+    __syncthreads();
+    float* orow = Om + ((int64_t)m * C + t) * Rk;
+    for (int r = threadIdx.x; r < Rk; r += blockDim.x) {
+      const int i = r - (c - 1);  // chunk-relative token of key row r (negative: window history)
+      float v = 0.0f;
+      if (i <= t) {
+        const int lo = i > 0 ? i : 0;
+        const int hi = (i + c - 1) < t ? (i + c - 1) : t;
+        for (int l = lo; l <= hi; ++l) v += tw[l];
+        if (c > 1) {  // gamma of token s0 + i of the call, or of the history before the call
+          const int64_t tau = s0 + i;
+          v *= (tau >= 0) ? gamma[(int64_t)m * ld + tau] : ghist[(int64_t)m * (c - 1) + (c - 1) + tau];
+        }
+      }
+      orow[r] = v;
+    }
+    if (threadIdx.x == 0) {
+      bA[((int64_t)m * C + t) * 2] = beta;
+      bA[((int64_t)m * C + t) * 2 + 1] = a;
+    }
+    __syncthreads();
+  }
+}
+
+atlasmem_status launch_ptr_coeffs(const float* theta, const float* eta, const float* alpha, const float* gamma,
+                                  int64_t ld, const float* ghist, int M, int64_t s0, int C, int c, float* bA,
+                                  float* Om, hipStream_t st) {
+  if (M == 0) return ATLASMEM_OK;
+  hipLaunchKernelGGL(ptr_coeff_kernel, dim3(M), dim3(256), (size_t)3 * C * sizeof(float), st, theta, eta, alpha,
+                     gamma, ld, ghist, s0, C, c, bA, Om);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
 // Window history: after a call of T tokens, keep the last c - 1 (key, value, gamma) rows of
 // (old history ++ this call), oldest first.  Rows that do not exist (fewer than c - 1 tokens
 // seen since the sequence start) keep gamma = 0 and zero vectors.

@@ -31,6 +31,8 @@ def maxrel(x, r) -> float:
 
 
 def config_for(spec, precision=am.PREC_AUTO, output_dtype=am.F32, flags=0):
+    if getattr(spec, "per_token_retrieve", False):
+        flags |= am.FLAG_PER_TOKEN_RETRIEVE
     return am.make_config(kind=spec.kind, batch=spec.batch, heads=spec.heads, d_key=spec.d_key,
                           d_value=spec.d_value, d_hidden=spec.d_hidden, poly_degree=spec.poly_degree,
                           chunk=spec.chunk, omega_window=spec.omega_window, gate_mode=spec.gate_mode,

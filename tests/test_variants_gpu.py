@@ -8,7 +8,7 @@ plain memory: max |x - r| / max |r| per tensor within 2e-2 for bf16 inputs.
 import numpy as np
 import pytest
 
-from helpers import BF16_TOL, DEV, compare, config_for, log, maxrel, oracle_run, run_gpu, segment, to_dev
+from helpers import BF16_TOL, DEV, F32_TOL, compare, config_for, log, maxrel, oracle_run, run_gpu, segment, to_dev
 from test_learned_neural_amd import atlasmem as am
 from test_learned_neural_amd import synth
 
@@ -118,3 +118,56 @@ def test_gated_retrieve():
     err = maxrel(Y.cpu().numpy(), ref)
     log(f"PARITY gated_retrieve: Y={err:.3e}")
     assert err <= BF16_TOL
+
+
+PTR = [
+    # (name, workload, variant, overrides, call boundaries or None)
+    ("linear_C4_w3", 0, "literal", dict(batch=2, heads=2, T=96, chunk=4, omega_window=3, d_key=20, d_value=12,
+                                        per_token_retrieve=True), None),
+    ("mlp64_T256", 1, "stabilised", dict(batch=1, heads=4, T=256, per_token_retrieve=True), [0, 64, 192, 256]),
+    ("window3_ragged_widths", 3, "stabilised",
+     dict(batch=1, heads=3, T=144, d_key=40, poly_degree=1, d_value=24, d_hidden=72, chunk=48, omega_window=3,
+          per_token_retrieve=True), [0, 48, 144]),
+    ("poly2_window4", 3, "stabilised", dict(batch=1, heads=2, T=192, per_token_retrieve=True), None),
+    ("residual_window2", 3, "stabilised",
+     dict(kind=R, batch=1, heads=2, T=96, d_key=24, poly_degree=1, d_value=24, d_hidden=40, chunk=32,
+          omega_window=2, per_token_retrieve=True), None),
+    ("gated_window3", 3, "stabilised",
+     dict(kind=G, batch=1, heads=2, T=96, d_key=16, poly_degree=1, d_value=20, d_hidden=36, chunk=48,
+          omega_window=3, per_token_retrieve=True), None),
+]
+
+
+@pytest.mark.parametrize("case", PTR, ids=[c[0] for c in PTR])
+def test_per_token_retrieve_parity(case):
+    """Queries answered from the state right after their token's update, against the oracle."""
+    name, idx, variant, ov, splits = case
+    log(f"CASE per_token_retrieve {name}")
+    inp = synth.make_inputs(idx, variant, **ov)
+    tol = F32_TOL if inp.spec.kind == synth.LINEAR else BF16_TOL
+    got = run_gpu(inp, splits=splits)
+    ref = oracle_run(inp)
+    errs = compare(f"ptr_{name}", inp.spec, got, ref, tol)
+    assert got[3] == am.OK
+    assert all(v <= tol for v in errs.values()), errs
+    # the chunk-start answers of the same run are different (the test would not see a mix-up)
+    import dataclasses
+    base = dataclasses.replace(inp, spec=dataclasses.replace(inp.spec, per_token_retrieve=False))
+    assert maxrel(oracle_run(base)[0], ref[0]) > 10 * tol
+
+
+def test_per_token_retrieve_unsupported():
+    s = synth.spec(4, "literal", batch=1, heads=1, T=256, per_token_retrieve=True)
+    with pytest.raises(am.AtlasMemError) as e:
+        am.Memory(config_for(s))
+    assert e.value.status == am.E_UNSUPPORTED
+    import torch
+    inp = synth.make_inputs(1, "stabilised", batch=1, heads=1, T=100, per_token_retrieve=True)
+    mem = am.Memory(config_for(inp.spec), to_dev(inp.W0))
+    seg = segment(inp, 0, 100)
+    Y = torch.empty((1, 100, inp.spec.d_value), dtype=torch.float32, device=DEV)
+    with pytest.raises(am.AtlasMemError) as e:
+        mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], None, 100, Y)
+    assert e.value.status == am.E_UNSUPPORTED
+    assert mem.pending == 0
+    mem.close()
