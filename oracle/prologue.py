@@ -29,6 +29,10 @@ What it computes, and where the pages define it
   the chunk's gates are pooled (Atlas-Torch README, Bug Fixes table, "no-omega ablation"
   row).  Reading taken: the gate of the chunk's mean-pooled input, i.e. the sigmoid of the
   mean of its tokens' logits; a final short chunk pools its own tokens.
+* Feature map stage: monomials of degree 0..p (p <= 3) with learnable per-degree coefficients
+  (default 1/k!, the exponential kernel's Taylor coefficients, which Dot uses with the Omega
+  rule) and the optional projection back (Atlas-Torch README, Atlas Extensions table,
+  "Polynomial Features"; ATLAS summary, sections 3.1 and 4.3).
 """
 
 from __future__ import annotations
@@ -136,3 +140,34 @@ def gates_bruteforce(U, Wg, bg, scale, chunk: int = 1):
                 z = sum(part) / len(part)
                 out[g][h][c] = float(scale[g]) / (1.0 + math.exp(-z))
     return out
+
+
+# ----------------------------------------------------------------------------- feature map stage
+
+def feature_map(x, degree: int, coeffs=None, P=None) -> np.ndarray:
+    """phi_c(x) of every row: all monomials of degree 0..p in combinations_with_replacement order
+    (degree-major), the monomials of degree k multiplied by coeffs[k] (default 1/k!, the Taylor
+    coefficients of the exponential kernel), optionally projected back, phi_c(x) P^T.
+
+    Atlas-Torch README, Atlas Extensions table, "Polynomial Features" (exact monomial expansion,
+    learnable coefficients initialised to 1/d!, optional project_back); ATLAS summary, sections 3.1
+    (polynomial features) and 4.1-4.3 (Dot: the exponential feature construction with the Omega
+    rule)."""
+    from itertools import combinations_with_replacement
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    c = [1.0 / math.factorial(k) for k in range(degree + 1)] if coeffs is None else list(coeffs)
+    assert len(c) == degree + 1
+    cols = []
+    for k in range(degree + 1):
+        for combo in combinations_with_replacement(range(d), k):
+            col = np.full(n, float(c[k]))
+            for i in combo:
+                col = col * x[:, i]
+            cols.append(col)
+    F = np.stack(cols, axis=1)
+    return F if P is None else F @ np.asarray(P, dtype=np.float64).T
+
+
+def feature_count(d: int, degree: int) -> int:
+    return math.comb(d + degree, degree)

@@ -163,3 +163,55 @@ def test_gates_all_layout():
     assert out.shape == (3, B, H, T)
     for b in range(B):
         np.testing.assert_array_equal(out[:, b], pro.gates(U[b], Wg, bg, scale))
+
+
+# ----------------------------------------------------------------------------- feature map stage
+
+def test_feature_map_golden_degree3():
+    rows = [ln for ln in open(os.path.join(GOLDEN, "feature_map_d2_deg3.txt")) if not ln.startswith("#")]
+    ref = np.array([float(v) for v in rows[0].split()])
+    got = pro.feature_map(np.array([[1.0, 2.0]]), 3)[0]
+    np.testing.assert_allclose(got, ref, rtol=1e-15)
+
+
+@pytest.mark.parametrize("d,p", [(3, 1), (5, 2), (4, 3), (32, 3)])
+def test_feature_count_is_binomial(d, p):
+    import math
+    assert pro.feature_map(np.ones((1, d)), p).shape[1] == math.comb(d + p, p) == pro.feature_count(d, p)
+
+
+def test_feature_map_degree2_equals_update_path_map():
+    import oracle
+    r = np.random.default_rng(9)
+    x = r.standard_normal((5, 6))
+    np.testing.assert_array_equal(pro.feature_map(x, 2), oracle.poly_features(x, 2))
+
+
+@pytest.mark.parametrize("p", [1, 2, 3])
+def test_feature_map_inner_product_closed_form(p):
+    """<phi(x), phi(y)> = sum_k c_k^2 h_k(z), z_i = x_i y_i, with the complete homogeneous symmetric
+    polynomials from the power sums P_k = sum z_i^k (Newton's identities): h_0 = 1, h_1 = P_1,
+    h_2 = (P_1^2 + P_2) / 2, h_3 = (P_1^3 + 3 P_1 P_2 + 2 P_3) / 6."""
+    r = np.random.default_rng(10 + p)
+    x, y = r.standard_normal(7), r.standard_normal(7)
+    c = r.uniform(0.2, 1.5, p + 1)
+    z = x * y
+    P1, P2, P3 = z.sum(), (z ** 2).sum(), (z ** 3).sum()
+    h = [1.0, P1, (P1 ** 2 + P2) / 2, (P1 ** 3 + 3 * P1 * P2 + 2 * P3) / 6]
+    ref = sum(c[k] ** 2 * h[k] for k in range(p + 1))
+    fx, fy = pro.feature_map(x[None], p, c)[0], pro.feature_map(y[None], p, c)[0]
+    np.testing.assert_allclose(fx @ fy, ref, rtol=1e-12)
+
+
+def test_feature_map_basis_vector_and_projection():
+    d, p = 4, 3
+    c = [0.7, 1.1, 0.3, 0.2]
+    f = pro.feature_map(np.eye(d)[2:3], p, c)[0]
+    # e_2: the constant, x_2, x_2^2 and x_2^3 are the only non-zero monomials
+    assert sorted(np.round(f[f != 0], 12).tolist()) == sorted([0.7, 1.1, 0.3, 0.2])
+    r = np.random.default_rng(11)
+    X = r.standard_normal((6, d))
+    Pm = r.standard_normal((5, pro.feature_count(d, p)))
+    F = pro.feature_map(X, p, c)
+    np.testing.assert_allclose(pro.feature_map(X, p, c, Pm), np.einsum("nf,of->no", F, Pm), rtol=1e-13)
+    assert np.array_equal(pro.feature_map(X, p, c, np.eye(F.shape[1])), F)
