@@ -239,6 +239,22 @@ atlasmem_status atlasmem_newton_schulz(const float* G, int64_t n_mat, int32_t ro
                                        int32_t steps, float a, float b, float c, float eps,
                                        int32_t precision, float* out, void* stream);
 
+/* Feature map of n rows of width d: every monomial of degree 0..degree (degree 1..3), degree-major
+ * and in combinations_with_replacement order inside a degree, the degree-k monomials multiplied
+ * by coeffs[k] -- and, with P, projected back (Atlas-Torch README, Atlas Extensions table,
+ * "Polynomial Features": exact monomial expansion, learnable coefficients initialised to 1/d!,
+ * optional project_back; ATLAS summary, section 4.3: Dot pairs these exponential-kernel features
+ * with the Omega rule, which the update then applies to the mapped rows).
+ *   X:      [n, d] in_dtype (d <= 1024, C(d + degree, degree) <= 2^20 features)
+ *   coeffs: HOST pointer to degree + 1 floats, or NULL for 1/k!
+ *   P:      fp32 [d_out, C(d + degree, degree)] (device) or NULL; d_out <= 65536
+ *   out:    fp32 [n, d_out] = phi_c(X) P^T, or [n, C(d + degree, degree)] = phi_c(X) without P
+ * With P the product runs on the matrix cores in split bf16 (hi/lo) with fp32 accumulation.
+ * Errors: E_INVALID for bad sizes, dtype or null pointers; E_SHAPE beyond the limits. */
+atlasmem_status atlasmem_feature_map(const void* X, int32_t in_dtype, int64_t n, int32_t d, int32_t degree,
+                                     const float* coeffs, const float* P, int32_t d_out, float* out,
+                                     void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * Input prologue: the steps just before the update, producing its K, Q, V and gates.
  * ------------------------------------------------------------------------------------- */

@@ -29,6 +29,7 @@ EXPORTS = (
     "atlasmem_set_state",
     "atlasmem_reset_history", "atlasmem_destroy", "atlasmem_gate_scan", "atlasmem_omega_coeffs",
     "atlasmem_poly_features", "atlasmem_newton_schulz", "atlasmem_short_conv", "atlasmem_gates",
+    "atlasmem_feature_map",
 )
 
 
@@ -85,6 +86,7 @@ def load():
         "atlasmem_short_conv": ([_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp],
                                 ctypes.c_int),
         "atlasmem_gates": ([_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
+        "atlasmem_feature_map": ([_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -222,3 +224,13 @@ def short_conv(X, in_dtype: int, M: int, T: int, d: int, heads: int, taps, bias,
 def gates(U, B: int, T: int, d_model: int, heads: int, n_gates: int, Wg, bg, scale, chunk: int, out, stream=None):
     _check(load().atlasmem_gates(_ptr(U), B, T, d_model, heads, n_gates, _ptr(Wg), _ptr(bg), _ptr(scale), chunk,
                                  _ptr(out), _stream(stream)), "atlasmem_gates")
+
+
+def feature_map(X, in_dtype: int, n: int, d: int, degree: int, out, coeffs=None, P=None, d_out: int = 0,
+                stream=None):
+    """coeffs: a host sequence of degree + 1 floats (None: 1/k!)."""
+    arr = None if coeffs is None else (ctypes.c_float * (degree + 1))(*[float(v) for v in coeffs])
+    c = None if arr is None else ctypes.cast(arr, ctypes.c_void_p)
+    _check(load().atlasmem_feature_map(_ptr(X), in_dtype, n, d, degree, c, _ptr(P), d_out, _ptr(out),
+                                       _stream(stream)), "atlasmem_feature_map")
+

@@ -572,4 +572,18 @@ atlasmem_status atlasmem_gates(const void* U, int64_t B, int64_t T, int32_t d_mo
   return launch_gates(U, B, T, d_model, heads, n_gates, Wg, bg, scale, chunk, out, S(stream));
 }
 
+atlasmem_status atlasmem_feature_map(const void* X, int32_t in_dtype, int64_t n, int32_t d, int32_t degree,
+                                     const float* coeffs, const float* P, int32_t d_out, float* out, void* stream) {
+  if (n < 0 || d < 1 || degree < 1 || degree > 3 || (in_dtype != ATLASMEM_F32 && in_dtype != ATLASMEM_BF16))
+    return ATLASMEM_E_INVALID;
+  if (P && d_out < 1) return ATLASMEM_E_INVALID;
+  if (d > 1024 || feature_count_host(d, degree) > (1 << 20) || (P && d_out > (1 << 16))) return ATLASMEM_E_SHAPE;
+  if (n == 0) return ATLASMEM_OK;
+  if (!X || !out) return ATLASMEM_E_INVALID;
+  float c4[4] = {1.0f, 1.0f, 0.5f, 1.0f / 6.0f};  // 1/k!
+  if (coeffs)
+    for (int k = 0; k <= degree; ++k) c4[k] = coeffs[k];
+  return launch_feature_map(X, in_dtype == ATLASMEM_BF16, n, d, degree, c4, P, P ? d_out : 0, out, S(stream));
+}
+
 }  // extern "C"

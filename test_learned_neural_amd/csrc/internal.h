@@ -42,6 +42,11 @@ atlasmem_status launch_ptr_coeffs(const float* theta, const float* eta, const fl
                                   int64_t ld, const float* ghist, int M, int64_t s0, int C, int c, float* bA,
                                   float* Om, hipStream_t st);
 
+// Feature map stage (k_features.hip): phi_c of degree <= 3, optionally projected by P.
+int64_t feature_count_host(int d, int degree);
+atlasmem_status launch_feature_map(const void* X, bool in_bf16, int64_t n, int d, int degree, const float* c4,
+                                   const float* P, int d_out, float* out, hipStream_t st);
+
 // Input prologue (k_prologue.hip)
 atlasmem_status launch_short_conv(const void* X, bool in_bf16, int64_t M, int64_t T, int d, int heads,
                                   const float* taps, const float* bias, const void* hist, bool l2norm, void* out,
@@ -159,6 +164,11 @@ atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void
 atlasmem_status launch_ptr_coeffs(const float* theta, const float* eta, const float* alpha, const float* gamma,
                                   int64_t ld, const float* ghist, int M, int64_t s0, int C, int c, float* bA,
                                   float* Om, hipStream_t st);
+
+// Feature map stage (k_features.hip): phi_c of degree <= 3, optionally projected by P.
+int64_t feature_count_host(int d, int degree);
+atlasmem_status launch_feature_map(const void* X, bool in_bf16, int64_t n, int d, int degree, const float* c4,
+                                   const float* P, int d_out, float* out, hipStream_t st);
 
 // Input prologue (k_prologue.hip)
 atlasmem_status launch_short_conv(const void* X, bool in_bf16, int64_t M, int64_t T, int d, int heads,

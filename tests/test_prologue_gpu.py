@@ -206,3 +206,97 @@ def test_prologue_full_size_sampled():
             errs = [maxrel(got[g, b], ref[g]) for g in range(3)]
             log(f"PARITY gates_full chunk {chunk} sequence {b}: " + " ".join(f"{e:.3e}" for e in errs))
             assert max(errs) <= GATE_TOL
+
+
+# ----------------------------------------------------------------------------- feature map stage
+
+FMAP_F32_TOL = 1e-6   # products of up to three inputs in fp32 against fp64
+FMAP_PROJ_TOL = 1e-4  # the projection runs in split bf16 (hi/lo) with fp32 accumulation
+
+FMAP_CASES = [
+    # (name, n, d, degree, in_dtype, coeffs, d_out or 0)
+    ("deg1_bf16", 37, 7, 1, am.BF16, None, 0),
+    ("deg2_default", 37, 7, 2, am.BF16, None, 0),
+    ("deg3_default_ragged", 1001, 5, 3, am.F32, None, 0),
+    ("deg3_learned_coeffs_d32", 64, 32, 3, am.BF16, [0.9, 1.2, 0.4, 0.3], 0),
+    ("deg2_single_row", 1, 33, 2, am.F32, [1.0, 0.5, 0.25], 0),
+    ("deg2_project_d64", 300, 16, 2, am.BF16, None, 64),
+    ("deg3_project_ragged_d70", 130, 6, 3, am.F32, [1.0, 1.0, 0.5, 0.2], 70),
+    ("deg1_project_d5", 77, 9, 1, am.BF16, None, 5),
+]
+
+
+@pytest.mark.parametrize("case", FMAP_CASES, ids=[c[0] for c in FMAP_CASES])
+def test_feature_map_parity(case):
+    import torch
+    name, n, d, deg, dt, coeffs, d_out = case
+    log(f"CASE feature_map {name}")
+    r = np.random.default_rng(7)
+    x = r.standard_normal((n, d)).astype(np.float32) * 0.7
+    xin = synth.f32_to_bf16_bits(x) if dt == am.BF16 else x
+    xf = as_f64(xin, dt)
+    F = pro.feature_count(d, deg)
+    P = (r.standard_normal((d_out, F)) / np.sqrt(F)).astype(np.float32) if d_out else None
+    out = torch.full((n, d_out or F), float("nan"), dtype=torch.float32, device=DEV)
+    am.feature_map(to_dev(xin), dt, n, d, deg, out, coeffs=coeffs, P=None if P is None else to_dev(P), d_out=d_out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = pro.feature_map(xf, deg, coeffs, None if P is None else P.astype(np.float64))
+    err = maxrel(got, ref)
+    tol = FMAP_PROJ_TOL if d_out else FMAP_F32_TOL
+    log(f"PARITY feature_map_{name}: {err:.3e} (tol {tol:g})")
+    assert np.all(np.isfinite(got)) and err <= tol
+
+
+def test_feature_map_errors():
+    import torch
+    out = torch.empty((4, 10), dtype=torch.float32, device=DEV)
+    x = torch.zeros((4, 3), dtype=torch.float32, device=DEV)
+    for kw, status in ((dict(degree=0), am.E_INVALID), (dict(degree=4), am.E_INVALID), (dict(d=0), am.E_INVALID),
+                       (dict(d=200, degree=3), am.E_SHAPE)):
+        a = dict(n=4, d=3, degree=2)
+        a.update(kw)
+        with pytest.raises(am.AtlasMemError) as e:
+            am.feature_map(x, am.F32, a["n"], a["d"], a["degree"], out)
+        assert e.value.status == status
+
+
+def test_dot_exponential_features_with_omega_update():
+    """Dot: degree-3 exponential-kernel features of the keys and queries (from the feature map
+    stage) as the inputs of the Omega-window memory update, against the oracle on the same
+    composition."""
+    import torch
+    import oracle
+    from helpers import compare, config_for, BF16_TOL
+    B, H, T, dk = 1, 2, 96, 4
+    F = pro.feature_count(dk, 3)  # 35
+    spec = synth.spec(3, "stabilised", batch=B, heads=H, T=T, d_key=F, poly_degree=1, d_value=24, d_hidden=40,
+                      chunk=32, omega_window=3, input_dtype=synth.F32)
+    inp = synth.make_inputs(3, "stabilised", batch=B, heads=H, T=T, d_key=F, poly_degree=1, d_value=24,
+                            d_hidden=40, chunk=32, omega_window=3, input_dtype=synth.F32)
+    r = np.random.default_rng(3)
+    k_raw = r.standard_normal((B * H, T, dk)).astype(np.float32) * 0.5
+    q_raw = r.standard_normal((B * H, T, dk)).astype(np.float32) * 0.5
+    log("CASE dot_degree3_omega3")
+    Kf = torch.empty((B * H * T, F), dtype=torch.float32, device=DEV)
+    Qf = torch.empty_like(Kf)
+    am.feature_map(to_dev(k_raw.reshape(-1, dk)), am.F32, B * H * T, dk, 3, Kf)
+    am.feature_map(to_dev(q_raw.reshape(-1, dk)), am.F32, B * H * T, dk, 3, Qf)
+    mem = am.Memory(config_for(spec), to_dev(inp.W0), to_dev(inp.S0))
+    Y = torch.empty((B * H, T, spec.d_value), dtype=torch.float32, device=DEV)
+    mem.update_chunked(Kf.view(B * H, T, F), Qf.view(B * H, T, F), to_dev(inp.V), to_dev(inp.theta),
+                       to_dev(inp.eta), to_dev(inp.alpha), to_dev(inp.gamma), T, Y)
+    W = torch.empty((B * H, mem.P), dtype=torch.float32, device=DEV)
+    S = torch.empty_like(W)
+    status = mem.get_state(W, S)
+    torch.cuda.synchronize()
+    mem.close()
+    # the oracle on the same composition: fp64 features, then the literal recurrence
+    inp.K = np.stack([pro.feature_map(k_raw[m], 3) for m in range(B * H)])
+    inp.Q = np.stack([pro.feature_map(q_raw[m], 3) for m in range(B * H)])
+    ref = oracle.run_inputs(inp)
+    got = (Y.cpu().numpy().astype(np.float64), W.cpu().numpy().astype(np.float64),
+           S.cpu().numpy().astype(np.float64))
+    errs = compare("dot_degree3_omega3", spec, got, ref, BF16_TOL)
+    assert status == am.OK
+    assert all(v <= BF16_TOL for v in errs.values()), errs
