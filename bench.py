@@ -102,7 +102,8 @@ def stage_rooflines(torch, am, synth, dev, stream):
     (width 32 -> 561), Newton-Schulz over 4096 gradient matrices of 128 x 64; the input prologue at
     the Newton-Schulz workload's shape: the keys' short convolution (128 memories x 32768 tokens x
     64, bf16 in and out, L2-normalised) and the gates of 8 x 32768 token inputs of width 512 for 16
-    heads (per token: theta, eta, alpha, gamma; per chunk of 128: theta, eta, alpha)."""
+    heads (per token: theta, eta, alpha, gamma; per chunk of 128: theta, eta, alpha); the feature map
+    stage (degree 3 of 16384 width-32 vectors, and degree 2 of the 262144 keys projected to 64)."""
     out = {}
     M, T, C, c, d = 256, 32768, 64, 4, 32
     th = torch.rand((M, T), device=dev)
@@ -134,6 +135,13 @@ def stage_rooflines(torch, am, synth, dev, stream):
     gsc = torch.tensor(synth.GATE_SCALES, device=dev)
     gout = torch.empty((4, GB, CH, CT), device=dev)
     gout_c = torch.empty((3, GB, CH, CT // 128), device=dev)
+    FN3, FD = 16384, 32
+    F3 = (FD + 1) * (FD + 2) * (FD + 3) // 6
+    X3 = torch.randn((FN3, FD), device=dev).to(torch.bfloat16).view(torch.int16)
+    F3out = torch.empty((FN3, F3), device=dev)
+    FDO = 64
+    Pproj = torch.randn((FDO, F.shape[1]), device=dev) / F.shape[1] ** 0.5
+    Fproj = torch.empty((NP, FDO), device=dev)
     cases = [
         ("gate_scan", lambda: am.gate_scan(th, et, al, M, T, C, cW, cS, sc),
          M * T * (12 + 8) + M * (T // C) * 12, "hbm", f"{M} memories x {T} tokens, chunk {C}"),
@@ -151,6 +159,10 @@ def stage_rooflines(torch, am, synth, dev, stream):
         ("gates_per_chunk", lambda: am.gates(U, GB, CT, DM, CH, 3, Wg[:3], bg[:3], gsc[:3], 128, gout_c),
          GB * CT * DM * 2 + 3 * GB * CH * (CT // 128) * 4, "hbm",
          f"{GB} x {CT} inputs of width {DM}, 3 gates x {CH} heads, pooled per chunk of 128"),
+        ("feature_map_deg3", lambda: am.feature_map(X3, synth.BF16, FN3, FD, 3, F3out),
+         FN3 * (2 * FD + 4 * F3), "hbm", f"{FN3} bf16 vectors of width {FD} -> {F3} fp32 (degree 3)"),
+        ("feature_project_deg2", lambda: am.feature_map(X, synth.BF16, NP, d, 2, Fproj, P=Pproj, d_out=FDO),
+         2 * NP * F.shape[1] * FDO, "mfma", f"{NP} bf16 vectors of width {d}: degree-2 features x {FDO}-row projection"),
     ]
     for name, fn, work, bound, shape in cases:
         for _ in range(3):

@@ -88,14 +88,44 @@ struct FeatureArgs {
   float* out;
 };
 
-// Rows of kFeatRows inputs are staged in LDS; the block writes their contiguous features as a
-// stream, four features (one 16-byte store) per thread step.
-constexpr int kFeatRows = 8;
+// A monomial packed into 32 bits: degree in bits 30-31, indices in three 10-bit fields (d <= 1024).
+__device__ __forceinline__ uint32_t mono_code(const Mono& m) {
+  return ((uint32_t)m.deg << 30) | ((uint32_t)m.k << 20) | ((uint32_t)m.j << 10) | (uint32_t)m.i;
+}
+__device__ __forceinline__ float code_value(uint32_t code, const float* x, const float* c) {
+  const int deg = (int)(code >> 30);
+  const int i = (int)(code & 1023u), j = (int)((code >> 10) & 1023u), k = (int)((code >> 20) & 1023u);
+  switch (deg) {
+    case 0: return c[0];
+    case 1: return c[1] * x[i];
+    case 2: return c[2] * (x[i] * x[j]);
+    default: return c[3] * (x[i] * x[j] * x[k]);
+  }
+}
+
+// kFeatRows input rows per block in LDS, then the monomial table (TAB, when it fits) so that each
+// feature costs one table read; the block streams the rows' contiguous features out as 16-byte
+// stores.  Without the table a thread decodes the monomial of each run of four features.
+constexpr int kFeatRows = 32;
+constexpr int kFeatTabMax = 12288;  // table entries (48 KB)
+template <bool TAB>
 __global__ void __launch_bounds__(256) feature_kernel(FeatureArgs a) {
-  extern __shared__ float xr[];  // [kFeatRows][d]
+  extern __shared__ float xr[];  // [kFeatRows][d], then the table
+  uint32_t* tab = (uint32_t*)(xr + kFeatRows * a.d);
   const int64_t r0 = (int64_t)blockIdx.x * kFeatRows;
   const int nr = (int)((a.n - r0) < kFeatRows ? (a.n - r0) : kFeatRows);
   for (int e = threadIdx.x; e < nr * a.d; e += blockDim.x) xr[e] = load_in(a.X, r0 * a.d + e, a.in_bf16);
+  if (TAB) {
+    const int per = (int)((a.F + blockDim.x - 1) / blockDim.x);
+    const int64_t f0 = (int64_t)threadIdx.x * per;
+    if (f0 < a.F) {  // each thread decodes one run and steps through it
+      Mono m = mono_of(f0, a.d);
+      for (int u = 0; u < per && f0 + u < a.F; ++u) {
+        tab[f0 + u] = mono_code(m);
+        if (f0 + u + 1 < a.F) m = mono_next(m, a.d);
+      }
+    }
+  }
   __syncthreads();
   const int64_t total = (int64_t)nr * a.F;
   float* base = a.out + r0 * a.F;
@@ -103,21 +133,33 @@ __global__ void __launch_bounds__(256) feature_kernel(FeatureArgs a) {
   for (int64_t e0 = (int64_t)threadIdx.x * 4; e0 < total; e0 += (int64_t)blockDim.x * 4) {
     int64_t r = e0 / a.F;
     int64_t f = e0 - r * a.F;
-    Mono m = mono_of(f, a.d);
     float v[4];
+    if (TAB) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (e0 + u < total) {
-        if (f == a.F) {  // the next row starts
+      for (int u = 0; u < 4; ++u) {
+        if (f == a.F) {
           ++r;
           f = 0;
-          m = Mono{0, 0, 0, 0};
         }
-        v[u] = mono_value(m, xr + r * a.d, a.c);
+        v[u] = (e0 + u < total) ? code_value(tab[f], xr + r * a.d, a.c) : 0.0f;
         ++f;
-        if (f < a.F) m = mono_next(m, a.d);
-      } else {
-        v[u] = 0.0f;
+      }
+    } else {
+      Mono m = mono_of(f, a.d);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (e0 + u < total) {
+          if (f == a.F) {  // the next row starts
+            ++r;
+            f = 0;
+            m = Mono{0, 0, 0, 0};
+          }
+          v[u] = mono_value(m, xr + r * a.d, a.c);
+          ++f;
+          if (f < a.F) m = mono_next(m, a.d);
+        } else {
+          v[u] = 0.0f;
+        }
       }
     }
     if (vec && e0 + 3 < total) {
@@ -144,21 +186,31 @@ struct FeatMapA {
       for (int u = 0; u < 8; ++u) v[u] = 0.0f;
       return;
     }
-    // the row's inputs are read through the cache; a monomial needs at most three of them
+    // Consecutive monomials mostly advance only their last index: the coefficient times the
+    // other factors is kept and refreshed when they change, so most features cost one load.
     Mono m = mono_of(f0, d);
     const int64_t rb = (int64_t)row * d;
+    auto head = [&](const Mono& q) -> float {
+      switch (q.deg) {
+        case 0: return c[0];
+        case 1: return c[1];
+        case 2: return c[2] * load_in(X, rb + q.i, in_bf16);
+        default: return c[3] * load_in(X, rb + q.i, in_bf16) * load_in(X, rb + q.j, in_bf16);
+      }
+    };
+    float pre = head(m);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       float x = 0.0f;
       if (f0 + u < F) {
-        switch (m.deg) {
-          case 0: x = c[0]; break;
-          case 1: x = c[1] * load_in(X, rb + m.i, in_bf16); break;
-          case 2: x = c[2] * (load_in(X, rb + m.i, in_bf16) * load_in(X, rb + m.j, in_bf16)); break;
-          default:
-            x = c[3] * (load_in(X, rb + m.i, in_bf16) * load_in(X, rb + m.j, in_bf16) * load_in(X, rb + m.k, in_bf16));
+        const int last = m.deg == 3 ? m.k : (m.deg == 2 ? m.j : m.i);
+        x = m.deg == 0 ? pre : pre * load_in(X, rb + last, in_bf16);
+        if (f0 + u + 1 < F) {
+          const Mono nx = mono_next(m, d);
+          const bool same_head = nx.deg == m.deg && (m.deg == 1 || (nx.i == m.i && (m.deg == 2 || nx.j == m.j)));
+          m = nx;
+          if (!same_head) pre = head(m);
         }
-        if (f0 + u + 1 < F) m = mono_next(m, d);
       }
       v[u] = x;
     }
@@ -196,7 +248,20 @@ atlasmem_status launch_feature_map(const void* X, bool in_bf16, int64_t n, int d
     a.out = out;
     const int64_t blocks = (n + kFeatRows - 1) / kFeatRows;
     if (blocks > INT32_MAX) return ATLASMEM_E_SHAPE;
-    hipLaunchKernelGGL(feature_kernel, dim3((unsigned)blocks), dim3(256), (size_t)kFeatRows * d * sizeof(float), st, a);
+    const size_t rows_lds = (size_t)kFeatRows * d * sizeof(float);
+    if (F <= kFeatTabMax) {
+      const size_t lds = rows_lds + (size_t)F * sizeof(uint32_t);
+      if (lds > 64 * 1024 && hipFuncSetAttribute((const void*)feature_kernel<true>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return ATLASMEM_E_DEVICE;
+      hipLaunchKernelGGL(feature_kernel<true>, dim3((unsigned)blocks), dim3(256), lds, st, a);
+    } else {
+      if (rows_lds > 64 * 1024 && hipFuncSetAttribute((const void*)feature_kernel<false>,
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                      (int)rows_lds) != hipSuccess)
+        return ATLASMEM_E_DEVICE;
+      hipLaunchKernelGGL(feature_kernel<false>, dim3((unsigned)blocks), dim3(256), rows_lds, st, a);
+    }
     AM_LAUNCH_CHECK();
     return ATLASMEM_OK;
   }
