@@ -1,0 +1,94 @@
+"""fp64 oracle of the outer-loop backward of the memory update: the gradients of an outer loss
+with respect to every input of the chunked test-time update (keys, queries, values, gates,
+initial state), i.e. the derivative of the inner recurrence, which itself contains the inner
+gradient (the "gradient of the gradient").
+
+TEST INFRASTRUCTURE.  Only the test suite may import this module.  The library never calls it.
+
+What it computes, and where the pages define it
+-----------------------------------------------
+The outer loop trains the model through the test-time updates: the full forward pass runs the
+inner updates, and the outer loss is back-propagated through them (Atlas-Torch README, "How the
+memory works": the two loops; Bug Fixes table, "Store-path gradient starvation": outer-loop
+gradient to the store-side parameters through the memory).  For a scalar outer loss L with
+adjoints dY = dL/dY and dW_T, dS_T = dL/d(final state), the gradients are those of
+    L = <dY, Y> + <dW_T, W_T> + <dS_T, S_T>
+with Y, W_T, S_T from the literal chunked recurrence (the fp64 oracle's algorithm, restated
+with torch operations) -- the plain definition of a vector-Jacobian product, taken here by
+torch autograd as a library step.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .neural_memory import LINEAR, MLP2_SILU, PER_TOKEN, MemoryConfig
+
+
+def _silu(z):
+    return z * torch.sigmoid(z)
+
+
+def _apply(params, x):
+    if len(params) == 1:
+        return params[0] @ x
+    return params[1] @ _silu(params[0] @ x)
+
+
+def _grad(params, x, v):
+    """The inner gradient of ||M_W(x) - v||^2, written out (so that it can itself be
+    differentiated): linear 2 (W x - v) x^T; MLP e = 2 (W2 h - v), (W2^T e) * silu'(z) x^T, e h^T."""
+    if len(params) == 1:
+        return [torch.outer(2.0 * (params[0] @ x - v), x)]
+    w1, w2 = params
+    z = w1 @ x
+    s = torch.sigmoid(z)
+    h = z * s
+    e = 2.0 * (w2 @ h - v)
+    sp = s * (1.0 + z * (1.0 - s))
+    return [torch.outer((w2.T @ e) * sp, x), torch.outer(e, h)]
+
+
+def run_memory_torch(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha):
+    """The literal chunked recurrence for one memory (per-token gates, window 1, identity
+    features) with torch tensors: Y, final params, final momenta."""
+    assert cfg.gate_mode == PER_TOKEN and cfg.omega_window == 1 and cfg.poly_degree == 1
+    W = list(params)
+    S = list(momenta)
+    T = K.shape[0]
+    C = cfg.chunk
+    Y = []
+    for s in range(0, T, C):
+        e = min(s + C, T)
+        wb = list(W)
+        for t in range(s, e):
+            Y.append(_apply(wb, Q[t]))
+        for t in range(s, e):
+            G = _grad(wb, K[t], V[t])
+            S = [eta[t] * S[m] - theta[t] * G[m] for m in range(len(W))]
+            W = [(1.0 - alpha[t]) * W[m] + S[m] for m in range(len(W))]
+    return torch.stack(Y), W, S
+
+
+def outer_grads(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, dY, dW_T=None, dS_T=None):
+    """Gradients of <dY, Y> + <dW_T, W_T> + <dS_T, S_T> (numpy in, numpy out, fp64):
+    dict with K, Q, V, theta, eta, alpha, W0 (list), S0 (list)."""
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
+    P = [t(p) for p in params]
+    M = [t(m) for m in momenta]
+    k, q, v, th, et, al = t(K), t(Q), t(V), t(theta), t(eta), t(alpha)
+    Y, W, S = run_memory_torch(cfg, P, M, k, q, v, th, et, al)
+    L = (Y * torch.tensor(np.asarray(dY, dtype=np.float64))).sum()
+    if dW_T is not None:
+        L = L + sum((w * torch.tensor(np.asarray(d, dtype=np.float64))).sum() for w, d in zip(W, dW_T))
+    if dS_T is not None:
+        L = L + sum((m * torch.tensor(np.asarray(d, dtype=np.float64))).sum() for m, d in zip(S, dS_T))
+    grads = torch.autograd.grad(L, [k, q, v, th, et, al] + P + M, allow_unused=True)
+    z = lambda g, ref: np.zeros(ref.shape) if g is None else g.detach().numpy()
+    names = ["K", "Q", "V", "theta", "eta", "alpha"]
+    srcs = [k, q, v, th, et, al]
+    out = {n: z(g, s) for n, g, s in zip(names, grads[:6], srcs)}
+    out["W0"] = [z(g, p) for g, p in zip(grads[6:6 + len(P)], P)]
+    out["S0"] = [z(g, m) for g, m in zip(grads[6 + len(P):], M)]
+    return out

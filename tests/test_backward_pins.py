@@ -1,0 +1,87 @@
+"""Pins of the outer-loop backward oracle: its torch restatement of the recurrence against the numpy
+oracle, and its autograd gradients against central finite differences of the numpy oracle's
+forward (independent of autograd), for every input group."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import LINEAR, MLP2_SILU, PER_TOKEN, MemoryConfig
+from oracle import backward as bw
+
+
+def problem(seed, kind, T=8, C=4, d=3, v=2, h=5):
+    r = np.random.default_rng(seed)
+    cfg = MemoryConfig(kind, d, v, h if kind != LINEAR else 0, 1, C, 1, PER_TOKEN, 0)
+    if kind == LINEAR:
+        params = [r.normal(0, 0.5, (v, d))]
+    else:
+        params = [r.normal(0, 0.5, (h, d)), r.normal(0, 0.5, (v, h))]
+    momenta = [r.normal(0, 0.1, p.shape) for p in params]
+    K = r.normal(0, 1, (T, d)) / np.sqrt(d)
+    Q = r.normal(0, 1, (T, d)) / np.sqrt(d)
+    V = r.normal(0, 1, (T, v))
+    th, et, al = r.uniform(0.01, 0.1, T), r.uniform(0.8, 0.99, T), r.uniform(0.0, 0.05, T)
+    dY = r.normal(size=(T, v))
+    dW = [r.normal(size=p.shape) for p in params]
+    dS = [r.normal(size=p.shape) for p in params]
+    return cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS
+
+
+def objective(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS):
+    res = oracle.run_memory(cfg, params, momenta, K, Q, V, th, et, al)
+    return (np.sum(res.Y * dY) + sum(np.sum(a * b) for a, b in zip(res.params, dW))
+            + sum(np.sum(a * b) for a, b in zip(res.momenta, dS)))
+
+
+@pytest.mark.parametrize("kind", [LINEAR, MLP2_SILU])
+def test_torch_restatement_matches_oracle(kind):
+    import torch
+    cfg, params, momenta, K, Q, V, th, et, al, *_ = problem(1, kind, T=10, C=4)
+    ref = oracle.run_memory(cfg, params, momenta, K, Q, V, th, et, al)
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
+    Y, W, S = bw.run_memory_torch(cfg, [t(p) for p in params], [t(m) for m in momenta], t(K), t(Q), t(V), t(th),
+                                  t(et), t(al))
+    np.testing.assert_allclose(Y.numpy(), ref.Y, rtol=1e-13, atol=1e-14)
+    for a, b in zip(W, ref.params):
+        np.testing.assert_allclose(a.numpy(), b, rtol=1e-13, atol=1e-14)
+    for a, b in zip(S, ref.momenta):
+        np.testing.assert_allclose(a.numpy(), b, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("kind", [LINEAR, MLP2_SILU])
+def test_outer_gradients_against_finite_differences(kind):
+    """<grad, delta> against (L(x + h delta) - L(x - h delta)) / 2h with L from the numpy oracle,
+    for a random direction in every input group (a wrong sign, index or dropped term in any
+    group changes its directional derivative)."""
+    cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS = problem(2, kind, T=9, C=4)
+    g = bw.outer_grads(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS)
+    r = np.random.default_rng(3)
+    args = dict(params=params, momenta=momenta, K=K, Q=Q, V=V, th=th, et=et, al=al)
+    groups = [("K", "K"), ("Q", "Q"), ("V", "V"), ("theta", "th"), ("eta", "et"), ("alpha", "al")]
+    hstep = 1e-6
+    for gname, aname in groups:
+        d = r.normal(size=np.shape(args[aname]))
+        plus = dict(args)
+        minus = dict(args)
+        plus[aname] = args[aname] + hstep * d
+        minus[aname] = args[aname] - hstep * d
+        fd = (objective(cfg, **plus, dY=dY, dW=dW, dS=dS) - objective(cfg, **minus, dY=dY, dW=dW, dS=dS)) / (2 * hstep)
+        an = float(np.sum(g[gname] * d))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (gname, fd, an)
+    for gname, aname in (("W0", "params"), ("S0", "momenta")):
+        ds = [r.normal(size=p.shape) for p in args[aname]]
+        plus = dict(args)
+        minus = dict(args)
+        plus[aname] = [p + hstep * dd for p, dd in zip(args[aname], ds)]
+        minus[aname] = [p - hstep * dd for p, dd in zip(args[aname], ds)]
+        fd = (objective(cfg, **plus, dY=dY, dW=dW, dS=dS) - objective(cfg, **minus, dY=dY, dW=dW, dS=dS)) / (2 * hstep)
+        an = float(sum(np.sum(a * b) for a, b in zip(g[gname], ds)))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (gname, fd, an)
+
+
+def test_zero_adjoints_give_zero_gradients():
+    cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS = problem(4, MLP2_SILU)
+    g = bw.outer_grads(cfg, params, momenta, K, Q, V, th, et, al, np.zeros_like(dY))
+    for k in ("K", "Q", "V", "theta", "eta", "alpha"):
+        assert not np.any(g[k])
