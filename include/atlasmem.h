@@ -239,6 +239,27 @@ atlasmem_status atlasmem_newton_schulz(const float* G, int64_t n_mat, int32_t ro
                                        int32_t steps, float a, float b, float c, float eps,
                                        int32_t precision, float* out, void* stream);
 
+/* Outer-loop backward (the training path): runs the update over T tokens exactly as
+ * atlasmem_update_chunked does (advancing the handle's state and writing Y when Y != NULL), and
+ * returns the gradients of an outer loss L, given dY = dL/dY and the adjoints dW_T, dS_T of the
+ * final state, with respect to every input of the update and the state it started from
+ * (Atlas-Torch README, "How the memory works": the outer loop trains through the inner updates;
+ * the derivative of the recurrence includes that of the inner gradient).
+ * Scope: MLP2_SILU, PER_TOKEN gates, omega_window 1, poly_degree 1, no per-token retrieval
+ * (E_UNSUPPORTED otherwise); T a multiple of the chunk and nothing pending (E_SHAPE otherwise).
+ *   dY: fp32 [M, T, d_value];  dW_T, dS_T: fp32 [M, P] or NULL (zero)
+ *   workspace: device memory of atlasmem_backward_workspace_bytes(h, T) bytes (the chunk-start
+ *          states of the forward and the backward's buffers); the call allocates nothing
+ *   dK, dQ: fp32 [M, T, d_key]; dV: fp32 [M, T, d_value]; dtheta, deta, dalpha: fp32 [M, T];
+ *   dW0, dS0: fp32 [M, P] (gradients with respect to the state at the start of the call) */
+int64_t atlasmem_backward_workspace_bytes(atlasmem_handle h, int64_t T);
+atlasmem_status atlasmem_update_backward(atlasmem_handle h, const void* K, const void* Q, const void* V,
+                                         const float* theta, const float* eta, const float* alpha, int64_t T,
+                                         void* Y, const float* dY, const float* dW_T, const float* dS_T,
+                                         void* workspace, int64_t workspace_bytes, float* dK, float* dQ,
+                                         float* dV, float* dtheta, float* deta, float* dalpha, float* dW0,
+                                         float* dS0, void* stream);
+
 /* Feature map of n rows of width d: every monomial of degree 0..degree (degree 1..3), degree-major
  * and in combinations_with_replacement order inside a degree, the degree-k monomials multiplied
  * by coeffs[k] -- and, with P, projected back (Atlas-Torch README, Atlas Extensions table,

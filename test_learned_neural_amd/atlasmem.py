@@ -29,7 +29,7 @@ EXPORTS = (
     "atlasmem_set_state",
     "atlasmem_reset_history", "atlasmem_destroy", "atlasmem_gate_scan", "atlasmem_omega_coeffs",
     "atlasmem_poly_features", "atlasmem_newton_schulz", "atlasmem_short_conv", "atlasmem_gates",
-    "atlasmem_feature_map",
+    "atlasmem_feature_map", "atlasmem_backward_workspace_bytes", "atlasmem_update_backward",
 )
 
 
@@ -87,6 +87,8 @@ def load():
                                 ctypes.c_int),
         "atlasmem_gates": ([_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
         "atlasmem_feature_map": ([_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
+        "atlasmem_backward_workspace_bytes": ([_vp, _i64], _i64),
+        "atlasmem_update_backward": ([_vp] * 7 + [_i64] + [_vp] * 5 + [_i64] + [_vp] * 9, ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -163,6 +165,17 @@ class Memory:
     @property
     def pending(self) -> int:
         return int(load().atlasmem_pending(self._h))
+
+    def backward_workspace_bytes(self, T: int) -> int:
+        return int(load().atlasmem_backward_workspace_bytes(self._h, int(T)))
+
+    def update_backward(self, K, Q, V, theta, eta, alpha, T: int, dY, dK, dQ, dV, dtheta, deta, dalpha, dW0, dS0,
+                        workspace, Y=None, dW_T=None, dS_T=None, stream=None):
+        _check(load().atlasmem_update_backward(
+            self._h, _ptr(K), _ptr(Q), _ptr(V), _ptr(theta), _ptr(eta), _ptr(alpha), int(T), _ptr(Y), _ptr(dY),
+            _ptr(dW_T), _ptr(dS_T), _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(dK),
+            _ptr(dQ), _ptr(dV), _ptr(dtheta), _ptr(deta), _ptr(dalpha), _ptr(dW0), _ptr(dS0), _stream(stream)),
+            "atlasmem_update_backward")
 
     def retrieve(self, Q, T: int, Y, stream=None):
         _check(load().atlasmem_retrieve(self._h, _ptr(Q), int(T), _ptr(Y), _stream(stream)), "atlasmem_retrieve")

@@ -586,4 +586,32 @@ atlasmem_status atlasmem_feature_map(const void* X, int32_t in_dtype, int64_t n,
   return launch_feature_map(X, in_dtype == ATLASMEM_BF16, n, d, degree, c4, P, P ? d_out : 0, out, S(stream));
 }
 
+int64_t atlasmem_backward_workspace_bytes(atlasmem_handle hh, int64_t T) {
+  const Handle* h = (const Handle*)hh;
+  if (!h || T < 0 || !backward_supported(h->d)) return -1;
+  return backward_workspace_bytes(h->d, T);
+}
+
+atlasmem_status atlasmem_update_backward(atlasmem_handle hh, const void* K, const void* Q, const void* V,
+                                         const float* theta, const float* eta, const float* alpha, int64_t T,
+                                         void* Y, const float* dY, const float* dW_T, const float* dS_T,
+                                         void* workspace, int64_t workspace_bytes, float* dK, float* dQ, float* dV,
+                                         float* dtheta, float* deta, float* dalpha, float* dW0, float* dS0,
+                                         void* stream) {
+  Handle* h = (Handle*)hh;
+  if (!h || T < 0) return ATLASMEM_E_INVALID;
+  const Dims& d = h->d;
+  if (!backward_supported(d)) return ATLASMEM_E_UNSUPPORTED;
+  if (T % d.C != 0 || h->pending != 0) return ATLASMEM_E_SHAPE;
+  if (T == 0) return ATLASMEM_OK;
+  if (!K || !Q || !V || !theta || !eta || !alpha || !dY || !workspace || !dK || !dQ || !dV || !dtheta || !deta ||
+      !dalpha || !dW0 || !dS0)
+    return ATLASMEM_E_INVALID;
+  if (workspace_bytes < backward_workspace_bytes(d, T)) return ATLASMEM_E_INVALID;
+  DeviceGuard g(h->device);
+  if (!g.ok) return ATLASMEM_E_DEVICE;
+  return backward(h, K, Q, V, theta, eta, alpha, T, Y, dY, dW_T, dS_T, workspace, dK, dQ, dV, dtheta, deta, dalpha,
+                  dW0, dS0, S(stream));
+}
+
 }  // extern "C"

@@ -112,6 +112,15 @@ namespace am {
 
 using Handle = ::atlasmem_handle_s;
 
+// Outer-loop backward (k_backward.hip)
+bool backward_supported(const Dims& d);
+int64_t backward_workspace_bytes(const Dims& d, int64_t T);
+atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V, const float* theta, const float* eta,
+                         const float* alpha, int64_t T, void* Y, const float* dY, const float* dWT, const float* dST,
+                         void* workspace, float* dK, float* dQ, float* dV, float* dth, float* det, float* dal,
+                         float* dW0, float* dS0, hipStream_t st);
+
+
 
 // Launchers (enqueue only; return ATLASMEM_OK or ATLASMEM_E_DEVICE on a launch error).
 atlasmem_status launch_gate_scan(const float* theta, const float* eta, const float* alpha, int M, int64_t ld_gate,

@@ -1,0 +1,526 @@
+// Outer-loop backward of the chunked update: the gradients of an outer loss with respect to the
+// keys, queries, values, gates and initial state of the test-time update (Atlas-Torch README,
+// "How the memory works": the outer loop trains through the inner updates).  Scope: the 2-layer
+// SiLU memory with per-token gates, window 1 and identity features.
+//
+// Forward of chunk k from (W, S) = (W1, W2, S1, S2), rows r of the chunk (titans-pytorch-mlx
+// README, Eq. 12-14; gradients at the chunk-start weights, ATLAS summary, section 3.3):
+//   Z = X W1^T, H = silu(Z), E = 2 (H W2^T - V), P = E W2, D1 = P * silu'(Z)
+//   W' = beta W + aS S - sum_r cW_r g_r,  S' = PC S - sum_r cS_r g_r,  g_r = (D1_r x_r^T, E_r h_r^T)
+//   Y = silu(Q W1^T) W2^T
+// with (cW, cS, PC, beta, aS) from the gate scan.  Given the adjoints (WA, SA) of (W', S') and dY,
+// the backward of the chunk is (every product batched over memories on the GEMM engine):
+//   U1 = X WA1^T, U1s = X SA1^T, U2 = H WA2^T, U2s = H SA2^T
+//   cW'_r = -(<D1_r, U1_r> + <E_r, U2_r>),  cS'_r = -(<D1_r, U1s_r> + <E_r, U2s_r>)
+//   D1' = -(cW U1 + cS U1s),  E'_g = -(cW U2 + cS U2s),  P' = D1' silu'(Z),  Z'_1 = D1' P silu''(Z)
+//   E' = E'_g + P' W2^T,  V' = -2 E'
+//   W2' = E^T P' + (2E')^T H + dY^T Hq
+//   H' = -(cW E) WA2 - (cS E) SA2 + (2E') W2,  Z' = Z'_1 + H' silu'(Z)
+//   X' = -(cW D1) WA1 - (cS D1) SA1 + Z' W1
+//   Zq' = (dY W2) silu'(Zq),  Q' = Zq' W1,  W1' = Z'^T X + Zq'^T Q
+//   beta' = <WA, W>, aS' = <WA, S>, PC' = <SA, S>;  gates' from (cW', cS', PC', beta', aS') by the
+//   reverse of the gate scan
+//   WA <- beta WA + (W1', W2'),  SA <- aS WA + PC SA        (the adjoints at the chunk start)
+#include "common.h"
+#include "gemm.h"
+#include "internal.h"
+
+namespace am {
+namespace bk {
+
+// One operand source: element (z, outer, k) of base[z * sz + outer * so + k * sk] (fp32, or bf16
+// input bits), optionally through silu or scaled by a per-outer coefficient, times `scale`.
+struct Src {
+  const void* base;
+  int bf16;
+  int64_t sz, so, sk;
+  int outer_dim, K;
+  int xf;  // 0 none, 1 silu, 2 times coef[z * cz + outer]
+  const float* coef;
+  int64_t cz;
+  float scale;
+  __device__ __forceinline__ float get(int z, int outer, int k) const {
+    if (outer >= outer_dim || k >= K) return 0.0f;
+    const int64_t i = (int64_t)z * sz + (int64_t)outer * so + (int64_t)k * sk;
+    float x = bf16 ? bf16_value(((const uint16_t*)base)[i]) : ((const float*)base)[i];
+    if (xf == 1) x = siluf_(x);
+    else if (xf == 2) x *= coef[(int64_t)z * cz + outer];
+    return x * scale;
+  }
+};
+
+__host__ __device__ inline Src src(const void* base, int bf16, int64_t sz, int64_t so, int64_t sk, int outer_dim,
+                                   int K, int xf = 0, const float* coef = nullptr, int64_t cz = 0,
+                                   float scale = 1.0f) {
+  Src s;
+  s.base = base;
+  s.bf16 = bf16;
+  s.sz = sz;
+  s.so = so;
+  s.sk = sk;
+  s.outer_dim = outer_dim;
+  s.K = K;
+  s.xf = xf;
+  s.coef = coef;
+  s.cz = cz;
+  s.scale = scale;
+  return s;
+}
+
+// Up to three sources concatenated along k: [0, k1) from a, [k1, k2) from b, [k2, K) from c.
+struct Cat {
+  Src a, b, c;
+  int k1, k2, K;
+  __device__ __forceinline__ void load8(int z, int outer, int k0, float* v) const {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u;
+      float x = 0.0f;
+      if (k < k1) x = a.get(z, outer, k);
+      else if (k < k2) x = b.get(z, outer, k - k1);
+      else if (k < K) x = c.get(z, outer, k - k2);
+      v[u] = x;
+    }
+  }
+};
+inline Cat cat1(const Src& a) { return Cat{a, a, a, a.K, a.K, a.K}; }
+inline Cat cat2(const Src& a, const Src& b, int k1) { return Cat{a, b, b, k1, k1 + b.K, k1 + b.K}; }
+inline Cat cat3(const Src& a, const Src& b, const Src& c, int k1, int k2) {
+  return Cat{a, b, c, k1, k2, k2 + c.K};
+}
+
+// ---------------------------------------------------------------------------- epilogues
+
+struct EpiSt {  // out[z * sz + row * ld + col]
+  float* out;
+  int64_t sz;
+  int ld;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    out[(int64_t)z * sz + (int64_t)row * ld + col] = v;
+  }
+};
+struct EpiE {  // E = 2 (acc - V)
+  float* E;
+  int64_t ez;
+  const void* V;
+  int bf16;
+  int64_t vz;  // V element stride per memory (T * dv); V already offset to the chunk
+  int dv;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    const float vv = load_in(V, (int64_t)z * vz + (int64_t)row * dv + col, bf16);
+    E[(int64_t)z * ez + (int64_t)row * dv + col] = 2.0f * (v - vv);
+  }
+};
+struct EpiPD1 {  // P = acc, D1 = acc * silu'(Z)
+  float* P;
+  float* D1;
+  const float* Z;
+  int64_t pz, zz;
+  int dh;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    const int64_t o = (int64_t)z * pz + (int64_t)row * dh + col;
+    P[o] = v;
+    D1[o] = v * silu_primef_(Z[(int64_t)z * zz + (int64_t)row * dh + col]);
+  }
+};
+struct EpiEa {  // Ea = Eg + acc (in place), dV = -2 Ea
+  float* Ea;
+  int64_t ez;
+  float* dV;
+  int64_t vz;  // dV already offset to the chunk
+  int dv;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    float* p = Ea + (int64_t)z * ez + (int64_t)row * dv + col;
+    const float e = *p + v;
+    *p = e;
+    dV[(int64_t)z * vz + (int64_t)row * dv + col] = -2.0f * e;
+  }
+};
+struct EpiZa {  // Za = Za1 + acc * silu'(Z) (in place)
+  float* Za;
+  const float* Z;
+  int64_t pz, zz;
+  int dh;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    float* p = Za + (int64_t)z * pz + (int64_t)row * dh + col;
+    *p += v * silu_primef_(Z[(int64_t)z * zz + (int64_t)row * dh + col]);
+  }
+};
+struct EpiScaleSp {  // out = acc * silu'(Z[row + zr0])
+  float* out;
+  const float* Z;
+  int64_t oz, zz;
+  int zr0, dh;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    out[(int64_t)z * oz + (int64_t)row * dh + col] =
+        v * silu_primef_(Z[(int64_t)z * zz + (int64_t)(zr0 + row) * dh + col]);
+  }
+};
+
+// ---------------------------------------------------------------------------- small kernels
+
+__device__ __forceinline__ float silu_second(float z) {
+  const float s = sigmoidf_(z);
+  return s * (1.0f - s) * (2.0f + z * (1.0f - 2.0f * s));
+}
+
+// Per (row, memory): the coefficient adjoints and the elementwise adjoints (see the header).
+// Each lane reads and then overwrites only its own elements.
+__global__ void row_kernel(const float* __restrict__ Z, int64_t zz, float* __restrict__ Pz, const float* __restrict__ D1,
+                           float* __restrict__ U1, float* __restrict__ U1s, const float* __restrict__ E,
+                           float* __restrict__ U2, const float* __restrict__ U2s, int64_t hz, int64_t vz, int dh,
+                           int dv, int C, const float* __restrict__ cW, const float* __restrict__ cS,
+                           float* __restrict__ cWa, float* __restrict__ cSa) {
+  const int r = blockIdx.x, z = blockIdx.y, lane = threadIdx.x;
+  const int64_t ho = (int64_t)z * hz + (int64_t)r * dh, vo = (int64_t)z * vz + (int64_t)r * dv;
+  float s1 = 0.0f, s1s = 0.0f, s2 = 0.0f, s2s = 0.0f;
+  for (int j = lane; j < dh; j += 64) {
+    s1 += D1[ho + j] * U1[ho + j];
+    s1s += D1[ho + j] * U1s[ho + j];
+  }
+  for (int j = lane; j < dv; j += 64) {
+    s2 += E[vo + j] * U2[vo + j];
+    s2s += E[vo + j] * U2s[vo + j];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    s1 += __shfl_xor(s1, off, 64);
+    s1s += __shfl_xor(s1s, off, 64);
+    s2 += __shfl_xor(s2, off, 64);
+    s2s += __shfl_xor(s2s, off, 64);
+  }
+  const float cw = cW[(int64_t)z * C + r], cs = cS[(int64_t)z * C + r];
+  if (lane == 0) {
+    cWa[(int64_t)z * C + r] = -(s1 + s2);
+    cSa[(int64_t)z * C + r] = -(s1s + s2s);
+  }
+  for (int j = lane; j < dh; j += 64) {
+    const float zv = Z[(int64_t)z * zz + (int64_t)r * dh + j];
+    const float d1a = -(cw * U1[ho + j] + cs * U1s[ho + j]);
+    const float p = Pz[ho + j];
+    U1s[ho + j] = d1a * silu_primef_(zv);  // P'
+    Pz[ho + j] = d1a * p * silu_second(zv);  // Z'_1
+  }
+  for (int j = lane; j < dv; j += 64) U2[vo + j] = -(cw * U2[vo + j] + cs * U2s[vo + j]);  // E'_g
+}
+
+// beta' = <WA, W>, aS' = <WA, S>, PC' = <SA, S> per memory; ck: [M][2P] (W then S).
+__global__ void scalar_adj_kernel(const float* __restrict__ WA, const float* __restrict__ SA,
+                                  const float* __restrict__ ck, int64_t P, float* __restrict__ out) {
+  __shared__ float red[3][4];
+  const int z = blockIdx.x;
+  const float* w = ck + (int64_t)z * 2 * P;
+  const float* s = w + P;
+  const float* wa = WA + (int64_t)z * P;
+  const float* sa = SA + (int64_t)z * P;
+  float b = 0.0f, a = 0.0f, p = 0.0f;
+  for (int64_t i = threadIdx.x; i < P; i += blockDim.x) {
+    b += wa[i] * w[i];
+    a += wa[i] * s[i];
+    p += sa[i] * s[i];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    b += __shfl_xor(b, off, 64);
+    a += __shfl_xor(a, off, 64);
+    p += __shfl_xor(p, off, 64);
+  }
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wv] = b;
+    red[1][wv] = a;
+    red[2][wv] = p;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    out[z * 3 + 0] = red[2][0] + red[2][1] + red[2][2] + red[2][3];  // PC'
+    out[z * 3 + 1] = red[0][0] + red[0][1] + red[0][2] + red[0][3];  // beta'
+    out[z * 3 + 2] = red[1][0] + red[1][1] + red[1][2] + red[1][3];  // aS'
+  }
+}
+
+// Reverse of the gate scan for one chunk of every memory (thread 0 of a block per memory walks the
+// chunk; e, b, w recomputed in LDS):  e_{C-1} = b_{C-1} = w_{C-1} = 1, e_r = eta_{r+1} e_{r+1},
+// b_r = (1 - alpha_{r+1}) b_{r+1}, w_r = b_r + eta_{r+1} w_{r+1}, cS = theta e, cW = theta w,
+// PC = eta_0 e_0, beta = (1 - alpha_0) b_0, aS = eta_0 w_0.
+__global__ void gate_bwd_kernel(const float* __restrict__ theta, const float* __restrict__ eta,
+                                const float* __restrict__ alpha, int64_t ld, int64_t s0, int C,
+                                const float* __restrict__ cWa, const float* __restrict__ cSa,
+                                const float* __restrict__ sca, float* __restrict__ dth, float* __restrict__ det,
+                                float* __restrict__ dal) {
+  extern __shared__ float gb[];  // e, b, w, ea, wa, ba [C] each
+  const int z = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  float* e = gb;
+  float* b = gb + C;
+  float* w = gb + 2 * C;
+  float* ea = gb + 3 * C;
+  float* wa = gb + 4 * C;
+  float* ba = gb + 5 * C;
+  const float* th = theta + (int64_t)z * ld + s0;
+  const float* et = eta + (int64_t)z * ld + s0;
+  const float* al = alpha + (int64_t)z * ld + s0;
+  float* oth = dth + (int64_t)z * ld + s0;
+  float* oet = det + (int64_t)z * ld + s0;
+  float* oal = dal + (int64_t)z * ld + s0;
+  e[C - 1] = b[C - 1] = w[C - 1] = 1.0f;
+  for (int r = C - 2; r >= 0; --r) {
+    e[r] = et[r + 1] * e[r + 1];
+    b[r] = (1.0f - al[r + 1]) * b[r + 1];
+    w[r] = b[r] + et[r + 1] * w[r + 1];
+  }
+  const float PCa = sca[z * 3 + 0], betaa = sca[z * 3 + 1], aSa = sca[z * 3 + 2];
+  for (int r = 0; r < C; ++r) {
+    const float cw = cWa[(int64_t)z * C + r], cs = cSa[(int64_t)z * C + r];
+    oth[r] = cs * e[r] + cw * w[r];
+    ea[r] = cs * th[r];
+    wa[r] = cw * th[r];
+    ba[r] = 0.0f;
+    oet[r] = 0.0f;
+    oal[r] = 0.0f;
+  }
+  oet[0] += PCa * e[0] + aSa * w[0];
+  ea[0] += PCa * et[0];
+  wa[0] += aSa * et[0];
+  oal[0] += -betaa * b[0];
+  ba[0] += betaa * (1.0f - al[0]);
+  for (int r = 0; r + 1 < C; ++r) {
+    ba[r] += wa[r];
+    oet[r + 1] += wa[r] * w[r + 1] + ea[r] * e[r + 1];
+    wa[r + 1] += wa[r] * et[r + 1];
+    ea[r + 1] += ea[r] * et[r + 1];
+    oal[r + 1] += -ba[r] * b[r + 1];
+    ba[r + 1] += ba[r] * (1.0f - al[r + 1]);
+  }
+}
+
+// WA <- beta WA + Wb, SA <- aS WA + PC SA (per memory scalars sc = (PC, beta, aS)), into the other
+// buffers of the ping-pong pair.
+__global__ void state_adj_kernel(const float* __restrict__ WA, const float* __restrict__ SA,
+                                 const float* __restrict__ Wb, const float* __restrict__ sc, int64_t P, int M,
+                                 float* __restrict__ WAn, float* __restrict__ SAn) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * P) return;
+  const int64_t z = i / P;
+  const float pc = sc[z * 3 + 0], beta = sc[z * 3 + 1], aS = sc[z * 3 + 2];
+  const float wa = WA[i];
+  WAn[i] = beta * wa + Wb[i];
+  SAn[i] = aS * wa + pc * SA[i];
+}
+
+}  // namespace bk
+
+// ---------------------------------------------------------------------------- host
+
+struct BwdLayout {
+  int64_t ck, wa0, wa1, sa0, sa1, wb, zk, e, pz, d1, u1, u1s, u2, u2s, zqa, cw, cs, cwa, csa, sc, sca, end;
+};
+
+static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
+  const int64_t M = d.M, C = d.C, P = d.P, dh = d.dh, dv = d.dv;
+  BwdLayout L;
+  int64_t o = 0;
+  auto take = [&](int64_t floats) {
+    const int64_t r = o;
+    o += (floats + 63) / 64 * 64;
+    return r;
+  };
+  L.ck = take(nchunks * M * 2 * P);
+  L.wa0 = take(M * P);
+  L.wa1 = take(M * P);
+  L.sa0 = take(M * P);
+  L.sa1 = take(M * P);
+  L.wb = take(M * P);
+  L.zk = take(M * 2 * C * dh);
+  L.e = take(M * C * dv);
+  L.pz = take(M * C * dh);
+  L.d1 = take(M * C * dh);
+  L.u1 = take(M * C * dh);
+  L.u1s = take(M * C * dh);
+  L.u2 = take(M * C * dv);
+  L.u2s = take(M * C * dv);
+  L.zqa = take(M * C * dh);
+  L.cw = take(M * C);
+  L.cs = take(M * C);
+  L.cwa = take(M * C);
+  L.csa = take(M * C);
+  L.sc = take(M * 3);
+  L.sca = take(M * 3);
+  L.end = o;
+  return L;
+}
+
+bool backward_supported(const Dims& d) {
+  return d.kind == ATLASMEM_MLP2_SILU && !d.residual && !d.gated && !d.ptr && d.gate_mode == ATLASMEM_PER_TOKEN &&
+         d.c == 1 && d.poly == 1 && d.ns_steps == 0;
+}
+
+int64_t backward_workspace_bytes(const Dims& d, int64_t T) {
+  if (T % d.C != 0) return -1;
+  return bwd_layout(d, T / d.C).end * (int64_t)sizeof(float);
+}
+
+atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V, const float* theta, const float* eta,
+                         const float* alpha, int64_t T, void* Y, const float* dY, const float* dWT, const float* dST,
+                         void* workspace, float* dK, float* dQ, float* dV, float* dth, float* det, float* dal,
+                         float* dW0, float* dS0, hipStream_t st) {
+  const Dims& d = h->d;
+  const int M = d.M, C = d.C, dh = d.dh, dv = d.dv, din = d.din;
+  const int64_t P = d.P, P1 = d.P1;
+  const int64_t nch = T / C;
+  const int bf = d.in_bf16;
+  const size_t esz = bf ? 2 : 4;
+  const BwdLayout L = bwd_layout(d, nch);
+  float* ws = (float*)workspace;
+  // ---- forward, saving the state at every chunk start
+  for (int64_t k = 0; k < nch; ++k) {
+    float* ck = ws + L.ck + k * M * 2 * P;
+    if (hipMemcpy2DAsync(ck, 2 * P * sizeof(float), h->W[h->cur], P * sizeof(float), P * sizeof(float), M,
+                         hipMemcpyDeviceToDevice, st) != hipSuccess ||
+        hipMemcpy2DAsync(ck + P, 2 * P * sizeof(float), h->S[h->cur], P * sizeof(float), P * sizeof(float), M,
+                         hipMemcpyDeviceToDevice, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return ATLASMEM_E_DEVICE;
+    }
+    const int64_t s = k * C;
+    const atlasmem_status stt =
+        mlp_update(h, d, (const char*)K + s * d.dk * esz, (const char*)Q + s * d.dk * esz,
+                   (const char*)V + s * dv * esz, theta + s, eta + s, alpha + s, nullptr, Span{C, T, T},
+                   Y ? (void*)((char*)Y + s * dv * (d.out_bf16 ? 2 : 4)) : nullptr, st);
+    if (stt != ATLASMEM_OK) return stt;
+  }
+  // ---- adjoints of the final state
+  float* WA = ws + L.wa0;
+  float* SA = ws + L.sa0;
+  float* WAn = ws + L.wa1;
+  float* SAn = ws + L.sa1;
+  const size_t pbytes = sizeof(float) * M * P;
+  bool ok = (dWT ? hipMemcpyAsync(WA, dWT, pbytes, hipMemcpyDeviceToDevice, st) : hipMemsetAsync(WA, 0, pbytes, st)) ==
+                hipSuccess &&
+            (dST ? hipMemcpyAsync(SA, dST, pbytes, hipMemcpyDeviceToDevice, st) : hipMemsetAsync(SA, 0, pbytes, st)) ==
+                hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    return ATLASMEM_E_DEVICE;
+  }
+  float *Zk = ws + L.zk, *E = ws + L.e, *Pz = ws + L.pz, *D1 = ws + L.d1, *U1 = ws + L.u1, *U1s = ws + L.u1s;
+  float *U2 = ws + L.u2, *U2s = ws + L.u2s, *Zqa = ws + L.zqa, *Wb = ws + L.wb;
+  float *cW = ws + L.cw, *cS = ws + L.cs, *cWa = ws + L.cwa, *cSa = ws + L.csa, *sc = ws + L.sc, *sca = ws + L.sca;
+  const int64_t zz = 2 * (int64_t)C * dh, hz = (int64_t)C * dh, vz = (int64_t)C * dv;
+  const int64_t inz = T * d.dk;  // input elements per memory (K, Q)
+  for (int64_t k = nch - 1; k >= 0; --k) {
+    const int64_t s = k * C;
+    const float* ck = ws + L.ck + k * M * 2 * P;  // [M][W | S]
+    const float* cW1 = ck;
+    const float* cW2 = ck + P1;
+    const char* Kc = (const char*)K + s * d.dk * esz;
+    const char* Qc = (const char*)Q + s * d.dk * esz;
+    atlasmem_status stt = launch_gate_scan(theta, eta, alpha, M, T, s, 1, C, cW, cS, C, sc, 3, st);
+    if (stt != ATLASMEM_OK) return stt;
+    // Z of key and query rows
+    {  // rows [0, C) keys, [C, 2C) queries (two launches into the two halves)
+      bk::Cat lk = bk::cat1(bk::src(Kc, bf, inz, din, 1, C, din));
+      bk::Cat lq = bk::cat1(bk::src(Qc, bf, inz, din, 1, C, din));
+      bk::Cat lb = bk::cat1(bk::src(cW1, 0, 2 * P, din, 1, dh, din));
+      launch_gemm<false, false>(true, C, dh, din, M, lk, lb, bk::EpiSt{Zk, zz, dh}, st);
+      launch_gemm<false, false>(true, C, dh, din, M, lq, lb, bk::EpiSt{Zk + (int64_t)C * dh, zz, dh}, st);
+    }
+    // E = 2 (H W2^T - V)
+    {
+      bk::Cat la = bk::cat1(bk::src(Zk, 0, zz, dh, 1, C, dh, 1));
+      bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh));
+      launch_gemm<false, false>(true, C, dv, dh, M, la, lb,
+                                bk::EpiE{E, vz, (const char*)V + s * dv * esz, bf, T * dv, dv}, st);
+    }
+    // P = E W2, D1 = P silu'(Z)
+    {
+      bk::Cat la = bk::cat1(bk::src(E, 0, vz, dv, 1, C, dv));
+      bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv));  // B(k=v, j=h) = W2[v][h]
+      launch_gemm<false, false>(true, C, dh, dv, M, la, lb, bk::EpiPD1{Pz, D1, Zk, hz, zz, dh}, st);
+    }
+    // U1 = X WA1^T, U1s = X SA1^T, U2 = H WA2^T, U2s = H SA2^T
+    {
+      bk::Cat lx = bk::cat1(bk::src(Kc, bf, inz, din, 1, C, din));
+      bk::Cat lh = bk::cat1(bk::src(Zk, 0, zz, dh, 1, C, dh, 1));
+      launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(WA, 0, P, din, 1, dh, din)),
+                                bk::EpiSt{U1, hz, dh}, st);
+      launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(SA, 0, P, din, 1, dh, din)),
+                                bk::EpiSt{U1s, hz, dh}, st);
+      launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(WA + P1, 0, P, dh, 1, dv, dh)),
+                                bk::EpiSt{U2, vz, dv}, st);
+      launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(SA + P1, 0, P, dh, 1, dv, dh)),
+                                bk::EpiSt{U2s, vz, dv}, st);
+    }
+    hipLaunchKernelGGL(bk::row_kernel, dim3(C, M), dim3(64), 0, st, Zk, zz, Pz, D1, U1, U1s, E, U2, U2s, hz, vz, dh,
+                       dv, C, cW, cS, cWa, cSa);
+    AM_LAUNCH_CHECK();
+    // now: U1s = P', Pz = Z'_1, U2 = E'_g.  E' = E'_g + P' W2^T (in U2), dV = -2 E'
+    {
+      bk::Cat la = bk::cat1(bk::src(U1s, 0, hz, dh, 1, C, dh));
+      bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh));  // B(k=h, j=v) = W2[v][h]
+      launch_gemm<false, false>(true, C, dv, dh, M, la, lb, bk::EpiEa{U2, vz, dV + s * dv, T * dv, dv}, st);
+    }
+    // W2' = E^T P' + (2E')^T H + dY^T Hq  -> Wb + P1   (A(i=v, k=row), B(k=row, j=h))
+    {
+      bk::Cat la = bk::cat3(bk::src(E, 0, vz, 1, dv, dv, C), bk::src(U2, 0, vz, 1, dv, dv, C, 0, nullptr, 0, 2.0f),
+                            bk::src(dY + s * dv, 0, T * dv, 1, dv, dv, C), C, 2 * C);
+      bk::Cat lb = bk::cat3(bk::src(U1s, 0, hz, 1, dh, dh, C), bk::src(Zk, 0, zz, 1, dh, dh, C, 1),
+                            bk::src(Zk + (int64_t)C * dh, 0, zz, 1, dh, dh, C, 1), C, 2 * C);
+      launch_gemm<false, false>(true, dv, dh, 3 * C, M, la, lb, bk::EpiSt{Wb + P1, P, dh}, st);
+    }
+    // H' = -(cW E) WA2 - (cS E) SA2 + (2E') W2;  Z' = Z'_1 + H' silu'(Z)  (in Pz)
+    {
+      bk::Cat la = bk::cat3(bk::src(E, 0, vz, dv, 1, C, dv, 2, cW, C, -1.0f),
+                            bk::src(E, 0, vz, dv, 1, C, dv, 2, cS, C, -1.0f),
+                            bk::src(U2, 0, vz, dv, 1, C, dv, 0, nullptr, 0, 2.0f), dv, 2 * dv);
+      bk::Cat lb = bk::cat3(bk::src(WA + P1, 0, P, 1, dh, dh, dv), bk::src(SA + P1, 0, P, 1, dh, dh, dv),
+                            bk::src(cW2, 0, 2 * P, 1, dh, dh, dv), dv, 2 * dv);  // B(k=v, j=h) = M[v][h]
+      launch_gemm<false, false>(true, C, dh, 3 * dv, M, la, lb, bk::EpiZa{Pz, Zk, hz, zz, dh}, st);
+    }
+    // X' = -(cW D1) WA1 - (cS D1) SA1 + Z' W1 -> dK rows
+    {
+      bk::Cat la = bk::cat3(bk::src(D1, 0, hz, dh, 1, C, dh, 2, cW, C, -1.0f),
+                            bk::src(D1, 0, hz, dh, 1, C, dh, 2, cS, C, -1.0f), bk::src(Pz, 0, hz, dh, 1, C, dh), dh,
+                            2 * dh);
+      bk::Cat lb = bk::cat3(bk::src(WA, 0, P, 1, din, din, dh), bk::src(SA, 0, P, 1, din, din, dh),
+                            bk::src(cW1, 0, 2 * P, 1, din, din, dh), dh, 2 * dh);  // B(k=h, j=f) = M[h][f]
+      launch_gemm<false, false>(true, C, din, 3 * dh, M, la, lb, bk::EpiSt{dK + s * din, T * din, din}, st);
+    }
+    // Zq' = (dY W2) silu'(Zq); Q' = Zq' W1 -> dQ rows
+    {
+      bk::Cat la = bk::cat1(bk::src(dY + s * dv, 0, T * dv, dv, 1, C, dv));
+      bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv));
+      launch_gemm<false, false>(true, C, dh, dv, M, la, lb, bk::EpiScaleSp{Zqa, Zk, hz, zz, C, dh}, st);
+      bk::Cat la2 = bk::cat1(bk::src(Zqa, 0, hz, dh, 1, C, dh));
+      bk::Cat lb2 = bk::cat1(bk::src(cW1, 0, 2 * P, 1, din, din, dh));
+      launch_gemm<false, false>(true, C, din, dh, M, la2, lb2, bk::EpiSt{dQ + s * din, T * din, din}, st);
+    }
+    // W1' = Z'^T X + Zq'^T Q -> Wb   (A(i=h, k=row), B(k=row, j=f))
+    {
+      bk::Cat la = bk::cat2(bk::src(Pz, 0, hz, 1, dh, dh, C), bk::src(Zqa, 0, hz, 1, dh, dh, C), C);
+      bk::Cat lb = bk::cat2(bk::src(Kc, bf, inz, 1, din, din, C), bk::src(Qc, bf, inz, 1, din, din, C), C);
+      launch_gemm<false, false>(true, dh, din, 2 * C, M, la, lb, bk::EpiSt{Wb, P, din}, st);
+    }
+    AM_LAUNCH_CHECK();
+    hipLaunchKernelGGL(bk::scalar_adj_kernel, dim3(M), dim3(256), 0, st, WA, SA, ck, P, sca);
+    AM_LAUNCH_CHECK();
+    hipLaunchKernelGGL(bk::gate_bwd_kernel, dim3(M), dim3(64), (size_t)6 * C * sizeof(float), st, theta, eta, alpha,
+                       T, s, C, cWa, cSa, sca, dth, det, dal);
+    AM_LAUNCH_CHECK();
+    const int64_t n = (int64_t)M * P;
+    hipLaunchKernelGGL(bk::state_adj_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, WA, SA, Wb, sc, P,
+                       M, WAn, SAn);
+    AM_LAUNCH_CHECK();
+    float* t;
+    t = WA, WA = WAn, WAn = t;
+    t = SA, SA = SAn, SAn = t;
+  }
+  if (hipMemcpyAsync(dW0, WA, pbytes, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+      hipMemcpyAsync(dS0, SA, pbytes, hipMemcpyDeviceToDevice, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return ATLASMEM_E_DEVICE;
+  }
+  return ATLASMEM_OK;
+}
+
+}  // namespace am

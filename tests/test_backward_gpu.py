@@ -1,0 +1,113 @@
+"""GPU parity of the outer-loop backward against the fp64 autograd oracle, through the C ABI.
+
+Every gradient group (keys, queries, values, the three gates, initial weights and momentum) is
+compared per tensor as max |x - r| / max |r| over all memories, against the 2e-2 bar of the
+bf16-input workloads (the products run in split bf16 with fp32 accumulation, the forward's
+checkpoints in fp32)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import backward as bw
+from helpers import BF16_TOL, DEV, config_for, log, maxrel, to_dev
+from test_learned_neural_amd import atlasmem as am
+from test_learned_neural_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (name, workload, variant, overrides)
+    ("mlp64x128_C64_two_chunks", 1, "stabilised", dict(batch=1, heads=2, T=128)),
+    ("ragged_widths_C16", 1, "stabilised", dict(batch=2, heads=1, T=48, d_key=24, d_value=20, d_hidden=36, chunk=16)),
+    ("fp32_inputs_C8", 1, "stabilised", dict(batch=1, heads=2, T=32, d_key=12, d_value=10, d_hidden=20, chunk=8,
+                                             input_dtype=synth.F32)),
+]
+
+
+def to_f64(a, dtype):
+    return synth.bf16_bits_to_f32(a).astype(np.float64) if dtype == synth.BF16 else a.astype(np.float64)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_autograd_oracle(case):
+    import torch
+    name, idx, variant, ov = case
+    log(f"CASE backward {name}")
+    inp = synth.make_inputs(idx, variant, **ov)
+    s = inp.spec
+    M, T = s.n_mem, s.T
+    r = np.random.default_rng(21)
+    dY = r.standard_normal((M, T, s.d_value)).astype(np.float32)
+    dWT = (0.1 * r.standard_normal((M, s.param_count))).astype(np.float32)
+    dST = (0.1 * r.standard_normal((M, s.param_count))).astype(np.float32)
+    mem = am.Memory(config_for(s), to_dev(inp.W0), to_dev(inp.S0))
+    ws = torch.empty(mem.backward_workspace_bytes(T), dtype=torch.uint8, device=DEV)
+    z = lambda *shape: torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+    dK, dQ, dV = z(M, T, s.d_key), z(M, T, s.d_key), z(M, T, s.d_value)
+    dth, det, dal = z(M, T), z(M, T), z(M, T)
+    dW0, dS0 = z(M, mem.P), z(M, mem.P)
+    Y = z(M, T, s.d_value)
+    mem.update_backward(to_dev(inp.K), to_dev(inp.Q), to_dev(inp.V), to_dev(inp.theta), to_dev(inp.eta),
+                        to_dev(inp.alpha), T, to_dev(dY), dK, dQ, dV, dth, det, dal, dW0, dS0, ws, Y=Y,
+                        dW_T=to_dev(dWT), dS_T=to_dev(dST))
+    W = torch.empty((M, mem.P), dtype=torch.float32, device=DEV)
+    S = torch.empty_like(W)
+    status = mem.get_state(W, S)
+    torch.cuda.synchronize()
+    mem.close()
+    assert status == am.OK
+    cfg = oracle.config_from(s)
+    K, Q, V = to_f64(inp.K, s.input_dtype), to_f64(inp.Q, s.input_dtype), to_f64(inp.V, s.input_dtype)
+    errs = {}
+    got = dict(K=dK, Q=dQ, V=dV, theta=dth, eta=det, alpha=dal)
+    ref = {k: [] for k in got}
+    ref["W0"], ref["S0"] = [], []
+    ys, wts = [], []
+    for m in range(M):
+        P0 = oracle.unflatten(cfg, inp.W0[m].astype(np.float64))
+        S0m = oracle.unflatten(cfg, inp.S0[m].astype(np.float64))
+        g = bw.outer_grads(cfg, P0, S0m, K[m], Q[m], V[m], inp.theta[m], inp.eta[m], inp.alpha[m], dY[m],
+                           oracle.unflatten(cfg, dWT[m].astype(np.float64)),
+                           oracle.unflatten(cfg, dST[m].astype(np.float64)))
+        for k in got:
+            ref[k].append(g[k])
+        ref["W0"].append(oracle.flatten(g["W0"]))
+        ref["S0"].append(oracle.flatten(g["S0"]))
+        res = oracle.run_memory(cfg, P0, S0m, K[m], Q[m], V[m], inp.theta[m], inp.eta[m], inp.alpha[m])
+        ys.append(res.Y)
+        wts.append(oracle.flatten(res.params))
+    for k, t in got.items():
+        errs[k] = maxrel(t.cpu().numpy(), np.stack(ref[k]))
+    errs["W0"] = maxrel(dW0.cpu().numpy(), np.stack(ref["W0"]))
+    errs["S0"] = maxrel(dS0.cpu().numpy(), np.stack(ref["S0"]))
+    errs["Y"] = maxrel(Y.cpu().numpy(), np.stack(ys))
+    errs["W_T"] = maxrel(W.cpu().numpy(), np.stack(wts))
+    label = lambda k: k if k in ("Y", "W_T") else "d" + k  # forward outputs, then gradients
+    log(f"PARITY backward_{name}: " + " ".join(f"{label(k)}={v:.3e}" for k, v in errs.items()) + f" (tol {BF16_TOL:g})")
+    assert all(v <= BF16_TOL for v in errs.values()), errs
+
+
+def test_backward_errors():
+    import torch
+    s4 = synth.spec(4, "literal", batch=1, heads=1, T=256)
+    mem = am.Memory(config_for(s4))
+    assert mem.backward_workspace_bytes(256) == -1
+    mem.close()
+    s = synth.spec(1, "stabilised", batch=1, heads=1, T=64)
+    mem = am.Memory(config_for(s))
+    need = mem.backward_workspace_bytes(64)
+    assert need > 0
+    small = torch.empty(need - 4, dtype=torch.uint8, device=DEV)
+    x = torch.zeros((1, 64, 64), dtype=torch.float32, device=DEV)
+    g = torch.zeros((1, 64), dtype=torch.float32, device=DEV)
+    p = torch.zeros((1, mem.P), dtype=torch.float32, device=DEV)
+    xb = torch.zeros((1, 64, 64), dtype=torch.int16, device=DEV)
+    with pytest.raises(am.AtlasMemError) as e:
+        mem.update_backward(xb, xb, xb, g, g, g, 64, x, x, x, x, g, g, g, p, p, small)
+    assert e.value.status == am.E_INVALID
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    with pytest.raises(am.AtlasMemError) as e:
+        mem.update_backward(xb, xb, xb, g, g, g, 40, x, x, x, x, g, g, g, p, p, ws)
+    assert e.value.status == am.E_SHAPE
+    mem.close()
