@@ -93,6 +93,18 @@ def event_ms(fn, iters, stream):
     return start.elapsed_time(end) / iters
 
 
+def _cfg(am, s, precision=0):
+    return am.make_config(kind=s.kind, batch=s.batch, heads=s.heads, d_key=s.d_key, d_value=s.d_value,
+                          d_hidden=s.d_hidden, poly_degree=s.poly_degree, chunk=s.chunk, omega_window=s.omega_window,
+                          gate_mode=s.gate_mode, ns_steps=s.ns_steps, input_dtype=s.input_dtype, precision=precision)
+
+
+def _dev(torch, a, dev):
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
 def stage_rooflines(torch, am, synth, dev, stream):
     """Stand-alone stages, each against its own roofline: the gate scan, Omega coefficients and
     feature map against HBM bandwidth (algorithmic bytes), Newton-Schulz against the bf16 matrix
@@ -103,7 +115,8 @@ def stage_rooflines(torch, am, synth, dev, stream):
     the Newton-Schulz workload's shape: the keys' short convolution (128 memories x 32768 tokens x
     64, bf16 in and out, L2-normalised) and the gates of 8 x 32768 token inputs of width 512 for 16
     heads (per token: theta, eta, alpha, gamma; per chunk of 128: theta, eta, alpha); the feature map
-    stage (degree 3 of 16384 width-32 vectors, and degree 2 of the 262144 keys projected to 64)."""
+    stage (degree 3 of 16384 width-32 vectors, and degree 2 of the 262144 keys projected to 64); the
+    outer-loop backward (with its recorded forward) of the 64 -> 128 -> 64 per-token workload."""
     out = {}
     M, T, C, c, d = 256, 32768, 64, 4, 32
     th = torch.rand((M, T), device=dev)
@@ -142,6 +155,28 @@ def stage_rooflines(torch, am, synth, dev, stream):
     FDO = 64
     Pproj = torch.randn((FDO, F.shape[1]), device=dev) / F.shape[1] ** 0.5
     Fproj = torch.empty((NP, FDO), device=dev)
+    # outer-loop backward at the 64 -> 128 -> 64 per-token workload's size (forward included)
+    bi = synth.make_inputs(1, "stabilised")
+    bs = bi.spec
+    bmem = am.Memory(_cfg(am, bs), torch.from_numpy(bi.W0).to(dev), torch.from_numpy(bi.S0).to(dev))
+    bdev = {k: _dev(torch, getattr(bi, k), dev) for k in ("K", "Q", "V", "theta", "eta", "alpha")}
+    BT, BM = bs.T, bs.n_mem
+    bws = torch.empty(bmem.backward_workspace_bytes(BT), dtype=torch.uint8, device=dev)
+    bz = lambda *shape: torch.zeros(shape, dtype=torch.float32, device=dev)
+    bout = dict(dK=bz(BM, BT, bs.d_key), dQ=bz(BM, BT, bs.d_key), dV=bz(BM, BT, bs.d_value), dth=bz(BM, BT),
+                det=bz(BM, BT), dal=bz(BM, BT), dW0=bz(BM, bmem.P), dS0=bz(BM, bmem.P))
+    bdY = torch.randn((BM, BT, bs.d_value), device=dev)
+    W0d, S0d = torch.from_numpy(bi.W0).to(dev), torch.from_numpy(bi.S0).to(dev)
+
+    def backward_call():
+        bmem.set_state(W0d, S0d)
+        bmem.update_backward(bdev["K"], bdev["Q"], bdev["V"], bdev["theta"], bdev["eta"], bdev["alpha"], BT, bdY,
+                             bout["dK"], bout["dQ"], bout["dV"], bout["dth"], bout["det"], bout["dal"], bout["dW0"],
+                             bout["dS0"], bws)
+    # algorithmic FLOPs per token: the recorded forward and the backward's products (chunk 64,
+    # 64 -> 128 -> 64): recomputed Z (keys and queries), E, P, the four adjoint projections, E',
+    # W2', H', X', Zq', Q' and W1'
+    bflops_tok = 147456 + 360448
     cases = [
         ("gate_scan", lambda: am.gate_scan(th, et, al, M, T, C, cW, cS, sc),
          M * T * (12 + 8) + M * (T // C) * 12, "hbm", f"{M} memories x {T} tokens, chunk {C}"),
@@ -163,6 +198,8 @@ def stage_rooflines(torch, am, synth, dev, stream):
          FN3 * (2 * FD + 4 * F3), "hbm", f"{FN3} bf16 vectors of width {FD} -> {F3} fp32 (degree 3)"),
         ("feature_project_deg2", lambda: am.feature_map(X, synth.BF16, NP, d, 2, Fproj, P=Pproj, d_out=FDO),
          2 * NP * F.shape[1] * FDO, "mfma", f"{NP} bf16 vectors of width {d}: degree-2 features x {FDO}-row projection"),
+        ("outer_backward", backward_call, BM * BT * bflops_tok, "mfma",
+         f"{bs.name} stabilised: forward with checkpoints and backward, {BM} memories x {BT} tokens"),
     ]
     for name, fn, work, bound, shape in cases:
         for _ in range(3):
