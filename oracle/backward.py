@@ -50,10 +50,24 @@ def _grad(params, x, v):
     return [torch.outer((w2.T @ e) * sp, x), torch.outer(e, h)]
 
 
+def _newton_schulz(g, steps, coeffs, eps):
+    """The quintic iteration of the oracle's newton_schulz, with torch operations."""
+    a, b, c = coeffs
+    x = g / (torch.linalg.norm(g) + eps)
+    tr = x.shape[0] > x.shape[1]
+    if tr:
+        x = x.T
+    for _ in range(steps):
+        A = x @ x.T
+        x = a * x + (b * A + c * (A @ A)) @ x
+    return x.T if tr else x
+
+
 def run_memory_torch(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha):
-    """The literal chunked recurrence for one memory (per-token gates, window 1, identity
-    features) with torch tensors: Y, final params, final momenta."""
-    assert cfg.gate_mode == PER_TOKEN and cfg.omega_window == 1 and cfg.poly_degree == 1
+    """The literal chunked recurrence for one memory (window 1, identity features; per-token
+    gates, or per-chunk gates with an optional Newton-Schulz orthogonalisation of the summed
+    chunk gradient) with torch tensors: Y, final params, final momenta."""
+    assert cfg.omega_window == 1 and cfg.poly_degree == 1
     W = list(params)
     S = list(momenta)
     T = K.shape[0]
@@ -64,10 +78,20 @@ def run_memory_torch(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, al
         wb = list(W)
         for t in range(s, e):
             Y.append(_apply(wb, Q[t]))
-        for t in range(s, e):
-            G = _grad(wb, K[t], V[t])
-            S = [eta[t] * S[m] - theta[t] * G[m] for m in range(len(W))]
-            W = [(1.0 - alpha[t]) * W[m] + S[m] for m in range(len(W))]
+        if cfg.gate_mode == PER_TOKEN:
+            for t in range(s, e):
+                G = _grad(wb, K[t], V[t])
+                S = [eta[t] * S[m] - theta[t] * G[m] for m in range(len(W))]
+                W = [(1.0 - alpha[t]) * W[m] + S[m] for m in range(len(W))]
+        else:
+            G = [torch.zeros_like(w) for w in W]
+            for t in range(s, e):
+                G = [G[m] + g for m, g in enumerate(_grad(wb, K[t], V[t]))]
+            if cfg.ns_steps > 0:
+                G = [_newton_schulz(g, cfg.ns_steps, cfg.ns_coeffs, cfg.ns_eps) for g in G]
+            k = s // C
+            S = [eta[k] * S[m] - theta[k] * G[m] for m in range(len(W))]
+            W = [(1.0 - alpha[k]) * W[m] + S[m] for m in range(len(W))]
     return torch.stack(Y), W, S
 
 

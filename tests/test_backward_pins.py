@@ -6,13 +6,13 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import LINEAR, MLP2_SILU, PER_TOKEN, MemoryConfig
+from oracle import LINEAR, MLP2_SILU, PER_CHUNK, PER_TOKEN, MemoryConfig
 from oracle import backward as bw
 
 
-def problem(seed, kind, T=8, C=4, d=3, v=2, h=5):
+def problem(seed, kind, T=8, C=4, d=3, v=2, h=5, mode=PER_TOKEN, ns=0):
     r = np.random.default_rng(seed)
-    cfg = MemoryConfig(kind, d, v, h if kind != LINEAR else 0, 1, C, 1, PER_TOKEN, 0)
+    cfg = MemoryConfig(kind, d, v, h if kind != LINEAR else 0, 1, C, 1, mode, ns)
     if kind == LINEAR:
         params = [r.normal(0, 0.5, (v, d))]
     else:
@@ -21,7 +21,8 @@ def problem(seed, kind, T=8, C=4, d=3, v=2, h=5):
     K = r.normal(0, 1, (T, d)) / np.sqrt(d)
     Q = r.normal(0, 1, (T, d)) / np.sqrt(d)
     V = r.normal(0, 1, (T, v))
-    th, et, al = r.uniform(0.01, 0.1, T), r.uniform(0.8, 0.99, T), r.uniform(0.0, 0.05, T)
+    ng = T if mode == PER_TOKEN else -(-T // C)
+    th, et, al = r.uniform(0.01, 0.1, ng), r.uniform(0.8, 0.99, ng), r.uniform(0.0, 0.05, ng)
     dY = r.normal(size=(T, v))
     dW = [r.normal(size=p.shape) for p in params]
     dS = [r.normal(size=p.shape) for p in params]
@@ -34,10 +35,14 @@ def objective(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS):
             + sum(np.sum(a * b) for a, b in zip(res.momenta, dS)))
 
 
-@pytest.mark.parametrize("kind", [LINEAR, MLP2_SILU])
-def test_torch_restatement_matches_oracle(kind):
+MODES = [(LINEAR, PER_TOKEN, 0), (MLP2_SILU, PER_TOKEN, 0), (MLP2_SILU, PER_CHUNK, 0), (MLP2_SILU, PER_CHUNK, 5),
+         (LINEAR, PER_CHUNK, 5)]
+
+
+@pytest.mark.parametrize("kind,mode,ns", MODES)
+def test_torch_restatement_matches_oracle(kind, mode, ns):
     import torch
-    cfg, params, momenta, K, Q, V, th, et, al, *_ = problem(1, kind, T=10, C=4)
+    cfg, params, momenta, K, Q, V, th, et, al, *_ = problem(1, kind, T=10, C=4, h=6, mode=mode, ns=ns)
     ref = oracle.run_memory(cfg, params, momenta, K, Q, V, th, et, al)
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
     Y, W, S = bw.run_memory_torch(cfg, [t(p) for p in params], [t(m) for m in momenta], t(K), t(Q), t(V), t(th),
@@ -49,12 +54,12 @@ def test_torch_restatement_matches_oracle(kind):
         np.testing.assert_allclose(a.numpy(), b, rtol=1e-13, atol=1e-14)
 
 
-@pytest.mark.parametrize("kind", [LINEAR, MLP2_SILU])
-def test_outer_gradients_against_finite_differences(kind):
+@pytest.mark.parametrize("kind,mode,ns", MODES)
+def test_outer_gradients_against_finite_differences(kind, mode, ns):
     """<grad, delta> against (L(x + h delta) - L(x - h delta)) / 2h with L from the numpy oracle,
     for a random direction in every input group (a wrong sign, index or dropped term in any
     group changes its directional derivative)."""
-    cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS = problem(2, kind, T=9, C=4)
+    cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS = problem(2, kind, T=9, C=4, h=6, mode=mode, ns=ns)
     g = bw.outer_grads(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS)
     r = np.random.default_rng(3)
     args = dict(params=params, momenta=momenta, K=K, Q=Q, V=V, th=th, et=et, al=al)
