@@ -1,7 +1,9 @@
 // Outer-loop backward of the chunked update: the gradients of an outer loss with respect to the
 // keys, queries, values, gates and initial state of the test-time update (Atlas-Torch README,
 // "How the memory works": the outer loop trains through the inner updates).  Scope: the 2-layer
-// SiLU memory with per-token gates, window 1 and identity features.
+// SiLU memory with window 1 and identity features; per-token gates, or per-chunk gates with the
+// optional Newton-Schulz orthogonalisation of the chunk gradient (differentiated through its
+// iterates, which the reverse step recomputes from the chunk-start checkpoint).
 //
 // Forward of chunk k from (W, S) = (W1, W2, S1, S2), rows r of the chunk (titans-pytorch-mlx
 // README, Eq. 12-14; gradients at the chunk-start weights, ATLAS summary, section 3.3):
@@ -157,6 +159,26 @@ struct EpiScaleSp {  // out = acc * silu'(Z[row + zr0])
   }
 };
 
+struct EpiAxpy {  // out = alpha * x + beta * acc (out may alias x: same element, same thread)
+  float* out;
+  const float* x;
+  int64_t sz;
+  int ld;
+  float alpha, beta;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    const int64_t o = (int64_t)z * sz + (int64_t)row * ld + col;
+    out[o] = alpha * (x ? x[o] : 0.0f) + beta * v;
+  }
+};
+struct EpiAcc {  // out += acc
+  float* out;
+  int64_t sz;
+  int ld;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    out[(int64_t)z * sz + (int64_t)row * ld + col] += v;
+  }
+};
+
 // ---------------------------------------------------------------------------- small kernels
 
 __device__ __forceinline__ float silu_second(float z) {
@@ -308,12 +330,140 @@ __global__ void state_adj_kernel(const float* __restrict__ WA, const float* __re
   SAn[i] = aS * wa + pc * SA[i];
 }
 
+// Fill n floats with v.
+__global__ void fill_kernel(float* __restrict__ p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Per-chunk gates: SAt = SA + WA (S_end also feeds W_end); per memory the gate adjoints
+// theta' = -<SAt, N>, eta' = <SAt, S0>, alpha' = -<WA, W0> at chunk k of the [M][ldg] gate arrays.
+__global__ void chunk_gate_adj_kernel(const float* __restrict__ WA, const float* __restrict__ SA,
+                                      const float* __restrict__ N, const float* __restrict__ ck, int64_t P,
+                                      float* __restrict__ SAt, int64_t ldg, int64_t k, float* __restrict__ dth,
+                                      float* __restrict__ det, float* __restrict__ dal) {
+  __shared__ float red[3][4];
+  const int z = blockIdx.x;
+  const float* w0 = ck + (int64_t)z * 2 * P;
+  const float* s0 = w0 + P;
+  const int64_t o = (int64_t)z * P;
+  float t = 0.0f, e = 0.0f, a = 0.0f;
+  for (int64_t i = threadIdx.x; i < P; i += blockDim.x) {
+    const float sat = SA[o + i] + WA[o + i];
+    SAt[o + i] = sat;
+    t += sat * N[o + i];
+    e += sat * s0[i];
+    a += WA[o + i] * w0[i];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    t += __shfl_xor(t, off, 64);
+    e += __shfl_xor(e, off, 64);
+    a += __shfl_xor(a, off, 64);
+  }
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wv] = t;
+    red[1][wv] = e;
+    red[2][wv] = a;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    dth[(int64_t)z * ldg + k] = -(red[0][0] + red[0][1] + red[0][2] + red[0][3]);
+    det[(int64_t)z * ldg + k] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    dal[(int64_t)z * ldg + k] = -(red[2][0] + red[2][1] + red[2][2] + red[2][3]);
+  }
+}
+
+// Per-chunk state carry: WA <- (1 - alpha_k) WA + Wb, SA <- eta_k SAt.
+__global__ void chunk_state_adj_kernel(const float* __restrict__ WA, const float* __restrict__ SAt,
+                                       const float* __restrict__ Wb, const float* __restrict__ eta,
+                                       const float* __restrict__ alpha, int64_t ldg, int64_t k, int64_t P, int M,
+                                       float* __restrict__ WAn, float* __restrict__ SAn) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * P) return;
+  const int64_t z = i / P;
+  const float om = 1.0f - alpha[z * ldg + k], et = eta[z * ldg + k];
+  WAn[i] = om * WA[i] + Wb[i];
+  SAn[i] = et * SAt[i];
+}
+
+// Per memory: <a, b> over n elements at a + z * za and b + z * zb (|G|_F^2 with a = b).
+__global__ void dot_kernel(const float* __restrict__ a, int64_t za, const float* __restrict__ b, int64_t zb, int64_t n,
+                           float* __restrict__ out) {
+  __shared__ float red[4];
+  const int z = blockIdx.x;
+  float acc = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) acc += a[(int64_t)z * za + i] * b[(int64_t)z * zb + i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[z] = red[0] + red[1] + red[2] + red[3];
+}
+
+// X0 = G / (|G| + eps), in the working orientation (transposed when rows > cols): out is
+// [M][r][c] with (r, c) = tr ? (cols, rows) : (rows, cols).
+__global__ void ns_init_kernel(const float* __restrict__ G, int64_t gz, int rows, int cols, int tr,
+                               const float* __restrict__ sq, float eps, float* __restrict__ X, int64_t xz, int M) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)rows * cols;
+  if (i >= (int64_t)M * n) return;
+  const int64_t z = i / n, e = i - z * n;
+  const int r = (int)(e / cols), c = (int)(e - (int64_t)r * cols);
+  const float inv = 1.0f / (sqrtf(sq[z]) + eps);
+  const float v = G[z * gz + e] * inv;
+  if (tr) X[z * xz + (int64_t)c * rows + r] = v;
+  else X[z * xz + e] = v;
+}
+
+// G' = Xa0 / n - (<Xa0, G> / n^2) G / |G|, Xa0 taken back to G's orientation; n = |G| + eps.
+// The same kernel copies a working-orientation matrix back to G's orientation when G is null.
+__global__ void ns_final_kernel(const float* __restrict__ Xa, int64_t xz, const float* __restrict__ G, int64_t gz,
+                                int rows, int cols, int tr, const float* __restrict__ sq,
+                                const float* __restrict__ dotv, float eps, float* __restrict__ Ga, int M) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)rows * cols;
+  if (i >= (int64_t)M * n) return;
+  const int64_t z = i / n, e = i - z * n;
+  const int r = (int)(e / cols), c = (int)(e - (int64_t)r * cols);
+  const float gn = sqrtf(sq[z]), nn = gn + eps;
+  const float xa = tr ? Xa[z * xz + (int64_t)c * rows + r] : Xa[z * xz + e];
+  const float corr = gn > 0.0f ? dotv[z] / (nn * gn) : 0.0f;  // dotv = <Xa0, X0> = <Xa0, G> / nn
+  Ga[z * gz + e] = G ? xa / nn - corr * G[z * gz + e] : xa;
+}
+
+// The other direction of the orientation change: out (working, [M][r][c]) from in (G's
+// orientation, [rows][cols]), times `scale` per memory (scale[z] * mul), or a plain copy.
+__global__ void to_work_kernel(const float* __restrict__ in, int64_t iz, int rows, int cols, int tr,
+                               const float* __restrict__ scale, int64_t sld, int64_t sk, float mul,
+                               float* __restrict__ out, int64_t oz, int M) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)rows * cols;
+  if (i >= (int64_t)M * n) return;
+  const int64_t z = i / n, e = i - z * n;
+  const int r = (int)(e / cols), c = (int)(e - (int64_t)r * cols);
+  const float f = scale ? scale[z * sld + sk] * mul : mul;
+  const float v = in[z * iz + e] * f;
+  if (tr) out[z * oz + (int64_t)c * rows + r] = v;
+  else out[z * oz + e] = v;
+}
+
 }  // namespace bk
 
 // ---------------------------------------------------------------------------- host
 
+struct NsLay {  // one matrix's Newton-Schulz buffers (working orientation r x c, r <= c)
+  int rows, cols, r, c, tr;
+  int64_t goff;  // offset of the matrix inside a memory's parameters
+  int64_t x, a, b, xa0, xa1, ba, aa, sq, dot;
+};
+
 struct BwdLayout {
-  int64_t ck, wa0, wa1, sa0, sa1, wb, zk, e, pz, d1, u1, u1s, u2, u2s, zqa, cw, cs, cwa, csa, sc, sca, end;
+  int64_t ck, wa0, wa1, sa0, sa1, wb, zk, e, pz, d1, u1, u1s, u2, u2s, zqa, cw, cs, cwa, csa, sc, sca;
+  int64_t gb, nb, nab, gab, sat;
+  NsLay ns[2];
+  int64_t end;
 };
 
 static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
@@ -346,13 +496,115 @@ static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
   L.csa = take(M * C);
   L.sc = take(M * 3);
   L.sca = take(M * 3);
+  L.gb = L.nb = L.nab = L.gab = L.sat = 0;
+  for (int m = 0; m < 2; ++m) L.ns[m] = NsLay{};
+  if (d.gate_mode == ATLASMEM_PER_CHUNK) {
+    L.gb = take(M * P);
+    L.nb = take(M * P);
+    L.nab = take(M * P);
+    L.gab = take(M * P);
+    L.sat = take(M * P);
+    if (d.ns_steps > 0) {
+      const int steps = d.ns_steps;
+      const int shp[2][2] = {{(int)dh, d.din}, {(int)dv, (int)dh}};
+      for (int m = 0; m < 2; ++m) {
+        NsLay& n = L.ns[m];
+        n.rows = shp[m][0];
+        n.cols = shp[m][1];
+        n.tr = n.rows > n.cols;
+        n.r = n.tr ? n.cols : n.rows;
+        n.c = n.tr ? n.rows : n.cols;
+        n.goff = m == 0 ? 0 : d.P1;
+        const int64_t rc = (int64_t)n.r * n.c, rr = (int64_t)n.r * n.r;
+        n.x = take(M * (steps + 1) * rc);
+        n.a = take(M * steps * rr);
+        n.b = take(M * steps * rr);
+        n.xa0 = take(M * rc);
+        n.xa1 = take(M * rc);
+        n.ba = take(M * rr);
+        n.aa = take(M * rr);
+        n.sq = take(M);
+        n.dot = take(M);
+      }
+    }
+  }
   L.end = o;
   return L;
 }
 
+static unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+// Newton-Schulz forward of one matrix of every memory, keeping its iterates: X_0 = G / (|G| + eps)
+// (working orientation), A_i = X_i X_i^T, B_i = b A_i + c A_i^2, X_{i+1} = a X_i + B_i X_i; the result
+// goes back to G's orientation in N (at the matrix's offset).
+static atlasmem_status ns_forward(const Dims& d, float* ws, const NsLay& n, const float* G, float* N, hipStream_t st) {
+  const int M = d.M, steps = d.ns_steps, r = n.r, c = n.c;
+  const int64_t P = d.P, rc = (int64_t)r * c, rr = (int64_t)r * r;
+  const int64_t xz = (steps + 1) * rc, az = steps * rr;
+  float *X = ws + n.x, *A = ws + n.a, *B = ws + n.b, *sq = ws + n.sq;
+  hipLaunchKernelGGL(bk::dot_kernel, dim3(M), dim3(256), 0, st, G + n.goff, P, G + n.goff, P,
+                     (int64_t)n.rows * n.cols, sq);
+  hipLaunchKernelGGL(bk::ns_init_kernel, dim3(blocks_of((int64_t)M * rc)), dim3(256), 0, st, G + n.goff, P, n.rows,
+                     n.cols, n.tr, sq, d.ns_eps, X, xz, M);
+  AM_LAUNCH_CHECK();
+  for (int i = 0; i < steps; ++i) {
+    float *Xi = X + i * rc, *Xn = X + (i + 1) * rc, *Ai = A + i * rr, *Bi = B + i * rr;
+    launch_gemm<false, false>(true, r, r, c, M, bk::cat1(bk::src(Xi, 0, xz, c, 1, r, c)),
+                              bk::cat1(bk::src(Xi, 0, xz, c, 1, r, c)), bk::EpiSt{Ai, az, r}, st);
+    launch_gemm<false, false>(true, r, r, r, M, bk::cat1(bk::src(Ai, 0, az, r, 1, r, r)),
+                              bk::cat1(bk::src(Ai, 0, az, 1, r, r, r)), bk::EpiAxpy{Bi, Ai, az, r, d.ns_b, d.ns_c},
+                              st);
+    launch_gemm<false, false>(true, r, c, r, M, bk::cat1(bk::src(Bi, 0, az, r, 1, r, r)),
+                              bk::cat1(bk::src(Xi, 0, xz, 1, c, c, r)), bk::EpiAxpy{Xn, Xi, xz, c, d.ns_a, 1.0f}, st);
+  }
+  hipLaunchKernelGGL(bk::ns_final_kernel, dim3(blocks_of((int64_t)M * rc)), dim3(256), 0, st, X + steps * rc, xz,
+                     (const float*)nullptr, P, n.rows, n.cols, n.tr, sq, sq, d.ns_eps, N + n.goff, M);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
+// Its reverse: from Na (the adjoint of N, G's orientation) to Ga (the adjoint of G):
+//   Ba = Xa X_i^T, Xa <- a Xa + B_i Xa + (Aa + Aa^T) X_i with Aa = b Ba + c (Ba A_i + A_i Ba),
+//   then G' = Xa0 / n - (<Xa0, G> / n^2) G / |G|.
+static atlasmem_status ns_backward(const Dims& d, float* ws, const NsLay& n, const float* G, const float* Na,
+                                   float* Ga, hipStream_t st) {
+  const int M = d.M, steps = d.ns_steps, r = n.r, c = n.c;
+  const int64_t P = d.P, rc = (int64_t)r * c, rr = (int64_t)r * r;
+  const int64_t xz = (steps + 1) * rc, az = steps * rr;
+  float *X = ws + n.x, *A = ws + n.a, *B = ws + n.b, *Ba = ws + n.ba, *Aa = ws + n.aa;
+  float* xa = ws + n.xa0;
+  float* xn = ws + n.xa1;
+  hipLaunchKernelGGL(bk::to_work_kernel, dim3(blocks_of((int64_t)M * rc)), dim3(256), 0, st, Na + n.goff, P, n.rows,
+                     n.cols, n.tr, (const float*)nullptr, (int64_t)0, (int64_t)0, 1.0f, xa, rc, M);
+  AM_LAUNCH_CHECK();
+  for (int i = steps - 1; i >= 0; --i) {
+    float *Xi = X + i * rc, *Ai = A + i * rr, *Bi = B + i * rr;
+    launch_gemm<false, false>(true, r, r, c, M, bk::cat1(bk::src(xa, 0, rc, c, 1, r, c)),
+                              bk::cat1(bk::src(Xi, 0, xz, c, 1, r, c)), bk::EpiSt{Ba, rr, r}, st);
+    launch_gemm<false, false>(true, r, c, r, M, bk::cat1(bk::src(Bi, 0, az, r, 1, r, r)),
+                              bk::cat1(bk::src(xa, 0, rc, 1, c, c, r)), bk::EpiAxpy{xn, xa, rc, c, d.ns_a, 1.0f}, st);
+    launch_gemm<false, false>(
+        true, r, r, 2 * r, M, bk::cat2(bk::src(Ba, 0, rr, r, 1, r, r), bk::src(Ai, 0, az, r, 1, r, r), r),
+        bk::cat2(bk::src(Ai, 0, az, 1, r, r, r), bk::src(Ba, 0, rr, 1, r, r, r), r),
+        bk::EpiAxpy{Aa, Ba, rr, r, d.ns_b, d.ns_c}, st);
+    launch_gemm<false, false>(
+        true, r, c, 2 * r, M, bk::cat2(bk::src(Aa, 0, rr, r, 1, r, r), bk::src(Aa, 0, rr, 1, r, r, r), r),
+        bk::cat2(bk::src(Xi, 0, xz, 1, c, c, r), bk::src(Xi, 0, xz, 1, c, c, r), r), bk::EpiAcc{xn, rc, c}, st);
+    float* t = xa;
+    xa = xn;
+    xn = t;
+  }
+  hipLaunchKernelGGL(bk::dot_kernel, dim3(M), dim3(256), 0, st, xa, rc, X, xz, rc, ws + n.dot);  // <Xa0, X_0>
+  AM_LAUNCH_CHECK();
+  hipLaunchKernelGGL(bk::ns_final_kernel, dim3(blocks_of((int64_t)M * rc)), dim3(256), 0, st, xa, rc, G + n.goff,
+                     P, n.rows, n.cols, n.tr, ws + n.sq, ws + n.dot, d.ns_eps, Ga + n.goff, M);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
 bool backward_supported(const Dims& d) {
-  return d.kind == ATLASMEM_MLP2_SILU && !d.residual && !d.gated && !d.ptr && d.gate_mode == ATLASMEM_PER_TOKEN &&
-         d.c == 1 && d.poly == 1 && d.ns_steps == 0;
+  return d.kind == ATLASMEM_MLP2_SILU && !d.residual && !d.gated && !d.ptr && d.c == 1 && d.poly == 1 &&
+         (d.gate_mode == ATLASMEM_PER_CHUNK || d.ns_steps == 0);
 }
 
 int64_t backward_workspace_bytes(const Dims& d, int64_t T) {
@@ -368,6 +620,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
   const int M = d.M, C = d.C, dh = d.dh, dv = d.dv, din = d.din;
   const int64_t P = d.P, P1 = d.P1;
   const int64_t nch = T / C;
+  const bool per_chunk = d.gate_mode == ATLASMEM_PER_CHUNK;
   const int bf = d.in_bf16;
   const size_t esz = bf ? 2 : 4;
   const BwdLayout L = bwd_layout(d, nch);
@@ -383,10 +636,12 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       return ATLASMEM_E_DEVICE;
     }
     const int64_t s = k * C;
+    const int64_t go = per_chunk ? k : s;  // this chunk's gates
     const atlasmem_status stt =
         mlp_update(h, d, (const char*)K + s * d.dk * esz, (const char*)Q + s * d.dk * esz,
-                   (const char*)V + s * dv * esz, theta + s, eta + s, alpha + s, nullptr, Span{C, T, T},
-                   Y ? (void*)((char*)Y + s * dv * (d.out_bf16 ? 2 : 4)) : nullptr, st);
+                   (const char*)V + s * dv * esz, theta + go, eta + go, alpha + go, nullptr,
+                   Span{C, T, per_chunk ? nch : T}, Y ? (void*)((char*)Y + s * dv * (d.out_bf16 ? 2 : 4)) : nullptr,
+                   st);
     if (stt != ATLASMEM_OK) return stt;
   }
   // ---- adjoints of the final state
@@ -415,8 +670,11 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     const float* cW2 = ck + P1;
     const char* Kc = (const char*)K + s * d.dk * esz;
     const char* Qc = (const char*)Q + s * d.dk * esz;
-    atlasmem_status stt = launch_gate_scan(theta, eta, alpha, M, T, s, 1, C, cW, cS, C, sc, 3, st);
-    if (stt != ATLASMEM_OK) return stt;
+    atlasmem_status stt = ATLASMEM_OK;
+    if (!per_chunk) {
+      stt = launch_gate_scan(theta, eta, alpha, M, T, s, 1, C, cW, cS, C, sc, 3, st);
+      if (stt != ATLASMEM_OK) return stt;
+    }
     // Z of key and query rows
     {  // rows [0, C) keys, [C, 2C) queries (two launches into the two halves)
       bk::Cat lk = bk::cat1(bk::src(Kc, bf, inz, din, 1, C, din));
@@ -438,17 +696,53 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv));  // B(k=v, j=h) = W2[v][h]
       launch_gemm<false, false>(true, C, dh, dv, M, la, lb, bk::EpiPD1{Pz, D1, Zk, hz, zz, dh}, st);
     }
+    // Per-chunk gates: G = (D1^T X, E^T H), N = NS(G) or G, S_end = eta S - theta N,
+    // W_end = (1 - alpha) W + S_end.  The adjoint of every row's gradient is G' (from N' = -theta
+    // (SA + WA) through the orthogonalisation), which the per-token products below take with
+    // cW = -1, cS = 0 in place of the state adjoints.
+    const float* WAg = WA;
+    const float* SAg = SA;
+    if (per_chunk) {
+      float *Gb = ws + L.gb, *Nb = ws + L.nb, *NAb = ws + L.nab, *GAb = ws + L.gab, *SAt = ws + L.sat;
+      launch_gemm<false, false>(true, dh, din, C, M, bk::cat1(bk::src(D1, 0, hz, 1, dh, dh, C)),
+                                bk::cat1(bk::src(Kc, bf, inz, 1, din, din, C)), bk::EpiSt{Gb, P, din}, st);
+      launch_gemm<false, false>(true, dv, dh, C, M, bk::cat1(bk::src(E, 0, vz, 1, dv, dv, C)),
+                                bk::cat1(bk::src(Zk, 0, zz, 1, dh, dh, C, 1)), bk::EpiSt{Gb + P1, P, dh}, st);
+      AM_LAUNCH_CHECK();
+      const float* N = Gb;
+      if (d.ns_steps > 0) {
+        for (int m = 0; m < 2; ++m)
+          if ((stt = ns_forward(d, ws, L.ns[m], Gb, Nb, st)) != ATLASMEM_OK) return stt;
+        N = Nb;
+      }
+      hipLaunchKernelGGL(bk::chunk_gate_adj_kernel, dim3(M), dim3(256), 0, st, WA, SA, N, ck, P, SAt, nch, k, dth,
+                         det, dal);
+      // N' = -theta_k SAt (G's orientation, whole parameter vector)
+      hipLaunchKernelGGL(bk::to_work_kernel, dim3(blocks_of((int64_t)M * P)), dim3(256), 0, st, SAt, P, 1, (int)P, 0,
+                         theta, nch, k, -1.0f, NAb, P, M);
+      AM_LAUNCH_CHECK();
+      if (d.ns_steps > 0) {
+        for (int m = 0; m < 2; ++m)
+          if ((stt = ns_backward(d, ws, L.ns[m], Gb, NAb, GAb, st)) != ATLASMEM_OK) return stt;
+        WAg = SAg = GAb;
+      } else {
+        WAg = SAg = NAb;
+      }
+      hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cW, (int64_t)M * C, -1.0f);
+      hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cS, (int64_t)M * C, 0.0f);
+      AM_LAUNCH_CHECK();
+    }
     // U1 = X WA1^T, U1s = X SA1^T, U2 = H WA2^T, U2s = H SA2^T
     {
       bk::Cat lx = bk::cat1(bk::src(Kc, bf, inz, din, 1, C, din));
       bk::Cat lh = bk::cat1(bk::src(Zk, 0, zz, dh, 1, C, dh, 1));
-      launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(WA, 0, P, din, 1, dh, din)),
+      launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(WAg, 0, P, din, 1, dh, din)),
                                 bk::EpiSt{U1, hz, dh}, st);
-      launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(SA, 0, P, din, 1, dh, din)),
+      launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(SAg, 0, P, din, 1, dh, din)),
                                 bk::EpiSt{U1s, hz, dh}, st);
-      launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(WA + P1, 0, P, dh, 1, dv, dh)),
+      launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(WAg + P1, 0, P, dh, 1, dv, dh)),
                                 bk::EpiSt{U2, vz, dv}, st);
-      launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(SA + P1, 0, P, dh, 1, dv, dh)),
+      launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(SAg + P1, 0, P, dh, 1, dv, dh)),
                                 bk::EpiSt{U2s, vz, dv}, st);
     }
     hipLaunchKernelGGL(bk::row_kernel, dim3(C, M), dim3(64), 0, st, Zk, zz, Pz, D1, U1, U1s, E, U2, U2s, hz, vz, dh,
@@ -473,7 +767,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat la = bk::cat3(bk::src(E, 0, vz, dv, 1, C, dv, 2, cW, C, -1.0f),
                             bk::src(E, 0, vz, dv, 1, C, dv, 2, cS, C, -1.0f),
                             bk::src(U2, 0, vz, dv, 1, C, dv, 0, nullptr, 0, 2.0f), dv, 2 * dv);
-      bk::Cat lb = bk::cat3(bk::src(WA + P1, 0, P, 1, dh, dh, dv), bk::src(SA + P1, 0, P, 1, dh, dh, dv),
+      bk::Cat lb = bk::cat3(bk::src(WAg + P1, 0, P, 1, dh, dh, dv), bk::src(SAg + P1, 0, P, 1, dh, dh, dv),
                             bk::src(cW2, 0, 2 * P, 1, dh, dh, dv), dv, 2 * dv);  // B(k=v, j=h) = M[v][h]
       launch_gemm<false, false>(true, C, dh, 3 * dv, M, la, lb, bk::EpiZa{Pz, Zk, hz, zz, dh}, st);
     }
@@ -482,7 +776,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat la = bk::cat3(bk::src(D1, 0, hz, dh, 1, C, dh, 2, cW, C, -1.0f),
                             bk::src(D1, 0, hz, dh, 1, C, dh, 2, cS, C, -1.0f), bk::src(Pz, 0, hz, dh, 1, C, dh), dh,
                             2 * dh);
-      bk::Cat lb = bk::cat3(bk::src(WA, 0, P, 1, din, din, dh), bk::src(SA, 0, P, 1, din, din, dh),
+      bk::Cat lb = bk::cat3(bk::src(WAg, 0, P, 1, din, din, dh), bk::src(SAg, 0, P, 1, din, din, dh),
                             bk::src(cW1, 0, 2 * P, 1, din, din, dh), dh, 2 * dh);  // B(k=h, j=f) = M[h][f]
       launch_gemm<false, false>(true, C, din, 3 * dh, M, la, lb, bk::EpiSt{dK + s * din, T * din, din}, st);
     }
@@ -502,15 +796,20 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       launch_gemm<false, false>(true, dh, din, 2 * C, M, la, lb, bk::EpiSt{Wb, P, din}, st);
     }
     AM_LAUNCH_CHECK();
-    hipLaunchKernelGGL(bk::scalar_adj_kernel, dim3(M), dim3(256), 0, st, WA, SA, ck, P, sca);
-    AM_LAUNCH_CHECK();
-    hipLaunchKernelGGL(bk::gate_bwd_kernel, dim3(M), dim3(64), (size_t)6 * C * sizeof(float), st, theta, eta, alpha,
-                       T, s, C, cWa, cSa, sca, dth, det, dal);
-    AM_LAUNCH_CHECK();
     const int64_t n = (int64_t)M * P;
-    hipLaunchKernelGGL(bk::state_adj_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, WA, SA, Wb, sc, P,
-                       M, WAn, SAn);
-    AM_LAUNCH_CHECK();
+    if (per_chunk) {
+      hipLaunchKernelGGL(bk::chunk_state_adj_kernel, dim3(blocks_of(n)), dim3(256), 0, st, WA, ws + L.sat, Wb, eta,
+                         alpha, nch, k, P, M, WAn, SAn);
+      AM_LAUNCH_CHECK();
+    } else {
+      hipLaunchKernelGGL(bk::scalar_adj_kernel, dim3(M), dim3(256), 0, st, WA, SA, ck, P, sca);
+      AM_LAUNCH_CHECK();
+      hipLaunchKernelGGL(bk::gate_bwd_kernel, dim3(M), dim3(64), (size_t)6 * C * sizeof(float), st, theta, eta,
+                         alpha, T, s, C, cWa, cSa, sca, dth, det, dal);
+      AM_LAUNCH_CHECK();
+      hipLaunchKernelGGL(bk::state_adj_kernel, dim3(blocks_of(n)), dim3(256), 0, st, WA, SA, Wb, sc, P, M, WAn, SAn);
+      AM_LAUNCH_CHECK();
+    }
     float* t;
     t = WA, WA = WAn, WAn = t;
     t = SA, SA = SAn, SAn = t;

@@ -22,6 +22,13 @@ CASES = [
     ("ragged_widths_C16", 1, "stabilised", dict(batch=2, heads=1, T=48, d_key=24, d_value=20, d_hidden=36, chunk=16)),
     ("fp32_inputs_C8", 1, "stabilised", dict(batch=1, heads=2, T=32, d_key=12, d_value=10, d_hidden=20, chunk=8,
                                              input_dtype=synth.F32)),
+    # per-chunk gates: the chunk gradient through 5 Newton-Schulz steps (W1 128 x 64 runs transposed)
+    ("ns5_per_chunk_C128", 4, "literal", dict(batch=1, heads=2, T=384)),
+    # both matrices transposed (rows > cols), ragged widths that span several 64-wide tiles
+    ("ns5_both_transposed", 4, "literal", dict(batch=1, heads=2, T=160, d_key=24, d_value=72, d_hidden=40, chunk=40)),
+    # neither transposed
+    ("ns5_none_transposed", 4, "literal", dict(batch=2, heads=1, T=96, d_key=56, d_value=20, d_hidden=36, chunk=32)),
+    ("per_chunk_no_ns", 4, "literal", dict(batch=2, heads=1, T=256, ns_steps=0)),
 ]
 
 
@@ -45,7 +52,8 @@ def test_backward_matches_autograd_oracle(case):
     ws = torch.empty(mem.backward_workspace_bytes(T), dtype=torch.uint8, device=DEV)
     z = lambda *shape: torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
     dK, dQ, dV = z(M, T, s.d_key), z(M, T, s.d_key), z(M, T, s.d_value)
-    dth, det, dal = z(M, T), z(M, T), z(M, T)
+    ng = inp.theta.shape[1]  # T per token, T / C per chunk
+    dth, det, dal = z(M, ng), z(M, ng), z(M, ng)
     dW0, dS0 = z(M, mem.P), z(M, mem.P)
     Y = z(M, T, s.d_value)
     mem.update_backward(to_dev(inp.K), to_dev(inp.Q), to_dev(inp.V), to_dev(inp.theta), to_dev(inp.eta),
@@ -90,10 +98,11 @@ def test_backward_matches_autograd_oracle(case):
 
 def test_backward_errors():
     import torch
-    s4 = synth.spec(4, "literal", batch=1, heads=1, T=256)
-    mem = am.Memory(config_for(s4))
-    assert mem.backward_workspace_bytes(256) == -1
-    mem.close()
+    for s3 in (synth.spec(3, "stabilised", batch=1, heads=1, T=256),  # window 4, polynomial features
+               synth.spec(1, "stabilised", batch=1, heads=1, T=256, kind=synth.MLP2_GATED)):
+        mem = am.Memory(config_for(s3))
+        assert mem.backward_workspace_bytes(256) == -1
+        mem.close()
     s = synth.spec(1, "stabilised", batch=1, heads=1, T=64)
     mem = am.Memory(config_for(s))
     need = mem.backward_workspace_bytes(64)
