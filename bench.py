@@ -52,6 +52,30 @@ def mlp_flops_per_chunk(spec) -> dict:
     return f
 
 
+def backward_flops_per_chunk(spec) -> int:
+    """Algorithmic FLOPs of one chunk of one memory in the outer-loop backward call (window 1,
+    identity features): the forward it records (as in mlp_flops_per_chunk) plus the reverse step's
+    products, which recompute the chunk's activations from its checkpoint: Z of keys and queries,
+    E, P, the adjoint projections (two per layer per token for per-token gates, one per layer for
+    per-chunk gates, whose gradient sum G and its Newton-Schulz iterates are recomputed too), E',
+    W2' (3C deep), H' and X' (3 or 2 terms), Zq', Q', W1' (2C deep), and the Newton-Schulz backward,
+    twice its forward."""
+    C, din, dh, dv = spec.chunk, spec.d_in, spec.d_hidden, spec.d_value
+    pc = spec.gate_mode == 1
+    p1, p2 = 2 * C * din * dh, 2 * C * dh * dv  # one product over the chunk's rows, per layer
+    terms = 2 if pc else 3
+    back = (2 * p1 + p2 + p2                      # Z (keys, queries), E, P
+            + (1 if pc else 2) * (p1 + p2)        # U projections
+            + p2 + 3 * p2 + terms * p2            # E', W2', H'
+            + terms * p1 + p2 + p1 + 2 * p1)      # X', Zq', Q', W1'
+    if pc:
+        back += p1 + p2                           # G recomputed
+        if spec.ns_steps:
+            nsf = ns_flops_per_matrix(dh, din, spec.ns_steps) + ns_flops_per_matrix(dv, dh, spec.ns_steps)
+            back += 3 * nsf                       # forward recomputed + backward (2x)
+    return int(sum(mlp_flops_per_chunk(spec).values()) + back)
+
+
 def ns_flops_per_matrix(rows, cols, steps):
     m, n = min(rows, cols), max(rows, cols)
     return steps * (2 * m * m * n + 2 * m * m * m + 2 * m * m * n)
@@ -105,7 +129,7 @@ def _dev(torch, a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def stage_rooflines(torch, am, synth, dev, stream):
+def stage_rooflines(torch, am, synth, dev, stream, only=None):
     """Stand-alone stages, each against its own roofline: the gate scan, Omega coefficients and
     feature map against HBM bandwidth (algorithmic bytes), Newton-Schulz against the bf16 matrix
     peak (algorithmic FLOPs).  Sizes are large enough for the launch to be bandwidth- or
@@ -173,10 +197,25 @@ def stage_rooflines(torch, am, synth, dev, stream):
         bmem.update_backward(bdev["K"], bdev["Q"], bdev["V"], bdev["theta"], bdev["eta"], bdev["alpha"], BT, bdY,
                              bout["dK"], bout["dQ"], bout["dV"], bout["dth"], bout["det"], bout["dal"], bout["dW0"],
                              bout["dS0"], bws)
-    # algorithmic FLOPs per token: the recorded forward and the backward's products (chunk 64,
-    # 64 -> 128 -> 64): recomputed Z (keys and queries), E, P, the four adjoint projections, E',
-    # W2', H', X', Zq', Q' and W1'
-    bflops_tok = 147456 + 360448
+    bwork = BM * (BT // bs.chunk) * backward_flops_per_chunk(bs)
+    # the same through per-chunk gates and 5 Newton-Schulz steps: every memory of the
+    # 8 x 16, 64 -> 128 -> 64, chunk-128 workload over its first 4096 tokens (32 chunks)
+    ni = synth.make_inputs(4, "literal", T=4096)
+    ns_ = ni.spec
+    nmem = am.Memory(_cfg(am, ns_), torch.from_numpy(ni.W0).to(dev), torch.from_numpy(ni.S0).to(dev))
+    ndev = {k: _dev(torch, getattr(ni, k), dev) for k in ("K", "Q", "V", "theta", "eta", "alpha")}
+    NT, NMm, NG = ns_.T, ns_.n_mem, ni.theta.shape[1]
+    nws = torch.empty(nmem.backward_workspace_bytes(NT), dtype=torch.uint8, device=dev)
+    nout = [bz(NMm, NT, ns_.d_key), bz(NMm, NT, ns_.d_key), bz(NMm, NT, ns_.d_value), bz(NMm, NG), bz(NMm, NG),
+            bz(NMm, NG), bz(NMm, nmem.P), bz(NMm, nmem.P)]
+    ndY = torch.randn((NMm, NT, ns_.d_value), device=dev)
+    nW0, nS0 = torch.from_numpy(ni.W0).to(dev), torch.from_numpy(ni.S0).to(dev)
+
+    def backward_ns_call():
+        nmem.set_state(nW0, nS0)
+        nmem.update_backward(ndev["K"], ndev["Q"], ndev["V"], ndev["theta"], ndev["eta"], ndev["alpha"], NT, ndY,
+                             *nout, nws)
+    nwork = NMm * (NT // ns_.chunk) * backward_flops_per_chunk(ns_)
     cases = [
         ("gate_scan", lambda: am.gate_scan(th, et, al, M, T, C, cW, cS, sc),
          M * T * (12 + 8) + M * (T // C) * 12, "hbm", f"{M} memories x {T} tokens, chunk {C}"),
@@ -198,10 +237,16 @@ def stage_rooflines(torch, am, synth, dev, stream):
          FN3 * (2 * FD + 4 * F3), "hbm", f"{FN3} bf16 vectors of width {FD} -> {F3} fp32 (degree 3)"),
         ("feature_project_deg2", lambda: am.feature_map(X, synth.BF16, NP, d, 2, Fproj, P=Pproj, d_out=FDO),
          2 * NP * F.shape[1] * FDO, "mfma", f"{NP} bf16 vectors of width {d}: degree-2 features x {FDO}-row projection"),
-        ("outer_backward", backward_call, BM * BT * bflops_tok, "mfma",
+        ("outer_backward", backward_call, bwork, "mfma",
          f"{bs.name} stabilised: forward with checkpoints and backward, {BM} memories x {BT} tokens"),
+        ("outer_backward_ns5", backward_ns_call, nwork, "mfma",
+         f"64 -> 128 -> 64 memory, chunk 128, per-chunk gates, 5 Newton-Schulz steps, forward with checkpoints "
+         f"and backward, "
+         f"{NMm} memories x {NT} tokens"),
     ]
     for name, fn, work, bound, shape in cases:
+        if only is not None and name != only:
+            continue
         for _ in range(3):
             fn()
         t = event_ms(fn, 20, stream)
@@ -279,6 +324,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the stand-alone stage rooflines")
+    ap.add_argument("--only-stage", default=None,
+                    help="time only this stand-alone stage (for profiling) and print its JSON object")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -295,6 +342,13 @@ def main():
     torch.cuda.set_device(0)
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
+    if args.only_stage:
+        st = stage_rooflines(torch, am, synth, dev, stream, only=args.only_stage)
+        if not st:
+            print(f"no stage named {args.only_stage}", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(st))
+        return
     inp = synth.make_inputs(args.workload, args.variant)
     s = inp.spec
 

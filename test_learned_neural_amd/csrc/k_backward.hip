@@ -23,6 +23,16 @@
 //   beta' = <WA, W>, aS' = <WA, S>, PC' = <SA, S>;  gates' from (cW', cS', PC', beta', aS') by the
 //   reverse of the gate scan
 //   WA <- beta WA + (W1', W2'),  SA <- aS WA + PC SA        (the adjoints at the chunk start)
+//
+// Per-chunk gates (one triple per chunk): G = sum_r g_r = (D1^T X, E^T H), N = NS(G) (or G),
+// S' = eta S - theta N, W' = (1 - alpha) W + S'.  With SAt = SA + WA (S' also feeds W'):
+//   theta' = -<SAt, N>, eta' = <SAt, S>, alpha' = -<WA, W>,  N' = -theta SAt,  G' = NS'(N')
+// and every row's gradient has the adjoint G', which the row products above take as WA with
+// cW = -1 and no momentum term.  NS' runs the iteration X <- a X + (b A + c A^2) X, A = X X^T,
+// backwards from its stored iterates:
+//   Ba = Xa X^T,  Aa = b Ba + c (Ba A + A Ba),  Xa <- a Xa + B Xa + (Aa + Aa^T) X
+// and through the normalisation X_0 = G / (|G| + eps):  G' = Xa_0 / n - (<Xa_0, G> / n^2) G / |G|.
+// The carry is WA <- (1 - alpha) WA + (W1', W2'), SA <- eta SAt.
 #include "common.h"
 #include "gemm.h"
 #include "internal.h"
@@ -187,22 +197,23 @@ __device__ __forceinline__ float silu_second(float z) {
 }
 
 // Per (row, memory): the coefficient adjoints and the elementwise adjoints (see the header).
-// Each lane reads and then overwrites only its own elements.
+// Each lane reads and then overwrites only its own elements.  With use_s = 0 (per-chunk gates:
+// cS = 0, the momentum adjoint is folded into the gradient adjoint) U1s and U2s are not read.
 __global__ void row_kernel(const float* __restrict__ Z, int64_t zz, float* __restrict__ Pz, const float* __restrict__ D1,
                            float* __restrict__ U1, float* __restrict__ U1s, const float* __restrict__ E,
                            float* __restrict__ U2, const float* __restrict__ U2s, int64_t hz, int64_t vz, int dh,
                            int dv, int C, const float* __restrict__ cW, const float* __restrict__ cS,
-                           float* __restrict__ cWa, float* __restrict__ cSa) {
+                           float* __restrict__ cWa, float* __restrict__ cSa, int use_s) {
   const int r = blockIdx.x, z = blockIdx.y, lane = threadIdx.x;
   const int64_t ho = (int64_t)z * hz + (int64_t)r * dh, vo = (int64_t)z * vz + (int64_t)r * dv;
   float s1 = 0.0f, s1s = 0.0f, s2 = 0.0f, s2s = 0.0f;
   for (int j = lane; j < dh; j += 64) {
     s1 += D1[ho + j] * U1[ho + j];
-    s1s += D1[ho + j] * U1s[ho + j];
+    if (use_s) s1s += D1[ho + j] * U1s[ho + j];
   }
   for (int j = lane; j < dv; j += 64) {
     s2 += E[vo + j] * U2[vo + j];
-    s2s += E[vo + j] * U2s[vo + j];
+    if (use_s) s2s += E[vo + j] * U2s[vo + j];
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -218,12 +229,12 @@ __global__ void row_kernel(const float* __restrict__ Z, int64_t zz, float* __res
   }
   for (int j = lane; j < dh; j += 64) {
     const float zv = Z[(int64_t)z * zz + (int64_t)r * dh + j];
-    const float d1a = -(cw * U1[ho + j] + cs * U1s[ho + j]);
+    const float d1a = -(cw * U1[ho + j] + (use_s ? cs * U1s[ho + j] : 0.0f));
     const float p = Pz[ho + j];
     U1s[ho + j] = d1a * silu_primef_(zv);  // P'
     Pz[ho + j] = d1a * p * silu_second(zv);  // Z'_1
   }
-  for (int j = lane; j < dv; j += 64) U2[vo + j] = -(cw * U2[vo + j] + cs * U2s[vo + j]);  // E'_g
+  for (int j = lane; j < dv; j += 64) U2[vo + j] = -(cw * U2[vo + j] + (use_s ? cs * U2s[vo + j] : 0.0f));  // E'_g
 }
 
 // beta' = <WA, W>, aS' = <WA, S>, PC' = <SA, S> per memory; ck: [M][2P] (W then S).
@@ -729,7 +740,6 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
         WAg = SAg = NAb;
       }
       hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cW, (int64_t)M * C, -1.0f);
-      hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cS, (int64_t)M * C, 0.0f);
       AM_LAUNCH_CHECK();
     }
     // U1 = X WA1^T, U1s = X SA1^T, U2 = H WA2^T, U2s = H SA2^T
@@ -738,15 +748,17 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat lh = bk::cat1(bk::src(Zk, 0, zz, dh, 1, C, dh, 1));
       launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(WAg, 0, P, din, 1, dh, din)),
                                 bk::EpiSt{U1, hz, dh}, st);
-      launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(SAg, 0, P, din, 1, dh, din)),
-                                bk::EpiSt{U1s, hz, dh}, st);
+      if (!per_chunk)
+        launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(SAg, 0, P, din, 1, dh, din)),
+                                  bk::EpiSt{U1s, hz, dh}, st);
       launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(WAg + P1, 0, P, dh, 1, dv, dh)),
                                 bk::EpiSt{U2, vz, dv}, st);
-      launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(SAg + P1, 0, P, dh, 1, dv, dh)),
-                                bk::EpiSt{U2s, vz, dv}, st);
+      if (!per_chunk)
+        launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(SAg + P1, 0, P, dh, 1, dv, dh)),
+                                  bk::EpiSt{U2s, vz, dv}, st);
     }
     hipLaunchKernelGGL(bk::row_kernel, dim3(C, M), dim3(64), 0, st, Zk, zz, Pz, D1, U1, U1s, E, U2, U2s, hz, vz, dh,
-                       dv, C, cW, cS, cWa, cSa);
+                       dv, C, cW, cS, cWa, cSa, per_chunk ? 0 : 1);
     AM_LAUNCH_CHECK();
     // now: U1s = P', Pz = Z'_1, U2 = E'_g.  E' = E'_g + P' W2^T (in U2), dV = -2 E'
     {
@@ -764,21 +776,34 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     }
     // H' = -(cW E) WA2 - (cS E) SA2 + (2E') W2;  Z' = Z'_1 + H' silu'(Z)  (in Pz)
     {
-      bk::Cat la = bk::cat3(bk::src(E, 0, vz, dv, 1, C, dv, 2, cW, C, -1.0f),
-                            bk::src(E, 0, vz, dv, 1, C, dv, 2, cS, C, -1.0f),
-                            bk::src(U2, 0, vz, dv, 1, C, dv, 0, nullptr, 0, 2.0f), dv, 2 * dv);
-      bk::Cat lb = bk::cat3(bk::src(WAg + P1, 0, P, 1, dh, dh, dv), bk::src(SAg + P1, 0, P, 1, dh, dh, dv),
-                            bk::src(cW2, 0, 2 * P, 1, dh, dh, dv), dv, 2 * dv);  // B(k=v, j=h) = M[v][h]
-      launch_gemm<false, false>(true, C, dh, 3 * dv, M, la, lb, bk::EpiZa{Pz, Zk, hz, zz, dh}, st);
+      const bk::Src ea = bk::src(E, 0, vz, dv, 1, C, dv, 2, cW, C, -1.0f);
+      const bk::Src e2 = bk::src(U2, 0, vz, dv, 1, C, dv, 0, nullptr, 0, 2.0f);
+      const bk::Src wa = bk::src(WAg + P1, 0, P, 1, dh, dh, dv);  // B(k=v, j=h) = M[v][h]
+      const bk::Src w2 = bk::src(cW2, 0, 2 * P, 1, dh, dh, dv);
+      if (per_chunk) {
+        launch_gemm<false, false>(true, C, dh, 2 * dv, M, bk::cat2(ea, e2, dv), bk::cat2(wa, w2, dv),
+                                  bk::EpiZa{Pz, Zk, hz, zz, dh}, st);
+      } else {
+        launch_gemm<false, false>(true, C, dh, 3 * dv, M,
+                                  bk::cat3(ea, bk::src(E, 0, vz, dv, 1, C, dv, 2, cS, C, -1.0f), e2, dv, 2 * dv),
+                                  bk::cat3(wa, bk::src(SAg + P1, 0, P, 1, dh, dh, dv), w2, dv, 2 * dv),
+                                  bk::EpiZa{Pz, Zk, hz, zz, dh}, st);
+      }
     }
     // X' = -(cW D1) WA1 - (cS D1) SA1 + Z' W1 -> dK rows
     {
-      bk::Cat la = bk::cat3(bk::src(D1, 0, hz, dh, 1, C, dh, 2, cW, C, -1.0f),
-                            bk::src(D1, 0, hz, dh, 1, C, dh, 2, cS, C, -1.0f), bk::src(Pz, 0, hz, dh, 1, C, dh), dh,
-                            2 * dh);
-      bk::Cat lb = bk::cat3(bk::src(WAg, 0, P, 1, din, din, dh), bk::src(SAg, 0, P, 1, din, din, dh),
-                            bk::src(cW1, 0, 2 * P, 1, din, din, dh), dh, 2 * dh);  // B(k=h, j=f) = M[h][f]
-      launch_gemm<false, false>(true, C, din, 3 * dh, M, la, lb, bk::EpiSt{dK + s * din, T * din, din}, st);
+      const bk::Src da = bk::src(D1, 0, hz, dh, 1, C, dh, 2, cW, C, -1.0f);
+      const bk::Src za = bk::src(Pz, 0, hz, dh, 1, C, dh);
+      const bk::Src wa = bk::src(WAg, 0, P, 1, din, din, dh);  // B(k=h, j=f) = M[h][f]
+      const bk::Src w1 = bk::src(cW1, 0, 2 * P, 1, din, din, dh);
+      const bk::EpiSt out{dK + s * din, T * din, din};
+      if (per_chunk) {
+        launch_gemm<false, false>(true, C, din, 2 * dh, M, bk::cat2(da, za, dh), bk::cat2(wa, w1, dh), out, st);
+      } else {
+        launch_gemm<false, false>(true, C, din, 3 * dh, M,
+                                  bk::cat3(da, bk::src(D1, 0, hz, dh, 1, C, dh, 2, cS, C, -1.0f), za, dh, 2 * dh),
+                                  bk::cat3(wa, bk::src(SAg, 0, P, 1, din, din, dh), w1, dh, 2 * dh), out, st);
+      }
     }
     // Zq' = (dY W2) silu'(Zq); Q' = Zq' W1 -> dQ rows
     {
