@@ -52,6 +52,35 @@ def mlp_flops_per_chunk(spec) -> dict:
     return f
 
 
+def gated_flops_per_chunk(spec) -> dict:
+    """Algorithmic FLOPs of one chunk of the gated memory M(x) = W2 (silu(W1 x) * (W3 x)): the
+    plain memory's products with the W1 products doubled (W3 beside W1) and three
+    Newton-Schulz matrices."""
+    C, din, dh, dv = spec.chunk, spec.d_in, spec.d_hidden, spec.d_value
+    R = C + spec.omega_window - 1
+    f = dict(
+        retrieval=2 * C * 2 * din * dh + 2 * C * dh * dv,
+        forward=2 * R * 2 * din * dh + 2 * R * dh * dv,
+        backward=2 * R * dv * dh,
+        wgrad=(2 if spec.gate_mode == 0 else 1) * (2 * R * dv * dh + 2 * 2 * R * dh * din),
+    )
+    if spec.ns_steps:
+        f["newton_schulz"] = 2 * ns_flops_per_matrix(dh, din, spec.ns_steps) + ns_flops_per_matrix(dv, dh,
+                                                                                                  spec.ns_steps)
+    return f
+
+
+def ptr_flops_per_chunk(spec) -> dict:
+    """The plain memory's chunk with per-token retrieval: the queries read W_t = beta_t W0 +
+    a_t S0 - sum_r Om[t][r] g_r through Z0 = Q W0_1^T, ZS = Q S0_1^T, the scores Q K^T, the mix
+    (Om * scores) D1, the hidden scores Hq Hk^T, Hq W0_2^T, Hq S0_2^T and (Om * scores) D2."""
+    C, din, dh, dv = spec.chunk, spec.d_in, spec.d_hidden, spec.d_value
+    R = C + spec.omega_window - 1
+    f = mlp_flops_per_chunk(spec)
+    f["retrieval"] = 2 * C * (2 * din * dh + R * din + 2 * R * dh + 2 * dh * dv + R * dv)
+    return f
+
+
 def backward_flops_per_chunk(spec) -> int:
     """Algorithmic FLOPs of one chunk of one memory in the outer-loop backward call (window 1,
     identity features): the forward it records (as in mlp_flops_per_chunk) plus the reverse step's
@@ -244,6 +273,76 @@ def stage_rooflines(torch, am, synth, dev, stream, only=None):
          f"and backward, "
          f"{NMm} memories x {NT} tokens"),
     ]
+    # the memory variants and the general per-chunk path at the Newton-Schulz workload's shape
+    # (128 memories, 64 -> 128 -> 64, chunk 128, 5 steps), over the first 4096 tokens
+    def update_case(spec_over, flags, label, flops_fn):
+        vi = synth.make_inputs(4, "literal", T=4096, **spec_over)
+        vs = vi.spec
+        vcfg = am.make_config(kind=vs.kind, batch=vs.batch, heads=vs.heads, d_key=vs.d_key, d_value=vs.d_value,
+                              d_hidden=vs.d_hidden, poly_degree=vs.poly_degree, chunk=vs.chunk,
+                              omega_window=vs.omega_window, gate_mode=vs.gate_mode, ns_steps=vs.ns_steps,
+                              input_dtype=vs.input_dtype, flags=flags)
+        W0v, S0v = torch.from_numpy(vi.W0).to(dev), torch.from_numpy(vi.S0).to(dev)
+        vm = am.Memory(vcfg, W0v, S0v)
+        vd = {k: _dev(torch, getattr(vi, k), dev) for k in ("K", "Q", "V", "theta", "eta", "alpha")}
+        Yv = torch.empty((vs.n_mem, vs.T, vs.d_value), dtype=torch.float32, device=dev)
+
+        def call():
+            vm.set_state(W0v, S0v)
+            vm.update_chunked(vd["K"], vd["Q"], vd["V"], vd["theta"], vd["eta"], vd["alpha"], None, vs.T, Yv)
+        work = vs.n_mem * (vs.T // vs.chunk) * sum(flops_fn(vs).values())
+        return (call, work, f"{label}: {vs.n_mem} memories x {vs.T} tokens, 64 -> 128 -> 64, chunk {vs.chunk}, "
+                            f"{vs.ns_steps} Newton-Schulz steps")
+    if only is None or only in ("update_general_ns5", "update_residual_ns5", "update_gated_ns5"):
+        ug = update_case({}, am.FLAG_NO_FUSED, "general per-chunk path (fused kernel off)", mlp_flops_per_chunk)
+        ur = update_case(dict(kind=synth.MLP2_SILU_RESIDUAL), 0, "residual memory", mlp_flops_per_chunk)
+        ugt = update_case(dict(kind=synth.MLP2_GATED), 0, "gated memory (W1, W3, W2)", gated_flops_per_chunk)
+        cases += [("update_general_ns5", ug[0], ug[1], "mfma", ug[2]),
+                  ("update_residual_ns5", ur[0], ur[1], "mfma", ur[2]),
+                  ("update_gated_ns5", ugt[0], ugt[1], "mfma", ugt[2])]
+    # per-token retrieval at the per-token workload's shape (8 memories x 4096 tokens, chunk 64)
+    if only is None or only == "update_per_token_retrieve":
+        pi = synth.make_inputs(1, "stabilised", per_token_retrieve=True)
+        ps = pi.spec
+        pcfg = am.make_config(kind=ps.kind, batch=ps.batch, heads=ps.heads, d_key=ps.d_key, d_value=ps.d_value,
+                              d_hidden=ps.d_hidden, chunk=ps.chunk, gate_mode=ps.gate_mode,
+                              input_dtype=ps.input_dtype, flags=am.FLAG_PER_TOKEN_RETRIEVE)
+        W0p, S0p = torch.from_numpy(pi.W0).to(dev), torch.from_numpy(pi.S0).to(dev)
+        pm = am.Memory(pcfg, W0p, S0p)
+        pd = {k: _dev(torch, getattr(pi, k), dev) for k in ("K", "Q", "V", "theta", "eta", "alpha")}
+        Yp = torch.empty((ps.n_mem, ps.T, ps.d_value), dtype=torch.float32, device=dev)
+
+        def ptr_call():
+            pm.set_state(W0p, S0p)
+            pm.update_chunked(pd["K"], pd["Q"], pd["V"], pd["theta"], pd["eta"], pd["alpha"], None, ps.T, Yp)
+        cases.append(("update_per_token_retrieve", ptr_call,
+                      ps.n_mem * (ps.T // ps.chunk) * sum(ptr_flops_per_chunk(ps).values()), "mfma",
+                      f"{ps.name}: queries read the state after their own token, {ps.n_mem} memories x {ps.T} tokens"))
+    # decoding: one token per call through the streaming path (the chunk's update runs on the
+    # call that completes it), 128 memories of the Newton-Schulz workload over two chunks.  Its
+    # algorithmic bytes per call: every memory's weights read for the query (fp32), the token's
+    # bf16 key, query and value, its fp32 output row.
+    if only is None or only == "decode_one_token_calls":
+        di = synth.make_inputs(4, "literal", T=256)
+        ds = di.spec
+        dm = am.Memory(_cfg(am, ds), torch.from_numpy(di.W0).to(dev), torch.from_numpy(di.S0).to(dev))
+        W0d2, S0d2 = torch.from_numpy(di.W0).to(dev), torch.from_numpy(di.S0).to(dev)
+        toks = []
+        for t in range(ds.T):
+            g0, g1 = t // ds.chunk, (t + 1) // ds.chunk
+            toks.append(dict(K=_dev(torch, di.K[:, t:t + 1], dev), Q=_dev(torch, di.Q[:, t:t + 1], dev),
+                             V=_dev(torch, di.V[:, t:t + 1], dev), th=_dev(torch, di.theta[:, g0:g1], dev),
+                             et=_dev(torch, di.eta[:, g0:g1], dev), al=_dev(torch, di.alpha[:, g0:g1], dev)))
+        Yd = torch.empty((ds.n_mem, 1, ds.d_value), dtype=torch.float32, device=dev)
+
+        def decode_call():
+            dm.set_state(W0d2, S0d2)
+            for tk in toks:
+                dm.update_chunked(tk["K"], tk["Q"], tk["V"], tk["th"], tk["et"], tk["al"], None, 1, Yd)
+        dbytes = ds.T * ds.n_mem * (dm.P * 4 + (2 * ds.d_key + ds.d_value) * 2 + ds.d_value * 4)
+        cases.append(("decode_one_token_calls", decode_call, dbytes, "hbm",
+                      f"{ds.n_mem} memories x {ds.T} tokens, one token per call (two chunks of {ds.chunk}), "
+                      f"64 -> 128 -> 64, 5 Newton-Schulz steps"))
     for name, fn, work, bound, shape in cases:
         if only is not None and name != only:
             continue

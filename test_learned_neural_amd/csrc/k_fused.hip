@@ -116,6 +116,8 @@ struct Args {
   int* flag;
 };
 
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
 // LDS buffer bases as opaque scalars: the bases lie beyond the 64 KB reach of a ds
 // instruction's immediate offset, so folding them into constants would cost one address
 // register per (buffer, constant) pair; kept opaque, only the small in-buffer constants fold.
@@ -362,6 +364,11 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
   for (int it = 3; it < a.ns_steps; ++it) iteration();
 }
 
+// RES: the residual memory M(x) = x + W2 silu(W1 x) (input and output widths are both D): the
+// key's own values enter the error, D2 = 2 (Yh - (V - x)); each V element register carries the
+// key element of the same position in its upper half.  The query's values are added to the
+// output after the launch (residual_output_kernel).
+template <bool RES>
 __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
   float* red = (float*)(sm + LDS_U16);
@@ -479,8 +486,17 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        vv[4 * rt + u] = buf_ld_u16(rV, (4 * (lane >> 4) * D + vcol) * 2 + u * D * 2, (rset + 16 * rt) * D * 2);
+      for (int u = 0; u < 4; ++u) {
+        const int vo = (4 * (lane >> 4) * D + vcol) * 2 + u * D * 2, so = (rset + 16 * rt) * D * 2;
+        if (RES) {
+          v2u16 pr;
+          pr.x = __builtin_amdgcn_raw_buffer_load_b16(rV, vo, so, 0);
+          pr.y = __builtin_amdgcn_raw_buffer_load_b16(rK, vo, so, 0);
+          vv[4 * rt + u] = __builtin_bit_cast(uint32_t, pr);
+        } else {
+          vv[4 * rt + u] = buf_ld_u16(rV, vo, so);
+        }
+      }
     // Z = X W1^T of keys and queries: this set's 32 rows, hidden units of this wave
     f32x16 zk = zero16(), zq = zero16();
 #pragma unroll
@@ -548,7 +564,11 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
       const int rr = GR * s + 16 * rt + 4 * (lane >> 4);
       float d2[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) d2[u] = 2.0f * (yk[rt][u] - bf16_value(vv[4 * rt + u]));
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t pv = vv[4 * rt + u];
+        d2[u] = RES ? 2.0f * (yk[rt][u] - (bf16_value(pv & 0xFFFFu) - __uint_as_float(pv & 0xFFFF0000u)))
+                    : 2.0f * (yk[rt][u] - bf16_value(pv));
+      }
       uint32_t h0, l0, h1, l1;
       split2(d2[0], d2[1], h0, l0);
       split2(d2[2], d2[3], h1, l1);
@@ -784,19 +804,40 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
 #undef AM_LANE_VARS
 }
 
+// The residual memory's retrieval adds the query to the fused kernel's output:
+// Y[m][t][v] += q[m][t][v] over the call's tokens (fp32 output; 8 elements per thread).
+__global__ void residual_output_kernel(const uint16_t* __restrict__ Q, float* __restrict__ Y, int64_t ld, int64_t n) {
+  const int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (e >= n) return;
+  const int64_t o = (int64_t)blockIdx.y * ld + e;
+  const u32x4 q = *(const u32x4*)(Q + o);
+  float4* y = (float4*)(Y + o);
+  float4 a = y[0], b = y[1];
+  a.x += bf16_value(q[0] & 0xFFFFu);
+  a.y += bf16_value(q[0] >> 16);
+  a.z += bf16_value(q[1] & 0xFFFFu);
+  a.w += bf16_value(q[1] >> 16);
+  b.x += bf16_value(q[2] & 0xFFFFu);
+  b.y += bf16_value(q[2] >> 16);
+  b.z += bf16_value(q[3] & 0xFFFFu);
+  b.w += bf16_value(q[3] >> 16);
+  y[0] = a;
+  y[1] = b;
+}
+
 }  // namespace fz
 
 bool fused_supported(const Dims& d) {
-  return d.kind == ATLASMEM_MLP2_SILU && !d.residual && !d.gated && d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0 && d.dk == fz::D &&
+  return d.kind == ATLASMEM_MLP2_SILU && !d.gated && d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0 && d.dk == fz::D &&
          d.din == fz::D && d.dv == fz::D && d.dh == fz::HD && d.c == 1 && d.C % fz::GROWS == 0 && d.in_bf16 &&
-         d.split;
+         d.split && !(d.residual && d.out_bf16);
 }
 
 atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
                              const float* theta, const float* eta, const float* alpha, const Span& sp, void* Y,
                              hipStream_t st) {
-  if (hipFuncSetAttribute((const void*)fz::fused_ns_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          fz::LDS_BYTES) != hipSuccess)
+  const void* kern = d.residual ? (const void*)fz::fused_ns_kernel<true> : (const void*)fz::fused_ns_kernel<false>;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, fz::LDS_BYTES) != hipSuccess)
     return ATLASMEM_E_DEVICE;
   // one launch per segment of at most 2^22 tokens, so that per-memory byte offsets fit 32 bits
   const int64_t nchunks = sp.T / d.C;
@@ -829,9 +870,16 @@ atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void
     a.ns_c = d.ns_c;
     a.ns_eps = d.ns_eps;
     a.flag = h->flag;
-    hipLaunchKernelGGL(fz::fused_ns_kernel, dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+    if (d.residual) hipLaunchKernelGGL(fz::fused_ns_kernel<true>, dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+    else hipLaunchKernelGGL(fz::fused_ns_kernel<false>, dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
     AM_LAUNCH_CHECK();
     h->cur = 1 - h->cur;
+  }
+  if (d.residual && Y && sp.T > 0) {
+    const int64_t n = sp.T * fz::D;  // a whole number of 8-element groups (D = 64)
+    hipLaunchKernelGGL(fz::residual_output_kernel, dim3((unsigned)((n / 8 + 255) / 256), d.M), dim3(256), 0, st,
+                       (const uint16_t*)Q, (float*)Y, sp.ld * fz::D, n);
+    AM_LAUNCH_CHECK();
   }
   return ATLASMEM_OK;
 }

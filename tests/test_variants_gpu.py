@@ -24,7 +24,8 @@ RESIDUAL = [
           omega_window=3), [0, 48, 96, 144]),
     ("poly2_d4_to_15_window2", 3, "stabilised",
      dict(kind=R, batch=2, heads=1, T=96, d_key=4, d_value=15, d_hidden=24, chunk=24, omega_window=2), None),
-    ("ns5_per_chunk_general_path", 4, "literal", dict(kind=R, batch=1, heads=3, T=512), None),
+    ("ns5_per_chunk_fused", 4, "literal", dict(kind=R, batch=1, heads=3, T=512), None),
+    ("ns5_fused_streamed", 4, "literal", dict(kind=R, batch=1, heads=2, T=512), [0, 1, 2, 130, 256, 300, 512]),
     ("streamed_uneven_calls", 1, "stabilised", dict(kind=R, batch=1, heads=2, T=192),
      [0, 1, 2, 3, 70, 71, 150, 192]),
 ]
@@ -40,6 +41,25 @@ def test_residual_memory_parity(case):
     errs = compare(f"residual_{name}", inp.spec, got, ref, BF16_TOL)
     assert got[3] == am.OK
     assert all(v <= BF16_TOL for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_residual_fused_matches_general(out):
+    """The fused kernel's residual variant (key values in the error, query values added to the
+    output afterwards) against the general per-chunk path on the same inputs, and both against
+    the oracle.  bf16 output runs the general path either way (one rounding of q + Yh)."""
+    log(f"CASE residual fused vs general ({out})")
+    inp = synth.make_inputs(4, "literal", kind=R, batch=1, heads=4, T=384)
+    od = am.BF16 if out == "bf16" else am.F32
+    fused = run_gpu(inp, output_dtype=od)
+    general = run_gpu(inp, output_dtype=od, flags=am.FLAG_NO_FUSED)
+    ref = oracle_run(inp)
+    errs = compare(f"residual_fused_{out}", inp.spec, fused, ref, BF16_TOL)
+    assert fused[3] == am.OK and general[3] == am.OK
+    assert all(v <= BF16_TOL for v in errs.values()), errs
+    agree = {k: maxrel(a, b) for k, a, b in zip(("Y", "W", "S"), fused[:3], general[:3])}
+    log(f"PARITY residual fused vs general ({out}): " + " ".join(f"{k}={v:.3e}" for k, v in agree.items()))
+    assert all(v <= 5e-4 for v in agree.values()), agree
 
 
 def test_residual_retrieve_and_shape_error():
