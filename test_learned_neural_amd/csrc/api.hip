@@ -326,6 +326,21 @@ bool append_pending(Handle* h, const void* K, const void* V, const float* theta,
 
 const char* at_token(const void* base, int64_t t, size_t row) { return base ? (const char*)base + t * row : nullptr; }
 
+// Tokens [0, n) of a streaming call that join the unfinished chunk: their queries are answered
+// from the current state (the chunk's start weights) and their rows appended.  A call of a few
+// tokens takes one decode launch; otherwise the GEMM-engine retrieval and strided copies.
+static atlasmem_status stream_rows(Handle* h, const void* Q, const void* K, const void* V, const float* theta,
+                                   const float* eta, const float* alpha, const float* gamma, int64_t ld, int64_t n,
+                                   void* Y, hipStream_t st) {
+  if (n == 0) return ATLASMEM_OK;
+  const atlasmem_status s = launch_decode(h, Q, K, V, theta, eta, alpha, gamma, ld, n, Y, true, st);
+  if (s != ATLASMEM_E_UNSUPPORTED) return s;
+  atlasmem_status r;
+  if (Y && (r = retrieve_rows(h, Q, n, ld, Y, st)) != ATLASMEM_OK) return r;
+  if (!append_pending(h, K, V, theta, eta, alpha, gamma, ld, n, st)) return ATLASMEM_E_DEVICE;
+  return ATLASMEM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -361,8 +376,7 @@ atlasmem_status atlasmem_update_chunked(atlasmem_handle hh, const void* K, const
     // tokens of the unfinished chunk: retrieved now, at its start weights (the current state),
     // and buffered until the chunk is complete
     const int64_t a = T < C - p0 ? T : C - p0;
-    if (Y && (s = retrieve_rows(h, Q, a, T, Y, st)) != ATLASMEM_OK) return s;
-    if (!append_pending(h, K, V, theta, eta, alpha, gamma, T, a, st)) return ATLASMEM_E_DEVICE;
+    if ((s = stream_rows(h, Q, K, V, theta, eta, alpha, gamma, T, a, Y, st)) != ATLASMEM_OK) return s;
     pos = a;
     if (h->pending == C) {
       const float* th = per_token ? h->pth : theta;
@@ -388,12 +402,11 @@ atlasmem_status atlasmem_update_chunked(atlasmem_handle hh, const void* K, const
   // the rest starts a new chunk
   const int64_t r = T - pos;
   if (r > 0) {
-    if (Y && (s = retrieve_rows(h, at_token(Q, pos, ek), r, T, (void*)at_token(Y, pos, ey), st)) != ATLASMEM_OK)
+    if ((s = stream_rows(h, Q ? at_token(Q, pos, ek) : nullptr, at_token(K, pos, ek), at_token(V, pos, ev),
+                         per_token ? theta + pos : nullptr, per_token ? eta + pos : nullptr,
+                         per_token ? alpha + pos : nullptr, gamma ? gamma + pos : nullptr, T, r,
+                         Y ? (void*)at_token(Y, pos, ey) : nullptr, st)) != ATLASMEM_OK)
       return s;
-    if (!append_pending(h, at_token(K, pos, ek), at_token(V, pos, ev), per_token ? theta + pos : nullptr,
-                        per_token ? eta + pos : nullptr, per_token ? alpha + pos : nullptr,
-                        gamma ? gamma + pos : nullptr, T, r, st))
-      return ATLASMEM_E_DEVICE;
   }
   return ATLASMEM_OK;
 }
@@ -434,6 +447,8 @@ atlasmem_status atlasmem_retrieve(atlasmem_handle hh, const void* Q, int64_t T, 
   if (!Q || !Y) return ATLASMEM_E_INVALID;
   DeviceGuard g(h->device);
   if (!g.ok) return ATLASMEM_E_DEVICE;
+  if (decode_supported(h->d, T))
+    return launch_decode(h, Q, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, T, T, Y, false, S(stream));
   return retrieve_rows(h, Q, T, T, Y, S(stream));
 }
 

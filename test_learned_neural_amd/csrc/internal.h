@@ -115,6 +115,13 @@ using Handle = ::atlasmem_handle_s;
 // Outer-loop backward (k_backward.hip)
 bool backward_supported(const Dims& d);
 int64_t backward_workspace_bytes(const Dims& d, int64_t T);
+// Streaming calls of at most a few tokens (k_decode.hip): the queries' retrieval from the current
+// state and, with `append`, the key / value rows and per-token gates appended to the unfinished
+// chunk, in one launch.  E_UNSUPPORTED when the configuration or the call does not qualify.
+bool decode_supported(const Dims& d, int64_t n);
+atlasmem_status launch_decode(Handle* h, const void* Q, const void* K, const void* V, const float* theta,
+                              const float* eta, const float* alpha, const float* gamma, int64_t ld, int64_t n,
+                              void* Y, bool append, hipStream_t st);
 atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V, const float* theta, const float* eta,
                          const float* alpha, int64_t T, void* Y, const float* dY, const float* dWT, const float* dST,
                          void* workspace, float* dK, float* dQ, float* dV, float* dth, float* det, float* dal,

@@ -1,0 +1,251 @@
+// Streaming calls of a few tokens (decoding): one launch per call answers the call's queries from
+// the current state and appends its key and value rows (and per-token gates) to the unfinished
+// chunk, in place of the GEMM-engine retrieval and the strided copies.
+//
+// Retrieval of an MLP memory at the chunk-start weights (titans-pytorch-mlx README, Core
+// Equations: the memory is read with the weights of the chunk's start; Atlas-Torch README, Atlas
+// Extensions table: the residual and gated memories):
+//   Z = W1 q (and Z3 = W3 q for the gated memory), H = silu(Z) (or silu(Z) * Z3),
+//   y = W2 H (+ q for the residual memory).
+// The products keep the library's precision policy: every fp32 operand is split into bf16
+// hi + lo and a product is summed as hi*hi + hi*lo + lo*hi in fp32 (a bf16 input is exact and
+// contributes no lo term; without the split only hi*hi), so answers do not depend on how the
+// sequence is cut into calls beyond the order of fp32 accumulation.
+//
+// One 256-thread workgroup per memory: the queries go to LDS in fp32; a row of W1 q (and then of
+// W2 H) is split over up to 64 lanes, each reading its segment of the weight row as 16-byte
+// vectors, all issued before the products, and the partial sums meet by cross-lane reduction.
+#include "common.h"
+#include "internal.h"
+
+namespace am {
+namespace dk {
+
+struct Args {
+  const void* Q;   // the call's first token of memory 0; memory m at + m * ld rows
+  const void* K;
+  const void* V;
+  int64_t ld;      // tokens per memory in the caller's arrays
+  int n;           // tokens of this call
+  int in_bf16;
+  const float* W;  // state [M][P]
+  int64_t P, P1;
+  int din, dh, dv, dz;
+  int gated, residual, split;
+  void* Y;         // the call's first output row of memory 0 (null: no retrieval)
+  int out_bf16;
+  // the unfinished chunk: rows r0 .. r0 + n of [M][C][width] buffers (append = 0: retrieval only)
+  int append;
+  void* pK;
+  void* pV;
+  int C;
+  int64_t r0;
+  const float* th;  // per-token gates and gamma of the call (null: none), [M][ld]
+  const float* et;
+  const float* al;
+  const float* gm;
+  float* pth;
+  float* pet;
+  float* pal;
+  float* pg;
+};
+
+__device__ __forceinline__ void split1(float x, float& hi, float& lo) {
+  uint32_t h, l;
+  split_bf16(x, h, l);
+  hi = bf16_value(h);
+  lo = bf16_value(l);
+}
+
+// sum_i w[i] x[i] over a segment of one fp32 weight row (16-byte aligned, length a multiple of
+// 4) and an fp32 vector in LDS whose bf16 halves are xh / xl (xl unused when x_exact).  The
+// segment is read 64 floats at a time with every load issued before the products, so a
+// segment of up to 64 floats costs one memory latency.
+__device__ __forceinline__ float seg_dot(const float* __restrict__ w, const float* xh, const float* xl, int len,
+                                         bool x_exact, bool split) {
+  float acc = 0.0f;
+  for (int i0 = 0; i0 < len; i0 += 64) {
+    float4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = (i0 + 4 * u < len) ? *(const float4*)(w + i0 + 4 * u) : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (i0 + 4 * u >= len) break;
+      const float wv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = i0 + 4 * u + c;
+        float wh, wl;
+        split1(wv[c], wh, wl);
+        const float a = xh[i];
+        acc = fmaf(a, wh, acc);
+        if (split) {
+          acc = fmaf(a, wl, acc);
+          if (!x_exact) acc = fmaf(xl[i], wh, acc);
+        }
+      }
+    }
+  }
+  return acc;
+}
+
+// Lanes per output row: the most (a power of two up to 64) that keeps every lane busy with a
+// segment of whole 16-byte vectors.
+__device__ __forceinline__ int lanes_per_row(int rows, int len) {
+  int p = 1;
+  while (p < 64 && rows * p * 2 <= 256 && len % (8 * p) == 0) p *= 2;
+  return p;
+}
+
+__global__ void __launch_bounds__(256) decode_kernel(Args a) {
+  extern __shared__ float ds[];
+  const int z = blockIdx.x, t = threadIdx.x, n = a.n;
+  const size_t esz = a.in_bf16 ? 2 : 4;
+  // the call's rows of this memory: token tt of memory z is row z * ld + tt
+  const int64_t row0 = (int64_t)z * a.ld;
+  // append keys, values and per-token gates to the unfinished chunk (raw element copies)
+  if (a.append) {
+    const int64_t kw = (int64_t)a.din * esz, vw = (int64_t)a.dv * esz;  // row bytes (identity features: din = dk)
+    const char* ks = (const char*)a.K + row0 * kw;
+    const char* vs = (const char*)a.V + row0 * vw;
+    char* kd = (char*)a.pK + ((int64_t)z * a.C + a.r0) * kw;
+    char* vd = (char*)a.pV + ((int64_t)z * a.C + a.r0) * vw;
+    for (int64_t e = t; e < n * kw / 2; e += 256) ((uint16_t*)kd)[e] = ((const uint16_t*)ks)[e];
+    for (int64_t e = t; e < n * vw / 2; e += 256) ((uint16_t*)vd)[e] = ((const uint16_t*)vs)[e];
+    if (t < n) {
+      const int64_t src = row0 + t, dst = (int64_t)z * a.C + a.r0 + t;
+      if (a.th) {
+        a.pth[dst] = a.th[src];
+        a.pet[dst] = a.et[src];
+        a.pal[dst] = a.al[src];
+      }
+      if (a.gm) a.pg[dst] = a.gm[src];
+    }
+  }
+  if (!a.Y) return;
+  // LDS: q hi, q lo [n][din]; Z [n][dz]; H hi, H lo [n][dh]
+  float* qh = ds;
+  float* ql = qh + n * a.din;
+  float* zs = ql + n * a.din;
+  float* hh = zs + n * a.dz;
+  float* hl = hh + n * a.dh;
+  const bool q_exact = a.in_bf16;
+  for (int e = t; e < n * a.din; e += 256) {
+    const float x = load_in(a.Q, row0 * a.din + e, a.in_bf16);
+    float h, l;
+    split1(x, h, l);
+    qh[e] = q_exact ? x : h;
+    ql[e] = q_exact ? 0.0f : l;
+  }
+  __syncthreads();
+  const float* W1 = a.W + (int64_t)z * a.P;
+  const float* W2 = W1 + a.P1;
+  {  // Z = W1 q: p lanes per (token, row), partial sums reduced across the p lanes
+    const int p = lanes_per_row(n * a.dz, a.din), seg = a.din / p;
+    for (int e0 = 0; e0 < n * a.dz * p; e0 += 256) {
+      const int e = e0 + t, task = e / p, part = e - task * p;
+      float acc = 0.0f;
+      if (task < n * a.dz) {
+        const int tt = task / a.dz, j = task - tt * a.dz, i0 = part * seg;
+        acc = seg_dot(W1 + (int64_t)j * a.din + i0, qh + tt * a.din + i0, ql + tt * a.din + i0, seg, q_exact,
+                      a.split);
+      }
+      for (int off = 1; off < p; off <<= 1) acc += __shfl_xor(acc, off, 64);
+      if (task < n * a.dz && part == 0) zs[task] = acc;
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < n * a.dh; e += 256) {
+    const int tt = e / a.dh, j = e - tt * a.dh;
+    const float zv = zs[tt * a.dz + j];
+    const float hv = a.gated ? siluf_(zv) * zs[tt * a.dz + a.dh + j] : siluf_(zv);
+    float h, l;
+    split1(hv, h, l);
+    hh[e] = h;
+    hl[e] = l;
+  }
+  __syncthreads();
+  {  // y = W2 H (+ q)
+    const int p = lanes_per_row(n * a.dv, a.dh), seg = a.dh / p;
+    for (int e0 = 0; e0 < n * a.dv * p; e0 += 256) {
+      const int e = e0 + t, task = e / p, part = e - task * p;
+      float y = 0.0f;
+      if (task < n * a.dv) {
+        const int tt = task / a.dv, v = task - tt * a.dv, i0 = part * seg;
+        y = seg_dot(W2 + (int64_t)v * a.dh + i0, hh + tt * a.dh + i0, hl + tt * a.dh + i0, seg, false, a.split);
+      }
+      for (int off = 1; off < p; off <<= 1) y += __shfl_xor(y, off, 64);
+      if (task < n * a.dv && part == 0) {
+        const int tt = task / a.dv, v = task - tt * a.dv;
+        if (a.residual) y += load_in(a.Q, (row0 + tt) * a.din + v, a.in_bf16);  // din = dv
+        const int64_t o = (row0 + tt) * a.dv + v;
+        if (a.out_bf16) ((uint16_t*)a.Y)[o] = (uint16_t)bf16_bits(y);
+        else ((float*)a.Y)[o] = y;
+      }
+    }
+  }
+}
+
+}  // namespace dk
+
+constexpr int kDecodeMaxTokens = 8;
+constexpr int kDecodeMaxLds = 64 * 1024;
+
+static size_t decode_lds(const Dims& d, int64_t n) {
+  return sizeof(float) * (size_t)n * (2 * (size_t)d.din + (size_t)d.dz + 2 * (size_t)d.dh);
+}
+
+bool decode_supported(const Dims& d, int64_t n) {
+  return d.kind == ATLASMEM_MLP2_SILU && d.poly == 1 && !d.ptr && n >= 1 && n <= kDecodeMaxTokens &&
+         d.din % 4 == 0 && d.dh % 4 == 0 && decode_lds(d, n) <= (size_t)kDecodeMaxLds;
+}
+
+atlasmem_status launch_decode(Handle* h, const void* Q, const void* K, const void* V, const float* theta,
+                              const float* eta, const float* alpha, const float* gamma, int64_t ld, int64_t n,
+                              void* Y, bool append, hipStream_t st) {
+  const Dims& d = h->d;
+  if (!decode_supported(d, n)) return ATLASMEM_E_UNSUPPORTED;
+  if (append && (h->pending + n > d.C || !K || !V || (d.c > 1 && !gamma) ||
+                 (d.gate_mode == ATLASMEM_PER_TOKEN && (!theta || !eta || !alpha))))
+    return ATLASMEM_E_UNSUPPORTED;
+  if (!append && !Y) return ATLASMEM_OK;
+  dk::Args a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.ld = ld;
+  a.n = (int)n;
+  a.in_bf16 = d.in_bf16;
+  a.W = h->W[h->cur];
+  a.P = d.P;
+  a.P1 = d.P1;
+  a.din = d.din;
+  a.dh = d.dh;
+  a.dv = d.dv;
+  a.dz = d.dz;
+  a.gated = d.gated;
+  a.residual = d.residual;
+  a.split = d.split;
+  a.Y = Y;
+  a.out_bf16 = d.out_bf16;
+  a.append = append;
+  a.pK = h->pK;
+  a.pV = h->pV;
+  a.C = d.C;
+  a.r0 = h->pending;
+  const bool per_token = d.gate_mode == ATLASMEM_PER_TOKEN;
+  a.th = per_token ? theta : nullptr;
+  a.et = per_token ? eta : nullptr;
+  a.al = per_token ? alpha : nullptr;
+  a.gm = d.c > 1 ? gamma : nullptr;
+  a.pth = h->pth;
+  a.pet = h->pet;
+  a.pal = h->pal;
+  a.pg = h->pg;
+  hipLaunchKernelGGL(dk::decode_kernel, dim3(d.M), dim3(256), Y ? decode_lds(d, n) : 0, st, a);
+  AM_LAUNCH_CHECK();
+  if (append) h->pending += n;
+  return ATLASMEM_OK;
+}
+
+}  // namespace am
