@@ -2,9 +2,9 @@
 // the current state and appends its key and value rows (and per-token gates) to the unfinished
 // chunk, in place of the GEMM-engine retrieval and the strided copies.
 //
-// Retrieval of an MLP memory at the chunk-start weights (titans-pytorch-mlx README, Core
-// Equations: the memory is read with the weights of the chunk's start; Atlas-Torch README, Atlas
-// Extensions table: the residual and gated memories):
+// Retrieval of an MLP memory (titans-pytorch-mlx README, MAC Eq. 21: the memory is read without
+// an update; the unfinished chunk's queries read the weights of its start, as inside a chunk;
+// ATLAS summary, section 5.1: the residual and gated memories):
 //   Z = W1 q (and Z3 = W3 q for the gated memory), H = silu(Z) (or silu(Z) * Z3),
 //   y = W2 H (+ q for the residual memory).
 // The products keep the library's precision policy: every fp32 operand is split into bf16
