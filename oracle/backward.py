@@ -23,29 +23,31 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .neural_memory import LINEAR, MLP2_SILU, PER_TOKEN, MemoryConfig
+from .neural_memory import LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, PER_TOKEN, MemoryConfig
 
 
 def _silu(z):
     return z * torch.sigmoid(z)
 
 
-def _apply(params, x):
+def _apply(params, x, residual=False):
     if len(params) == 1:
         return params[0] @ x
-    return params[1] @ _silu(params[0] @ x)
+    y = params[1] @ _silu(params[0] @ x)
+    return x + y if residual else y
 
 
-def _grad(params, x, v):
+def _grad(params, x, v, residual=False):
     """The inner gradient of ||M_W(x) - v||^2, written out (so that it can itself be
-    differentiated): linear 2 (W x - v) x^T; MLP e = 2 (W2 h - v), (W2^T e) * silu'(z) x^T, e h^T."""
+    differentiated): linear 2 (W x - v) x^T; MLP e = 2 (W2 h - v), (W2^T e) * silu'(z) x^T, e h^T;
+    the residual memory x + W2 silu(W1 x) has e = 2 (W2 h + x - v) (ATLAS summary, section 5.1)."""
     if len(params) == 1:
         return [torch.outer(2.0 * (params[0] @ x - v), x)]
     w1, w2 = params
     z = w1 @ x
     s = torch.sigmoid(z)
     h = z * s
-    e = 2.0 * (w2 @ h - v)
+    e = 2.0 * (w2 @ h + x - v) if residual else 2.0 * (w2 @ h - v)
     sp = s * (1.0 + z * (1.0 - s))
     return [torch.outer((w2.T @ e) * sp, x), torch.outer(e, h)]
 
@@ -66,8 +68,10 @@ def _newton_schulz(g, steps, coeffs, eps):
 def run_memory_torch(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha):
     """The literal chunked recurrence for one memory (window 1, identity features; per-token
     gates, or per-chunk gates with an optional Newton-Schulz orthogonalisation of the summed
-    chunk gradient) with torch tensors: Y, final params, final momenta."""
+    chunk gradient) with torch tensors: Y, final params, final momenta.  Plain, residual or
+    linear memory."""
     assert cfg.omega_window == 1 and cfg.poly_degree == 1
+    res = cfg.kind == MLP2_SILU_RESIDUAL
     W = list(params)
     S = list(momenta)
     T = K.shape[0]
@@ -77,16 +81,16 @@ def run_memory_torch(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, al
         e = min(s + C, T)
         wb = list(W)
         for t in range(s, e):
-            Y.append(_apply(wb, Q[t]))
+            Y.append(_apply(wb, Q[t], res))
         if cfg.gate_mode == PER_TOKEN:
             for t in range(s, e):
-                G = _grad(wb, K[t], V[t])
+                G = _grad(wb, K[t], V[t], res)
                 S = [eta[t] * S[m] - theta[t] * G[m] for m in range(len(W))]
                 W = [(1.0 - alpha[t]) * W[m] + S[m] for m in range(len(W))]
         else:
             G = [torch.zeros_like(w) for w in W]
             for t in range(s, e):
-                G = [G[m] + g for m, g in enumerate(_grad(wb, K[t], V[t]))]
+                G = [G[m] + g for m, g in enumerate(_grad(wb, K[t], V[t], res))]
             if cfg.ns_steps > 0:
                 G = [_newton_schulz(g, cfg.ns_steps, cfg.ns_coeffs, cfg.ns_eps) for g in G]
             k = s // C

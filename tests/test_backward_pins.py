@@ -6,12 +6,14 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import LINEAR, MLP2_SILU, PER_CHUNK, PER_TOKEN, MemoryConfig
+from oracle import LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, PER_CHUNK, PER_TOKEN, MemoryConfig
 from oracle import backward as bw
 
 
 def problem(seed, kind, T=8, C=4, d=3, v=2, h=5, mode=PER_TOKEN, ns=0):
     r = np.random.default_rng(seed)
+    if kind == MLP2_SILU_RESIDUAL:
+        v = d  # the residual memory adds its input to its output
     cfg = MemoryConfig(kind, d, v, h if kind != LINEAR else 0, 1, C, 1, mode, ns)
     if kind == LINEAR:
         params = [r.normal(0, 0.5, (v, d))]
@@ -36,7 +38,7 @@ def objective(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS):
 
 
 MODES = [(LINEAR, PER_TOKEN, 0), (MLP2_SILU, PER_TOKEN, 0), (MLP2_SILU, PER_CHUNK, 0), (MLP2_SILU, PER_CHUNK, 5),
-         (LINEAR, PER_CHUNK, 5)]
+         (LINEAR, PER_CHUNK, 5), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0), (MLP2_SILU_RESIDUAL, PER_CHUNK, 5)]
 
 
 @pytest.mark.parametrize("kind,mode,ns", MODES)
