@@ -245,9 +245,10 @@ atlasmem_status atlasmem_newton_schulz(const float* G, int64_t n_mat, int32_t ro
  * final state, with respect to every input of the update and the state it started from
  * (Atlas-Torch README, "How the memory works": the outer loop trains through the inner updates;
  * the derivative of the recurrence includes that of the inner gradient).
- * Scope: MLP2_SILU, omega_window 1, poly_degree 1, no per-token retrieval, and either PER_TOKEN
- * gates (ns_steps 0) or PER_CHUNK gates with or without the Newton-Schulz orthogonalisation of
- * the chunk gradient (its iteration differentiated step by step) (E_UNSUPPORTED otherwise);
+ * Scope: MLP2_SILU or MLP2_SILU_RESIDUAL, omega_window 1, poly_degree 1, no per-token retrieval,
+ * and either PER_TOKEN gates (ns_steps 0) or PER_CHUNK gates with or without the Newton-Schulz
+ * orthogonalisation of the chunk gradient (its iteration differentiated step by step)
+ * (E_UNSUPPORTED otherwise);
  * T a multiple of the chunk and nothing pending (E_SHAPE otherwise).
  *   theta, eta, alpha: as in atlasmem_update_chunked ([M, T] per token, [M, T/C] per chunk)
  *   dY: fp32 [M, T, d_value];  dW_T, dS_T: fp32 [M, P] or NULL (zero)

@@ -1,7 +1,8 @@
 // Outer-loop backward of the chunked update: the gradients of an outer loss with respect to the
 // keys, queries, values, gates and initial state of the test-time update (Atlas-Torch README,
 // "How the memory works": the outer loop trains through the inner updates).  Scope: the 2-layer
-// SiLU memory with window 1 and identity features; per-token gates, or per-chunk gates with the
+// SiLU memory (plain or residual, x + W2 silu(W1 x)) with window 1 and identity features;
+// per-token gates, or per-chunk gates with the
 // optional Newton-Schulz orthogonalisation of the chunk gradient (differentiated through its
 // iterates, which the reverse step recomputes from the chunk-start checkpoint).
 //
@@ -111,16 +112,19 @@ struct EpiSt {  // out[z * sz + row * ld + col]
     out[(int64_t)z * sz + (int64_t)row * ld + col] = v;
   }
 };
-struct EpiE {  // E = 2 (acc - V)
+struct EpiE {  // E = 2 (acc - V), or 2 (acc + X - V) for the residual memory (X: the keys, din = dv)
   float* E;
   int64_t ez;
   const void* V;
   int bf16;
   int64_t vz;  // V element stride per memory (T * dv); V already offset to the chunk
   int dv;
+  const void* X;  // null unless residual; same layout as V
   __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    const float vv = load_in(V, (int64_t)z * vz + (int64_t)row * dv + col, bf16);
-    E[(int64_t)z * ez + (int64_t)row * dv + col] = 2.0f * (v - vv);
+    const int64_t i = (int64_t)z * vz + (int64_t)row * dv + col;
+    const float vv = load_in(V, i, bf16);
+    const float xv = X ? load_in(X, i, bf16) : 0.0f;
+    E[(int64_t)z * ez + (int64_t)row * dv + col] = 2.0f * (v + xv - vv);
   }
 };
 struct EpiPD1 {  // P = acc, D1 = acc * silu'(Z)
@@ -166,6 +170,20 @@ struct EpiScaleSp {  // out = acc * silu'(Z[row + zr0])
   __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
     out[(int64_t)z * oz + (int64_t)row * dh + col] =
         v * silu_primef_(Z[(int64_t)z * zz + (int64_t)(zr0 + row) * dh + col]);
+  }
+};
+
+struct EpiStAdd {  // out = acc (+ scale * add[z * az + row * ald + col] when add is given)
+  float* out;
+  int64_t sz;
+  int ld;
+  const float* add;
+  int64_t az;
+  int ald;
+  float scale;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    if (add) v += scale * add[(int64_t)z * az + (int64_t)row * ald + col];
+    out[(int64_t)z * sz + (int64_t)row * ld + col] = v;
   }
 };
 
@@ -614,7 +632,7 @@ static atlasmem_status ns_backward(const Dims& d, float* ws, const NsLay& n, con
 }
 
 bool backward_supported(const Dims& d) {
-  return d.kind == ATLASMEM_MLP2_SILU && !d.residual && !d.gated && !d.ptr && d.c == 1 && d.poly == 1 &&
+  return d.kind == ATLASMEM_MLP2_SILU && !d.gated && !d.ptr && d.c == 1 && d.poly == 1 &&
          (d.gate_mode == ATLASMEM_PER_CHUNK || d.ns_steps == 0);
 }
 
@@ -699,7 +717,9 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat la = bk::cat1(bk::src(Zk, 0, zz, dh, 1, C, dh, 1));
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh));
       launch_gemm<false, false>(true, C, dv, dh, M, la, lb,
-                                bk::EpiE{E, vz, (const char*)V + s * dv * esz, bf, T * dv, dv}, st);
+                                bk::EpiE{E, vz, (const char*)V + s * dv * esz, bf, T * dv, dv,
+                                         d.residual ? (const void*)Kc : nullptr},
+                                st);
     }
     // P = E W2, D1 = P silu'(Z)
     {
@@ -796,7 +816,8 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       const bk::Src za = bk::src(Pz, 0, hz, dh, 1, C, dh);
       const bk::Src wa = bk::src(WAg, 0, P, 1, din, din, dh);  // B(k=h, j=f) = M[h][f]
       const bk::Src w1 = bk::src(cW1, 0, 2 * P, 1, din, din, dh);
-      const bk::EpiSt out{dK + s * din, T * din, din};
+      // the residual memory's keys also enter E directly: + 2 E' (E' in U2, din = dv)
+      const bk::EpiStAdd out{dK + s * din, T * din, din, d.residual ? U2 : nullptr, vz, dv, 2.0f};
       if (per_chunk) {
         launch_gemm<false, false>(true, C, din, 2 * dh, M, bk::cat2(da, za, dh), bk::cat2(wa, w1, dh), out, st);
       } else {
@@ -812,7 +833,11 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       launch_gemm<false, false>(true, C, dh, dv, M, la, lb, bk::EpiScaleSp{Zqa, Zk, hz, zz, C, dh}, st);
       bk::Cat la2 = bk::cat1(bk::src(Zqa, 0, hz, dh, 1, C, dh));
       bk::Cat lb2 = bk::cat1(bk::src(cW1, 0, 2 * P, 1, din, din, dh));
-      launch_gemm<false, false>(true, C, din, dh, M, la2, lb2, bk::EpiSt{dQ + s * din, T * din, din}, st);
+      // the residual memory's retrieval adds the query: + dY
+      launch_gemm<false, false>(true, C, din, dh, M, la2, lb2,
+                                bk::EpiStAdd{dQ + s * din, T * din, din, d.residual ? dY + s * dv : nullptr, T * dv,
+                                             dv, 1.0f},
+                                st);
     }
     // W1' = Z'^T X + Zq'^T Q -> Wb   (A(i=h, k=row), B(k=row, j=f))
     {

@@ -29,6 +29,10 @@ CASES = [
     # neither transposed
     ("ns5_none_transposed", 4, "literal", dict(batch=2, heads=1, T=96, d_key=56, d_value=20, d_hidden=36, chunk=32)),
     ("per_chunk_no_ns", 4, "literal", dict(batch=2, heads=1, T=256, ns_steps=0)),
+    # the residual memory x + W2 silu(W1 x): keys in the error, queries in the output
+    ("residual_per_token_C16", 1, "stabilised", dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, heads=2, T=48, d_key=24,
+                                                      d_value=24, d_hidden=40, chunk=16)),
+    ("residual_ns5_per_chunk", 4, "literal", dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, heads=2, T=256)),
 ]
 
 
