@@ -431,35 +431,78 @@ __global__ void dot_kernel(const float* __restrict__ a, int64_t za, const float*
   if (threadIdx.x == 0) out[z] = red[0] + red[1] + red[2] + red[3];
 }
 
-// X0 = G / (|G| + eps), in the working orientation (transposed when rows > cols): out is
-// [M][r][c] with (r, c) = tr ? (cols, rows) : (rows, cols).
-__global__ void ns_init_kernel(const float* __restrict__ G, int64_t gz, int rows, int cols, int tr,
-                               const float* __restrict__ sq, float eps, float* __restrict__ X, int64_t xz, int M) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n = (int64_t)rows * cols;
-  if (i >= (int64_t)M * n) return;
+// Geometry of one Newton-Schulz batch: slab z is matrix z / M (of nm matrices that share the
+// working shape r x c) of memory z % M.  Matrix i lies at goff[i] in a memory's P parameters as
+// rows x cols; its working orientation is transposed when rows > cols.
+struct NsGeo {
+  int M, nm;
+  int64_t P;
+  int64_t goff[2];
+  int rows[2], cols[2], tr[2];
+};
+
+// Element i of the batch (slab z, element e of the matrix in its own orientation): its index in
+// the parameter layout and in a working slab of stride xz.
+struct NsIdx {
+  int64_t z, g, w;
+};
+__device__ __forceinline__ NsIdx ns_idx(const NsGeo& g, int64_t i, int64_t n, int64_t xz) {
   const int64_t z = i / n, e = i - z * n;
-  const int r = (int)(e / cols), c = (int)(e - (int64_t)r * cols);
-  const float inv = 1.0f / (sqrtf(sq[z]) + eps);
-  const float v = G[z * gz + e] * inv;
-  if (tr) X[z * xz + (int64_t)c * rows + r] = v;
-  else X[z * xz + e] = v;
+  const int mi = (int)(z / g.M);
+  const int64_t zm = z - (int64_t)mi * g.M;
+  const int r = (int)(e / g.cols[mi]), c = (int)(e - (int64_t)r * g.cols[mi]);
+  return NsIdx{z, zm * g.P + g.goff[mi] + e, z * xz + (g.tr[mi] ? (int64_t)c * g.rows[mi] + r : e)};
+}
+
+// |G|^2 of every slab (one block each)
+__global__ void ns_gsq_kernel(NsGeo g, const float* __restrict__ G, float* __restrict__ out) {
+  __shared__ float red[4];
+  const int z = blockIdx.x, mi = z / g.M;
+  const float* p = G + (int64_t)(z - mi * g.M) * g.P + g.goff[mi];
+  const int64_t n = (int64_t)g.rows[mi] * g.cols[mi];
+  float acc = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) acc += p[i] * p[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[z] = red[0] + red[1] + red[2] + red[3];
+}
+
+// X0 = G / (|G| + eps) in the working orientation.
+__global__ void ns_init_kernel(NsGeo g, const float* __restrict__ G, const float* __restrict__ sq, float eps,
+                               float* __restrict__ X, int64_t xz, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)g.nm * g.M * n) return;
+  const NsIdx x = ns_idx(g, i, n, xz);
+  X[x.w] = G[x.g] * (1.0f / (sqrtf(sq[x.z]) + eps));
 }
 
 // G' = Xa0 / n - (<Xa0, G> / n^2) G / |G|, Xa0 taken back to G's orientation; n = |G| + eps.
-// The same kernel copies a working-orientation matrix back to G's orientation when G is null.
-__global__ void ns_final_kernel(const float* __restrict__ Xa, int64_t xz, const float* __restrict__ G, int64_t gz,
-                                int rows, int cols, int tr, const float* __restrict__ sq,
-                                const float* __restrict__ dotv, float eps, float* __restrict__ Ga, int M) {
+// With G null the kernel copies a working slab back to G's orientation (Ga = Xa).
+__global__ void ns_final_kernel(NsGeo g, const float* __restrict__ Xa, int64_t xz, const float* __restrict__ G,
+                                const float* __restrict__ sq, const float* __restrict__ dotv, float eps,
+                                float* __restrict__ Ga, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n = (int64_t)rows * cols;
-  if (i >= (int64_t)M * n) return;
-  const int64_t z = i / n, e = i - z * n;
-  const int r = (int)(e / cols), c = (int)(e - (int64_t)r * cols);
-  const float gn = sqrtf(sq[z]), nn = gn + eps;
-  const float xa = tr ? Xa[z * xz + (int64_t)c * rows + r] : Xa[z * xz + e];
-  const float corr = gn > 0.0f ? dotv[z] / (nn * gn) : 0.0f;  // dotv = <Xa0, X0> = <Xa0, G> / nn
-  Ga[z * gz + e] = G ? xa / nn - corr * G[z * gz + e] : xa;
+  if (i >= (int64_t)g.nm * g.M * n) return;
+  const NsIdx x = ns_idx(g, i, n, xz);
+  const float xa = Xa[x.w];
+  if (!G) {
+    Ga[x.g] = xa;
+    return;
+  }
+  const float gn = sqrtf(sq[x.z]), nn = gn + eps;
+  const float corr = gn > 0.0f ? dotv[x.z] / (nn * gn) : 0.0f;  // dotv = <Xa0, X0> = <Xa0, G> / nn
+  Ga[x.g] = xa / nn - corr * G[x.g];
+}
+
+// A parameter-layout matrix to its working slab (the adjoint of N entering the reverse).
+__global__ void ns_to_work_kernel(NsGeo g, const float* __restrict__ in, float* __restrict__ out, int64_t xz,
+                                  int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)g.nm * g.M * n) return;
+  const NsIdx x = ns_idx(g, i, n, xz);
+  out[x.w] = in[x.g];
 }
 
 // The other direction of the orientation change: out (working, [M][r][c]) from in (G's
@@ -482,9 +525,9 @@ __global__ void to_work_kernel(const float* __restrict__ in, int64_t iz, int row
 
 // ---------------------------------------------------------------------------- host
 
-struct NsLay {  // one matrix's Newton-Schulz buffers (working orientation r x c, r <= c)
-  int rows, cols, r, c, tr;
-  int64_t goff;  // offset of the matrix inside a memory's parameters
+struct NsLay {  // Newton-Schulz buffers of g.nm matrices of one working shape r x c (r <= c), batched
+  bk::NsGeo g;
+  int r, c;
   int64_t x, a, b, xa0, xa1, ba, aa, sq, dot;
 };
 
@@ -492,6 +535,7 @@ struct BwdLayout {
   int64_t ck, wa0, wa1, sa0, sa1, wb, zk, e, pz, d1, u1, u1s, u2, u2s, zqa, cw, cs, cwa, csa, sc, sca;
   int64_t gb, nb, nab, gab, sat;
   NsLay ns[2];
+  int nns;  // Newton-Schulz batches: 1 when both matrices share a working shape, else 2
   int64_t end;
 };
 
@@ -526,6 +570,7 @@ static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
   L.sc = take(M * 3);
   L.sca = take(M * 3);
   L.gb = L.nb = L.nab = L.gab = L.sat = 0;
+  L.nns = 0;
   for (int m = 0; m < 2; ++m) L.ns[m] = NsLay{};
   if (d.gate_mode == ATLASMEM_PER_CHUNK) {
     L.gb = take(M * P);
@@ -536,24 +581,39 @@ static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
     if (d.ns_steps > 0) {
       const int steps = d.ns_steps;
       const int shp[2][2] = {{(int)dh, d.din}, {(int)dv, (int)dh}};
+      const int64_t goff[2] = {0, d.P1};
+      int wr[2], wc[2];
       for (int m = 0; m < 2; ++m) {
-        NsLay& n = L.ns[m];
-        n.rows = shp[m][0];
-        n.cols = shp[m][1];
-        n.tr = n.rows > n.cols;
-        n.r = n.tr ? n.cols : n.rows;
-        n.c = n.tr ? n.rows : n.cols;
-        n.goff = m == 0 ? 0 : d.P1;
+        wr[m] = shp[m][0] < shp[m][1] ? shp[m][0] : shp[m][1];
+        wc[m] = shp[m][0] < shp[m][1] ? shp[m][1] : shp[m][0];
+      }
+      const bool paired = wr[0] == wr[1] && wc[0] == wc[1];
+      L.nns = paired ? 1 : 2;
+      for (int b = 0; b < L.nns; ++b) {
+        NsLay& n = L.ns[b];
+        n.g.M = (int)M;
+        n.g.nm = paired ? 2 : 1;
+        n.g.P = P;
+        for (int j = 0; j < n.g.nm; ++j) {
+          const int m = paired ? j : b;
+          n.g.goff[j] = goff[m];
+          n.g.rows[j] = shp[m][0];
+          n.g.cols[j] = shp[m][1];
+          n.g.tr[j] = shp[m][0] > shp[m][1];
+        }
+        n.r = wr[b];
+        n.c = wc[b];
+        const int64_t S = (int64_t)n.g.nm * M;  // slabs
         const int64_t rc = (int64_t)n.r * n.c, rr = (int64_t)n.r * n.r;
-        n.x = take(M * (steps + 1) * rc);
-        n.a = take(M * steps * rr);
-        n.b = take(M * steps * rr);
-        n.xa0 = take(M * rc);
-        n.xa1 = take(M * rc);
-        n.ba = take(M * rr);
-        n.aa = take(M * rr);
-        n.sq = take(M);
-        n.dot = take(M);
+        n.x = take(S * (steps + 1) * rc);
+        n.a = take(S * steps * rr);
+        n.b = take(S * steps * rr);
+        n.xa0 = take(S * rc);
+        n.xa1 = take(S * rc);
+        n.ba = take(S * rr);
+        n.aa = take(S * rr);
+        n.sq = take(S);
+        n.dot = take(S);
       }
     }
   }
@@ -563,31 +623,31 @@ static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
 
 static unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
 
-// Newton-Schulz forward of one matrix of every memory, keeping its iterates: X_0 = G / (|G| + eps)
+// Newton-Schulz forward of one batch (both matrices of every memory when they share a working
+// shape, else one), keeping its iterates: X_0 = G / (|G| + eps)
 // (working orientation), A_i = X_i X_i^T, B_i = b A_i + c A_i^2, X_{i+1} = a X_i + B_i X_i; the result
 // goes back to G's orientation in N (at the matrix's offset).
 static atlasmem_status ns_forward(const Dims& d, float* ws, const NsLay& n, const float* G, float* N, hipStream_t st) {
-  const int M = d.M, steps = d.ns_steps, r = n.r, c = n.c;
-  const int64_t P = d.P, rc = (int64_t)r * c, rr = (int64_t)r * r;
+  const int steps = d.ns_steps, r = n.r, c = n.c, B = n.g.nm * d.M;  // B: slabs of the batch
+  const int64_t rc = (int64_t)r * c, rr = (int64_t)r * r;
   const int64_t xz = (steps + 1) * rc, az = steps * rr;
-  float *X = ws + n.x, *A = ws + n.a, *B = ws + n.b, *sq = ws + n.sq;
-  hipLaunchKernelGGL(bk::dot_kernel, dim3(M), dim3(256), 0, st, G + n.goff, P, G + n.goff, P,
-                     (int64_t)n.rows * n.cols, sq);
-  hipLaunchKernelGGL(bk::ns_init_kernel, dim3(blocks_of((int64_t)M * rc)), dim3(256), 0, st, G + n.goff, P, n.rows,
-                     n.cols, n.tr, sq, d.ns_eps, X, xz, M);
+  float *X = ws + n.x, *A = ws + n.a, *Bm = ws + n.b, *sq = ws + n.sq;
+  hipLaunchKernelGGL(bk::ns_gsq_kernel, dim3(B), dim3(256), 0, st, n.g, G, sq);
+  hipLaunchKernelGGL(bk::ns_init_kernel, dim3(blocks_of((int64_t)B * rc)), dim3(256), 0, st, n.g, G, sq, d.ns_eps, X,
+                     xz, rc);
   AM_LAUNCH_CHECK();
   for (int i = 0; i < steps; ++i) {
-    float *Xi = X + i * rc, *Xn = X + (i + 1) * rc, *Ai = A + i * rr, *Bi = B + i * rr;
-    launch_gemm<false, false>(true, r, r, c, M, bk::cat1(bk::src(Xi, 0, xz, c, 1, r, c)),
+    float *Xi = X + i * rc, *Xn = X + (i + 1) * rc, *Ai = A + i * rr, *Bi = Bm + i * rr;
+    launch_gemm<false, false>(true, r, r, c, B, bk::cat1(bk::src(Xi, 0, xz, c, 1, r, c)),
                               bk::cat1(bk::src(Xi, 0, xz, c, 1, r, c)), bk::EpiSt{Ai, az, r}, st);
-    launch_gemm<false, false>(true, r, r, r, M, bk::cat1(bk::src(Ai, 0, az, r, 1, r, r)),
+    launch_gemm<false, false>(true, r, r, r, B, bk::cat1(bk::src(Ai, 0, az, r, 1, r, r)),
                               bk::cat1(bk::src(Ai, 0, az, 1, r, r, r)), bk::EpiAxpy{Bi, Ai, az, r, d.ns_b, d.ns_c},
                               st);
-    launch_gemm<false, false>(true, r, c, r, M, bk::cat1(bk::src(Bi, 0, az, r, 1, r, r)),
+    launch_gemm<false, false>(true, r, c, r, B, bk::cat1(bk::src(Bi, 0, az, r, 1, r, r)),
                               bk::cat1(bk::src(Xi, 0, xz, 1, c, c, r)), bk::EpiAxpy{Xn, Xi, xz, c, d.ns_a, 1.0f}, st);
   }
-  hipLaunchKernelGGL(bk::ns_final_kernel, dim3(blocks_of((int64_t)M * rc)), dim3(256), 0, st, X + steps * rc, xz,
-                     (const float*)nullptr, P, n.rows, n.cols, n.tr, sq, sq, d.ns_eps, N + n.goff, M);
+  hipLaunchKernelGGL(bk::ns_final_kernel, dim3(blocks_of((int64_t)B * rc)), dim3(256), 0, st, n.g, X + steps * rc,
+                     xz, (const float*)nullptr, sq, sq, d.ns_eps, N, rc);
   AM_LAUNCH_CHECK();
   return ATLASMEM_OK;
 }
@@ -597,36 +657,35 @@ static atlasmem_status ns_forward(const Dims& d, float* ws, const NsLay& n, cons
 //   then G' = Xa0 / n - (<Xa0, G> / n^2) G / |G|.
 static atlasmem_status ns_backward(const Dims& d, float* ws, const NsLay& n, const float* G, const float* Na,
                                    float* Ga, hipStream_t st) {
-  const int M = d.M, steps = d.ns_steps, r = n.r, c = n.c;
-  const int64_t P = d.P, rc = (int64_t)r * c, rr = (int64_t)r * r;
+  const int steps = d.ns_steps, r = n.r, c = n.c, B = n.g.nm * d.M;
+  const int64_t rc = (int64_t)r * c, rr = (int64_t)r * r;
   const int64_t xz = (steps + 1) * rc, az = steps * rr;
-  float *X = ws + n.x, *A = ws + n.a, *B = ws + n.b, *Ba = ws + n.ba, *Aa = ws + n.aa;
+  float *X = ws + n.x, *A = ws + n.a, *Bm = ws + n.b, *Ba = ws + n.ba, *Aa = ws + n.aa;
   float* xa = ws + n.xa0;
   float* xn = ws + n.xa1;
-  hipLaunchKernelGGL(bk::to_work_kernel, dim3(blocks_of((int64_t)M * rc)), dim3(256), 0, st, Na + n.goff, P, n.rows,
-                     n.cols, n.tr, (const float*)nullptr, (int64_t)0, (int64_t)0, 1.0f, xa, rc, M);
+  hipLaunchKernelGGL(bk::ns_to_work_kernel, dim3(blocks_of((int64_t)B * rc)), dim3(256), 0, st, n.g, Na, xa, rc, rc);
   AM_LAUNCH_CHECK();
   for (int i = steps - 1; i >= 0; --i) {
-    float *Xi = X + i * rc, *Ai = A + i * rr, *Bi = B + i * rr;
-    launch_gemm<false, false>(true, r, r, c, M, bk::cat1(bk::src(xa, 0, rc, c, 1, r, c)),
+    float *Xi = X + i * rc, *Ai = A + i * rr, *Bi = Bm + i * rr;
+    launch_gemm<false, false>(true, r, r, c, B, bk::cat1(bk::src(xa, 0, rc, c, 1, r, c)),
                               bk::cat1(bk::src(Xi, 0, xz, c, 1, r, c)), bk::EpiSt{Ba, rr, r}, st);
-    launch_gemm<false, false>(true, r, c, r, M, bk::cat1(bk::src(Bi, 0, az, r, 1, r, r)),
+    launch_gemm<false, false>(true, r, c, r, B, bk::cat1(bk::src(Bi, 0, az, r, 1, r, r)),
                               bk::cat1(bk::src(xa, 0, rc, 1, c, c, r)), bk::EpiAxpy{xn, xa, rc, c, d.ns_a, 1.0f}, st);
     launch_gemm<false, false>(
-        true, r, r, 2 * r, M, bk::cat2(bk::src(Ba, 0, rr, r, 1, r, r), bk::src(Ai, 0, az, r, 1, r, r), r),
+        true, r, r, 2 * r, B, bk::cat2(bk::src(Ba, 0, rr, r, 1, r, r), bk::src(Ai, 0, az, r, 1, r, r), r),
         bk::cat2(bk::src(Ai, 0, az, 1, r, r, r), bk::src(Ba, 0, rr, 1, r, r, r), r),
         bk::EpiAxpy{Aa, Ba, rr, r, d.ns_b, d.ns_c}, st);
     launch_gemm<false, false>(
-        true, r, c, 2 * r, M, bk::cat2(bk::src(Aa, 0, rr, r, 1, r, r), bk::src(Aa, 0, rr, 1, r, r, r), r),
+        true, r, c, 2 * r, B, bk::cat2(bk::src(Aa, 0, rr, r, 1, r, r), bk::src(Aa, 0, rr, 1, r, r, r), r),
         bk::cat2(bk::src(Xi, 0, xz, 1, c, c, r), bk::src(Xi, 0, xz, 1, c, c, r), r), bk::EpiAcc{xn, rc, c}, st);
     float* t = xa;
     xa = xn;
     xn = t;
   }
-  hipLaunchKernelGGL(bk::dot_kernel, dim3(M), dim3(256), 0, st, xa, rc, X, xz, rc, ws + n.dot);  // <Xa0, X_0>
+  hipLaunchKernelGGL(bk::dot_kernel, dim3(B), dim3(256), 0, st, xa, rc, X, xz, rc, ws + n.dot);  // <Xa0, X_0>
   AM_LAUNCH_CHECK();
-  hipLaunchKernelGGL(bk::ns_final_kernel, dim3(blocks_of((int64_t)M * rc)), dim3(256), 0, st, xa, rc, G + n.goff,
-                     P, n.rows, n.cols, n.tr, ws + n.sq, ws + n.dot, d.ns_eps, Ga + n.goff, M);
+  hipLaunchKernelGGL(bk::ns_final_kernel, dim3(blocks_of((int64_t)B * rc)), dim3(256), 0, st, n.g, xa, rc, G,
+                     ws + n.sq, ws + n.dot, d.ns_eps, Ga, rc);
   AM_LAUNCH_CHECK();
   return ATLASMEM_OK;
 }
@@ -742,7 +801,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       AM_LAUNCH_CHECK();
       const float* N = Gb;
       if (d.ns_steps > 0) {
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < L.nns; ++m)
           if ((stt = ns_forward(d, ws, L.ns[m], Gb, Nb, st)) != ATLASMEM_OK) return stt;
         N = Nb;
       }
@@ -753,7 +812,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
                          theta, nch, k, -1.0f, NAb, P, M);
       AM_LAUNCH_CHECK();
       if (d.ns_steps > 0) {
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < L.nns; ++m)
           if ((stt = ns_backward(d, ws, L.ns[m], Gb, NAb, GAb, st)) != ATLASMEM_OK) return stt;
         WAg = SAg = GAb;
       } else {
