@@ -65,12 +65,16 @@ def _newton_schulz(g, steps, coeffs, eps):
     return x.T if tr else x
 
 
-def run_memory_torch(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha):
-    """The literal chunked recurrence for one memory (window 1, identity features; per-token
-    gates, or per-chunk gates with an optional Newton-Schulz orthogonalisation of the summed
-    chunk gradient) with torch tensors: Y, final params, final momenta.  Plain, residual or
-    linear memory."""
-    assert cfg.omega_window == 1 and cfg.poly_degree == 1
+def run_memory_torch(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, gamma=None):
+    """The literal chunked recurrence for one memory (identity features; per-token gates with an
+    Omega window of c tokens, or per-chunk gates with an optional Newton-Schulz
+    orthogonalisation of the summed chunk gradient) with torch tensors: Y, final params, final
+    momenta.  Plain, residual or linear memory.  The window starts with the sequence (no history
+    from a previous call): token t's step uses sum_{i=t-c+1..t, i>=0} gamma_i g_i, every g_i taken
+    at the weights of the chunk that holds t (ATLAS summary, sections 3.2-3.3)."""
+    assert cfg.poly_degree == 1
+    c = cfg.omega_window
+    assert c == 1 or cfg.gate_mode == PER_TOKEN
     res = cfg.kind == MLP2_SILU_RESIDUAL
     W = list(params)
     S = list(momenta)
@@ -83,8 +87,14 @@ def run_memory_torch(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, al
         for t in range(s, e):
             Y.append(_apply(wb, Q[t], res))
         if cfg.gate_mode == PER_TOKEN:
+            grads = {}
             for t in range(s, e):
-                G = _grad(wb, K[t], V[t], res)
+                G = None
+                for i in range(max(t - c + 1, 0), t + 1):
+                    if i not in grads:
+                        grads[i] = _grad(wb, K[i], V[i], res)
+                    w_i = 1.0 if c == 1 else gamma[i]
+                    G = [w_i * g for g in grads[i]] if G is None else [G[m] + w_i * g for m, g in enumerate(grads[i])]
                 S = [eta[t] * S[m] - theta[t] * G[m] for m in range(len(W))]
                 W = [(1.0 - alpha[t]) * W[m] + S[m] for m in range(len(W))]
         else:
@@ -99,24 +109,29 @@ def run_memory_torch(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, al
     return torch.stack(Y), W, S
 
 
-def outer_grads(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, dY, dW_T=None, dS_T=None):
+def outer_grads(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, dY, dW_T=None, dS_T=None,
+                gamma=None):
     """Gradients of <dY, Y> + <dW_T, W_T> + <dS_T, S_T> (numpy in, numpy out, fp64):
-    dict with K, Q, V, theta, eta, alpha, W0 (list), S0 (list)."""
+    dict with K, Q, V, theta, eta, alpha, W0 (list), S0 (list), and gamma for a window > 1."""
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
     P = [t(p) for p in params]
     M = [t(m) for m in momenta]
     k, q, v, th, et, al = t(K), t(Q), t(V), t(theta), t(eta), t(alpha)
-    Y, W, S = run_memory_torch(cfg, P, M, k, q, v, th, et, al)
+    gm = t(gamma) if cfg.omega_window > 1 else None
+    Y, W, S = run_memory_torch(cfg, P, M, k, q, v, th, et, al, gm)
     L = (Y * torch.tensor(np.asarray(dY, dtype=np.float64))).sum()
     if dW_T is not None:
         L = L + sum((w * torch.tensor(np.asarray(d, dtype=np.float64))).sum() for w, d in zip(W, dW_T))
     if dS_T is not None:
         L = L + sum((m * torch.tensor(np.asarray(d, dtype=np.float64))).sum() for m, d in zip(S, dS_T))
-    grads = torch.autograd.grad(L, [k, q, v, th, et, al] + P + M, allow_unused=True)
+    extra = [gm] if gm is not None else []
+    grads = torch.autograd.grad(L, [k, q, v, th, et, al] + P + M + extra, allow_unused=True)
     z = lambda g, ref: np.zeros(ref.shape) if g is None else g.detach().numpy()
     names = ["K", "Q", "V", "theta", "eta", "alpha"]
     srcs = [k, q, v, th, et, al]
     out = {n: z(g, s) for n, g, s in zip(names, grads[:6], srcs)}
     out["W0"] = [z(g, p) for g, p in zip(grads[6:6 + len(P)], P)]
-    out["S0"] = [z(g, m) for g, m in zip(grads[6 + len(P):], M)]
+    out["S0"] = [z(g, m) for g, m in zip(grads[6 + len(P):6 + len(P) + len(M)], M)]
+    if gm is not None:
+        out["gamma"] = z(grads[-1], gm)
     return out

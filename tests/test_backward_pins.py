@@ -10,11 +10,11 @@ from oracle import LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, PER_CHUNK, PER_TOKEN, 
 from oracle import backward as bw
 
 
-def problem(seed, kind, T=8, C=4, d=3, v=2, h=5, mode=PER_TOKEN, ns=0):
+def problem(seed, kind, T=8, C=4, d=3, v=2, h=5, mode=PER_TOKEN, ns=0, c=1):
     r = np.random.default_rng(seed)
     if kind == MLP2_SILU_RESIDUAL:
         v = d  # the residual memory adds its input to its output
-    cfg = MemoryConfig(kind, d, v, h if kind != LINEAR else 0, 1, C, 1, mode, ns)
+    cfg = MemoryConfig(kind, d, v, h if kind != LINEAR else 0, 1, C, c, mode, ns)
     if kind == LINEAR:
         params = [r.normal(0, 0.5, (v, d))]
     else:
@@ -28,27 +28,31 @@ def problem(seed, kind, T=8, C=4, d=3, v=2, h=5, mode=PER_TOKEN, ns=0):
     dY = r.normal(size=(T, v))
     dW = [r.normal(size=p.shape) for p in params]
     dS = [r.normal(size=p.shape) for p in params]
-    return cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS
+    gm = r.uniform(0.2, 1.0, T) if c > 1 else None  # Omega-rule context gates
+    return cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS, gm
 
 
-def objective(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS):
-    res = oracle.run_memory(cfg, params, momenta, K, Q, V, th, et, al)
+def objective(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS, gm=None):
+    res = oracle.run_memory(cfg, params, momenta, K, Q, V, th, et, al, gm)
     return (np.sum(res.Y * dY) + sum(np.sum(a * b) for a, b in zip(res.params, dW))
             + sum(np.sum(a * b) for a, b in zip(res.momenta, dS)))
 
 
-MODES = [(LINEAR, PER_TOKEN, 0), (MLP2_SILU, PER_TOKEN, 0), (MLP2_SILU, PER_CHUNK, 0), (MLP2_SILU, PER_CHUNK, 5),
-         (LINEAR, PER_CHUNK, 5), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0), (MLP2_SILU_RESIDUAL, PER_CHUNK, 5)]
+# (kind, gate mode, Newton-Schulz steps, Omega window)
+MODES = [(LINEAR, PER_TOKEN, 0, 1), (MLP2_SILU, PER_TOKEN, 0, 1), (MLP2_SILU, PER_CHUNK, 0, 1),
+         (MLP2_SILU, PER_CHUNK, 5, 1), (LINEAR, PER_CHUNK, 5, 1), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 1),
+         (MLP2_SILU_RESIDUAL, PER_CHUNK, 5, 1), (MLP2_SILU, PER_TOKEN, 0, 3), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 2),
+         (LINEAR, PER_TOKEN, 0, 3), (MLP2_SILU, PER_TOKEN, 0, 6)]
 
 
-@pytest.mark.parametrize("kind,mode,ns", MODES)
-def test_torch_restatement_matches_oracle(kind, mode, ns):
+@pytest.mark.parametrize("kind,mode,ns,c", MODES)
+def test_torch_restatement_matches_oracle(kind, mode, ns, c):
     import torch
-    cfg, params, momenta, K, Q, V, th, et, al, *_ = problem(1, kind, T=10, C=4, h=6, mode=mode, ns=ns)
-    ref = oracle.run_memory(cfg, params, momenta, K, Q, V, th, et, al)
+    cfg, params, momenta, K, Q, V, th, et, al, _, _, _, gm = problem(1, kind, T=10, C=4, h=6, mode=mode, ns=ns, c=c)
+    ref = oracle.run_memory(cfg, params, momenta, K, Q, V, th, et, al, gm)
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
     Y, W, S = bw.run_memory_torch(cfg, [t(p) for p in params], [t(m) for m in momenta], t(K), t(Q), t(V), t(th),
-                                  t(et), t(al))
+                                  t(et), t(al), None if gm is None else t(gm))
     np.testing.assert_allclose(Y.numpy(), ref.Y, rtol=1e-13, atol=1e-14)
     for a, b in zip(W, ref.params):
         np.testing.assert_allclose(a.numpy(), b, rtol=1e-13, atol=1e-14)
@@ -56,16 +60,19 @@ def test_torch_restatement_matches_oracle(kind, mode, ns):
         np.testing.assert_allclose(a.numpy(), b, rtol=1e-13, atol=1e-14)
 
 
-@pytest.mark.parametrize("kind,mode,ns", MODES)
-def test_outer_gradients_against_finite_differences(kind, mode, ns):
+@pytest.mark.parametrize("kind,mode,ns,c", MODES)
+def test_outer_gradients_against_finite_differences(kind, mode, ns, c):
     """<grad, delta> against (L(x + h delta) - L(x - h delta)) / 2h with L from the numpy oracle,
     for a random direction in every input group (a wrong sign, index or dropped term in any
     group changes its directional derivative)."""
-    cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS = problem(2, kind, T=9, C=4, h=6, mode=mode, ns=ns)
-    g = bw.outer_grads(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS)
+    cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS, gm = problem(2, kind, T=9, C=4, h=6, mode=mode, ns=ns,
+                                                                        c=c)
+    g = bw.outer_grads(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS, gamma=gm)
     r = np.random.default_rng(3)
-    args = dict(params=params, momenta=momenta, K=K, Q=Q, V=V, th=th, et=et, al=al)
+    args = dict(params=params, momenta=momenta, K=K, Q=Q, V=V, th=th, et=et, al=al, gm=gm)
     groups = [("K", "K"), ("Q", "Q"), ("V", "V"), ("theta", "th"), ("eta", "et"), ("alpha", "al")]
+    if c > 1:
+        groups.append(("gamma", "gm"))
     hstep = 1e-6
     for gname, aname in groups:
         d = r.normal(size=np.shape(args[aname]))
@@ -88,7 +95,7 @@ def test_outer_gradients_against_finite_differences(kind, mode, ns):
 
 
 def test_zero_adjoints_give_zero_gradients():
-    cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS = problem(4, MLP2_SILU)
+    cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS, _ = problem(4, MLP2_SILU)
     g = bw.outer_grads(cfg, params, momenta, K, Q, V, th, et, al, np.zeros_like(dY))
     for k in ("K", "Q", "V", "theta", "eta", "alpha"):
         assert not np.any(g[k])
