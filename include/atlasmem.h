@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ATLASMEM_ABI_VERSION 1
+#define ATLASMEM_ABI_VERSION 2
 
 typedef enum {
   ATLASMEM_OK = 0,
@@ -245,25 +245,30 @@ atlasmem_status atlasmem_newton_schulz(const float* G, int64_t n_mat, int32_t ro
  * final state, with respect to every input of the update and the state it started from
  * (Atlas-Torch README, "How the memory works": the outer loop trains through the inner updates;
  * the derivative of the recurrence includes that of the inner gradient).
- * Scope: MLP2_SILU or MLP2_SILU_RESIDUAL, omega_window 1, poly_degree 1, no per-token retrieval,
- * and either PER_TOKEN gates (ns_steps 0) or PER_CHUNK gates with or without the Newton-Schulz
- * orthogonalisation of the chunk gradient (its iteration differentiated step by step)
- * (E_UNSUPPORTED otherwise);
+ * Scope: MLP2_SILU or MLP2_SILU_RESIDUAL, poly_degree 1, no per-token retrieval, and either
+ * PER_TOKEN gates (ns_steps 0) with any Omega window, or PER_CHUNK gates (window 1) with or
+ * without the Newton-Schulz orthogonalisation of the chunk gradient (its iteration
+ * differentiated step by step) (E_UNSUPPORTED otherwise).  With a window > 1 the c - 1 rows of
+ * window history the call starts with are constants of the call: gradients flow to this call's
+ * tokens only (ATLAS summary, sections 3.2-3.3: the Omega rule over a sliding window);
  * T a multiple of the chunk and nothing pending (E_SHAPE otherwise).
  *   theta, eta, alpha: as in atlasmem_update_chunked ([M, T] per token, [M, T/C] per chunk)
+ *   gamma: fp32 [M, T], the Omega-rule gates (window > 1; ignored, may be NULL, otherwise)
  *   dY: fp32 [M, T, d_value];  dW_T, dS_T: fp32 [M, P] or NULL (zero)
  *   workspace: device memory of atlasmem_backward_workspace_bytes(h, T) bytes (the chunk-start
  *          states of the forward and the backward's buffers); the call allocates nothing
  *   dK, dQ: fp32 [M, T, d_key]; dV: fp32 [M, T, d_value];
- *   dtheta, deta, dalpha: fp32, the gates' shape ([M, T] or [M, T/C]);
+ *   dtheta, deta, dalpha: fp32, the gates' shape ([M, T] or [M, T/C]); dgamma: fp32 [M, T]
+ *          (window > 1; may be NULL otherwise);
  *   dW0, dS0: fp32 [M, P] (gradients with respect to the state at the start of the call) */
 int64_t atlasmem_backward_workspace_bytes(atlasmem_handle h, int64_t T);
 atlasmem_status atlasmem_update_backward(atlasmem_handle h, const void* K, const void* Q, const void* V,
-                                         const float* theta, const float* eta, const float* alpha, int64_t T,
-                                         void* Y, const float* dY, const float* dW_T, const float* dS_T,
-                                         void* workspace, int64_t workspace_bytes, float* dK, float* dQ,
-                                         float* dV, float* dtheta, float* deta, float* dalpha, float* dW0,
-                                         float* dS0, void* stream);
+                                         const float* theta, const float* eta, const float* alpha,
+                                         const float* gamma, int64_t T, void* Y, const float* dY,
+                                         const float* dW_T, const float* dS_T, void* workspace,
+                                         int64_t workspace_bytes, float* dK, float* dQ, float* dV, float* dtheta,
+                                         float* deta, float* dalpha, float* dgamma, float* dW0, float* dS0,
+                                         void* stream);
 
 /* Feature map of n rows of width d: every monomial of degree 0..degree (degree 1..3), degree-major
  * and in combinations_with_replacement order inside a degree, the degree-k monomials multiplied

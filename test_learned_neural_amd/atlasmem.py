@@ -21,7 +21,7 @@ F32, BF16 = 0, 1
 PREC_AUTO, PREC_BF16, PREC_BF16X3 = 0, 1, 2
 FLAG_NO_FUSED = 1
 FLAG_PER_TOKEN_RETRIEVE = 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTS = (
     "atlasmem_abi_version", "atlasmem_status_string", "atlasmem_param_count", "atlasmem_create",
@@ -88,7 +88,7 @@ def load():
         "atlasmem_gates": ([_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
         "atlasmem_feature_map": ([_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
         "atlasmem_backward_workspace_bytes": ([_vp, _i64], _i64),
-        "atlasmem_update_backward": ([_vp] * 7 + [_i64] + [_vp] * 5 + [_i64] + [_vp] * 9, ctypes.c_int),
+        "atlasmem_update_backward": ([_vp] * 8 + [_i64] + [_vp] * 5 + [_i64] + [_vp] * 10, ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -170,11 +170,12 @@ class Memory:
         return int(load().atlasmem_backward_workspace_bytes(self._h, int(T)))
 
     def update_backward(self, K, Q, V, theta, eta, alpha, T: int, dY, dK, dQ, dV, dtheta, deta, dalpha, dW0, dS0,
-                        workspace, Y=None, dW_T=None, dS_T=None, stream=None):
+                        workspace, Y=None, dW_T=None, dS_T=None, gamma=None, dgamma=None, stream=None):
         _check(load().atlasmem_update_backward(
-            self._h, _ptr(K), _ptr(Q), _ptr(V), _ptr(theta), _ptr(eta), _ptr(alpha), int(T), _ptr(Y), _ptr(dY),
-            _ptr(dW_T), _ptr(dS_T), _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(dK),
-            _ptr(dQ), _ptr(dV), _ptr(dtheta), _ptr(deta), _ptr(dalpha), _ptr(dW0), _ptr(dS0), _stream(stream)),
+            self._h, _ptr(K), _ptr(Q), _ptr(V), _ptr(theta), _ptr(eta), _ptr(alpha), _ptr(gamma), int(T), _ptr(Y),
+            _ptr(dY), _ptr(dW_T), _ptr(dS_T), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+            _ptr(dK), _ptr(dQ), _ptr(dV), _ptr(dtheta), _ptr(deta), _ptr(dalpha), _ptr(dgamma), _ptr(dW0), _ptr(dS0),
+            _stream(stream)),
             "atlasmem_update_backward")
 
     def retrieve(self, Q, T: int, Y, stream=None):

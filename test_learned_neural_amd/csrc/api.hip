@@ -608,10 +608,11 @@ int64_t atlasmem_backward_workspace_bytes(atlasmem_handle hh, int64_t T) {
 }
 
 atlasmem_status atlasmem_update_backward(atlasmem_handle hh, const void* K, const void* Q, const void* V,
-                                         const float* theta, const float* eta, const float* alpha, int64_t T,
-                                         void* Y, const float* dY, const float* dW_T, const float* dS_T,
-                                         void* workspace, int64_t workspace_bytes, float* dK, float* dQ, float* dV,
-                                         float* dtheta, float* deta, float* dalpha, float* dW0, float* dS0,
+                                         const float* theta, const float* eta, const float* alpha,
+                                         const float* gamma, int64_t T, void* Y, const float* dY,
+                                         const float* dW_T, const float* dS_T, void* workspace,
+                                         int64_t workspace_bytes, float* dK, float* dQ, float* dV, float* dtheta,
+                                         float* deta, float* dalpha, float* dgamma, float* dW0, float* dS0,
                                          void* stream) {
   Handle* h = (Handle*)hh;
   if (!h || T < 0) return ATLASMEM_E_INVALID;
@@ -620,13 +621,13 @@ atlasmem_status atlasmem_update_backward(atlasmem_handle hh, const void* K, cons
   if (T % d.C != 0 || h->pending != 0) return ATLASMEM_E_SHAPE;
   if (T == 0) return ATLASMEM_OK;
   if (!K || !Q || !V || !theta || !eta || !alpha || !dY || !workspace || !dK || !dQ || !dV || !dtheta || !deta ||
-      !dalpha || !dW0 || !dS0)
+      !dalpha || !dW0 || !dS0 || (d.c > 1 && (!gamma || !dgamma)))
     return ATLASMEM_E_INVALID;
   if (workspace_bytes < backward_workspace_bytes(d, T)) return ATLASMEM_E_INVALID;
   DeviceGuard g(h->device);
   if (!g.ok) return ATLASMEM_E_DEVICE;
-  return backward(h, K, Q, V, theta, eta, alpha, T, Y, dY, dW_T, dS_T, workspace, dK, dQ, dV, dtheta, deta, dalpha,
-                  dW0, dS0, S(stream));
+  return backward(h, K, Q, V, theta, eta, alpha, gamma, T, Y, dY, dW_T, dS_T, workspace, dK, dQ, dV, dtheta, deta,
+                  dalpha, dgamma, dW0, dS0, S(stream));
 }
 
 }  // extern "C"

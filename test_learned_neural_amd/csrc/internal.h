@@ -123,9 +123,9 @@ atlasmem_status launch_decode(Handle* h, const void* Q, const void* K, const voi
                               const float* eta, const float* alpha, const float* gamma, int64_t ld, int64_t n,
                               void* Y, bool append, hipStream_t st);
 atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V, const float* theta, const float* eta,
-                         const float* alpha, int64_t T, void* Y, const float* dY, const float* dWT, const float* dST,
-                         void* workspace, float* dK, float* dQ, float* dV, float* dth, float* det, float* dal,
-                         float* dW0, float* dS0, hipStream_t st);
+                         const float* alpha, const float* gamma, int64_t T, void* Y, const float* dY,
+                         const float* dWT, const float* dST, void* workspace, float* dK, float* dQ, float* dV,
+                         float* dth, float* det, float* dal, float* dgamma, float* dW0, float* dS0, hipStream_t st);
 
 
 

@@ -143,13 +143,19 @@ struct EpiEa {  // Ea = Eg + acc (in place), dV = -2 Ea
   float* Ea;
   int64_t ez;
   float* dV;
-  int64_t vz;  // dV already offset to the chunk
+  int64_t vz;  // dV already offset to the chunk (acc = 0) or not (acc = 1)
   int dv;
+  int64_t tau0;  // acc = 1: row r is token tau0 + r; tokens before 0 are dropped, the rest accumulate
+  int acc;
   __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
     float* p = Ea + (int64_t)z * ez + (int64_t)row * dv + col;
     const float e = *p + v;
     *p = e;
-    dV[(int64_t)z * vz + (int64_t)row * dv + col] = -2.0f * e;
+    if (!acc) {
+      dV[(int64_t)z * vz + (int64_t)row * dv + col] = -2.0f * e;
+    } else if (tau0 + row >= 0) {
+      dV[(int64_t)z * vz + (tau0 + row) * dv + col] += -2.0f * e;
+    }
   }
 };
 struct EpiZa {  // Za = Za1 + acc * silu'(Z) (in place)
@@ -181,9 +187,15 @@ struct EpiStAdd {  // out = acc (+ scale * add[z * az + row * ald + col] when ad
   int64_t az;
   int ald;
   float scale;
+  int64_t tau0;  // acc = 1: row r goes to row tau0 + r of out, accumulated; rows before 0 dropped
+  int acc;
   __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
     if (add) v += scale * add[(int64_t)z * az + (int64_t)row * ald + col];
-    out[(int64_t)z * sz + (int64_t)row * ld + col] = v;
+    if (!acc) {
+      out[(int64_t)z * sz + (int64_t)row * ld + col] = v;
+    } else if (tau0 + row >= 0) {
+      out[(int64_t)z * sz + (tau0 + row) * ld + col] += v;
+    }
   }
 };
 
@@ -357,6 +369,71 @@ __global__ void state_adj_kernel(const float* __restrict__ WA, const float* __re
   const float wa = WA[i];
   WAn[i] = beta * wa + Wb[i];
   SAn[i] = aS * wa + pc * SA[i];
+}
+
+// Omega window (per-token gates, window c): key row r of the chunk at token s is token
+// tau = s - (c - 1) + r; rows before the call come from the window history the call started with
+// (hk, hv, hg: [M][c - 1][*], oldest first).  Keys, values and gamma of the R rows to fp32 staging.
+__global__ void stage_rows_kernel(const void* __restrict__ K, const void* __restrict__ V,
+                                  const float* __restrict__ gamma, int bf16, int64_t T, int64_t s, int c, int R,
+                                  int dk, int dv, const float* __restrict__ hk, const float* __restrict__ hv,
+                                  const float* __restrict__ hg, float* __restrict__ ks, float* __restrict__ vs,
+                                  float* __restrict__ gs) {
+  const int r = blockIdx.x, z = blockIdx.y, H = c - 1;
+  const int64_t tau = s - H + r;
+  const int64_t row = (int64_t)z * R + r;
+  for (int e = threadIdx.x; e < dk; e += blockDim.x)
+    ks[row * dk + e] = tau >= 0 ? load_in(K, ((int64_t)z * T + tau) * dk + e, bf16)
+                                : hk[((int64_t)z * H + H + tau) * dk + e];
+  for (int e = threadIdx.x; e < dv; e += blockDim.x)
+    vs[row * dv + e] = tau >= 0 ? load_in(V, ((int64_t)z * T + tau) * dv + e, bf16)
+                                : hv[((int64_t)z * H + H + tau) * dv + e];
+  if (threadIdx.x == 0) gs[row] = tau >= 0 ? gamma[(int64_t)z * T + tau] : hg[(int64_t)z * H + H + tau];
+}
+
+// The coefficients of the key rows' gradients: g_r enters every step t of the chunk whose window
+// holds it, so oW_r = gamma_r * sum_{t = max(j, 0)}^{min(j + c - 1, C - 1)} cW_t with j = r - (c - 1)
+// (oS likewise); the window sums are kept for the adjoint.
+__global__ void omega_coef_kernel(const float* __restrict__ cW, const float* __restrict__ cS,
+                                  const float* __restrict__ gs, int C, int c, int R, int M, float* __restrict__ oW,
+                                  float* __restrict__ oS, float* __restrict__ sW, float* __restrict__ sS) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * R) return;
+  const int64_t z = i / R;
+  const int r = (int)(i - z * R), j = r - (c - 1);
+  const int t0 = j > 0 ? j : 0, t1 = j + c - 1 < C - 1 ? j + c - 1 : C - 1;
+  float a = 0.0f, b = 0.0f;
+  for (int t = t0; t <= t1; ++t) {
+    a += cW[z * C + t];
+    b += cS[z * C + t];
+  }
+  sW[i] = a;
+  sS[i] = b;
+  oW[i] = gs[i] * a;
+  oS[i] = gs[i] * b;
+}
+
+// Its adjoint: cW'_t = sum_{r = t}^{t + c - 1} gamma_r oW'_r (cS' likewise) for the chunk's C tokens,
+// and gamma'_r += oW'_r sW_r + oS'_r sS_r for the rows that are tokens of the call.
+__global__ void omega_adj_kernel(const float* __restrict__ oWa, const float* __restrict__ oSa,
+                                 const float* __restrict__ gs, const float* __restrict__ sW,
+                                 const float* __restrict__ sS, int C, int c, int R, int M, int64_t T, int64_t s,
+                                 float* __restrict__ cWa, float* __restrict__ cSa, float* __restrict__ dgamma) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * R) return;
+  const int64_t z = i / R;
+  const int r = (int)(i - z * R);
+  const int64_t tau = s - (c - 1) + r;
+  if (tau >= 0) dgamma[z * T + tau] += oWa[i] * sW[i] + oSa[i] * sS[i];
+  if (r < C) {
+    float a = 0.0f, b = 0.0f;
+    for (int q = r; q < r + c; ++q) {
+      a += gs[z * R + q] * oWa[z * R + q];
+      b += gs[z * R + q] * oSa[z * R + q];
+    }
+    cWa[z * C + r] = a;
+    cSa[z * C + r] = b;
+  }
 }
 
 // Fill n floats with v.
@@ -533,6 +610,8 @@ struct NsLay {  // Newton-Schulz buffers of g.nm matrices of one working shape r
 
 struct BwdLayout {
   int64_t ck, wa0, wa1, sa0, sa1, wb, zk, e, pz, d1, u1, u1s, u2, u2s, zqa, cw, cs, cwa, csa, sc, sca;
+  int64_t R;  // key rows per chunk: C, or C + c - 1 with an Omega window
+  int64_t ow, os, sw, ss, cwt, cst, ks, vs, gs, hk0, hv0, hg0;  // Omega window buffers
   int64_t gb, nb, nab, gab, sat;
   NsLay ns[2];
   int nns;  // Newton-Schulz batches: 1 when both matrices share a working shape, else 2
@@ -542,6 +621,8 @@ struct BwdLayout {
 static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
   const int64_t M = d.M, C = d.C, P = d.P, dh = d.dh, dv = d.dv;
   BwdLayout L;
+  const int64_t R = d.c > 1 ? C + d.c - 1 : C;
+  L.R = R;
   int64_t o = 0;
   auto take = [&](int64_t floats) {
     const int64_t r = o;
@@ -554,19 +635,35 @@ static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
   L.sa0 = take(M * P);
   L.sa1 = take(M * P);
   L.wb = take(M * P);
-  L.zk = take(M * 2 * C * dh);
-  L.e = take(M * C * dv);
-  L.pz = take(M * C * dh);
-  L.d1 = take(M * C * dh);
-  L.u1 = take(M * C * dh);
-  L.u1s = take(M * C * dh);
-  L.u2 = take(M * C * dv);
-  L.u2s = take(M * C * dv);
-  L.zqa = take(M * C * dh);
+  L.zk = take(M * (R + C) * dh);
+  L.e = take(M * R * dv);
+  L.pz = take(M * R * dh);
+  L.d1 = take(M * R * dh);
+  L.u1 = take(M * R * dh);
+  L.u1s = take(M * R * dh);
+  L.u2 = take(M * R * dv);
+  L.u2s = take(M * R * dv);
+  L.zqa = take(M * R * dh);
   L.cw = take(M * C);
   L.cs = take(M * C);
-  L.cwa = take(M * C);
-  L.csa = take(M * C);
+  L.cwa = take(M * R);
+  L.csa = take(M * R);
+  L.ow = L.os = L.sw = L.ss = L.cwt = L.cst = L.ks = L.vs = L.gs = L.hk0 = L.hv0 = L.hg0 = 0;
+  if (d.c > 1) {
+    const int64_t H = d.c - 1;
+    L.ow = take(M * R);
+    L.os = take(M * R);
+    L.sw = take(M * R);
+    L.ss = take(M * R);
+    L.cwt = take(M * C);
+    L.cst = take(M * C);
+    L.ks = take(M * R * d.dk);
+    L.vs = take(M * R * dv);
+    L.gs = take(M * R);
+    L.hk0 = take(M * H * d.dk);
+    L.hv0 = take(M * H * dv);
+    L.hg0 = take(M * H);
+  }
   L.sc = take(M * 3);
   L.sca = take(M * 3);
   L.gb = L.nb = L.nab = L.gab = L.sat = 0;
@@ -691,8 +788,8 @@ static atlasmem_status ns_backward(const Dims& d, float* ws, const NsLay& n, con
 }
 
 bool backward_supported(const Dims& d) {
-  return d.kind == ATLASMEM_MLP2_SILU && !d.gated && !d.ptr && d.c == 1 && d.poly == 1 &&
-         (d.gate_mode == ATLASMEM_PER_CHUNK || d.ns_steps == 0);
+  return d.kind == ATLASMEM_MLP2_SILU && !d.gated && !d.ptr && d.poly == 1 &&
+         (d.gate_mode == ATLASMEM_PER_CHUNK ? d.c == 1 : d.ns_steps == 0);
 }
 
 int64_t backward_workspace_bytes(const Dims& d, int64_t T) {
@@ -701,9 +798,9 @@ int64_t backward_workspace_bytes(const Dims& d, int64_t T) {
 }
 
 atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V, const float* theta, const float* eta,
-                         const float* alpha, int64_t T, void* Y, const float* dY, const float* dWT, const float* dST,
-                         void* workspace, float* dK, float* dQ, float* dV, float* dth, float* det, float* dal,
-                         float* dW0, float* dS0, hipStream_t st) {
+                         const float* alpha, const float* gamma, int64_t T, void* Y, const float* dY,
+                         const float* dWT, const float* dST, void* workspace, float* dK, float* dQ, float* dV,
+                         float* dth, float* det, float* dal, float* dgamma, float* dW0, float* dS0, hipStream_t st) {
   const Dims& d = h->d;
   const int M = d.M, C = d.C, dh = d.dh, dv = d.dv, din = d.din;
   const int64_t P = d.P, P1 = d.P1;
@@ -713,6 +810,24 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
   const size_t esz = bf ? 2 : 4;
   const BwdLayout L = bwd_layout(d, nch);
   float* ws = (float*)workspace;
+  const int c = d.c;
+  const bool win = c > 1;  // Omega window: key rows reach c - 1 tokens back, outputs accumulate
+  if (win) {
+    // the window history the call starts with (the forward below advances the handle's), and
+    // zeroed gradients of the rows that several chunks touch
+    const size_t H = (size_t)(c - 1) * M;
+    if (hipMemcpyAsync(ws + L.hk0, h->hk[h->hcur], sizeof(float) * H * d.dk, hipMemcpyDeviceToDevice, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(ws + L.hv0, h->hv[h->hcur], sizeof(float) * H * dv, hipMemcpyDeviceToDevice, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(ws + L.hg0, h->hg[h->hcur], sizeof(float) * H, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+        hipMemsetAsync(dK, 0, sizeof(float) * M * T * din, st) != hipSuccess ||
+        hipMemsetAsync(dV, 0, sizeof(float) * M * T * dv, st) != hipSuccess ||
+        hipMemsetAsync(dgamma, 0, sizeof(float) * M * T, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return ATLASMEM_E_DEVICE;
+    }
+  }
   // ---- forward, saving the state at every chunk start
   for (int64_t k = 0; k < nch; ++k) {
     float* ck = ws + L.ck + k * M * 2 * P;
@@ -727,7 +842,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     const int64_t go = per_chunk ? k : s;  // this chunk's gates
     const atlasmem_status stt =
         mlp_update(h, d, (const char*)K + s * d.dk * esz, (const char*)Q + s * d.dk * esz,
-                   (const char*)V + s * dv * esz, theta + go, eta + go, alpha + go, nullptr,
+                   (const char*)V + s * dv * esz, theta + go, eta + go, alpha + go, win ? gamma + s : nullptr,
                    Span{C, T, per_chunk ? nch : T}, Y ? (void*)((char*)Y + s * dv * (d.out_bf16 ? 2 : 4)) : nullptr,
                    st);
     if (stt != ATLASMEM_OK) return stt;
@@ -749,8 +864,13 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
   float *Zk = ws + L.zk, *E = ws + L.e, *Pz = ws + L.pz, *D1 = ws + L.d1, *U1 = ws + L.u1, *U1s = ws + L.u1s;
   float *U2 = ws + L.u2, *U2s = ws + L.u2s, *Zqa = ws + L.zqa, *Wb = ws + L.wb;
   float *cW = ws + L.cw, *cS = ws + L.cs, *cWa = ws + L.cwa, *cSa = ws + L.csa, *sc = ws + L.sc, *sca = ws + L.sca;
-  const int64_t zz = 2 * (int64_t)C * dh, hz = (int64_t)C * dh, vz = (int64_t)C * dv;
+  const int R = (int)L.R;  // key rows per chunk (the queries are the chunk's C rows)
+  const int64_t zz = (int64_t)(R + C) * dh, hz = (int64_t)R * dh, vz = (int64_t)R * dv;
   const int64_t inz = T * d.dk;  // input elements per memory (K, Q)
+  // per key row: the coefficients of its gradient and their adjoints (window: oW / oS over R rows)
+  const float* rW = win ? ws + L.ow : cW;
+  const float* rS = win ? ws + L.os : cS;
+  const int rld = win ? R : C;
   for (int64_t k = nch - 1; k >= 0; --k) {
     const int64_t s = k * C;
     const float* ck = ws + L.ck + k * M * 2 * P;  // [M][W | S]
@@ -758,33 +878,44 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     const float* cW2 = ck + P1;
     const char* Kc = (const char*)K + s * d.dk * esz;
     const char* Qc = (const char*)Q + s * d.dk * esz;
+    // key rows: the chunk's keys (or, with a window, the R staged rows); values likewise
+    const void* Kr = win ? (const void*)(ws + L.ks) : (const void*)Kc;
+    const int kbf = win ? 0 : bf;
+    const int64_t kz = win ? (int64_t)R * din : inz;
+    const void* Vr = win ? (const void*)(ws + L.vs) : (const void*)((const char*)V + s * dv * esz);
+    const int64_t vrz = win ? (int64_t)R * dv : T * dv;
     atlasmem_status stt = ATLASMEM_OK;
     if (!per_chunk) {
       stt = launch_gate_scan(theta, eta, alpha, M, T, s, 1, C, cW, cS, C, sc, 3, st);
       if (stt != ATLASMEM_OK) return stt;
     }
+    if (win) {
+      hipLaunchKernelGGL(bk::stage_rows_kernel, dim3(R, M), dim3(64), 0, st, K, V, gamma, bf, T, s, c, R, d.dk, dv,
+                         ws + L.hk0, ws + L.hv0, ws + L.hg0, ws + L.ks, ws + L.vs, ws + L.gs);
+      hipLaunchKernelGGL(bk::omega_coef_kernel, dim3(blocks_of((int64_t)M * R)), dim3(256), 0, st, cW, cS,
+                         ws + L.gs, C, c, R, M, ws + L.ow, ws + L.os, ws + L.sw, ws + L.ss);
+      AM_LAUNCH_CHECK();
+    }
     // Z of key and query rows
-    {  // rows [0, C) keys, [C, 2C) queries (two launches into the two halves)
-      bk::Cat lk = bk::cat1(bk::src(Kc, bf, inz, din, 1, C, din));
+    {  // rows [0, R) keys, [R, R + C) queries (two launches into the two parts)
+      bk::Cat lk = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
       bk::Cat lq = bk::cat1(bk::src(Qc, bf, inz, din, 1, C, din));
       bk::Cat lb = bk::cat1(bk::src(cW1, 0, 2 * P, din, 1, dh, din));
-      launch_gemm<false, false>(true, C, dh, din, M, lk, lb, bk::EpiSt{Zk, zz, dh}, st);
-      launch_gemm<false, false>(true, C, dh, din, M, lq, lb, bk::EpiSt{Zk + (int64_t)C * dh, zz, dh}, st);
+      launch_gemm<false, false>(true, R, dh, din, M, lk, lb, bk::EpiSt{Zk, zz, dh}, st);
+      launch_gemm<false, false>(true, C, dh, din, M, lq, lb, bk::EpiSt{Zk + (int64_t)R * dh, zz, dh}, st);
     }
     // E = 2 (H W2^T - V)
     {
-      bk::Cat la = bk::cat1(bk::src(Zk, 0, zz, dh, 1, C, dh, 1));
+      bk::Cat la = bk::cat1(bk::src(Zk, 0, zz, dh, 1, R, dh, 1));
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh));
-      launch_gemm<false, false>(true, C, dv, dh, M, la, lb,
-                                bk::EpiE{E, vz, (const char*)V + s * dv * esz, bf, T * dv, dv,
-                                         d.residual ? (const void*)Kc : nullptr},
-                                st);
+      launch_gemm<false, false>(true, R, dv, dh, M, la, lb,
+                                bk::EpiE{E, vz, Vr, kbf, vrz, dv, d.residual ? Kr : nullptr}, st);
     }
     // P = E W2, D1 = P silu'(Z)
     {
-      bk::Cat la = bk::cat1(bk::src(E, 0, vz, dv, 1, C, dv));
+      bk::Cat la = bk::cat1(bk::src(E, 0, vz, dv, 1, R, dv));
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv));  // B(k=v, j=h) = W2[v][h]
-      launch_gemm<false, false>(true, C, dh, dv, M, la, lb, bk::EpiPD1{Pz, D1, Zk, hz, zz, dh}, st);
+      launch_gemm<false, false>(true, R, dh, dv, M, la, lb, bk::EpiPD1{Pz, D1, Zk, hz, zz, dh}, st);
     }
     // Per-chunk gates: G = (D1^T X, E^T H), N = NS(G) or G, S_end = eta S - theta N,
     // W_end = (1 - alpha) W + S_end.  The adjoint of every row's gradient is G' (from N' = -theta
@@ -823,65 +954,70 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     }
     // U1 = X WA1^T, U1s = X SA1^T, U2 = H WA2^T, U2s = H SA2^T
     {
-      bk::Cat lx = bk::cat1(bk::src(Kc, bf, inz, din, 1, C, din));
-      bk::Cat lh = bk::cat1(bk::src(Zk, 0, zz, dh, 1, C, dh, 1));
-      launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(WAg, 0, P, din, 1, dh, din)),
+      bk::Cat lx = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
+      bk::Cat lh = bk::cat1(bk::src(Zk, 0, zz, dh, 1, R, dh, 1));
+      launch_gemm<false, false>(true, R, dh, din, M, lx, bk::cat1(bk::src(WAg, 0, P, din, 1, dh, din)),
                                 bk::EpiSt{U1, hz, dh}, st);
       if (!per_chunk)
-        launch_gemm<false, false>(true, C, dh, din, M, lx, bk::cat1(bk::src(SAg, 0, P, din, 1, dh, din)),
+        launch_gemm<false, false>(true, R, dh, din, M, lx, bk::cat1(bk::src(SAg, 0, P, din, 1, dh, din)),
                                   bk::EpiSt{U1s, hz, dh}, st);
-      launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(WAg + P1, 0, P, dh, 1, dv, dh)),
+      launch_gemm<false, false>(true, R, dv, dh, M, lh, bk::cat1(bk::src(WAg + P1, 0, P, dh, 1, dv, dh)),
                                 bk::EpiSt{U2, vz, dv}, st);
       if (!per_chunk)
-        launch_gemm<false, false>(true, C, dv, dh, M, lh, bk::cat1(bk::src(SAg + P1, 0, P, dh, 1, dv, dh)),
+        launch_gemm<false, false>(true, R, dv, dh, M, lh, bk::cat1(bk::src(SAg + P1, 0, P, dh, 1, dv, dh)),
                                   bk::EpiSt{U2s, vz, dv}, st);
     }
-    hipLaunchKernelGGL(bk::row_kernel, dim3(C, M), dim3(64), 0, st, Zk, zz, Pz, D1, U1, U1s, E, U2, U2s, hz, vz, dh,
-                       dv, C, cW, cS, cWa, cSa, per_chunk ? 0 : 1);
+    hipLaunchKernelGGL(bk::row_kernel, dim3(R, M), dim3(64), 0, st, Zk, zz, Pz, D1, U1, U1s, E, U2, U2s, hz, vz, dh,
+                       dv, rld, rW, rS, cWa, cSa, per_chunk ? 0 : 1);
     AM_LAUNCH_CHECK();
     // now: U1s = P', Pz = Z'_1, U2 = E'_g.  E' = E'_g + P' W2^T (in U2), dV = -2 E'
     {
-      bk::Cat la = bk::cat1(bk::src(U1s, 0, hz, dh, 1, C, dh));
+      bk::Cat la = bk::cat1(bk::src(U1s, 0, hz, dh, 1, R, dh));
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh));  // B(k=h, j=v) = W2[v][h]
-      launch_gemm<false, false>(true, C, dv, dh, M, la, lb, bk::EpiEa{U2, vz, dV + s * dv, T * dv, dv}, st);
+      const bk::EpiEa ep = win ? bk::EpiEa{U2, vz, dV, T * dv, dv, s - (c - 1), 1}
+                               : bk::EpiEa{U2, vz, dV + s * dv, T * dv, dv, 0, 0};
+      launch_gemm<false, false>(true, R, dv, dh, M, la, lb, ep, st);
     }
     // W2' = E^T P' + (2E')^T H + dY^T Hq  -> Wb + P1   (A(i=v, k=row), B(k=row, j=h))
     {
-      bk::Cat la = bk::cat3(bk::src(E, 0, vz, 1, dv, dv, C), bk::src(U2, 0, vz, 1, dv, dv, C, 0, nullptr, 0, 2.0f),
-                            bk::src(dY + s * dv, 0, T * dv, 1, dv, dv, C), C, 2 * C);
-      bk::Cat lb = bk::cat3(bk::src(U1s, 0, hz, 1, dh, dh, C), bk::src(Zk, 0, zz, 1, dh, dh, C, 1),
-                            bk::src(Zk + (int64_t)C * dh, 0, zz, 1, dh, dh, C, 1), C, 2 * C);
-      launch_gemm<false, false>(true, dv, dh, 3 * C, M, la, lb, bk::EpiSt{Wb + P1, P, dh}, st);
+      bk::Cat la = bk::cat3(bk::src(E, 0, vz, 1, dv, dv, R), bk::src(U2, 0, vz, 1, dv, dv, R, 0, nullptr, 0, 2.0f),
+                            bk::src(dY + s * dv, 0, T * dv, 1, dv, dv, C), R, 2 * R);
+      bk::Cat lb = bk::cat3(bk::src(U1s, 0, hz, 1, dh, dh, R), bk::src(Zk, 0, zz, 1, dh, dh, R, 1),
+                            bk::src(Zk + (int64_t)R * dh, 0, zz, 1, dh, dh, C, 1), R, 2 * R);
+      launch_gemm<false, false>(true, dv, dh, 2 * R + C, M, la, lb, bk::EpiSt{Wb + P1, P, dh}, st);
     }
     // H' = -(cW E) WA2 - (cS E) SA2 + (2E') W2;  Z' = Z'_1 + H' silu'(Z)  (in Pz)
     {
-      const bk::Src ea = bk::src(E, 0, vz, dv, 1, C, dv, 2, cW, C, -1.0f);
-      const bk::Src e2 = bk::src(U2, 0, vz, dv, 1, C, dv, 0, nullptr, 0, 2.0f);
+      const bk::Src ea = bk::src(E, 0, vz, dv, 1, R, dv, 2, rW, rld, -1.0f);
+      const bk::Src e2 = bk::src(U2, 0, vz, dv, 1, R, dv, 0, nullptr, 0, 2.0f);
       const bk::Src wa = bk::src(WAg + P1, 0, P, 1, dh, dh, dv);  // B(k=v, j=h) = M[v][h]
       const bk::Src w2 = bk::src(cW2, 0, 2 * P, 1, dh, dh, dv);
       if (per_chunk) {
-        launch_gemm<false, false>(true, C, dh, 2 * dv, M, bk::cat2(ea, e2, dv), bk::cat2(wa, w2, dv),
+        launch_gemm<false, false>(true, R, dh, 2 * dv, M, bk::cat2(ea, e2, dv), bk::cat2(wa, w2, dv),
                                   bk::EpiZa{Pz, Zk, hz, zz, dh}, st);
       } else {
-        launch_gemm<false, false>(true, C, dh, 3 * dv, M,
-                                  bk::cat3(ea, bk::src(E, 0, vz, dv, 1, C, dv, 2, cS, C, -1.0f), e2, dv, 2 * dv),
+        launch_gemm<false, false>(true, R, dh, 3 * dv, M,
+                                  bk::cat3(ea, bk::src(E, 0, vz, dv, 1, R, dv, 2, rS, rld, -1.0f), e2, dv, 2 * dv),
                                   bk::cat3(wa, bk::src(SAg + P1, 0, P, 1, dh, dh, dv), w2, dv, 2 * dv),
                                   bk::EpiZa{Pz, Zk, hz, zz, dh}, st);
       }
     }
     // X' = -(cW D1) WA1 - (cS D1) SA1 + Z' W1 -> dK rows
     {
-      const bk::Src da = bk::src(D1, 0, hz, dh, 1, C, dh, 2, cW, C, -1.0f);
-      const bk::Src za = bk::src(Pz, 0, hz, dh, 1, C, dh);
+      const bk::Src da = bk::src(D1, 0, hz, dh, 1, R, dh, 2, rW, rld, -1.0f);
+      const bk::Src za = bk::src(Pz, 0, hz, dh, 1, R, dh);
       const bk::Src wa = bk::src(WAg, 0, P, 1, din, din, dh);  // B(k=h, j=f) = M[h][f]
       const bk::Src w1 = bk::src(cW1, 0, 2 * P, 1, din, din, dh);
       // the residual memory's keys also enter E directly: + 2 E' (E' in U2, din = dv)
-      const bk::EpiStAdd out{dK + s * din, T * din, din, d.residual ? U2 : nullptr, vz, dv, 2.0f};
+      const bk::EpiStAdd out = win ? bk::EpiStAdd{dK, T * din, din, d.residual ? U2 : nullptr, vz, dv, 2.0f,
+                                                  s - (c - 1), 1}
+                                   : bk::EpiStAdd{dK + s * din, T * din, din, d.residual ? U2 : nullptr, vz, dv,
+                                                  2.0f, 0, 0};
       if (per_chunk) {
-        launch_gemm<false, false>(true, C, din, 2 * dh, M, bk::cat2(da, za, dh), bk::cat2(wa, w1, dh), out, st);
+        launch_gemm<false, false>(true, R, din, 2 * dh, M, bk::cat2(da, za, dh), bk::cat2(wa, w1, dh), out, st);
       } else {
-        launch_gemm<false, false>(true, C, din, 3 * dh, M,
-                                  bk::cat3(da, bk::src(D1, 0, hz, dh, 1, C, dh, 2, cS, C, -1.0f), za, dh, 2 * dh),
+        launch_gemm<false, false>(true, R, din, 3 * dh, M,
+                                  bk::cat3(da, bk::src(D1, 0, hz, dh, 1, R, dh, 2, rS, rld, -1.0f), za, dh, 2 * dh),
                                   bk::cat3(wa, bk::src(SAg, 0, P, 1, din, din, dh), w1, dh, 2 * dh), out, st);
       }
     }
@@ -889,7 +1025,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     {
       bk::Cat la = bk::cat1(bk::src(dY + s * dv, 0, T * dv, dv, 1, C, dv));
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv));
-      launch_gemm<false, false>(true, C, dh, dv, M, la, lb, bk::EpiScaleSp{Zqa, Zk, hz, zz, C, dh}, st);
+      launch_gemm<false, false>(true, C, dh, dv, M, la, lb, bk::EpiScaleSp{Zqa, Zk, hz, zz, R, dh}, st);
       bk::Cat la2 = bk::cat1(bk::src(Zqa, 0, hz, dh, 1, C, dh));
       bk::Cat lb2 = bk::cat1(bk::src(cW1, 0, 2 * P, 1, din, din, dh));
       // the residual memory's retrieval adds the query: + dY
@@ -900,9 +1036,9 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     }
     // W1' = Z'^T X + Zq'^T Q -> Wb   (A(i=h, k=row), B(k=row, j=f))
     {
-      bk::Cat la = bk::cat2(bk::src(Pz, 0, hz, 1, dh, dh, C), bk::src(Zqa, 0, hz, 1, dh, dh, C), C);
-      bk::Cat lb = bk::cat2(bk::src(Kc, bf, inz, 1, din, din, C), bk::src(Qc, bf, inz, 1, din, din, C), C);
-      launch_gemm<false, false>(true, dh, din, 2 * C, M, la, lb, bk::EpiSt{Wb, P, din}, st);
+      bk::Cat la = bk::cat2(bk::src(Pz, 0, hz, 1, dh, dh, R), bk::src(Zqa, 0, hz, 1, dh, dh, C), R);
+      bk::Cat lb = bk::cat2(bk::src(Kr, kbf, kz, 1, din, din, R), bk::src(Qc, bf, inz, 1, din, din, C), R);
+      launch_gemm<false, false>(true, dh, din, R + C, M, la, lb, bk::EpiSt{Wb, P, din}, st);
     }
     AM_LAUNCH_CHECK();
     const int64_t n = (int64_t)M * P;
@@ -913,8 +1049,17 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     } else {
       hipLaunchKernelGGL(bk::scalar_adj_kernel, dim3(M), dim3(256), 0, st, WA, SA, ck, P, sca);
       AM_LAUNCH_CHECK();
+      const float* cWt = cWa;  // the per-token coefficient adjoints entering the gate scan's reverse
+      const float* cSt = cSa;
+      if (win) {
+        hipLaunchKernelGGL(bk::omega_adj_kernel, dim3(blocks_of((int64_t)M * R)), dim3(256), 0, st, cWa, cSa,
+                           ws + L.gs, ws + L.sw, ws + L.ss, C, c, R, M, T, s, ws + L.cwt, ws + L.cst, dgamma);
+        AM_LAUNCH_CHECK();
+        cWt = ws + L.cwt;
+        cSt = ws + L.cst;
+      }
       hipLaunchKernelGGL(bk::gate_bwd_kernel, dim3(M), dim3(64), (size_t)6 * C * sizeof(float), st, theta, eta,
-                         alpha, T, s, C, cWa, cSa, sca, dth, det, dal);
+                         alpha, T, s, C, cWt, cSt, sca, dth, det, dal);
       AM_LAUNCH_CHECK();
       hipLaunchKernelGGL(bk::state_adj_kernel, dim3(blocks_of(n)), dim3(256), 0, st, WA, SA, Wb, sc, P, M, WAn, SAn);
       AM_LAUNCH_CHECK();

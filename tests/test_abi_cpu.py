@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert am.abi_version() == am.ABI_VERSION == 1
+    assert am.abi_version() == am.ABI_VERSION == 2
     for s in range(7):
         assert am.status_string(s) and am.status_string(s) != "unknown status"
     assert am.status_string(99) == "unknown status"
@@ -83,7 +83,7 @@ def test_create_rejects_bad_configs_before_any_device_call(kw, status):
 def test_wrong_abi_version_and_null_config():
     lib = am.load()
     cfg = cfg4()
-    cfg.abi_version = 2
+    cfg.abi_version = am.ABI_VERSION + 1
     h = ctypes.c_void_p()
     assert lib.atlasmem_create(ctypes.byref(cfg), None, None, None, ctypes.byref(h)) == am.E_INVALID
     assert lib.atlasmem_create(None, None, None, None, ctypes.byref(h)) == am.E_INVALID

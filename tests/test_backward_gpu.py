@@ -33,6 +33,12 @@ CASES = [
     ("residual_per_token_C16", 1, "stabilised", dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, heads=2, T=48, d_key=24,
                                                       d_value=24, d_hidden=40, chunk=16)),
     ("residual_ns5_per_chunk", 4, "literal", dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, heads=2, T=256)),
+    # the Omega window (per-token gates): key rows reach c - 1 tokens into the previous chunk
+    ("omega3_C64", 1, "stabilised", dict(batch=1, heads=2, T=128, omega_window=3)),
+    ("omega6_ragged_C16", 1, "stabilised", dict(batch=2, heads=1, T=48, d_key=24, d_value=20, d_hidden=36, chunk=16,
+                                                omega_window=6)),
+    ("omega2_residual_C16", 1, "stabilised", dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, heads=2, T=32, d_key=16,
+                                                  d_value=16, d_hidden=24, chunk=16, omega_window=2)),
 ]
 
 
@@ -58,11 +64,13 @@ def test_backward_matches_autograd_oracle(case):
     dK, dQ, dV = z(M, T, s.d_key), z(M, T, s.d_key), z(M, T, s.d_value)
     ng = inp.theta.shape[1]  # T per token, T / C per chunk
     dth, det, dal = z(M, ng), z(M, ng), z(M, ng)
+    win = s.omega_window > 1
+    dgm = z(M, T) if win else None
     dW0, dS0 = z(M, mem.P), z(M, mem.P)
     Y = z(M, T, s.d_value)
     mem.update_backward(to_dev(inp.K), to_dev(inp.Q), to_dev(inp.V), to_dev(inp.theta), to_dev(inp.eta),
                         to_dev(inp.alpha), T, to_dev(dY), dK, dQ, dV, dth, det, dal, dW0, dS0, ws, Y=Y,
-                        dW_T=to_dev(dWT), dS_T=to_dev(dST))
+                        dW_T=to_dev(dWT), dS_T=to_dev(dST), gamma=to_dev(inp.gamma) if win else None, dgamma=dgm)
     W = torch.empty((M, mem.P), dtype=torch.float32, device=DEV)
     S = torch.empty_like(W)
     status = mem.get_state(W, S)
@@ -73,6 +81,8 @@ def test_backward_matches_autograd_oracle(case):
     K, Q, V = to_f64(inp.K, s.input_dtype), to_f64(inp.Q, s.input_dtype), to_f64(inp.V, s.input_dtype)
     errs = {}
     got = dict(K=dK, Q=dQ, V=dV, theta=dth, eta=det, alpha=dal)
+    if win:
+        got["gamma"] = dgm
     ref = {k: [] for k in got}
     ref["W0"], ref["S0"] = [], []
     ys, wts = [], []
@@ -81,12 +91,14 @@ def test_backward_matches_autograd_oracle(case):
         S0m = oracle.unflatten(cfg, inp.S0[m].astype(np.float64))
         g = bw.outer_grads(cfg, P0, S0m, K[m], Q[m], V[m], inp.theta[m], inp.eta[m], inp.alpha[m], dY[m],
                            oracle.unflatten(cfg, dWT[m].astype(np.float64)),
-                           oracle.unflatten(cfg, dST[m].astype(np.float64)))
+                           oracle.unflatten(cfg, dST[m].astype(np.float64)),
+                           gamma=inp.gamma[m] if win else None)
         for k in got:
             ref[k].append(g[k])
         ref["W0"].append(oracle.flatten(g["W0"]))
         ref["S0"].append(oracle.flatten(g["S0"]))
-        res = oracle.run_memory(cfg, P0, S0m, K[m], Q[m], V[m], inp.theta[m], inp.eta[m], inp.alpha[m])
+        res = oracle.run_memory(cfg, P0, S0m, K[m], Q[m], V[m], inp.theta[m], inp.eta[m], inp.alpha[m],
+                                inp.gamma[m] if win else None)
         ys.append(res.Y)
         wts.append(oracle.flatten(res.params))
     for k, t in got.items():
@@ -123,4 +135,12 @@ def test_backward_errors():
     with pytest.raises(am.AtlasMemError) as e:
         mem.update_backward(xb, xb, xb, g, g, g, 40, x, x, x, x, g, g, g, p, p, ws)
     assert e.value.status == am.E_SHAPE
+    mem.close()
+    # an Omega window needs its gates and their gradient
+    sw = synth.spec(1, "stabilised", batch=1, heads=1, T=64, omega_window=3)
+    mem = am.Memory(config_for(sw))
+    ws = torch.empty(mem.backward_workspace_bytes(64), dtype=torch.uint8, device=DEV)
+    with pytest.raises(am.AtlasMemError) as e:
+        mem.update_backward(xb, xb, xb, g, g, g, 64, x, x, x, x, g, g, g, p, p, ws)
+    assert e.value.status == am.E_INVALID
     mem.close()
