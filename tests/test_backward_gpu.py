@@ -33,6 +33,8 @@ CASES = [
     ("residual_per_token_C16", 1, "stabilised", dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, heads=2, T=48, d_key=24,
                                                       d_value=24, d_hidden=40, chunk=16)),
     ("residual_ns5_per_chunk", 4, "literal", dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, heads=2, T=256)),
+    # the wide memory (384 -> 768 -> 384): tiles of every product span several 64-wide blocks
+    ("wide_384x768_C64", 2, "stabilised", dict(batch=1, heads=1, T=128)),
     # the Omega window (per-token gates): key rows reach c - 1 tokens into the previous chunk
     ("omega3_C64", 1, "stabilised", dict(batch=1, heads=2, T=128, omega_window=3)),
     ("omega6_ragged_C16", 1, "stabilised", dict(batch=2, heads=1, T=48, d_key=24, d_value=20, d_hidden=36, chunk=16,
