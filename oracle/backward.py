@@ -20,6 +20,9 @@ torch autograd as a library step.
 
 from __future__ import annotations
 
+import math
+from itertools import combinations_with_replacement
+
 import numpy as np
 import torch
 
@@ -28,6 +31,22 @@ from .neural_memory import LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, PER_TOKEN, Mem
 
 def _silu(z):
     return z * torch.sigmoid(z)
+
+
+def _poly(x, degree):
+    """phi of every row of x ([T, d]) with torch operations: the monomials of degree 0..p, each
+    degree's coefficient 1/deg!, degree-major and in combinations_with_replacement order inside a
+    degree (Atlas-Torch README, Atlas Extensions table, Polynomial Features); identity for p = 1."""
+    if degree == 1:
+        return x
+    cols = []
+    for deg in range(degree + 1):
+        for combo in combinations_with_replacement(range(x.shape[1]), deg):
+            col = torch.full((x.shape[0],), 1.0 / math.factorial(deg), dtype=x.dtype)
+            for i in combo:
+                col = col * x[:, i]
+            cols.append(col)
+    return torch.stack(cols, dim=1)
 
 
 def _apply(params, x, residual=False):
@@ -66,16 +85,16 @@ def _newton_schulz(g, steps, coeffs, eps):
 
 
 def run_memory_torch(cfg: MemoryConfig, params, momenta, K, Q, V, theta, eta, alpha, gamma=None):
-    """The literal chunked recurrence for one memory (identity features; per-token gates with an
-    Omega window of c tokens, or per-chunk gates with an optional Newton-Schulz
-    orthogonalisation of the summed chunk gradient) with torch tensors: Y, final params, final
-    momenta.  Plain, residual or linear memory.  The window starts with the sequence (no history
+    """The literal chunked recurrence for one memory (keys and queries through the polynomial
+    feature map; per-token gates with an Omega window of c tokens, or per-chunk gates with an
+    optional Newton-Schulz orthogonalisation of the summed chunk gradient) with torch tensors:
+    Y, final params, final momenta.  Plain, residual or linear memory.  The window starts with the sequence (no history
     from a previous call): token t's step uses sum_{i=t-c+1..t, i>=0} gamma_i g_i, every g_i taken
     at the weights of the chunk that holds t (ATLAS summary, sections 3.2-3.3)."""
-    assert cfg.poly_degree == 1
     c = cfg.omega_window
     assert c == 1 or cfg.gate_mode == PER_TOKEN
     res = cfg.kind == MLP2_SILU_RESIDUAL
+    K, Q = _poly(K, cfg.poly_degree), _poly(Q, cfg.poly_degree)  # the memory reads features
     W = list(params)
     S = list(momenta)
     T = K.shape[0]

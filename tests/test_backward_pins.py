@@ -10,15 +10,16 @@ from oracle import LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, PER_CHUNK, PER_TOKEN, 
 from oracle import backward as bw
 
 
-def problem(seed, kind, T=8, C=4, d=3, v=2, h=5, mode=PER_TOKEN, ns=0, c=1):
+def problem(seed, kind, T=8, C=4, d=3, v=2, h=5, mode=PER_TOKEN, ns=0, c=1, poly=1):
     r = np.random.default_rng(seed)
+    din = oracle.poly_feature_count(d, poly)
     if kind == MLP2_SILU_RESIDUAL:
-        v = d  # the residual memory adds its input to its output
-    cfg = MemoryConfig(kind, d, v, h if kind != LINEAR else 0, 1, C, c, mode, ns)
+        v = din  # the residual memory adds its input (features) to its output
+    cfg = MemoryConfig(kind, d, v, h if kind != LINEAR else 0, poly, C, c, mode, ns)
     if kind == LINEAR:
-        params = [r.normal(0, 0.5, (v, d))]
+        params = [r.normal(0, 0.5, (v, din))]
     else:
-        params = [r.normal(0, 0.5, (h, d)), r.normal(0, 0.5, (v, h))]
+        params = [r.normal(0, 0.5, (h, din)), r.normal(0, 0.5, (v, h))]
     momenta = [r.normal(0, 0.1, p.shape) for p in params]
     K = r.normal(0, 1, (T, d)) / np.sqrt(d)
     Q = r.normal(0, 1, (T, d)) / np.sqrt(d)
@@ -38,17 +39,19 @@ def objective(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS, gm=None):
             + sum(np.sum(a * b) for a, b in zip(res.momenta, dS)))
 
 
-# (kind, gate mode, Newton-Schulz steps, Omega window)
-MODES = [(LINEAR, PER_TOKEN, 0, 1), (MLP2_SILU, PER_TOKEN, 0, 1), (MLP2_SILU, PER_CHUNK, 0, 1),
-         (MLP2_SILU, PER_CHUNK, 5, 1), (LINEAR, PER_CHUNK, 5, 1), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 1),
-         (MLP2_SILU_RESIDUAL, PER_CHUNK, 5, 1), (MLP2_SILU, PER_TOKEN, 0, 3), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 2),
-         (LINEAR, PER_TOKEN, 0, 3), (MLP2_SILU, PER_TOKEN, 0, 6)]
+# (kind, gate mode, Newton-Schulz steps, Omega window, feature degree)
+MODES = [(LINEAR, PER_TOKEN, 0, 1, 1), (MLP2_SILU, PER_TOKEN, 0, 1, 1), (MLP2_SILU, PER_CHUNK, 0, 1, 1),
+         (MLP2_SILU, PER_CHUNK, 5, 1, 1), (LINEAR, PER_CHUNK, 5, 1, 1), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 1, 1),
+         (MLP2_SILU_RESIDUAL, PER_CHUNK, 5, 1, 1), (MLP2_SILU, PER_TOKEN, 0, 3, 1),
+         (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 2, 1), (LINEAR, PER_TOKEN, 0, 3, 1), (MLP2_SILU, PER_TOKEN, 0, 6, 1),
+         (MLP2_SILU, PER_TOKEN, 0, 3, 2), (MLP2_SILU, PER_TOKEN, 0, 1, 2), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 2, 2)]
 
 
-@pytest.mark.parametrize("kind,mode,ns,c", MODES)
-def test_torch_restatement_matches_oracle(kind, mode, ns, c):
+@pytest.mark.parametrize("kind,mode,ns,c,poly", MODES)
+def test_torch_restatement_matches_oracle(kind, mode, ns, c, poly):
     import torch
-    cfg, params, momenta, K, Q, V, th, et, al, _, _, _, gm = problem(1, kind, T=10, C=4, h=6, mode=mode, ns=ns, c=c)
+    cfg, params, momenta, K, Q, V, th, et, al, _, _, _, gm = problem(1, kind, T=10, C=4, h=6, mode=mode, ns=ns, c=c,
+                                                                     poly=poly)
     ref = oracle.run_memory(cfg, params, momenta, K, Q, V, th, et, al, gm)
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
     Y, W, S = bw.run_memory_torch(cfg, [t(p) for p in params], [t(m) for m in momenta], t(K), t(Q), t(V), t(th),
@@ -60,13 +63,13 @@ def test_torch_restatement_matches_oracle(kind, mode, ns, c):
         np.testing.assert_allclose(a.numpy(), b, rtol=1e-13, atol=1e-14)
 
 
-@pytest.mark.parametrize("kind,mode,ns,c", MODES)
-def test_outer_gradients_against_finite_differences(kind, mode, ns, c):
+@pytest.mark.parametrize("kind,mode,ns,c,poly", MODES)
+def test_outer_gradients_against_finite_differences(kind, mode, ns, c, poly):
     """<grad, delta> against (L(x + h delta) - L(x - h delta)) / 2h with L from the numpy oracle,
     for a random direction in every input group (a wrong sign, index or dropped term in any
     group changes its directional derivative)."""
     cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS, gm = problem(2, kind, T=9, C=4, h=6, mode=mode, ns=ns,
-                                                                        c=c)
+                                                                        c=c, poly=poly)
     g = bw.outer_grads(cfg, params, momenta, K, Q, V, th, et, al, dY, dW, dS, gamma=gm)
     r = np.random.default_rng(3)
     args = dict(params=params, momenta=momenta, K=K, Q=Q, V=V, th=th, et=et, al=al, gm=gm)
