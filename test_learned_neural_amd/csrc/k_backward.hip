@@ -112,18 +112,19 @@ struct EpiSt {  // out[z * sz + row * ld + col]
     out[(int64_t)z * sz + (int64_t)row * ld + col] = v;
   }
 };
-struct EpiE {  // E = 2 (acc - V), or 2 (acc + X - V) for the residual memory (X: the keys, din = dv)
+struct EpiE {  // E = 2 (acc - V), or 2 (acc + X - V) for the residual memory (X: the key features, din = dv)
   float* E;
   int64_t ez;
   const void* V;
   int bf16;
-  int64_t vz;  // V element stride per memory (T * dv); V already offset to the chunk
+  int64_t vz;  // V element stride per memory; V already offset to the chunk's first row
   int dv;
-  const void* X;  // null unless residual; same layout as V
+  const void* X;  // null unless residual: rows of dv elements, stride xz per memory
+  int xbf16;
+  int64_t xz;
   __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    const int64_t i = (int64_t)z * vz + (int64_t)row * dv + col;
-    const float vv = load_in(V, i, bf16);
-    const float xv = X ? load_in(X, i, bf16) : 0.0f;
+    const float vv = load_in(V, (int64_t)z * vz + (int64_t)row * dv + col, bf16);
+    const float xv = X ? load_in(X, (int64_t)z * xz + (int64_t)row * dv + col, xbf16) : 0.0f;
     E[(int64_t)z * ez + (int64_t)row * dv + col] = 2.0f * (v + xv - vv);
   }
 };
@@ -373,22 +374,70 @@ __global__ void state_adj_kernel(const float* __restrict__ WA, const float* __re
 
 // Omega window (per-token gates, window c): key row r of the chunk at token s is token
 // tau = s - (c - 1) + r; rows before the call come from the window history the call started with
-// (hk, hv, hg: [M][c - 1][*], oldest first).  Keys, values and gamma of the R rows to fp32 staging.
-__global__ void stage_rows_kernel(const void* __restrict__ K, const void* __restrict__ V,
-                                  const float* __restrict__ gamma, int bf16, int64_t T, int64_t s, int c, int R,
-                                  int dk, int dv, const float* __restrict__ hk, const float* __restrict__ hv,
-                                  const float* __restrict__ hg, float* __restrict__ ks, float* __restrict__ vs,
-                                  float* __restrict__ gs) {
+// (hv, hg: [M][c - 1][*], oldest first).  Values and gamma of the R rows to fp32 staging.
+__global__ void stage_vg_kernel(const void* __restrict__ V, const float* __restrict__ gamma, int bf16, int64_t T,
+                                int64_t s, int c, int R, int dv, const float* __restrict__ hv,
+                                const float* __restrict__ hg, float* __restrict__ vs, float* __restrict__ gs) {
   const int r = blockIdx.x, z = blockIdx.y, H = c - 1;
   const int64_t tau = s - H + r;
   const int64_t row = (int64_t)z * R + r;
-  for (int e = threadIdx.x; e < dk; e += blockDim.x)
-    ks[row * dk + e] = tau >= 0 ? load_in(K, ((int64_t)z * T + tau) * dk + e, bf16)
-                                : hk[((int64_t)z * H + H + tau) * dk + e];
   for (int e = threadIdx.x; e < dv; e += blockDim.x)
     vs[row * dv + e] = tau >= 0 ? load_in(V, ((int64_t)z * T + tau) * dv + e, bf16)
                                 : hv[((int64_t)z * H + H + tau) * dv + e];
   if (threadIdx.x == 0) gs[row] = tau >= 0 ? gamma[(int64_t)z * T + tau] : hg[(int64_t)z * H + H + tau];
+}
+
+// Feature rows phi(x) of `rows` consecutive tokens tau0 + r of every memory (identity for degree 1;
+// degree 2: 1, x_i, x_i x_j / 2 for i <= j in combinations_with_replacement order), the raw row
+// from X (tau >= 0) or from the window history hist ([M][H][dk], tau < 0), to out [M][rows][din].
+__global__ void stage_feat_kernel(const void* __restrict__ X, int bf16, int64_t T, int64_t tau0, int rows, int dk,
+                                  int din, int poly, const float* __restrict__ hist, int H, float* __restrict__ out) {
+  extern __shared__ float xr[];  // the raw row
+  const int r = blockIdx.x, z = blockIdx.y;
+  const int64_t tau = tau0 + r;
+  for (int e = threadIdx.x; e < dk; e += blockDim.x)
+    xr[e] = tau >= 0 ? load_in(X, ((int64_t)z * T + tau) * dk + e, bf16) : hist[((int64_t)z * H + H + tau) * dk + e];
+  __syncthreads();
+  float* o = out + ((int64_t)z * rows + r) * din;
+  for (int f = threadIdx.x; f < din; f += blockDim.x) {
+    float v;
+    if (poly == 1) {
+      v = xr[f];
+    } else if (f == 0) {
+      v = 1.0f;
+    } else if (f <= dk) {
+      v = xr[f - 1];
+    } else {
+      int i, j;
+      pair_of(f - 1 - dk, dk, i, j);
+      v = 0.5f * (xr[i] * xr[j]);
+    }
+    o[f] = v;
+  }
+}
+
+// The gradient of the raw rows from that of their degree-2 features: phi's monomials of degree 1
+// give 1, x_i^2 / 2 gives x_i, x_i x_j / 2 (i < j) gives x_j / 2 to x_i, so
+// dx_i = g_{1+i} + g_{ii} x_i + sum_{j != i} g_{ij} x_j / 2  (x_j read back from the features).
+// Row r is token tau0 + r of out ([M][T][dk]); acc: accumulated (tokens before 0 dropped).
+__global__ void feat_jac_kernel(const float* __restrict__ G, const float* __restrict__ F, int rows, int dk, int din,
+                                int64_t T, int64_t tau0, int acc, float* __restrict__ out) {
+  const int r = blockIdx.x, z = blockIdx.y;
+  const int64_t tau = tau0 + r;
+  if (tau < 0) return;
+  const float* g = G + ((int64_t)z * rows + r) * din;
+  const float* x = F + ((int64_t)z * rows + r) * din + 1;  // the degree-1 features are the raw row
+  for (int i = threadIdx.x; i < dk; i += blockDim.x) {
+    float v = g[1 + i];
+    for (int j = 0; j < dk; ++j) {
+      const int a = i < j ? i : j, b = i < j ? j : i;
+      const float gp = g[1 + dk + pair_start(a, dk) + (b - a)];
+      v += (i == j ? 1.0f : 0.5f) * gp * x[j];
+    }
+    float* o = out + ((int64_t)z * T + tau) * dk + i;
+    if (acc) *o += v;
+    else *o = v;
+  }
 }
 
 // The coefficients of the key rows' gradients: g_r enters every step t of the chunk whose window
@@ -612,6 +661,7 @@ struct BwdLayout {
   int64_t ck, wa0, wa1, sa0, sa1, wb, zk, e, pz, d1, u1, u1s, u2, u2s, zqa, cw, cs, cwa, csa, sc, sca;
   int64_t R;  // key rows per chunk: C, or C + c - 1 with an Omega window
   int64_t ow, os, sw, ss, cwt, cst, ks, vs, gs, hk0, hv0, hg0;  // Omega window buffers
+  int64_t qs, xg, qg;  // polynomial features: query features, feature-space gradients of keys / queries
   int64_t gb, nb, nab, gab, sat;
   NsLay ns[2];
   int nns;  // Newton-Schulz batches: 1 when both matrices share a working shape, else 2
@@ -649,6 +699,13 @@ static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
   L.cwa = take(M * R);
   L.csa = take(M * R);
   L.ow = L.os = L.sw = L.ss = L.cwt = L.cst = L.ks = L.vs = L.gs = L.hk0 = L.hv0 = L.hg0 = 0;
+  L.qs = L.xg = L.qg = 0;
+  if (d.c > 1 || d.poly > 1) L.ks = take(M * R * d.din);  // staged key rows (features)
+  if (d.poly > 1) {
+    L.qs = take(M * C * d.din);
+    L.xg = take(M * R * d.din);
+    L.qg = take(M * C * d.din);
+  }
   if (d.c > 1) {
     const int64_t H = d.c - 1;
     L.ow = take(M * R);
@@ -657,7 +714,6 @@ static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
     L.ss = take(M * R);
     L.cwt = take(M * C);
     L.cst = take(M * C);
-    L.ks = take(M * R * d.dk);
     L.vs = take(M * R * dv);
     L.gs = take(M * R);
     L.hk0 = take(M * H * d.dk);
@@ -788,8 +844,8 @@ static atlasmem_status ns_backward(const Dims& d, float* ws, const NsLay& n, con
 }
 
 bool backward_supported(const Dims& d) {
-  return d.kind == ATLASMEM_MLP2_SILU && !d.gated && !d.ptr && d.poly == 1 &&
-         (d.gate_mode == ATLASMEM_PER_CHUNK ? d.c == 1 : d.ns_steps == 0);
+  return d.kind == ATLASMEM_MLP2_SILU && !d.gated && !d.ptr && d.poly <= 2 &&
+         (d.gate_mode == ATLASMEM_PER_CHUNK ? d.c == 1 && d.poly == 1 : d.ns_steps == 0);
 }
 
 int64_t backward_workspace_bytes(const Dims& d, int64_t T) {
@@ -811,7 +867,9 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
   const BwdLayout L = bwd_layout(d, nch);
   float* ws = (float*)workspace;
   const int c = d.c;
-  const bool win = c > 1;  // Omega window: key rows reach c - 1 tokens back, outputs accumulate
+  const bool win = c > 1;          // Omega window: key rows reach c - 1 tokens back, outputs accumulate
+  const bool feat = d.poly > 1;    // polynomial features: the memory reads phi(k), phi(q)
+  const bool staged = win || feat;  // key rows staged in fp32 (features, window history)
   if (win) {
     // the window history the call starts with (the forward below advances the handle's), and
     // zeroed gradients of the rows that several chunks touch
@@ -821,7 +879,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
         hipMemcpyAsync(ws + L.hv0, h->hv[h->hcur], sizeof(float) * H * dv, hipMemcpyDeviceToDevice, st) !=
             hipSuccess ||
         hipMemcpyAsync(ws + L.hg0, h->hg[h->hcur], sizeof(float) * H, hipMemcpyDeviceToDevice, st) != hipSuccess ||
-        hipMemsetAsync(dK, 0, sizeof(float) * M * T * din, st) != hipSuccess ||
+        hipMemsetAsync(dK, 0, sizeof(float) * M * T * d.dk, st) != hipSuccess ||
         hipMemsetAsync(dV, 0, sizeof(float) * M * T * dv, st) != hipSuccess ||
         hipMemsetAsync(dgamma, 0, sizeof(float) * M * T, st) != hipSuccess) {
       (void)hipGetLastError();
@@ -878,20 +936,34 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     const float* cW2 = ck + P1;
     const char* Kc = (const char*)K + s * d.dk * esz;
     const char* Qc = (const char*)Q + s * d.dk * esz;
-    // key rows: the chunk's keys (or, with a window, the R staged rows); values likewise
-    const void* Kr = win ? (const void*)(ws + L.ks) : (const void*)Kc;
-    const int kbf = win ? 0 : bf;
-    const int64_t kz = win ? (int64_t)R * din : inz;
+    // key rows: the chunk's keys (or the R staged feature rows); values, queries likewise
+    const void* Kr = staged ? (const void*)(ws + L.ks) : (const void*)Kc;
+    const int kbf = staged ? 0 : bf;
+    const int64_t kz = staged ? (int64_t)R * din : inz;
     const void* Vr = win ? (const void*)(ws + L.vs) : (const void*)((const char*)V + s * dv * esz);
+    const int vbf = win ? 0 : bf;
     const int64_t vrz = win ? (int64_t)R * dv : T * dv;
+    const void* Qr = feat ? (const void*)(ws + L.qs) : (const void*)Qc;
+    const int qbf = feat ? 0 : bf;
+    const int64_t qz = feat ? (int64_t)C * din : inz;
     atlasmem_status stt = ATLASMEM_OK;
     if (!per_chunk) {
       stt = launch_gate_scan(theta, eta, alpha, M, T, s, 1, C, cW, cS, C, sc, 3, st);
       if (stt != ATLASMEM_OK) return stt;
     }
+    if (staged) {
+      hipLaunchKernelGGL(bk::stage_feat_kernel, dim3(R, M), dim3(256), sizeof(float) * d.dk, st, K, bf, T,
+                         s - (c - 1), R, d.dk, din, d.poly, win ? ws + L.hk0 : nullptr, c - 1, ws + L.ks);
+      AM_LAUNCH_CHECK();
+    }
+    if (feat) {
+      hipLaunchKernelGGL(bk::stage_feat_kernel, dim3(C, M), dim3(256), sizeof(float) * d.dk, st, Q, bf, T, s, C,
+                         d.dk, din, d.poly, (const float*)nullptr, 0, ws + L.qs);
+      AM_LAUNCH_CHECK();
+    }
     if (win) {
-      hipLaunchKernelGGL(bk::stage_rows_kernel, dim3(R, M), dim3(64), 0, st, K, V, gamma, bf, T, s, c, R, d.dk, dv,
-                         ws + L.hk0, ws + L.hv0, ws + L.hg0, ws + L.ks, ws + L.vs, ws + L.gs);
+      hipLaunchKernelGGL(bk::stage_vg_kernel, dim3(R, M), dim3(64), 0, st, V, gamma, bf, T, s, c, R, dv,
+                         ws + L.hv0, ws + L.hg0, ws + L.vs, ws + L.gs);
       hipLaunchKernelGGL(bk::omega_coef_kernel, dim3(blocks_of((int64_t)M * R)), dim3(256), 0, st, cW, cS,
                          ws + L.gs, C, c, R, M, ws + L.ow, ws + L.os, ws + L.sw, ws + L.ss);
       AM_LAUNCH_CHECK();
@@ -899,7 +971,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     // Z of key and query rows
     {  // rows [0, R) keys, [R, R + C) queries (two launches into the two parts)
       bk::Cat lk = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
-      bk::Cat lq = bk::cat1(bk::src(Qc, bf, inz, din, 1, C, din));
+      bk::Cat lq = bk::cat1(bk::src(Qr, qbf, qz, din, 1, C, din));
       bk::Cat lb = bk::cat1(bk::src(cW1, 0, 2 * P, din, 1, dh, din));
       launch_gemm<false, false>(true, R, dh, din, M, lk, lb, bk::EpiSt{Zk, zz, dh}, st);
       launch_gemm<false, false>(true, C, dh, din, M, lq, lb, bk::EpiSt{Zk + (int64_t)R * dh, zz, dh}, st);
@@ -909,7 +981,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat la = bk::cat1(bk::src(Zk, 0, zz, dh, 1, R, dh, 1));
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh));
       launch_gemm<false, false>(true, R, dv, dh, M, la, lb,
-                                bk::EpiE{E, vz, Vr, kbf, vrz, dv, d.residual ? Kr : nullptr}, st);
+                                bk::EpiE{E, vz, Vr, vbf, vrz, dv, d.residual ? Kr : nullptr, kbf, kz}, st);
     }
     // P = E W2, D1 = P silu'(Z)
     {
@@ -1009,10 +1081,13 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       const bk::Src wa = bk::src(WAg, 0, P, 1, din, din, dh);  // B(k=h, j=f) = M[h][f]
       const bk::Src w1 = bk::src(cW1, 0, 2 * P, 1, din, din, dh);
       // the residual memory's keys also enter E directly: + 2 E' (E' in U2, din = dv)
-      const bk::EpiStAdd out = win ? bk::EpiStAdd{dK, T * din, din, d.residual ? U2 : nullptr, vz, dv, 2.0f,
-                                                  s - (c - 1), 1}
-                                   : bk::EpiStAdd{dK + s * din, T * din, din, d.residual ? U2 : nullptr, vz, dv,
-                                                  2.0f, 0, 0};
+      // with features the rows' feature-space gradient goes to xg and through phi's Jacobian below
+      const bk::EpiStAdd out = feat ? bk::EpiStAdd{ws + L.xg, (int64_t)R * din, din, d.residual ? U2 : nullptr, vz,
+                                                   dv, 2.0f, 0, 0}
+                               : win ? bk::EpiStAdd{dK, T * din, din, d.residual ? U2 : nullptr, vz, dv, 2.0f,
+                                                    s - (c - 1), 1}
+                                     : bk::EpiStAdd{dK + s * din, T * din, din, d.residual ? U2 : nullptr, vz, dv,
+                                                    2.0f, 0, 0};
       if (per_chunk) {
         launch_gemm<false, false>(true, R, din, 2 * dh, M, bk::cat2(da, za, dh), bk::cat2(wa, w1, dh), out, st);
       } else {
@@ -1030,14 +1105,23 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat lb2 = bk::cat1(bk::src(cW1, 0, 2 * P, 1, din, din, dh));
       // the residual memory's retrieval adds the query: + dY
       launch_gemm<false, false>(true, C, din, dh, M, la2, lb2,
-                                bk::EpiStAdd{dQ + s * din, T * din, din, d.residual ? dY + s * dv : nullptr, T * dv,
-                                             dv, 1.0f},
+                                feat ? bk::EpiStAdd{ws + L.qg, (int64_t)C * din, din,
+                                                    d.residual ? dY + s * dv : nullptr, T * dv, dv, 1.0f, 0, 0}
+                                     : bk::EpiStAdd{dQ + s * din, T * din, din, d.residual ? dY + s * dv : nullptr,
+                                                    T * dv, dv, 1.0f, 0, 0},
                                 st);
+    }
+    if (feat) {  // the raw rows' gradients through the feature map
+      hipLaunchKernelGGL(bk::feat_jac_kernel, dim3(R, M), dim3(64), 0, st, ws + L.xg, ws + L.ks, R, d.dk, din, T,
+                         s - (c - 1), win ? 1 : 0, dK);
+      hipLaunchKernelGGL(bk::feat_jac_kernel, dim3(C, M), dim3(64), 0, st, ws + L.qg, ws + L.qs, C, d.dk, din, T, s,
+                         0, dQ);
+      AM_LAUNCH_CHECK();
     }
     // W1' = Z'^T X + Zq'^T Q -> Wb   (A(i=h, k=row), B(k=row, j=f))
     {
       bk::Cat la = bk::cat2(bk::src(Pz, 0, hz, 1, dh, dh, R), bk::src(Zqa, 0, hz, 1, dh, dh, C), R);
-      bk::Cat lb = bk::cat2(bk::src(Kr, kbf, kz, 1, din, din, R), bk::src(Qc, bf, inz, 1, din, din, C), R);
+      bk::Cat lb = bk::cat2(bk::src(Kr, kbf, kz, 1, din, din, R), bk::src(Qr, qbf, qz, 1, din, din, C), R);
       launch_gemm<false, false>(true, dh, din, R + C, M, la, lb, bk::EpiSt{Wb, P, din}, st);
     }
     AM_LAUNCH_CHECK();

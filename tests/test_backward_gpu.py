@@ -41,6 +41,13 @@ CASES = [
                                                 omega_window=6)),
     ("omega2_residual_C16", 1, "stabilised", dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, heads=2, T=32, d_key=16,
                                                   d_value=16, d_hidden=24, chunk=16, omega_window=2)),
+    # degree-2 polynomial features (the memory reads phi(k), phi(q); 32 -> 561 features) with the
+    # window of 4, as in the Omega workload
+    ("poly2_omega4_C64", 3, "stabilised", dict(batch=1, heads=2, T=128)),
+    ("poly2_no_window_C16", 3, "stabilised", dict(batch=2, heads=1, T=48, d_key=6, d_value=20, d_hidden=36,
+                                                  chunk=16, omega_window=1)),
+    ("poly2_residual_window2", 3, "stabilised", dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, heads=2, T=48, d_key=4,
+                                                     d_value=15, d_hidden=24, chunk=16, omega_window=2)),
 ]
 
 
@@ -116,7 +123,7 @@ def test_backward_matches_autograd_oracle(case):
 
 def test_backward_errors():
     import torch
-    for s3 in (synth.spec(3, "stabilised", batch=1, heads=1, T=256),  # window 4, polynomial features
+    for s3 in (synth.spec(3, "stabilised", batch=1, heads=1, T=256, gate_mode=synth.PER_CHUNK, omega_window=1),
                synth.spec(1, "stabilised", batch=1, heads=1, T=256, kind=synth.MLP2_GATED)):
         mem = am.Memory(config_for(s3))
         assert mem.backward_workspace_bytes(256) == -1
