@@ -271,7 +271,7 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
 
 }  // extern "C"
 
-namespace {
+namespace am {
 
 // One launch sequence of the update over sp.T tokens (a multiple of d.C), then the window
 // history of those tokens.
@@ -289,6 +289,10 @@ atlasmem_status run_update(Handle* h, const Dims& d, const void* K, const void* 
   }
   return ATLASMEM_OK;
 }
+
+}  // namespace am
+
+namespace {
 
 atlasmem_status retrieve_rows(Handle* h, const void* Q, int64_t T, int64_t ld, void* Y, hipStream_t st) {
   if (T == 0) return ATLASMEM_OK;

@@ -118,6 +118,10 @@ int64_t backward_workspace_bytes(const Dims& d, int64_t T);
 // Streaming calls of at most a few tokens (k_decode.hip): the queries' retrieval from the current
 // state and, with `append`, the key / value rows and per-token gates appended to the unfinished
 // chunk, in one launch.  E_UNSUPPORTED when the configuration or the call does not qualify.
+// One update of T tokens (api.hip): the MLP path or the linear memory's, with the window history.
+atlasmem_status run_update(Handle* h, const Dims& d, const void* K, const void* Q, const void* V, const float* theta,
+                           const float* eta, const float* alpha, const float* gamma, const Span& sp, void* Y,
+                           hipStream_t st);
 bool decode_supported(const Dims& d, int64_t n);
 atlasmem_status launch_decode(Handle* h, const void* Q, const void* K, const void* V, const float* theta,
                               const float* eta, const float* alpha, const float* gamma, int64_t ld, int64_t n,

@@ -268,6 +268,39 @@ __global__ void row_kernel(const float* __restrict__ Z, int64_t zz, float* __res
   for (int j = lane; j < dv; j += 64) U2[vo + j] = -(cw * U2[vo + j] + (use_s ? cs * U2s[vo + j] : 0.0f));  // E'_g
 }
 
+// The linear memory's rows (g_r = E_r x_r^T, E = 2 (X W^T - V)): with U = X WA^T and Us = X SA^T,
+// the coefficient adjoints -<E_r, U_r>, -<E_r, Us_r> and E'_r = -(oW_r U_r + oS_r Us_r) (in U), and
+// dV = -2 E' (row r is token tau0 + r when acc, accumulated, tokens before 0 dropped; else row r
+// of the chunk's dV).
+__global__ void lin_row_kernel(const float* __restrict__ E, float* __restrict__ U, const float* __restrict__ Us,
+                               int64_t vz, int dv, int ld, const float* __restrict__ rW, const float* __restrict__ rS,
+                               float* __restrict__ cWa, float* __restrict__ cSa, float* __restrict__ dV, int64_t dvz,
+                               int64_t tau0, int acc) {
+  const int r = blockIdx.x, z = blockIdx.y, lane = threadIdx.x;
+  const int64_t o = (int64_t)z * vz + (int64_t)r * dv;
+  float a = 0.0f, b = 0.0f;
+  for (int j = lane; j < dv; j += 64) {
+    a += E[o + j] * U[o + j];
+    b += E[o + j] * Us[o + j];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    a += __shfl_xor(a, off, 64);
+    b += __shfl_xor(b, off, 64);
+  }
+  if (lane == 0) {
+    cWa[(int64_t)z * ld + r] = -a;
+    cSa[(int64_t)z * ld + r] = -b;
+  }
+  const float w = rW[(int64_t)z * ld + r], sv = rS[(int64_t)z * ld + r];
+  for (int j = lane; j < dv; j += 64) {
+    const float ea = -(w * U[o + j] + sv * Us[o + j]);
+    U[o + j] = ea;
+    if (!acc) dV[(int64_t)z * dvz + (int64_t)r * dv + j] = -2.0f * ea;
+    else if (tau0 + r >= 0) dV[(int64_t)z * dvz + (tau0 + r) * dv + j] += -2.0f * ea;
+  }
+}
+
 // beta' = <WA, W>, aS' = <WA, S>, PC' = <SA, S> per memory; ck: [M][2P] (W then S).
 __global__ void scalar_adj_kernel(const float* __restrict__ WA, const float* __restrict__ SA,
                                   const float* __restrict__ ck, int64_t P, float* __restrict__ out) {
@@ -844,6 +877,7 @@ static atlasmem_status ns_backward(const Dims& d, float* ws, const NsLay& n, con
 }
 
 bool backward_supported(const Dims& d) {
+  if (d.kind == ATLASMEM_LINEAR) return !d.ptr && d.poly <= 2 && d.gate_mode == ATLASMEM_PER_TOKEN;
   return d.kind == ATLASMEM_MLP2_SILU && !d.gated && !d.ptr && d.poly <= 2 &&
          (d.gate_mode == ATLASMEM_PER_CHUNK ? d.c == 1 && d.poly == 1 : d.ns_steps == 0);
 }
@@ -899,7 +933,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     const int64_t s = k * C;
     const int64_t go = per_chunk ? k : s;  // this chunk's gates
     const atlasmem_status stt =
-        mlp_update(h, d, (const char*)K + s * d.dk * esz, (const char*)Q + s * d.dk * esz,
+        run_update(h, d, (const char*)K + s * d.dk * esz, (const char*)Q + s * d.dk * esz,
                    (const char*)V + s * dv * esz, theta + go, eta + go, alpha + go, win ? gamma + s : nullptr,
                    Span{C, T, per_chunk ? nch : T}, Y ? (void*)((char*)Y + s * dv * (d.out_bf16 ? 2 : 4)) : nullptr,
                    st);
@@ -968,6 +1002,53 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
                          ws + L.gs, C, c, R, M, ws + L.ow, ws + L.os, ws + L.sw, ws + L.ss);
       AM_LAUNCH_CHECK();
     }
+    const bool lin = d.kind == ATLASMEM_LINEAR;
+    if (lin) {
+      // the linear memory M(x) = W x: E = 2 (X W^T - V), g_r = E_r x_r^T
+      const float* cW0 = ck;
+      const bk::Cat lk = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
+      launch_gemm<false, false>(true, R, dv, din, M, lk, bk::cat1(bk::src(cW0, 0, 2 * P, din, 1, dv, din)),
+                                bk::EpiE{E, vz, Vr, vbf, vrz, dv, nullptr, 0, 0}, st);
+      launch_gemm<false, false>(true, R, dv, din, M, lk, bk::cat1(bk::src(WA, 0, P, din, 1, dv, din)),
+                                bk::EpiSt{U2, vz, dv}, st);
+      launch_gemm<false, false>(true, R, dv, din, M, lk, bk::cat1(bk::src(SA, 0, P, din, 1, dv, din)),
+                                bk::EpiSt{U2s, vz, dv}, st);
+      hipLaunchKernelGGL(bk::lin_row_kernel, dim3(R, M), dim3(64), 0, st, E, U2, U2s, vz, dv, rld, rW, rS, cWa, cSa,
+                         win ? dV : dV + s * dv, T * dv, s - (c - 1), win ? 1 : 0);
+      AM_LAUNCH_CHECK();
+      // X' = -(oW E) WA - (oS E) SA + 2 E' W   (B(k=v, j=f) = M[v][f])
+      const bk::EpiStAdd out = feat ? bk::EpiStAdd{ws + L.xg, (int64_t)R * din, din, nullptr, 0, 0, 0.0f, 0, 0}
+                               : win ? bk::EpiStAdd{dK, T * din, din, nullptr, 0, 0, 0.0f, s - (c - 1), 1}
+                                     : bk::EpiStAdd{dK + s * din, T * din, din, nullptr, 0, 0, 0.0f, 0, 0};
+      launch_gemm<false, false>(
+          true, R, din, 3 * dv, M,
+          bk::cat3(bk::src(E, 0, vz, dv, 1, R, dv, 2, rW, rld, -1.0f), bk::src(E, 0, vz, dv, 1, R, dv, 2, rS, rld, -1.0f),
+                   bk::src(U2, 0, vz, dv, 1, R, dv, 0, nullptr, 0, 2.0f), dv, 2 * dv),
+          bk::cat3(bk::src(WA, 0, P, 1, din, din, dv), bk::src(SA, 0, P, 1, din, din, dv),
+                   bk::src(cW0, 0, 2 * P, 1, din, din, dv), dv, 2 * dv),
+          out, st);
+      // Q' = dY W
+      launch_gemm<false, false>(true, C, din, dv, M, bk::cat1(bk::src(dY + s * dv, 0, T * dv, dv, 1, C, dv)),
+                                bk::cat1(bk::src(cW0, 0, 2 * P, 1, din, din, dv)),
+                                feat ? bk::EpiStAdd{ws + L.qg, (int64_t)C * din, din, nullptr, 0, 0, 0.0f, 0, 0}
+                                     : bk::EpiStAdd{dQ + s * din, T * din, din, nullptr, 0, 0, 0.0f, 0, 0},
+                                st);
+      // W' = (2E')^T X + dY^T Q   (A(i=v, k=row), B(k=row, j=f))
+      launch_gemm<false, false>(
+          true, dv, din, R + C, M,
+          bk::cat2(bk::src(U2, 0, vz, 1, dv, dv, R, 0, nullptr, 0, 2.0f), bk::src(dY + s * dv, 0, T * dv, 1, dv, dv, C),
+                   R),
+          bk::cat2(bk::src(Kr, kbf, kz, 1, din, din, R), bk::src(Qr, qbf, qz, 1, din, din, C), R),
+          bk::EpiSt{Wb, P, din}, st);
+      AM_LAUNCH_CHECK();
+      if (feat) {
+        hipLaunchKernelGGL(bk::feat_jac_kernel, dim3(R, M), dim3(64), 0, st, ws + L.xg, ws + L.ks, R, d.dk, din, T,
+                           s - (c - 1), win ? 1 : 0, dK);
+        hipLaunchKernelGGL(bk::feat_jac_kernel, dim3(C, M), dim3(64), 0, st, ws + L.qg, ws + L.qs, C, d.dk, din, T,
+                           s, 0, dQ);
+        AM_LAUNCH_CHECK();
+      }
+    } else {
     // Z of key and query rows
     {  // rows [0, R) keys, [R, R + C) queries (two launches into the two parts)
       bk::Cat lk = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
@@ -1124,6 +1205,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat lb = bk::cat2(bk::src(Kr, kbf, kz, 1, din, din, R), bk::src(Qr, qbf, qz, 1, din, din, C), R);
       launch_gemm<false, false>(true, dh, din, R + C, M, la, lb, bk::EpiSt{Wb, P, din}, st);
     }
+    }  // MLP memory
     AM_LAUNCH_CHECK();
     const int64_t n = (int64_t)M * P;
     if (per_chunk) {
