@@ -158,7 +158,22 @@ def _dev(torch, a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def stage_rooflines(torch, am, synth, dev, stream, only=None):
+def _oracle_backward_sample(synth, inp, Tn):
+    """The fp64 autograd oracle of the outer-loop backward on memory 0's first Tn tokens."""
+    import oracle
+    from oracle import backward as bw
+    s = inp.spec
+    cfg = oracle.config_from(s)
+    f64 = lambda a: synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+    ng = Tn if s.gate_mode == synth.PER_TOKEN else Tn // s.chunk
+    dY = np.random.default_rng(5).standard_normal((Tn, s.d_value))
+    bw.outer_grads(cfg, oracle.unflatten(cfg, inp.W0[0].astype(np.float64)),
+                   oracle.unflatten(cfg, inp.S0[0].astype(np.float64)), f64(inp.K[0, :Tn]), f64(inp.Q[0, :Tn]),
+                   f64(inp.V[0, :Tn]), inp.theta[0, :ng], inp.eta[0, :ng], inp.alpha[0, :ng], dY)
+    return Tn
+
+
+def stage_rooflines(torch, am, synth, dev, stream, only=None, cpu=False):
     """Stand-alone stages, each against its own roofline: the gate scan, Omega coefficients and
     feature map against HBM bandwidth (algorithmic bytes), Newton-Schulz against the bf16 matrix
     peak (algorithmic FLOPs).  Sizes are large enough for the launch to be bandwidth- or
@@ -267,11 +282,12 @@ def stage_rooflines(torch, am, synth, dev, stream, only=None):
         ("feature_project_deg2", lambda: am.feature_map(X, synth.BF16, NP, d, 2, Fproj, P=Pproj, d_out=FDO),
          2 * NP * F.shape[1] * FDO, "mfma", f"{NP} bf16 vectors of width {d}: degree-2 features x {FDO}-row projection"),
         ("outer_backward", backward_call, bwork, "mfma",
-         f"{bs.name} stabilised: forward with checkpoints and backward, {BM} memories x {BT} tokens"),
+         f"{bs.name} stabilised: forward with checkpoints and backward, {BM} memories x {BT} tokens",
+         lambda: _oracle_backward_sample(synth, bi, 2 * bs.chunk)),
         ("outer_backward_ns5", backward_ns_call, nwork, "mfma",
          f"64 -> 128 -> 64 memory, chunk 128, per-chunk gates, 5 Newton-Schulz steps, forward with checkpoints "
          f"and backward, "
-         f"{NMm} memories x {NT} tokens"),
+         f"{NMm} memories x {NT} tokens", lambda: _oracle_backward_sample(synth, ni, ns_.chunk)),
     ]
     # the memory variants and the general per-chunk path at the Newton-Schulz workload's shape
     # (128 memories, 64 -> 128 -> 64, chunk 128, 5 steps), over the first 4096 tokens
@@ -291,15 +307,20 @@ def stage_rooflines(torch, am, synth, dev, stream, only=None):
             vm.set_state(W0v, S0v)
             vm.update_chunked(vd["K"], vd["Q"], vd["V"], vd["theta"], vd["eta"], vd["alpha"], None, vs.T, Yv)
         work = vs.n_mem * (vs.T // vs.chunk) * sum(flops_fn(vs).values())
+
+        def sample():
+            import oracle
+            oracle.run_inputs(vi, mems=[0], T=2 * vs.chunk)
+            return 2 * vs.chunk
         return (call, work, f"{label}: {vs.n_mem} memories x {vs.T} tokens, 64 -> 128 -> 64, chunk {vs.chunk}, "
-                            f"{vs.ns_steps} Newton-Schulz steps")
+                            f"{vs.ns_steps} Newton-Schulz steps", sample)
     if only is None or only in ("update_general_ns5", "update_residual_ns5", "update_gated_ns5"):
         ug = update_case({}, am.FLAG_NO_FUSED, "general per-chunk path (fused kernel off)", mlp_flops_per_chunk)
         ur = update_case(dict(kind=synth.MLP2_SILU_RESIDUAL), 0, "residual memory", mlp_flops_per_chunk)
         ugt = update_case(dict(kind=synth.MLP2_GATED), 0, "gated memory (W1, W3, W2)", gated_flops_per_chunk)
-        cases += [("update_general_ns5", ug[0], ug[1], "mfma", ug[2]),
-                  ("update_residual_ns5", ur[0], ur[1], "mfma", ur[2]),
-                  ("update_gated_ns5", ugt[0], ugt[1], "mfma", ugt[2])]
+        cases += [("update_general_ns5",) + ug[:2] + ("mfma",) + ug[2:],
+                  ("update_residual_ns5",) + ur[:2] + ("mfma",) + ur[2:],
+                  ("update_gated_ns5",) + ugt[:2] + ("mfma",) + ugt[2:]]
     # per-token retrieval at the per-token workload's shape (8 memories x 4096 tokens, chunk 64)
     if only is None or only == "update_per_token_retrieve":
         pi = synth.make_inputs(1, "stabilised", per_token_retrieve=True)
@@ -315,9 +336,14 @@ def stage_rooflines(torch, am, synth, dev, stream, only=None):
         def ptr_call():
             pm.set_state(W0p, S0p)
             pm.update_chunked(pd["K"], pd["Q"], pd["V"], pd["theta"], pd["eta"], pd["alpha"], None, ps.T, Yp)
+        def ptr_sample():
+            import oracle
+            oracle.run_inputs(pi, mems=[0], T=2 * ps.chunk)
+            return 2 * ps.chunk
         cases.append(("update_per_token_retrieve", ptr_call,
                       ps.n_mem * (ps.T // ps.chunk) * sum(ptr_flops_per_chunk(ps).values()), "mfma",
-                      f"{ps.name}: queries read the state after their own token, {ps.n_mem} memories x {ps.T} tokens"))
+                      f"{ps.name}: queries read the state after their own token, {ps.n_mem} memories x {ps.T} tokens",
+                      ptr_sample))
     # decoding: one token per call through the streaming path (the chunk's update runs on the
     # call that completes it), 128 memories of the Newton-Schulz workload over two chunks.  Its
     # algorithmic bytes per call: every memory's weights read for the query (fp32), the token's
@@ -340,10 +366,15 @@ def stage_rooflines(torch, am, synth, dev, stream, only=None):
             for tk in toks:
                 dm.update_chunked(tk["K"], tk["Q"], tk["V"], tk["th"], tk["et"], tk["al"], None, 1, Yd)
         dbytes = ds.T * ds.n_mem * (dm.P * 4 + (2 * ds.d_key + ds.d_value) * 2 + ds.d_value * 4)
+        def decode_sample():
+            import oracle
+            oracle.run_inputs(di, mems=[0], T=ds.T)
+            return ds.T
         cases.append(("decode_one_token_calls", decode_call, dbytes, "hbm",
                       f"{ds.n_mem} memories x {ds.T} tokens, one token per call (two chunks of {ds.chunk}), "
-                      f"64 -> 128 -> 64, 5 Newton-Schulz steps"))
-    for name, fn, work, bound, shape in cases:
+                      f"64 -> 128 -> 64, 5 Newton-Schulz steps", decode_sample))
+    for case in cases:
+        name, fn, work, bound, shape = case[:5]
         if only is not None and name != only:
             continue
         for _ in range(3):
@@ -358,6 +389,18 @@ def stage_rooflines(torch, am, synth, dev, stream, only=None):
             out[name] = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                              frac=round(ach / PEAK_BF16_TFLOPS, 5), algorithmic_flops=int(work), ms=round(t, 5),
                              shape=shape)
+        if cpu and len(case) > 5:
+            # the fp64 oracle on a small sample of the same workload, one process, for context
+            # (repeated until half a second has passed, for a steadier rate)
+            t0 = time.perf_counter()
+            ntok, reps = 0, 0
+            with np.errstate(all="ignore"):
+                while reps == 0 or time.perf_counter() - t0 < 0.5:
+                    ntok += case[5]()
+                    reps += 1
+            dt = time.perf_counter() - t0
+            out[name]["cpu_oracle"] = dict(tokens_per_s=round(ntok / dt, 1), cores=1, kind="oracle",
+                                           sample=f"memory 0, first {ntok // reps} tokens, {reps} runs, {dt:.2f} s")
     return out
 
 
@@ -537,7 +580,7 @@ def main():
         check = dict(memory=m, status=st, Y=rel(Y[m].cpu().numpy(), Yr[0]), W=rel(Wg[m].cpu().numpy(), Wr[0]),
                      S=rel(Sg[m].cpu().numpy(), Sr[0]))
 
-    stages = None if args.no_stages else stage_rooflines(torch, am, synth, dev, stream)
+    stages = None if args.no_stages else stage_rooflines(torch, am, synth, dev, stream, cpu=not args.no_cpu)
 
     cpu = None
     if not args.no_cpu:
