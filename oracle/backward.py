@@ -52,6 +52,8 @@ def _poly(x, degree):
 def _apply(params, x, residual=False):
     if len(params) == 1:
         return params[0] @ x
+    if len(params) == 3:  # the gated memory [W1, W3, W2]: W2 (silu(W1 x) * (W3 x))
+        return params[2] @ (_silu(params[0] @ x) * (params[1] @ x))
     y = params[1] @ _silu(params[0] @ x)
     return x + y if residual else y
 
@@ -62,6 +64,17 @@ def _grad(params, x, v, residual=False):
     the residual memory x + W2 silu(W1 x) has e = 2 (W2 h + x - v) (ATLAS summary, section 5.1)."""
     if len(params) == 1:
         return [torch.outer(2.0 * (params[0] @ x - v), x)]
+    if len(params) == 3:
+        # the gated memory (ATLAS summary, section 5.1): a = silu(z1), h = a * z3, e = 2 (W2 h - v),
+        # b = W2^T e: (b * z3 * silu'(z1)) x^T, (b * a) x^T, e h^T
+        w1, w3, w2 = params
+        z1, z3 = w1 @ x, w3 @ x
+        s1 = torch.sigmoid(z1)
+        a = z1 * s1
+        e = 2.0 * (w2 @ (a * z3) - v)
+        b = w2.T @ e
+        sp = s1 * (1.0 + z1 * (1.0 - s1))
+        return [torch.outer(b * z3 * sp, x), torch.outer(b * a, x), torch.outer(e, a * z3)]
     w1, w2 = params
     z = w1 @ x
     s = torch.sigmoid(z)

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, PER_CHUNK, PER_TOKEN, MemoryConfig
+from oracle import LINEAR, MLP2_GATED, MLP2_SILU, MLP2_SILU_RESIDUAL, PER_CHUNK, PER_TOKEN, MemoryConfig
 from oracle import backward as bw
 
 
@@ -18,6 +18,8 @@ def problem(seed, kind, T=8, C=4, d=3, v=2, h=5, mode=PER_TOKEN, ns=0, c=1, poly
     cfg = MemoryConfig(kind, d, v, h if kind != LINEAR else 0, poly, C, c, mode, ns)
     if kind == LINEAR:
         params = [r.normal(0, 0.5, (v, din))]
+    elif kind == MLP2_GATED:
+        params = [r.normal(0, 0.5, (h, din)), r.normal(0, 0.5, (h, din)), r.normal(0, 0.5, (v, h))]
     else:
         params = [r.normal(0, 0.5, (h, din)), r.normal(0, 0.5, (v, h))]
     momenta = [r.normal(0, 0.1, p.shape) for p in params]
@@ -44,7 +46,8 @@ MODES = [(LINEAR, PER_TOKEN, 0, 1, 1), (MLP2_SILU, PER_TOKEN, 0, 1, 1), (MLP2_SI
          (MLP2_SILU, PER_CHUNK, 5, 1, 1), (LINEAR, PER_CHUNK, 5, 1, 1), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 1, 1),
          (MLP2_SILU_RESIDUAL, PER_CHUNK, 5, 1, 1), (MLP2_SILU, PER_TOKEN, 0, 3, 1),
          (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 2, 1), (LINEAR, PER_TOKEN, 0, 3, 1), (MLP2_SILU, PER_TOKEN, 0, 6, 1),
-         (MLP2_SILU, PER_TOKEN, 0, 3, 2), (MLP2_SILU, PER_TOKEN, 0, 1, 2), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 2, 2)]
+         (MLP2_SILU, PER_TOKEN, 0, 3, 2), (MLP2_SILU, PER_TOKEN, 0, 1, 2), (MLP2_SILU_RESIDUAL, PER_TOKEN, 0, 2, 2),
+         (MLP2_GATED, PER_TOKEN, 0, 1, 1), (MLP2_GATED, PER_TOKEN, 0, 3, 2), (MLP2_GATED, PER_CHUNK, 5, 1, 1)]
 
 
 @pytest.mark.parametrize("kind,mode,ns,c,poly", MODES)
