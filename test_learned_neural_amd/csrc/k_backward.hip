@@ -48,16 +48,18 @@ struct Src {
   int bf16;
   int64_t sz, so, sk;
   int outer_dim, K;
-  int xf;  // 0 none, 1 silu, 2 times coef[z * cz + outer]
+  int xf;  // 0 none, 1 silu, 2 times coef[z * cz + outer], 3 silu(x) times the element gofs further on
   const float* coef;
   int64_t cz;
   float scale;
+  int64_t gofs;  // xf 3: the gated memory's silu(Z1) * Z3 with Z3 beside Z1 (fp32 sources)
   __device__ __forceinline__ float get(int z, int outer, int k) const {
     if (outer >= outer_dim || k >= K) return 0.0f;
     const int64_t i = (int64_t)z * sz + (int64_t)outer * so + (int64_t)k * sk;
     float x = bf16 ? bf16_value(((const uint16_t*)base)[i]) : ((const float*)base)[i];
     if (xf == 1) x = siluf_(x);
     else if (xf == 2) x *= coef[(int64_t)z * cz + outer];
+    else if (xf == 3) x = siluf_(x) * ((const float*)base)[i + gofs];
     return x * scale;
   }
 };
@@ -77,6 +79,14 @@ __host__ __device__ inline Src src(const void* base, int bf16, int64_t sz, int64
   s.coef = coef;
   s.cz = cz;
   s.scale = scale;
+  s.gofs = 0;
+  return s;
+}
+// the gated hidden activation silu(Z1) * Z3 of rows laid out as [Z1 | Z3] (Z3 at offset gofs)
+__host__ __device__ inline Src gated(const float* base, int64_t sz, int64_t so, int64_t sk, int outer_dim, int K,
+                                     int64_t gofs) {
+  Src s = src(base, 0, sz, so, sk, outer_dim, K, 3);
+  s.gofs = gofs;
   return s;
 }
 
@@ -200,6 +210,52 @@ struct EpiStAdd {  // out = acc (+ scale * add[z * az + row * ald + col] when ad
   }
 };
 
+// Gated memory (rows of Z are [Z1 | Z3], dh each; a = silu(Z1)):
+// b = acc (= E W2), D1 = b Z3 silu'(Z1), D3 = b a  -> B [row][dh], D [row][D1 | D3]
+struct EpiPDg {
+  float* B;
+  float* D;
+  const float* Z;
+  int64_t bz, dzz, zz;
+  int dh;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    const float* zr = Z + (int64_t)z * zz + (int64_t)row * 2 * dh;
+    const float z1 = zr[col], z3 = zr[dh + col];
+    B[(int64_t)z * bz + (int64_t)row * dh + col] = v;
+    float* dr = D + (int64_t)z * dzz + (int64_t)row * 2 * dh;
+    dr[col] = v * z3 * silu_primef_(z1);
+    dr[dh + col] = v * siluf_(z1);
+  }
+};
+// H' = acc: Za1 += H' Z3 silu'(Z1), Za3 += H' a (in place)
+struct EpiZag {
+  float* Za;
+  const float* Z;
+  int64_t az, zz;
+  int dh;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    const float* zr = Z + (int64_t)z * zz + (int64_t)row * 2 * dh;
+    const float z1 = zr[col], z3 = zr[dh + col];
+    float* ar = Za + (int64_t)z * az + (int64_t)row * 2 * dh;
+    ar[col] += v * z3 * silu_primef_(z1);
+    ar[dh + col] += v * siluf_(z1);
+  }
+};
+// query rows: hq' = acc (= dY W2): Zq1' = hq' Zq3 silu'(Zq1), Zq3' = hq' silu(Zq1) (Zq: rows zr0..)
+struct EpiScaleSpG {
+  float* out;
+  const float* Z;
+  int64_t oz, zz;
+  int zr0, dh;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    const float* zr = Z + (int64_t)z * zz + (int64_t)(zr0 + row) * 2 * dh;
+    const float z1 = zr[col], z3 = zr[dh + col];
+    float* o = out + (int64_t)z * oz + (int64_t)row * 2 * dh;
+    o[col] = v * z3 * silu_primef_(z1);
+    o[dh + col] = v * siluf_(z1);
+  }
+};
+
 struct EpiAxpy {  // out = alpha * x + beta * acc (out may alias x: same element, same thread)
   float* out;
   const float* x;
@@ -299,6 +355,56 @@ __global__ void lin_row_kernel(const float* __restrict__ E, float* __restrict__ 
     if (!acc) dV[(int64_t)z * dvz + (int64_t)r * dv + j] = -2.0f * ea;
     else if (tau0 + r >= 0) dV[(int64_t)z * dvz + (tau0 + r) * dv + j] += -2.0f * ea;
   }
+}
+
+// The gated memory's rows: coefficient adjoints -(<D, U1> + <E, U2>) (D = [D1 | D3], dz = 2 dh
+// wide) and likewise with U1s, U2s; D' = -(cW U1 + cS U1s), then
+//   b' = D1' Z3 s'(Z1) + D3' a                     (into U1s[:, :dh])
+//   Za1 = D1' b Z3 s''(Z1) + D3' b s'(Z1),  Za3 = D1' b s'(Z1)   (into Za)
+//   E'_g = -(cW U2 + cS U2s)                       (in U2)
+// Each lane reads and then overwrites only its own elements (j and dh + j together).
+__global__ void row_kernel_gated(const float* __restrict__ Z, int64_t zz, const float* __restrict__ B,
+                                 int64_t bz, const float* __restrict__ D, float* __restrict__ U1,
+                                 float* __restrict__ U1s, int64_t uz, float* __restrict__ Za,
+                                 const float* __restrict__ E, float* __restrict__ U2, const float* __restrict__ U2s,
+                                 int64_t vz, int dh, int dv, int C, const float* __restrict__ cW,
+                                 const float* __restrict__ cS, float* __restrict__ cWa, float* __restrict__ cSa) {
+  const int r = blockIdx.x, z = blockIdx.y, lane = threadIdx.x, dz = 2 * dh;
+  const int64_t ho = (int64_t)z * uz + (int64_t)r * dz, vo = (int64_t)z * vz + (int64_t)r * dv;
+  float s1 = 0.0f, s1s = 0.0f, s2 = 0.0f, s2s = 0.0f;
+  for (int j = lane; j < dz; j += 64) {
+    s1 += D[ho + j] * U1[ho + j];
+    s1s += D[ho + j] * U1s[ho + j];
+  }
+  for (int j = lane; j < dv; j += 64) {
+    s2 += E[vo + j] * U2[vo + j];
+    s2s += E[vo + j] * U2s[vo + j];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    s1 += __shfl_xor(s1, off, 64);
+    s1s += __shfl_xor(s1s, off, 64);
+    s2 += __shfl_xor(s2, off, 64);
+    s2s += __shfl_xor(s2s, off, 64);
+  }
+  const float cw = cW[(int64_t)z * C + r], cs = cS[(int64_t)z * C + r];
+  if (lane == 0) {
+    cWa[(int64_t)z * C + r] = -(s1 + s2);
+    cSa[(int64_t)z * C + r] = -(s1s + s2s);
+  }
+  const float* zr = Z + (int64_t)z * zz + (int64_t)r * dz;
+  const float* br = B + (int64_t)z * bz + (int64_t)r * dh;
+  for (int j = lane; j < dh; j += 64) {
+    const float z1 = zr[j], z3 = zr[dh + j], b = br[j];
+    const float sg = sigmoidf_(z1), a = z1 * sg;
+    const float sp = sg * (1.0f + z1 * (1.0f - sg)), spp = silu_second(z1);
+    const float d1a = -(cw * U1[ho + j] + cs * U1s[ho + j]);
+    const float d3a = -(cw * U1[ho + dh + j] + cs * U1s[ho + dh + j]);
+    U1s[ho + j] = d1a * z3 * sp + d3a * a;  // b'
+    Za[ho + j] = d1a * b * z3 * spp + d3a * b * sp;
+    Za[ho + dh + j] = d1a * b * sp;
+  }
+  for (int j = lane; j < dv; j += 64) U2[vo + j] = -(cw * U2[vo + j] + cs * U2s[vo + j]);  // E'_g
 }
 
 // beta' = <WA, W>, aS' = <WA, S>, PC' = <SA, S> per memory; ck: [M][2P] (W then S).
@@ -695,6 +801,7 @@ struct BwdLayout {
   int64_t R;  // key rows per chunk: C, or C + c - 1 with an Omega window
   int64_t ow, os, sw, ss, cwt, cst, ks, vs, gs, hk0, hv0, hg0;  // Omega window buffers
   int64_t qs, xg, qg;  // polynomial features: query features, feature-space gradients of keys / queries
+  int64_t za;          // gated memory: the first-layer pre-activation adjoints [R][dz]
   int64_t gb, nb, nab, gab, sat;
   NsLay ns[2];
   int nns;  // Newton-Schulz batches: 1 when both matrices share a working shape, else 2
@@ -718,15 +825,17 @@ static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
   L.sa0 = take(M * P);
   L.sa1 = take(M * P);
   L.wb = take(M * P);
-  L.zk = take(M * (R + C) * dh);
+  const int64_t dz = d.dz;  // first-layer rows: dh, or 2 dh for the gated memory ([W1; W3])
+  L.zk = take(M * (R + C) * dz);
   L.e = take(M * R * dv);
   L.pz = take(M * R * dh);
-  L.d1 = take(M * R * dh);
-  L.u1 = take(M * R * dh);
-  L.u1s = take(M * R * dh);
+  L.d1 = take(M * R * dz);
+  L.u1 = take(M * R * dz);
+  L.u1s = take(M * R * dz);
   L.u2 = take(M * R * dv);
   L.u2s = take(M * R * dv);
-  L.zqa = take(M * R * dh);
+  L.zqa = take(M * R * dz);
+  L.za = d.gated ? take(M * R * dz) : 0;
   L.cw = take(M * C);
   L.cs = take(M * C);
   L.cwa = take(M * R);
@@ -878,7 +987,8 @@ static atlasmem_status ns_backward(const Dims& d, float* ws, const NsLay& n, con
 
 bool backward_supported(const Dims& d) {
   if (d.kind == ATLASMEM_LINEAR) return !d.ptr && d.poly <= 2 && d.gate_mode == ATLASMEM_PER_TOKEN;
-  return d.kind == ATLASMEM_MLP2_SILU && !d.gated && !d.ptr && d.poly <= 2 &&
+  if (d.gated) return !d.ptr && d.poly <= 2 && d.gate_mode == ATLASMEM_PER_TOKEN;
+  return d.kind == ATLASMEM_MLP2_SILU && !d.ptr && d.poly <= 2 &&
          (d.gate_mode == ATLASMEM_PER_CHUNK ? d.c == 1 && d.poly == 1 : d.ns_steps == 0);
 }
 
@@ -1040,6 +1150,96 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
                    R),
           bk::cat2(bk::src(Kr, kbf, kz, 1, din, din, R), bk::src(Qr, qbf, qz, 1, din, din, C), R),
           bk::EpiSt{Wb, P, din}, st);
+      AM_LAUNCH_CHECK();
+      if (feat) {
+        hipLaunchKernelGGL(bk::feat_jac_kernel, dim3(R, M), dim3(64), 0, st, ws + L.xg, ws + L.ks, R, d.dk, din, T,
+                           s - (c - 1), win ? 1 : 0, dK);
+        hipLaunchKernelGGL(bk::feat_jac_kernel, dim3(C, M), dim3(64), 0, st, ws + L.qg, ws + L.qs, C, d.dk, din, T,
+                           s, 0, dQ);
+        AM_LAUNCH_CHECK();
+      }
+    } else if (d.gated) {
+      // the gated memory M(x) = W2 (silu(Z1) * Z3): Z rows are [Z1 | Z3] (dz = 2 dh), first-layer
+      // weights [W1; W3] one block; b = E W2, D = [b Z3 silu'(Z1) | b silu(Z1)]
+      const int dzz = 2 * dh;
+      const int64_t gzz = (int64_t)(R + C) * dzz, gz = (int64_t)R * dzz;
+      float* Za = ws + L.za;
+      {
+        bk::Cat lk = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
+        bk::Cat lq = bk::cat1(bk::src(Qr, qbf, qz, din, 1, C, din));
+        bk::Cat lb = bk::cat1(bk::src(cW1, 0, 2 * P, din, 1, dzz, din));
+        launch_gemm<false, false>(true, R, dzz, din, M, lk, lb, bk::EpiSt{Zk, gzz, dzz}, st);
+        launch_gemm<false, false>(true, C, dzz, din, M, lq, lb, bk::EpiSt{Zk + (int64_t)R * dzz, gzz, dzz}, st);
+      }
+      const bk::Src hk = bk::gated(Zk, gzz, dzz, 1, R, dh, dh);  // H of the key rows, A(i = row, k = h)
+      launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(hk), bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh)),
+                                bk::EpiE{E, vz, Vr, vbf, vrz, dv, nullptr, 0, 0}, st);
+      launch_gemm<false, false>(true, R, dh, dv, M, bk::cat1(bk::src(E, 0, vz, dv, 1, R, dv)),
+                                bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv)),
+                                bk::EpiPDg{Pz, D1, Zk, hz, gz, gzz, dh}, st);
+      {  // U1 = X WAz^T, U1s = X SAz^T (dz wide), U2 = H WA2^T, U2s = H SA2^T
+        bk::Cat lx = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
+        launch_gemm<false, false>(true, R, dzz, din, M, lx, bk::cat1(bk::src(WA, 0, P, din, 1, dzz, din)),
+                                  bk::EpiSt{U1, gz, dzz}, st);
+        launch_gemm<false, false>(true, R, dzz, din, M, lx, bk::cat1(bk::src(SA, 0, P, din, 1, dzz, din)),
+                                  bk::EpiSt{U1s, gz, dzz}, st);
+        launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(hk), bk::cat1(bk::src(WA + P1, 0, P, dh, 1, dv, dh)),
+                                  bk::EpiSt{U2, vz, dv}, st);
+        launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(hk), bk::cat1(bk::src(SA + P1, 0, P, dh, 1, dv, dh)),
+                                  bk::EpiSt{U2s, vz, dv}, st);
+      }
+      hipLaunchKernelGGL(bk::row_kernel_gated, dim3(R, M), dim3(64), 0, st, Zk, gzz, Pz, hz, D1, U1, U1s, gz, Za, E,
+                         U2, U2s, vz, dh, dv, rld, rW, rS, cWa, cSa);
+      AM_LAUNCH_CHECK();
+      {  // E' = E'_g + b' W2^T (b' in U1s[:, :dh]), dV = -2 E'
+        const bk::EpiEa ep = win ? bk::EpiEa{U2, vz, dV, T * dv, dv, s - (c - 1), 1}
+                                 : bk::EpiEa{U2, vz, dV + s * dv, T * dv, dv, 0, 0};
+        launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(bk::src(U1s, 0, gz, dzz, 1, R, dh)),
+                                  bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh)), ep, st);
+      }
+      {  // W2' = E^T b' + (2E')^T H + dY^T Hq
+        bk::Cat la = bk::cat3(bk::src(E, 0, vz, 1, dv, dv, R), bk::src(U2, 0, vz, 1, dv, dv, R, 0, nullptr, 0, 2.0f),
+                              bk::src(dY + s * dv, 0, T * dv, 1, dv, dv, C), R, 2 * R);
+        bk::Cat lb = bk::cat3(bk::src(U1s, 0, gz, 1, dzz, dh, R), bk::gated(Zk, gzz, 1, dzz, dh, R, dh),
+                              bk::gated(Zk + (int64_t)R * dzz, gzz, 1, dzz, dh, C, dh), R, 2 * R);
+        launch_gemm<false, false>(true, dv, dh, 2 * R + C, M, la, lb, bk::EpiSt{Wb + P1, P, dh}, st);
+      }
+      // H' = -(cW E) WA2 - (cS E) SA2 + (2E') W2, scattered into Za through the gate
+      launch_gemm<false, false>(
+          true, R, dh, 3 * dv, M,
+          bk::cat3(bk::src(E, 0, vz, dv, 1, R, dv, 2, rW, rld, -1.0f), bk::src(E, 0, vz, dv, 1, R, dv, 2, rS, rld, -1.0f),
+                   bk::src(U2, 0, vz, dv, 1, R, dv, 0, nullptr, 0, 2.0f), dv, 2 * dv),
+          bk::cat3(bk::src(WA + P1, 0, P, 1, dh, dh, dv), bk::src(SA + P1, 0, P, 1, dh, dh, dv),
+                   bk::src(cW2, 0, 2 * P, 1, dh, dh, dv), dv, 2 * dv),
+          bk::EpiZag{Za, Zk, gz, gzz, dh}, st);
+      {  // X' = -(cW D) WAz - (cS D) SAz + Za Wz
+        const bk::EpiStAdd out = feat ? bk::EpiStAdd{ws + L.xg, (int64_t)R * din, din, nullptr, 0, 0, 0.0f, 0, 0}
+                                 : win ? bk::EpiStAdd{dK, T * din, din, nullptr, 0, 0, 0.0f, s - (c - 1), 1}
+                                       : bk::EpiStAdd{dK + s * din, T * din, din, nullptr, 0, 0, 0.0f, 0, 0};
+        launch_gemm<false, false>(
+            true, R, din, 3 * dzz, M,
+            bk::cat3(bk::src(D1, 0, gz, dzz, 1, R, dzz, 2, rW, rld, -1.0f),
+                     bk::src(D1, 0, gz, dzz, 1, R, dzz, 2, rS, rld, -1.0f), bk::src(Za, 0, gz, dzz, 1, R, dzz), dzz,
+                     2 * dzz),
+            bk::cat3(bk::src(WA, 0, P, 1, din, din, dzz), bk::src(SA, 0, P, 1, din, din, dzz),
+                     bk::src(cW1, 0, 2 * P, 1, din, din, dzz), dzz, 2 * dzz),
+            out, st);
+      }
+      {  // Zq' through the gate, Q' = Zq' Wz
+        launch_gemm<false, false>(true, C, dh, dv, M, bk::cat1(bk::src(dY + s * dv, 0, T * dv, dv, 1, C, dv)),
+                                  bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv)),
+                                  bk::EpiScaleSpG{Zqa, Zk, gz, gzz, R, dh}, st);
+        launch_gemm<false, false>(true, C, din, dzz, M, bk::cat1(bk::src(Zqa, 0, gz, dzz, 1, C, dzz)),
+                                  bk::cat1(bk::src(cW1, 0, 2 * P, 1, din, din, dzz)),
+                                  feat ? bk::EpiStAdd{ws + L.qg, (int64_t)C * din, din, nullptr, 0, 0, 0.0f, 0, 0}
+                                       : bk::EpiStAdd{dQ + s * din, T * din, din, nullptr, 0, 0, 0.0f, 0, 0},
+                                  st);
+      }
+      {  // Wz' = Za^T X + Zq'^T Q -> Wb
+        bk::Cat la = bk::cat2(bk::src(Za, 0, gz, 1, dzz, dzz, R), bk::src(Zqa, 0, gz, 1, dzz, dzz, C), R);
+        bk::Cat lb = bk::cat2(bk::src(Kr, kbf, kz, 1, din, din, R), bk::src(Qr, qbf, qz, 1, din, din, C), R);
+        launch_gemm<false, false>(true, dzz, din, R + C, M, la, lb, bk::EpiSt{Wb, P, din}, st);
+      }
       AM_LAUNCH_CHECK();
       if (feat) {
         hipLaunchKernelGGL(bk::feat_jac_kernel, dim3(R, M), dim3(64), 0, st, ws + L.xg, ws + L.ks, R, d.dk, din, T,

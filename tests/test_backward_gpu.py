@@ -52,6 +52,12 @@ CASES = [
     ("linear_C1", 0, "literal", dict(batch=1, heads=2, T=48)),
     ("linear_C4_window3", 0, "literal", dict(batch=2, heads=1, T=40, chunk=4, omega_window=3, d_key=20, d_value=12)),
     ("linear_poly2_C8", 0, "literal", dict(batch=1, heads=2, T=32, chunk=8, poly_degree=2, d_key=5, d_value=7)),
+    # the gated memory W2 (silu(W1 x) * W3 x): [W1; W3] one first-layer block
+    ("gated_mlp64_C64", 1, "stabilised", dict(kind=synth.MLP2_GATED, batch=1, heads=2, T=128)),
+    ("gated_ragged_C16", 1, "stabilised", dict(kind=synth.MLP2_GATED, batch=2, heads=1, T=48, d_key=20, d_value=12,
+                                                d_hidden=36, chunk=16)),
+    ("gated_omega3_poly2", 3, "stabilised", dict(kind=synth.MLP2_GATED, batch=1, heads=2, T=48, d_key=6, d_value=20,
+                                                  d_hidden=24, chunk=16, omega_window=3)),
 ]
 
 
@@ -129,7 +135,7 @@ def test_backward_matches_autograd_oracle(case):
 def test_backward_errors():
     import torch
     for s3 in (synth.spec(3, "stabilised", batch=1, heads=1, T=256, gate_mode=synth.PER_CHUNK, omega_window=1),
-               synth.spec(1, "stabilised", batch=1, heads=1, T=256, kind=synth.MLP2_GATED)):
+               synth.spec(4, "literal", batch=1, heads=1, T=256, kind=synth.MLP2_GATED)):  # gated, per chunk
         mem = am.Memory(config_for(s3))
         assert mem.backward_workspace_bytes(256) == -1
         mem.close()
