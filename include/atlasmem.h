@@ -245,11 +245,11 @@ atlasmem_status atlasmem_newton_schulz(const float* G, int64_t n_mat, int32_t ro
  * final state, with respect to every input of the update and the state it started from
  * (Atlas-Torch README, "How the memory works": the outer loop trains through the inner updates;
  * the derivative of the recurrence includes that of the inner gradient).
- * Scope: no per-token retrieval, and either PER_TOKEN gates (ns_steps 0) with any Omega window
- * and poly_degree 1 or 2 (gradients reach the raw keys and queries through the feature map) for
- * every memory kind, or PER_CHUNK gates (window 1, poly_degree 1) with or without the
- * Newton-Schulz orthogonalisation of the chunk gradient (its iteration differentiated step by
- * step) for MLP2_SILU and MLP2_SILU_RESIDUAL (E_UNSUPPORTED otherwise).  With a window > 1 the c - 1 rows of
+ * Scope: every memory kind without per-token retrieval, with either PER_TOKEN gates (ns_steps 0),
+ * any Omega window and poly_degree 1 or 2 (gradients reach the raw keys and queries through the
+ * feature map), or, for the 2-layer memories, PER_CHUNK gates (window 1, poly_degree 1) with or
+ * without the Newton-Schulz orthogonalisation of the chunk gradient (its iteration
+ * differentiated step by step) (E_UNSUPPORTED otherwise).  With a window > 1 the c - 1 rows of
  * window history the call starts with are constants of the call: gradients flow to this call's
  * tokens only (ATLAS summary, sections 3.2-3.3: the Omega rule over a sliding window);
  * T a multiple of the chunk and nothing pending (E_SHAPE otherwise).

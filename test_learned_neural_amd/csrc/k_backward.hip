@@ -696,14 +696,14 @@ __global__ void dot_kernel(const float* __restrict__ a, int64_t za, const float*
   if (threadIdx.x == 0) out[z] = red[0] + red[1] + red[2] + red[3];
 }
 
-// Geometry of one Newton-Schulz batch: slab z is matrix z / M (of nm matrices that share the
+// Geometry of one Newton-Schulz batch: slab z is matrix z / M (of nm <= 3 matrices that share the
 // working shape r x c) of memory z % M.  Matrix i lies at goff[i] in a memory's P parameters as
 // rows x cols; its working orientation is transposed when rows > cols.
 struct NsGeo {
   int M, nm;
   int64_t P;
-  int64_t goff[2];
-  int rows[2], cols[2], tr[2];
+  int64_t goff[3];
+  int rows[3], cols[3], tr[3];
 };
 
 // Element i of the batch (slab z, element e of the matrix in its own orientation): its index in
@@ -803,8 +803,8 @@ struct BwdLayout {
   int64_t qs, xg, qg;  // polynomial features: query features, feature-space gradients of keys / queries
   int64_t za;          // gated memory: the first-layer pre-activation adjoints [R][dz]
   int64_t gb, nb, nab, gab, sat;
-  NsLay ns[2];
-  int nns;  // Newton-Schulz batches: 1 when both matrices share a working shape, else 2
+  NsLay ns[3];
+  int nns;  // Newton-Schulz batches: the matrices (W1, [W3,] W2) grouped by working shape
   int64_t end;
 };
 
@@ -866,7 +866,7 @@ static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
   L.sca = take(M * 3);
   L.gb = L.nb = L.nab = L.gab = L.sat = 0;
   L.nns = 0;
-  for (int m = 0; m < 2; ++m) L.ns[m] = NsLay{};
+  for (int m = 0; m < 3; ++m) L.ns[m] = NsLay{};
   if (d.gate_mode == ATLASMEM_PER_CHUNK) {
     L.gb = take(M * P);
     L.nb = take(M * P);
@@ -875,29 +875,33 @@ static BwdLayout bwd_layout(const Dims& d, int64_t nchunks) {
     L.sat = take(M * P);
     if (d.ns_steps > 0) {
       const int steps = d.ns_steps;
-      const int shp[2][2] = {{(int)dh, d.din}, {(int)dv, (int)dh}};
-      const int64_t goff[2] = {0, d.P1};
-      int wr[2], wc[2];
-      for (int m = 0; m < 2; ++m) {
-        wr[m] = shp[m][0] < shp[m][1] ? shp[m][0] : shp[m][1];
-        wc[m] = shp[m][0] < shp[m][1] ? shp[m][1] : shp[m][0];
-      }
-      const bool paired = wr[0] == wr[1] && wc[0] == wc[1];
-      L.nns = paired ? 1 : 2;
-      for (int b = 0; b < L.nns; ++b) {
-        NsLay& n = L.ns[b];
+      // the matrices: W1 [dh][din], W3 [dh][din] (gated, after W1), W2 [dv][dh] at P1
+      int nmat = 0, shp[3][2];
+      int64_t goff[3];
+      shp[nmat][0] = (int)dh; shp[nmat][1] = d.din; goff[nmat++] = 0;
+      if (d.gated) { shp[nmat][0] = (int)dh; shp[nmat][1] = d.din; goff[nmat++] = (int64_t)dh * d.din; }
+      shp[nmat][0] = (int)dv; shp[nmat][1] = (int)dh; goff[nmat++] = d.P1;
+      bool done[3] = {false, false, false};
+      L.nns = 0;
+      for (int m0 = 0; m0 < nmat; ++m0) {
+        if (done[m0]) continue;
+        NsLay& n = L.ns[L.nns++];
+        n.r = shp[m0][0] < shp[m0][1] ? shp[m0][0] : shp[m0][1];
+        n.c = shp[m0][0] < shp[m0][1] ? shp[m0][1] : shp[m0][0];
         n.g.M = (int)M;
-        n.g.nm = paired ? 2 : 1;
+        n.g.nm = 0;
         n.g.P = P;
-        for (int j = 0; j < n.g.nm; ++j) {
-          const int m = paired ? j : b;
+        for (int m = m0; m < nmat; ++m) {  // every remaining matrix of this working shape
+          const int wr = shp[m][0] < shp[m][1] ? shp[m][0] : shp[m][1];
+          const int wc = shp[m][0] < shp[m][1] ? shp[m][1] : shp[m][0];
+          if (done[m] || wr != n.r || wc != n.c) continue;
+          done[m] = true;
+          const int j = n.g.nm++;
           n.g.goff[j] = goff[m];
           n.g.rows[j] = shp[m][0];
           n.g.cols[j] = shp[m][1];
           n.g.tr[j] = shp[m][0] > shp[m][1];
         }
-        n.r = wr[b];
-        n.c = wc[b];
         const int64_t S = (int64_t)n.g.nm * M;  // slabs
         const int64_t rc = (int64_t)n.r * n.c, rr = (int64_t)n.r * n.r;
         n.x = take(S * (steps + 1) * rc);
@@ -987,7 +991,8 @@ static atlasmem_status ns_backward(const Dims& d, float* ws, const NsLay& n, con
 
 bool backward_supported(const Dims& d) {
   if (d.kind == ATLASMEM_LINEAR) return !d.ptr && d.poly <= 2 && d.gate_mode == ATLASMEM_PER_TOKEN;
-  if (d.gated) return !d.ptr && d.poly <= 2 && d.gate_mode == ATLASMEM_PER_TOKEN;
+  if (d.gated)
+    return !d.ptr && d.poly <= 2 && (d.gate_mode == ATLASMEM_PER_CHUNK ? d.c == 1 && d.poly == 1 : d.ns_steps == 0);
   return d.kind == ATLASMEM_MLP2_SILU && !d.ptr && d.poly <= 2 &&
          (d.gate_mode == ATLASMEM_PER_CHUNK ? d.c == 1 && d.poly == 1 : d.ns_steps == 0);
 }
@@ -1177,15 +1182,50 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       launch_gemm<false, false>(true, R, dh, dv, M, bk::cat1(bk::src(E, 0, vz, dv, 1, R, dv)),
                                 bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv)),
                                 bk::EpiPDg{Pz, D1, Zk, hz, gz, gzz, dh}, st);
+      // per-chunk gates: G = (Dz^T X, E^T H) over the chunk's rows, its Newton-Schulz image N, and
+      // every row's gradient adjoint G' taken in place of the state adjoints (cW = -1, cS = 0)
+      const float* WAg = WA;
+      const float* SAg = SA;
+      if (per_chunk) {
+        float *Gb = ws + L.gb, *Nb = ws + L.nb, *NAb = ws + L.nab, *GAb = ws + L.gab, *SAt = ws + L.sat;
+        launch_gemm<false, false>(true, dzz, din, C, M, bk::cat1(bk::src(D1, 0, gz, 1, dzz, dzz, C)),
+                                  bk::cat1(bk::src(Kr, kbf, kz, 1, din, din, C)), bk::EpiSt{Gb, P, din}, st);
+        launch_gemm<false, false>(true, dv, dh, C, M, bk::cat1(bk::src(E, 0, vz, 1, dv, dv, C)),
+                                  bk::cat1(bk::gated(Zk, gzz, 1, dzz, dh, C, dh)), bk::EpiSt{Gb + P1, P, dh}, st);
+        AM_LAUNCH_CHECK();
+        const float* N = Gb;
+        if (d.ns_steps > 0) {
+          for (int m = 0; m < L.nns; ++m)
+            if ((stt = ns_forward(d, ws, L.ns[m], Gb, Nb, st)) != ATLASMEM_OK) return stt;
+          N = Nb;
+        }
+        hipLaunchKernelGGL(bk::chunk_gate_adj_kernel, dim3(M), dim3(256), 0, st, WA, SA, N, ck, P, SAt, nch, k, dth,
+                           det, dal);
+        hipLaunchKernelGGL(bk::to_work_kernel, dim3(blocks_of((int64_t)M * P)), dim3(256), 0, st, SAt, P, 1, (int)P,
+                           0, theta, nch, k, -1.0f, NAb, P, M);  // N' = -theta_k SAt
+        AM_LAUNCH_CHECK();
+        if (d.ns_steps > 0) {
+          for (int m = 0; m < L.nns; ++m)
+            if ((stt = ns_backward(d, ws, L.ns[m], Gb, NAb, GAb, st)) != ATLASMEM_OK) return stt;
+          WAg = SAg = GAb;
+        } else {
+          WAg = SAg = NAb;
+        }
+        hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cW, (int64_t)M * C,
+                           -1.0f);
+        hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cS, (int64_t)M * C,
+                           0.0f);
+        AM_LAUNCH_CHECK();
+      }
       {  // U1 = X WAz^T, U1s = X SAz^T (dz wide), U2 = H WA2^T, U2s = H SA2^T
         bk::Cat lx = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
-        launch_gemm<false, false>(true, R, dzz, din, M, lx, bk::cat1(bk::src(WA, 0, P, din, 1, dzz, din)),
+        launch_gemm<false, false>(true, R, dzz, din, M, lx, bk::cat1(bk::src(WAg, 0, P, din, 1, dzz, din)),
                                   bk::EpiSt{U1, gz, dzz}, st);
-        launch_gemm<false, false>(true, R, dzz, din, M, lx, bk::cat1(bk::src(SA, 0, P, din, 1, dzz, din)),
+        launch_gemm<false, false>(true, R, dzz, din, M, lx, bk::cat1(bk::src(SAg, 0, P, din, 1, dzz, din)),
                                   bk::EpiSt{U1s, gz, dzz}, st);
-        launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(hk), bk::cat1(bk::src(WA + P1, 0, P, dh, 1, dv, dh)),
+        launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(hk), bk::cat1(bk::src(WAg + P1, 0, P, dh, 1, dv, dh)),
                                   bk::EpiSt{U2, vz, dv}, st);
-        launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(hk), bk::cat1(bk::src(SA + P1, 0, P, dh, 1, dv, dh)),
+        launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(hk), bk::cat1(bk::src(SAg + P1, 0, P, dh, 1, dv, dh)),
                                   bk::EpiSt{U2s, vz, dv}, st);
       }
       hipLaunchKernelGGL(bk::row_kernel_gated, dim3(R, M), dim3(64), 0, st, Zk, gzz, Pz, hz, D1, U1, U1s, gz, Za, E,
@@ -1209,7 +1249,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
           true, R, dh, 3 * dv, M,
           bk::cat3(bk::src(E, 0, vz, dv, 1, R, dv, 2, rW, rld, -1.0f), bk::src(E, 0, vz, dv, 1, R, dv, 2, rS, rld, -1.0f),
                    bk::src(U2, 0, vz, dv, 1, R, dv, 0, nullptr, 0, 2.0f), dv, 2 * dv),
-          bk::cat3(bk::src(WA + P1, 0, P, 1, dh, dh, dv), bk::src(SA + P1, 0, P, 1, dh, dh, dv),
+          bk::cat3(bk::src(WAg + P1, 0, P, 1, dh, dh, dv), bk::src(SAg + P1, 0, P, 1, dh, dh, dv),
                    bk::src(cW2, 0, 2 * P, 1, dh, dh, dv), dv, 2 * dv),
           bk::EpiZag{Za, Zk, gz, gzz, dh}, st);
       {  // X' = -(cW D) WAz - (cS D) SAz + Za Wz
@@ -1221,7 +1261,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
             bk::cat3(bk::src(D1, 0, gz, dzz, 1, R, dzz, 2, rW, rld, -1.0f),
                      bk::src(D1, 0, gz, dzz, 1, R, dzz, 2, rS, rld, -1.0f), bk::src(Za, 0, gz, dzz, 1, R, dzz), dzz,
                      2 * dzz),
-            bk::cat3(bk::src(WA, 0, P, 1, din, din, dzz), bk::src(SA, 0, P, 1, din, din, dzz),
+            bk::cat3(bk::src(WAg, 0, P, 1, din, din, dzz), bk::src(SAg, 0, P, 1, din, din, dzz),
                      bk::src(cW1, 0, 2 * P, 1, din, din, dzz), dzz, 2 * dzz),
             out, st);
       }

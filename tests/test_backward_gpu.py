@@ -58,6 +58,12 @@ CASES = [
                                                 d_hidden=36, chunk=16)),
     ("gated_omega3_poly2", 3, "stabilised", dict(kind=synth.MLP2_GATED, batch=1, heads=2, T=48, d_key=6, d_value=20,
                                                   d_hidden=24, chunk=16, omega_window=3)),
+    # gated, per-chunk gates: three Newton-Schulz matrices (one batch at 64 -> 128 -> 64; W1 and
+    # W3 paired, W2 apart at ragged widths)
+    ("gated_ns5_per_chunk", 4, "literal", dict(kind=synth.MLP2_GATED, batch=1, heads=2, T=256)),
+    ("gated_ns5_ragged", 4, "literal", dict(kind=synth.MLP2_GATED, batch=1, heads=2, T=96, d_key=24, d_value=40,
+                                            d_hidden=32, chunk=32)),
+    ("gated_per_chunk_no_ns", 4, "literal", dict(kind=synth.MLP2_GATED, batch=2, heads=1, T=256, ns_steps=0)),
 ]
 
 
@@ -135,7 +141,7 @@ def test_backward_matches_autograd_oracle(case):
 def test_backward_errors():
     import torch
     for s3 in (synth.spec(3, "stabilised", batch=1, heads=1, T=256, gate_mode=synth.PER_CHUNK, omega_window=1),
-               synth.spec(4, "literal", batch=1, heads=1, T=256, kind=synth.MLP2_GATED)):  # gated, per chunk
+               synth.spec(1, "stabilised", batch=1, heads=1, T=256, per_token_retrieve=True)):
         mem = am.Memory(config_for(s3))
         assert mem.backward_workspace_bytes(256) == -1
         mem.close()
