@@ -740,9 +740,12 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) bad |= !(isfinite(sv[tt][r]) && isfinite(x[tt][r]));
     }
-    // The weight copies overwrite the Newton-Schulz X buffers, which nobody reads after the
-    // last iteration's second barrier; the W1 handoff overwrites the A buffers, dead after its
-    // third.
+    // The W1 handoff overwrites the A buffers, dead after the last iteration's third barrier.
+    // Set 1's W2^T operand copies overwrite its Newton-Schulz X^T buffer, which the last
+    // iteration's B X still reads (each wave its own columns, but the copy rows of one wave span
+    // columns of its neighbours): they are written after the barrier below, which every wave
+    // reaches only after that product.  Until the next group's first barrier nothing reads
+    // W2^T, and the group writes only its H buffers, which lie outside the copies.
     u32x4* ho = (u32x4*)(sm + opq(HOFF));
     {
     AM_LANE_VARS;
@@ -779,13 +782,6 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
         ho[(w * 8 + ks) * 64 + lane] = wh;
         ho[(w * 8 + 4 + ks) * 64 + lane] = wl;
       }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 wh, wl;
-        tile_op(x[ks >> 1], ks & 1, wh, wl);
-        store_rows_T(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
-      }
     }
     }
     __syncthreads();
@@ -793,6 +789,14 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
     // Newton-Schulz phase)
     {
       AM_LANE_VARS;
+      if (s == 1) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          u32x4 wh, wl;
+          tile_op(x[ks >> 1], ks & 1, wh, wl);
+          store_rows_T(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         w1h[ks] = ho[(w * 8 + ks) * 64 + lane];
