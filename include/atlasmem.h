@@ -122,6 +122,12 @@ typedef struct {
  * chunk-start state plus a masked sum of the chunk's rank-one gradients, so the queries are
  * answered through query-key score products. */
 #define ATLASMEM_FLAG_PER_TOKEN_RETRIEVE 2
+/* Run the chunks of a call as one separate launch per matrix product (five per chunk) instead of
+ * the chunk-loop kernel, which walks every chunk of a block inside one launch with one workgroup
+ * per memory and is used where a memory's per-chunk products are small (the general MLP path
+ * with per-token gates, or per-chunk gates without Newton-Schulz).  Both run the same tile
+ * loaders and epilogues; results are bitwise equal. */
+#define ATLASMEM_FLAG_NO_CHUNK_LOOP 4
 
 typedef struct atlasmem_handle_s* atlasmem_handle;
 

@@ -41,7 +41,8 @@ atlasmem_status validate(const atlasmem_config* c) {
     return ATLASMEM_E_INVALID;
   if (c->precision < ATLASMEM_PREC_AUTO || c->precision > ATLASMEM_PREC_BF16X3) return ATLASMEM_E_INVALID;
   if (c->ns_steps > 0 && !(c->ns_eps >= 0.0f)) return ATLASMEM_E_INVALID;
-  if (c->flags & ~(ATLASMEM_FLAG_NO_FUSED | ATLASMEM_FLAG_PER_TOKEN_RETRIEVE)) return ATLASMEM_E_INVALID;
+  if (c->flags & ~(ATLASMEM_FLAG_NO_FUSED | ATLASMEM_FLAG_PER_TOKEN_RETRIEVE | ATLASMEM_FLAG_NO_CHUNK_LOOP))
+    return ATLASMEM_E_INVALID;
   if ((int64_t)c->batch * c->heads > (1 << 20)) return ATLASMEM_E_SHAPE;
   if (c->d_key > 1024 || c->d_value > 1024 || c->d_hidden > 4096 || c->chunk > 1024 || c->omega_window > 64)
     return ATLASMEM_E_SHAPE;
@@ -97,6 +98,7 @@ Dims make_dims(const atlasmem_config* c) {
   d.out_bf16 = c->output_dtype == ATLASMEM_BF16;
   d.split = c->precision != ATLASMEM_PREC_BF16;
   d.no_fused = (c->flags & ATLASMEM_FLAG_NO_FUSED) != 0;
+  d.no_loop = (c->flags & ATLASMEM_FLAG_NO_CHUNK_LOOP) != 0;
   d.ptr = (c->flags & ATLASMEM_FLAG_PER_TOKEN_RETRIEVE) != 0;
   return d;
 }

@@ -12,6 +12,8 @@
 // MFMA blocks of 16 x 16.  Grid: (ceil(N/64), ceil(M/64), batch).
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace am {
@@ -23,16 +25,28 @@ constexpr int GT = 64;       // output tile
 constexpr int GK = 32;       // k step
 constexpr int GLD = GK + 8;  // LDS row stride in bf16 (80 bytes: 16-byte aligned, staggers banks)
 
-template <bool SPLIT, bool A_EXACT, bool B_EXACT, class LA, class LB, class EP>
-__global__ void __launch_bounds__(256) gemm_tile_kernel(int M, int N, int K, LA la, LB lb, EP ep) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ah[GT * GLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bh[GT * GLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Al[SPLIT && !A_EXACT ? GT * GLD : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Bl[SPLIT && !B_EXACT ? GT * GLD : 8];
+// An epilogue that reads memory declares `Pre` (what one element reads), `Pre load(z, row, col)`
+// and `store(z, row, col, acc, pre)`; one that only writes has just operator()(z, row, col, acc).
+template <class EP, class = void>
+struct EpiTwoPhase : std::false_type {};
+template <class EP>
+struct EpiTwoPhase<EP, std::void_t<typename EP::Pre>> : std::true_type {};
 
-  const int z = blockIdx.z;
-  const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
-  const int t = threadIdx.x;
+// LDS staging of one 64 x 64 x 32 tile step: hi (and, for split operands, lo) words of A and B.
+template <bool SPLIT, bool A_EXACT, bool B_EXACT>
+struct TileSmem {
+  uint16_t Ah[GT * GLD];
+  uint16_t Bh[GT * GLD];
+  uint16_t Al[SPLIT && !A_EXACT ? GT * GLD : 8];
+  uint16_t Bl[SPLIT && !B_EXACT ? GT * GLD : 8];
+};
+
+// One output tile (rows m0.., columns n0.. of batch z) by the 256 threads t = 0..255 of a tile
+// group.  Every thread of the workgroup executes the same barriers: a group with no tile in a
+// round passes active = false and only takes part in them (barriers are workgroup-wide).
+template <bool SPLIT, bool A_EXACT, bool B_EXACT, class LA, class LB, class EP>
+__device__ __forceinline__ void gemm_tile(int M, int N, int K, const LA& la, const LB& lb, const EP& ep, int z, int m0,
+                                          int n0, int t, TileSmem<SPLIT, A_EXACT, B_EXACT>& sm, bool active) {
   const int lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
   const int lr = lane & 15, lk = (lane >> 4) * 8;
@@ -45,64 +59,103 @@ __global__ void __launch_bounds__(256) gemm_tile_kernel(int M, int N, int K, LA 
 
   const int srow = t >> 2, sk = (t & 3) * 8;
   for (int k0 = 0; k0 < K; k0 += GK) {
-    {
-      float v[8];
-      la.load8(z, m0 + srow, k0 + sk, v);
-      u32x4 hi, lo;
-      if (SPLIT && !A_EXACT) {
-        pack8(v, hi, lo);
-        *(u32x4*)&Al[srow * GLD + sk] = lo;
-      } else {
-        pack8_hi(v, hi);
+    if (active) {
+      {
+        float v[8];
+        la.load8(z, m0 + srow, k0 + sk, v);
+        u32x4 hi, lo;
+        if (SPLIT && !A_EXACT) {
+          pack8(v, hi, lo);
+          *(u32x4*)&sm.Al[srow * GLD + sk] = lo;
+        } else {
+          pack8_hi(v, hi);
+        }
+        *(u32x4*)&sm.Ah[srow * GLD + sk] = hi;
       }
-      *(u32x4*)&Ah[srow * GLD + sk] = hi;
-    }
-    {
-      float v[8];
-      lb.load8(z, n0 + srow, k0 + sk, v);
-      u32x4 hi, lo;
-      if (SPLIT && !B_EXACT) {
-        pack8(v, hi, lo);
-        *(u32x4*)&Bl[srow * GLD + sk] = lo;
-      } else {
-        pack8_hi(v, hi);
+      {
+        float v[8];
+        lb.load8(z, n0 + srow, k0 + sk, v);
+        u32x4 hi, lo;
+        if (SPLIT && !B_EXACT) {
+          pack8(v, hi, lo);
+          *(u32x4*)&sm.Bl[srow * GLD + sk] = lo;
+        } else {
+          pack8_hi(v, hi);
+        }
+        *(u32x4*)&sm.Bh[srow * GLD + sk] = hi;
       }
-      *(u32x4*)&Bh[srow * GLD + sk] = hi;
     }
     __syncthreads();
-    u32x4 ah[2], bh[2], al[2], bl[2];
+    if (active) {
+      u32x4 ah[2], bh[2], al[2], bl[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = (wm * 32 + i * 16 + lr) * GLD + lk;
-      ah[i] = *(const u32x4*)&Ah[r];
-      if (SPLIT && !A_EXACT) al[i] = *(const u32x4*)&Al[r];
-    }
+      for (int i = 0; i < 2; ++i) {
+        const int r = (wm * 32 + i * 16 + lr) * GLD + lk;
+        ah[i] = *(const u32x4*)&sm.Ah[r];
+        if (SPLIT && !A_EXACT) al[i] = *(const u32x4*)&sm.Al[r];
+      }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = (wn * 32 + j * 16 + lr) * GLD + lk;
-      bh[j] = *(const u32x4*)&Bh[r];
-      if (SPLIT && !B_EXACT) bl[j] = *(const u32x4*)&Bl[r];
+      for (int j = 0; j < 2; ++j) {
+        const int r = (wn * 32 + j * 16 + lr) * GLD + lk;
+        bh[j] = *(const u32x4*)&sm.Bh[r];
+        if (SPLIT && !B_EXACT) bl[j] = *(const u32x4*)&sm.Bl[r];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = mfma16(ah[i], bh[j], acc[i][j]);
+          if (SPLIT && !B_EXACT) acc[i][j] = mfma16(ah[i], bl[j], acc[i][j]);
+          if (SPLIT && !A_EXACT) acc[i][j] = mfma16(al[i], bh[j], acc[i][j]);
+        }
     }
+    __syncthreads();
+  }
+  if (!active) return;
+  if constexpr (EpiTwoPhase<EP>::value) {
+    // every element's loads first, then every element's stores: element r + 1's loads may not
+    // move above element r's stores (the compiler cannot rule out aliasing), so a one-pass loop
+    // would chain sixteen memory latencies
+    typename EP::Pre pre[2][2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = mfma16(ah[i], bh[j], acc[i][j]);
-        if (SPLIT && !B_EXACT) acc[i][j] = mfma16(ah[i], bl[j], acc[i][j]);
-        if (SPLIT && !A_EXACT) acc[i][j] = mfma16(al[i], bh[j], acc[i][j]);
-      }
-    __syncthreads();
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+          const int col = n0 + wn * 32 + j * 16 + lr;
+          if (row < M && col < N) pre[i][j][r] = ep.load(z, row, col);
+        }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+          const int col = n0 + wn * 32 + j * 16 + lr;
+          if (row < M && col < N) ep.store(z, row, col, acc[i][j][r], pre[i][j][r]);
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+          const int col = n0 + wn * 32 + j * 16 + lr;
+          if (row < M && col < N) ep(z, row, col, acc[i][j][r]);
+        }
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
-        const int col = n0 + wn * 32 + j * 16 + lr;
-        if (row < M && col < N) ep(z, row, col, acc[i][j][r]);
-      }
+}
+
+template <bool SPLIT, bool A_EXACT, bool B_EXACT, class LA, class LB, class EP>
+__global__ void __launch_bounds__(256) gemm_tile_kernel(int M, int N, int K, LA la, LB lb, EP ep) {
+  __shared__ __attribute__((aligned(16))) TileSmem<SPLIT, A_EXACT, B_EXACT> sm;
+  gemm_tile<SPLIT, A_EXACT, B_EXACT>(M, N, K, la, lb, ep, blockIdx.z, blockIdx.y * GT, blockIdx.x * GT, threadIdx.x,
+                                     sm, true);
 }
 
 template <bool A_EXACT, bool B_EXACT, class LA, class LB, class EP>
@@ -164,5 +217,59 @@ struct StridedLoader {
     }
   }
 };
+// The same loader with clamped indices and every load of a call issued before any is used: fewer
+// instructions per element where the whole call is in range.  Used by the chunk-loop kernel, one
+// workgroup per memory, where the loaders' instruction count sets the chunk's time (the
+// per-product launches, with many workgroups per product, run the plain loader).
+struct StridedLoaderC : StridedLoader {
+  __device__ __forceinline__ void load8(int z, int outer, int k0, float* v) const {
+    const int zz = z / zdiv;
+    const bool orow = outer < outer_dim;
+    const int oc = orow ? outer : 0;
+    const float* p = base + zz * sz + (int64_t)oc * so;
+    const float* cf = nullptr;
+    if (xf == XF_COEF) cf = ((zdiv == 2 && (z & 1)) ? coef1 : coef0) + zz * cz;
+    if (xf == XF_MAT) cf = coef0 + zz * cz + (int64_t)oc * cld;
+    float x[8], g[8];
+    if (k0 + 8 <= K) {
+      // all eight in range: one base address, 32-bit strides (immediate offsets when sk == 1)
+      const float* q = p + (int64_t)k0 * sk;
+      const int s32 = (int)sk;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        x[u] = sk == 1 ? q[u] : q[u * s32];
+        g[u] = 1.0f;
+        if (xf == XF_GATED) g[u] = sk == 1 ? q[u + gofs] : q[u * s32 + gofs];
+        else if (xf == XF_COEF || xf == XF_MAT) g[u] = cf[k0 + u];
+        else if (xf == XF_SCALE) g[u] = scale[z];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u;
+        const int kc = k < K ? k : K - 1;
+        x[u] = p[(int64_t)kc * sk];
+        g[u] = 1.0f;
+        if (xf == XF_GATED) g[u] = p[(int64_t)kc * sk + gofs];
+        else if (xf == XF_COEF || xf == XF_MAT) g[u] = cf[kc];
+        else if (xf == XF_SCALE) g[u] = scale[z];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float y = x[u];
+      if (xf == XF_SILU) y = siluf_(y);
+      else if (xf == XF_GATED) y = siluf_(y) * g[u];
+      else if (xf == XF_COEF || xf == XF_MAT || xf == XF_SCALE) y *= g[u];
+      v[u] = (orow && k0 + u < K) ? y : 0.0f;
+    }
+  }
+};
+__host__ __device__ inline StridedLoaderC clamped(const StridedLoader& l) {
+  StridedLoaderC c;
+  static_cast<StridedLoader&>(c) = l;
+  return c;
+}
+
 
 }  // namespace am

@@ -27,6 +27,7 @@ struct Dims {
   int in_bf16, out_bf16;
   bool split;   // bf16 hi/lo split products
   bool no_fused;
+  bool no_loop;  // one launch per product and chunk instead of the chunk-loop kernel
 };
 
 // The token arrays of one launch sequence: T tokens; per memory, token stride `ld` of K, Q, V, Y,

@@ -132,10 +132,15 @@ struct EpiE {  // E = 2 (acc - V), or 2 (acc + X - V) for the residual memory (X
   const void* X;  // null unless residual: rows of dv elements, stride xz per memory
   int xbf16;
   int64_t xz;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    const float vv = load_in(V, (int64_t)z * vz + (int64_t)row * dv + col, bf16);
-    const float xv = X ? load_in(X, (int64_t)z * xz + (int64_t)row * dv + col, xbf16) : 0.0f;
-    E[(int64_t)z * ez + (int64_t)row * dv + col] = 2.0f * (v + xv - vv);
+  struct Pre {
+    float vv, xv;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    return Pre{load_in(V, (int64_t)z * vz + (int64_t)row * dv + col, bf16),
+               X ? load_in(X, (int64_t)z * xz + (int64_t)row * dv + col, xbf16) : 0.0f};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    E[(int64_t)z * ez + (int64_t)row * dv + col] = 2.0f * (v + p.xv - p.vv);
   }
 };
 struct EpiPD1 {  // P = acc, D1 = acc * silu'(Z)
@@ -144,10 +149,16 @@ struct EpiPD1 {  // P = acc, D1 = acc * silu'(Z)
   const float* Z;
   int64_t pz, zz;
   int dh;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+  struct Pre {
+    float zv;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    return Pre{Z[(int64_t)z * zz + (int64_t)row * dh + col]};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
     const int64_t o = (int64_t)z * pz + (int64_t)row * dh + col;
     P[o] = v;
-    D1[o] = v * silu_primef_(Z[(int64_t)z * zz + (int64_t)row * dh + col]);
+    D1[o] = v * silu_primef_(p.zv);
   }
 };
 struct EpiEa {  // Ea = Eg + acc (in place), dV = -2 Ea
@@ -158,14 +169,20 @@ struct EpiEa {  // Ea = Eg + acc (in place), dV = -2 Ea
   int dv;
   int64_t tau0;  // acc = 1: row r is token tau0 + r; tokens before 0 are dropped, the rest accumulate
   int acc;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    float* p = Ea + (int64_t)z * ez + (int64_t)row * dv + col;
-    const float e = *p + v;
-    *p = e;
+  struct Pre {
+    float ea, dv_old;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    return Pre{Ea[(int64_t)z * ez + (int64_t)row * dv + col],
+               (acc && tau0 + row >= 0) ? dV[(int64_t)z * vz + (tau0 + row) * dv + col] : 0.0f};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    const float e = p.ea + v;
+    Ea[(int64_t)z * ez + (int64_t)row * dv + col] = e;
     if (!acc) {
       dV[(int64_t)z * vz + (int64_t)row * dv + col] = -2.0f * e;
     } else if (tau0 + row >= 0) {
-      dV[(int64_t)z * vz + (tau0 + row) * dv + col] += -2.0f * e;
+      dV[(int64_t)z * vz + (tau0 + row) * dv + col] = p.dv_old + -2.0f * e;
     }
   }
 };
@@ -174,9 +191,14 @@ struct EpiZa {  // Za = Za1 + acc * silu'(Z) (in place)
   const float* Z;
   int64_t pz, zz;
   int dh;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    float* p = Za + (int64_t)z * pz + (int64_t)row * dh + col;
-    *p += v * silu_primef_(Z[(int64_t)z * zz + (int64_t)row * dh + col]);
+  struct Pre {
+    float za, zv;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    return Pre{Za[(int64_t)z * pz + (int64_t)row * dh + col], Z[(int64_t)z * zz + (int64_t)row * dh + col]};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    Za[(int64_t)z * pz + (int64_t)row * dh + col] = p.za + v * silu_primef_(p.zv);
   }
 };
 struct EpiScaleSp {  // out = acc * silu'(Z[row + zr0])
@@ -184,9 +206,14 @@ struct EpiScaleSp {  // out = acc * silu'(Z[row + zr0])
   const float* Z;
   int64_t oz, zz;
   int zr0, dh;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    out[(int64_t)z * oz + (int64_t)row * dh + col] =
-        v * silu_primef_(Z[(int64_t)z * zz + (int64_t)(zr0 + row) * dh + col]);
+  struct Pre {
+    float zv;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    return Pre{Z[(int64_t)z * zz + (int64_t)(zr0 + row) * dh + col]};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    out[(int64_t)z * oz + (int64_t)row * dh + col] = v * silu_primef_(p.zv);
   }
 };
 
@@ -200,12 +227,19 @@ struct EpiStAdd {  // out = acc (+ scale * add[z * az + row * ald + col] when ad
   float scale;
   int64_t tau0;  // acc = 1: row r goes to row tau0 + r of out, accumulated; rows before 0 dropped
   int acc;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    if (add) v += scale * add[(int64_t)z * az + (int64_t)row * ald + col];
+  struct Pre {
+    float addv, old;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    return Pre{add ? add[(int64_t)z * az + (int64_t)row * ald + col] : 0.0f,
+               (acc && tau0 + row >= 0) ? out[(int64_t)z * sz + (tau0 + row) * ld + col] : 0.0f};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    if (add) v += scale * p.addv;
     if (!acc) {
       out[(int64_t)z * sz + (int64_t)row * ld + col] = v;
     } else if (tau0 + row >= 0) {
-      out[(int64_t)z * sz + (tau0 + row) * ld + col] += v;
+      out[(int64_t)z * sz + (tau0 + row) * ld + col] = p.old + v;
     }
   }
 };
@@ -218,9 +252,15 @@ struct EpiPDg {
   const float* Z;
   int64_t bz, dzz, zz;
   int dh;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+  struct Pre {
+    float z1, z3;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
     const float* zr = Z + (int64_t)z * zz + (int64_t)row * 2 * dh;
-    const float z1 = zr[col], z3 = zr[dh + col];
+    return Pre{zr[col], zr[dh + col]};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    const float z1 = p.z1, z3 = p.z3;
     B[(int64_t)z * bz + (int64_t)row * dh + col] = v;
     float* dr = D + (int64_t)z * dzz + (int64_t)row * 2 * dh;
     dr[col] = v * z3 * silu_primef_(z1);
@@ -233,12 +273,19 @@ struct EpiZag {
   const float* Z;
   int64_t az, zz;
   int dh;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+  struct Pre {
+    float z1, z3, a1, a3;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
     const float* zr = Z + (int64_t)z * zz + (int64_t)row * 2 * dh;
-    const float z1 = zr[col], z3 = zr[dh + col];
+    const float* ar = Za + (int64_t)z * az + (int64_t)row * 2 * dh;
+    return Pre{zr[col], zr[dh + col], ar[col], ar[dh + col]};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    const float z1 = p.z1, z3 = p.z3;
     float* ar = Za + (int64_t)z * az + (int64_t)row * 2 * dh;
-    ar[col] += v * z3 * silu_primef_(z1);
-    ar[dh + col] += v * siluf_(z1);
+    ar[col] = p.a1 + v * z3 * silu_primef_(z1);
+    ar[dh + col] = p.a3 + v * siluf_(z1);
   }
 };
 // query rows: hq' = acc (= dY W2): Zq1' = hq' Zq3 silu'(Zq1), Zq3' = hq' silu(Zq1) (Zq: rows zr0..)
@@ -247,9 +294,15 @@ struct EpiScaleSpG {
   const float* Z;
   int64_t oz, zz;
   int zr0, dh;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+  struct Pre {
+    float z1, z3;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
     const float* zr = Z + (int64_t)z * zz + (int64_t)(zr0 + row) * 2 * dh;
-    const float z1 = zr[col], z3 = zr[dh + col];
+    return Pre{zr[col], zr[dh + col]};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    const float z1 = p.z1, z3 = p.z3;
     float* o = out + (int64_t)z * oz + (int64_t)row * 2 * dh;
     o[col] = v * z3 * silu_primef_(z1);
     o[dh + col] = v * siluf_(z1);
@@ -262,17 +315,28 @@ struct EpiAxpy {  // out = alpha * x + beta * acc (out may alias x: same element
   int64_t sz;
   int ld;
   float alpha, beta;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    const int64_t o = (int64_t)z * sz + (int64_t)row * ld + col;
-    out[o] = alpha * (x ? x[o] : 0.0f) + beta * v;
+  struct Pre {
+    float xv;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    return Pre{x ? x[(int64_t)z * sz + (int64_t)row * ld + col] : 0.0f};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    out[(int64_t)z * sz + (int64_t)row * ld + col] = alpha * p.xv + beta * v;
   }
 };
 struct EpiAcc {  // out += acc
   float* out;
   int64_t sz;
   int ld;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    out[(int64_t)z * sz + (int64_t)row * ld + col] += v;
+  struct Pre {
+    float old;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    return Pre{out[(int64_t)z * sz + (int64_t)row * ld + col]};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    out[(int64_t)z * sz + (int64_t)row * ld + col] = p.old + v;
   }
 };
 

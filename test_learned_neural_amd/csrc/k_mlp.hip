@@ -51,40 +51,136 @@ struct FeatRows {
     pair_of(f - 1 - dk, dk, i, j);
     return 0.5f * (raw(mem, row, i) * raw(mem, row, j));
   }
+
+  // Batched loads (FeatA, FeatB): the source of a row is located first, then every load of a
+  // call is issued as raw bits before any is converted, so that the loads overlap.
+  // Row `row` (< nrows): element i at src[off + i] (K or Q), or, for a key row before the call's
+  // first token, at hk[hoff + i] (hist).
+  __device__ __forceinline__ void locate(int mem, int row, const void*& src, int64_t& off, int64_t& hoff,
+                                         bool& hist) const {
+    if (row < Rk) {
+      const int64_t tau = s - (c - 1) + row;
+      hist = tau < 0;
+      src = K;
+      off = ((int64_t)mem * T + (hist ? 0 : tau)) * dk;
+      hoff = hist ? ((int64_t)mem * (c - 1) + (c - 1) + tau) * dk : 0;
+    } else {
+      hist = false;
+      src = Q;
+      off = ((int64_t)mem * T + s + (row - Rk)) * dk;
+      hoff = 0;
+    }
+  }
+  // whether any row of this chunk comes from the window history (uniform)
+  __device__ __forceinline__ bool any_hist() const { return c > 1 && s < c - 1; }
+  __device__ __forceinline__ uint32_t ld_bits(const void* src, int64_t idx) const {
+    return in_bf16 ? (uint32_t)((const uint16_t*)src)[idx] : __float_as_uint(((const float*)src)[idx]);
+  }
+  __device__ __forceinline__ float bits_val(uint32_t b) const {
+    return in_bf16 ? __uint_as_float(b << 16) : __uint_as_float(b);
+  }
 };
+
+// Feature f of the map: 0 the constant, 1 a raw element (index i), 2 half the product of
+// elements i and j, 3 padding beyond din.
+__device__ __forceinline__ int feat_kind(const FeatRows& fr, int f, int& i, int& j) {
+  if (f >= fr.din) {
+    i = j = 0;
+    return 3;
+  }
+  if (fr.poly == 1) {
+    i = j = f;
+    return 1;
+  }
+  if (f == 0) {
+    i = j = 0;
+    return 0;
+  }
+  if (f <= fr.dk) {
+    i = j = f - 1;
+    return 1;
+  }
+  pair_of(f - 1 - fr.dk, fr.dk, i, j);
+  return 2;
+}
+
+__device__ __forceinline__ float feat_value(int kind, float xi, float xj) {
+  return kind == 0 ? 1.0f : kind == 1 ? xi : kind == 2 ? 0.5f * (xi * xj) : 0.0f;
+}
 
 // A role: outer = row, k = feature.
 struct FeatA {
   FeatRows fr;
   __device__ __forceinline__ void load8(int z, int row, int f0, float* v) const {
     const int mem = z / fr.zdiv;
-    if (row >= fr.nrows) {
+    const bool rok = row < fr.nrows;
+    const void* src;
+    int64_t off, hoff;
+    bool hist;
+    fr.locate(mem, rok ? row : 0, src, off, hoff, hist);
+    const bool hh = fr.any_hist();
+    if (fr.poly == 1 && fr.in_bf16 && !hh && f0 + 8 <= fr.din &&
+        (((uintptr_t)((const uint16_t*)src + off + f0)) & 15) == 0) {
+      // eight consecutive bf16 of one row: a single 16-byte load
+      const u32x4 w4 = *(const u32x4*)((const uint16_t*)src + off + f0);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = 0.0f;
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = rok ? __uint_as_float(w4[q] << 16) : 0.0f;
+        v[2 * q + 1] = rok ? __uint_as_float(w4[q] & 0xFFFF0000u) : 0.0f;
+      }
       return;
     }
-    if (fr.poly == 1) {
+    int kind[8], ia[8], ja[8];
+    if (fr.poly == 1 || f0 + 8 <= fr.dk + 1) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (f0 + u < fr.din) ? fr.raw(mem, row, f0 + u) : 0.0f;
-      return;
-    }
-    // degree 2: walk the monomials from f0 (decode the first pair once, then step)
-    int i = 0, j = 0;
-    if (f0 > fr.dk) pair_of(f0 - 1 - fr.dk, fr.dk, i, j);
+      for (int u = 0; u < 8; ++u) kind[u] = feat_kind(fr, f0 + u, ia[u], ja[u]);
+    } else {
+      // degree 2: decode the first pair once, then step through the monomials
+      int i = 0, j = 0;
+      if (f0 > fr.dk) pair_of(f0 - 1 - fr.dk, fr.dk, i, j);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int f = f0 + u;
-      float x = 0.0f;
-      if (f < fr.din) {
-        if (f == 0) x = 1.0f;
-        else if (f <= fr.dk) x = fr.raw(mem, row, f - 1);
-        else {
-          if (f == fr.dk + 1) { i = 0; j = 0; }
-          x = 0.5f * (fr.raw(mem, row, i) * fr.raw(mem, row, j));
-          if (++j == fr.dk) { ++i; j = i; }
+      for (int u = 0; u < 8; ++u) {
+        const int f = f0 + u;
+        if (f >= fr.din) {
+          kind[u] = 3;
+          ia[u] = ja[u] = 0;
+        } else if (f == 0) {
+          kind[u] = 0;
+          ia[u] = ja[u] = 0;
+        } else if (f <= fr.dk) {
+          kind[u] = 1;
+          ia[u] = ja[u] = f - 1;
+        } else {
+          if (f == fr.dk + 1) i = j = 0;
+          kind[u] = 2;
+          ia[u] = i;
+          ja[u] = j;
+          if (++j == fr.dk) {
+            ++i;
+            j = i;
+          }
         }
       }
-      v[u] = x;
+    }
+    uint32_t bi[8], bj[8];
+    float hi[8], hj[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      bi[u] = fr.ld_bits(src, off + ia[u]);
+      bj[u] = fr.poly == 2 ? fr.ld_bits(src, off + ja[u]) : 0u;
+      if (hh) {
+        hi[u] = fr.hk[hoff + ia[u]];
+        hj[u] = fr.hk[hoff + ja[u]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float xi = fr.bits_val(bi[u]), xj = fr.bits_val(bj[u]);
+      if (hh && hist) {
+        xi = hi[u];
+        xj = hj[u];
+      }
+      v[u] = rok ? feat_value(kind[u], xi, xj) : 0.0f;
     }
   }
 };
@@ -94,10 +190,47 @@ struct FeatB {
   FeatRows fr;
   __device__ __forceinline__ void load8(int z, int f, int r0, float* v) const {
     const int mem = z / fr.zdiv;
+    int i, j;
+    const int kind = feat_kind(fr, f, i, j);
+    const bool hh = fr.any_hist();
+    if (fr.poly == 1 && !hh && r0 + 8 <= fr.nrows && (r0 + 8 <= fr.Rk || r0 >= fr.Rk)) {
+      // eight consecutive rows of one array (K or Q): one base, a 32-bit row stride
+      const void* src;
+      int64_t off, hoff;
+      bool hist;
+      fr.locate(mem, r0, src, off, hoff, hist);
+      const int st = fr.dk;
+      uint32_t b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) b[u] = fr.ld_bits((const char*)src, off + i + (int64_t)(u * st));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = kind == 1 ? fr.bits_val(b[u]) : 0.0f;
+      return;
+    }
+    uint32_t bi[8], bj[8];
+    float hi[8], hj[8];
+    bool hist[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int row = r0 + u;
-      v[u] = (f < fr.din && row < fr.nrows) ? fr.feat(mem, row, f) : 0.0f;
+      const void* src;
+      int64_t off, hoff;
+      fr.locate(mem, row < fr.nrows ? row : 0, src, off, hoff, hist[u]);
+      bi[u] = fr.ld_bits(src, off + i);
+      bj[u] = fr.poly == 2 ? fr.ld_bits(src, off + j) : 0u;
+      if (hh) {
+        hi[u] = fr.hk[hoff + i];
+        hj[u] = fr.hk[hoff + j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float xi = fr.bits_val(bi[u]), xj = fr.bits_val(bj[u]);
+      if (hh && hist[u]) {
+        xi = hi[u];
+        xj = hj[u];
+      }
+      v[u] = (r0 + u < fr.nrows) ? feat_value(kind, xi, xj) : 0.0f;
     }
   }
 };
@@ -127,13 +260,23 @@ struct EpiY {
   int out_bf16;
   int residual;  // the residual memory adds its input: feature `col` of the same row
   FeatRows fr;   // the rows of the product (keys, then queries), for the residual input
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    if (residual) v += fr.feat(z, row, col);
+  struct Pre {
+    float vv, res;  // the key row's value, the residual input
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    Pre p{0.0f, 0.0f};
+    if (residual) p.res = fr.feat(z, row, col);
     if (row < Rk) {
       const int64_t tau = s - (c - 1) + row;
-      const float vv = (tau >= 0) ? load_in(V, ((int64_t)z * T + tau) * dv + col, in_bf16)
-                                  : hv[((int64_t)z * (c - 1) + (c - 1) + tau) * dv + col];
-      D2[(int64_t)z * d2z + (int64_t)row * dv + col] = 2.0f * (v - vv);
+      p.vv = (tau >= 0) ? load_in(V, ((int64_t)z * T + tau) * dv + col, in_bf16)
+                        : hv[((int64_t)z * (c - 1) + (c - 1) + tau) * dv + col];
+    }
+    return p;
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    if (residual) v += p.res;
+    if (row < Rk) {
+      D2[(int64_t)z * d2z + (int64_t)row * dv + col] = 2.0f * (v - p.vv);
     } else if (Y) {
       const int64_t yo = ((int64_t)z * T + s + (row - Rk)) * dv + col;
       if (out_bf16) ((uint16_t*)Y)[yo] = (uint16_t)bf16_bits(v);
@@ -151,10 +294,15 @@ struct EpiZq {
   const float* bA;
   int64_t zs_z, z_z, zr0;
   int dz, C;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    float* o = ZS + (int64_t)z * zs_z + (int64_t)row * dz + col;
+  struct Pre {
+    float b0, b1, z0, zs;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
     const float* b = bA + ((int64_t)z * C + row) * 2;
-    *o = b[0] * Z[(int64_t)z * z_z + (zr0 + row) * dz + col] + b[1] * *o - v;
+    return Pre{b[0], b[1], Z[(int64_t)z * z_z + (zr0 + row) * dz + col], ZS[(int64_t)z * zs_z + (int64_t)row * dz + col]};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    ZS[(int64_t)z * zs_z + (int64_t)row * dz + col] = p.b0 * p.z0 + p.b1 * p.zs - v;
   }
 };
 // out = which-th coefficient of the row times acc (acc = 0) or added to out (acc = 1)
@@ -163,10 +311,15 @@ struct EpiRowMix {
   const float* bA;
   int64_t oz;
   int ld, C, which, add;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    float* o = out + (int64_t)z * oz + (int64_t)row * ld + col;
-    const float x = bA[((int64_t)z * C + row) * 2 + which] * v;
-    *o = add ? *o + x : x;
+  struct Pre {
+    float coef, old;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    return Pre{bA[((int64_t)z * C + row) * 2 + which], add ? out[(int64_t)z * oz + (int64_t)row * ld + col] : 0.0f};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    const float x = p.coef * v;
+    out[(int64_t)z * oz + (int64_t)row * ld + col] = add ? p.old + x : x;
   }
 };
 // Y of the chunk's queries: the accumulated beta/a terms minus acc (plus the query's features for
@@ -180,9 +333,15 @@ struct EpiYptr {
   int out_bf16;
   int residual;
   FeatRows fr;    // the queries, for the residual input
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
-    float y = YB[(int64_t)z * yb_z + (int64_t)row * dv + col] - v;
-    if (residual) y += fr.feat(z, row, col);
+  struct Pre {
+    float yb, res;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
+    return Pre{YB[(int64_t)z * yb_z + (int64_t)row * dv + col], residual ? fr.feat(z, row, col) : 0.0f};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    float y = p.yb - v;
+    if (residual) y += p.res;
     const int64_t yo = ((int64_t)z * ld + s + row) * dv + col;
     if (out_bf16) ((uint16_t*)Y)[yo] = (uint16_t)bf16_bits(y);
     else ((float*)Y)[yo] = y;
@@ -196,12 +355,18 @@ struct EpiP {
   const float* Z;
   int64_t d1z, zz;
   int dh, dz, gated;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+  struct Pre {
+    float z1, z3;
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
     const float* zr = Z + (int64_t)z * zz + (int64_t)row * dz;
+    return Pre{zr[col], gated ? zr[dh + col] : 0.0f};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
     float* dr = D1 + (int64_t)z * d1z + (int64_t)row * dz;
-    const float z1 = zr[col];
+    const float z1 = p.z1;
     if (gated) {
-      const float z3 = zr[dh + col];
+      const float z3 = p.z3;
       dr[col] = v * z3 * silu_primef_(z1);
       dr[dh + col] = v * siluf_(z1);
     } else {
@@ -221,16 +386,24 @@ struct EpiUpdPair {
   const float* scal;  // chunk scalars of this chunk: scal + mem * ld_s -> (P, beta, a_S)
   int64_t ld_s;
   int* flag;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+  struct Pre {
+    float s0, s1, s2, w, s;  // chunk scalars, W and S at the element
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
     const int mem = z >> 1;
     const int64_t e = (int64_t)mem * P + off + (int64_t)row * ld + col;
     const float* sc = scal + (int64_t)mem * ld_s;
+    return Pre{sc[0], sc[1], sc[2], (z & 1) == 0 ? Win[e] : 0.0f, Sin[e]};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    const int mem = z >> 1;
+    const int64_t e = (int64_t)mem * P + off + (int64_t)row * ld + col;
     float o;
     if ((z & 1) == 0) {
-      o = sc[1] * Win[e] + sc[2] * Sin[e] - v;
+      o = p.s1 * p.w + p.s2 * p.s - v;
       Wout[e] = o;
     } else {
-      o = sc[0] * Sin[e] - v;
+      o = p.s0 * p.s - v;
       Sout[e] = o;
     }
     if (!isfinite(o)) flag[0] = 1;
@@ -250,11 +423,18 @@ struct EpiUpdChunk {
   const float* alpha;
   int64_t ld_gate, k;
   int* flag;
-  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+  struct Pre {
+    float et, th, al, w, s;  // the chunk's gates, W and S at the element
+  };
+  __device__ __forceinline__ Pre load(int z, int row, int col) const {
     const int64_t e = (int64_t)z * P + off + (int64_t)row * ld + col;
     const int64_t g = (int64_t)z * ld_gate + k;
-    const float s = eta[g] * Sin[e] - theta[g] * v;
-    const float w = (1.0f - alpha[g]) * Win[e] + s;
+    return Pre{eta[g], theta[g], alpha[g], Win[e], Sin[e]};
+  }
+  __device__ __forceinline__ void store(int z, int row, int col, float v, const Pre& p) const {
+    const int64_t e = (int64_t)z * P + off + (int64_t)row * ld + col;
+    const float s = p.et * p.s - p.th * v;
+    const float w = (1.0f - p.al) * p.w + s;
     Sout[e] = s;
     Wout[e] = w;
     if (!(isfinite(s) && isfinite(w))) flag[0] = 1;
@@ -263,7 +443,7 @@ struct EpiUpdChunk {
 
 // ---------------------------------------------------------------------------- helpers
 
-static StridedLoader strided(const float* base, int64_t sz, int64_t so, int64_t sk, int zdiv, int outer_dim, int K,
+static __host__ __device__ StridedLoader strided(const float* base, int64_t sz, int64_t so, int64_t sk, int zdiv, int outer_dim, int K,
                              int xf = XF_NONE) {
   StridedLoader l;
   l.base = base;
@@ -284,7 +464,7 @@ static StridedLoader strided(const float* base, int64_t sz, int64_t so, int64_t 
 
 // The hidden activation H of the memory from the stored first-layer outputs: silu(Z) or, for the
 // gated memory, silu(Z1) * Z3 with Z3 d_hidden elements after Z1.
-static StridedLoader hidden(const Dims& d, const float* Z, int64_t sz, int64_t so, int64_t sk, int zdiv, int outer_dim,
+static __host__ __device__ StridedLoader hidden(const Dims& d, const float* Z, int64_t sz, int64_t so, int64_t sk, int zdiv, int outer_dim,
                             int K) {
   StridedLoader l = strided(Z, sz, so, sk, zdiv, outer_dim, K, d.gated ? XF_GATED : XF_SILU);
   l.gofs = d.dh;
@@ -394,6 +574,181 @@ static atlasmem_status ptr_retrieve(Handle* h, const Dims& d, const void* K, con
 
 // ---------------------------------------------------------------------------- one call
 
+// ---------------------------------------------------------------------------- chunk loop
+
+// The same chunk sequence as the per-product launches of mlp_update (Z, Yh, Pm, then the two
+// weighted-gradient products with the state update in their epilogues), run for a block of
+// chunks inside one launch: workgroup m walks the chunks of memory m, and its four groups of 256
+// threads share out each product's 64 x 64 output tiles.  The intermediates Z, D2, D1 go through
+// the memory's own slice of the workspace (written and read by the same workgroup, so a
+// workgroup barrier orders them).  Chunk kb of the block reads state buffer cur ^ (kb & 1).
+struct LoopArgs {
+  Dims d;
+  const void* K;
+  const void* Q;
+  const void* V;
+  const float* theta;  // per-chunk gates (per-chunk gates without Newton-Schulz)
+  const float* eta;
+  const float* alpha;
+  int64_t ld, ldg;  // token stride of K, Q, V, Y; gate stride
+  void* Y;
+  const float* hk;  // window history at the start of the call
+  const float* hv;
+  float* W[2];
+  float* S[2];
+  int cur;
+  float* Z;
+  float* D2;
+  float* D1;
+  const float* cW;  // coefficients of the block (per-token gates)
+  const float* cS;
+  const float* oW;
+  const float* oS;
+  const float* scal;
+  int ncb;
+  int64_t kb0;  // first chunk of the block within the call
+  int nb;       // chunks in the block
+  int* flag;
+};
+
+constexpr int LOOP_GROUPS = 4;
+constexpr int LOOP_THREADS = 256 * LOOP_GROUPS;
+constexpr int LOOP_LDS = LOOP_GROUPS * (int)sizeof(TileSmem<true, false, false>);
+
+// All tiles of one product (batches z0 .. z0 + nz - 1), LOOP_GROUPS at a time, then a barrier so
+// that the next product reads this one's epilogue stores.
+template <bool SPLIT, bool AE, bool BE, class LA, class LB, class EP>
+__device__ __forceinline__ void loop_stage(int M, int N, int K, int z0, int nz, const LA& la, const LB& lb,
+                                           const EP& ep, uint16_t* lsm) {
+  if (M <= 0 || N <= 0) return;
+  // the thread index made opaque here, so that the compiler derives each product's addresses
+  // where they are used instead of keeping every product's live across the whole chunk loop
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int grp = __builtin_amdgcn_readfirstlane(tid >> 8), t = tid & 255;
+  auto& sm = ((TileSmem<SPLIT, AE, BE>*)lsm)[grp];
+  const int tm = (M + GT - 1) / GT, tn = (N + GT - 1) / GT, per = tm * tn, nt = per * nz;
+  for (int r0 = 0; r0 < nt; r0 += LOOP_GROUPS) {
+    const int tile = r0 + grp;
+    const bool active = tile < nt;
+    const int tz = active ? tile / per : 0, rem = active ? tile % per : 0;
+    gemm_tile<SPLIT, AE, BE>(M, N, K, la, lb, ep, z0 + tz, (rem / tn) * GT, (rem % tn) * GT, t, sm, active);
+  }
+  __syncthreads();
+}
+
+template <bool SPLIT, bool FEAT_EXACT>
+__global__ void __launch_bounds__(LOOP_THREADS) mlp_loop_kernel(LoopArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lsm[];
+  const Dims& d = a.d;
+  const int mem = blockIdx.x;
+  const int C = d.C, c = d.c, Rk = d.Rk, dh = d.dh, dv = d.dv, din = d.din, dz = d.dz;
+  const int nrows = Rk + (a.Y ? C : 0);
+  const int64_t zsz = (int64_t)d.Rt * dz;
+  const bool per_token = d.gate_mode == ATLASMEM_PER_TOKEN;
+  for (int kb = 0; kb < a.nb; ++kb) {
+    const int64_t k = a.kb0 + kb;
+    const int64_t s = k * C;
+    const int pp = a.cur ^ (kb & 1);
+    const float* Win = a.W[pp];
+    const float* Sin = a.S[pp];
+    float* Wout = a.W[1 - pp];
+    float* Sout = a.S[1 - pp];
+    FeatRows fr;
+    fr.K = a.K;
+    fr.Q = a.Q;
+    fr.in_bf16 = d.in_bf16;
+    fr.hk = a.hk;
+    fr.T = a.ld;
+    fr.s = s;
+    fr.Rk = Rk;
+    fr.nrows = nrows;
+    fr.c = c;
+    fr.dk = d.dk;
+    fr.din = din;
+    fr.poly = d.poly;
+    fr.zdiv = 1;
+    FeatRows frk = fr;  // key rows only
+    frk.nrows = Rk;
+    {  // Z = X W1^T over key and query rows
+      FeatA la{fr};
+      StridedLoaderC lb = clamped(strided(Win, d.P, din, 1, 1, dz, din));
+      EpiStore ep{a.Z, zsz, dz, 1};
+      loop_stage<SPLIT, FEAT_EXACT, false>(nrows, dz, din, mem, 1, la, lb, ep, lsm);
+    }
+    {  // Yh = H W2^T -> D2 (key rows), Y (query rows)
+      StridedLoaderC la = clamped(hidden(d, a.Z, zsz, dz, 1, 1, nrows, dh));
+      StridedLoaderC lb = clamped(strided(Win + d.P1, d.P, dh, 1, 1, dv, dh));
+      EpiY ep{a.D2, (int64_t)Rk * dv, a.V, d.in_bf16, a.hv, a.ld, s, Rk, c, dv, a.Y, d.out_bf16, d.residual, fr};
+      loop_stage<SPLIT, false, false>(nrows, dv, dh, mem, 1, la, lb, ep, lsm);
+    }
+    {  // Pm = D2 W2 -> D1
+      StridedLoaderC la = clamped(strided(a.D2, (int64_t)Rk * dv, dv, 1, 1, Rk, dv));
+      StridedLoaderC lb = clamped(strided(Win + d.P1, d.P, 1, dh, 1, dh, dv));
+      EpiP ep{a.D1, a.Z, (int64_t)Rk * dz, zsz, dh, dz, d.gated};
+      loop_stage<SPLIT, false, false>(Rk, dh, dv, mem, 1, la, lb, ep, lsm);
+    }
+    if (per_token) {
+      const float* c0 = (c > 1) ? a.oW + (int64_t)kb * Rk : a.cW + (int64_t)kb * C;
+      const float* c1 = (c > 1) ? a.oS + (int64_t)kb * Rk : a.cS + (int64_t)kb * C;
+      const int64_t cz = (c > 1) ? (int64_t)a.ncb * Rk : (int64_t)a.ncb * C;
+      const float* sc = a.scal + (int64_t)kb * 3;
+      {
+        StridedLoaderC la = clamped(strided(a.D2, (int64_t)Rk * dv, 1, dv, 2, dv, Rk, XF_COEF));
+        la.coef0 = c0;
+        la.coef1 = c1;
+        la.cz = cz;
+        StridedLoaderC lb = clamped(hidden(d, a.Z, zsz, 1, dz, 2, dh, Rk));
+        EpiUpdPair ep{Win, Sin, Wout, Sout, d.P, d.P1, dh, sc, (int64_t)a.ncb * 3, a.flag};
+        loop_stage<SPLIT, false, false>(dv, dh, Rk, 2 * mem, 2, la, lb, ep, lsm);
+      }
+      {
+        StridedLoaderC la = clamped(strided(a.D1, (int64_t)Rk * dz, 1, dz, 2, dz, Rk, XF_COEF));
+        la.coef0 = c0;
+        la.coef1 = c1;
+        la.cz = cz;
+        FeatB lb{frk};
+        lb.fr.zdiv = 2;
+        EpiUpdPair ep{Win, Sin, Wout, Sout, d.P, 0, din, sc, (int64_t)a.ncb * 3, a.flag};
+        loop_stage<SPLIT, false, FEAT_EXACT>(dz, din, Rk, 2 * mem, 2, la, lb, ep, lsm);
+      }
+    } else {
+      {
+        StridedLoaderC la = clamped(strided(a.D2, (int64_t)Rk * dv, 1, dv, 1, dv, Rk));
+        StridedLoaderC lb = clamped(hidden(d, a.Z, zsz, 1, dz, 1, dh, Rk));
+        EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, d.P1, dh, a.theta, a.eta, a.alpha, a.ldg, k, a.flag};
+        loop_stage<SPLIT, false, false>(dv, dh, Rk, mem, 1, la, lb, ep, lsm);
+      }
+      {
+        StridedLoaderC la = clamped(strided(a.D1, (int64_t)Rk * dz, 1, dz, 1, dz, Rk));
+        FeatB lb{frk};
+        EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, 0, din, a.theta, a.eta, a.alpha, a.ldg, k, a.flag};
+        loop_stage<SPLIT, false, FEAT_EXACT>(dz, din, Rk, mem, 1, la, lb, ep, lsm);
+      }
+    }
+  }
+}
+
+// Length of the chunk's dependent chain in tile steps when one workgroup with LOOP_GROUPS tile
+// groups runs a memory's products: sum over the products of ceil(tiles / groups) x k-steps.
+static int64_t loop_chain(const Dims& d, bool with_y) {
+  auto cd = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+  const int64_t nrows = d.Rk + (with_y ? d.C : 0);
+  const int64_t pair = d.gate_mode == ATLASMEM_PER_TOKEN ? 2 : 1;
+  auto st = [&](int64_t m, int64_t n, int64_t k, int64_t nz) { return cd(cd(m, GT) * cd(n, GT) * nz, LOOP_GROUPS) * cd(k, GK); };
+  return st(nrows, d.dz, d.din, 1) + st(nrows, d.dv, d.dh, 1) + st(d.Rk, d.dh, d.dv, 1) +
+         st(d.dv, d.dh, d.Rk, pair) + st(d.dz, d.din, d.Rk, pair);
+}
+
+// The chunk loop replaces the per-product launches where a memory's chunk is a short chain of
+// tile steps: the 64 -> 128 -> 64 memory takes 12 (4.9 -> 3.8 ms for 8 memories x 4096 tokens on
+// MI355X).  Longer chains keep one launch per product, whose tiles then spread over many
+// workgroups: degree-2 features of 32-wide keys (72 steps) ran 2x slower in the loop, and the
+// 384 -> 768 -> 384 memory takes 324.
+static bool loop_supported(const Dims& d, bool with_y) {
+  return !d.no_loop && !d.ptr && (d.gate_mode == ATLASMEM_PER_TOKEN || d.ns_steps == 0) && loop_chain(d, with_y) <= 24;
+}
+
 atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* Q, const void* V, const float* theta,
                            const float* eta, const float* alpha, const float* gamma, const Span& sp, void* Y,
                            hipStream_t st) {
@@ -420,6 +775,52 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
                            h->oS, (int64_t)h->ncb * Rk, st);
         if (stt != ATLASMEM_OK) return stt;
       }
+    }
+    if (loop_supported(d, Y != nullptr)) {
+      LoopArgs la;
+      la.d = d;
+      la.K = K;
+      la.Q = Q;
+      la.V = V;
+      la.theta = theta;
+      la.eta = eta;
+      la.alpha = alpha;
+      la.ld = ld;
+      la.ldg = sp.ldg;
+      la.Y = Y;
+      la.hk = h->hk[h->hcur];
+      la.hv = h->hv[h->hcur];
+      la.W[0] = h->W[0];
+      la.W[1] = h->W[1];
+      la.S[0] = h->S[0];
+      la.S[1] = h->S[1];
+      la.cur = h->cur;
+      la.Z = h->Z;
+      la.D2 = h->D2;
+      la.D1 = h->D1;
+      la.cW = h->cW;
+      la.cS = h->cS;
+      la.oW = h->oW;
+      la.oS = h->oS;
+      la.scal = h->scal;
+      la.ncb = h->ncb;
+      la.kb0 = kb0;
+      la.nb = nb;
+      la.flag = h->flag;
+      const void* kern = split ? (feat_exact ? (const void*)mlp_loop_kernel<true, true> : (const void*)mlp_loop_kernel<true, false>)
+                               : (feat_exact ? (const void*)mlp_loop_kernel<false, true> : (const void*)mlp_loop_kernel<false, false>);
+      if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LOOP_LDS) != hipSuccess)
+        return ATLASMEM_E_DEVICE;
+      if (split) {
+        if (feat_exact) hipLaunchKernelGGL((mlp_loop_kernel<true, true>), dim3(M), dim3(LOOP_THREADS), LOOP_LDS, st, la);
+        else hipLaunchKernelGGL((mlp_loop_kernel<true, false>), dim3(M), dim3(LOOP_THREADS), LOOP_LDS, st, la);
+      } else {
+        if (feat_exact) hipLaunchKernelGGL((mlp_loop_kernel<false, true>), dim3(M), dim3(LOOP_THREADS), LOOP_LDS, st, la);
+        else hipLaunchKernelGGL((mlp_loop_kernel<false, false>), dim3(M), dim3(LOOP_THREADS), LOOP_LDS, st, la);
+      }
+      AM_LAUNCH_CHECK();
+      if (nb & 1) h->cur = 1 - h->cur;
+      continue;
     }
     for (int kb = 0; kb < nb; ++kb) {
       const int64_t k = kb0 + kb;

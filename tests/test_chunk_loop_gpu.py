@@ -1,0 +1,54 @@
+"""The chunk-loop kernel (every chunk of a block in one launch, one workgroup per memory) against
+the same update run as one launch per product and chunk, through the C ABI, and both against the
+fp64 oracle.
+
+Both paths run the same tile loaders and epilogues, so they agree to rounding (the compiler may
+contract a multiply-add differently in the two kernels); the check is a 1e-5 max relative
+difference per tensor, far inside the 2e-2 bar both must meet against the oracle.  Cases cover
+per-token gates (plain, residual and gated memories, Omega windows, degree-2 features, calls
+that cut chunks), per-chunk gates without Newton-Schulz, bf16 output and update-only calls.
+"""
+
+import numpy as np
+import pytest
+
+from helpers import BF16_TOL, compare, log, maxrel, oracle_run, run_gpu
+from test_learned_neural_amd import atlasmem as am
+from test_learned_neural_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+AGREE = 1e-5
+
+CASES = [
+    # (name, workload, variant, overrides, call boundaries or None, output dtype, with Y)
+    ("mlp64_per_token", 1, "stabilised", dict(T=512), None, am.F32, True),
+    ("mlp64_streamed", 1, "stabilised", dict(batch=1, heads=3, T=320), [0, 1, 65, 130, 200, 320], am.F32, True),
+    ("mlp64_bf16_out", 1, "stabilised", dict(batch=1, heads=2, T=256), None, am.BF16, True),
+    ("mlp64_no_retrieval", 1, "stabilised", dict(batch=1, heads=2, T=256), None, am.F32, False),
+    ("omega4_poly2", 3, "stabilised", dict(batch=1, heads=4, T=256), [0, 128, 256], am.F32, True),
+    ("residual_window3", 3, "stabilised",
+     dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, heads=3, T=144, d_key=40, poly_degree=1, d_value=40,
+          d_hidden=72, chunk=48, omega_window=3), [0, 48, 96, 144], am.F32, True),
+    ("gated_per_token", 1, "stabilised", dict(kind=synth.MLP2_GATED, batch=1, heads=2, T=256), None, am.F32, True),
+    ("per_chunk_no_ns", 4, "literal", dict(batch=1, heads=3, T=512, ns_steps=0), None, am.F32, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_chunk_loop_matches_per_product_launches(case):
+    name, idx, variant, ov, splits, od, with_y = case
+    log(f"CASE chunk loop {name}")
+    inp = synth.make_inputs(idx, variant, **ov)
+    loop = run_gpu(inp, splits=splits, output_dtype=od, with_y=with_y)
+    launches = run_gpu(inp, splits=splits, output_dtype=od, with_y=with_y, flags=am.FLAG_NO_CHUNK_LOOP)
+    assert loop[3] == am.OK and launches[3] == am.OK
+    agree = {k: maxrel(a, b) for k, a, b in zip(("Y", "W", "S"), loop[:3], launches[:3]) if with_y or k != "Y"}
+    bitwise = all(np.array_equal(a, b, equal_nan=True) for a, b in zip(loop[:3], launches[:3]))
+    log(f"AGREE {name}: " + " ".join(f"{k}={v:.2e}" for k, v in agree.items()) + f" bitwise={bitwise}")
+    assert all(v <= AGREE for v in agree.values()), agree
+    ref = oracle_run(inp)
+    errs = compare(f"chunk_loop_{name}", inp.spec, loop, ref, BF16_TOL, check_state=True)
+    if not with_y:
+        errs.pop("Y")
+    assert all(v <= BF16_TOL for v in errs.values()), errs
