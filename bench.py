@@ -454,6 +454,45 @@ def _oracle_one(args):
     return m
 
 
+def config_lines(torch, am, synth, dev, stream, steps=5, warmup=2) -> dict:
+    """Every smaller workload's whole update call timed like the main line (state restored before
+    each step, inputs resident): tokens/s and, for the MLP memories, algorithmic TFLOP/s against
+    the bf16 matrix peak.  Workloads 1-3 run their stabilised inputs (the literal ones overflow
+    fp32, which leaves nothing meaningful to time); workload 0 is the literal linear memory."""
+    out = {}
+    for idx, variant in ((0, "literal"), (1, "stabilised"), (2, "stabilised"), (3, "stabilised")):
+        inp = synth.make_inputs(idx, variant)
+        s = inp.spec
+        K, Q, V = (_dev(torch, a, dev) for a in (inp.K, inp.Q, inp.V))
+        th, et, al = (_dev(torch, a, dev) for a in (inp.theta, inp.eta, inp.alpha))
+        ga = None if inp.gamma is None else _dev(torch, inp.gamma, dev)
+        W0, S0 = _dev(torch, inp.W0, dev), _dev(torch, inp.S0, dev)
+        mem = am.Memory(_cfg(am, s), W0, S0)
+        Y = torch.empty((s.n_mem, s.T, s.d_value), dtype=torch.float32, device=dev)
+
+        def step():
+            mem.set_state(W0, S0)
+            mem.reset_history()
+            mem.update_chunked(K, Q, V, th, et, al, ga, s.T, Y)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ms = event_ms(step, steps, stream)
+        tokens = s.n_mem * s.T
+        line = dict(workload=s.name, variant=variant, ms=round(ms, 4), tokens_per_s=round(tokens / (ms * 1e-3), 1))
+        if s.kind == synth.LINEAR:
+            line["path"] = "lin_kernel (one launch, sequential over tokens)"
+        else:
+            fl = sum(mlp_flops_per_chunk(s).values()) * (s.T // s.chunk) * s.n_mem
+            tf = fl / (ms * 1e-3) / 1e12
+            line.update(tflops=round(tf, 3), frac_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 6))
+        out[f"workload_{idx}"] = line
+        mem.close()
+        del K, Q, V, th, et, al, ga, W0, S0, Y
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -581,6 +620,7 @@ def main():
                      S=rel(Sg[m].cpu().numpy(), Sr[0]))
 
     stages = None if args.no_stages else stage_rooflines(torch, am, synth, dev, stream, cpu=not args.no_cpu)
+    configs = None if args.no_stages else config_lines(torch, am, synth, dev, stream)
 
     cpu = None
     if not args.no_cpu:
@@ -610,6 +650,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "check": check,
+        "configs": configs,
         "stages": stages,
     }
     print(json.dumps(out))

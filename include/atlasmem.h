@@ -125,8 +125,8 @@ typedef struct {
 /* Run the chunks of a call as one separate launch per matrix product (five per chunk) instead of
  * the chunk-loop kernel, which walks every chunk of a block inside one launch with one workgroup
  * per memory and is used where a memory's per-chunk products are small (the general MLP path
- * with per-token gates, or per-chunk gates without Newton-Schulz).  Both run the same tile
- * loaders and epilogues; results are bitwise equal. */
+ * with per-token gates, or per-chunk gates without Newton-Schulz).  Both compute the same
+ * products and epilogues; results agree to rounding. */
 #define ATLASMEM_FLAG_NO_CHUNK_LOOP 4
 
 typedef struct atlasmem_handle_s* atlasmem_handle;
