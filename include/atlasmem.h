@@ -128,6 +128,12 @@ typedef struct {
  * with per-token gates, or per-chunk gates without Newton-Schulz).  Both compute the same
  * products and epilogues; results agree to rounding. */
 #define ATLASMEM_FLAG_NO_CHUNK_LOOP 4
+/* Run every matrix product of the per-product launches over its whole k range in one launch.
+ * By default a product with few 64 x 64 output tiles and a long k range (the first-layer
+ * product of degree-2 features, the wide memory's output products) is split into k-slices whose
+ * partial tiles a second launch sums in slice order, so the slices' global-load round trips run
+ * in parallel.  Results agree to rounding. */
+#define ATLASMEM_FLAG_NO_SPLIT_K 8
 
 typedef struct atlasmem_handle_s* atlasmem_handle;
 

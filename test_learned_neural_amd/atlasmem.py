@@ -22,6 +22,7 @@ PREC_AUTO, PREC_BF16, PREC_BF16X3 = 0, 1, 2
 FLAG_NO_FUSED = 1
 FLAG_PER_TOKEN_RETRIEVE = 2
 FLAG_NO_CHUNK_LOOP = 4
+FLAG_NO_SPLIT_K = 8
 ABI_VERSION = 2
 
 EXPORTS = (

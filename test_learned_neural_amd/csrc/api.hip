@@ -41,7 +41,8 @@ atlasmem_status validate(const atlasmem_config* c) {
     return ATLASMEM_E_INVALID;
   if (c->precision < ATLASMEM_PREC_AUTO || c->precision > ATLASMEM_PREC_BF16X3) return ATLASMEM_E_INVALID;
   if (c->ns_steps > 0 && !(c->ns_eps >= 0.0f)) return ATLASMEM_E_INVALID;
-  if (c->flags & ~(ATLASMEM_FLAG_NO_FUSED | ATLASMEM_FLAG_PER_TOKEN_RETRIEVE | ATLASMEM_FLAG_NO_CHUNK_LOOP))
+  if (c->flags & ~(ATLASMEM_FLAG_NO_FUSED | ATLASMEM_FLAG_PER_TOKEN_RETRIEVE | ATLASMEM_FLAG_NO_CHUNK_LOOP |
+                   ATLASMEM_FLAG_NO_SPLIT_K))
     return ATLASMEM_E_INVALID;
   if ((int64_t)c->batch * c->heads > (1 << 20)) return ATLASMEM_E_SHAPE;
   if (c->d_key > 1024 || c->d_value > 1024 || c->d_hidden > 4096 || c->chunk > 1024 || c->omega_window > 64)
@@ -99,6 +100,7 @@ Dims make_dims(const atlasmem_config* c) {
   d.split = c->precision != ATLASMEM_PREC_BF16;
   d.no_fused = (c->flags & ATLASMEM_FLAG_NO_FUSED) != 0;
   d.no_loop = (c->flags & ATLASMEM_FLAG_NO_CHUNK_LOOP) != 0;
+  d.no_splitk = (c->flags & ATLASMEM_FLAG_NO_SPLIT_K) != 0;
   d.ptr = (c->flags & ATLASMEM_FLAG_PER_TOKEN_RETRIEVE) != 0;
   return d;
 }
@@ -183,12 +185,18 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
   const size_t opg = cv.take(sizeof(float) * M * d.C), opth = cv.take(sizeof(float) * M * d.C);
   const size_t opet = cv.take(sizeof(float) * M * d.C), opal = cv.take(sizeof(float) * M * d.C);
   const size_t state_end = cv.off;
-  size_t oZ = 0, oD2 = 0, oD1 = 0, ocW = 0, ocS = 0, ooW = 0, ooS = 0, oscal = 0, oG = 0, oZr = 0;
+  size_t oZ = 0, oD2 = 0, oD1 = 0, osk = 0, ocW = 0, ocS = 0, ooW = 0, ooS = 0, oscal = 0, oG = 0, oZr = 0;
   size_t opZS = 0, opA1 = 0, opYB = 0, opbA = 0, opOm = 0;
   if (d.kind == ATLASMEM_MLP2_SILU) {
     oZ = cv.take(sizeof(float) * M * d.Rt * d.dz);
     oD2 = cv.take(sizeof(float) * M * d.Rk * d.dv);
     oD1 = cv.take(sizeof(float) * M * d.Rk * d.dz);
+    {  // room for 16 k-slices of the chunk's row products, at most 16 MB
+      const int64_t w = d.dz > d.dv ? d.dz : d.dv;
+      int64_t f = 16 * M * (int64_t)d.Rt * w;
+      h->sk_floats = f < ((int64_t)4 << 20) ? f : ((int64_t)4 << 20);
+      osk = cv.take(sizeof(float) * h->sk_floats);
+    }
     const int64_t per_chunk_floats = M * (2 * (int64_t)d.C + 2 * (int64_t)d.Rk + 3);
     int64_t ncb = ((int64_t)32 << 20) / 4 / per_chunk_floats;
     ncb = ncb < 1 ? 1 : (ncb > 4096 ? 4096 : ncb);
@@ -241,6 +249,7 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
     h->Z = (float*)(base + oZ);
     h->D2 = (float*)(base + oD2);
     h->D1 = (float*)(base + oD1);
+    h->sk = (float*)(base + osk);
     h->cW = ocW ? (float*)(base + ocW) : nullptr;
     h->cS = ocS ? (float*)(base + ocS) : nullptr;
     h->oW = ooW ? (float*)(base + ooW) : nullptr;

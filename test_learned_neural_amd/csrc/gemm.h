@@ -46,7 +46,9 @@ struct TileSmem {
 // round passes active = false and only takes part in them (barriers are workgroup-wide).
 template <bool SPLIT, bool A_EXACT, bool B_EXACT, class LA, class LB, class EP>
 __device__ __forceinline__ void gemm_tile(int M, int N, int K, const LA& la, const LB& lb, const EP& ep, int z, int m0,
-                                          int n0, int t, TileSmem<SPLIT, A_EXACT, B_EXACT>& sm, bool active) {
+                                          int n0, int t, TileSmem<SPLIT, A_EXACT, B_EXACT>& sm, bool active,
+                                          int kbeg = 0, int kend = -1) {
+  if (kend < 0) kend = K;
   const int lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
   const int lr = lane & 15, lk = (lane >> 4) * 8;
@@ -58,7 +60,7 @@ __device__ __forceinline__ void gemm_tile(int M, int N, int K, const LA& la, con
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int srow = t >> 2, sk = (t & 3) * 8;
-  for (int k0 = 0; k0 < K; k0 += GK) {
+  for (int k0 = kbeg; k0 < kend; k0 += GK) {
     if (active) {
       {
         float v[8];
@@ -158,10 +160,77 @@ __global__ void __launch_bounds__(256) gemm_tile_kernel(int M, int N, int K, LA 
                                      sm, true);
 }
 
+// Split-K: a product with few output tiles and a long k range (each k-step is a dependent
+// global-load round trip) runs as nsplit k-slices, slice sp of batch z writing its partial tile
+// to part[((sp * batch + z) * M + row) * N + col]; the reduction sums the slices in slice order
+// (deterministic) and applies the product's epilogue.
+struct EpiPart {
+  float* part;
+  int64_t mn;
+  int N, batch, sp;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    part[((int64_t)sp * batch + z) * mn + (int64_t)row * N + col] = v;
+  }
+};
+
+template <bool SPLIT, bool A_EXACT, bool B_EXACT, class LA, class LB>
+__global__ void __launch_bounds__(256) gemm_part_kernel(int M, int N, int K, int batch, int kslice, LA la, LB lb,
+                                                        float* part) {
+  __shared__ __attribute__((aligned(16))) TileSmem<SPLIT, A_EXACT, B_EXACT> sm;
+  const int z = blockIdx.z % batch, sp = blockIdx.z / batch;
+  const int kb = sp * kslice, ke = kb + kslice < K ? kb + kslice : K;
+  const EpiPart ep{part, (int64_t)M * N, N, batch, sp};
+  gemm_tile<SPLIT, A_EXACT, B_EXACT>(M, N, K, la, lb, ep, z, blockIdx.y * GT, blockIdx.x * GT, threadIdx.x, sm, true,
+                                     kb, ke);
+}
+
+template <class EP>
+__global__ void splitk_reduce_kernel(int M, int N, int batch, int nsplit, const float* __restrict__ part, EP ep) {
+  const int64_t mn = (int64_t)M * N;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= mn * batch) return;
+  const int z = (int)(e / mn);
+  const int64_t rem = e - z * mn;
+  const int row = (int)(rem / N), col = (int)(rem - (int64_t)row * N);
+  float v = 0.0f;
+  for (int sp = 0; sp < nsplit; ++sp) v += part[((int64_t)sp * batch + z) * mn + rem];
+  if constexpr (EpiTwoPhase<EP>::value) ep.store(z, row, col, v, ep.load(z, row, col));
+  else ep(z, row, col, v);
+}
+
+// Slices for a product of `tiles` output tiles and nk k-steps: enough workgroups to spread over
+// the chip, at least four k-steps per slice, and partials that fit the scratch.
+inline int splitk_slices(int M, int N, int K, int batch, int64_t scratch_floats) {
+  const int64_t tiles = (int64_t)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * batch;
+  const int nk = (K + GK - 1) / GK;
+  if (scratch_floats <= 0 || tiles >= 256 || nk < 8) return 1;
+  int ns = (int)((512 + tiles - 1) / tiles);
+  if (ns > nk / 4) ns = nk / 4;
+  while (ns > 1 && (int64_t)ns * batch * M * N > scratch_floats) --ns;
+  return ns < 1 ? 1 : ns;
+}
+
 template <bool A_EXACT, bool B_EXACT, class LA, class LB, class EP>
 inline void launch_gemm(bool split, int M, int N, int K, int batch, const LA& la, const LB& lb, const EP& ep,
-                        hipStream_t st) {
+                        hipStream_t st, float* scratch = nullptr, int64_t scratch_floats = 0) {
   if (M <= 0 || N <= 0 || batch <= 0) return;
+  const int ns = splitk_slices(M, N, K, batch, scratch ? scratch_floats : 0);
+  if (ns > 1) {
+    const int nk = (K + GK - 1) / GK;
+    const int kslice = ((nk + ns - 1) / ns) * GK;
+    const int nsl = (K + kslice - 1) / kslice;
+    dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch * nsl);
+    if (split)
+      hipLaunchKernelGGL((gemm_part_kernel<true, A_EXACT, B_EXACT, LA, LB>), grid, dim3(256), 0, st, M, N, K, batch,
+                         kslice, la, lb, scratch);
+    else
+      hipLaunchKernelGGL((gemm_part_kernel<false, A_EXACT, B_EXACT, LA, LB>), grid, dim3(256), 0, st, M, N, K, batch,
+                         kslice, la, lb, scratch);
+    const int64_t n = (int64_t)M * N * batch;
+    hipLaunchKernelGGL((splitk_reduce_kernel<EP>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, M, N, batch,
+                       nsl, (const float*)scratch, ep);
+    return;
+  }
   dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch);
   if (split)
     hipLaunchKernelGGL((gemm_tile_kernel<true, A_EXACT, B_EXACT, LA, LB, EP>), grid, dim3(256), 0, st, M, N, K, la,

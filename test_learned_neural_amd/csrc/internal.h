@@ -28,6 +28,7 @@ struct Dims {
   bool split;   // bf16 hi/lo split products
   bool no_fused;
   bool no_loop;  // one launch per product and chunk instead of the chunk-loop kernel
+  bool no_splitk;  // every product over its whole k range in one launch
 };
 
 // The token arrays of one launch sequence: T tokens; per memory, token stride `ld` of K, Q, V, Y,
@@ -78,6 +79,8 @@ struct atlasmem_handle_s {
   float* Z;      // [M][Rt][dh]
   float* D2;     // [M][Rk][dv]
   float* D1;     // [M][Rk][dh]
+  float* sk;     // split-K partial products of the per-product launches
+  int64_t sk_floats;
   // gate coefficients for a batch of up to ncb chunks
   int ncb;
   float* cW;     // [M][ncb*C]

@@ -471,13 +471,16 @@ static __host__ __device__ StridedLoader hidden(const Dims& d, const float* Z, i
   return l;
 }
 
+// `h` supplies the split-K scratch (null: no split).
 template <class LA, class LB, class EP>
 static void gemm_any(bool split, bool a_exact, bool b_exact, int M, int N, int K, int batch, const LA& la, const LB& lb,
-                     const EP& ep, hipStream_t st) {
-  if (a_exact && b_exact) launch_gemm<true, true>(split, M, N, K, batch, la, lb, ep, st);
-  else if (a_exact) launch_gemm<true, false>(split, M, N, K, batch, la, lb, ep, st);
-  else if (b_exact) launch_gemm<false, true>(split, M, N, K, batch, la, lb, ep, st);
-  else launch_gemm<false, false>(split, M, N, K, batch, la, lb, ep, st);
+                     const EP& ep, hipStream_t st, const Handle* h = nullptr) {
+  float* sk = (h && !h->d.no_splitk) ? h->sk : nullptr;
+  const int64_t skf = h ? h->sk_floats : 0;
+  if (a_exact && b_exact) launch_gemm<true, true>(split, M, N, K, batch, la, lb, ep, st, sk, skf);
+  else if (a_exact) launch_gemm<true, false>(split, M, N, K, batch, la, lb, ep, st, sk, skf);
+  else if (b_exact) launch_gemm<false, true>(split, M, N, K, batch, la, lb, ep, st, sk, skf);
+  else launch_gemm<false, false>(split, M, N, K, batch, la, lb, ep, st, sk, skf);
 }
 
 static FeatRows feat_rows(const Handle* h, const void* K, const void* Q, int64_t ld, int64_t s, int Rk, int nrows,
@@ -526,14 +529,14 @@ static atlasmem_status ptr_retrieve(Handle* h, const Dims& d, const void* K, con
     FeatA la{qrows};
     StridedLoader lb = strided(Sin, d.P, din, 1, 1, dz, din);
     EpiStore ep{h->pZS, qz, dz, 1};
-    gemm_any(split, feat_exact, false, C, dz, din, M, la, lb, ep, st);
+    gemm_any(split, feat_exact, false, C, dz, din, M, la, lb, ep, st, h);
   }
   // scores A1[t][r] = q_t . x_r over the key rows (window history included)
   {
     FeatA la{qrows};
     FeatA lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)};
     EpiStore ep{h->pA1, az, Rk, 1};
-    gemm_any(split, feat_exact, feat_exact, C, Rk, din, M, la, lb, ep, st);
+    gemm_any(split, feat_exact, feat_exact, C, Rk, din, M, la, lb, ep, st, h);
   }
   // Zq = beta Z0 + a ZS - (Om * A1) D1
   {
@@ -543,21 +546,21 @@ static atlasmem_status ptr_retrieve(Handle* h, const Dims& d, const void* K, con
     la.cld = Rk;
     StridedLoader lb = strided(h->D1, (int64_t)Rk * dz, 1, dz, 1, dz, Rk);  // B(k=r, j) = D1[r][j]
     EpiZq ep{h->pZS, h->Z, h->pbA, qz, zsz, (int64_t)Rk, dz, C};
-    gemm_any(split, false, false, C, dz, Rk, M, la, lb, ep, st);
+    gemm_any(split, false, false, C, dz, Rk, M, la, lb, ep, st, h);
   }
   // scores A2[t][r] = Hq_t . h_r
   {
     StridedLoader la = hidden(d, h->pZS, qz, dz, 1, 1, C, dh);
     StridedLoader lb = hidden(d, h->Z, zsz, dz, 1, 1, Rk, dh);  // B(k=h, j=r) = H[r][h]
     EpiStore ep{h->pA1, az, Rk, 1};
-    gemm_any(split, false, false, C, Rk, dh, M, la, lb, ep, st);
+    gemm_any(split, false, false, C, Rk, dh, M, la, lb, ep, st, h);
   }
   // YB = beta Hq W0_2^T + a Hq S0_2^T
   for (int which = 0; which < 2; ++which) {
     StridedLoader la = hidden(d, h->pZS, qz, dz, 1, 1, C, dh);
     StridedLoader lb = strided((which ? Sin : Win) + d.P1, d.P, dh, 1, 1, dv, dh);  // B(k=h, j=v) = W2[v][h]
     EpiRowMix ep{h->pYB, h->pbA, yz, dv, C, which, which};
-    gemm_any(split, false, false, C, dv, dh, M, la, lb, ep, st);
+    gemm_any(split, false, false, C, dv, dh, M, la, lb, ep, st, h);
   }
   // Y = YB - (Om * A2) D2 (+ the query's features for the residual memory)
   {
@@ -567,7 +570,7 @@ static atlasmem_status ptr_retrieve(Handle* h, const Dims& d, const void* K, con
     la.cld = Rk;
     StridedLoader lb = strided(h->D2, (int64_t)Rk * dv, 1, dv, 1, dv, Rk);  // B(k=r, j=v) = D2[r][v]
     EpiYptr ep{h->pYB, yz, dv, ld, s, Y, d.out_bf16, d.residual, qrows};
-    gemm_any(split, false, false, C, dv, Rk, M, la, lb, ep, st);
+    gemm_any(split, false, false, C, dv, Rk, M, la, lb, ep, st, h);
   }
   return ATLASMEM_OK;
 }
@@ -837,7 +840,7 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
         FeatA la{feat_rows(h, K, Q, ld, s, Rk, nrows, 1)};
         StridedLoader lb = strided(W1, d.P, din, 1, 1, dz, din);  // B(k=f, j=h) = W1[h][f]
         EpiStore ep{h->Z, zsz, dz, 1};
-        gemm_any(split, feat_exact, false, nrows, dz, din, M, la, lb, ep, st);
+        gemm_any(split, feat_exact, false, nrows, dz, din, M, la, lb, ep, st, h);
       }
       // Yh = H W2^T -> D2 (key rows), Y (query rows; with per-token retrieval they are answered
       // below from the per-token states instead)
@@ -847,14 +850,14 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
         StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);  // B(k=h, j=v) = W2[v][h]
         EpiY ep{h->D2, (int64_t)Rk * dv, V, d.in_bf16, h->hv[h->hcur], ld, s, Rk, c, dv, Y, d.out_bf16,
                 d.residual, feat_rows(h, K, Q, ld, s, Rk, nrows, 1)};
-        gemm_any(split, false, false, yrows, dv, dh, M, la, lb, ep, st);
+        gemm_any(split, false, false, yrows, dv, dh, M, la, lb, ep, st, h);
       }
       // Pm = D2 W2 -> D1 = Pm * silu'(Z)
       {
         StridedLoader la = strided(h->D2, (int64_t)Rk * dv, dv, 1, 1, Rk, dv);
         StridedLoader lb = strided(W2, d.P, 1, dh, 1, dh, dv);  // B(k=v, j=h) = W2[v][h]
         EpiP ep{h->D1, h->Z, (int64_t)Rk * dz, zsz, dh, dz, d.gated};
-        gemm_any(split, false, false, Rk, dh, dv, M, la, lb, ep, st);
+        gemm_any(split, false, false, Rk, dh, dv, M, la, lb, ep, st, h);
       }
       if (per_token) {
         const float* c0 = (c > 1) ? h->oW + (int64_t)kb * Rk : h->cW + (int64_t)kb * C;
@@ -869,7 +872,7 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
           la.cz = cz;
           StridedLoader lb = hidden(d, h->Z, zsz, 1, dz, 2, dh, Rk);
           EpiUpdPair ep{Win, Sin, Wout, Sout, d.P, d.P1, dh, sc, (int64_t)h->ncb * 3, h->flag};
-          gemm_any(split, false, false, dv, dh, Rk, 2 * M, la, lb, ep, st);
+          gemm_any(split, false, false, dv, dh, Rk, 2 * M, la, lb, ep, st, h);
         }
         // W1 pair (gated: W1 and W3 as one block of 2 d_hidden rows): A(i=h, k=row) =
         // D1[row][h] * coef[row], B(k=row, j=f) = X[row][f]
@@ -880,33 +883,33 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
           la.cz = cz;
           FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 2)};
           EpiUpdPair ep{Win, Sin, Wout, Sout, d.P, 0, din, sc, (int64_t)h->ncb * 3, h->flag};
-          gemm_any(split, false, feat_exact, dz, din, Rk, 2 * M, la, lb, ep, st);
+          gemm_any(split, false, feat_exact, dz, din, Rk, 2 * M, la, lb, ep, st, h);
         }
       } else if (d.ns_steps == 0) {
         {
           StridedLoader la = strided(h->D2, (int64_t)Rk * dv, 1, dv, 1, dv, Rk);
           StridedLoader lb = hidden(d, h->Z, zsz, 1, dz, 1, dh, Rk);
           EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, d.P1, dh, theta, eta, alpha, sp.ldg, k, h->flag};
-          gemm_any(split, false, false, dv, dh, Rk, M, la, lb, ep, st);
+          gemm_any(split, false, false, dv, dh, Rk, M, la, lb, ep, st, h);
         }
         {
           StridedLoader la = strided(h->D1, (int64_t)Rk * dz, 1, dz, 1, dz, Rk);
           FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)};
           EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, 0, din, theta, eta, alpha, sp.ldg, k, h->flag};
-          gemm_any(split, false, feat_exact, dz, din, Rk, M, la, lb, ep, st);
+          gemm_any(split, false, feat_exact, dz, din, Rk, M, la, lb, ep, st, h);
         }
       } else {
         {
           StridedLoader la = strided(h->D2, (int64_t)Rk * dv, 1, dv, 1, dv, Rk);
           StridedLoader lb = hidden(d, h->Z, zsz, 1, dz, 1, dh, Rk);
           EpiStore ep{h->G + d.P1, d.P, dh, 1};
-          gemm_any(split, false, false, dv, dh, Rk, M, la, lb, ep, st);
+          gemm_any(split, false, false, dv, dh, Rk, M, la, lb, ep, st, h);
         }
         {
           StridedLoader la = strided(h->D1, (int64_t)Rk * dz, 1, dz, 1, dz, Rk);
           FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)};
           EpiStore ep{h->G, d.P, din, 1};
-          gemm_any(split, false, feat_exact, dz, din, Rk, M, la, lb, ep, st);
+          gemm_any(split, false, feat_exact, dz, din, Rk, M, la, lb, ep, st, h);
         }
         // each weight matrix separately: W1, (W3,) W2
         NsUpdate u1{Win, Sin, Wout, Sout, d.P, 0, 1, theta, eta, alpha, sp.ldg, k, h->flag};
@@ -951,14 +954,14 @@ atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, int64_t ld, vo
       FeatA la{feat_rows(h, nullptr, Q, ld, s, 0, rows, 1)};
       StridedLoader lb = strided(W1, d.P, din, 1, 1, dz, din);
       EpiStore ep{h->Zr, zsz, dz, 1};
-      gemm_any(d.split, feat_exact, false, rows, dz, din, M, la, lb, ep, st);
+      gemm_any(d.split, feat_exact, false, rows, dz, din, M, la, lb, ep, st, h);
     }
     {
       StridedLoader la = hidden(d, h->Zr, zsz, dz, 1, 1, rows, dh);
       StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);
       EpiY ep{nullptr, 0, nullptr, d.in_bf16, nullptr, ld, s, 0, d.c, dv, Y, d.out_bf16, d.residual,
               feat_rows(h, nullptr, Q, ld, s, 0, rows, 1)};
-      gemm_any(d.split, false, false, rows, dv, dh, M, la, lb, ep, st);
+      gemm_any(d.split, false, false, rows, dv, dh, M, la, lb, ep, st, h);
     }
     AM_LAUNCH_CHECK();
   }

@@ -52,3 +52,30 @@ def test_chunk_loop_matches_per_product_launches(case):
     if not with_y:
         errs.pop("Y")
     assert all(v <= BF16_TOL for v in errs.values()), errs
+
+
+SPLIT_CASES = [
+    # (name, workload, variant, overrides, call boundaries or None)
+    ("omega4_poly2_first_layer", 3, "stabilised", dict(batch=1, heads=4, T=256), [0, 128, 256]),
+    ("wide_384x768", 2, "stabilised", dict(T=256), None),
+    ("wide_residual_streamed", 2, "stabilised", dict(kind=synth.MLP2_SILU_RESIDUAL, batch=1, T=192), [0, 5, 64, 192]),
+    ("wide_per_chunk_gates", 2, "stabilised", dict(batch=1, T=256, gate_mode=synth.PER_CHUNK, ns_steps=0), None),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_k_matches_whole_k(case):
+    """Products split into k-slices (partial tiles summed in slice order, then the epilogue)
+    against the same products over the whole k range, and against the oracle."""
+    name, idx, variant, ov, splits = case
+    log(f"CASE split-K {name}")
+    inp = synth.make_inputs(idx, variant, **ov)
+    sk = run_gpu(inp, splits=splits)
+    whole = run_gpu(inp, splits=splits, flags=am.FLAG_NO_SPLIT_K)
+    assert sk[3] == am.OK and whole[3] == am.OK
+    agree = {k: maxrel(a, b) for k, a, b in zip(("Y", "W", "S"), sk[:3], whole[:3])}
+    log(f"AGREE {name}: " + " ".join(f"{k}={v:.2e}" for k, v in agree.items()))
+    assert all(v <= AGREE for v in agree.values()), agree
+    ref = oracle_run(inp)
+    errs = compare(f"split_k_{name}", inp.spec, sk, ref, BF16_TOL)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
