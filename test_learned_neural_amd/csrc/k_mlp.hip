@@ -193,18 +193,22 @@ struct FeatB {
     int i, j;
     const int kind = feat_kind(fr, f, i, j);
     const bool hh = fr.any_hist();
-    if (fr.poly == 1 && !hh && r0 + 8 <= fr.nrows && (r0 + 8 <= fr.Rk || r0 >= fr.Rk)) {
-      // eight consecutive rows of one array (K or Q): one base, a 32-bit row stride
+    if (!hh && r0 + 8 <= fr.nrows && (r0 + 8 <= fr.Rk || r0 >= fr.Rk)) {
+      // eight consecutive rows of one array (K or Q): one base, a 32-bit row stride; the
+      // feature's monomial (i, j) is the same for all eight
       const void* src;
       int64_t off, hoff;
       bool hist;
       fr.locate(mem, r0, src, off, hoff, hist);
       const int st = fr.dk;
-      uint32_t b[8];
+      uint32_t bi[8], bj[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) b[u] = fr.ld_bits((const char*)src, off + i + (int64_t)(u * st));
+      for (int u = 0; u < 8; ++u) {
+        bi[u] = fr.ld_bits(src, off + i + (int64_t)(u * st));
+        bj[u] = kind == 2 ? fr.ld_bits(src, off + j + (int64_t)(u * st)) : 0u;
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = kind == 1 ? fr.bits_val(b[u]) : 0.0f;
+      for (int u = 0; u < 8; ++u) v[u] = feat_value(kind, fr.bits_val(bi[u]), fr.bits_val(bj[u]));
       return;
     }
     uint32_t bi[8], bj[8];
