@@ -122,3 +122,22 @@ def test_create_without_a_gpu_reports_device_error():
     h = ctypes.c_void_p()
     assert lib.atlasmem_create(ctypes.byref(cfg4()), None, None, None, ctypes.byref(h)) == am.E_DEVICE
     assert h.value is None
+
+
+def test_binding_flags_match_header():
+    """Every ATLASMEM_FLAG_* the header defines has the same value in the binding, and the
+    library rejects a flag bit the header does not define."""
+    text = open(HEADER).read()
+    flags = dict((n, int(v)) for n, v in re.findall(r"#define ATLASMEM_FLAG_([A-Z_]+) (\d+)", text))
+    assert {"NO_FUSED", "PER_TOKEN_RETRIEVE", "NO_CHUNK_LOOP", "NO_SPLIT_K"} <= set(flags)
+    for n, v in flags.items():
+        assert getattr(am, "FLAG_" + n) == v, n
+    assert len(set(flags.values())) == len(flags)
+    lib = am.load()
+    unknown = 1
+    while unknown in flags.values():
+        unknown <<= 1
+    cfg = am.make_config(kind=am.MLP2_SILU, batch=1, heads=1, d_key=64, d_value=64, d_hidden=128, chunk=64,
+                         input_dtype=am.BF16, flags=unknown)
+    h = ctypes.c_void_p()
+    assert lib.atlasmem_create(ctypes.byref(cfg), None, None, None, ctypes.byref(h)) == am.E_INVALID
