@@ -132,15 +132,31 @@ __global__ void ptr_coeff_kernel(const float* __restrict__ theta, const float* _
                                  const float* __restrict__ alpha, const float* __restrict__ gamma, int64_t ld,
                                  const float* __restrict__ ghist, int64_t s0, int C, int c, float* __restrict__ bA,
                                  float* __restrict__ Om) {
-  extern __shared__ float pc[];  // w[C], E[C], tw[C]
+  // w[C], E[C], tw[C], then the chunk's gates th, et, al [C] and the key rows' gamma [Rk], staged
+  // once so that the sequential loop over the chunk's tokens makes no global loads
+  extern __shared__ float pc[];
   float* w = pc;
   float* E = pc + C;
   float* tw = pc + 2 * C;
+  float* th = pc + 3 * C;
+  float* et = pc + 4 * C;
+  float* al = pc + 5 * C;
+  float* gr = pc + 6 * C;
   const int m = blockIdx.x;
   const int Rk = C + c - 1;
-  const float* th = theta + (int64_t)m * ld + s0;
-  const float* et = eta + (int64_t)m * ld + s0;
-  const float* al = alpha + (int64_t)m * ld + s0;
+  for (int l = threadIdx.x; l < C; l += blockDim.x) {
+    const int64_t o = (int64_t)m * ld + s0 + l;
+    th[l] = theta[o];
+    et[l] = eta[o];
+    al[l] = alpha[o];
+  }
+  if (c > 1) {
+    for (int r = threadIdx.x; r < Rk; r += blockDim.x) {  // gamma of token s0 + r - (c - 1)
+      const int64_t tau = s0 + r - (c - 1);
+      gr[r] = (tau >= 0) ? gamma[(int64_t)m * ld + tau] : ghist[(int64_t)m * (c - 1) + (c - 1) + tau];
+    }
+  }
+  __syncthreads();
   float beta = 1.0f, a = 0.0f, P = 1.0f;
   for (int t = 0; t < C; ++t) {
     const float om = 1.0f - al[t], e = et[t];
@@ -171,10 +187,7 @@ __global__ void ptr_coeff_kernel(const float* __restrict__ theta, const float* _
         const int lo = i > 0 ? i : 0;
         const int hi = (i + c - 1) < t ? (i + c - 1) : t;
         for (int l = lo; l <= hi; ++l) v += tw[l];
-        if (c > 1) {  // gamma of token s0 + i of the call, or of the history before the call
-          const int64_t tau = s0 + i;
-          v *= (tau >= 0) ? gamma[(int64_t)m * ld + tau] : ghist[(int64_t)m * (c - 1) + (c - 1) + tau];
-        }
+        if (c > 1) v *= gr[r];  // gamma of token s0 + i of the call, or of the history before it
       }
       orow[r] = v;
     }
@@ -190,8 +203,13 @@ atlasmem_status launch_ptr_coeffs(const float* theta, const float* eta, const fl
                                   int64_t ld, const float* ghist, int M, int64_t s0, int C, int c, float* bA,
                                   float* Om, hipStream_t st) {
   if (M == 0) return ATLASMEM_OK;
-  hipLaunchKernelGGL(ptr_coeff_kernel, dim3(M), dim3(256), (size_t)3 * C * sizeof(float), st, theta, eta, alpha,
-                     gamma, ld, ghist, s0, C, c, bA, Om);
+  const size_t lds = ((size_t)6 * C + C + c - 1) * sizeof(float);
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)ptr_coeff_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+          hipSuccess)
+    return ATLASMEM_E_DEVICE;
+  hipLaunchKernelGGL(ptr_coeff_kernel, dim3(M), dim3(256), lds, st, theta, eta, alpha, gamma, ld, ghist, s0, C, c,
+                     bA, Om);
   AM_LAUNCH_CHECK();
   return ATLASMEM_OK;
 }
