@@ -10,6 +10,9 @@
 // of B X); A and B are kept as hi/lo in LDS (A is symmetric, so its rows serve as columns).
 // The result is written back in G's orientation, or consumed by the momentum / forgetting
 // epilogue S = eta_c S - theta_c X, W = (1 - alpha_c) W + S.
+// The B operand of B X (eight consecutive rows of one column of X per lane) is read from the
+// row-major copy with the transposing LDS read, so X is kept once: 71.6 KB of LDS per workgroup,
+// two workgroups per CU.
 #include "common.h"
 #include "internal.h"
 
@@ -18,6 +21,14 @@ namespace am {
 constexpr int NSM = 64, NSN = 128;
 constexpr int LX = NSN + 8;  // row stride of X (bf16)
 constexpr int LT = NSM + 8;  // row stride of X^T, A, B (bf16)
+
+typedef short ns_v4i16 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4e + q names the 8-byte chunk of row e,
+// columns 4q..4q+3 of a 4 x 16 block of bf16; lane i receives column i of the four rows.
+__device__ __forceinline__ uint2 ns_tr16(const uint16_t* p) {
+  const ns_v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ns_v4i16*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 struct NsArgs {
   const float* G;
@@ -33,8 +44,6 @@ template <bool SPLIT>
 __global__ void __launch_bounds__(256) ns_kernel(NsArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t Xh[NSM * LX];
   __shared__ __attribute__((aligned(16))) uint16_t Xl[SPLIT ? NSM * LX : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t XTh[NSN * LT];
-  __shared__ __attribute__((aligned(16))) uint16_t XTl[SPLIT ? NSN * LT : 8];
   __shared__ __attribute__((aligned(16))) uint16_t Ah[NSM * LT];
   __shared__ __attribute__((aligned(16))) uint16_t Al[SPLIT ? NSM * LT : 8];
   __shared__ __attribute__((aligned(16))) uint16_t Bh[NSM * LT];
@@ -81,11 +90,7 @@ __global__ void __launch_bounds__(256) ns_kernel(NsArgs p) {
           uint32_t hi, lo;
           split_bf16(x[ri][cj][r], hi, lo);
           Xh[i * LX + j] = (uint16_t)hi;
-          XTh[j * LT + i] = (uint16_t)hi;
-          if (SPLIT) {
-            Xl[i * LX + j] = (uint16_t)lo;
-            XTl[j * LT + i] = (uint16_t)lo;
-          }
+          if (SPLIT) Xl[i * LX + j] = (uint16_t)lo;
         }
   };
 #pragma unroll
@@ -171,14 +176,21 @@ __global__ void __launch_bounds__(256) ns_kernel(NsArgs p) {
     for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
       for (int cj = 0; cj < 2; ++cj) acc[ri][cj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // transposing reads: lane 4e + q of group lq addresses row 32 kk + 8 lq + e (+4), columns
+    // 32 w + 16 cj + 4q .. +3, and receives column 32 w + 16 cj + lr of those rows
+    const int te = (lane & 15) >> 2, tq = lane & 3;
 #pragma unroll
     for (int kk = 0; kk < NSM / 32; ++kk) {
       u32x4 bh[2], bl[2];
 #pragma unroll
       for (int cj = 0; cj < 2; ++cj) {
-        const int bo = (32 * w + 16 * cj + lr) * LT + kk * 32 + lk;
-        bh[cj] = *(const u32x4*)&XTh[bo];
-        if (SPLIT) bl[cj] = *(const u32x4*)&XTl[bo];
+        const int bo = (32 * kk + 8 * lq + te) * LX + 32 * w + 16 * cj + 4 * tq;
+        const uint2 h0 = ns_tr16(&Xh[bo]), h1 = ns_tr16(&Xh[bo + 4 * LX]);
+        bh[cj] = u32x4{h0.x, h0.y, h1.x, h1.y};
+        if (SPLIT) {
+          const uint2 l0 = ns_tr16(&Xl[bo]), l1 = ns_tr16(&Xl[bo + 4 * LX]);
+          bl[cj] = u32x4{l0.x, l0.y, l1.x, l1.y};
+        }
       }
 #pragma unroll
       for (int ri = 0; ri < 4; ++ri) {
@@ -202,7 +214,7 @@ __global__ void __launch_bounds__(256) ns_kernel(NsArgs p) {
       for (int cj = 0; cj < 2; ++cj)
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[ri][cj][r] = p.a * x[ri][cj][r] + acc[ri][cj][r];
-    __syncthreads();  // every wave is done reading X, X^T, B
+    __syncthreads();  // every wave is done reading X and B
     store_x();
     __syncthreads();
   }
