@@ -48,6 +48,10 @@ struct Args {
   float* pet;
   float* pal;
   float* pg;
+  // One-token calls whose W2 product takes every thread once (dv rows x p lanes = 256) with a
+  // segment of at most 32 floats: each thread loads its own W2 segment (w2v float4) at the start,
+  // so that those loads overlap the query staging and W1 q instead of following them.
+  int w2v;
 };
 
 __device__ __forceinline__ void split1(float x, float& hi, float& lo) {
@@ -123,6 +127,14 @@ __global__ void __launch_bounds__(256) decode_kernel(Args a) {
     }
   }
   if (!a.Y) return;
+  float4 w2r[8];
+  if (a.w2v) {
+    const int p = lanes_per_row(a.dv, a.dh), seg = a.dh / p;
+    const float4* w2 = (const float4*)(a.W + (int64_t)z * a.P + a.P1 + (int64_t)(t / p) * a.dh + (t % p) * seg);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < a.w2v) w2r[u] = w2[u];
+  }
   // LDS: q hi, q lo [n][din]; Z [n][dz]; H hi, H lo [n][dh]
   float* qh = ds;
   float* ql = qh + n * a.din;
@@ -170,7 +182,26 @@ __global__ void __launch_bounds__(256) decode_kernel(Args a) {
     for (int e0 = 0; e0 < n * a.dv * p; e0 += 256) {
       const int e = e0 + t, task = e / p, part = e - task * p;
       float y = 0.0f;
-      if (task < n * a.dv) {
+      if (a.w2v) {  // n = 1, one task per thread: row t / p, segment t % p, weights in registers
+        const int i0 = part * seg;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (u >= a.w2v) break;
+          const float wv[4] = {w2r[u].x, w2r[u].y, w2r[u].z, w2r[u].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int i = i0 + 4 * u + c;
+            float wh, wl;
+            split1(wv[c], wh, wl);
+            const float ah = hh[i];
+            y = fmaf(ah, wh, y);
+            if (a.split) {
+              y = fmaf(ah, wl, y);
+              y = fmaf(hl[i], wh, y);
+            }
+          }
+        }
+      } else if (task < n * a.dv) {
         const int tt = task / a.dv, v = task - tt * a.dv, i0 = part * seg;
         y = seg_dot(W2 + (int64_t)v * a.dh + i0, hh + tt * a.dh + i0, hl + tt * a.dh + i0, seg, false, a.split);
       }
@@ -242,6 +273,12 @@ atlasmem_status launch_decode(Handle* h, const void* Q, const void* K, const voi
   a.pet = h->pet;
   a.pal = h->pal;
   a.pg = h->pg;
+  a.w2v = 0;
+  if (Y && n == 1 && d.P % 4 == 0 && d.P1 % 4 == 0) {  // the kernel's lane split of the W2 product
+    int p = 1;
+    while (p < 64 && d.dv * p * 2 <= 256 && d.dh % (8 * p) == 0) p *= 2;
+    if (d.dv * p == 256 && (d.dh / p) % 4 == 0 && d.dh / p <= 32) a.w2v = d.dh / p / 4;
+  }
   hipLaunchKernelGGL(dk::decode_kernel, dim3(d.M), dim3(256), Y ? decode_lds(d, n) : 0, st, a);
   AM_LAUNCH_CHECK();
   if (append) h->pending += n;
