@@ -79,3 +79,24 @@ def test_split_k_matches_whole_k(case):
     ref = oracle_run(inp)
     errs = compare(f"split_k_{name}", inp.spec, sk, ref, BF16_TOL)
     assert all(v <= BF16_TOL for v in errs.values()), errs
+
+
+def test_chunk_loop_spans_coefficient_blocks():
+    """A call longer than one block of gate coefficients: 2048 memories with chunk 16 give
+    blocks of 61 chunks, so a 1024-token call runs blocks of 61 and 3 chunks (an odd first
+    block flips the state buffers). The chunk loop against the per-product launches on every
+    memory, and against the oracle on three memories."""
+    log("CASE chunk loop over two coefficient blocks")
+    inp = synth.make_inputs(1, "stabilised", batch=64, heads=32, T=1024, chunk=16, d_key=16, d_value=16,
+                            d_hidden=32)
+    loop = run_gpu(inp)
+    launches = run_gpu(inp, flags=am.FLAG_NO_CHUNK_LOOP)
+    assert loop[3] == am.OK and launches[3] == am.OK
+    agree = {k: maxrel(a, b) for k, a, b in zip(("Y", "W", "S"), loop[:3], launches[:3])}
+    log("AGREE blocks: " + " ".join(f"{k}={v:.2e}" for k, v in agree.items()))
+    assert all(v <= AGREE for v in agree.values()), agree
+    mems = [0, 1029, 2047]
+    ref = oracle_run(inp, mems=mems)
+    got = tuple(x[mems] for x in loop[:3])
+    errs = compare("chunk_loop_blocks", inp.spec, got, ref, BF16_TOL)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
