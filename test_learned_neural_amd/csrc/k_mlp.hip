@@ -403,11 +403,13 @@ struct EpiUpdPair {
     const int mem = z >> 1;
     const int64_t e = (int64_t)mem * P + off + (int64_t)row * ld + col;
     float o;
+    // explicit fused multiply-adds: every kernel that inlines this epilogue (the per-product
+    // launches and the chunk loop) rounds alike, whatever the compiler would contract
     if ((z & 1) == 0) {
-      o = p.s1 * p.w + p.s2 * p.s - v;
+      o = fmaf(p.s1, p.w, fmaf(p.s2, p.s, -v));
       Wout[e] = o;
     } else {
-      o = p.s0 * p.s - v;
+      o = fmaf(p.s0, p.s, -v);
       Sout[e] = o;
     }
     if (!isfinite(o)) flag[0] = 1;
