@@ -115,9 +115,9 @@ __device__ __forceinline__ void gemm_tile(int M, int N, int K, const LA& la, con
   }
   if (!active) return;
   if constexpr (EpiTwoPhase<EP>::value) {
-    // every element's loads first, then every element's stores: element r + 1's loads may not
-    // move above element r's stores (the compiler cannot rule out aliasing), so a one-pass loop
-    // would chain sixteen memory latencies
+    // every element's loads first, then every element's stores: the compiler may not move
+    // element r + 1's loads above element r's stores (it cannot rule out aliasing), so this is
+    // what lets a lane's sixteen loads be in flight together
     typename EP::Pre pre[2][2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
