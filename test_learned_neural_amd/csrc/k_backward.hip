@@ -1070,6 +1070,10 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
                          const float* alpha, const float* gamma, int64_t T, void* Y, const float* dY,
                          const float* dWT, const float* dST, void* workspace, float* dK, float* dQ, float* dV,
                          float* dth, float* det, float* dal, float* dgamma, float* dW0, float* dS0, hipStream_t st) {
+  // split-K scratch for the products with few tiles and long k ranges (the concatenated-k
+  // adjoint products), as on the forward path; null for a handle without one
+  float* sk = h->d.no_splitk ? nullptr : h->sk;
+  const int64_t skf = h->sk_floats;
   const Dims& d = h->d;
   const int M = d.M, C = d.C, dh = d.dh, dv = d.dv, din = d.din;
   const int64_t P = d.P, P1 = d.P1;
@@ -1187,11 +1191,11 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       const float* cW0 = ck;
       const bk::Cat lk = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
       launch_gemm<false, false>(true, R, dv, din, M, lk, bk::cat1(bk::src(cW0, 0, 2 * P, din, 1, dv, din)),
-                                bk::EpiE{E, vz, Vr, vbf, vrz, dv, nullptr, 0, 0}, st);
+                                bk::EpiE{E, vz, Vr, vbf, vrz, dv, nullptr, 0, 0}, st, sk, skf);
       launch_gemm<false, false>(true, R, dv, din, M, lk, bk::cat1(bk::src(WA, 0, P, din, 1, dv, din)),
-                                bk::EpiSt{U2, vz, dv}, st);
+                                bk::EpiSt{U2, vz, dv}, st, sk, skf);
       launch_gemm<false, false>(true, R, dv, din, M, lk, bk::cat1(bk::src(SA, 0, P, din, 1, dv, din)),
-                                bk::EpiSt{U2s, vz, dv}, st);
+                                bk::EpiSt{U2s, vz, dv}, st, sk, skf);
       hipLaunchKernelGGL(bk::lin_row_kernel, dim3(R, M), dim3(64), 0, st, E, U2, U2s, vz, dv, rld, rW, rS, cWa, cSa,
                          win ? dV : dV + s * dv, T * dv, s - (c - 1), win ? 1 : 0);
       AM_LAUNCH_CHECK();
@@ -1205,20 +1209,20 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
                    bk::src(U2, 0, vz, dv, 1, R, dv, 0, nullptr, 0, 2.0f), dv, 2 * dv),
           bk::cat3(bk::src(WA, 0, P, 1, din, din, dv), bk::src(SA, 0, P, 1, din, din, dv),
                    bk::src(cW0, 0, 2 * P, 1, din, din, dv), dv, 2 * dv),
-          out, st);
+          out, st, sk, skf);
       // Q' = dY W
       launch_gemm<false, false>(true, C, din, dv, M, bk::cat1(bk::src(dY + s * dv, 0, T * dv, dv, 1, C, dv)),
                                 bk::cat1(bk::src(cW0, 0, 2 * P, 1, din, din, dv)),
                                 feat ? bk::EpiStAdd{ws + L.qg, (int64_t)C * din, din, nullptr, 0, 0, 0.0f, 0, 0}
                                      : bk::EpiStAdd{dQ + s * din, T * din, din, nullptr, 0, 0, 0.0f, 0, 0},
-                                st);
+                                st, sk, skf);
       // W' = (2E')^T X + dY^T Q   (A(i=v, k=row), B(k=row, j=f))
       launch_gemm<false, false>(
           true, dv, din, R + C, M,
           bk::cat2(bk::src(U2, 0, vz, 1, dv, dv, R, 0, nullptr, 0, 2.0f), bk::src(dY + s * dv, 0, T * dv, 1, dv, dv, C),
                    R),
           bk::cat2(bk::src(Kr, kbf, kz, 1, din, din, R), bk::src(Qr, qbf, qz, 1, din, din, C), R),
-          bk::EpiSt{Wb, P, din}, st);
+          bk::EpiSt{Wb, P, din}, st, sk, skf);
       AM_LAUNCH_CHECK();
       if (feat) {
         hipLaunchKernelGGL(bk::feat_jac_kernel, dim3(R, M), dim3(64), 0, st, ws + L.xg, ws + L.ks, R, d.dk, din, T,
@@ -1237,15 +1241,15 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
         bk::Cat lk = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
         bk::Cat lq = bk::cat1(bk::src(Qr, qbf, qz, din, 1, C, din));
         bk::Cat lb = bk::cat1(bk::src(cW1, 0, 2 * P, din, 1, dzz, din));
-        launch_gemm<false, false>(true, R, dzz, din, M, lk, lb, bk::EpiSt{Zk, gzz, dzz}, st);
-        launch_gemm<false, false>(true, C, dzz, din, M, lq, lb, bk::EpiSt{Zk + (int64_t)R * dzz, gzz, dzz}, st);
+        launch_gemm<false, false>(true, R, dzz, din, M, lk, lb, bk::EpiSt{Zk, gzz, dzz}, st, sk, skf);
+        launch_gemm<false, false>(true, C, dzz, din, M, lq, lb, bk::EpiSt{Zk + (int64_t)R * dzz, gzz, dzz}, st, sk, skf);
       }
       const bk::Src hk = bk::gated(Zk, gzz, dzz, 1, R, dh, dh);  // H of the key rows, A(i = row, k = h)
       launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(hk), bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh)),
-                                bk::EpiE{E, vz, Vr, vbf, vrz, dv, nullptr, 0, 0}, st);
+                                bk::EpiE{E, vz, Vr, vbf, vrz, dv, nullptr, 0, 0}, st, sk, skf);
       launch_gemm<false, false>(true, R, dh, dv, M, bk::cat1(bk::src(E, 0, vz, dv, 1, R, dv)),
                                 bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv)),
-                                bk::EpiPDg{Pz, D1, Zk, hz, gz, gzz, dh}, st);
+                                bk::EpiPDg{Pz, D1, Zk, hz, gz, gzz, dh}, st, sk, skf);
       // per-chunk gates: G = (Dz^T X, E^T H) over the chunk's rows, its Newton-Schulz image N, and
       // every row's gradient adjoint G' taken in place of the state adjoints (cW = -1, cS = 0)
       const float* WAg = WA;
@@ -1253,9 +1257,9 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       if (per_chunk) {
         float *Gb = ws + L.gb, *Nb = ws + L.nb, *NAb = ws + L.nab, *GAb = ws + L.gab, *SAt = ws + L.sat;
         launch_gemm<false, false>(true, dzz, din, C, M, bk::cat1(bk::src(D1, 0, gz, 1, dzz, dzz, C)),
-                                  bk::cat1(bk::src(Kr, kbf, kz, 1, din, din, C)), bk::EpiSt{Gb, P, din}, st);
+                                  bk::cat1(bk::src(Kr, kbf, kz, 1, din, din, C)), bk::EpiSt{Gb, P, din}, st, sk, skf);
         launch_gemm<false, false>(true, dv, dh, C, M, bk::cat1(bk::src(E, 0, vz, 1, dv, dv, C)),
-                                  bk::cat1(bk::gated(Zk, gzz, 1, dzz, dh, C, dh)), bk::EpiSt{Gb + P1, P, dh}, st);
+                                  bk::cat1(bk::gated(Zk, gzz, 1, dzz, dh, C, dh)), bk::EpiSt{Gb + P1, P, dh}, st, sk, skf);
         AM_LAUNCH_CHECK();
         const float* N = Gb;
         if (d.ns_steps > 0) {
@@ -1284,13 +1288,13 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       {  // U1 = X WAz^T, U1s = X SAz^T (dz wide), U2 = H WA2^T, U2s = H SA2^T
         bk::Cat lx = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
         launch_gemm<false, false>(true, R, dzz, din, M, lx, bk::cat1(bk::src(WAg, 0, P, din, 1, dzz, din)),
-                                  bk::EpiSt{U1, gz, dzz}, st);
+                                  bk::EpiSt{U1, gz, dzz}, st, sk, skf);
         launch_gemm<false, false>(true, R, dzz, din, M, lx, bk::cat1(bk::src(SAg, 0, P, din, 1, dzz, din)),
-                                  bk::EpiSt{U1s, gz, dzz}, st);
+                                  bk::EpiSt{U1s, gz, dzz}, st, sk, skf);
         launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(hk), bk::cat1(bk::src(WAg + P1, 0, P, dh, 1, dv, dh)),
-                                  bk::EpiSt{U2, vz, dv}, st);
+                                  bk::EpiSt{U2, vz, dv}, st, sk, skf);
         launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(hk), bk::cat1(bk::src(SAg + P1, 0, P, dh, 1, dv, dh)),
-                                  bk::EpiSt{U2s, vz, dv}, st);
+                                  bk::EpiSt{U2s, vz, dv}, st, sk, skf);
       }
       hipLaunchKernelGGL(bk::row_kernel_gated, dim3(R, M), dim3(64), 0, st, Zk, gzz, Pz, hz, D1, U1, U1s, gz, Za, E,
                          U2, U2s, vz, dh, dv, rld, rW, rS, cWa, cSa);
@@ -1299,14 +1303,14 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
         const bk::EpiEa ep = win ? bk::EpiEa{U2, vz, dV, T * dv, dv, s - (c - 1), 1}
                                  : bk::EpiEa{U2, vz, dV + s * dv, T * dv, dv, 0, 0};
         launch_gemm<false, false>(true, R, dv, dh, M, bk::cat1(bk::src(U1s, 0, gz, dzz, 1, R, dh)),
-                                  bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh)), ep, st);
+                                  bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh)), ep, st, sk, skf);
       }
       {  // W2' = E^T b' + (2E')^T H + dY^T Hq
         bk::Cat la = bk::cat3(bk::src(E, 0, vz, 1, dv, dv, R), bk::src(U2, 0, vz, 1, dv, dv, R, 0, nullptr, 0, 2.0f),
                               bk::src(dY + s * dv, 0, T * dv, 1, dv, dv, C), R, 2 * R);
         bk::Cat lb = bk::cat3(bk::src(U1s, 0, gz, 1, dzz, dh, R), bk::gated(Zk, gzz, 1, dzz, dh, R, dh),
                               bk::gated(Zk + (int64_t)R * dzz, gzz, 1, dzz, dh, C, dh), R, 2 * R);
-        launch_gemm<false, false>(true, dv, dh, 2 * R + C, M, la, lb, bk::EpiSt{Wb + P1, P, dh}, st);
+        launch_gemm<false, false>(true, dv, dh, 2 * R + C, M, la, lb, bk::EpiSt{Wb + P1, P, dh}, st, sk, skf);
       }
       // H' = -(cW E) WA2 - (cS E) SA2 + (2E') W2, scattered into Za through the gate
       launch_gemm<false, false>(
@@ -1315,7 +1319,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
                    bk::src(U2, 0, vz, dv, 1, R, dv, 0, nullptr, 0, 2.0f), dv, 2 * dv),
           bk::cat3(bk::src(WAg + P1, 0, P, 1, dh, dh, dv), bk::src(SAg + P1, 0, P, 1, dh, dh, dv),
                    bk::src(cW2, 0, 2 * P, 1, dh, dh, dv), dv, 2 * dv),
-          bk::EpiZag{Za, Zk, gz, gzz, dh}, st);
+          bk::EpiZag{Za, Zk, gz, gzz, dh}, st, sk, skf);
       {  // X' = -(cW D) WAz - (cS D) SAz + Za Wz
         const bk::EpiStAdd out = feat ? bk::EpiStAdd{ws + L.xg, (int64_t)R * din, din, nullptr, 0, 0, 0.0f, 0, 0}
                                  : win ? bk::EpiStAdd{dK, T * din, din, nullptr, 0, 0, 0.0f, s - (c - 1), 1}
@@ -1327,22 +1331,22 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
                      2 * dzz),
             bk::cat3(bk::src(WAg, 0, P, 1, din, din, dzz), bk::src(SAg, 0, P, 1, din, din, dzz),
                      bk::src(cW1, 0, 2 * P, 1, din, din, dzz), dzz, 2 * dzz),
-            out, st);
+            out, st, sk, skf);
       }
       {  // Zq' through the gate, Q' = Zq' Wz
         launch_gemm<false, false>(true, C, dh, dv, M, bk::cat1(bk::src(dY + s * dv, 0, T * dv, dv, 1, C, dv)),
                                   bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv)),
-                                  bk::EpiScaleSpG{Zqa, Zk, gz, gzz, R, dh}, st);
+                                  bk::EpiScaleSpG{Zqa, Zk, gz, gzz, R, dh}, st, sk, skf);
         launch_gemm<false, false>(true, C, din, dzz, M, bk::cat1(bk::src(Zqa, 0, gz, dzz, 1, C, dzz)),
                                   bk::cat1(bk::src(cW1, 0, 2 * P, 1, din, din, dzz)),
                                   feat ? bk::EpiStAdd{ws + L.qg, (int64_t)C * din, din, nullptr, 0, 0, 0.0f, 0, 0}
                                        : bk::EpiStAdd{dQ + s * din, T * din, din, nullptr, 0, 0, 0.0f, 0, 0},
-                                  st);
+                                  st, sk, skf);
       }
       {  // Wz' = Za^T X + Zq'^T Q -> Wb
         bk::Cat la = bk::cat2(bk::src(Za, 0, gz, 1, dzz, dzz, R), bk::src(Zqa, 0, gz, 1, dzz, dzz, C), R);
         bk::Cat lb = bk::cat2(bk::src(Kr, kbf, kz, 1, din, din, R), bk::src(Qr, qbf, qz, 1, din, din, C), R);
-        launch_gemm<false, false>(true, dzz, din, R + C, M, la, lb, bk::EpiSt{Wb, P, din}, st);
+        launch_gemm<false, false>(true, dzz, din, R + C, M, la, lb, bk::EpiSt{Wb, P, din}, st, sk, skf);
       }
       AM_LAUNCH_CHECK();
       if (feat) {
@@ -1358,21 +1362,21 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat lk = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
       bk::Cat lq = bk::cat1(bk::src(Qr, qbf, qz, din, 1, C, din));
       bk::Cat lb = bk::cat1(bk::src(cW1, 0, 2 * P, din, 1, dh, din));
-      launch_gemm<false, false>(true, R, dh, din, M, lk, lb, bk::EpiSt{Zk, zz, dh}, st);
-      launch_gemm<false, false>(true, C, dh, din, M, lq, lb, bk::EpiSt{Zk + (int64_t)R * dh, zz, dh}, st);
+      launch_gemm<false, false>(true, R, dh, din, M, lk, lb, bk::EpiSt{Zk, zz, dh}, st, sk, skf);
+      launch_gemm<false, false>(true, C, dh, din, M, lq, lb, bk::EpiSt{Zk + (int64_t)R * dh, zz, dh}, st, sk, skf);
     }
     // E = 2 (H W2^T - V)
     {
       bk::Cat la = bk::cat1(bk::src(Zk, 0, zz, dh, 1, R, dh, 1));
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh));
       launch_gemm<false, false>(true, R, dv, dh, M, la, lb,
-                                bk::EpiE{E, vz, Vr, vbf, vrz, dv, d.residual ? Kr : nullptr, kbf, kz}, st);
+                                bk::EpiE{E, vz, Vr, vbf, vrz, dv, d.residual ? Kr : nullptr, kbf, kz}, st, sk, skf);
     }
     // P = E W2, D1 = P silu'(Z)
     {
       bk::Cat la = bk::cat1(bk::src(E, 0, vz, dv, 1, R, dv));
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv));  // B(k=v, j=h) = W2[v][h]
-      launch_gemm<false, false>(true, R, dh, dv, M, la, lb, bk::EpiPD1{Pz, D1, Zk, hz, zz, dh}, st);
+      launch_gemm<false, false>(true, R, dh, dv, M, la, lb, bk::EpiPD1{Pz, D1, Zk, hz, zz, dh}, st, sk, skf);
     }
     // Per-chunk gates: G = (D1^T X, E^T H), N = NS(G) or G, S_end = eta S - theta N,
     // W_end = (1 - alpha) W + S_end.  The adjoint of every row's gradient is G' (from N' = -theta
@@ -1383,9 +1387,9 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     if (per_chunk) {
       float *Gb = ws + L.gb, *Nb = ws + L.nb, *NAb = ws + L.nab, *GAb = ws + L.gab, *SAt = ws + L.sat;
       launch_gemm<false, false>(true, dh, din, C, M, bk::cat1(bk::src(D1, 0, hz, 1, dh, dh, C)),
-                                bk::cat1(bk::src(Kc, bf, inz, 1, din, din, C)), bk::EpiSt{Gb, P, din}, st);
+                                bk::cat1(bk::src(Kc, bf, inz, 1, din, din, C)), bk::EpiSt{Gb, P, din}, st, sk, skf);
       launch_gemm<false, false>(true, dv, dh, C, M, bk::cat1(bk::src(E, 0, vz, 1, dv, dv, C)),
-                                bk::cat1(bk::src(Zk, 0, zz, 1, dh, dh, C, 1)), bk::EpiSt{Gb + P1, P, dh}, st);
+                                bk::cat1(bk::src(Zk, 0, zz, 1, dh, dh, C, 1)), bk::EpiSt{Gb + P1, P, dh}, st, sk, skf);
       AM_LAUNCH_CHECK();
       const float* N = Gb;
       if (d.ns_steps > 0) {
@@ -1414,15 +1418,15 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat lx = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
       bk::Cat lh = bk::cat1(bk::src(Zk, 0, zz, dh, 1, R, dh, 1));
       launch_gemm<false, false>(true, R, dh, din, M, lx, bk::cat1(bk::src(WAg, 0, P, din, 1, dh, din)),
-                                bk::EpiSt{U1, hz, dh}, st);
+                                bk::EpiSt{U1, hz, dh}, st, sk, skf);
       if (!per_chunk)
         launch_gemm<false, false>(true, R, dh, din, M, lx, bk::cat1(bk::src(SAg, 0, P, din, 1, dh, din)),
-                                  bk::EpiSt{U1s, hz, dh}, st);
+                                  bk::EpiSt{U1s, hz, dh}, st, sk, skf);
       launch_gemm<false, false>(true, R, dv, dh, M, lh, bk::cat1(bk::src(WAg + P1, 0, P, dh, 1, dv, dh)),
-                                bk::EpiSt{U2, vz, dv}, st);
+                                bk::EpiSt{U2, vz, dv}, st, sk, skf);
       if (!per_chunk)
         launch_gemm<false, false>(true, R, dv, dh, M, lh, bk::cat1(bk::src(SAg + P1, 0, P, dh, 1, dv, dh)),
-                                  bk::EpiSt{U2s, vz, dv}, st);
+                                  bk::EpiSt{U2s, vz, dv}, st, sk, skf);
     }
     hipLaunchKernelGGL(bk::row_kernel, dim3(R, M), dim3(64), 0, st, Zk, zz, Pz, D1, U1, U1s, E, U2, U2s, hz, vz, dh,
                        dv, rld, rW, rS, cWa, cSa, per_chunk ? 0 : 1);
@@ -1433,7 +1437,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, dh, 1, dv, dh));  // B(k=h, j=v) = W2[v][h]
       const bk::EpiEa ep = win ? bk::EpiEa{U2, vz, dV, T * dv, dv, s - (c - 1), 1}
                                : bk::EpiEa{U2, vz, dV + s * dv, T * dv, dv, 0, 0};
-      launch_gemm<false, false>(true, R, dv, dh, M, la, lb, ep, st);
+      launch_gemm<false, false>(true, R, dv, dh, M, la, lb, ep, st, sk, skf);
     }
     // W2' = E^T P' + (2E')^T H + dY^T Hq  -> Wb + P1   (A(i=v, k=row), B(k=row, j=h))
     {
@@ -1441,7 +1445,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
                             bk::src(dY + s * dv, 0, T * dv, 1, dv, dv, C), R, 2 * R);
       bk::Cat lb = bk::cat3(bk::src(U1s, 0, hz, 1, dh, dh, R), bk::src(Zk, 0, zz, 1, dh, dh, R, 1),
                             bk::src(Zk + (int64_t)R * dh, 0, zz, 1, dh, dh, C, 1), R, 2 * R);
-      launch_gemm<false, false>(true, dv, dh, 2 * R + C, M, la, lb, bk::EpiSt{Wb + P1, P, dh}, st);
+      launch_gemm<false, false>(true, dv, dh, 2 * R + C, M, la, lb, bk::EpiSt{Wb + P1, P, dh}, st, sk, skf);
     }
     // H' = -(cW E) WA2 - (cS E) SA2 + (2E') W2;  Z' = Z'_1 + H' silu'(Z)  (in Pz)
     {
@@ -1451,12 +1455,12 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       const bk::Src w2 = bk::src(cW2, 0, 2 * P, 1, dh, dh, dv);
       if (per_chunk) {
         launch_gemm<false, false>(true, R, dh, 2 * dv, M, bk::cat2(ea, e2, dv), bk::cat2(wa, w2, dv),
-                                  bk::EpiZa{Pz, Zk, hz, zz, dh}, st);
+                                  bk::EpiZa{Pz, Zk, hz, zz, dh}, st, sk, skf);
       } else {
         launch_gemm<false, false>(true, R, dh, 3 * dv, M,
                                   bk::cat3(ea, bk::src(E, 0, vz, dv, 1, R, dv, 2, rS, rld, -1.0f), e2, dv, 2 * dv),
                                   bk::cat3(wa, bk::src(SAg + P1, 0, P, 1, dh, dh, dv), w2, dv, 2 * dv),
-                                  bk::EpiZa{Pz, Zk, hz, zz, dh}, st);
+                                  bk::EpiZa{Pz, Zk, hz, zz, dh}, st, sk, skf);
       }
     }
     // X' = -(cW D1) WA1 - (cS D1) SA1 + Z' W1 -> dK rows
@@ -1474,18 +1478,18 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
                                      : bk::EpiStAdd{dK + s * din, T * din, din, d.residual ? U2 : nullptr, vz, dv,
                                                     2.0f, 0, 0};
       if (per_chunk) {
-        launch_gemm<false, false>(true, R, din, 2 * dh, M, bk::cat2(da, za, dh), bk::cat2(wa, w1, dh), out, st);
+        launch_gemm<false, false>(true, R, din, 2 * dh, M, bk::cat2(da, za, dh), bk::cat2(wa, w1, dh), out, st, sk, skf);
       } else {
         launch_gemm<false, false>(true, R, din, 3 * dh, M,
                                   bk::cat3(da, bk::src(D1, 0, hz, dh, 1, R, dh, 2, rS, rld, -1.0f), za, dh, 2 * dh),
-                                  bk::cat3(wa, bk::src(SAg, 0, P, 1, din, din, dh), w1, dh, 2 * dh), out, st);
+                                  bk::cat3(wa, bk::src(SAg, 0, P, 1, din, din, dh), w1, dh, 2 * dh), out, st, sk, skf);
       }
     }
     // Zq' = (dY W2) silu'(Zq); Q' = Zq' W1 -> dQ rows
     {
       bk::Cat la = bk::cat1(bk::src(dY + s * dv, 0, T * dv, dv, 1, C, dv));
       bk::Cat lb = bk::cat1(bk::src(cW2, 0, 2 * P, 1, dh, dh, dv));
-      launch_gemm<false, false>(true, C, dh, dv, M, la, lb, bk::EpiScaleSp{Zqa, Zk, hz, zz, R, dh}, st);
+      launch_gemm<false, false>(true, C, dh, dv, M, la, lb, bk::EpiScaleSp{Zqa, Zk, hz, zz, R, dh}, st, sk, skf);
       bk::Cat la2 = bk::cat1(bk::src(Zqa, 0, hz, dh, 1, C, dh));
       bk::Cat lb2 = bk::cat1(bk::src(cW1, 0, 2 * P, 1, din, din, dh));
       // the residual memory's retrieval adds the query: + dY
@@ -1494,7 +1498,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
                                                     d.residual ? dY + s * dv : nullptr, T * dv, dv, 1.0f, 0, 0}
                                      : bk::EpiStAdd{dQ + s * din, T * din, din, d.residual ? dY + s * dv : nullptr,
                                                     T * dv, dv, 1.0f, 0, 0},
-                                st);
+                                st, sk, skf);
     }
     if (feat) {  // the raw rows' gradients through the feature map
       hipLaunchKernelGGL(bk::feat_jac_kernel, dim3(R, M), dim3(64), 0, st, ws + L.xg, ws + L.ks, R, d.dk, din, T,
@@ -1507,7 +1511,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
     {
       bk::Cat la = bk::cat2(bk::src(Pz, 0, hz, 1, dh, dh, R), bk::src(Zqa, 0, hz, 1, dh, dh, C), R);
       bk::Cat lb = bk::cat2(bk::src(Kr, kbf, kz, 1, din, din, R), bk::src(Qr, qbf, qz, 1, din, din, C), R);
-      launch_gemm<false, false>(true, dh, din, R + C, M, la, lb, bk::EpiSt{Wb, P, din}, st);
+      launch_gemm<false, false>(true, dh, din, R + C, M, la, lb, bk::EpiSt{Wb, P, din}, st, sk, skf);
     }
     }  // MLP memory
     AM_LAUNCH_CHECK();
