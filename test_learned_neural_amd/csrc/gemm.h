@@ -198,13 +198,13 @@ __global__ void splitk_reduce_kernel(int M, int N, int batch, int nsplit, const 
   else ep(z, row, col, v);
 }
 
-// Slices for a product of `tiles` output tiles and nk k-steps: enough workgroups to spread over
-// the chip (about four per CU), at least two k-steps per slice, and partials that fit the
+// Slices for a product of `tiles` output tiles and nk >= 4 k-steps: enough workgroups to spread
+// over the chip (about four per CU), at least two k-steps per slice, and partials that fit the
 // scratch.
 inline int splitk_slices(int M, int N, int K, int batch, int64_t scratch_floats) {
   const int64_t tiles = (int64_t)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * batch;
   const int nk = (K + GK - 1) / GK;
-  if (scratch_floats <= 0 || tiles >= 256 || nk < 8) return 1;
+  if (scratch_floats <= 0 || tiles >= 256 || nk < 4) return 1;
   int ns = (int)((1024 + tiles - 1) / tiles);
   if (ns > nk / 2) ns = nk / 2;
   while (ns > 1 && (int64_t)ns * batch * M * N > scratch_floats) --ns;

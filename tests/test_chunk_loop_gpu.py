@@ -2,9 +2,10 @@
 the same update run as one launch per product and chunk, through the C ABI, and both against the
 fp64 oracle.
 
-Both paths run the same tile loaders and epilogues, so they agree to rounding (the compiler may
-contract a multiply-add differently in the two kernels); the check is a 1e-5 max relative
-difference per tensor, far inside the 2e-2 bar both must meet against the oracle.  Cases cover
+Both paths compute the same products and epilogues, but the per-product launches split long-k
+products into k-slices summed in another order, so the two agree to rounding: the check is a
+1e-4 max relative difference per tensor (one bf16 ulp, 2^-8, for a bf16 output, where a rounding
+difference can flip the last bit), far inside the 2e-2 bar both must meet against the oracle.  Cases cover
 per-token gates (plain, residual and gated memories, Omega windows, degree-2 features, calls
 that cut chunks), per-chunk gates without Newton-Schulz, bf16 output and update-only calls.
 """
@@ -18,7 +19,8 @@ from test_learned_neural_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-AGREE = 1e-5
+AGREE = 1e-4
+AGREE_BF16_OUT = 2.0 ** -8
 
 CASES = [
     # (name, workload, variant, overrides, call boundaries or None, output dtype, with Y)
@@ -46,7 +48,8 @@ def test_chunk_loop_matches_per_product_launches(case):
     agree = {k: maxrel(a, b) for k, a, b in zip(("Y", "W", "S"), loop[:3], launches[:3]) if with_y or k != "Y"}
     bitwise = all(np.array_equal(a, b, equal_nan=True) for a, b in zip(loop[:3], launches[:3]))
     log(f"AGREE {name}: " + " ".join(f"{k}={v:.2e}" for k, v in agree.items()) + f" bitwise={bitwise}")
-    assert all(v <= AGREE for v in agree.values()), agree
+    bars = {k: (AGREE_BF16_OUT if (k == "Y" and od == am.BF16) else AGREE) for k in agree}
+    assert all(agree[k] <= bars[k] for k in agree), agree
     ref = oracle_run(inp)
     errs = compare(f"chunk_loop_{name}", inp.spec, loop, ref, BF16_TOL, check_state=True)
     if not with_y:
