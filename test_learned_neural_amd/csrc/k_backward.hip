@@ -481,7 +481,21 @@ __global__ void scalar_adj_kernel(const float* __restrict__ WA, const float* __r
   const float* wa = WA + (int64_t)z * P;
   const float* sa = SA + (int64_t)z * P;
   float b = 0.0f, a = 0.0f, p = 0.0f;
-  for (int64_t i = threadIdx.x; i < P; i += blockDim.x) {
+  int64_t i0 = 0;
+  if (((P & 3) == 0) && ((((uintptr_t)w) | ((uintptr_t)wa) | ((uintptr_t)sa)) & 15) == 0) {
+    // 16-byte loads, four per array in flight per thread
+    const int64_t n4 = P / 4;
+#pragma unroll 4
+    for (int64_t q = threadIdx.x; q < n4; q += blockDim.x) {
+      const float4 x = ((const float4*)w)[q], y = ((const float4*)s)[q];
+      const float4 u = ((const float4*)wa)[q], v = ((const float4*)sa)[q];
+      b += u.x * x.x + u.y * x.y + u.z * x.z + u.w * x.w;
+      a += u.x * y.x + u.y * y.y + u.z * y.z + u.w * y.w;
+      p += v.x * y.x + v.y * y.y + v.z * y.z + v.w * y.w;
+    }
+    i0 = P;
+  }
+  for (int64_t i = i0 + threadIdx.x; i < P; i += blockDim.x) {
     b += wa[i] * w[i];
     a += wa[i] * s[i];
     p += sa[i] * s[i];
@@ -515,49 +529,71 @@ __global__ void gate_bwd_kernel(const float* __restrict__ theta, const float* __
                                 const float* __restrict__ cWa, const float* __restrict__ cSa,
                                 const float* __restrict__ sca, float* __restrict__ dth, float* __restrict__ det,
                                 float* __restrict__ dal) {
-  extern __shared__ float gb[];  // e, b, w, ea, wa, ba [C] each
+  // e, b, w, ea, wa, ba, then the chunk's gates th, et, al, the coefficient adjoints cw, cs and
+  // the outputs oth, oet, oal [C] each in LDS: the block loads and stores them in parallel, and
+  // thread 0 runs the recurrences without a global access
+  extern __shared__ float gb[];
   const int z = blockIdx.x;
-  if (threadIdx.x != 0) return;
   float* e = gb;
   float* b = gb + C;
   float* w = gb + 2 * C;
   float* ea = gb + 3 * C;
   float* wa = gb + 4 * C;
   float* ba = gb + 5 * C;
-  const float* th = theta + (int64_t)z * ld + s0;
-  const float* et = eta + (int64_t)z * ld + s0;
-  const float* al = alpha + (int64_t)z * ld + s0;
-  float* oth = dth + (int64_t)z * ld + s0;
-  float* oet = det + (int64_t)z * ld + s0;
-  float* oal = dal + (int64_t)z * ld + s0;
-  e[C - 1] = b[C - 1] = w[C - 1] = 1.0f;
-  for (int r = C - 2; r >= 0; --r) {
-    e[r] = et[r + 1] * e[r + 1];
-    b[r] = (1.0f - al[r + 1]) * b[r + 1];
-    w[r] = b[r] + et[r + 1] * w[r + 1];
+  float* th = gb + 6 * C;
+  float* et = gb + 7 * C;
+  float* al = gb + 8 * C;
+  float* cwv = gb + 9 * C;
+  float* csv = gb + 10 * C;
+  float* oth = gb + 11 * C;
+  float* oet = gb + 12 * C;
+  float* oal = gb + 13 * C;
+  for (int r = threadIdx.x; r < C; r += blockDim.x) {
+    const int64_t o = (int64_t)z * ld + s0 + r;
+    th[r] = theta[o];
+    et[r] = eta[o];
+    al[r] = alpha[o];
+    cwv[r] = cWa[(int64_t)z * C + r];
+    csv[r] = cSa[(int64_t)z * C + r];
   }
-  const float PCa = sca[z * 3 + 0], betaa = sca[z * 3 + 1], aSa = sca[z * 3 + 2];
-  for (int r = 0; r < C; ++r) {
-    const float cw = cWa[(int64_t)z * C + r], cs = cSa[(int64_t)z * C + r];
-    oth[r] = cs * e[r] + cw * w[r];
-    ea[r] = cs * th[r];
-    wa[r] = cw * th[r];
-    ba[r] = 0.0f;
-    oet[r] = 0.0f;
-    oal[r] = 0.0f;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    e[C - 1] = b[C - 1] = w[C - 1] = 1.0f;
+    for (int r = C - 2; r >= 0; --r) {
+      e[r] = et[r + 1] * e[r + 1];
+      b[r] = (1.0f - al[r + 1]) * b[r + 1];
+      w[r] = b[r] + et[r + 1] * w[r + 1];
+    }
+    const float PCa = sca[z * 3 + 0], betaa = sca[z * 3 + 1], aSa = sca[z * 3 + 2];
+    for (int r = 0; r < C; ++r) {
+      const float cw = cwv[r], cs = csv[r];
+      oth[r] = cs * e[r] + cw * w[r];
+      ea[r] = cs * th[r];
+      wa[r] = cw * th[r];
+      ba[r] = 0.0f;
+      oet[r] = 0.0f;
+      oal[r] = 0.0f;
+    }
+    oet[0] += PCa * e[0] + aSa * w[0];
+    ea[0] += PCa * et[0];
+    wa[0] += aSa * et[0];
+    oal[0] += -betaa * b[0];
+    ba[0] += betaa * (1.0f - al[0]);
+    for (int r = 0; r + 1 < C; ++r) {
+      ba[r] += wa[r];
+      oet[r + 1] += wa[r] * w[r + 1] + ea[r] * e[r + 1];
+      wa[r + 1] += wa[r] * et[r + 1];
+      ea[r + 1] += ea[r] * et[r + 1];
+      oal[r + 1] += -ba[r] * b[r + 1];
+      ba[r + 1] += ba[r] * (1.0f - al[r + 1]);
+    }
   }
-  oet[0] += PCa * e[0] + aSa * w[0];
-  ea[0] += PCa * et[0];
-  wa[0] += aSa * et[0];
-  oal[0] += -betaa * b[0];
-  ba[0] += betaa * (1.0f - al[0]);
-  for (int r = 0; r + 1 < C; ++r) {
-    ba[r] += wa[r];
-    oet[r + 1] += wa[r] * w[r + 1] + ea[r] * e[r + 1];
-    wa[r + 1] += wa[r] * et[r + 1];
-    ea[r + 1] += ea[r] * et[r + 1];
-    oal[r + 1] += -ba[r] * b[r + 1];
-    ba[r + 1] += ba[r] * (1.0f - al[r + 1]);
+  __syncthreads();
+  for (int r = threadIdx.x; r < C; r += blockDim.x) {
+    const int64_t o = (int64_t)z * ld + s0 + r;
+    dth[o] = oth[r];
+    det[o] = oet[r];
+    dal[o] = oal[r];
   }
 }
 
@@ -1532,7 +1568,7 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
         cWt = ws + L.cwt;
         cSt = ws + L.cst;
       }
-      hipLaunchKernelGGL(bk::gate_bwd_kernel, dim3(M), dim3(64), (size_t)6 * C * sizeof(float), st, theta, eta,
+      hipLaunchKernelGGL(bk::gate_bwd_kernel, dim3(M), dim3(64), (size_t)14 * C * sizeof(float), st, theta, eta,
                          alpha, T, s, C, cWt, cSt, sca, dth, det, dal);
       AM_LAUNCH_CHECK();
       hipLaunchKernelGGL(bk::state_adj_kernel, dim3(blocks_of(n)), dim3(256), 0, st, WA, SA, Wb, sc, P, M, WAn, SAn);
