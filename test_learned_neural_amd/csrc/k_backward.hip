@@ -529,9 +529,9 @@ __global__ void gate_bwd_kernel(const float* __restrict__ theta, const float* __
                                 const float* __restrict__ cWa, const float* __restrict__ cSa,
                                 const float* __restrict__ sca, float* __restrict__ dth, float* __restrict__ det,
                                 float* __restrict__ dal) {
-  // e, b, w, ea, wa, ba, then the chunk's gates th, et, al, the coefficient adjoints cw, cs and
-  // the outputs oth, oet, oal [C] each in LDS: the block loads and stores them in parallel, and
-  // thread 0 runs the recurrences without a global access
+  // e, b, w, ea, wa, (unused), then the chunk's gates th, et, al, the coefficient adjoints cw, cs
+  // and the outputs oth, oet, oal [C] each in LDS: the block loads and stores them in parallel,
+  // and thread 0 runs the recurrences without a global access
   extern __shared__ float gb[];
   const int z = blockIdx.x;
   float* e = gb;
@@ -558,34 +558,43 @@ __global__ void gate_bwd_kernel(const float* __restrict__ theta, const float* __
   }
   __syncthreads();
   if (threadIdx.x == 0) {
+    // the recurrences carry their running values in registers; the loads they need do not
+    // depend on the chain
+    float ec = 1.0f, bc = 1.0f, wc = 1.0f;
     e[C - 1] = b[C - 1] = w[C - 1] = 1.0f;
+#pragma unroll 4
     for (int r = C - 2; r >= 0; --r) {
-      e[r] = et[r + 1] * e[r + 1];
-      b[r] = (1.0f - al[r + 1]) * b[r + 1];
-      w[r] = b[r] + et[r + 1] * w[r + 1];
+      const float etn = et[r + 1], aln = al[r + 1];
+      ec = etn * ec;
+      bc = (1.0f - aln) * bc;
+      wc = bc + etn * wc;
+      e[r] = ec;
+      b[r] = bc;
+      w[r] = wc;
     }
     const float PCa = sca[z * 3 + 0], betaa = sca[z * 3 + 1], aSa = sca[z * 3 + 2];
+#pragma unroll 4
     for (int r = 0; r < C; ++r) {
       const float cw = cwv[r], cs = csv[r];
       oth[r] = cs * e[r] + cw * w[r];
       ea[r] = cs * th[r];
       wa[r] = cw * th[r];
-      ba[r] = 0.0f;
-      oet[r] = 0.0f;
-      oal[r] = 0.0f;
     }
-    oet[0] += PCa * e[0] + aSa * w[0];
-    ea[0] += PCa * et[0];
-    wa[0] += aSa * et[0];
-    oal[0] += -betaa * b[0];
-    ba[0] += betaa * (1.0f - al[0]);
+    oet[0] = PCa * e[0] + aSa * w[0];
+    float ea_c = ea[0] + PCa * et[0];
+    float wa_c = wa[0] + aSa * et[0];
+    oal[0] = -betaa * b[0];
+    float ba_c = betaa * (1.0f - al[0]);
+#pragma unroll 4
     for (int r = 0; r + 1 < C; ++r) {
-      ba[r] += wa[r];
-      oet[r + 1] += wa[r] * w[r + 1] + ea[r] * e[r + 1];
-      wa[r + 1] += wa[r] * et[r + 1];
-      ea[r + 1] += ea[r] * et[r + 1];
-      oal[r + 1] += -ba[r] * b[r + 1];
-      ba[r + 1] += ba[r] * (1.0f - al[r + 1]);
+      const float w1 = w[r + 1], e1 = e[r + 1], et1 = et[r + 1], b1 = b[r + 1], al1 = al[r + 1];
+      const float wan = wa[r + 1], ean = ea[r + 1];
+      ba_c += wa_c;
+      oet[r + 1] = wa_c * w1 + ea_c * e1;
+      wa_c = wan + wa_c * et1;
+      ea_c = ean + ea_c * et1;
+      oal[r + 1] = -ba_c * b1;
+      ba_c = ba_c * (1.0f - al1);
     }
   }
   __syncthreads();
