@@ -177,6 +177,16 @@ struct NsUpdate {
 atlasmem_status launch_ns(const float* G, int64_t ldG_mat, int n_mat, int rows, int cols, int steps, float a, float b,
                           float c, float eps, bool split, float* out, const NsUpdate* upd, hipStream_t st);
 bool ns_supported(int rows, int cols);
+// Several matrices of each memory in one launch (up to three groups of n_mat matrices, memory m's
+// matrix of group i at G + goff_i + m ldG_mat, rows_i x cols_i), each followed by the momentum /
+// forgetting epilogue at state offset uoff_i (upd.off is not used).
+struct NsGroup {
+  int rows, cols;
+  int64_t goff, uoff;
+};
+atlasmem_status launch_ns_groups(const float* G, int64_t ldG_mat, int n_mat, int ngroups, const NsGroup* grp, int steps,
+                                 float a, float b, float c, float eps, bool split, const NsUpdate& upd,
+                                 hipStream_t st);
 bool fused_supported(const Dims& d);
 atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
                              const float* theta, const float* eta, const float* alpha, const Span& sp, void* Y,

@@ -917,20 +917,15 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
           EpiStore ep{h->G, d.P, din, 1};
           gemm_any(split, false, feat_exact, dz, din, Rk, M, la, lb, ep, st, h);
         }
-        // each weight matrix separately: W1, (W3,) W2
-        NsUpdate u1{Win, Sin, Wout, Sout, d.P, 0, 1, theta, eta, alpha, sp.ldg, k, h->flag};
-        stt = launch_ns(h->G, d.P, M, dh, din, d.ns_steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, split, nullptr, &u1, st);
-        if (stt != ATLASMEM_OK) return stt;
-        if (d.gated) {
-          const int64_t o3 = (int64_t)dh * din;
-          NsUpdate u3{Win, Sin, Wout, Sout, d.P, o3, 1, theta, eta, alpha, sp.ldg, k, h->flag};
-          stt = launch_ns(h->G + o3, d.P, M, dh, din, d.ns_steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, split, nullptr,
-                          &u3, st);
-          if (stt != ATLASMEM_OK) return stt;
-        }
-        NsUpdate u2{Win, Sin, Wout, Sout, d.P, d.P1, 1, theta, eta, alpha, sp.ldg, k, h->flag};
-        stt = launch_ns(h->G + d.P1, d.P, M, dv, dh, d.ns_steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, split, nullptr,
-                        &u2, st);
+        // each weight matrix separately, W1, (W3,) W2, as groups of one launch
+        const int64_t o3 = (int64_t)dh * din;
+        NsGroup grp[3];
+        int ng = 0;
+        grp[ng++] = NsGroup{dh, din, 0, 0};
+        if (d.gated) grp[ng++] = NsGroup{dh, din, o3, o3};
+        grp[ng++] = NsGroup{dv, dh, d.P1, d.P1};
+        const NsUpdate u{Win, Sin, Wout, Sout, d.P, 0, 1, theta, eta, alpha, sp.ldg, k, h->flag};
+        stt = launch_ns_groups(h->G, d.P, M, ng, grp, d.ns_steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, split, u, st);
         if (stt != ATLASMEM_OK) return stt;
       }
       if (d.ptr && Y) {

@@ -38,6 +38,11 @@ struct NsArgs {
   float* out;
   NsUpdate u;
   int has_upd;
+  // groups of gsize matrices each (block b: group b / gsize, matrix b % gsize of it): shape, offset
+  // of the group's matrices in G and in the state (the update epilogue)
+  int gsize;
+  int grows[3], gcols[3];
+  int64_t goff[3], uoff[3];
 };
 
 template <bool SPLIT>
@@ -50,13 +55,14 @@ __global__ void __launch_bounds__(256) ns_kernel(NsArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t Bl[SPLIT ? NSM * LT : 8];
   __shared__ float red[4];
 
-  const int mat = blockIdx.x;
+  const int gi = blockIdx.x / p.gsize, mat = blockIdx.x - gi * p.gsize;
+  const int rows = p.grows[gi], cols = p.gcols[gi];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
-  const bool tr = p.rows > p.cols;
-  const int m = tr ? p.cols : p.rows;
-  const int n = tr ? p.rows : p.cols;
-  const float* g = p.G + (int64_t)mat * p.ldG;
+  const bool tr = rows > cols;
+  const int m = tr ? cols : rows;
+  const int n = tr ? rows : cols;
+  const float* g = p.G + p.goff[gi] + (int64_t)mat * p.ldG;
 
   // x[ri][cj][r]: X(i, j) with i = 16 ri + 4 lq + r, j = 32 w + 16 cj + lr
   float x[4][2][4];
@@ -69,7 +75,7 @@ __global__ void __launch_bounds__(256) ns_kernel(NsArgs p) {
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ri + 4 * lq + r, j = 32 * w + 16 * cj + lr;
         float v = 0.0f;
-        if (i < m && j < n) v = tr ? g[(int64_t)j * p.cols + i] : g[(int64_t)i * p.cols + j];
+        if (i < m && j < n) v = tr ? g[(int64_t)j * cols + i] : g[(int64_t)i * cols + j];
         x[ri][cj][r] = v;
         ss = fmaf(v, v, ss);
       }
@@ -232,11 +238,11 @@ __global__ void __launch_bounds__(256) ns_kernel(NsArgs p) {
           const int gr = tr ? j : i, gc = tr ? i : j;
           const float v = x[ri][cj][r];
           if (!p.has_upd) {
-            p.out[(int64_t)mat * p.rows * p.cols + (int64_t)gr * p.cols + gc] = v;
+            p.out[(int64_t)mat * rows * cols + (int64_t)gr * cols + gc] = v;
           } else {
             const NsUpdate& u = p.u;
             const int mem = mat / u.mats_per_mem;
-            const int64_t e = (int64_t)mem * u.P + u.off + (int64_t)gr * p.cols + gc;
+            const int64_t e = (int64_t)mem * u.P + p.uoff[gi] + (int64_t)gr * cols + gc;
             const int64_t gi = (int64_t)mem * u.ld_gate + u.k;
             const float s = u.eta[gi] * u.Sin[e] - u.theta[gi] * v;
             const float wv = (1.0f - u.alpha[gi]) * u.Win[e] + s;
@@ -272,8 +278,48 @@ atlasmem_status launch_ns(const float* G, int64_t ldG_mat, int n_mat, int rows, 
   p.has_upd = upd != nullptr;
   if (upd) p.u = *upd;
   else p.u = NsUpdate{};
+  p.gsize = n_mat;
+  p.grows[0] = rows;
+  p.gcols[0] = cols;
+  p.goff[0] = 0;
+  p.uoff[0] = upd ? upd->off : 0;
   if (split) hipLaunchKernelGGL(ns_kernel<true>, dim3(n_mat), dim3(256), 0, st, p);
   else hipLaunchKernelGGL(ns_kernel<false>, dim3(n_mat), dim3(256), 0, st, p);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
+atlasmem_status launch_ns_groups(const float* G, int64_t ldG_mat, int n_mat, int ngroups, const NsGroup* grp, int steps,
+                                 float a, float b, float c, float eps, bool split, const NsUpdate& upd,
+                                 hipStream_t st) {
+  if (ngroups < 1 || ngroups > 3) return ATLASMEM_E_INVALID;
+  for (int i = 0; i < ngroups; ++i)
+    if (!ns_supported(grp[i].rows, grp[i].cols)) return ATLASMEM_E_UNSUPPORTED;
+  if (n_mat == 0) return ATLASMEM_OK;
+  NsArgs p;
+  p.G = G;
+  p.ldG = ldG_mat;
+  p.rows = grp[0].rows;
+  p.cols = grp[0].cols;
+  p.steps = steps;
+  p.a = a;
+  p.b = b;
+  p.c = c;
+  p.eps = eps;
+  p.out = nullptr;
+  p.has_upd = 1;
+  p.u = upd;
+  p.gsize = n_mat;
+  for (int i = 0; i < 3; ++i) {
+    const NsGroup& q = grp[i < ngroups ? i : 0];
+    p.grows[i] = q.rows;
+    p.gcols[i] = q.cols;
+    p.goff[i] = q.goff;
+    p.uoff[i] = q.uoff;
+  }
+  const dim3 grid((unsigned)((int64_t)n_mat * ngroups));
+  if (split) hipLaunchKernelGGL(ns_kernel<true>, grid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL(ns_kernel<false>, grid, dim3(256), 0, st, p);
   AM_LAUNCH_CHECK();
   return ATLASMEM_OK;
 }
