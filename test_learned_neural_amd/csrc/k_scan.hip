@@ -128,7 +128,77 @@ atlasmem_status launch_omega(const float* cW, const float* cS, int64_t ld_c, con
 // With the Omega window G_l = sum_{i=l-c+1..l} gamma_i g_i (ATLAS summary, section 3.2), so g_i
 // enters W_t with Om_{t,i} = gamma_i sum_{l in [max(i, s), min(i + c - 1, t)]} w_{t,l} theta_l.
 // One block per memory walks the chunk's tokens in order; w and E live in LDS, one column per l.
+// Om[t][r] = gamma_r * sum over the tokens l of key row r's window (l <= t) of theta_l w_{t,l}, with
+// w_{l,l} = E_{l,l} = 1 and, for t > l, E_{t,l} = eta_t E_{t-1,l}, w_{t,l} = (1 - alpha_t) w_{t-1,l}
+// + E_{t,l}: each (t, l) sequence is its own scalar recurrence in t, so thread r carries the
+// w and E of its window's (at most PTR_MAXC) tokens in registers through the chunk, with no
+// barrier per token.  beta_t and a_t follow from the gates alone (thread 0).
+constexpr int PTR_MAXC = 8;
 __global__ void ptr_coeff_kernel(const float* __restrict__ theta, const float* __restrict__ eta,
+                                 const float* __restrict__ alpha, const float* __restrict__ gamma, int64_t ld,
+                                 const float* __restrict__ ghist, int64_t s0, int C, int c, float* __restrict__ bA,
+                                 float* __restrict__ Om) {
+  extern __shared__ float pc[];  // the chunk's gates th, et, al [C]
+  float* th = pc;
+  float* et = pc + C;
+  float* al = pc + 2 * C;
+  const int m = blockIdx.x;
+  const int Rk = C + c - 1;
+  for (int l = threadIdx.x; l < C; l += blockDim.x) {
+    const int64_t o = (int64_t)m * ld + s0 + l;
+    th[l] = theta[o];
+    et[l] = eta[o];
+    al[l] = alpha[o];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float beta = 1.0f, a = 0.0f, P = 1.0f;
+    for (int t = 0; t < C; ++t) {
+      const float om = 1.0f - al[t], e = et[t];
+      P *= e;
+      a = om * a + P;
+      beta *= om;
+      bA[((int64_t)m * C + t) * 2] = beta;
+      bA[((int64_t)m * C + t) * 2 + 1] = a;
+    }
+  }
+  for (int r = threadIdx.x; r < Rk; r += blockDim.x) {
+    const int i = r - (c - 1);  // chunk-relative token of key row r (negative: window history)
+    float g = 1.0f;
+    if (c > 1) {  // gamma of token s0 + i of the call, or of the history before the call
+      const int64_t tau = s0 + i;
+      g = (tau >= 0) ? gamma[(int64_t)m * ld + tau] : ghist[(int64_t)m * (c - 1) + (c - 1) + tau];
+    }
+    const int lo = i > 0 ? i : 0;             // first window token inside the chunk
+    const int hi = (i + c - 1) < C ? (i + c - 1) : C - 1;
+    float w[PTR_MAXC], E[PTR_MAXC];
+#pragma unroll
+    for (int q = 0; q < PTR_MAXC; ++q) w[q] = E[q] = 0.0f;
+    float* col = Om + (int64_t)m * C * Rk + r;
+    for (int t = 0; t < C; ++t) {
+      const float om = 1.0f - al[t], e = et[t];
+      float v = 0.0f;
+#pragma unroll
+      for (int q = 0; q < PTR_MAXC; ++q) {
+        const int l = lo + q;
+        if (l > hi) break;
+        if (l < t) {
+          E[q] = e * E[q];
+          w[q] = om * w[q] + E[q];
+        } else if (l == t) {
+          E[q] = 1.0f;
+          w[q] = 1.0f;
+        }
+        if (l <= t) v += th[l] * w[q];
+      }
+      col[(int64_t)t * Rk] = (i <= t) ? ((c > 1) ? v * g : v) : 0.0f;
+    }
+  }
+}
+
+// Windows wider than PTR_MAXC: the same coefficients token by token, the block walking the
+// chunk with two barriers per token.
+__global__ void ptr_coeff_seq_kernel(const float* __restrict__ theta, const float* __restrict__ eta,
                                  const float* __restrict__ alpha, const float* __restrict__ gamma, int64_t ld,
                                  const float* __restrict__ ghist, int64_t s0, int C, int c, float* __restrict__ bA,
                                  float* __restrict__ Om) {
@@ -203,13 +273,15 @@ atlasmem_status launch_ptr_coeffs(const float* theta, const float* eta, const fl
                                   int64_t ld, const float* ghist, int M, int64_t s0, int C, int c, float* bA,
                                   float* Om, hipStream_t st) {
   if (M == 0) return ATLASMEM_OK;
-  const size_t lds = ((size_t)6 * C + C + c - 1) * sizeof(float);
-  if (lds > 64 * 1024 &&
-      hipFuncSetAttribute((const void*)ptr_coeff_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-          hipSuccess)
-    return ATLASMEM_E_DEVICE;
-  hipLaunchKernelGGL(ptr_coeff_kernel, dim3(M), dim3(256), lds, st, theta, eta, alpha, gamma, ld, ghist, s0, C, c,
-                     bA, Om);
+  if (c > PTR_MAXC) {
+    const size_t lds = ((size_t)6 * C + C + c - 1) * sizeof(float);
+    hipLaunchKernelGGL(ptr_coeff_seq_kernel, dim3(M), dim3(256), lds, st, theta, eta, alpha, gamma, ld, ghist, s0, C,
+                       c, bA, Om);
+  } else {
+    const size_t lds = (size_t)3 * C * sizeof(float);
+    hipLaunchKernelGGL(ptr_coeff_kernel, dim3(M), dim3(256), lds, st, theta, eta, alpha, gamma, ld, ghist, s0, C, c,
+                       bA, Om);
+  }
   AM_LAUNCH_CHECK();
   return ATLASMEM_OK;
 }

@@ -155,6 +155,10 @@ PTR = [
     ("gated_window3", 3, "stabilised",
      dict(kind=G, batch=1, heads=2, T=96, d_key=16, poly_degree=1, d_value=20, d_hidden=36, chunk=48,
           omega_window=3, per_token_retrieve=True), None),
+    # a window wider than the coefficient kernel's register window (8): the token-by-token kernel
+    ("window10_wide", 3, "stabilised",
+     dict(batch=1, heads=2, T=96, d_key=16, poly_degree=1, d_value=16, d_hidden=32, chunk=32, omega_window=10,
+          per_token_retrieve=True), [0, 32, 96]),
 ]
 
 
