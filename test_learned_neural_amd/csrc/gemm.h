@@ -204,7 +204,7 @@ __global__ void splitk_reduce_kernel(int M, int N, int batch, int nsplit, const 
 inline int splitk_slices(int M, int N, int K, int batch, int64_t scratch_floats) {
   const int64_t tiles = (int64_t)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * batch;
   const int nk = (K + GK - 1) / GK;
-  if (scratch_floats <= 0 || tiles >= 256 || nk < 4) return 1;
+  if (scratch_floats <= 0 || tiles > 256 || nk < 4) return 1;
   int ns = (int)((1024 + tiles - 1) / tiles);
   if (ns > nk / 2) ns = nk / 2;
   while (ns > 1 && (int64_t)ns * batch * M * N > scratch_floats) --ns;
