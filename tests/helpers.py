@@ -123,3 +123,112 @@ def compare(name, spec, got, ref, tol, check_state=True):
 def oracle_run(inp, mems=None, T=None, processes=1):
     with np.errstate(all="ignore"):
         return oracle.run_inputs(inp, mems=mems, T=T, processes=processes)
+
+
+# ----------------------------------------------------------------------------- per-chunk parity
+#
+# The stabilised workloads' state shrinks geometrically (W = 0 attracts under the forgetting gate),
+# so a whole-tensor max|x - r| / max|r| is set by the first chunks and cannot see the late ones.
+# These checks scale every chunk of every memory by its own magnitude, down to FLOOR: a million
+# times fp32's smallest normal (1.2e-38), so that even the low halves of the split products
+# (2^-8 of the high ones) stay normal and the relative error still means something.
+
+FLOOR = 1e-32
+
+
+def per_chunk_y_errors(Yg, Yr, chunk, floor=FLOOR):
+    """Per memory and chunk k: max|Yg - Yr| / max|Yr| over the chunk's rows, for every chunk whose
+    reference magnitude is at least `floor`.  Yg, Yr: [m, T, d_v].  Returns (worst error, number of
+    chunks checked per memory, the last chunk checked per memory)."""
+    Yg = np.asarray(Yg, dtype=np.float64)
+    Yr = np.asarray(Yr, dtype=np.float64)
+    m, T = Yr.shape[:2]
+    worst, counts, last = 0.0, [], []
+    for i in range(m):
+        n, lk = 0, -1
+        for k, s in enumerate(range(0, T, chunk)):
+            r = Yr[i, s:s + chunk]
+            scale = float(np.max(np.abs(r)))
+            if not scale >= floor:
+                continue
+            g = Yg[i, s:s + chunk]
+            err = float(np.max(np.abs(g - r))) / scale if np.all(np.isfinite(g)) else float("inf")
+            worst = max(worst, err)
+            n += 1
+            lk = k
+        counts.append(n)
+        last.append(lk)
+    return worst, counts, last
+
+
+def oracle_boundaries(inp, mems, T=None):
+    """The oracle's Y and its (W, S) at every chunk boundary (flat [P] vectors) of each memory."""
+    cfg = oracle.config_from(inp.spec)
+    s = inp.spec
+    T = s.T if T is None else T
+    ng = T if s.gate_mode == synth.PER_TOKEN else -(-T // s.chunk)
+    out = []
+    with np.errstate(all="ignore"):
+        for m in mems:
+            r = oracle.run_memory(cfg, oracle.unflatten(cfg, inp.W0[m]), oracle.unflatten(cfg, inp.S0[m]),
+                                  inp.values("K", [m])[0, :T], inp.values("Q", [m])[0, :T],
+                                  inp.values("V", [m])[0, :T], inp.values("theta", [m])[0, :ng],
+                                  inp.values("eta", [m])[0, :ng], inp.values("alpha", [m])[0, :ng],
+                                  None if inp.gamma is None else inp.values("gamma", [m])[0, :T],
+                                  keep_boundaries=True)
+            bounds = [(oracle.flatten(w), oracle.flatten(sm)) for w, sm in r.boundary_states]
+            out.append((r.Y, bounds))
+    return out
+
+
+def boundary_state_errors(spec, got_states, ref_bounds, chunk_ids, floor=FLOOR):
+    """Relative error of every weight and momentum matrix at the given chunk boundaries, each matrix
+    scaled by its own reference magnitude, where that magnitude is at least `floor`.
+    got_states[j] = (W [P], S [P]) at boundary chunk_ids[j] of one memory; ref_bounds[k] = the
+    oracle's (W, S) at boundary k.  Returns (worst error, last boundary checked)."""
+    worst, last = 0.0, -1
+    for (Wg, Sg), k in zip(got_states, chunk_ids):
+        Wr, Sr = ref_bounds[k]
+        for a, b in list(zip(split_params(spec, Wg), split_params(spec, Wr))) + \
+                list(zip(split_params(spec, Sg), split_params(spec, Sr))):
+            scale = float(np.max(np.abs(b)))
+            if not scale >= floor:
+                continue
+            err = float(np.max(np.abs(np.asarray(a, dtype=np.float64) - b))) / scale
+            worst = max(worst, err if np.isfinite(err) else float("inf"))
+            last = max(last, k)
+    return worst, last
+
+
+def run_gpu_states(inp, mems, calls, chunks_per_call, precision=am.PREC_AUTO, flags=0):
+    """The library over the given memories only (their inputs sliced out, so the handle holds just
+    them), in `calls` update calls of `chunks_per_call` chunks each, with the state read after every
+    call.  Returns (Y [m, T, d_v], [(W [m, P], S [m, P]) after each call])."""
+    import dataclasses
+    import torch
+    s = inp.spec
+    sub = dataclasses.replace(inp, spec=dataclasses.replace(s, batch=1, heads=len(mems)),
+                              **{k: (None if getattr(inp, k) is None else getattr(inp, k)[np.asarray(mems)])
+                                 for k in ("K", "Q", "V", "theta", "eta", "alpha", "gamma", "W0", "S0")})
+    ss = sub.spec
+    cfg = config_for(ss, precision, am.F32, flags)
+    mem = am.Memory(cfg, to_dev(sub.W0), to_dev(sub.S0))
+    T = calls * chunks_per_call * ss.chunk
+    Y = torch.full((ss.n_mem, T, ss.d_value), float("nan"), dtype=torch.float32, device=DEV)
+    W = torch.empty((ss.n_mem, mem.P), dtype=torch.float32, device=DEV)
+    S = torch.empty_like(W)
+    states = []
+    step = chunks_per_call * ss.chunk
+    for j in range(calls):
+        a, b = j * step, (j + 1) * step
+        seg = segment(sub, a, b)
+        y = torch.empty((ss.n_mem, b - a, ss.d_value), dtype=torch.float32, device=DEV)
+        mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], seg["gamma"],
+                           b - a, y)
+        Y[:, a:b] = y
+        st = mem.get_state(W, S)
+        assert st == am.OK, st
+        states.append((W.cpu().numpy().astype(np.float64), S.cpu().numpy().astype(np.float64)))
+    torch.cuda.synchronize()
+    mem.close()
+    return y_to_np(Y), states

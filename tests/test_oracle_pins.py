@@ -383,22 +383,26 @@ def test_per_token_retrieve_against_bruteforce(case):
         oracle.run_memory(dataclasses.replace(cfg, gate_mode=PER_CHUNK), params, momenta, K, Q, V, th, et, al, ga)
 
 
-def coefficient_form(cfg, params, momenta, K, V, th, et, al, ga):
+def coefficient_form(cfg, params, momenta, K, V, th, et, al, ga, hist=None):
     """Chunk-wise closed form built on oracle.coefficients (coefficients written out as products):
     S_end = P S0 - sum_i oS_i g_i, W_end = beta W0 + a_S S0 - sum_i oW_i g_i, every g_i at the
-    chunk-start weights, i over the chunk and the window - 1 tokens before it."""
+    chunk-start weights, i over the chunk and the window - 1 tokens before it.  `hist` = (K, V,
+    gamma) of the tokens before this call (oldest first), whose gammas reach the coefficients
+    through omega_coefficients' gamma_hist; None = the start of a sequence."""
     from oracle.coefficients import chunk_coefficients, omega_coefficients
     W = [p.copy() for p in params]
     S = [m.copy() for m in momenta]
     X = phi_triu(K, cfg.poly_degree)
     T, C, c = K.shape[0], cfg.chunk, cfg.omega_window
+    Xh = None if hist is None else phi_triu(hist[0], cfg.poly_degree)
     cW_all = np.zeros(T)
     cS_all = np.zeros(T)
     scal = []
     for s in range(0, T, C):
         cW_all[s:s + C], cS_all[s:s + C], sc = chunk_coefficients(th[s:s + C], et[s:s + C], al[s:s + C])
         scal.append(sc)
-    oW, oS = omega_coefficients(cW_all, cS_all, ga if c > 1 else np.ones(T), C, c)
+    oW, oS = omega_coefficients(cW_all, cS_all, ga if c > 1 else np.ones(T), C, c,
+                                gamma_hist=None if hist is None else hist[2])
     for k, s in enumerate(range(0, T, C)):
         P, beta, aS = scal[k]
         GW = [np.zeros_like(x) for x in W]
@@ -406,8 +410,11 @@ def coefficient_form(cfg, params, momenta, K, V, th, et, al, ga):
         for r in range(C + c - 1):
             i = s - (c - 1) + r
             if i < 0:
-                continue
-            g = oracle.loss_grad(W, X[i], V[i])
+                if Xh is None or len(Xh) + i < 0:
+                    continue
+                g = oracle.loss_grad(W, Xh[len(Xh) + i], hist[1][len(Xh) + i])
+            else:
+                g = oracle.loss_grad(W, X[i], V[i])
             for m in range(len(W)):
                 GW[m] += oW[k, r] * g[m]
                 GS[m] += oS[k, r] * g[m]
@@ -445,6 +452,32 @@ def test_recurrence_matches_derived_coefficient_form(kind, c):
         assert maxrel(a, b) < 1e-12
     for a, b in zip(res.momenta, S):
         assert maxrel(a, b) < 1e-12
+
+
+@pytest.mark.parametrize("c", [2, 4, 6])
+def test_omega_coefficients_with_carried_gamma_history(c):
+    """The coefficient form of a second call, whose window reaches back into the first call's last
+    c - 1 tokens (their gammas through gamma_hist, oldest first), equals the literal recurrence run
+    as two calls with the carried history.  An index slip in the gamma_hist branch (off by one, the
+    newest gamma first, gamma taken as 1) moves W and S far beyond 1e-12."""
+    T, T1 = 16, 8
+    cfg, params, momenta, K, Q, V, th, et, al, ga = tiny_problem(40 + c, MLP2_SILU, T, 3, 2, 4, 1, 4, c, PER_TOKEN)
+    a = oracle.run_memory(cfg, params, momenta, K[:T1], Q[:T1], V[:T1], th[:T1], et[:T1], al[:T1], ga[:T1])
+    b = oracle.run_memory(cfg, a.params, a.momenta, K[T1:], Q[T1:], V[T1:], th[T1:], et[T1:], al[T1:], ga[T1:],
+                          history=a.history)
+    h0 = T1 - (c - 1)
+    hist = (K[h0:T1], V[h0:T1], ga[h0:T1])
+    W, S = coefficient_form(cfg, a.params, a.momenta, K[T1:], V[T1:], th[T1:], et[T1:], al[T1:], ga[T1:], hist=hist)
+    for x, y in zip(b.params + b.momenta, W + S):
+        assert maxrel(y, x) < 1e-12
+    # the carried gammas matter: the same history rows with their gammas taken as 1, or the
+    # window clipped at the call boundary, give a different state
+    flipped = (hist[0], hist[1], np.ones(c - 1))
+    Wf, _ = coefficient_form(cfg, a.params, a.momenta, K[T1:], V[T1:], th[T1:], et[T1:], al[T1:], ga[T1:],
+                             hist=flipped)
+    Wc, _ = coefficient_form(cfg, a.params, a.momenta, K[T1:], V[T1:], th[T1:], et[T1:], al[T1:], ga[T1:])
+    assert maxrel(Wf[0], b.params[0]) > 1e-9
+    assert maxrel(Wc[0], b.params[0]) > 1e-9
 
 
 def test_omega_window_one_is_single_token_rule():
