@@ -134,6 +134,65 @@ def measured_traffic():
         return None
 
 
+STATS_FILE = os.path.join(ROOT, "profiles", "ns5_B8H16_T32768_fused_kernel_stats.md")
+
+
+def sources_sha16():
+    import hashlib
+    m = hashlib.sha256()
+    for f in FUSED_SOURCES:
+        m.update(open(f, "rb").read())
+    return m.hexdigest()[:16]
+
+
+def rocprof_kernel_ms():
+    """Average duration (ms) of the fused kernel from the committed rocprofv3 --kernel-trace --stats
+    summary, or None when the kernel's sources have changed since it was taken."""
+    try:
+        kv = {}
+        for ln in open(STATS_FILE):
+            if "=" in ln and not ln.startswith("#") and not ln.startswith("|"):
+                k, v = ln.split("=", 1)
+                kv[k.strip()] = v.strip()
+        if sources_sha16() != kv["kernel_sources_sha256_16"]:
+            return None
+        return float(kv["avg_ns"]) * 1e-6
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def calibration(torch, am, dev, stream):
+    """The measured ceilings: the bf16 matrix-core rate of a kernel that does nothing else (256
+    workgroups of eight waves, eight independent 32x32x16 chains per wave) and the rate of a plain
+    16-byte streaming copy of 1 GiB."""
+    sink = torch.empty(256, dtype=torch.float32, device=dev)
+    iters = 20000
+    flops = 256 * 8 * iters * 8 * 32768
+    am.calibrate_mfma(iters, 256, sink, stream)
+    t = event_ms(lambda: am.calibrate_mfma(iters, 256, sink, stream), 5, stream)
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    am.calibrate_copy(src, dst, n, stream)
+    tc = event_ms(lambda: am.calibrate_copy(src, dst, n, stream), 10, stream)
+    del src, dst
+    return dict(mfma_bf16_tflops=round(flops / (t * 1e-3) / 1e12, 1), mfma_kernel_ms=round(t, 4),
+                copy_gbs=round(2 * n / (tc * 1e-3) / 1e9, 1), copy_bytes=n,
+                note="am::mfma_peak_kernel (v_mfma_f32_32x32x16_bf16 chains, no memory traffic) and "
+                     "am::copy16_kernel (read + write counted)")
+
+
 def event_ms(fn, iters, stream):
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -430,7 +489,7 @@ def cpu_baseline(inp, seconds_target: float, cores: int):
     with ctx.Pool(cores, initializer=_limit_threads) as pool:
         pool.map(_oracle_one, [(m, Ts) for m in mems], chunksize=1)
     wall = time.perf_counter() - t0
-    return dict(value=n_mem * Ts / wall, unit="tokens/s", cores=cores, kind="oracle",
+    return dict(value=n_mem * Ts / wall, unit="tokens/s", cores=cores, kind="oracle", cpu_model=cpu_model(),
                 sample=f"{n_mem} memories x first {Ts} tokens ({n_chunks} of {chunks_per_mem} chunks) of "
                        f"{s.name}, fp64 NumPy, one memory per process, {wall:.1f} s wall")
 
@@ -500,7 +559,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--variant", default="literal")
-    ap.add_argument("--precision", type=int, default=0, help="0 auto (split bf16), 1 bf16, 2 split bf16")
+    ap.add_argument("--precision", type=int, default=0, help="0 auto (split bf16), 1 bf16, 2 split bf16, 3 fp32 operands")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-check", action="store_true")
@@ -552,7 +611,7 @@ def main():
         n = args.copy_calibration << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        am.calibrate_copy(src, dst, n, stream)
         torch.cuda.synchronize()
         del src, dst
 
@@ -594,7 +653,7 @@ def main():
     # dominant kernel: the update call.  On the fused path it is one launch of the whole-call
     # kernel; on the general path it is the whole per-chunk launch sequence.
     fused = (s.kind == synth.MLP2_SILU and s.gate_mode == synth.PER_CHUNK and s.ns_steps > 0 and s.d_key == 64
-             and s.d_value == 64 and s.d_hidden == 128 and s.chunk % 64 == 0 and args.precision != am.PREC_BF16)
+             and s.d_value == 64 and s.d_hidden == 128 and s.chunk % 64 == 0 and args.precision in (am.PREC_AUTO, am.PREC_BF16X3))
     ach = step_flops / (upd_ms * 1e-3) / 1e12
     roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                 frac=round(ach / PEAK_BF16_TFLOPS, 5),
@@ -604,6 +663,16 @@ def main():
                         if fused else "per-chunk launches"),
                 avg_launch_ms=round(upd_ms, 5),
                 algorithmic_flops_per_launch=int(step_flops))
+
+    calib = None if args.no_stages else calibration(torch, am, dev, stream)
+    if calib:
+        roof["peak_measured"] = calib["mfma_bf16_tflops"]
+        roof["frac_of_measured_peak"] = round(ach / calib["mfma_bf16_tflops"], 5)
+    if fused and s.T == 32768 and s.n_mem == 128:
+        rp = rocprof_kernel_ms()
+        roof["kernel_sources_sha256_16"] = sources_sha16()
+        roof["rocprof_avg_launch_ms"] = None if rp is None else round(rp, 5)
+        roof["frac_rocprof"] = None if rp is None else round(step_flops / (rp * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5)
 
     check = None
     if not args.no_check:
@@ -638,11 +707,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16x3" if args.precision != 1 else "bf16",
+        "dtype": {1: "bf16", 3: "f32"}.get(args.precision, "bf16x3"),
         "data": "synthetic (seeded, generator inputs resident in HBM)",
         "config": {"workload": s.name, "batch": s.batch, "heads": s.heads, "T": s.T, "chunk": s.chunk,
                    "d_key": s.d_key, "d_hidden": s.d_hidden, "d_value": s.d_value, "ns_steps": s.ns_steps,
                    "gate_mode": "per_chunk" if s.gate_mode else "per_token", "variant": args.variant,
+                   "key_norm": "l2" if s.norm_k else "none", "query_norm": "l2" if s.norm_q else "none",
+                   "value_norm": "l2" if s.norm_v else "none",
                    "tokens_per_step": tokens, "parallelism": "single GPU; memories spread over workgroups"},
         "path_tflops": round(path_tflops, 2),
         "path_frac_bf16_peak": round(path_tflops / PEAK_BF16_TFLOPS, 5),
@@ -650,6 +721,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "check": check,
+        "calibration": calib,
         "configs": configs,
         "stages": stages,
     }

@@ -82,11 +82,17 @@ typedef enum { ATLASMEM_F32 = 0, ATLASMEM_BF16 = 1 } atlasmem_dtype;
 /* Operand precision of the matrix-core products (state and accumulation are fp32 always).
  * BF16X3 splits every fp32 operand x into hi = bf16(x), lo = bf16(x - hi) and sums
  * hi*hi + hi*lo + lo*hi (two products where one side is an exact bf16 input).
+ * F32 keeps every operand in fp32 (the matrix cores' fp32 path, v_mfma_f32_16x16x4_f32, and
+ * fp32 fused multiply-adds for Newton-Schulz): for inputs whose rounding the Newton-Schulz
+ * feedback amplifies beyond what the split holds (e.g. keys that are not normalised); it runs the
+ * general per-product path only (no fused whole-call kernel, no chunk loop, no decode kernel) and
+ * the outer-loop backward of the 2-layer memories rejects it (E_UNSUPPORTED).
  * AUTO = BF16X3.  The linear memory always runs in fp32 FMA. */
 typedef enum {
   ATLASMEM_PREC_AUTO = 0,
   ATLASMEM_PREC_BF16 = 1,
-  ATLASMEM_PREC_BF16X3 = 2
+  ATLASMEM_PREC_BF16X3 = 2,
+  ATLASMEM_PREC_F32 = 3
 } atlasmem_precision;
 
 typedef struct {

@@ -18,7 +18,7 @@ OK, E_INVALID, E_SHAPE, E_UNSUPPORTED, E_DEVICE, E_NOMEM, E_NONFINITE = range(7)
 LINEAR, MLP2_SILU, MLP2_SILU_RESIDUAL, MLP2_GATED = 0, 1, 2, 3
 PER_TOKEN, PER_CHUNK = 0, 1
 F32, BF16 = 0, 1
-PREC_AUTO, PREC_BF16, PREC_BF16X3 = 0, 1, 2
+PREC_AUTO, PREC_BF16, PREC_BF16X3, PREC_F32 = 0, 1, 2, 3
 FLAG_NO_FUSED = 1
 FLAG_PER_TOKEN_RETRIEVE = 2
 FLAG_NO_CHUNK_LOOP = 4
@@ -32,6 +32,7 @@ EXPORTS = (
     "atlasmem_reset_history", "atlasmem_destroy", "atlasmem_gate_scan", "atlasmem_omega_coeffs",
     "atlasmem_poly_features", "atlasmem_newton_schulz", "atlasmem_short_conv", "atlasmem_gates",
     "atlasmem_feature_map", "atlasmem_backward_workspace_bytes", "atlasmem_update_backward",
+    "atlasmem_calibrate_mfma", "atlasmem_calibrate_copy",
 )
 
 
@@ -91,6 +92,8 @@ def load():
         "atlasmem_feature_map": ([_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
         "atlasmem_backward_workspace_bytes": ([_vp, _i64], _i64),
         "atlasmem_update_backward": ([_vp] * 8 + [_i64] + [_vp] * 5 + [_i64] + [_vp] * 10, ctypes.c_int),
+        "atlasmem_calibrate_mfma": ([_i64, _i32, _vp, _vp], ctypes.c_int),
+        "atlasmem_calibrate_copy": ([_vp, _vp, _i64, _vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -228,6 +231,15 @@ def newton_schulz(G, n_mat: int, rows: int, cols: int, steps: int, coeffs, eps: 
     a, b, c = coeffs
     _check(load().atlasmem_newton_schulz(_ptr(G), n_mat, rows, cols, steps, a, b, c, eps, precision, _ptr(out),
                                          _stream(stream)), "atlasmem_newton_schulz")
+
+
+def calibrate_mfma(iters: int, n_workgroups: int, sink, stream=None):
+    """FLOPs of the call: n_workgroups * 8 * iters * 8 * 32768."""
+    _check(load().atlasmem_calibrate_mfma(iters, n_workgroups, _ptr(sink), _stream(stream)), "atlasmem_calibrate_mfma")
+
+
+def calibrate_copy(src, dst, nbytes: int, stream=None):
+    _check(load().atlasmem_calibrate_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "atlasmem_calibrate_copy")
 
 
 def short_conv(X, in_dtype: int, M: int, T: int, d: int, heads: int, taps, bias, hist, l2norm: bool, out,

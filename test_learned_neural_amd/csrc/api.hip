@@ -39,7 +39,7 @@ atlasmem_status validate(const atlasmem_config* c) {
   if ((c->input_dtype != ATLASMEM_F32 && c->input_dtype != ATLASMEM_BF16) ||
       (c->output_dtype != ATLASMEM_F32 && c->output_dtype != ATLASMEM_BF16))
     return ATLASMEM_E_INVALID;
-  if (c->precision < ATLASMEM_PREC_AUTO || c->precision > ATLASMEM_PREC_BF16X3) return ATLASMEM_E_INVALID;
+  if (c->precision < ATLASMEM_PREC_AUTO || c->precision > ATLASMEM_PREC_F32) return ATLASMEM_E_INVALID;
   if (c->ns_steps > 0 && !(c->ns_eps >= 0.0f)) return ATLASMEM_E_INVALID;
   if (c->flags & ~(ATLASMEM_FLAG_NO_FUSED | ATLASMEM_FLAG_PER_TOKEN_RETRIEVE | ATLASMEM_FLAG_NO_CHUNK_LOOP |
                    ATLASMEM_FLAG_NO_SPLIT_K))
@@ -97,7 +97,8 @@ Dims make_dims(const atlasmem_config* c) {
   d.ns_eps = c->ns_eps;
   d.in_bf16 = c->input_dtype == ATLASMEM_BF16;
   d.out_bf16 = c->output_dtype == ATLASMEM_BF16;
-  d.split = c->precision != ATLASMEM_PREC_BF16;
+  d.prec = c->precision == ATLASMEM_PREC_BF16 ? 0 : (c->precision == ATLASMEM_PREC_F32 ? 2 : 1);
+  d.split = d.prec == 1;
   d.no_fused = (c->flags & ATLASMEM_FLAG_NO_FUSED) != 0;
   d.no_loop = (c->flags & ATLASMEM_FLAG_NO_CHUNK_LOOP) != 0;
   d.no_splitk = (c->flags & ATLASMEM_FLAG_NO_SPLIT_K) != 0;
@@ -565,13 +566,14 @@ atlasmem_status atlasmem_newton_schulz(const float* G, int64_t n_mat, int32_t ro
                                        float a, float b, float c, float eps, int32_t precision, float* out,
                                        void* stream) {
   if (n_mat < 0 || rows < 1 || cols < 1 || steps < 0 || steps > 16 || !(eps >= 0.0f)) return ATLASMEM_E_INVALID;
-  if (precision < ATLASMEM_PREC_AUTO || precision > ATLASMEM_PREC_BF16X3) return ATLASMEM_E_INVALID;
+  if (precision < ATLASMEM_PREC_AUTO || precision > ATLASMEM_PREC_F32) return ATLASMEM_E_INVALID;
   if (!ns_supported(rows, cols)) return ATLASMEM_E_UNSUPPORTED;
   if (n_mat == 0) return ATLASMEM_OK;
   if (!G || !out || G == out) return ATLASMEM_E_INVALID;
   if (n_mat > INT32_MAX) return ATLASMEM_E_SHAPE;
   return launch_ns(G, (int64_t)rows * cols, (int)n_mat, rows, cols, steps, a, b, c, eps,
-                   precision != ATLASMEM_PREC_BF16, out, nullptr, S(stream));
+                   precision == ATLASMEM_PREC_BF16 ? 0 : (precision == ATLASMEM_PREC_F32 ? 2 : 1), out, nullptr,
+                   S(stream));
 }
 
 atlasmem_status atlasmem_short_conv(const void* X, int32_t in_dtype, int64_t M, int64_t T, int32_t d, int32_t heads,

@@ -241,6 +241,95 @@ inline void launch_gemm(bool split, int M, int N, int K, int batch, const LA& la
                        lb, ep);
 }
 
+// ---------------------------------------------------------------------------- fp32 operands
+//
+// The F32 precision: operands kept in fp32 and multiplied on the matrix cores' fp32 path
+// (v_mfma_f32_16x16x4_f32, fp32 products and accumulation), for configurations whose rounding
+// the split bf16 products amplify too much.  Same 64 x 64 x 32 tiles, loaders, epilogues and
+// output layout as gemm_tile (lane l of a 16 x 16 block holds rows 4(l/16) + r of column l % 16);
+// a k-step of 32 is eight k = 4 products, lane l supplying k = 4s + l/16 of its row (A) or column
+// (B).  No split-K: this path is for accuracy, not speed.
+constexpr int GLDF = GK + 4;  // fp32 row stride: rows 36 words apart put 16 rows x 4 k on 64 banks
+
+template <class LA, class LB, class EP>
+__global__ void __launch_bounds__(256) gemm_f32_kernel(int M, int N, int K, LA la, LB lb, EP ep) {
+  __shared__ __attribute__((aligned(16))) float As[GT * GLDF];
+  __shared__ __attribute__((aligned(16))) float Bs[GT * GLDF];
+  const int z = blockIdx.z, m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int lr = lane & 15, lq = lane >> 4;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int srow = t >> 2, sk = (t & 3) * 8;
+  for (int k0 = 0; k0 < K; k0 += GK) {
+    {
+      float v[8];
+      la.load8(z, m0 + srow, k0 + sk, v);
+      *(float4*)&As[srow * GLDF + sk] = float4{v[0], v[1], v[2], v[3]};
+      *(float4*)&As[srow * GLDF + sk + 4] = float4{v[4], v[5], v[6], v[7]};
+      lb.load8(z, n0 + srow, k0 + sk, v);
+      *(float4*)&Bs[srow * GLDF + sk] = float4{v[0], v[1], v[2], v[3]};
+      *(float4*)&Bs[srow * GLDF + sk + 4] = float4{v[4], v[5], v[6], v[7]};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s4 = 0; s4 < GK / 4; ++s4) {
+      float a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = As[(wm * 32 + i * 16 + lr) * GLDF + 4 * s4 + lq];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = Bs[(wn * 32 + j * 16 + lr) * GLDF + 4 * s4 + lq];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  if constexpr (EpiTwoPhase<EP>::value) {
+    typename EP::Pre pre[2][2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * 32 + i * 16 + lq * 4 + r, col = n0 + wn * 32 + j * 16 + lr;
+          if (row < M && col < N) pre[i][j][r] = ep.load(z, row, col);
+        }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * 32 + i * 16 + lq * 4 + r, col = n0 + wn * 32 + j * 16 + lr;
+          if (row < M && col < N) ep.store(z, row, col, acc[i][j][r], pre[i][j][r]);
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * 32 + i * 16 + lq * 4 + r, col = n0 + wn * 32 + j * 16 + lr;
+          if (row < M && col < N) ep(z, row, col, acc[i][j][r]);
+        }
+  }
+}
+
+template <class LA, class LB, class EP>
+inline void launch_gemm_f32(int M, int N, int K, int batch, const LA& la, const LB& lb, const EP& ep, hipStream_t st) {
+  if (M <= 0 || N <= 0 || batch <= 0) return;
+  dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch);
+  hipLaunchKernelGGL((gemm_f32_kernel<LA, LB, EP>), grid, dim3(256), 0, st, M, N, K, la, lb, ep);
+}
+
 // ---------------------------------------------------------------------------- generic loaders
 
 enum Xform { XF_NONE = 0, XF_SILU = 1, XF_COEF = 2, XF_SCALE = 3, XF_GATED = 4, XF_MAT = 5 };

@@ -26,6 +26,7 @@ struct Dims {
   float ns_a, ns_b, ns_c, ns_eps;
   int in_bf16, out_bf16;
   bool split;   // bf16 hi/lo split products
+  int prec;     // operand precision of the products: 0 plain bf16, 1 split bf16 (hi/lo), 2 fp32
   bool no_fused;
   bool no_loop;  // one launch per product and chunk instead of the chunk-loop kernel
   bool no_splitk;  // every product over its whole k range in one launch
@@ -175,7 +176,7 @@ struct NsUpdate {
   int* flag;
 };
 atlasmem_status launch_ns(const float* G, int64_t ldG_mat, int n_mat, int rows, int cols, int steps, float a, float b,
-                          float c, float eps, bool split, float* out, const NsUpdate* upd, hipStream_t st);
+                          float c, float eps, int prec, float* out, const NsUpdate* upd, hipStream_t st);
 bool ns_supported(int rows, int cols);
 // Several matrices of each memory in one launch (up to three groups of n_mat matrices, memory m's
 // matrix of group i at G + goff_i + m ldG_mat, rows_i x cols_i), each followed by the momentum /
@@ -185,7 +186,7 @@ struct NsGroup {
   int64_t goff, uoff;
 };
 atlasmem_status launch_ns_groups(const float* G, int64_t ldG_mat, int n_mat, int ngroups, const NsGroup* grp, int steps,
-                                 float a, float b, float c, float eps, bool split, const NsUpdate& upd,
+                                 float a, float b, float c, float eps, int prec, const NsUpdate& upd,
                                  hipStream_t st);
 bool fused_supported(const Dims& d);
 atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,

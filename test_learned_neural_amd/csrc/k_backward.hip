@@ -1100,6 +1100,7 @@ static atlasmem_status ns_backward(const Dims& d, float* ws, const NsLay& n, con
 
 bool backward_supported(const Dims& d) {
   if (d.kind == ATLASMEM_LINEAR) return !d.ptr && d.poly <= 2 && d.gate_mode == ATLASMEM_PER_TOKEN;
+  if (d.prec == 2) return false;  // the 2-layer memories' backward products run in split bf16
   if (d.gated)
     return !d.ptr && d.poly <= 2 && (d.gate_mode == ATLASMEM_PER_CHUNK ? d.c == 1 && d.poly == 1 : d.ns_steps == 0);
   return d.kind == ATLASMEM_MLP2_SILU && !d.ptr && d.poly <= 2 &&

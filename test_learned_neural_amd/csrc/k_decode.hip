@@ -227,7 +227,7 @@ static size_t decode_lds(const Dims& d, int64_t n) {
 }
 
 bool decode_supported(const Dims& d, int64_t n) {
-  return d.kind == ATLASMEM_MLP2_SILU && d.poly == 1 && !d.ptr && n >= 1 && n <= kDecodeMaxTokens &&
+  return d.kind == ATLASMEM_MLP2_SILU && d.poly == 1 && !d.ptr && d.prec != 2 && n >= 1 && n <= kDecodeMaxTokens &&
          d.din % 4 == 0 && d.dh % 4 == 0 && decode_lds(d, n) <= (size_t)kDecodeMaxLds;
 }
 

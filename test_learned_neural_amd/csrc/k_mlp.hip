@@ -478,9 +478,15 @@ static __host__ __device__ StridedLoader hidden(const Dims& d, const float* Z, i
 }
 
 // `h` supplies the split-K scratch (null: no split).
+// `prec`: 0 plain bf16 operands, 1 split bf16 (hi/lo), 2 fp32 operands (Dims::prec).
 template <class LA, class LB, class EP>
-static void gemm_any(bool split, bool a_exact, bool b_exact, int M, int N, int K, int batch, const LA& la, const LB& lb,
+static void gemm_any(int prec, bool a_exact, bool b_exact, int M, int N, int K, int batch, const LA& la, const LB& lb,
                      const EP& ep, hipStream_t st, const Handle* h = nullptr) {
+  if (prec == 2) {
+    launch_gemm_f32(M, N, K, batch, la, lb, ep, st);
+    return;
+  }
+  const bool split = prec == 1;
   float* sk = (h && !h->d.no_splitk) ? h->sk : nullptr;
   const int64_t skf = h ? h->sk_floats : 0;
   if (a_exact && b_exact) launch_gemm<true, true>(split, M, N, K, batch, la, lb, ep, st, sk, skf);
@@ -524,7 +530,8 @@ static atlasmem_status ptr_retrieve(Handle* h, const Dims& d, const void* K, con
                                     const float* eta, const float* alpha, const float* gamma, int64_t ld, int64_t s,
                                     const float* Win, const float* Sin, void* Y, hipStream_t st) {
   const int M = d.M, C = d.C, Rk = d.Rk, dh = d.dh, dv = d.dv, din = d.din, dz = d.dz;
-  const bool split = d.split, feat_exact = d.poly == 1 && d.in_bf16;
+  const int split = d.prec;
+  const bool feat_exact = d.poly == 1 && d.in_bf16;
   const int64_t zsz = (int64_t)d.Rt * dz, qz = (int64_t)C * dz, az = (int64_t)C * Rk, yz = (int64_t)C * dv;
   atlasmem_status stt = launch_ptr_coeffs(theta, eta, alpha, gamma, ld, h->hg[h->hcur], M, s, C, d.c, h->pbA,
                                           h->pOm, st);
@@ -755,7 +762,7 @@ static int64_t loop_chain(const Dims& d, bool with_y) {
 // workgroups: degree-2 features of 32-wide keys (72 steps) ran 2x slower in the loop, and the
 // 384 -> 768 -> 384 memory takes 324.
 static bool loop_supported(const Dims& d, bool with_y) {
-  return !d.no_loop && !d.ptr && (d.gate_mode == ATLASMEM_PER_TOKEN || d.ns_steps == 0) && loop_chain(d, with_y) <= 24;
+  return !d.no_loop && !d.ptr && d.prec != 2 && (d.gate_mode == ATLASMEM_PER_TOKEN || d.ns_steps == 0) && loop_chain(d, with_y) <= 24;
 }
 
 atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* Q, const void* V, const float* theta,
@@ -763,7 +770,7 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
                            hipStream_t st) {
   const int64_t T = sp.T, ld = sp.ld;
   const int M = d.M, C = d.C, c = d.c, Rk = d.Rk, dh = d.dh, dv = d.dv, din = d.din, dz = d.dz;
-  const bool split = d.split;
+  const int split = d.prec;
   const bool feat_exact = d.poly == 1 && d.in_bf16;
   const int64_t nchunks = T / C;
   const int nq = Y ? C : 0;
@@ -816,11 +823,11 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
       la.kb0 = kb0;
       la.nb = nb;
       la.flag = h->flag;
-      const void* kern = split ? (feat_exact ? (const void*)mlp_loop_kernel<true, true> : (const void*)mlp_loop_kernel<true, false>)
+      const void* kern = split == 1 ? (feat_exact ? (const void*)mlp_loop_kernel<true, true> : (const void*)mlp_loop_kernel<true, false>)
                                : (feat_exact ? (const void*)mlp_loop_kernel<false, true> : (const void*)mlp_loop_kernel<false, false>);
       if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LOOP_LDS) != hipSuccess)
         return ATLASMEM_E_DEVICE;
-      if (split) {
+      if (split == 1) {
         if (feat_exact) hipLaunchKernelGGL((mlp_loop_kernel<true, true>), dim3(M), dim3(LOOP_THREADS), LOOP_LDS, st, la);
         else hipLaunchKernelGGL((mlp_loop_kernel<true, false>), dim3(M), dim3(LOOP_THREADS), LOOP_LDS, st, la);
       } else {
@@ -955,14 +962,14 @@ atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, int64_t ld, vo
       FeatA la{feat_rows(h, nullptr, Q, ld, s, 0, rows, 1)};
       StridedLoader lb = strided(W1, d.P, din, 1, 1, dz, din);
       EpiStore ep{h->Zr, zsz, dz, 1};
-      gemm_any(d.split, feat_exact, false, rows, dz, din, M, la, lb, ep, st, h);
+      gemm_any(d.prec, feat_exact, false, rows, dz, din, M, la, lb, ep, st, h);
     }
     {
       StridedLoader la = hidden(d, h->Zr, zsz, dz, 1, 1, rows, dh);
       StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);
       EpiY ep{nullptr, 0, nullptr, d.in_bf16, nullptr, ld, s, 0, d.c, dv, Y, d.out_bf16, d.residual,
               feat_rows(h, nullptr, Q, ld, s, 0, rows, 1)};
-      gemm_any(d.split, false, false, rows, dv, dh, M, la, lb, ep, st, h);
+      gemm_any(d.prec, false, false, rows, dv, dh, M, la, lb, ep, st, h);
     }
     AM_LAUNCH_CHECK();
   }

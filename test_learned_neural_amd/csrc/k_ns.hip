@@ -255,13 +255,110 @@ __global__ void __launch_bounds__(256) ns_kernel(NsArgs p) {
   if (bad) p.u.flag[0] = 1;
 }
 
+// The F32 precision: the same iteration with fp32 operands and fp32 fused multiply-adds on the
+// vector units, one workgroup per matrix.  X (64 x 128, zero-padded), A and B live in LDS as fp32;
+// every product walks its k index in natural order.  For configurations whose rounding the split
+// bf16 products amplify beyond the tolerance; speed is not the point here.
+constexpr int FXL = NSN + 1;  // fp32 row strides (odd: a column walk touches distinct banks)
+constexpr int FAL = NSM + 1;
+
+__global__ void __launch_bounds__(256) ns_f32_kernel(NsArgs p) {
+  __shared__ float Xs[NSM * FXL];
+  __shared__ float As[NSM * FAL];  // A, then B = b A + c A^2 in its place
+  __shared__ float red[4];
+  const int gi = blockIdx.x / p.gsize, mat = blockIdx.x - gi * p.gsize;
+  const int rows = p.grows[gi], cols = p.gcols[gi];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const bool tr = rows > cols;
+  const int m = tr ? cols : rows;
+  const int n = tr ? rows : cols;
+  const float* g = p.G + p.goff[gi] + (int64_t)mat * p.ldG;
+  float ss = 0.0f;
+  for (int e = t; e < NSM * NSN; e += 256) {
+    const int i = e / NSN, j = e % NSN;
+    float v = 0.0f;
+    if (i < m && j < n) v = tr ? g[(int64_t)j * cols + i] : g[(int64_t)i * cols + j];
+    Xs[i * FXL + j] = v;
+    ss = fmaf(v, v, ss);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  const float inv = 1.0f / (sqrtf(red[0] + red[1] + red[2] + red[3]) + p.eps);
+  for (int e = t; e < NSM * NSN; e += 256) Xs[(e / NSN) * FXL + e % NSN] *= inv;
+  __syncthreads();
+  // thread t owns row i = t / 4 and columns j = t % 4 + 4 q of A and B (q < 16) and of X (q < 32)
+  const int i = t >> 2, j0 = t & 3;
+  for (int step = 0; step < p.steps; ++step) {
+    float acc[32];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+    for (int k = 0; k < NSN; ++k) {  // A = X X^T
+      const float xi = Xs[i * FXL + k];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = fmaf(xi, Xs[(j0 + 4 * q) * FXL + k], acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) As[i * FAL + j0 + 4 * q] = acc[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+    for (int k = 0; k < NSM; ++k) {  // A^2
+      const float aik = As[i * FAL + k];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = fmaf(aik, As[k * FAL + j0 + 4 * q], acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = fmaf(p.b, As[i * FAL + j0 + 4 * q], p.c * acc[q]);
+    __syncthreads();  // every thread is done reading A
+#pragma unroll
+    for (int q = 0; q < 16; ++q) As[i * FAL + j0 + 4 * q] = acc[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 32; ++q) acc[q] = 0.0f;
+    for (int k = 0; k < NSM; ++k) {  // B X
+      const float bik = As[i * FAL + k];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) acc[q] = fmaf(bik, Xs[k * FXL + j0 + 4 * q], acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 32; ++q) acc[q] = fmaf(p.a, Xs[i * FXL + j0 + 4 * q], acc[q]);
+    __syncthreads();  // every thread is done reading X
+#pragma unroll
+    for (int q = 0; q < 32; ++q) Xs[i * FXL + j0 + 4 * q] = acc[q];
+    __syncthreads();
+  }
+  bool bad = false;
+  for (int e = t; e < NSM * NSN; e += 256) {
+    const int ii = e / NSN, jj = e % NSN;
+    if (ii >= m || jj >= n) continue;
+    const int gr = tr ? jj : ii, gc = tr ? ii : jj;
+    const float v = Xs[ii * FXL + jj];
+    if (!p.has_upd) {
+      p.out[(int64_t)mat * rows * cols + (int64_t)gr * cols + gc] = v;
+    } else {
+      const NsUpdate& u = p.u;
+      const int mem = mat / u.mats_per_mem;
+      const int64_t el = (int64_t)mem * u.P + p.uoff[gi] + (int64_t)gr * cols + gc;
+      const int64_t gk = (int64_t)mem * u.ld_gate + u.k;
+      const float sn = u.eta[gk] * u.Sin[el] - u.theta[gk] * v;
+      const float wn = (1.0f - u.alpha[gk]) * u.Win[el] + sn;
+      u.Sout[el] = sn;
+      u.Wout[el] = wn;
+      bad |= !(isfinite(sn) && isfinite(wn));
+    }
+  }
+  if (bad) p.u.flag[0] = 1;
+}
+
 bool ns_supported(int rows, int cols) {
   const int m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
   return m >= 1 && m <= NSM && n <= NSN;
 }
 
 atlasmem_status launch_ns(const float* G, int64_t ldG_mat, int n_mat, int rows, int cols, int steps, float a, float b,
-                          float c, float eps, bool split, float* out, const NsUpdate* upd, hipStream_t st) {
+                          float c, float eps, int prec, float* out, const NsUpdate* upd, hipStream_t st) {
   if (!ns_supported(rows, cols)) return ATLASMEM_E_UNSUPPORTED;
   if (n_mat == 0) return ATLASMEM_OK;
   NsArgs p;
@@ -283,14 +380,15 @@ atlasmem_status launch_ns(const float* G, int64_t ldG_mat, int n_mat, int rows, 
   p.gcols[0] = cols;
   p.goff[0] = 0;
   p.uoff[0] = upd ? upd->off : 0;
-  if (split) hipLaunchKernelGGL(ns_kernel<true>, dim3(n_mat), dim3(256), 0, st, p);
+  if (prec == 2) hipLaunchKernelGGL(ns_f32_kernel, dim3(n_mat), dim3(256), 0, st, p);
+  else if (prec == 1) hipLaunchKernelGGL(ns_kernel<true>, dim3(n_mat), dim3(256), 0, st, p);
   else hipLaunchKernelGGL(ns_kernel<false>, dim3(n_mat), dim3(256), 0, st, p);
   AM_LAUNCH_CHECK();
   return ATLASMEM_OK;
 }
 
 atlasmem_status launch_ns_groups(const float* G, int64_t ldG_mat, int n_mat, int ngroups, const NsGroup* grp, int steps,
-                                 float a, float b, float c, float eps, bool split, const NsUpdate& upd,
+                                 float a, float b, float c, float eps, int prec, const NsUpdate& upd,
                                  hipStream_t st) {
   if (ngroups < 1 || ngroups > 3) return ATLASMEM_E_INVALID;
   for (int i = 0; i < ngroups; ++i)
@@ -318,7 +416,8 @@ atlasmem_status launch_ns_groups(const float* G, int64_t ldG_mat, int n_mat, int
     p.uoff[i] = q.uoff;
   }
   const dim3 grid((unsigned)((int64_t)n_mat * ngroups));
-  if (split) hipLaunchKernelGGL(ns_kernel<true>, grid, dim3(256), 0, st, p);
+  if (prec == 2) hipLaunchKernelGGL(ns_f32_kernel, grid, dim3(256), 0, st, p);
+  else if (prec == 1) hipLaunchKernelGGL(ns_kernel<true>, grid, dim3(256), 0, st, p);
   else hipLaunchKernelGGL(ns_kernel<false>, grid, dim3(256), 0, st, p);
   AM_LAUNCH_CHECK();
   return ATLASMEM_OK;
