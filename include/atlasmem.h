@@ -215,6 +215,31 @@ atlasmem_status atlasmem_reset_history(atlasmem_handle h, void* stream);
 /* Waits for the handle's work and frees everything it owns.  NULL is a no-op. */
 void atlasmem_destroy(atlasmem_handle h);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): atlasmem_update_chunked without a handle, for the
+ * configurations the fused whole-call kernel covers (the 64 -> 128 -> 64 SiLU memory, plain or
+ * residual, PER_CHUNK gates, ns_steps >= 1, window 1, poly_degree 1, bf16 inputs, AUTO / BF16X3
+ * precision, chunk a multiple of 64, flags 0; E_UNSUPPORTED otherwise).  Same results as
+ * update_chunked from the same state over the same tokens.
+ *   cfg:   validated as by atlasmem_create (batch * heads <= ATLASMEM_STATIC_MAX_MEMORIES, else
+ *          E_SHAPE)
+ *   K, Q, V, theta, eta, alpha, Y: as in atlasmem_update_chunked, with T a multiple of the chunk
+ *          (E_SHAPE otherwise; no tokens are buffered between calls)
+ *   W, S:  [M, P] fp32 device arrays, the weights and momentum before the call, overwritten in
+ *          place with the state after it
+ *   nonfinite: optional device int32, set to 1 if a state element became NaN/Inf, else 0
+ * The kernel's per-memory scratch (the second-layer state between chunks, 64 KB per memory) lives
+ * in a static device array of the library: at most ATLASMEM_STATIC_MAX_MEMORIES memories (8 MB per
+ * device, held from the first call on a device until the process ends).  Nothing is allocated;
+ * the first call on a device looks the array's address up once.  Every call on one GPU shares that
+ * array, so calls that overlap on one GPU (concurrent streams or threads) race and must be
+ * serialised by the caller. */
+#define ATLASMEM_STATIC_MAX_MEMORIES 128
+atlasmem_status atlasmem_update_chunked_static(const atlasmem_config* cfg, const void* K, const void* Q,
+                                               const void* V, const float* theta, const float* eta,
+                                               const float* alpha, int64_t T, float* W, float* S, void* Y,
+                                               int32_t* nonfinite, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * Stand-alone stages of the path (the same kernels the update runs), for callers that
  * want one stage and for measuring each against its own roofline.  Device pointers,

@@ -32,8 +32,9 @@ EXPORTS = (
     "atlasmem_reset_history", "atlasmem_destroy", "atlasmem_gate_scan", "atlasmem_omega_coeffs",
     "atlasmem_poly_features", "atlasmem_newton_schulz", "atlasmem_short_conv", "atlasmem_gates",
     "atlasmem_feature_map", "atlasmem_backward_workspace_bytes", "atlasmem_update_backward",
-    "atlasmem_calibrate_mfma", "atlasmem_calibrate_copy",
+    "atlasmem_calibrate_mfma", "atlasmem_calibrate_copy", "atlasmem_update_chunked_static",
 )
+STATIC_MAX_MEMORIES = 128
 
 
 class Config(ctypes.Structure):
@@ -94,6 +95,7 @@ def load():
         "atlasmem_update_backward": ([_vp] * 8 + [_i64] + [_vp] * 5 + [_i64] + [_vp] * 10, ctypes.c_int),
         "atlasmem_calibrate_mfma": ([_i64, _i32, _vp, _vp], ctypes.c_int),
         "atlasmem_calibrate_copy": ([_vp, _vp, _i64, _vp], ctypes.c_int),
+        "atlasmem_update_chunked_static": ([ctypes.POINTER(Config)] + [_vp] * 6 + [_i64] + [_vp] * 5, ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -231,6 +233,15 @@ def newton_schulz(G, n_mat: int, rows: int, cols: int, steps: int, coeffs, eps: 
     a, b, c = coeffs
     _check(load().atlasmem_newton_schulz(_ptr(G), n_mat, rows, cols, steps, a, b, c, eps, precision, _ptr(out),
                                          _stream(stream)), "atlasmem_newton_schulz")
+
+
+def update_chunked_static(cfg: Config, K, Q, V, theta, eta, alpha, T: int, W, S, Y=None, nonfinite=None,
+                          stream=None):
+    """The allocation-free update (no handle): W, S updated in place; returns the status."""
+    return _check(load().atlasmem_update_chunked_static(ctypes.byref(cfg), _ptr(K), _ptr(Q), _ptr(V), _ptr(theta),
+                                                        _ptr(eta), _ptr(alpha), T, _ptr(W), _ptr(S), _ptr(Y),
+                                                        _ptr(nonfinite), _stream(stream)),
+                  "atlasmem_update_chunked_static")
 
 
 def calibrate_mfma(iters: int, n_workgroups: int, sink, stream=None):

@@ -361,6 +361,24 @@ static atlasmem_status stream_rows(Handle* h, const void* Q, const void* K, cons
 
 extern "C" {
 
+atlasmem_status atlasmem_update_chunked_static(const atlasmem_config* cfg, const void* K, const void* Q,
+                                               const void* V, const float* theta, const float* eta,
+                                               const float* alpha, int64_t T, float* W, float* Sm, void* Y,
+                                               int32_t* nonfinite, void* stream) {
+  const atlasmem_status v = validate(cfg);
+  if (v != ATLASMEM_OK) return v;
+  const Dims d = make_dims(cfg);
+  if (cfg->flags != 0 || !fused_supported(d)) return ATLASMEM_E_UNSUPPORTED;
+  if (d.M > fused_static_max_memories()) return ATLASMEM_E_SHAPE;
+  if (T < 0 || !W || !Sm) return ATLASMEM_E_INVALID;
+  if (T % d.C != 0) return ATLASMEM_E_SHAPE;
+  if (T == 0) return ATLASMEM_OK;
+  if (!K || !V || !theta || !eta || !alpha || (Y && !Q)) return ATLASMEM_E_INVALID;
+  if (T > INT64_MAX / d.C) return ATLASMEM_E_SHAPE;
+  return launch_fused_static(d, K, Q, V, theta, eta, alpha, Span{T, T, T / d.C}, Y, W, Sm, (int*)nonfinite,
+                             S(stream));
+}
+
 atlasmem_status atlasmem_update_chunked(atlasmem_handle hh, const void* K, const void* Q, const void* V,
                                         const float* theta, const float* eta, const float* alpha, const float* gamma,
                                         int64_t T, void* Y, void* stream) {

@@ -189,6 +189,12 @@ atlasmem_status launch_ns_groups(const float* G, int64_t ldG_mat, int n_mat, int
                                  float a, float b, float c, float eps, int prec, const NsUpdate& upd,
                                  hipStream_t st);
 bool fused_supported(const Dims& d);
+// The fused update without a handle and without allocating: the caller's W, S ([M, P]) updated in
+// place, the kernel's scratch in a static device array (k_fused.hip).
+int fused_static_max_memories();
+atlasmem_status launch_fused_static(const Dims& d, const void* K, const void* Q, const void* V, const float* theta,
+                                    const float* eta, const float* alpha, const Span& sp, void* Y, float* W, float* S,
+                                    int* nonfinite, hipStream_t st);
 atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
                              const float* theta, const float* eta, const float* alpha, const Span& sp, void* Y,
                              hipStream_t st);

@@ -34,6 +34,10 @@
 //    partials through LDS, so that set 0 holds all of G1 and set 1 all of G2; each set then
 //    orthogonalises and applies its own matrix, and the new W1 slices pass from set 0 to set 1
 //    through LDS.
+#include <string.h>
+
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
@@ -837,9 +841,15 @@ bool fused_supported(const Dims& d) {
          d.split && !(d.residual && d.out_bf16);
 }
 
-atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
-                             const float* theta, const float* eta, const float* alpha, const Span& sp, void* Y,
-                             hipStream_t st) {
+// The fused kernel sequence over sp.T tokens (a whole number of chunks).  The state moves from
+// (Wb[cur], Sb[cur]) to (Wb[1 - cur], Sb[1 - cur]) in each launch segment and `cur` flips with it;
+// Wb[0] == Wb[1] (and Sb likewise) updates the state in place, which the kernel allows: every
+// state element it writes was read earlier by the same lane, or before a workgroup barrier that
+// precedes the write.  T2: per memory 2 x 64 x 128 floats of scratch; flag: the non-finite flag.
+static atlasmem_status launch_fused_bufs(const Dims& d, const void* K, const void* Q, const void* V,
+                                         const float* theta, const float* eta, const float* alpha, const Span& sp,
+                                         void* Y, float* const Wb[2], float* const Sb[2], int& cur, float* T2,
+                                         int* flag, hipStream_t st) {
   const void* kern = d.residual ? (const void*)fz::fused_ns_kernel<true> : (const void*)fz::fused_ns_kernel<false>;
   if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, fz::LDS_BYTES) != hipSuccess)
     return ATLASMEM_E_DEVICE;
@@ -861,11 +871,11 @@ atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void
     a.ld_gate = sp.ldg;
     a.C = d.C;
     a.nchunks = (int)nc;
-    a.Win = h->W[h->cur];
-    a.Sin = h->S[h->cur];
-    a.Wout = h->W[1 - h->cur];
-    a.Sout = h->S[1 - h->cur];
-    a.T2 = h->G;
+    a.Win = Wb[cur];
+    a.Sin = Sb[cur];
+    a.Wout = Wb[1 - cur];
+    a.Sout = Sb[1 - cur];
+    a.T2 = T2;
     a.Y = Y ? (void*)((char*)Y + t0 * fz::D * ysz) : nullptr;
     a.out_bf16 = d.out_bf16;
     a.ns_steps = d.ns_steps;
@@ -873,11 +883,11 @@ atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void
     a.ns_b = d.ns_b;
     a.ns_c = d.ns_c;
     a.ns_eps = d.ns_eps;
-    a.flag = h->flag;
+    a.flag = flag;
     if (d.residual) hipLaunchKernelGGL(fz::fused_ns_kernel<true>, dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
     else hipLaunchKernelGGL(fz::fused_ns_kernel<false>, dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
     AM_LAUNCH_CHECK();
-    h->cur = 1 - h->cur;
+    cur = 1 - cur;
   }
   if (d.residual && Y && sp.T > 0) {
     const int64_t n = sp.T * fz::D;  // a whole number of 8-element groups (D = 64)
@@ -886,6 +896,76 @@ atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void
     AM_LAUNCH_CHECK();
   }
   return ATLASMEM_OK;
+}
+
+atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
+                             const float* theta, const float* eta, const float* alpha, const Span& sp, void* Y,
+                             hipStream_t st) {
+  return launch_fused_bufs(d, K, Q, V, theta, eta, alpha, sp, Y, h->W, h->S, h->cur, h->G, h->flag, st);
+}
+
+// ---------------------------------------------------------------------------- no allocation
+//
+// For callers that cannot allocate: the same kernel with the caller's state updated in place and
+// its per-memory scratch (the W2 half of the state between the chunks of a launch) in this static
+// device array, 64 KB per memory for at most kStaticMaxMem memories (8 MB) plus a flag word.  Each
+// device holds its own copy until the process ends; its address is looked up once per device.
+
+namespace fz {
+constexpr int kStaticMaxMem = ATLASMEM_STATIC_MAX_MEMORIES;
+constexpr int64_t kStaticFloats = (int64_t)kStaticMaxMem * 2 * P2 + 64;
+constexpr int kMaxDevices = 64;
+
+__global__ void zero_flag_kernel(int* f) { f[0] = 0; }
+}  // namespace fz
+
+static __device__ __align__(256) float scratch[fz::kStaticFloats];
+
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch[fz::kMaxDevices];       // device address of `scratch`, per device
+bool g_scratch_gfx950[fz::kMaxDevices];  // the device is a gfx950
+}  // namespace
+
+// The device address of this device's copy of `scratch` (set up on the first call on a device).
+static atlasmem_status static_scratch(int dev, float** out) {
+  if (dev < 0 || dev >= fz::kMaxDevices) return ATLASMEM_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATLASMEM_E_DEVICE;
+    g_scratch_gfx950[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (!g_scratch_gfx950[dev]) return ATLASMEM_E_DEVICE;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATLASMEM_E_DEVICE;
+    g_scratch[dev] = (float*)p;
+  }
+  *out = g_scratch[dev];
+  return ATLASMEM_OK;
+}
+
+int fused_static_max_memories() { return fz::kStaticMaxMem; }
+
+atlasmem_status launch_fused_static(const Dims& d, const void* K, const void* Q, const void* V, const float* theta,
+                                    const float* eta, const float* alpha, const Span& sp, void* Y, float* W, float* S,
+                                    int* nonfinite, hipStream_t st) {
+  if (d.M > fz::kStaticMaxMem) return ATLASMEM_E_SHAPE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ATLASMEM_E_DEVICE;
+  float* base = nullptr;
+  const atlasmem_status s = static_scratch(dev, &base);
+  if (s != ATLASMEM_OK) return s;
+  // the flag: the caller's word (cleared by a small kernel, so the call also records into a
+  // captured graph), or the scratch's last word, which nothing reads
+  int* flag = nonfinite ? (int*)nonfinite : (int*)(base + fz::kStaticFloats - 1);
+  if (nonfinite) {
+    hipLaunchKernelGGL(fz::zero_flag_kernel, dim3(1), dim3(1), 0, st, flag);
+    AM_LAUNCH_CHECK();
+  }
+  float* Wb[2] = {W, W};
+  float* Sb[2] = {S, S};
+  int cur = 0;
+  return launch_fused_bufs(d, K, Q, V, theta, eta, alpha, sp, Y, Wb, Sb, cur, base, flag, st);
 }
 
 }  // namespace am
