@@ -380,6 +380,49 @@ def stage_rooflines(torch, am, synth, dev, stream, only=None, cpu=False):
         cases += [("update_general_ns5",) + ug[:2] + ("mfma",) + ug[2:],
                   ("update_residual_ns5",) + ur[:2] + ("mfma",) + ur[2:],
                   ("update_gated_ns5",) + ugt[:2] + ("mfma",) + ugt[2:]]
+    # the short convolution of K, Q, V before the update: three stand-alone convolutions writing the
+    # convolved rows, then the update reading them, against the update that convolves while it
+    # stages its operands (atlasmem_update_chunked_conv), both on the general per-product path, at
+    # the Newton-Schulz workload's shape over 4096 tokens (keys and queries L2-normalised)
+    if only is None or only in ("conv_then_update", "conv_folded_update"):
+        ci = synth.make_inputs(4, "literal", T=4096, norm_k=False)
+        cs = ci.spec
+        ctaps, cvbias = synth.make_conv_params(4, cs.heads, cs.d_key, cs.d_value)
+        ccfg = am.make_config(kind=cs.kind, batch=cs.batch, heads=cs.heads, d_key=cs.d_key, d_value=cs.d_value,
+                              d_hidden=cs.d_hidden, chunk=cs.chunk, gate_mode=cs.gate_mode, ns_steps=cs.ns_steps,
+                              input_dtype=cs.input_dtype, flags=am.FLAG_NO_FUSED)
+        W0c, S0c = torch.from_numpy(ci.W0).to(dev), torch.from_numpy(ci.S0).to(dev)
+        cmem = am.Memory(ccfg, W0c, S0c)
+        cd = {k: _dev(torch, getattr(ci, k), dev) for k in ("K", "Q", "V", "theta", "eta", "alpha")}
+        ctd = [torch.from_numpy(t).to(dev) for t in ctaps]
+        cbd = [torch.from_numpy(b).to(dev) for b in cvbias]
+        cconv = [torch.empty_like(cd[k]) for k in ("K", "Q", "V")]
+        Yc = torch.empty((cs.n_mem, cs.T, cs.d_value), dtype=torch.float32, device=dev)
+        ntok = cs.n_mem * cs.T
+
+        def conv_then_update():
+            cmem.set_state(W0c, S0c)
+            cmem.reset_history()
+            for x, o, tp, bs, d, l2 in ((cd["K"], cconv[0], ctd[0], cbd[0], cs.d_key, True),
+                                         (cd["Q"], cconv[1], ctd[1], cbd[1], cs.d_key, True),
+                                         (cd["V"], cconv[2], ctd[2], cbd[2], cs.d_value, False)):
+                am.short_conv(x, synth.BF16, cs.n_mem, cs.T, d, cs.heads, tp, bs, None, l2, o, synth.BF16)
+            cmem.update_chunked(cconv[0], cconv[1], cconv[2], cd["theta"], cd["eta"], cd["alpha"], None, cs.T, Yc)
+
+        def conv_folded_update():
+            cmem.set_state(W0c, S0c)
+            cmem.reset_history()
+            cmem.update_chunked_conv(cd["K"], cd["Q"], cd["V"], ctd, cbd, (True, True), cd["theta"], cd["eta"],
+                                     cd["alpha"], None, cs.T, Yc)
+        cwork = cs.n_mem * (cs.T // cs.chunk) * sum(mlp_flops_per_chunk(cs).values())
+        row = 2 * (2 * cs.d_key + cs.d_value)  # bf16 bytes of one token's K, Q, V rows
+        cases += [("conv_then_update", conv_then_update, cwork, "mfma",
+                   f"short convolution of K, Q, V (three launches, convolved rows written: {3 * ntok * row / 1e9:.3f} "
+                   f"GB of row traffic) then the update on the general path, {cs.n_mem} memories x {cs.T} tokens"),
+                  ("conv_folded_update", conv_folded_update, cwork, "mfma",
+                   f"the update convolving its K, Q, V rows while staging them (raw rows read by the update, "
+                   f"{ntok * row / 1e9:.3f} GB, plus 8 B of inverse norms per token; {2 * ntok * row / 1e9:.3f} GB of "
+                   f"row traffic saved), {cs.n_mem} memories x {cs.T} tokens")]
     # per-token retrieval at the per-token workload's shape (8 memories x 4096 tokens, chunk 64)
     if only is None or only == "update_per_token_retrieve":
         pi = synth.make_inputs(1, "stabilised", per_token_retrieve=True)

@@ -182,6 +182,37 @@ atlasmem_status atlasmem_update_chunked(atlasmem_handle h, const void* K, const 
                                         const float* theta, const float* eta, const float* alpha,
                                         const float* gamma, int64_t T, void* Y, void* stream);
 
+/* The causal short convolution of the keys, queries and values (kernel 4, depthwise, one filter per
+ * (head, channel); keys and queries optionally L2-normalised after it) folded into the update:
+ * Atlas-Torch README, Atlas Extensions table, "Short Convolution"; titans-pytorch-mlx README,
+ * Configuration table (use_conv, conv_kernel_size 4).  Tap j multiplies token t - 3 + j, exactly as
+ * atlasmem_short_conv below. */
+typedef struct atlasmem_short_conv_params_s {
+  const float* taps_k;  /* [heads, d_key, 4] fp32 (device, 16-byte aligned; likewise taps_q, v) */
+  const float* taps_q;  /* [heads, d_key, 4]                                                      */
+  const float* taps_v;  /* [heads, d_value, 4]                                                    */
+  const float* bias_k;  /* [heads, d_key] fp32 or NULL (zero); bias_q, bias_v likewise            */
+  const float* bias_q;
+  const float* bias_v;
+  int32_t l2norm_k;     /* 1: each convolved key row divided by max(its L2 norm, 1e-12)           */
+  int32_t l2norm_q;     /* the same for the query rows (values are never normalised)              */
+} atlasmem_short_conv_params;
+
+/* atlasmem_update_chunked on the convolved rows without writing them: given the RAW rows K, Q, V,
+ * the update reads conv(K), conv(Q), conv(V) (fp32 arithmetic, the normalisation, one rounding to
+ * input_dtype: the rows atlasmem_short_conv would produce) while staging each chunk's operands,
+ * so only a 4-byte inverse norm per key and query row passes through memory.  The handle carries
+ * the three raw rows before the next call of each tensor (zeros at the start of a sequence and
+ * after atlasmem_reset_history), so a sequence cut into calls gives the same result as one call.
+ * Scope: the 2-layer memories (plain, residual, gated) without per-token retrieval, d_key and
+ * d_value <= 512, calls of whole chunks with nothing pending (E_UNSUPPORTED otherwise); runs the
+ * general per-product path.  Arguments as atlasmem_update_chunked; Q is required; `conv` is a
+ * HOST pointer to the parameters.  Never allocates. */
+atlasmem_status atlasmem_update_chunked_conv(atlasmem_handle h, const void* K, const void* Q, const void* V,
+                                             const atlasmem_short_conv_params* conv, const float* theta,
+                                             const float* eta, const float* alpha, const float* gamma, int64_t T,
+                                             void* Y, void* stream);
+
 /* Applies the buffered tokens of an unfinished chunk (r = atlasmem_pending(h) > 0 of them) as
  * one final chunk of r tokens, e.g. at the end of a sequence; no-op when none are buffered.
  *   theta, eta, alpha: PER_CHUNK: fp32 [M, 1], the gates of that chunk; PER_TOKEN: ignored (the

@@ -33,6 +33,7 @@ EXPORTS = (
     "atlasmem_poly_features", "atlasmem_newton_schulz", "atlasmem_short_conv", "atlasmem_gates",
     "atlasmem_feature_map", "atlasmem_backward_workspace_bytes", "atlasmem_update_backward",
     "atlasmem_calibrate_mfma", "atlasmem_calibrate_copy", "atlasmem_update_chunked_static",
+    "atlasmem_update_chunked_conv",
 )
 STATIC_MAX_MEMORIES = 128
 
@@ -47,6 +48,12 @@ class Config(ctypes.Structure):
         ("input_dtype", ctypes.c_int32), ("output_dtype", ctypes.c_int32), ("precision", ctypes.c_int32),
         ("flags", ctypes.c_int32),
     ]
+
+
+class ConvParams(ctypes.Structure):
+    _fields_ = [("taps_k", ctypes.c_void_p), ("taps_q", ctypes.c_void_p), ("taps_v", ctypes.c_void_p),
+                ("bias_k", ctypes.c_void_p), ("bias_q", ctypes.c_void_p), ("bias_v", ctypes.c_void_p),
+                ("l2norm_k", ctypes.c_int32), ("l2norm_q", ctypes.c_int32)]
 
 
 class AtlasMemError(RuntimeError):
@@ -96,6 +103,8 @@ def load():
         "atlasmem_calibrate_mfma": ([_i64, _i32, _vp, _vp], ctypes.c_int),
         "atlasmem_calibrate_copy": ([_vp, _vp, _i64, _vp], ctypes.c_int),
         "atlasmem_update_chunked_static": ([ctypes.POINTER(Config)] + [_vp] * 6 + [_i64] + [_vp] * 5, ctypes.c_int),
+        "atlasmem_update_chunked_conv": ([_vp, _vp, _vp, _vp, ctypes.POINTER(ConvParams), _vp, _vp, _vp, _vp, _i64, _vp,
+                                          _vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -165,6 +174,17 @@ class Memory:
         _check(load().atlasmem_update_chunked(self._h, _ptr(K), _ptr(Q), _ptr(V), _ptr(theta), _ptr(eta),
                                               _ptr(alpha), _ptr(gamma), int(T), _ptr(Y), _stream(stream)),
                "atlasmem_update_chunked")
+
+    def update_chunked_conv(self, K, Q, V, taps, bias, l2norm, theta, eta, alpha, gamma, T: int, Y=None,
+                            stream=None):
+        """K, Q, V raw rows; taps = (taps_k, taps_q, taps_v) [heads, d, 4]; bias = (bias_k, bias_q,
+        bias_v) or None entries; l2norm = (keys, queries)."""
+        bias = bias or (None, None, None)
+        p = ConvParams(_ptr(taps[0]), _ptr(taps[1]), _ptr(taps[2]), _ptr(bias[0]), _ptr(bias[1]), _ptr(bias[2]),
+                       int(bool(l2norm[0])), int(bool(l2norm[1])))
+        _check(load().atlasmem_update_chunked_conv(self._h, _ptr(K), _ptr(Q), _ptr(V), ctypes.byref(p), _ptr(theta),
+                                                   _ptr(eta), _ptr(alpha), _ptr(gamma), int(T), _ptr(Y),
+                                                   _stream(stream)), "atlasmem_update_chunked_conv")
 
     def flush(self, theta=None, eta=None, alpha=None, stream=None):
         _check(load().atlasmem_flush(self._h, _ptr(theta), _ptr(eta), _ptr(alpha), _stream(stream)), "atlasmem_flush")

@@ -103,6 +103,7 @@ Dims make_dims(const atlasmem_config* c) {
   d.no_loop = (c->flags & ATLASMEM_FLAG_NO_CHUNK_LOOP) != 0;
   d.no_splitk = (c->flags & ATLASMEM_FLAG_NO_SPLIT_K) != 0;
   d.ptr = (c->flags & ATLASMEM_FLAG_PER_TOKEN_RETRIEVE) != 0;
+  d.conv = false;
   return d;
 }
 
@@ -185,9 +186,16 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
   const size_t opK = cv.take(esz * M * d.C * d.dk), opV = cv.take(esz * M * d.C * d.dv);
   const size_t opg = cv.take(sizeof(float) * M * d.C), opth = cv.take(sizeof(float) * M * d.C);
   const size_t opet = cv.take(sizeof(float) * M * d.C), opal = cv.take(sizeof(float) * M * d.C);
+  // the raw rows before the next call for the folded short convolution (zero: sequence start)
+  size_t ochk[2], ochq[2], ochv[2];
+  for (int i = 0; i < 2; ++i) {
+    ochk[i] = cv.take(esz * M * 3 * d.dk);
+    ochq[i] = cv.take(esz * M * 3 * d.dk);
+    ochv[i] = cv.take(esz * M * 3 * d.dv);
+  }
   const size_t state_end = cv.off;
   size_t oZ = 0, oD2 = 0, oD1 = 0, osk = 0, ocW = 0, ocS = 0, ooW = 0, ooS = 0, oscal = 0, oG = 0, oZr = 0;
-  size_t opZS = 0, opA1 = 0, opYB = 0, opbA = 0, opOm = 0;
+  size_t opZS = 0, opA1 = 0, opYB = 0, opbA = 0, opOm = 0, ocik = 0, ociq = 0;
   if (d.kind == ATLASMEM_MLP2_SILU) {
     oZ = cv.take(sizeof(float) * M * d.Rt * d.dz);
     oD2 = cv.take(sizeof(float) * M * d.Rk * d.dv);
@@ -212,6 +220,8 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
       }
     }
     if (d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0) oG = cv.take(sizeof(float) * M * d.P);
+    ocik = cv.take(sizeof(float) * M * (ncb * d.C + d.c - 1));
+    ociq = cv.take(sizeof(float) * M * ncb * d.C);
     int64_t rb = 1024;
     while (rb > 64 && (int64_t)M * rb * d.dz * 4 > ((int64_t)256 << 20)) rb /= 2;
     h->rb = (int)rb;
@@ -246,7 +256,19 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
   h->pet = (float*)(base + opet);
   h->pal = (float*)(base + opal);
   h->pending = 0;
+  for (int i = 0; i < 2; ++i) {
+    h->chk[i] = base + ochk[i];
+    h->chq[i] = base + ochq[i];
+    h->chv[i] = base + ochv[i];
+  }
+  h->chcur = 0;
+  h->conv = nullptr;
+  h->conv_v = nullptr;
+  h->cinvk = h->cinvq = nullptr;
+  h->cinv_t0k = h->cinv_t0q = 0;
   if (d.kind == ATLASMEM_MLP2_SILU) {
+    h->cinvk = (float*)(base + ocik);
+    h->cinvq = (float*)(base + ociq);
     h->Z = (float*)(base + oZ);
     h->D2 = (float*)(base + oD2);
     h->D1 = (float*)(base + oD1);
@@ -377,6 +399,46 @@ atlasmem_status atlasmem_update_chunked_static(const atlasmem_config* cfg, const
   if (T > INT64_MAX / d.C) return ATLASMEM_E_SHAPE;
   return launch_fused_static(d, K, Q, V, theta, eta, alpha, Span{T, T, T / d.C}, Y, W, Sm, (int*)nonfinite,
                              S(stream));
+}
+
+atlasmem_status atlasmem_update_chunked_conv(atlasmem_handle hh, const void* K, const void* Q, const void* V,
+                                             const atlasmem_short_conv_params* conv, const float* theta,
+                                             const float* eta, const float* alpha, const float* gamma, int64_t T,
+                                             void* Y, void* stream) {
+  Handle* h = (Handle*)hh;
+  if (!h || !conv || T < 0) return ATLASMEM_E_INVALID;
+  const Dims& d = h->d;
+  if (d.kind != ATLASMEM_MLP2_SILU || d.ptr) return ATLASMEM_E_UNSUPPORTED;
+  if (d.dk > 512 || d.dv > 512) return ATLASMEM_E_SHAPE;
+  if (h->pending != 0 || T % d.C != 0) return ATLASMEM_E_UNSUPPORTED;
+  if (T == 0) return ATLASMEM_OK;
+  if (!K || !Q || !V || !theta || !eta || !alpha) return ATLASMEM_E_INVALID;
+  if (!conv->taps_k || !conv->taps_q || !conv->taps_v) return ATLASMEM_E_INVALID;
+  // each channel's four taps are read as one 16-byte vector
+  if ((((uintptr_t)conv->taps_k) | ((uintptr_t)conv->taps_q) | ((uintptr_t)conv->taps_v)) & 15)
+    return ATLASMEM_E_INVALID;
+  if ((d.c > 1) != (gamma != nullptr)) return ATLASMEM_E_INVALID;
+  DeviceGuard g(h->device);
+  if (!g.ok) return ATLASMEM_E_DEVICE;
+  hipStream_t st = S(stream);
+  Dims dc = d;
+  dc.conv = true;
+  const atlasmem_short_conv_params params = *conv;
+  h->conv = &params;
+  h->conv_v = V;
+  atlasmem_status s = mlp_update(h, dc, K, Q, V, theta, eta, alpha, gamma,
+                                 Span{T, T, d.gate_mode == ATLASMEM_PER_TOKEN ? T : T / d.C}, Y, st);
+  h->conv = nullptr;
+  h->conv_v = nullptr;
+  if (s != ATLASMEM_OK) return s;
+  // the three raw rows of each tensor before the next call
+  const int nx = 1 - h->chcur;
+  if ((s = launch_conv_carry(K, h->chk[h->chcur], d.in_bf16, d.M, T, T, d.dk, h->chk[nx], st)) != ATLASMEM_OK ||
+      (s = launch_conv_carry(Q, h->chq[h->chcur], d.in_bf16, d.M, T, T, d.dk, h->chq[nx], st)) != ATLASMEM_OK ||
+      (s = launch_conv_carry(V, h->chv[h->chcur], d.in_bf16, d.M, T, T, d.dv, h->chv[nx], st)) != ATLASMEM_OK)
+    return s;
+  h->chcur = nx;
+  return ATLASMEM_OK;
 }
 
 atlasmem_status atlasmem_update_chunked(atlasmem_handle hh, const void* K, const void* Q, const void* V,
@@ -532,6 +594,11 @@ atlasmem_status atlasmem_reset_history(atlasmem_handle hh, void* stream) {
         hipMemsetAsync(h->hg[i], 0, sizeof(float) * d.M * H, st) != hipSuccess)
       return ATLASMEM_E_DEVICE;
   }
+  const size_t esz = d.in_bf16 ? 2 : 4;
+  if (hipMemsetAsync(h->chk[h->chcur], 0, esz * d.M * 3 * d.dk, st) != hipSuccess ||
+      hipMemsetAsync(h->chq[h->chcur], 0, esz * d.M * 3 * d.dk, st) != hipSuccess ||
+      hipMemsetAsync(h->chv[h->chcur], 0, esz * d.M * 3 * d.dv, st) != hipSuccess)
+    return ATLASMEM_E_DEVICE;
   h->pending = 0;  // a new sequence starts with a new chunk
   return ATLASMEM_OK;
 }

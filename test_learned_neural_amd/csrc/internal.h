@@ -30,6 +30,7 @@ struct Dims {
   bool no_fused;
   bool no_loop;  // one launch per product and chunk instead of the chunk-loop kernel
   bool no_splitk;  // every product over its whole k range in one launch
+  bool conv;       // this call's rows are convolved while they are read (update_chunked_conv)
 };
 
 // The token arrays of one launch sequence: T tokens; per memory, token stride `ld` of K, Q, V, Y,
@@ -49,6 +50,15 @@ atlasmem_status launch_ptr_coeffs(const float* theta, const float* eta, const fl
 int64_t feature_count_host(int d, int degree);
 atlasmem_status launch_feature_map(const void* X, bool in_bf16, int64_t n, int d, int degree, const float* c4,
                                    const float* P, int d_out, float* out, hipStream_t st);
+
+// Short convolution folded into the update (k_prologue.hip): inverse L2 norms of the convolved
+// rows [t0, t0 + n) of every memory (X token stride ld; taps / bias as atlasmem_short_conv), written
+// to inv[m * ld_inv + (t - t0)]; and the carried rows: hist_out = the last three of hist ++ X[0, T).
+atlasmem_status launch_conv_inv_norm(const void* X, const void* hist, bool in_bf16, int M, int64_t ld, int64_t t0,
+                                     int64_t n, int d, int heads, const float* taps, const float* bias, float* inv,
+                                     int64_t ld_inv, hipStream_t st);
+atlasmem_status launch_conv_carry(const void* X, const void* hist, bool in_bf16, int M, int64_t ld, int64_t T, int d,
+                                  void* hist_out, hipStream_t st);
 
 // Input prologue (k_prologue.hip)
 atlasmem_status launch_short_conv(const void* X, bool in_bf16, int64_t M, int64_t T, int d, int heads,
@@ -111,6 +121,18 @@ struct atlasmem_handle_s {
   float* pet;
   float* pal;
   int64_t pending;
+  // short convolution folded into the update (update_chunked_conv): the three raw rows before the
+  // next call of keys, queries and values ([M][3][d], input dtype, ping-pong), the inverse row
+  // norms of a block of chunks' keys (window rows included) and queries, and the call's taps
+  void* chk[2];
+  void* chq[2];
+  void* chv[2];
+  int chcur;
+  float* cinvk;  // [M][ncb * C + c - 1]
+  float* cinvq;  // [M][ncb * C]
+  const struct atlasmem_short_conv_params_s* conv;  // set during update_chunked_conv only
+  const void* conv_v;                                // the call's raw value rows (with conv)
+  int64_t cinv_t0k, cinv_t0q;                        // first token of cinvk / cinvq
 };
 
 namespace am {

@@ -15,6 +15,7 @@
 // summed gradient (delta^T @ activations): same page, MLX Optimizations, Gradient Computation.
 // The coefficient vectors cW, cS and the chunk scalars come from the gate scan / Omega kernels.
 #include "common.h"
+#include "conv_rows.h"
 #include "gemm.h"
 #include "internal.h"
 
@@ -289,6 +290,146 @@ struct EpiY {
   }
 };
 
+// ---------------------------------------------------------------------------- convolved rows
+//
+// The rows of a call to atlasmem_update_chunked_conv: K, Q, V hold raw rows that are convolved as
+// they are read (conv_rows.h); the window history rows are already convolved.  Separate types, so
+// that the plain loaders above keep their code.
+struct ConvRows {
+  FeatRows fr;
+  ConvTensor ck, cq, cv;
+  __device__ __forceinline__ float raw(int mem, int row, int i) const {
+    if (row < fr.Rk) {
+      const int64_t tau = fr.s - (fr.c - 1) + row;
+      if (tau >= 0) return ck.at(mem, fr.T, tau, i);
+      return fr.hk[((int64_t)mem * (fr.c - 1) + (fr.c - 1) + tau) * fr.dk + i];
+    }
+    return cq.at(mem, fr.T, fr.s + (row - fr.Rk), i);
+  }
+  __device__ __forceinline__ float feat(int mem, int row, int f) const {
+    if (f >= fr.din) return 0.0f;
+    if (fr.poly == 1) return raw(mem, row, f);
+    if (f == 0) return 1.0f;
+    if (f <= fr.dk) return raw(mem, row, f - 1);
+    int i, j;
+    pair_of(f - 1 - fr.dk, fr.dk, i, j);
+    return 0.5f * (raw(mem, row, i) * raw(mem, row, j));
+  }
+};
+// Eight convolved elements at once: channels i0..i0+7 of token tau (eight consecutive bf16 per row,
+// one 16-byte load per tap row), or channel i of tokens tau0..tau0+7 (a sliding window over eleven
+// rows).  Same multiply-adds in the same order as ConvTensor::at.
+__device__ __forceinline__ void conv_row8(const ConvTensor& ct, int m, int64_t ld, int64_t tau, int i0, float* v) {
+  const int h = m % ct.heads;
+  uint32_t w[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t2 = tau - 3 + j;
+    const uint16_t* src = t2 >= 0 ? (const uint16_t*)ct.X + ((int64_t)m * ld + t2) * ct.d + i0
+                                  : (const uint16_t*)ct.hist + ((int64_t)m * 3 + 3 + t2) * ct.d + i0;
+    const u32x4 q = *(const u32x4*)src;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w[j][p] = q[p];
+  }
+  const float4* tp = (const float4*)(ct.taps + ((int64_t)h * ct.d + i0) * 4);
+  const float sc = ct.inv ? ct.inv[(int64_t)m * ct.ninv + (tau - ct.t0)] : 1.0f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const float4 t4 = tp[u];
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = __uint_as_float((u & 1) ? (w[j][u >> 1] & 0xFFFF0000u) : (w[j][u >> 1] << 16));
+    float acc = ct.bias ? ct.bias[(int64_t)h * ct.d + i0 + u] : 0.0f;
+    acc = fmaf(t4.x, x[0], acc);
+    acc = fmaf(t4.y, x[1], acc);
+    acc = fmaf(t4.z, x[2], acc);
+    acc = fmaf(t4.w, x[3], acc);
+    if (ct.inv) acc *= sc;
+    v[u] = bf16_value(bf16_bits(acc));
+  }
+}
+__device__ __forceinline__ void conv_col8(const ConvTensor& ct, int m, int64_t ld, int64_t tau0, int i, float* v) {
+  const int h = m % ct.heads;
+  float x[11];
+#pragma unroll
+  for (int r = 0; r < 11; ++r) {
+    const int64_t t2 = tau0 - 3 + r;
+    x[r] = t2 >= 0 ? load_in(ct.X, ((int64_t)m * ld + t2) * ct.d + i, ct.in_bf16)
+                   : load_in(ct.hist, ((int64_t)m * 3 + 3 + t2) * ct.d + i, ct.in_bf16);
+  }
+  const float4 t4 = *(const float4*)(ct.taps + ((int64_t)h * ct.d + i) * 4);
+  const float b = ct.bias ? ct.bias[(int64_t)h * ct.d + i] : 0.0f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    float acc = b;
+    acc = fmaf(t4.x, x[u], acc);
+    acc = fmaf(t4.y, x[u + 1], acc);
+    acc = fmaf(t4.z, x[u + 2], acc);
+    acc = fmaf(t4.w, x[u + 3], acc);
+    if (ct.inv) acc *= ct.inv[(int64_t)m * ct.ninv + (tau0 + u - ct.t0)];
+    v[u] = ct.in_bf16 ? bf16_value(bf16_bits(acc)) : acc;
+  }
+}
+
+struct FeatAConv {
+  ConvRows cr;
+  __device__ __forceinline__ void load8(int z, int row, int f0, float* v) const {
+    const FeatRows& fr = cr.fr;
+    const int mem = z / fr.zdiv;
+    const bool rok = row < fr.nrows;
+    if (rok && fr.poly == 1 && fr.in_bf16 && (fr.dk & 7) == 0 && f0 + 8 <= fr.din) {
+      const bool key = row < fr.Rk;
+      const int64_t tau = key ? fr.s - (fr.c - 1) + row : fr.s + (row - fr.Rk);
+      const ConvTensor& ct = key ? cr.ck : cr.cq;
+      if (tau >= 0 && (((uintptr_t)ct.X) & 15) == 0) {  // rows of dk bf16 (dk % 8 == 0): 16-byte aligned
+        conv_row8(ct, mem, fr.T, tau, f0, v);
+        return;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = rok ? cr.feat(mem, row, f0 + u) : 0.0f;
+  }
+};
+struct FeatBConv {
+  ConvRows cr;
+  __device__ __forceinline__ void load8(int z, int f, int r0, float* v) const {
+    const FeatRows& fr = cr.fr;
+    const int mem = z / fr.zdiv;
+    if (fr.poly == 1 && f < fr.din && r0 + 8 <= fr.Rk && fr.s - (fr.c - 1) + r0 >= 0) {
+      conv_col8(cr.ck, mem, fr.T, fr.s - (fr.c - 1) + r0, f, v);  // eight key rows of this call
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (r0 + u < fr.nrows) ? cr.feat(mem, r0 + u, f) : 0.0f;
+  }
+};
+// EpiY on convolved rows: the key row's value and the residual input come from the convolution.
+// One element at a time (no two-phase gather): each value is a short chain of loads and
+// multiply-adds, and gathering sixteen of them at once spills.
+struct EpiYConv {
+  float* D2;
+  int64_t d2z;
+  const float* hv;
+  int64_t s;
+  int Rk, c, dv;
+  void* Y;
+  int out_bf16;
+  int residual;
+  ConvRows cr;
+  __device__ __forceinline__ void operator()(int z, int row, int col, float v) const {
+    if (residual) v += cr.feat(z, row, col);
+    if (row < Rk) {
+      const int64_t tau = s - (c - 1) + row;
+      const float vv = (tau >= 0) ? cr.cv.at(z, cr.fr.T, tau, col) : hv[((int64_t)z * (c - 1) + (c - 1) + tau) * dv + col];
+      D2[(int64_t)z * d2z + (int64_t)row * dv + col] = 2.0f * (v - vv);
+    } else if (Y) {
+      const int64_t yo = ((int64_t)z * cr.fr.T + s + (row - Rk)) * dv + col;
+      if (out_bf16) ((uint16_t*)Y)[yo] = (uint16_t)bf16_bits(v);
+      else ((float*)Y)[yo] = v;
+    }
+  }
+};
+
 // Per-token retrieval epilogues (rows = the chunk's queries t; bA = (beta_t, a_t)).
 // Zq = beta_t Z0 + a_t ZS - acc, in place in ZS: Z0 = the chunk-start first-layer product of the
 // queries (rows zr0.. of Z), ZS = their product with the chunk-start momentum.
@@ -513,6 +654,23 @@ static FeatRows feat_rows(const Handle* h, const void* K, const void* Q, int64_t
   fr.poly = d.poly;
   fr.zdiv = zdiv;
   return fr;
+}
+
+// The rows of a convolved call (h->conv set): FeatRows plus the three tensors' convolutions.
+static ConvRows conv_rows(const Handle* h, const void* K, const void* Q, int64_t ld, int64_t s, int Rk, int nrows,
+                          int zdiv) {
+  const Dims& d = h->d;
+  ConvRows cr;
+  cr.fr = feat_rows(h, K, Q, ld, s, Rk, nrows, zdiv);
+  const atlasmem_short_conv_params* p = h->conv;
+  const int heads = h->cfg.heads;
+  const int nk = h->ncb * d.C + d.c - 1, nq = h->ncb * d.C;
+  cr.ck = ConvTensor{K, h->chk[h->chcur], p->taps_k, p->bias_k, p->l2norm_k ? h->cinvk : nullptr, h->cinv_t0k, nk,
+                     heads, d.dk, d.in_bf16};
+  cr.cq = ConvTensor{Q, h->chq[h->chcur], p->taps_q, p->bias_q, p->l2norm_q ? h->cinvq : nullptr, h->cinv_t0q, nq,
+                     heads, d.dk, d.in_bf16};
+  cr.cv = ConvTensor{h->conv_v, h->chv[h->chcur], p->taps_v, p->bias_v, nullptr, 0, 0, heads, d.dv, d.in_bf16};
+  return cr;
 }
 
 // ---------------------------------------------------------------------------- per-token retrieval
@@ -762,7 +920,31 @@ static int64_t loop_chain(const Dims& d, bool with_y) {
 // workgroups: degree-2 features of 32-wide keys (72 steps) ran 2x slower in the loop, and the
 // 384 -> 768 -> 384 memory takes 324.
 static bool loop_supported(const Dims& d, bool with_y) {
-  return !d.no_loop && !d.ptr && d.prec != 2 && (d.gate_mode == ATLASMEM_PER_TOKEN || d.ns_steps == 0) && loop_chain(d, with_y) <= 24;
+  return !d.no_loop && !d.ptr && !d.conv && d.prec != 2 && (d.gate_mode == ATLASMEM_PER_TOKEN || d.ns_steps == 0) && loop_chain(d, with_y) <= 24;
+}
+
+// The window history of a call whose rows are convolved while read: the last c - 1 convolved keys
+// and values (and gammas) of (old history ++ this call), as the plain history kernel keeps them.
+__global__ void history_conv_kernel(ConvTensor ck, ConvTensor cv, const float* __restrict__ gamma, int M, int64_t T,
+                                    int64_t ld, int c, int dk, int dv, const float* __restrict__ hk,
+                                    const float* __restrict__ hv, const float* __restrict__ hg, float* __restrict__ nk,
+                                    float* __restrict__ nv, float* __restrict__ ng) {
+  const int H = c - 1;
+  const int width = dk + dv + 1;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * H * width) return;
+  const int e = (int)(idx % width);
+  const int hrow = (int)((idx / width) % H);
+  const int m = (int)(idx / ((int64_t)width * H));
+  const int64_t tau = T - H + hrow;
+  if (e < dk) {
+    nk[((int64_t)m * H + hrow) * dk + e] = tau >= 0 ? ck.at(m, ld, tau, e) : hk[((int64_t)m * H + hrow + T) * dk + e];
+  } else if (e < dk + dv) {
+    const int ev = e - dk;
+    nv[((int64_t)m * H + hrow) * dv + ev] = tau >= 0 ? cv.at(m, ld, tau, ev) : hv[((int64_t)m * H + hrow + T) * dv + ev];
+  } else {
+    ng[(int64_t)m * H + hrow] = tau >= 0 ? gamma[(int64_t)m * ld + tau] : hg[(int64_t)m * H + hrow + T];
+  }
 }
 
 atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* Q, const void* V, const float* theta,
@@ -778,10 +960,26 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
   const int64_t zsz = (int64_t)d.Rt * dz;
   const bool per_token = d.gate_mode == ATLASMEM_PER_TOKEN;
   atlasmem_status stt;
-  if (!d.no_fused && fused_supported(d)) return launch_fused(h, d, K, Q, V, theta, eta, alpha, sp, Y, st);
+  if (!d.no_fused && !d.conv && fused_supported(d)) return launch_fused(h, d, K, Q, V, theta, eta, alpha, sp, Y, st);
 
   for (int64_t kb0 = 0; kb0 < nchunks; kb0 += h->ncb) {
     const int nb = (int)((nchunks - kb0) < h->ncb ? (nchunks - kb0) : h->ncb);
+    if (d.conv) {  // inverse norms of the block's convolved key rows (window rows included) and queries
+      const atlasmem_short_conv_params* p = h->conv;
+      const int64_t tk0 = kb0 * C - (c - 1) > 0 ? kb0 * C - (c - 1) : 0, tk1 = (kb0 + nb) * C;
+      h->cinv_t0k = tk0;
+      h->cinv_t0q = kb0 * C;
+      if (p->l2norm_k) {
+        stt = launch_conv_inv_norm(K, h->chk[h->chcur], d.in_bf16, M, ld, tk0, tk1 - tk0, d.dk, h->cfg.heads, p->taps_k,
+                                   p->bias_k, h->cinvk, (int64_t)h->ncb * C + c - 1, st);
+        if (stt != ATLASMEM_OK) return stt;
+      }
+      if (p->l2norm_q && (Y || d.residual)) {
+        stt = launch_conv_inv_norm(Q, h->chq[h->chcur], d.in_bf16, M, ld, kb0 * C, (int64_t)nb * C, d.dk, h->cfg.heads,
+                                   p->taps_q, p->bias_q, h->cinvq, (int64_t)h->ncb * C, st);
+        if (stt != ATLASMEM_OK) return stt;
+      }
+    }
     if (per_token) {
       stt = launch_gate_scan(theta, eta, alpha, M, ld, kb0 * C, nb, C, h->cW, h->cS, (int64_t)h->ncb * C, h->scal,
                              (int64_t)h->ncb * 3, st);
@@ -850,10 +1048,14 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
 
       // Z = X W1^T over key rows (+ query rows); gated: [Z1 | Z3] = X [W1; W3]^T
       {
-        FeatA la{feat_rows(h, K, Q, ld, s, Rk, nrows, 1)};
         StridedLoader lb = strided(W1, d.P, din, 1, 1, dz, din);  // B(k=f, j=h) = W1[h][f]
         EpiStore ep{h->Z, zsz, dz, 1};
-        gemm_any(split, feat_exact, false, nrows, dz, din, M, la, lb, ep, st, h);
+        if (d.conv)
+          gemm_any(split, feat_exact, false, nrows, dz, din, M, FeatAConv{conv_rows(h, K, Q, ld, s, Rk, nrows, 1)}, lb,
+                   ep, st, h);
+        else
+          gemm_any(split, feat_exact, false, nrows, dz, din, M, FeatA{feat_rows(h, K, Q, ld, s, Rk, nrows, 1)}, lb, ep,
+                   st, h);
       }
       // Yh = H W2^T -> D2 (key rows), Y (query rows; with per-token retrieval they are answered
       // below from the per-token states instead)
@@ -861,9 +1063,15 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
       {
         StridedLoader la = hidden(d, h->Z, zsz, dz, 1, 1, yrows, dh);
         StridedLoader lb = strided(W2, d.P, dh, 1, 1, dv, dh);  // B(k=h, j=v) = W2[v][h]
-        EpiY ep{h->D2, (int64_t)Rk * dv, V, d.in_bf16, h->hv[h->hcur], ld, s, Rk, c, dv, Y, d.out_bf16,
-                d.residual, feat_rows(h, K, Q, ld, s, Rk, nrows, 1)};
-        gemm_any(split, false, false, yrows, dv, dh, M, la, lb, ep, st, h);
+        if (d.conv) {
+          EpiYConv ep{h->D2, (int64_t)Rk * dv, h->hv[h->hcur], s, Rk, c, dv, Y, d.out_bf16, d.residual,
+                      conv_rows(h, K, Q, ld, s, Rk, nrows, 1)};
+          gemm_any(split, false, false, yrows, dv, dh, M, la, lb, ep, st, h);
+        } else {
+          EpiY ep{h->D2, (int64_t)Rk * dv, V, d.in_bf16, h->hv[h->hcur], ld, s, Rk, c, dv, Y, d.out_bf16,
+                  d.residual, feat_rows(h, K, Q, ld, s, Rk, nrows, 1)};
+          gemm_any(split, false, false, yrows, dv, dh, M, la, lb, ep, st, h);
+        }
       }
       // Pm = D2 W2 -> D1 = Pm * silu'(Z)
       {
@@ -894,9 +1102,13 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
           la.coef0 = c0;
           la.coef1 = c1;
           la.cz = cz;
-          FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 2)};
           EpiUpdPair ep{Win, Sin, Wout, Sout, d.P, 0, din, sc, (int64_t)h->ncb * 3, h->flag};
-          gemm_any(split, false, feat_exact, dz, din, Rk, 2 * M, la, lb, ep, st, h);
+          if (d.conv)
+            gemm_any(split, false, feat_exact, dz, din, Rk, 2 * M, la, FeatBConv{conv_rows(h, K, Q, ld, s, Rk, Rk, 2)},
+                     ep, st, h);
+          else
+            gemm_any(split, false, feat_exact, dz, din, Rk, 2 * M, la, FeatB{feat_rows(h, K, Q, ld, s, Rk, Rk, 2)}, ep,
+                     st, h);
         }
       } else if (d.ns_steps == 0) {
         {
@@ -907,9 +1119,13 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
         }
         {
           StridedLoader la = strided(h->D1, (int64_t)Rk * dz, 1, dz, 1, dz, Rk);
-          FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)};
           EpiUpdChunk ep{Win, Sin, Wout, Sout, d.P, 0, din, theta, eta, alpha, sp.ldg, k, h->flag};
-          gemm_any(split, false, feat_exact, dz, din, Rk, M, la, lb, ep, st, h);
+          if (d.conv)
+            gemm_any(split, false, feat_exact, dz, din, Rk, M, la, FeatBConv{conv_rows(h, K, Q, ld, s, Rk, Rk, 1)}, ep,
+                     st, h);
+          else
+            gemm_any(split, false, feat_exact, dz, din, Rk, M, la, FeatB{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)}, ep, st,
+                     h);
         }
       } else {
         {
@@ -920,9 +1136,13 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
         }
         {
           StridedLoader la = strided(h->D1, (int64_t)Rk * dz, 1, dz, 1, dz, Rk);
-          FeatB lb{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)};
           EpiStore ep{h->G, d.P, din, 1};
-          gemm_any(split, false, feat_exact, dz, din, Rk, M, la, lb, ep, st, h);
+          if (d.conv)
+            gemm_any(split, false, feat_exact, dz, din, Rk, M, la, FeatBConv{conv_rows(h, K, Q, ld, s, Rk, Rk, 1)}, ep,
+                     st, h);
+          else
+            gemm_any(split, false, feat_exact, dz, din, Rk, M, la, FeatB{feat_rows(h, K, Q, ld, s, Rk, Rk, 1)}, ep, st,
+                     h);
         }
         // each weight matrix separately, W1, (W3,) W2, as groups of one launch
         const int64_t o3 = (int64_t)dh * din;
@@ -942,6 +1162,28 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
       AM_LAUNCH_CHECK();
       h->cur = 1 - h->cur;
     }
+  }
+  if (d.conv) {
+    if (c > 1 && T > 0) {
+      // the window history keeps convolved keys and values: the last c - 1 rows' norms, then the rows
+      const atlasmem_short_conv_params* p = h->conv;
+      const int64_t th0 = T - (c - 1) > 0 ? T - (c - 1) : 0;
+      h->cinv_t0k = th0;
+      if (p->l2norm_k) {
+        stt = launch_conv_inv_norm(K, h->chk[h->chcur], d.in_bf16, M, ld, th0, T - th0, d.dk, h->cfg.heads, p->taps_k,
+                                   p->bias_k, h->cinvk, (int64_t)h->ncb * C + c - 1, st);
+        if (stt != ATLASMEM_OK) return stt;
+      }
+      const ConvRows cr = conv_rows(h, K, Q, ld, 0, 0, 0, 1);
+      const int64_t total = (int64_t)M * (c - 1) * (d.dk + d.dv + 1);
+      const int src = h->hcur, dst = 1 - h->hcur;
+      hipLaunchKernelGGL(history_conv_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, cr.ck, cr.cv,
+                         gamma, M, T, ld, c, d.dk, d.dv, h->hk[src], h->hv[src], h->hg[src], h->hk[dst], h->hv[dst],
+                         h->hg[dst]);
+      AM_LAUNCH_CHECK();
+      h->hcur = 1 - h->hcur;
+    }
+    return ATLASMEM_OK;
   }
   stt = launch_history_update(h, K, V, gamma, T, ld, st);
   if (stt != ATLASMEM_OK) return stt;

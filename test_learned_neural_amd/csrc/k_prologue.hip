@@ -279,6 +279,95 @@ atlasmem_status launch_short_conv(const void* X, bool in_bf16, int64_t M, int64_
   return ATLASMEM_OK;
 }
 
+// ------------------------------------------------------------------------ convolution folded into the update
+//
+// The inverse L2 norm of each convolved row, for the update's loaders, which convolve the raw rows
+// as they read them (the convolved rows are never written: only this 4-byte factor per row).  The
+// lanes, channels and order of the multiply-adds and of the norm's reduction are those of
+// conv_kernel, so the loaders' rows equal the stand-alone convolution's bit for bit.
+__global__ void __launch_bounds__(256) conv_inv_norm_kernel(const void* __restrict__ X, const void* __restrict__ hist,
+                                                            int in_bf16, int64_t M, int64_t ld, int64_t t0, int64_t n,
+                                                            int d, int heads, int log_lpr, const float* __restrict__ taps,
+                                                            const float* __restrict__ bias, float* __restrict__ inv,
+                                                            int64_t ld_inv) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int lpr = 1 << log_lpr;
+  const int g = (int)(gid & (lpr - 1));
+  const int64_t row = gid >> log_lpr;  // (memory, token)
+  const bool valid = row < M * n;
+  const int64_t m = valid ? row / n : 0;
+  const int64_t t = t0 + (valid ? row % n : 0);
+  const int h = (int)(m % heads);
+  const int c0 = g * kConvCh;
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kConvCh; ++k) {
+    const int c = c0 + k;
+    const bool on = valid && c < d;
+    const int cc = on ? c : 0;
+    const float* tp = taps + ((int64_t)h * d + cc) * 4;
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t2 = t - 3 + j;
+      x[j] = !on ? 0.0f
+                 : (t2 >= 0 ? load_in(X, (m * ld + t2) * d + cc, in_bf16)
+                            : load_in(hist, (m * 3 + 3 + t2) * d + cc, in_bf16));
+    }
+    float acc = (on && bias) ? bias[(int64_t)h * d + cc] : 0.0f;
+    acc = fmaf(on ? tp[0] : 0.0f, x[0], acc);
+    acc = fmaf(on ? tp[1] : 0.0f, x[1], acc);
+    acc = fmaf(on ? tp[2] : 0.0f, x[2], acc);
+    acc = fmaf(on ? tp[3] : 0.0f, x[3], acc);
+    ss = fmaf(acc, acc, ss);
+  }
+  for (int off = 1; off < lpr; off <<= 1) ss += __shfl_xor(ss, off, 64);
+  if (valid && g == 0) inv[m * ld_inv + (t - t0)] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+}
+
+// The three rows before the next call's first token: the last three of hist ++ X[0, T).
+__global__ void conv_carry_kernel(const void* __restrict__ X, const void* __restrict__ hist, int esz, int64_t M,
+                                  int64_t ld, int64_t T, int d, void* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= M * 3 * d) return;
+  const int i = (int)(e % d);
+  const int r = (int)((e / d) % 3);
+  const int64_t m = e / (3 * (int64_t)d);
+  const int64_t tau = T - 3 + r;
+  if (esz == 2) {
+    const uint16_t v = tau >= 0 ? ((const uint16_t*)X)[(m * ld + tau) * d + i]
+                                : ((const uint16_t*)hist)[(m * 3 + 3 + tau) * d + i];
+    ((uint16_t*)out)[e] = v;
+  } else {
+    const float v = tau >= 0 ? ((const float*)X)[(m * ld + tau) * d + i] : ((const float*)hist)[(m * 3 + 3 + tau) * d + i];
+    ((float*)out)[e] = v;
+  }
+}
+
+atlasmem_status launch_conv_inv_norm(const void* X, const void* hist, bool in_bf16, int M, int64_t ld, int64_t t0,
+                                     int64_t n, int d, int heads, const float* taps, const float* bias, float* inv,
+                                     int64_t ld_inv, hipStream_t st) {
+  if (n <= 0 || M <= 0) return ATLASMEM_OK;
+  if (d < 1 || d > 512) return ATLASMEM_E_SHAPE;
+  int log_lpr = 0;
+  while ((1 << log_lpr) * kConvCh < d) ++log_lpr;
+  const int64_t threads = (int64_t)M * n << log_lpr;
+  hipLaunchKernelGGL(conv_inv_norm_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, X, hist,
+                     (int)in_bf16, (int64_t)M, ld, t0, n, d, heads, log_lpr, taps, bias, inv, ld_inv);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
+atlasmem_status launch_conv_carry(const void* X, const void* hist, bool in_bf16, int M, int64_t ld, int64_t T, int d,
+                                  void* hist_out, hipStream_t st) {
+  const int64_t n = (int64_t)M * 3 * d;
+  if (n == 0) return ATLASMEM_OK;
+  hipLaunchKernelGGL(conv_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, X, hist, in_bf16 ? 2 : 4,
+                     (int64_t)M, ld, T, d, hist_out);
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
 // ------------------------------------------------------------------------ gates
 
 constexpr int kGateCols = 64;    // output columns (gate, head) per pass

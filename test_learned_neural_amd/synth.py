@@ -308,3 +308,17 @@ def make_prologue_inputs(seed: int, B: int, H: int, T: int, d: int, d_model: int
         hist = f32_to_bf16_bits(hist)
     return PrologueInputs(X=X, hist=hist, taps=taps, bias=bias, U=f32_to_bf16_bits(U), Wg=Wg, bg=bg, scale=scale)
 
+
+
+def make_conv_params(seed: int, heads: int, d_key: int, d_value: int):
+    """Seeded short-convolution parameters for keys, queries and values: taps ~ N(0, 0.5^2)
+    [heads, d, 4] and biases ~ N(0, 0.1^2) [heads, d], fp32, drawn in the order taps_k, taps_q,
+    taps_v, bias_k, bias_q, bias_v."""
+    rng = np.random.default_rng(np.random.SeedSequence([2000 + seed, heads, d_key, d_value]))
+    tk = (0.5 * rng.standard_normal((heads, d_key, 4))).astype(np.float32)
+    tq = (0.5 * rng.standard_normal((heads, d_key, 4))).astype(np.float32)
+    tv = (0.5 * rng.standard_normal((heads, d_value, 4))).astype(np.float32)
+    bk = (0.1 * rng.standard_normal((heads, d_key))).astype(np.float32)
+    bq = (0.1 * rng.standard_normal((heads, d_key))).astype(np.float32)
+    bv = (0.1 * rng.standard_normal((heads, d_value))).astype(np.float32)
+    return (tk, tq, tv), (bk, bq, bv)
