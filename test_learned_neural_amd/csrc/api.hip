@@ -219,7 +219,8 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
         ooS = cv.take(sizeof(float) * M * ncb * d.Rk);
       }
     }
-    if (d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0) oG = cv.take(sizeof(float) * M * d.P);
+    // the per-chunk gradient (Newton-Schulz), or the fused kernels' transposed second-layer state
+    oG = cv.take(sizeof(float) * M * d.P);
     ocik = cv.take(sizeof(float) * M * (ncb * d.C + d.c - 1));
     ociq = cv.take(sizeof(float) * M * ncb * d.C);
     int64_t rb = 1024;

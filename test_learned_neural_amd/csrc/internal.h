@@ -211,6 +211,11 @@ atlasmem_status launch_ns_groups(const float* G, int64_t ldG_mat, int n_mat, int
                                  float a, float b, float c, float eps, int prec, const NsUpdate& upd,
                                  hipStream_t st);
 bool fused_supported(const Dims& d);
+// The fused kernel for per-token gates (the same memory, chunks of 64): chunks [kb0, kb0 + nb) of a
+// call, after the gate scan of that block of chunks.
+bool fused_pt_supported(const Dims& d);
+atlasmem_status launch_fused_pt(Handle* h, const Dims& d, const void* K, const void* Q, const void* V, int64_t kb0,
+                                int nb, int64_t ld, void* Y, hipStream_t st);
 // The fused update without a handle and without allocating: the caller's W, S ([M, P]) updated in
 // place, the kernel's scratch in a static device array (k_fused.hip).
 int fused_static_max_memories();

@@ -812,6 +812,472 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
 #undef AM_LANE_VARS
 }
 
+// ---------------------------------------------------------------------------- per-token gates
+//
+// The same memory with per-token gates and no orthogonalisation, chunks of exactly 64 tokens (one
+// double group per chunk).  The chunk's update is the coefficient form of the per-token recurrence
+// (titans-pytorch-mlx README, Core Equations, Eq. 13-14, with every gradient of the chunk at its
+// start weights: ATLAS summary, section 3.3):
+//   S_end = P S0 - sum_j cS_j g_j,   W_end = beta W0 + a_S S0 - sum_j cW_j g_j,
+// with cW, cS and (P, beta, a_S) from the gate scan.  The two weighted gradient sums are formed one
+// after the other from the same chunk activations, kept in registers: D1 and H of the set's rows
+// are weighted per row before their hi/lo split (G1^T = X^T (c D1), G2 = D2^T (c H)); each sum's
+// partials are swapped between the sets like the per-chunk kernel's, so that set 0 applies W1's
+// update and set 1 W2's.  The S sum comes first: S_end is stored at once and only S0 stays live
+// for the W update.
+struct PtArgs {
+  Args a;
+  const float* cW;    // chunk 0 of this launch, memory 0; memory m at + m * ld_c
+  const float* cS;
+  const float* scal;  // (P, beta, a_S) per chunk; memory m at + m * ld_s
+  int64_t ld_c, ld_s;
+};
+constexpr int PT_CF = LDS_U16 * 2 + 16 * 4;            // byte offset of the chunk's coefficients
+constexpr int PT_LDS_BYTES = PT_CF + (2 * GROWS + 4) * 4;
+static_assert(PT_LDS_BYTES <= 160 * 1024, "LDS");
+
+template <bool RES>
+__global__ void __launch_bounds__(NT) fused_pt_kernel(PtArgs pa) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
+  const Args& a = pa.a;
+  float* cf = (float*)((char*)sm + PT_CF);  // [cW of 64 rows | cS of 64 rows | P, beta, a_S]
+  const int m = blockIdx.x;
+  const int t0 = threadIdx.x;
+  const int w8 = __builtin_amdgcn_readfirstlane(t0 >> 6);
+  const int s = w8 >> 2, w = w8 & 3;
+#define AM_LANE_VARS                                                                \
+  const int t = opv(t0), lane = t & 63, hf = lane >> 5, l32 = lane & 31;          \
+  const int h_own = 32 * w + l32;                                                 \
+  (void)hf; (void)l32; (void)h_own
+  const int nT = a.nchunks * a.C;
+  const rsrc_t rK = make_rsrc(a.K + (int64_t)m * a.ldT * D, (uint32_t)nT * D * 2);
+  const rsrc_t rQ = (a.Y && a.Q) ? make_rsrc(a.Q + (int64_t)m * a.ldT * D, (uint32_t)nT * D * 2) : rK;
+  const rsrc_t rV = make_rsrc(a.V + (int64_t)m * a.ldT * D, (uint32_t)nT * D * 2);
+  const int ysz = a.out_bf16 ? 2 : 4;
+  const rsrc_t rY = make_rsrc(a.Y ? (const char*)a.Y + (int64_t)m * a.ldT * D * ysz : nullptr,
+                              a.Y ? (uint32_t)nT * D * ysz : 0u);
+  const float* Win = a.Win + (int64_t)m * P;
+  const float* Sin = a.Sin + (int64_t)m * P;
+  float* Wout = a.Wout + (int64_t)m * P;
+  float* Sout = a.Sout + (int64_t)m * P;
+  const int wth = opq(WTH), wtl = opq(WTL);
+  const int d2h = opq(D2H), d2l = opq(D2L), dth = opq(DTH), dtl = opq(DTL), xth = opq(XTH);
+  const int rb = opq(RB);
+
+  // prologue: W1 slice in registers, W2^T in LDS, set 1's transposed W2 state (as the per-chunk kernel)
+  u32x4 w1h[4], w1l[4];
+  {
+  AM_LANE_VARS;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    float v[8];
+    const float4 p0 = *(const float4*)(Win + (int64_t)h_own * D + 16 * ks + 4 * hf);
+    const float4 p1 = *(const float4*)(Win + (int64_t)h_own * D + 16 * ks + 8 + 4 * hf);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+    v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+    pack8(v, w1h[ks], w1l[ks]);
+  }
+  for (int e = t; e < D * HD; e += NT) {
+    const int vv = e / HD, hh = e % HD;
+    uint32_t hi, lo;
+    split_bf16(Win[P1 + e], hi, lo);
+    sm[wth + hh * LE + vv] = (uint16_t)hi;
+    sm[wtl + hh * LE + vv] = (uint16_t)lo;
+  }
+  if (s == 1) {
+    const rsrc_t rt2 = make_rsrc(a.T2 + (int64_t)m * 2 * P2, (uint32_t)(2 * P2 * 4));
+    const int vt = (h_own * D + 4 * hf) * 4;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float wv4[4], sv4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t o = P1 + (int64_t)(32 * tt + 8 * q + 4 * hf + u) * HD + h_own;
+          wv4[u] = Win[o];
+          sv4[u] = Sin[o];
+        }
+        buf_st4(rt2, vt, (32 * tt + 8 * q) * 4, float4{wv4[0], wv4[1], wv4[2], wv4[3]});
+        buf_st4(rt2, vt + P2 * 4, (32 * tt + 8 * q) * 4, float4{sv4[0], sv4[1], sv4[2], sv4[3]});
+      }
+  }
+  }
+  __syncthreads();
+
+  const bool withq = a.Y != nullptr;
+  auto load_x = [&](int k, u32x4 (&pq)[4], u32x4 (&pk)[4]) __attribute__((always_inline)) {
+    AM_LANE_VARS;
+    if (k >= a.nchunks) k = a.nchunks - 1;  // past the end of the launch: repeat the last loads
+    const int rset = (k * a.C + GR * s) * D * 2;
+    const int vx = (l32 * D + 4 * hf) * 2;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      pk[ks] = cat2(buf_ld8(rK, vx + 32 * ks, rset), buf_ld8(rK, vx + 32 * ks + 16, rset));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      pq[ks] = cat2(buf_ld8(rQ, vx + 32 * ks, rset), buf_ld8(rQ, vx + 32 * ks + 16, rset));
+  };
+
+  bool bad = false;
+  const int hq = opq(HQ);
+  // The chunk's rows: Z, H and Yh of queries and keys, Y of the queries, D2 (LDS), X^T (LDS);
+  // returns the keys' D1 (p) and H (hz) tiles of this set's rows, fp32.
+  auto run_group = [&](int k, u32x4 (&pq)[4], u32x4 (&pk)[4], f32x16& p, f32x16& hz) __attribute__((always_inline)) {
+    AM_LANE_VARS;
+    const int vcol = 16 * w + (lane & 15);
+    const int row0 = k * a.C;
+    const int rset = row0 + GR * s;
+    const u32x4 xt = buf_ld16(rK, ((t >> 3) * D + (t & 7) * 8) * 2, row0 * D * 2);
+    uint32_t vv[8];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int vo = (4 * (lane >> 4) * D + vcol) * 2 + u * D * 2, so = (rset + 16 * rt) * D * 2;
+        if (RES) {
+          v2u16 pr;
+          pr.x = __builtin_amdgcn_raw_buffer_load_b16(rV, vo, so, 0);
+          pr.y = __builtin_amdgcn_raw_buffer_load_b16(rK, vo, so, 0);
+          vv[4 * rt + u] = __builtin_bit_cast(uint32_t, pr);
+        } else {
+          vv[4 * rt + u] = buf_ld_u16(rV, vo, so);
+        }
+      }
+    f32x16 zk = zero16(), zq = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      zk = mfma32(pk[ks], w1h[ks], zk);
+      zk = mfma32(pk[ks], w1l[ks], zk);
+    }
+    if (withq) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        zq = mfma32(pq[ks], w1h[ks], zq);
+        zq = mfma32(pq[ks], w1l[ks], zq);
+      }
+    }
+    load_x(k + 1, pq, pk);
+    f32x16 zp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float sg = sigmoidf_(zk[r]);
+      hz[r] = zk[r] * sg;
+      zp[r] = sg * (1.0f + zk[r] * (1.0f - sg));
+    }
+#pragma unroll
+    for (int kl = 0; kl < 2; ++kl) {
+      u32x4 hh, hl;
+      tile_op(hz, kl, hh, hl);
+      store_rows(sm, rb, rb + HSZ, LH, hh, hl, GR * s + 16 * kl, h_own, hf);
+    }
+    if (withq) {
+      f32x16 hqz;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hqz[r] = zq[r] * sigmoidf_(zq[r]);
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl) {
+        u32x4 qh, ql;
+        tile_op(hqz, kl, qh, ql);
+        store_rows(sm, hq, hq + HSZ, LH, qh, ql, GR * s + 16 * kl, h_own, hf);
+      }
+    }
+    __syncthreads();
+    f32x4 yk[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 yq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      const int ob = ((lane >> 4) * 8 + ((lane >> 2) & 3)) * LE + 16 * w + 4 * (lane & 3);
+#pragma unroll
+      for (int ks = 0; ks < HD / 32; ++ks) {
+        const int o1 = ob + 32 * ks * LE, o2 = o1 + 4 * LE;
+        const u32x4 bh = cat2(lds_tr16(sm + wth + o1), lds_tr16(sm + wth + o2));
+        const u32x4 bl = cat2(lds_tr16(sm + wtl + o1), lds_tr16(sm + wtl + o2));
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const int oa = (GR * s + 16 * rt + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
+          yk[rt] = mma3_16(lds16(sm, rb + oa), lds16(sm, rb + HSZ + oa), bh, bl, yk[rt]);
+          if (withq) yq[rt] = mma3_16(lds16(sm, hq + oa), lds16(sm, hq + HSZ + oa), bh, bl, yq[rt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int rr = GR * s + 16 * rt + 4 * (lane >> 4);
+      float d2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t pv = vv[4 * rt + u];
+        d2[u] = RES ? 2.0f * (yk[rt][u] - (bf16_value(pv & 0xFFFFu) - __uint_as_float(pv & 0xFFFF0000u)))
+                    : 2.0f * (yk[rt][u] - bf16_value(pv));
+      }
+      uint32_t h0, l0, h1, l1;
+      split2(d2[0], d2[1], h0, l0);
+      split2(d2[2], d2[3], h1, l1);
+      const uint32_t hh[4] = {h0 & 0xFFFFu, h0 >> 16, h1 & 0xFFFFu, h1 >> 16};
+      const uint32_t ll[4] = {l0 & 0xFFFFu, l0 >> 16, l1 & 0xFFFFu, l1 >> 16};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sm[d2h + (rr + u) * LE + vcol] = (uint16_t)hh[u];
+        sm[d2l + (rr + u) * LE + vcol] = (uint16_t)ll[u];
+      }
+      *(uint2*)(sm + dth + vcol * LR + rr) = uint2{h0, h1};
+      *(uint2*)(sm + dtl + vcol * LR + rr) = uint2{l0, l1};
+    }
+    {
+      const int r = t >> 3, d0 = (t & 7) * 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sm[xth + (d0 + 2 * i) * LR + r] = (uint16_t)(xt[i] & 0xFFFFu);
+        sm[xth + (d0 + 2 * i + 1) * LR + r] = (uint16_t)(xt[i] >> 16);
+      }
+    }
+    if (withq) {
+      const int vy = 4 * (lane >> 4) * D + vcol;
+      if (a.out_bf16) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            buf_st_u16(rY, vy * 2 + u * D * 2, (rset + 16 * rt) * D * 2, bf16_bits(yq[rt][u]));
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) buf_st(rY, vy * 4 + u * D * 4, (rset + 16 * rt) * D * 4, yq[rt][u]);
+      }
+    }
+    __syncthreads();
+    p = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int o0 = (GR * s + l32) * LE + 16 * ks + 4 * hf;
+      const u32x4 ah = cat2(lds8(sm, d2h + o0), lds8(sm, d2h + o0 + 8));
+      const u32x4 al = cat2(lds8(sm, d2l + o0), lds8(sm, d2l + o0 + 8));
+      const int ob = h_own * LE + 16 * ks + 4 * hf;
+      const u32x4 bh = cat2(lds8(sm, wth + ob), lds8(sm, wth + ob + 8));
+      const u32x4 bl = cat2(lds8(sm, wtl + ob), lds8(sm, wtl + ob + 8));
+      p = mma3(ah, al, bh, bl, p);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] *= zp[r];
+  };
+
+  // One weighted gradient sum over this set's rows: G1^T += X^T (c D1), G2 += D2^T (c H), the row
+  // weights c from LDS (coefficient array `co`: 0 = cW, 64 = cS).
+  auto weighted_sum = [&](const f32x16& p, const f32x16& hz, int co, f32x16 (&gr)[2][2]) __attribute__((always_inline)) {
+    AM_LANE_VARS;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) gr[i][j] = zero16();
+#pragma unroll
+    for (int kl = 0; kl < 2; ++kl) {
+      // registers 8kl..8kl+7 hold rows GR s + 16kl + 4hf + 0..3 and GR s + 16kl + 8 + 4hf + 0..3
+      const float4 c0 = *(const float4*)(cf + co + GR * s + 16 * kl + 4 * hf);
+      const float4 c1 = *(const float4*)(cf + co + GR * s + 16 * kl + 8 + 4 * hf);
+      const float cr[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      float vd[8], vh[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        vd[e] = cr[e] * p[8 * kl + e];
+        vh[e] = cr[e] * hz[8 * kl + e];
+      }
+      u32x4 dh, dl, hh, hl;
+      pack8(vd, dh, dl);
+      pack8(vh, hh, hl);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int o0 = (32 * tt + l32) * LR + GR * s + 16 * kl + 4 * hf;
+        const u32x4 xa = cat2(lds8(sm, xth + o0), lds8(sm, xth + o0 + 8));
+        gr[0][tt] = mfma32(xa, dh, gr[0][tt]);
+        gr[0][tt] = mfma32(xa, dl, gr[0][tt]);
+        const u32x4 ah = cat2(lds8(sm, dth + o0), lds8(sm, dth + o0 + 8));
+        const u32x4 al = cat2(lds8(sm, dtl + o0), lds8(sm, dtl + o0 + 8));
+        gr[1][tt] = mma3(ah, al, hh, hl, gr[1][tt]);
+      }
+    }
+  };
+  // Swap the partial sums: set 0 ends with all of G1 (W1's sum), set 1 with all of G2.  The slots
+  // are free from the group's H W2^T on; `first` tells whether a previous swap's reads must be
+  // waited for.
+  auto swap_partials = [&](f32x16 (&gr)[2][2], f32x16 (&g)[2], bool first) __attribute__((always_inline)) {
+    AM_LANE_VARS;
+    float* xg1 = (float*)(sm + opq(XG1));
+    float* xg2 = (float*)(sm + opq(XG2));
+    if (!first) __syncthreads();
+    if (s == 0) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(float4*)(xg2 + (((w * 2 + tt) * 4 + q) * 64 + lane) * 4) =
+              float4{gr[1][tt][4 * q], gr[1][tt][4 * q + 1], gr[1][tt][4 * q + 2], gr[1][tt][4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(float4*)(xg1 + (((w * 2 + tt) * 4 + q) * 64 + lane) * 4) =
+              float4{gr[0][tt][4 * q], gr[0][tt][4 * q + 1], gr[0][tt][4 * q + 2], gr[0][tt][4 * q + 3]};
+    }
+    __syncthreads();
+    const float* src = s ? xg2 : xg1;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *(const float4*)(src + (((w * 2 + tt) * 4 + q) * 64 + lane) * 4);
+        const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) g[tt][4 * q + u] = (s ? gr[1][tt][4 * q + u] : gr[0][tt][4 * q + u]) + fv[u];
+      }
+  };
+
+  u32x4 pq[4], pk[4];
+  load_x(0, pq, pk);
+  for (int k = 0; k < a.nchunks; ++k) {
+    {  // the chunk's coefficients (the previous chunk's readers are past its last barrier)
+      AM_LANE_VARS;
+      if (t < GROWS) cf[t] = pa.cW[(int64_t)m * pa.ld_c + (int64_t)k * GROWS + t];
+      else if (t < 2 * GROWS) cf[t] = pa.cS[(int64_t)m * pa.ld_c + (int64_t)k * GROWS + (t - GROWS)];
+      else if (t < 2 * GROWS + 3) cf[t] = pa.scal[(int64_t)m * pa.ld_s + (int64_t)k * 3 + (t - 2 * GROWS)];
+    }
+    f32x16 p, hz;
+    run_group(k, pq, pk, p, hz);
+
+    // this set's state (W1[h_own][d] or the transposed W2[v][h_own] in T2), as the per-chunk kernel
+    const rsrc_t rt2 = make_rsrc(a.T2 + (int64_t)m * 2 * P2, (uint32_t)(2 * P2 * 4));
+    const float* Wsrc = (k == 0) ? Win : Wout;
+    const float* Ssrc = (k == 0) ? Sin : Sout;
+    const rsrc_t rs = s ? rt2 : make_rsrc(Ssrc, (uint32_t)(P * 4));
+    const rsrc_t rw = s ? rt2 : make_rsrc(Wsrc, (uint32_t)(P * 4));
+    float sv[2][16], wv[2][16];
+    {
+      AM_LANE_VARS;
+      const int vo1 = (h_own * D + 4 * hf) * 4;
+      const int vs = vo1 + (s ? P2 * 4 : 0);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 so = buf_ld4(rs, vs, (32 * tt + 8 * q) * 4);
+          sv[tt][4 * q] = so.x; sv[tt][4 * q + 1] = so.y; sv[tt][4 * q + 2] = so.z; sv[tt][4 * q + 3] = so.w;
+        }
+    }
+    const float cP = cf[2 * GROWS], cB = cf[2 * GROWS + 1], cA = cf[2 * GROWS + 2];
+    f32x16 gr[2][2], g[2];
+    // momentum: S_end = P S0 - sum_j cS_j g_j
+    weighted_sum(p, hz, GROWS, gr);
+    {
+      AM_LANE_VARS;
+      const int vo1 = (h_own * D + 4 * hf) * 4;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 wo = buf_ld4(rw, vo1, (32 * tt + 8 * q) * 4);
+          wv[tt][4 * q] = wo.x; wv[tt][4 * q + 1] = wo.y; wv[tt][4 * q + 2] = wo.z; wv[tt][4 * q + 3] = wo.w;
+        }
+    }
+    swap_partials(gr, g, true);
+    // S_end of this set's matrix, stored at once (W1 rows of set 0; set 1's W2 transposed in T2,
+    // or in [v][h] after the last chunk)
+    {
+      AM_LANE_VARS;
+      const bool last = k + 1 == a.nchunks;
+      float sn[2][16];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sn[tt][r] = fmaf(cP, sv[tt][r], -g[tt][r]);
+          if (last) bad |= !isfinite(sn[tt][r]);
+        }
+      const rsrc_t rs_out = make_rsrc(Sout, (uint32_t)(P * 4));
+      if (s == 0 || !last) {
+        const rsrc_t rs2 = s ? rt2 : rs_out;
+        const int vs = (h_own * D + 4 * hf) * 4 + (s ? P2 * 4 : 0);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            buf_st4(rs2, vs, (32 * tt + 8 * q) * 4,
+                    float4{sn[tt][4 * q], sn[tt][4 * q + 1], sn[tt][4 * q + 2], sn[tt][4 * q + 3]});
+      } else {
+        const int wo2 = ((int)P1 + 4 * hf * HD + h_own) * 4;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) buf_st(rs_out, wo2, (32 * tt + 8 * (r >> 2) + (r & 3)) * HD * 4, sn[tt][r]);
+      }
+    }
+    // weights: W_end = beta W0 + a_S S0 - sum_j cW_j g_j
+    weighted_sum(p, hz, 0, gr);
+    swap_partials(gr, g, false);
+    f32x16 x[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[tt][r] = fmaf(cB, wv[tt][r], fmaf(cA, sv[tt][r], -g[tt][r]));
+        if (k + 1 == a.nchunks) bad |= !isfinite(x[tt][r]);
+      }
+    // store W_end, hand the new W1 slices to set 1 (region A: D2, D2^T, X^T are dead, every wave
+    // read them last before the second swap's first barrier) and write the new W2^T operand copies
+    // (read last in the group's products), as the per-chunk kernel
+    u32x4* ho = (u32x4*)(sm + opq(HOFF));
+    {
+      AM_LANE_VARS;
+      const rsrc_t rw_out = make_rsrc(Wout, (uint32_t)(P * 4));
+      const bool last = k + 1 == a.nchunks;
+      const int wo1 = (h_own * D + 4 * hf) * 4, wo2 = ((int)P1 + 4 * hf * HD + h_own) * 4;
+      if (s == 0 || !last) {
+        const rsrc_t rw2 = s ? rt2 : rw_out;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            buf_st4(rw2, wo1, (32 * tt + 8 * q) * 4,
+                    float4{x[tt][4 * q], x[tt][4 * q + 1], x[tt][4 * q + 2], x[tt][4 * q + 3]});
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) buf_st(rw_out, wo2, (32 * tt + 8 * (r >> 2) + (r & 3)) * HD * 4, x[tt][r]);
+      }
+      if (s == 0) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          u32x4 wh, wl;
+          tile_op(x[ks >> 1], ks & 1, wh, wl);
+          ho[(w * 8 + ks) * 64 + lane] = wh;
+          ho[(w * 8 + 4 + ks) * 64 + lane] = wl;
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          u32x4 wh, wl;
+          tile_op(x[ks >> 1], ks & 1, wh, wl);
+          store_rows_T(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
+        }
+      }
+    }
+    __syncthreads();
+    {
+      AM_LANE_VARS;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        w1h[ks] = ho[(w * 8 + ks) * 64 + lane];
+        w1l[ks] = ho[(w * 8 + 4 + ks) * 64 + lane];
+      }
+    }
+    // the next chunk overwrites region A after its first barrier, which every wave reaches after
+    // these handoff reads
+  }
+  if (bad) a.flag[0] = 1;
+#undef AM_LANE_VARS
+}
+
 // The residual memory's retrieval adds the query to the fused kernel's output:
 // Y[m][t][v] += q[m][t][v] over the call's tokens (fp32 output; 8 elements per thread).
 __global__ void residual_output_kernel(const uint16_t* __restrict__ Q, float* __restrict__ Y, int64_t ld, int64_t n) {
@@ -893,6 +1359,61 @@ static atlasmem_status launch_fused_bufs(const Dims& d, const void* K, const voi
     const int64_t n = sp.T * fz::D;  // a whole number of 8-element groups (D = 64)
     hipLaunchKernelGGL(fz::residual_output_kernel, dim3((unsigned)((n / 8 + 255) / 256), d.M), dim3(256), 0, st,
                        (const uint16_t*)Q, (float*)Y, sp.ld * fz::D, n);
+    AM_LAUNCH_CHECK();
+  }
+  return ATLASMEM_OK;
+}
+
+bool fused_pt_supported(const Dims& d) {
+  return d.kind == ATLASMEM_MLP2_SILU && !d.gated && !d.ptr && !d.conv && !d.no_fused &&
+         d.gate_mode == ATLASMEM_PER_TOKEN && d.ns_steps == 0 && d.dk == fz::D && d.din == fz::D && d.dv == fz::D &&
+         d.dh == fz::HD && d.c == 1 && d.C == fz::GROWS && d.in_bf16 && d.split && !(d.residual && d.out_bf16);
+}
+
+// Chunks [kb0, kb0 + nb) of a call (tokens from kb0 * C, token stride ld), with the gate scan's
+// coefficients of these chunks at h->cW, h->cS, h->scal (chunk kb of the block at column kb).
+atlasmem_status launch_fused_pt(Handle* h, const Dims& d, const void* K, const void* Q, const void* V, int64_t kb0,
+                                int nb, int64_t ld, void* Y, hipStream_t st) {
+  const void* kern = d.residual ? (const void*)fz::fused_pt_kernel<true> : (const void*)fz::fused_pt_kernel<false>;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, fz::PT_LDS_BYTES) != hipSuccess)
+    return ATLASMEM_E_DEVICE;
+  const int64_t t0 = kb0 * d.C;
+  const int ysz = d.out_bf16 ? 2 : 4;
+  fz::PtArgs pa;
+  fz::Args& a = pa.a;
+  a.K = (const uint16_t*)K + t0 * fz::D;
+  a.Q = (const uint16_t*)Q + t0 * fz::D;
+  a.V = (const uint16_t*)V + t0 * fz::D;
+  a.theta = a.eta = a.alpha = nullptr;
+  a.ldT = ld;
+  a.ld_gate = 0;
+  a.C = d.C;
+  a.nchunks = nb;
+  a.Win = h->W[h->cur];
+  a.Sin = h->S[h->cur];
+  a.Wout = h->W[1 - h->cur];
+  a.Sout = h->S[1 - h->cur];
+  a.T2 = h->G;
+  a.Y = Y ? (void*)((char*)Y + t0 * fz::D * ysz) : nullptr;
+  a.out_bf16 = d.out_bf16;
+  a.ns_steps = 0;
+  a.ns_a = a.ns_b = a.ns_c = a.ns_eps = 0.0f;
+  a.flag = h->flag;
+  pa.cW = h->cW;
+  pa.cS = h->cS;
+  pa.scal = h->scal;
+  pa.ld_c = (int64_t)h->ncb * d.C;
+  pa.ld_s = (int64_t)h->ncb * 3;
+  if (d.residual)
+    hipLaunchKernelGGL(fz::fused_pt_kernel<true>, dim3(d.M), dim3(fz::NT), fz::PT_LDS_BYTES, st, pa);
+  else
+    hipLaunchKernelGGL(fz::fused_pt_kernel<false>, dim3(d.M), dim3(fz::NT), fz::PT_LDS_BYTES, st, pa);
+  AM_LAUNCH_CHECK();
+  h->cur = 1 - h->cur;
+  if (d.residual && Y) {
+    const int64_t n = (int64_t)nb * d.C * fz::D;
+    hipLaunchKernelGGL(fz::residual_output_kernel, dim3((unsigned)((n / 8 + 255) / 256), d.M), dim3(256), 0, st,
+                       (const uint16_t*)Q + t0 * fz::D, (float*)Y + t0 * fz::D, ld * fz::D, n);
     AM_LAUNCH_CHECK();
   }
   return ATLASMEM_OK;

@@ -990,6 +990,11 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
         if (stt != ATLASMEM_OK) return stt;
       }
     }
+    if (fused_pt_supported(d)) {
+      stt = launch_fused_pt(h, d, K, Q, V, kb0, nb, ld, Y, st);
+      if (stt != ATLASMEM_OK) return stt;
+      continue;
+    }
     if (loop_supported(d, Y != nullptr)) {
       LoopArgs la;
       la.d = d;

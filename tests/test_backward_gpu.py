@@ -71,10 +71,29 @@ def to_f64(a, dtype):
     return synth.bf16_bits_to_f32(a).astype(np.float64) if dtype == synth.BF16 else a.astype(np.float64)
 
 
+# The benchmark's backward shapes: every memory runs on the GPU, the oracle recomputes sampled ones
+# over the whole sequence (thousands of tokens, dozens of chunks).
+LARGE = [
+    ("bench_per_token_8x4096", 1, "stabilised", dict(), [0, 5]),
+    ("bench_ns5_128x4096", 4, "literal", dict(T=4096), [0, 77]),
+]
+
+
+@pytest.mark.parametrize("case", LARGE, ids=[c[0] for c in LARGE])
+def test_backward_at_benchmark_size_sampled(case):
+    name, idx, variant, ov, mems = case
+    _backward_case(name, idx, variant, ov, mems)
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_backward_matches_autograd_oracle(case):
-    import torch
     name, idx, variant, ov = case
+    _backward_case(name, idx, variant, ov, None)
+
+
+def _backward_case(name, idx, variant, ov, mems):
+    """The library's backward over every memory; the oracle over `mems` (None: all of them)."""
+    import torch
     log(f"CASE backward {name}")
     inp = synth.make_inputs(idx, variant, **ov)
     s = inp.spec
@@ -111,7 +130,8 @@ def test_backward_matches_autograd_oracle(case):
     ref = {k: [] for k in got}
     ref["W0"], ref["S0"] = [], []
     ys, wts = [], []
-    for m in range(M):
+    mems = list(range(M)) if mems is None else mems
+    for m in mems:
         P0 = oracle.unflatten(cfg, inp.W0[m].astype(np.float64))
         S0m = oracle.unflatten(cfg, inp.S0[m].astype(np.float64))
         g = bw.outer_grads(cfg, P0, S0m, K[m], Q[m], V[m], inp.theta[m], inp.eta[m], inp.alpha[m], dY[m],
@@ -127,14 +147,15 @@ def test_backward_matches_autograd_oracle(case):
         ys.append(res.Y)
         wts.append(oracle.flatten(res.params))
     for k, t in got.items():
-        errs[k] = maxrel(t.cpu().numpy(), np.stack(ref[k]))
-    errs["W0"] = maxrel(dW0.cpu().numpy(), np.stack(ref["W0"]))
-    errs["S0"] = maxrel(dS0.cpu().numpy(), np.stack(ref["S0"]))
-    errs["Y"] = maxrel(Y.cpu().numpy(), np.stack(ys))
-    errs["W_T"] = maxrel(W.cpu().numpy(), np.stack(wts))
+        errs[k] = maxrel(t.cpu().numpy()[mems], np.stack(ref[k]))
+    errs["W0"] = maxrel(dW0.cpu().numpy()[mems], np.stack(ref["W0"]))
+    errs["S0"] = maxrel(dS0.cpu().numpy()[mems], np.stack(ref["S0"]))
+    errs["Y"] = maxrel(Y.cpu().numpy()[mems], np.stack(ys))
+    errs["W_T"] = maxrel(W.cpu().numpy()[mems], np.stack(wts))
     label = lambda k: k if k in ("Y", "W_T") else "d" + k  # forward outputs, then gradients
     tol = F32_TOL if s.kind == synth.LINEAR else BF16_TOL  # the linear workload's fp32 bar
-    log(f"PARITY backward_{name}: " + " ".join(f"{label(k)}={v:.3e}" for k, v in errs.items()) + f" (tol {tol:g})")
+    log(f"PARITY backward_{name} (memories {mems}, T {T}): " + " ".join(f"{label(k)}={v:.3e}" for k, v in errs.items())
+        + f" (tol {tol:g})")
     assert all(v <= tol for v in errs.values()), errs
 
 

@@ -42,8 +42,10 @@ def test_chunk_loop_matches_per_product_launches(case):
     name, idx, variant, ov, splits, od, with_y = case
     log(f"CASE chunk loop {name}")
     inp = synth.make_inputs(idx, variant, **ov)
-    loop = run_gpu(inp, splits=splits, output_dtype=od, with_y=with_y)
-    launches = run_gpu(inp, splits=splits, output_dtype=od, with_y=with_y, flags=am.FLAG_NO_CHUNK_LOOP)
+    # (the 64 -> 128 -> 64 per-token memory would take the fused kernel by default)
+    loop = run_gpu(inp, splits=splits, output_dtype=od, with_y=with_y, flags=am.FLAG_NO_FUSED)
+    launches = run_gpu(inp, splits=splits, output_dtype=od, with_y=with_y,
+                       flags=am.FLAG_NO_CHUNK_LOOP | am.FLAG_NO_FUSED)
     assert loop[3] == am.OK and launches[3] == am.OK
     agree = {k: maxrel(a, b) for k, a, b in zip(("Y", "W", "S"), loop[:3], launches[:3]) if with_y or k != "Y"}
     bitwise = all(np.array_equal(a, b, equal_nan=True) for a, b in zip(loop[:3], launches[:3]))
