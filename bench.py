@@ -696,7 +696,7 @@ def main():
     # dominant kernel: the update call.  On the fused path it is one launch of the whole-call
     # kernel; on the general path it is the whole per-chunk launch sequence.
     fused = (s.kind == synth.MLP2_SILU and s.gate_mode == synth.PER_CHUNK and s.ns_steps > 0 and s.d_key == 64
-             and s.d_value == 64 and s.d_hidden == 128 and s.chunk % 64 == 0 and args.precision in (am.PREC_AUTO, am.PREC_BF16X3))
+             and s.d_value == 64 and s.d_hidden == 128 and s.chunk % 64 == 0 and args.precision in (am.PREC_AUTO, am.PREC_BF16X3, am.PREC_BF16))
     ach = step_flops / (upd_ms * 1e-3) / 1e12
     roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                 frac=round(ach / PEAK_BF16_TFLOPS, 5),

@@ -171,9 +171,22 @@ __device__ __forceinline__ f32x4 mma3_16(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl,
   c = mfma16(al, bh, c);
   return c;
 }
+// PL (the plain bf16 precision): every operand is its bf16 rounding (hi) alone, one product per
+// term; the lo words are neither formed nor stored.  Otherwise the three split products.
+template <bool PL>
+__device__ __forceinline__ f32x16 mmp(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x16 c) {
+  if constexpr (PL) return mfma32(ah, bh, c);
+  else return mma3(ah, al, bh, bl, c);
+}
+template <bool PL>
+__device__ __forceinline__ f32x4 mmp16(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+  if constexpr (PL) return mfma16(ah, bh, c);
+  else return mma3_16(ah, al, bh, bl, c);
+}
 
 // Write a 32x32 fp32 tile (rows r0.., cols c0..) transposed into an LDS matrix [col][row] as
 // hi/lo: four consecutive rows of a column are one 8-byte store.
+template <bool PL = false>
 __device__ __forceinline__ void store_tile_T(uint16_t* sm, int offh, int offl, int ld, const f32x16& t, int r0, int c0,
                                              int lane) {
   const int hf = lane >> 5, col = c0 + (lane & 31);
@@ -184,7 +197,7 @@ __device__ __forceinline__ void store_tile_T(uint16_t* sm, int offh, int offl, i
     split2(t[4 * q + 2], t[4 * q + 3], h1, l1);
     const int o = col * ld + r0 + 8 * q + 4 * hf;
     *(uint2*)(sm + offh + o) = uint2{h0, h1};
-    *(uint2*)(sm + offl + o) = uint2{l0, l1};
+    if constexpr (!PL) *(uint2*)(sm + offl + o) = uint2{l0, l1};
   }
 }
 
@@ -204,6 +217,7 @@ __device__ __forceinline__ void store_tile(uint16_t* sm, int offh, int offl, int
 
 // Store the packed operand words of one k-step (16 rows starting at r0, one column) into a
 // row-major LDS matrix [row][col]: word p holds rows r0 + 8(p/2) + 4h + 2(p%2) and the next.
+template <bool PL = false>
 __device__ __forceinline__ void store_rows(uint16_t* sm, int offh, int offl, int ld, const u32x4& hi, const u32x4& lo,
                                            int r0, int col, int hf) {
 #pragma unroll
@@ -211,18 +225,23 @@ __device__ __forceinline__ void store_rows(uint16_t* sm, int offh, int offl, int
     const int r = r0 + 8 * (p >> 1) + 4 * hf + 2 * (p & 1);
     sm[offh + r * ld + col] = (uint16_t)hi[p];
     sm[offh + (r + 1) * ld + col] = (uint16_t)(hi[p] >> 16);
-    sm[offl + r * ld + col] = (uint16_t)lo[p];
-    sm[offl + (r + 1) * ld + col] = (uint16_t)(lo[p] >> 16);
+    if constexpr (!PL) {
+      sm[offl + r * ld + col] = (uint16_t)lo[p];
+      sm[offl + (r + 1) * ld + col] = (uint16_t)(lo[p] >> 16);
+    }
   }
 }
 // The same k-step words into a transposed LDS matrix [col][row] (two 8-byte stores each).
+template <bool PL = false>
 __device__ __forceinline__ void store_rows_T(uint16_t* sm, int offh, int offl, int ld, const u32x4& hi,
                                              const u32x4& lo, int r0, int col, int hf) {
   const int o = col * ld + r0 + 4 * hf;
   *(uint2*)(sm + offh + o) = uint2{hi[0], hi[1]};
   *(uint2*)(sm + offh + o + 8) = uint2{hi[2], hi[3]};
-  *(uint2*)(sm + offl + o) = uint2{lo[0], lo[1]};
-  *(uint2*)(sm + offl + o + 8) = uint2{lo[2], lo[3]};
+  if constexpr (!PL) {
+    *(uint2*)(sm + offl + o) = uint2{lo[0], lo[1]};
+    *(uint2*)(sm + offl + o + 8) = uint2{lo[2], lo[3]};
+  }
 }
 
 // X^T element (c, r) of the Newton-Schulz buffer lives at c * 64 + (r ^ swz(c)): the XOR moves
@@ -250,7 +269,7 @@ struct Part {
 // pre(Part<p>) (p = 0..3) is called before iteration p: it issues the p-th quarter of the state
 // loads, so that they stream in under the matrix work instead of stalling the vector memory path
 // all at once.
-template <class Pre>
+template <bool PL, class Pre>
 __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int bxh, int bxl, int bah, int bal,
                                                int bbh, int bbl, float* red, const Args& a, int lane, int w,
                                                Pre&& pre) {
@@ -294,7 +313,7 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
         split2(x[t][4 * q + 2], x[t][4 * q + 3], h1, l1);
         const int o = opv(xrow + ((32 * t + 8 * q) ^ xsw));
         *(uint2*)(sm + bxh + o) = uint2{h0, h1};
-        *(uint2*)(sm + bxl + o) = uint2{l0, l1};
+        if constexpr (!PL) *(uint2*)(sm + bxl + o) = uint2{l0, l1};
       }
     __syncthreads();
     // A = X X^T, tile (rt, ct), k = the 128 columns in steps of 16 (natural order)
@@ -308,10 +327,10 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
         const u32x4 al = cat2(lds_tr16(sm + bxl + kb + (pa1 ^ f)), lds_tr16(sm + bxl + kb + (pa2 ^ f)));
         const u32x4 bh = cat2(lds_tr16(sm + bxh + kb + (pb1 ^ f)), lds_tr16(sm + bxh + kb + (pb2 ^ f)));
         const u32x4 bl = cat2(lds_tr16(sm + bxl + kb + (pb1 ^ f)), lds_tr16(sm + bxl + kb + (pb2 ^ f)));
-        A = mma3(ah, al, bh, bl, A);
+        A = mmp<PL>(ah, al, bh, bl, A);
       }
     }
-    store_tile_T(sm, bah, bal, LD, A, 32 * rt, 32 * ct, lane);
+    store_tile_T<PL>(sm, bah, bal, LD, A, 32 * rt, 32 * ct, lane);
     __syncthreads();
     // B = b A + c A^2, tile (rt, ct), accumulated in place of A as c (A^2 + (b/c) A)
     if (a.ns_c != 0.0f) {
@@ -323,7 +342,7 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
       for (int ks = 0; ks < D / 16; ++ks) {
         const int oa = ara + 16 * ks;
         const int ob = arb + 16 * ks;
-        A = mma3(lds16(sm, bah + oa), lds16(sm, bal + oa), lds16(sm, bah + ob), lds16(sm, bal + ob), A);
+        A = mmp<PL>(lds16(sm, bah + oa), lds16(sm, bal + oa), lds16(sm, bah + ob), lds16(sm, bal + ob), A);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) A[r] *= a.ns_c;
@@ -331,7 +350,7 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
 #pragma unroll
       for (int r = 0; r < 16; ++r) A[r] *= a.ns_b;
     }
-    store_tile_T(sm, bbh, bbl, LE, A, 32 * rt, 32 * ct, lane);
+    store_tile_T<PL>(sm, bbh, bbl, LE, A, 32 * rt, 32 * ct, lane);
     __syncthreads();
     // X = a X + B X: rows 0..63, columns 32w..32w+31; B X's k-operand X (rows of column cx in
     // the order 4hf..4hf+3, 8+4hf..8+4hf+3 of each k-step) comes back from X^T
@@ -351,7 +370,7 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
         const int o0 = brow + 32 * t * LE + 16 * ks;
         const u32x4 ah = cat2(lds8(sm, bbh + o0), lds8(sm, bbh + o0 + 8));
         const u32x4 al = cat2(lds8(sm, bbl + o0), lds8(sm, bbl + o0 + 8));
-        x[t] = mma3(ah, al, xh, xl, x[t]);
+        x[t] = mmp<PL>(ah, al, xh, xl, x[t]);
       }
     }
     // No barrier here: B X reads only the X^T rows of this lane's own column, which this lane
@@ -372,7 +391,7 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
 // key's own values enter the error, D2 = 2 (Yh - (V - x)); each V element register carries the
 // key element of the same position in its upper half.  The query's values are added to the
 // output after the launch (residual_output_kernel).
-template <bool RES>
+template <bool RES, bool PL>
 __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
   float* red = (float*)(sm + LDS_U16);
@@ -506,13 +525,13 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       zk = mfma32(pk[ks], w1h[ks], zk);
-      zk = mfma32(pk[ks], w1l[ks], zk);
+      if constexpr (!PL) zk = mfma32(pk[ks], w1l[ks], zk);
     }
     if (withq) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         zq = mfma32(pq[ks], w1h[ks], zq);
-        zq = mfma32(pq[ks], w1l[ks], zq);
+        if constexpr (!PL) zq = mfma32(pq[ks], w1l[ks], zq);
       }
     }
     if (g + 1 < ngroups) load_x(k, g + 1, pq, pk);
@@ -529,7 +548,7 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
 #pragma unroll
     for (int kl = 0; kl < 2; ++kl) {
       tile_op(hz, kl, hph[kl], hpl[kl]);
-      store_rows(sm, rb, rb + HSZ, LH, hph[kl], hpl[kl], GR * s + 16 * kl, h_own, hf);
+      store_rows<PL>(sm, rb, rb + HSZ, LH, hph[kl], hpl[kl], GR * s + 16 * kl, h_own, hf);
     }
     if (withq) {
 #pragma unroll
@@ -538,7 +557,7 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
       for (int kl = 0; kl < 2; ++kl) {
         u32x4 qh, ql;
         tile_op(hz, kl, qh, ql);
-        store_rows(sm, hq, hq + HSZ, LH, qh, ql, GR * s + 16 * kl, h_own, hf);
+        store_rows<PL>(sm, hq, hq + HSZ, LH, qh, ql, GR * s + 16 * kl, h_own, hf);
       }
     }
     __syncthreads();
@@ -557,8 +576,8 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
           const int oa = (GR * s + 16 * rt + (lane & 15)) * LH + 32 * ks + 8 * (lane >> 4);
-          yk[rt] = mma3_16(lds16(sm, rb + oa), lds16(sm, rb + HSZ + oa), bh, bl, yk[rt]);
-          if (withq) yq[rt] = mma3_16(lds16(sm, hq + oa), lds16(sm, hq + HSZ + oa), bh, bl, yq[rt]);
+          yk[rt] = mmp16<PL>(lds16(sm, rb + oa), lds16(sm, rb + HSZ + oa), bh, bl, yk[rt]);
+          if (withq) yq[rt] = mmp16<PL>(lds16(sm, hq + oa), lds16(sm, hq + HSZ + oa), bh, bl, yq[rt]);
         }
       }
     }
@@ -581,10 +600,10 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         sm[d2h + (rr + u) * LE + vcol] = (uint16_t)hh[u];
-        sm[d2l + (rr + u) * LE + vcol] = (uint16_t)ll[u];
+        if constexpr (!PL) sm[d2l + (rr + u) * LE + vcol] = (uint16_t)ll[u];
       }
       *(uint2*)(sm + dth + vcol * LR + rr) = uint2{h0, h1};
-      *(uint2*)(sm + dtl + vcol * LR + rr) = uint2{l0, l1};
+      if constexpr (!PL) *(uint2*)(sm + dtl + vcol * LR + rr) = uint2{l0, l1};
     }
     {  // X^T of the group for the G1 product
       const int r = t >> 3, d0 = (t & 7) * 8;
@@ -621,7 +640,7 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
       const int ob = h_own * LE + 16 * ks + 4 * hf;
       const u32x4 bh = cat2(lds8(sm, wth + ob), lds8(sm, wth + ob + 8));
       const u32x4 bl = cat2(lds8(sm, wtl + ob), lds8(sm, wtl + ob + 8));
-      p = mma3(ah, al, bh, bl, p);
+      p = mmp<PL>(ah, al, bh, bl, p);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] *= zp[r];
@@ -636,10 +655,10 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
         const int o0 = (32 * tt + l32) * LR + GR * s + 16 * kl + 4 * hf;
         const u32x4 xa = cat2(lds8(sm, xth + o0), lds8(sm, xth + o0 + 8));
         gr[0][tt] = mfma32(xa, dh, gr[0][tt]);
-        gr[0][tt] = mfma32(xa, dl, gr[0][tt]);
+        if constexpr (!PL) gr[0][tt] = mfma32(xa, dl, gr[0][tt]);
         const u32x4 ah = cat2(lds8(sm, dth + o0), lds8(sm, dth + o0 + 8));
         const u32x4 al = cat2(lds8(sm, dtl + o0), lds8(sm, dtl + o0 + 8));
-        gr[1][tt] = mma3(ah, al, hh, hl, gr[1][tt]);
+        gr[1][tt] = mmp<PL>(ah, al, hh, hl, gr[1][tt]);
       }
     }
     // No barrier here: the next group writes H after its X W1^T (every wave is past this
@@ -722,8 +741,8 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
     {
       AM_LANE_VARS;
       const int bxh = opq(NX + s * NXS), bah = opq(NA + s * NAS), bbh = opq(NB + s * NBS);
-      newton_schulz1(x, sm, bxh, bxh + HD * 64, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red + 4 * s, a, lane, w,
-                     pre);
+      newton_schulz1<PL>(x, sm, bxh, bxh + HD * 64, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red + 4 * s, a, lane,
+                         w, pre);
     }
     // S = eta S - theta NS(G), W = (1 - alpha) W + S for this set's matrix
 #pragma unroll
@@ -784,7 +803,7 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
         u32x4 wh, wl;
         tile_op(x[ks >> 1], ks & 1, wh, wl);
         ho[(w * 8 + ks) * 64 + lane] = wh;
-        ho[(w * 8 + 4 + ks) * 64 + lane] = wl;
+        if constexpr (!PL) ho[(w * 8 + 4 + ks) * 64 + lane] = wl;
       }
     }
     }
@@ -798,13 +817,13 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
         for (int ks = 0; ks < 4; ++ks) {
           u32x4 wh, wl;
           tile_op(x[ks >> 1], ks & 1, wh, wl);
-          store_rows_T(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
+          store_rows_T<PL>(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
         }
       }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         w1h[ks] = ho[(w * 8 + ks) * 64 + lane];
-        w1l[ks] = ho[(w * 8 + 4 + ks) * 64 + lane];
+        if constexpr (!PL) w1l[ks] = ho[(w * 8 + 4 + ks) * 64 + lane];
       }
     }
   }
@@ -1304,7 +1323,7 @@ __global__ void residual_output_kernel(const uint16_t* __restrict__ Q, float* __
 bool fused_supported(const Dims& d) {
   return d.kind == ATLASMEM_MLP2_SILU && !d.gated && d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0 && d.dk == fz::D &&
          d.din == fz::D && d.dv == fz::D && d.dh == fz::HD && d.c == 1 && d.C % fz::GROWS == 0 && d.in_bf16 &&
-         d.split && !(d.residual && d.out_bf16);
+         d.prec != 2 && !(d.residual && d.out_bf16);
 }
 
 // The fused kernel sequence over sp.T tokens (a whole number of chunks).  The state moves from
@@ -1316,7 +1335,9 @@ static atlasmem_status launch_fused_bufs(const Dims& d, const void* K, const voi
                                          const float* theta, const float* eta, const float* alpha, const Span& sp,
                                          void* Y, float* const Wb[2], float* const Sb[2], int& cur, float* T2,
                                          int* flag, hipStream_t st) {
-  const void* kern = d.residual ? (const void*)fz::fused_ns_kernel<true> : (const void*)fz::fused_ns_kernel<false>;
+  const bool pl = d.prec == 0;  // plain bf16 products
+  const void* kern = d.residual ? (pl ? (const void*)fz::fused_ns_kernel<true, true> : (const void*)fz::fused_ns_kernel<true, false>)
+                                : (pl ? (const void*)fz::fused_ns_kernel<false, true> : (const void*)fz::fused_ns_kernel<false, false>);
   if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, fz::LDS_BYTES) != hipSuccess)
     return ATLASMEM_E_DEVICE;
   // one launch per segment of at most 2^22 tokens, so that per-memory byte offsets fit 32 bits
@@ -1350,8 +1371,13 @@ static atlasmem_status launch_fused_bufs(const Dims& d, const void* K, const voi
     a.ns_c = d.ns_c;
     a.ns_eps = d.ns_eps;
     a.flag = flag;
-    if (d.residual) hipLaunchKernelGGL(fz::fused_ns_kernel<true>, dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
-    else hipLaunchKernelGGL(fz::fused_ns_kernel<false>, dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+    if (d.residual) {
+      if (pl) hipLaunchKernelGGL((fz::fused_ns_kernel<true, true>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+      else hipLaunchKernelGGL((fz::fused_ns_kernel<true, false>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+    } else {
+      if (pl) hipLaunchKernelGGL((fz::fused_ns_kernel<false, true>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+      else hipLaunchKernelGGL((fz::fused_ns_kernel<false, false>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+    }
     AM_LAUNCH_CHECK();
     cur = 1 - cur;
   }

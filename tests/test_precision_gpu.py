@@ -89,3 +89,17 @@ def test_f32_newton_schulz_stage():
         e = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
         log(f"PARITY ns_f32_{rows}x{cols}: {e:.3e}")
         assert e <= 1e-4
+
+
+@pytest.mark.xfail(reason="plain bf16 products (no lo terms) on the Newton-Schulz workload: the orthogonalisation "
+                          "feeds their rounding back into the state, far beyond the 2e-2 bar; the split products hold it",
+                   strict=False)
+def test_plain_bf16_fused_full_length_known_failure():
+    """The fused kernel with plain bf16 products (the benchmark's fast-mode line) over the whole
+    sequence of two memories, normalised keys: recorded, not hidden."""
+    inp = synth.make_inputs(4, "literal")
+    ref = oracle_run(inp, mems=MEMS)
+    got = _one_call(inp, am.PREC_BF16)
+    assert np.all(np.isfinite(got[0]))
+    errs = compare("ns5_plain_bf16_fused", inp.spec, got, ref, BF16_TOL)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
