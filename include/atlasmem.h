@@ -123,10 +123,12 @@ typedef struct {
 /* Per-token retrieval: Y[t] = M_{W_t}(phi(Q[t])) with W_t the state right after token t's
  * update, instead of the chunk-start weights (Atlas-Torch README, "Known deviations from the
  * paper's MAC": the Atlas configuration reads the post-update per-token state).  Per-token gates
- * only (E_UNSUPPORTED otherwise); update calls must then cover whole chunks with nothing pending
- * (E_UNSUPPORTED otherwise).  No per-token weights are formed: inside a chunk W_t is the
+ * only (E_UNSUPPORTED otherwise).  No per-token weights are formed: inside a chunk W_t is the
  * chunk-start state plus a masked sum of the chunk's rank-one gradients, so the queries are
- * answered through query-key score products. */
+ * answered through query-key score products.  Streaming calls (tokens of an unfinished chunk)
+ * are answered from the buffered rows of that chunk, which W_t depends on alone, so decoding
+ * equals one call (Atlas-Torch README, "Status and scope", limitation 4: the decode path must read
+ * the state the parallel path reads); for the LINEAR memory such calls return E_UNSUPPORTED. */
 #define ATLASMEM_FLAG_PER_TOKEN_RETRIEVE 2
 /* Run the chunks of a call as one separate launch per matrix product (five per chunk) instead of
  * the chunk-loop kernel, which walks every chunk of a block inside one launch with one workgroup

@@ -186,6 +186,9 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
   const size_t opK = cv.take(esz * M * d.C * d.dk), opV = cv.take(esz * M * d.C * d.dv);
   const size_t opg = cv.take(sizeof(float) * M * d.C), opth = cv.take(sizeof(float) * M * d.C);
   const size_t opet = cv.take(sizeof(float) * M * d.C), opal = cv.take(sizeof(float) * M * d.C);
+  // per-token retrieval: the unfinished chunk's queries and their answers
+  const size_t oesz = d.out_bf16 ? 2 : 4;
+  const size_t opQ = d.ptr ? cv.take(esz * M * d.C * d.dk) : 0, opYs = d.ptr ? cv.take(oesz * M * d.C * d.dv) : 0;
   // the raw rows before the next call for the folded short convolution (zero: sequence start)
   size_t ochk[2], ochq[2], ochv[2];
   for (int i = 0; i < 2; ++i) {
@@ -252,6 +255,8 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
   h->flag = (int*)(base + oflag);
   h->pK = base + opK;
   h->pV = base + opV;
+  h->pQ = d.ptr ? base + opQ : nullptr;
+  h->pYs = d.ptr ? base + opYs : nullptr;
   h->pg = (float*)(base + opg);
   h->pth = (float*)(base + opth);
   h->pet = (float*)(base + opet);
@@ -372,6 +377,26 @@ static atlasmem_status stream_rows(Handle* h, const void* Q, const void* K, cons
                                    const float* eta, const float* alpha, const float* gamma, int64_t ld, int64_t n,
                                    void* Y, hipStream_t st) {
   if (n == 0) return ATLASMEM_OK;
+  if (h->d.ptr) {
+    // per-token retrieval: each query reads the state right after its own token, which depends on
+    // the unfinished chunk's rows up to that token only, so the rows are buffered first and the
+    // buffered chunk's queries answered from them (the state is not updated until the chunk is
+    // complete); the new tokens' answers are copied out
+    const Dims& d = h->d;
+    const int64_t r0 = h->pending;
+    if (Q && !to_pending(h->pQ, Q, ld, r0, n, (d.in_bf16 ? 2 : 4) * (size_t)d.dk, d, st)) return ATLASMEM_E_DEVICE;
+    if (!append_pending(h, K, V, theta, eta, alpha, gamma, ld, n, st)) return ATLASMEM_E_DEVICE;
+    if (!Y) return ATLASMEM_OK;
+    const atlasmem_status s = ptr_partial_retrieve(h, h->pending, st);
+    if (s != ATLASMEM_OK) return s;
+    const size_t row = (d.out_bf16 ? 2 : 4) * (size_t)d.dv;
+    if (hipMemcpy2DAsync(Y, (size_t)ld * row, (const char*)h->pYs + r0 * row, (size_t)d.C * row, (size_t)n * row, d.M,
+                         hipMemcpyDeviceToDevice, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return ATLASMEM_E_DEVICE;
+    }
+    return ATLASMEM_OK;
+  }
   const atlasmem_status s = launch_decode(h, Q, K, V, theta, eta, alpha, gamma, ld, n, Y, true, st);
   if (s != ATLASMEM_E_UNSUPPORTED) return s;
   atlasmem_status r;
@@ -460,8 +485,8 @@ atlasmem_status atlasmem_update_chunked(atlasmem_handle hh, const void* K, const
   if (!g.ok) return ATLASMEM_E_DEVICE;
   hipStream_t st = S(stream);
   const int64_t ldg = per_token ? T : ncomp;
-  // per-token retrieval answers a chunk's queries once its last token is known
-  if (d.ptr && (p0 != 0 || T % C != 0)) return ATLASMEM_E_UNSUPPORTED;
+  // per-token retrieval of an unfinished chunk's queries runs on the 2-layer memories' path
+  if (d.ptr && d.kind == ATLASMEM_LINEAR && (p0 != 0 || T % C != 0)) return ATLASMEM_E_UNSUPPORTED;
   if (p0 == 0 && T % C == 0)
     return run_update(h, d, K, Q, V, theta, eta, alpha, gamma, Span{T, T, ldg}, Y, st);
 

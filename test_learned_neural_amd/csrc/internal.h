@@ -116,6 +116,8 @@ struct atlasmem_handle_s {
   // dtype), gamma and per-token gates, [M][C] each; `pending` of them are filled
   void* pK;
   void* pV;
+  void* pQ;   // per-token retrieval: the unfinished chunk's query rows [M][C][d_key] (input dtype)
+  void* pYs;  // ... and its answers [M][C][d_value] (output dtype), rows 0..pending-1
   float* pg;
   float* pth;
   float* pet;
@@ -150,6 +152,10 @@ atlasmem_status run_update(Handle* h, const Dims& d, const void* K, const void* 
                            const float* eta, const float* alpha, const float* gamma, const Span& sp, void* Y,
                            hipStream_t st);
 bool decode_supported(const Dims& d, int64_t n);
+// Per-token retrieval of the unfinished chunk's r buffered tokens (2-layer memories): the chunk's
+// forward at its start weights over the buffered rows and their per-token-state answers into
+// h->pYs, without the update (k_mlp.hip).
+atlasmem_status ptr_partial_retrieve(Handle* h, int64_t r, hipStream_t st);
 atlasmem_status launch_decode(Handle* h, const void* Q, const void* K, const void* V, const float* theta,
                               const float* eta, const float* alpha, const float* gamma, int64_t ld, int64_t n,
                               void* Y, bool append, hipStream_t st);

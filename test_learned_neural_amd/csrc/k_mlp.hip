@@ -1196,6 +1196,49 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
   return ATLASMEM_OK;
 }
 
+atlasmem_status ptr_partial_retrieve(Handle* h, int64_t r, hipStream_t st) {
+  // the buffered rows as a chunk of r tokens (token stride C of the pending buffers)
+  Dims d = h->d;
+  d.C = (int)r;
+  d.Rk = d.C + d.c - 1;
+  d.Rt = d.Rk + d.C;
+  const int M = d.M, Rk = d.Rk, dh = d.dh, dv = d.dv, din = d.din, dz = d.dz;
+  const int split = d.prec;
+  const bool feat_exact = d.poly == 1 && d.in_bf16;
+  const int64_t ld = h->d.C;
+  const int64_t zsz = (int64_t)d.Rt * dz;
+  const void* K = h->pK;
+  const void* Q = h->pQ;
+  const float* Win = h->W[h->cur];
+  const float* Sin = h->S[h->cur];
+  // Z of the key rows (window history included) and of the query rows (their chunk-start part of
+  // the per-token first layer), D2 of the keys, then D1, all at the chunk-start weights
+  {
+    StridedLoader lb = strided(Win, d.P, din, 1, 1, dz, din);
+    EpiStore ep{h->Z, zsz, dz, 1};
+    gemm_any(split, feat_exact, false, Rk + d.C, dz, din, M, FeatA{feat_rows(h, K, Q, ld, 0, Rk, Rk + d.C, 1)}, lb,
+             ep, st, h);
+  }
+  {
+    StridedLoader la = hidden(d, h->Z, zsz, dz, 1, 1, Rk, dh);
+    StridedLoader lb = strided(Win + d.P1, d.P, dh, 1, 1, dv, dh);
+    EpiY ep{h->D2, (int64_t)Rk * dv, h->pV, d.in_bf16, h->hv[h->hcur], ld, 0, Rk, d.c, dv, nullptr, d.out_bf16,
+            d.residual, feat_rows(h, K, Q, ld, 0, Rk, Rk, 1)};
+    gemm_any(split, false, false, Rk, dv, dh, M, la, lb, ep, st, h);
+  }
+  {
+    StridedLoader la = strided(h->D2, (int64_t)Rk * dv, dv, 1, 1, Rk, dv);
+    StridedLoader lb = strided(Win + d.P1, d.P, 1, dh, 1, dh, dv);
+    EpiP ep{h->D1, h->Z, (int64_t)Rk * dz, zsz, dh, dz, d.gated};
+    gemm_any(split, false, false, Rk, dh, dv, M, la, lb, ep, st, h);
+  }
+  const atlasmem_status s = ptr_retrieve(h, d, K, Q, h->pth, h->pet, h->pal, d.c > 1 ? h->pg : nullptr, ld, 0, Win,
+                                         Sin, h->pYs, st);
+  if (s != ATLASMEM_OK) return s;
+  AM_LAUNCH_CHECK();
+  return ATLASMEM_OK;
+}
+
 atlasmem_status mlp_retrieve(Handle* h, const void* Q, int64_t T, int64_t ld, void* Y, hipStream_t st) {
   const Dims& d = h->d;
   const int M = d.M, dh = d.dh, dv = d.dv, din = d.din, dz = d.dz;

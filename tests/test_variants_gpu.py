@@ -186,12 +186,49 @@ def test_per_token_retrieve_unsupported():
         am.Memory(config_for(s))
     assert e.value.status == am.E_UNSUPPORTED
     import torch
-    inp = synth.make_inputs(1, "stabilised", batch=1, heads=1, T=100, per_token_retrieve=True)
+    # the linear memory answers per-token queries only for whole chunks
+    inp = synth.make_inputs(0, "literal", batch=1, heads=1, T=10, chunk=4, per_token_retrieve=True)
     mem = am.Memory(config_for(inp.spec), to_dev(inp.W0))
-    seg = segment(inp, 0, 100)
-    Y = torch.empty((1, 100, inp.spec.d_value), dtype=torch.float32, device=DEV)
+    seg = segment(inp, 0, 10)
+    Y = torch.empty((1, 10, inp.spec.d_value), dtype=torch.float32, device=DEV)
     with pytest.raises(am.AtlasMemError) as e:
-        mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], None, 100, Y)
+        mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], None, 10, Y)
     assert e.value.status == am.E_UNSUPPORTED
     assert mem.pending == 0
     mem.close()
+
+
+PTR_STREAM = [
+    # (name, workload, variant, overrides, call boundaries): one-token decoding and mixed calls
+    ("mlp64_decode_then_calls", 1, "stabilised", dict(batch=1, heads=2, T=256, per_token_retrieve=True),
+     [0, 1, 2, 3, 5, 64, 100, 128, 129, 200, 256]),
+    ("window3_ragged_streamed", 3, "stabilised",
+     dict(batch=1, heads=2, T=144, d_key=40, poly_degree=1, d_value=24, d_hidden=72, chunk=48, omega_window=3,
+          per_token_retrieve=True), [0, 7, 40, 48, 49, 100, 144]),
+    ("poly2_window4_streamed", 3, "stabilised", dict(batch=1, heads=2, T=192, per_token_retrieve=True),
+     [0, 1, 33, 64, 65, 130, 192]),
+    ("gated_streamed", 3, "stabilised",
+     dict(kind=G, batch=1, heads=2, T=96, d_key=16, poly_degree=1, d_value=20, d_hidden=36, chunk=48,
+          omega_window=3, per_token_retrieve=True), [0, 10, 11, 60, 96]),
+    ("residual_streamed", 3, "stabilised",
+     dict(kind=R, batch=1, heads=2, T=96, d_key=24, poly_degree=1, d_value=24, d_hidden=40, chunk=32,
+          omega_window=2, per_token_retrieve=True), [0, 31, 33, 96]),
+]
+
+
+@pytest.mark.parametrize("case", PTR_STREAM, ids=[c[0] for c in PTR_STREAM])
+def test_per_token_retrieve_streaming(case):
+    """Queries of an unfinished chunk read the per-token states of its buffered rows: calls of any
+    size (single tokens included) give one call's result, and the oracle's."""
+    name, idx, variant, ov, splits = case
+    inp = synth.make_inputs(idx, variant, **ov)
+    log(f"CASE per-token retrieval streamed {name}")
+    one = run_gpu(inp)
+    streamed = run_gpu(inp, splits=splits)
+    assert one[3] == am.OK and streamed[3] == am.OK
+    agree = {k: maxrel(a, b) for k, a, b in zip(("Y", "W", "S"), streamed[:3], one[:3])}
+    log(f"AGREE ptr_streamed_{name}: " + " ".join(f"{k}={v:.2e}" for k, v in agree.items()))
+    assert all(v <= 1e-5 for v in agree.values()), agree
+    ref = oracle_run(inp)
+    errs = compare(f"ptr_streamed_{name}", inp.spec, streamed, ref, BF16_TOL)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
