@@ -732,6 +732,10 @@ def main():
                      S=rel(Sg[m].cpu().numpy(), Sr[0]))
 
     stages = None if args.no_stages else stage_rooflines(torch, am, synth, dev, stream, cpu=not args.no_cpu)
+    if calib and stages:
+        for v in stages.values():  # HBM-bound stages also against the copy rate this chip reaches
+            if v.get("bound") == "hbm":
+                v["frac_of_measured_copy"] = round(v["achieved"] / calib["copy_gbs"], 4)
     configs = None if args.no_stages else config_lines(torch, am, synth, dev, stream)
 
     cpu = None

@@ -31,19 +31,20 @@ __global__ void __launch_bounds__(512) mfma_peak_kernel(int64_t iters, float* si
   if (t == 0) sink[blockIdx.x] = s;
 }
 
-// Four 16-byte loads in flight per thread before their stores; a block covers 4 x 256 consecutive
+// Eight 16-byte loads in flight per thread before their stores; a block covers 8 x 256 consecutive
 // 16-byte words per round.
+constexpr int kCopyUnroll = 8;
 __global__ void __launch_bounds__(256) copy16_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * 1024;
-  for (int64_t b = (int64_t)blockIdx.x * 1024; b < n; b += stride) {
-    u32x4 v[4];
+  const int64_t stride = (int64_t)gridDim.x * (256 * kCopyUnroll);
+  for (int64_t b = (int64_t)blockIdx.x * (256 * kCopyUnroll); b < n; b += stride) {
+    u32x4 v[kCopyUnroll];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kCopyUnroll; ++u) {
       const int64_t i = b + u * 256 + threadIdx.x;
       if (i < n) v[u] = __builtin_nontemporal_load(src + i);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kCopyUnroll; ++u) {
       const int64_t i = b + u * 256 + threadIdx.x;
       if (i < n) __builtin_nontemporal_store(v[u], dst + i);
     }
@@ -68,7 +69,8 @@ int atlasmem_calibrate_copy(const void* src, void* dst, int64_t bytes, void* str
   if (s < d + bytes && d < s + bytes && bytes > 0) return ATLASMEM_E_INVALID;
   if (bytes == 0) return ATLASMEM_OK;
   const int64_t n = bytes / 16;
-  const int64_t blocks = (n + 1023) / 1024 < 16384 ? (n + 1023) / 1024 : 16384;
+  const int64_t per_block = 256 * am::kCopyUnroll;
+  const int64_t blocks = (n + per_block - 1) / per_block < 8192 ? (n + per_block - 1) / per_block : 8192;
   hipLaunchKernelGGL(am::copy16_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
                      (u32x4*)dst, n);
   AM_LAUNCH_CHECK();

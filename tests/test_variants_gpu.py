@@ -180,6 +180,26 @@ def test_per_token_retrieve_parity(case):
     assert maxrel(oracle_run(base)[0], ref[0]) > 10 * tol
 
 
+def test_per_token_retrieve_full_size_sampled():
+    """The benchmark's per-token-retrieval shape (8 memories x 4096 tokens, 64 -> 128 -> 64, chunk
+    64) in one call; the oracle recomputes two memories over the whole sequence, and every chunk's
+    answers are compared on their own scale (the stabilised memory shrinks geometrically)."""
+    from helpers import per_chunk_y_errors
+    inp = synth.make_inputs(1, "stabilised", per_token_retrieve=True)
+    s = inp.spec
+    log(f"CASE per_token_retrieve full size {s.name}")
+    got = run_gpu(inp)
+    assert got[3] == am.OK
+    mems = [2, 7]
+    ref = oracle_run(inp, mems=mems)
+    sub = tuple(x[mems] for x in got[:3])
+    errs = compare("ptr_full_size_memories_2_7", s, sub, ref, BF16_TOL)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
+    ey, counts, last = per_chunk_y_errors(sub[0], ref[0], s.chunk)
+    log(f"PARITY ptr_full_size_per_chunk_Y: worst={ey:.3e} chunks checked={counts} last={last} of {s.T // s.chunk}")
+    assert ey <= BF16_TOL and min(counts) >= 36  # the chunks above the floor: 39-40 of 64 for these memories
+
+
 def test_per_token_retrieve_unsupported():
     s = synth.spec(4, "literal", batch=1, heads=1, T=256, per_token_retrieve=True)
     with pytest.raises(am.AtlasMemError) as e:
