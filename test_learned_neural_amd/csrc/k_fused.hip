@@ -259,6 +259,28 @@ __device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Barrier of the four waves of one set, for the Newton-Schulz iterations, where the two sets work
+// on disjoint LDS buffers: a set does not wait for the other, so the sets drift apart and one
+// set's matrix work overlaps the other's splits and stores.  A per-set count in LDS only grows
+// (each wave adds one per barrier; `target` counts the set's barriers times four).  The release
+// fence completes this wave's LDS accesses before its arrival, the acquire fence orders the next
+// phase's accesses after the wait.  The wait is bounded, so every wave ends whatever happens; a
+// wave that gives up sets `stuck` (raised to the kernel's error flag).
+__device__ __forceinline__ void set_barrier(int* ctr, int& target, bool& stuck, int lane) {
+  target += 4;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  int spins = 0;
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > (1 << 22)) {
+      stuck = true;
+      break;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // Newton-Schulz on one 64 x 128 matrix held by the four waves of a set as two 32 x 32 tiles
 // per wave (wave w: columns 32w..32w+31), in place.  xh/xl/ah/al/bh/bl: the set's LDS buffers;
 // red: the set's four partial sums of squares.
@@ -269,10 +291,10 @@ struct Part {
 // pre(Part<p>) (p = 0..3) is called before iteration p: it issues the p-th quarter of the state
 // loads, so that they stream in under the matrix work instead of stalling the vector memory path
 // all at once.
-template <bool PL, class Pre>
+template <bool PL, class Pre, class Bar>
 __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int bxh, int bxl, int bah, int bal,
                                                int bbh, int bbl, float* red, const Args& a, int lane, int w,
-                                               Pre&& pre) {
+                                               Pre&& pre, Bar&& set_bar) {
   const int hf = lane >> 5, l32 = lane & 31;
   float ss = 0.0f;
 #pragma unroll
@@ -315,7 +337,7 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
         *(uint2*)(sm + bxh + o) = uint2{h0, h1};
         if constexpr (!PL) *(uint2*)(sm + bxl + o) = uint2{l0, l1};
       }
-    __syncthreads();
+    set_bar();
     // A = X X^T, tile (rt, ct), k = the 128 columns in steps of 16 (natural order)
     f32x16 A = zero16();
     {
@@ -331,7 +353,7 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
       }
     }
     store_tile_T<PL>(sm, bah, bal, LD, A, 32 * rt, 32 * ct, lane);
-    __syncthreads();
+    set_bar();
     // B = b A + c A^2, tile (rt, ct), accumulated in place of A as c (A^2 + (b/c) A)
     if (a.ns_c != 0.0f) {
       const float r_bc = a.ns_b / a.ns_c;
@@ -351,7 +373,7 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
       for (int r = 0; r < 16; ++r) A[r] *= a.ns_b;
     }
     store_tile_T<PL>(sm, bbh, bbl, LE, A, 32 * rt, 32 * ct, lane);
-    __syncthreads();
+    set_bar();
     // X = a X + B X: rows 0..63, columns 32w..32w+31; B X's k-operand X (rows of column cx in
     // the order 4hf..4hf+3, 8+4hf..8+4hf+3 of each k-step) comes back from X^T
     // (accumulated onto a X in place)
@@ -399,6 +421,13 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
   const int t0 = threadIdx.x;
   const int w8 = __builtin_amdgcn_readfirstlane(t0 >> 6);
   const int s = w8 >> 2, w = w8 & 3;  // row set, hidden-unit slice
+  int* set_count = (int*)(red + 8) + s;  // this set's barrier count (red[8], red[9])
+  int set_target = 0;
+  bool stuck = false;
+  if (t0 == 0) {
+    ((int*)(red + 8))[0] = 0;
+    ((int*)(red + 8))[1] = 0;
+  }
   // Lane-dependent values are re-derived in each phase from an opaque copy of the thread index,
   // so that the compiler does not keep them (and every address made from them) live across the
   // whole chunk loop.  h_own: the hidden unit this lane owns in register slices.
@@ -741,8 +770,9 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
     {
       AM_LANE_VARS;
       const int bxh = opq(NX + s * NXS), bah = opq(NA + s * NAS), bbh = opq(NB + s * NBS);
+      auto set_bar = [&]() __attribute__((always_inline)) { set_barrier(set_count, set_target, stuck, lane); };
       newton_schulz1<PL>(x, sm, bxh, bxh + HD * 64, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red + 4 * s, a, lane,
-                         w, pre);
+                         w, pre, set_bar);
     }
     // S = eta S - theta NS(G), W = (1 - alpha) W + S for this set's matrix
 #pragma unroll
@@ -797,6 +827,8 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
           buf_st(rw_out, wo2, so, x[tt][r]);
         }
     }
+    // the handoff lies over both sets' A buffers: wait for the other set's last iteration
+    __syncthreads();
     if (s == 0) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -827,7 +859,7 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
       }
     }
   }
-  if (bad) a.flag[0] = 1;
+  if (bad || stuck) a.flag[0] = 1;
 #undef AM_LANE_VARS
 }
 
