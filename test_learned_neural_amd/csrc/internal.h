@@ -101,6 +101,9 @@ struct atlasmem_handle_s {
   float* scal;   // [M][ncb][3]
   // per-chunk gradient (PER_CHUNK path)
   float* G;      // [M][P]
+  // hidden-split chunk kernel (k_hsplit.hip): partial outputs and key-row pre-activations of two
+  // chunks, or null when the configuration does not qualify
+  float* hsw;
   // retrieval workspace
   int rb;        // rows per retrieval block
   float* Zr;     // [M][rb][dh]
@@ -217,6 +220,13 @@ atlasmem_status launch_ns_groups(const float* G, int64_t ldG_mat, int n_mat, int
                                  float a, float b, float c, float eps, int prec, const NsUpdate& upd,
                                  hipStream_t st);
 bool fused_supported(const Dims& d);
+// The hidden-split chunk kernel for per-token gates (2-layer SiLU memory, Omega window, features of
+// degree <= 2): chunks [kb0, kb0 + nb) of a call, after the gate scan (and window coefficients) of
+// that block, in nb + 1 launches.
+bool hsplit_supported(const Dims& d);
+int64_t hsplit_workspace_floats(const Dims& d);
+atlasmem_status launch_hsplit(Handle* h, const Dims& d, const void* K, const void* Q, const void* V, int64_t kb0,
+                              int nb, int64_t ld, void* Y, hipStream_t st);
 // The fused kernel for per-token gates (the same memory, chunks of 64): chunks [kb0, kb0 + nb) of a
 // call, after the gate scan of that block of chunks.
 bool fused_pt_supported(const Dims& d);

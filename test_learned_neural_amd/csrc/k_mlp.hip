@@ -995,6 +995,14 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
       if (stt != ATLASMEM_OK) return stt;
       continue;
     }
+    // (its vector loads and stores need 16-byte aligned rows, its buffer offsets a memory's rows
+    // within 2 GB)
+    if (!d.no_fused && h->hsw && hsplit_supported(d) && ld * (d.dk > d.dv ? d.dk : d.dv) * 4 < ((int64_t)1 << 31) &&
+        (((uintptr_t)K | (uintptr_t)Q | (uintptr_t)V | (uintptr_t)Y) & 15) == 0) {
+      stt = launch_hsplit(h, d, K, Q, V, kb0, nb, ld, Y, st);
+      if (stt != ATLASMEM_OK) return stt;
+      continue;
+    }
     if (loop_supported(d, Y != nullptr)) {
       LoopArgs la;
       la.d = d;
