@@ -442,10 +442,13 @@ __global__ void __launch_bounds__(kThreads) hsplit_kernel(Args a) {
         }
       }
     }
-    for (int e = t; e < (a.dk + 2) * L.RkK; e += kThreads) {
-      const int i = e / L.RkK, r = e - i * L.RkK;
-      if (i >= a.dk) xT[i * L.xts + r] = i == a.dk ? 1.0f : 0.0f;
-      else if (r >= a.Rk) xT[i * L.xts + r] = 0.0f;
+    for (int e = t; e < 2 * L.RkK; e += kThreads) {
+      const bool one = e < L.RkK;
+      xT[(a.dk + (one ? 0 : 1)) * L.xts + (one ? e : e - L.RkK)] = one ? 1.0f : 0.0f;
+    }
+    for (int e = t; e < a.dk * 32; e += kThreads) {  // columns Rk .. RkK - 1 (fewer than 32)
+      const int i = e >> 5, c = e & 31;
+      if (a.Rk + c < L.RkK) xT[i * L.xts + a.Rk + c] = 0.0f;
     }
     // E = 2 (sum_g Yhat_g - V) over the key rows, hi / lo in [r][v] and [v][r]
 #pragma unroll
@@ -543,8 +546,9 @@ __global__ void __launch_bounds__(kThreads) hsplit_kernel(Args a) {
         st_split4(hsh_, hsl_, io, hs4[0], hs4[1], hs4[2], hs4[3]);
       }
     }
-    // the update's state values are taken here, in one wait: the gradient tiles below then wait
-    // for nothing (a wait inside them would also wait for the previous tiles' stores)
+    // the update's state values and the forwarded chunk's rows are taken here, in one wait: the
+    // gradient tiles and the staging below then wait for nothing (a wait there would also wait for
+    // the stores issued before it)
 #pragma unroll
     for (int j = 0; j < kT1; ++j)
 #pragma unroll
@@ -553,6 +557,8 @@ __global__ void __launch_bounds__(kThreads) hsplit_kernel(Args a) {
     for (int j = 0; j < kT2; ++j) asm volatile("" ::"v"(w2p[j].x), "v"(w2p[j].y), "v"(w2p[j].z), "v"(w2p[j].w),
                                             "v"(s2p[j].x), "v"(s2p[j].y), "v"(s2p[j].z), "v"(s2p[j].w));
     asm volatile("" ::"v"(cP), "v"(cB), "v"(cA));
+#pragma unroll
+    for (int it = 0; it < kStage; ++it) asm volatile("" ::"v"(kx[it][0]), "v"(kx[it][1]), "v"(kx[it][2]), "v"(kx[it][3]));
     __syncthreads();
 
     // W1_g, S1_g: G1^W = (c^W D1)^T phi, G1^S = (c^S D1)^T phi; tiles of 16 features, the k-step
@@ -719,12 +725,16 @@ __global__ void __launch_bounds__(kThreads) hsplit_kernel(Args a) {
         }
       }
     }
-    // the one and zero columns, and the padding rows
-    for (int e = t; e < nrow * (a.dk + 4); e += kThreads) {
-      const int row = e / (a.dk + 4), i = e - row * (a.dk + 4);
-      const bool pad = row < L.RkT ? row >= a.Rk : row - L.RkT >= a.nq;
-      if (i >= a.dk) xr[row * L.xs + i] = i == a.dk ? 1.0f : 0.0f;
-      else if (pad) xr[row * L.xs + i] = 0.0f;
+    // the one and zero columns (dk .. dk + 3) of every row, then the padding rows (key rows
+    // Rk .. RkT - 1, query rows nq .. nqT - 1: fewer than 32) as float4s, d_key / 4 <= 16 per row
+    for (int e = t; e < nrow; e += kThreads) *(float4*)(xr + e * L.xs + a.dk) = float4{1.0f, 0.0f, 0.0f, 0.0f};
+    {
+      const int pk = L.RkT - a.Rk, pq = L.nqT - a.nq;
+      const int p = t >> 4, q = t & 15;
+      if (q < (a.dk >> 2) && p < pk + pq) {
+        const int row = p < pk ? a.Rk + p : L.RkT + a.nq + (p - pk);
+        *(float4*)(xr + row * L.xs + 4 * q) = float4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
     }
     __syncthreads();
     // Z_g = phi W1_g^T over key and query rows; H_g = silu(Z_g) into [row][h]
@@ -842,7 +852,7 @@ bool hsplit_supported(const Dims& d) {
   if (d.gate_mode != ATLASMEM_PER_TOKEN || d.ns_steps != 0 || d.prec != 1 || !d.in_bf16) return false;
   if (d.poly != 1 && d.poly != 2) return false;
   if (d.dh % hsk::HS != 0 || d.dh / hsk::HS > hsk::kMaxG) return false;
-  if (d.dv % 32 != 0 || d.dk % 8 != 0 || d.dk + 2 > 255) return false;
+  if (d.dv % 32 != 0 || d.dk % 8 != 0 || d.dk > 64) return false;
   using namespace hsk;
   const int G = d.dh / HS;
   const Layout L = make_layout(d.dk, d.din, d.dv, d.Rk, d.C, block_qb(d));
