@@ -586,6 +586,9 @@ def config_lines(torch, am, synth, dev, stream, steps=5, warmup=2) -> dict:
         if s.kind == synth.LINEAR:
             line["path"] = "lin_kernel (one launch, sequential over tokens)"
         else:
+            line["path"] = {1: "fused_pt_kernel (one launch per block of chunks, one workgroup per memory)",
+                            2: "general path (per-product launches, split-K)",
+                            3: "hsplit_kernel (one launch per chunk, 8 workgroups per memory)"}[idx]
             fl = sum(mlp_flops_per_chunk(s).values()) * (s.T // s.chunk) * s.n_mem
             tf = fl / (ms * 1e-3) / 1e12
             line.update(tflops=round(tf, 3), frac_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 6))
