@@ -198,7 +198,7 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
   }
   const size_t state_end = cv.off;
   size_t oZ = 0, oD2 = 0, oD1 = 0, osk = 0, ocW = 0, ocS = 0, ooW = 0, ooS = 0, oscal = 0, oG = 0, oZr = 0;
-  size_t opZS = 0, opA1 = 0, opYB = 0, opbA = 0, opOm = 0, ocik = 0, ociq = 0, ohs = 0;
+  size_t opZS = 0, opA1 = 0, opYB = 0, opbA = 0, opOm = 0, ocik = 0, ociq = 0, ohs = 0, ofxs = 0;
   if (d.kind == ATLASMEM_MLP2_SILU) {
     oZ = cv.take(sizeof(float) * M * d.Rt * d.dz);
     oD2 = cv.take(sizeof(float) * M * d.Rk * d.dv);
@@ -225,6 +225,7 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
     // the per-chunk gradient (Newton-Schulz), or the fused kernels' transposed second-layer state
     oG = cv.take(sizeof(float) * M * d.P);
     if (hsplit_supported(d)) ohs = cv.take(sizeof(float) * hsplit_workspace_floats(d));
+    if (fused_split_workspace_floats(d) > 0) ofxs = cv.take(sizeof(float) * fused_split_workspace_floats(d));
     ocik = cv.take(sizeof(float) * M * (ncb * d.C + d.c - 1));
     ociq = cv.take(sizeof(float) * M * ncb * d.C);
     int64_t rb = 1024;
@@ -287,6 +288,7 @@ atlasmem_status atlasmem_create(const atlasmem_config* cfg, const float* W0, con
     h->scal = oscal ? (float*)(base + oscal) : nullptr;
     h->G = oG ? (float*)(base + oG) : nullptr;
     h->hsw = ohs ? (float*)(base + ohs) : nullptr;
+    h->fxs = ofxs ? (float*)(base + ofxs) : nullptr;
     h->Zr = (float*)(base + oZr);
     h->pZS = d.ptr ? (float*)(base + opZS) : nullptr;
     h->pA1 = d.ptr ? (float*)(base + opA1) : nullptr;

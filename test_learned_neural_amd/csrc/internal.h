@@ -104,6 +104,9 @@ struct atlasmem_handle_s {
   // hidden-split chunk kernel (k_hsplit.hip): partial outputs and key-row pre-activations of two
   // chunks, or null when the configuration does not qualify
   float* hsw;
+  // the fused Newton-Schulz kernel's two-workgroup form (k_fused.hip): exchange slots and the
+  // workgroup pairs' counts, or null when the configuration does not qualify
+  float* fxs;
   // retrieval workspace
   int rb;        // rows per retrieval block
   float* Zr;     // [M][rb][dh]
@@ -220,6 +223,7 @@ atlasmem_status launch_ns_groups(const float* G, int64_t ldG_mat, int n_mat, int
                                  float a, float b, float c, float eps, int prec, const NsUpdate& upd,
                                  hipStream_t st);
 bool fused_supported(const Dims& d);
+int64_t fused_split_workspace_floats(const Dims& d);
 // The hidden-split chunk kernel for per-token gates (2-layer SiLU memory, Omega window, features of
 // degree <= 2): chunks [kb0, kb0 + nb) of a call, after the gate scan (and window coefficients) of
 // that block, in nb + 1 launches.

@@ -118,6 +118,12 @@ struct Args {
   int ns_steps;
   float ns_a, ns_b, ns_c, ns_eps;
   int* flag;
+  // Two workgroups per memory (one per set; null otherwise): per memory two exchange slots of
+  // 64 x 128 floats (the partial gradient each set passes to the other) and a count of arrivals at
+  // the pair's waits (one int, 128 bytes apart), zero at the launch.
+  float* xs;
+  int* sync;
+  int M;
 };
 
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
@@ -281,6 +287,38 @@ __device__ __forceinline__ void set_barrier(int* ctr, int& target, bool& stuck, 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Wait of the two workgroups of a memory (one per set, on different CUs): one lane counts the
+// workgroup's arrival and waits until the pair has made `target` arrivals in all.  Ordering:
+//  - the pair on one XCD (`local`, the case under round-robin placement), which shares that XCD's
+//    L2: before the barrier each wave waits until its stores have reached L2 (vector L1 writes
+//    through); after it, the CU's L1 is invalidated (`buffer_inv sc0`, the invalidate that the
+//    compiler uses when one workgroup's waves span CUs), so the other workgroup's data is read
+//    from L2.  Neither touches L2 itself;
+//  - otherwise device-scope release and acquire fences, which write back and invalidate L2.
+// The wait is bounded, so every wave ends whatever happens; one that gives up sets `stuck` (raised
+// to the kernel's error flag), and after that the workgroup no longer waits at all, so a broken
+// pair costs one bounded wait, not one per chunk.
+__device__ __forceinline__ void pair_sync(int* ctr, int& target, bool& stuck, bool local) {
+  target += 2;
+  if (local) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0 && !stuck) {
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > (1 << 20)) {
+        stuck = true;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (local) asm volatile("buffer_inv sc0" ::: "memory");
+  else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
 // Newton-Schulz on one 64 x 128 matrix held by the four waves of a set as two 32 x 32 tiles
 // per wave (wave w: columns 32w..32w+31), in place.  xh/xl/ah/al/bh/bl: the set's LDS buffers;
 // red: the set's four partial sums of squares.
@@ -413,20 +451,44 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
 // key's own values enter the error, D2 = 2 (Yh - (V - x)); each V element register carries the
 // key element of the same position in its upper half.  The query's values are added to the
 // output after the launch (residual_output_kernel).
-template <bool RES, bool PL>
-__global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
+//
+// SPLIT: each set is a workgroup of its own (256 threads, one wave per SIMD) on its own CU, so that
+// 128 memories occupy 256 CUs.  Workgroups b and b + 8 of each run of 16 form a memory's pair (the
+// same XCD under round-robin placement, so their exchanges stay in one L2; each workgroup reads its
+// XCD id at the start, and a pair found on two XCDs orders its exchanges with device-scope fences
+// instead).  Within a set the work
+// is the same as in the one-workgroup form (the thread index is offset by 256 for set 1); what the
+// sets pass each other through LDS there goes through global memory here, around two waits of the
+// pair per chunk: the partial gradients (exchange slots), and the new weights, which each set reads
+// back from the state it has just stored (W1 from the state, W2^T from T2).  The results are those
+// of the one-workgroup form bit for bit.  The launch is cooperative, so both workgroups of a pair
+// are resident together.
+template <bool RES, bool PL, bool SPLIT>
+__global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
   float* red = (float*)(sm + LDS_U16);
-  const int m = blockIdx.x;
-  const int t0 = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int m = SPLIT ? (blk >> 4) * 8 + (blk & 7) : blk;
+  const int s_blk = SPLIT ? (blk >> 3) & 1 : 0;
+  if (SPLIT && m >= a.M) return;  // both workgroups of a pair past the last memory
+  const int t0 = threadIdx.x + 256 * s_blk;
   const int w8 = __builtin_amdgcn_readfirstlane(t0 >> 6);
   const int s = w8 >> 2, w = w8 & 3;  // row set, hidden-unit slice
   int* set_count = (int*)(red + 8) + s;  // this set's barrier count (red[8], red[9])
   int set_target = 0;
   bool stuck = false;
-  if (t0 == 0) {
+  // the pair's words: [0] arrivals, [2 + set] the set's XCD id + 1
+  int* pair_ctr = SPLIT ? a.sync + (int64_t)m * 32 : nullptr;
+  int pair_target = 0;
+  if (threadIdx.x == 0) {
     ((int*)(red + 8))[0] = 0;
     ((int*)(red + 8))[1] = 0;
+  }
+  int xcc = 0;
+  if constexpr (SPLIT) {
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    xcc &= 0xF;
+    if (threadIdx.x == 0) __hip_atomic_store(pair_ctr + 2 + s_blk, xcc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // Lane-dependent values are re-derived in each phase from an opaque copy of the thread index,
   // so that the compiler does not keep them (and every address made from them) live across the
@@ -466,7 +528,7 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
     pack8(v, w1h[ks], w1l[ks]);
   }
   // W2 in LDS as [h][v]: B operand of D2 W2 (direct reads) and of H W2^T (transposing reads)
-  for (int e = t; e < D * HD; e += NT) {
+  for (int e = SPLIT ? t - 256 * s : t; e < D * HD; e += (SPLIT ? NT / 2 : NT)) {
     const int vv = e / HD, hh = e % HD;
     uint32_t hi, lo;
     split_bf16(Win[P1 + e], hi, lo);
@@ -495,6 +557,23 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
   }
   }
   __syncthreads();
+  bool pair_local = false;  // both workgroups of the pair on this XCD
+  if constexpr (SPLIT) {
+    int* loc = (int*)(red + 10);
+    if (threadIdx.x == 0) {
+      int other = 0, spins = 0;
+      while ((other = __hip_atomic_load(pair_ctr + 3 - s_blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > (1 << 20)) {
+          stuck = true;
+          break;
+        }
+      }
+      *loc = other == xcc + 1 ? 1 : 0;
+    }
+    __syncthreads();
+    pair_local = __builtin_amdgcn_readfirstlane(*loc) != 0;
+  }
 
   // A chunk is processed in double groups: the query rows and the key rows [64g, 64g + 64)
   // together (only the key rows when nothing is retrieved), so that the two X W1^T and H W2^T
@@ -709,7 +788,38 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
     // Swap partial gradients: set 0 keeps G1 and passes its G2 partial, set 1 the reverse.
     // The slots were last read by the final group's H W2^T, before its second barrier.
     f32x16 x[2];
-    {
+    if constexpr (SPLIT) {
+      // through this memory's exchange slots: slot s holds the partial this set passes on
+      AM_LANE_VARS;
+      const rsrc_t rx = make_rsrc(a.xs + (int64_t)m * 2 * P2, (uint32_t)(2 * P2 * 4));
+      const int vx = (((w * 2) * 4) * 64 + lane) * 16;  // byte offset of (tile 0, quad 0) of this lane
+      if (s == 0) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            buf_st4(rx, vx, ((tt * 4 + q) * 64) * 16,
+                    float4{gr[1][tt][4 * q], gr[1][tt][4 * q + 1], gr[1][tt][4 * q + 2], gr[1][tt][4 * q + 3]});
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            buf_st4(rx, vx + P2 * 4, ((tt * 4 + q) * 64) * 16,
+                    float4{gr[0][tt][4 * q], gr[0][tt][4 * q + 1], gr[0][tt][4 * q + 2], gr[0][tt][4 * q + 3]});
+      }
+      pair_sync(pair_ctr, pair_target, stuck, pair_local);
+      const int vsrc = vx + (s ? 0 : P2 * 4);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = buf_ld4(rx, vsrc, ((tt * 4 + q) * 64) * 16);
+          const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[tt][4 * q + u] = (s ? gr[1][tt][4 * q + u] : gr[0][tt][4 * q + u]) + fv[u];
+        }
+    } else {
       AM_LANE_VARS;
       float* xg1 = (float*)(sm + opq(XG1));
       float* xg2 = (float*)(sm + opq(XG2));
@@ -770,7 +880,10 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
     {
       AM_LANE_VARS;
       const int bxh = opq(NX + s * NXS), bah = opq(NA + s * NAS), bbh = opq(NB + s * NBS);
-      auto set_bar = [&]() __attribute__((always_inline)) { set_barrier(set_count, set_target, stuck, lane); };
+      auto set_bar = [&]() __attribute__((always_inline)) {
+        if constexpr (SPLIT) __syncthreads();
+        else set_barrier(set_count, set_target, stuck, lane);
+      };
       newton_schulz1<PL>(x, sm, bxh, bxh + HD * 64, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red + 4 * s, a, lane,
                          w, pre, set_bar);
     }
@@ -827,6 +940,7 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
           buf_st(rw_out, wo2, so, x[tt][r]);
         }
     }
+    if constexpr (!SPLIT) {
     // the handoff lies over both sets' A buffers: wait for the other set's last iteration
     __syncthreads();
     if (s == 0) {
@@ -838,6 +952,53 @@ __global__ void __launch_bounds__(NT) fused_ns_kernel(Args a) {
         if constexpr (!PL) ho[(w * 8 + 4 + ks) * 64 + lane] = wl;
       }
     }
+    }
+    }
+    if constexpr (SPLIT) {
+      // Both sets' new weights are stored (set 0: W1 in the state, set 1: W2^T in T2); after the
+      // pair's wait each set builds the operands of the next chunk from its own registers and the
+      // other's stored matrix.  The barrier inside the wait also orders these LDS writes after the
+      // last Newton-Schulz reads of the buffers below them.
+      if (k + 1 < a.nchunks) {
+        pair_sync(pair_ctr, pair_target, stuck, pair_local);
+        AM_LANE_VARS;
+        if (s == 0) {
+          f32x16 y2[2];
+          const int vo1 = (h_own * D + 4 * hf) * 4;  // W2^T[h_own][4hf] in T2
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 f = buf_ld4(rt2, vo1, (32 * tt + 8 * q) * 4);
+              y2[tt][4 * q] = f.x; y2[tt][4 * q + 1] = f.y; y2[tt][4 * q + 2] = f.z; y2[tt][4 * q + 3] = f.w;
+            }
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            u32x4 wh, wl;
+            tile_op(y2[ks >> 1], ks & 1, wh, wl);
+            store_rows_T<PL>(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
+            tile_op(x[ks >> 1], ks & 1, w1h[ks], w1l[ks]);
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            u32x4 wh, wl;
+            tile_op(x[ks >> 1], ks & 1, wh, wl);
+            store_rows_T<PL>(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
+          }
+          const rsrc_t rw1 = make_rsrc(Wout, (uint32_t)(P1 * 4));
+          const int vw = (h_own * D + 4 * hf) * 4;  // W1[h_own][4hf] in the state
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const float4 p0 = buf_ld4(rw1, vw, 16 * ks * 4);
+            const float4 p1 = buf_ld4(rw1, vw, (16 * ks + 8) * 4);
+            const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            pack8(v, w1h[ks], w1l[ks]);
+          }
+        }
+        // the next group's first LDS reads of W2^T come after its first barrier
+      }
+      continue;
     }
     __syncthreads();
     // both sets take the new W1 slices from LDS (the registers then hold nothing across the
@@ -1358,20 +1519,42 @@ bool fused_supported(const Dims& d) {
          d.prec != 2 && !(d.residual && d.out_bf16);
 }
 
+namespace fz {
+// Memories of one launch of the two-workgroup form: 2 x 8 x ceil(M / 8) workgroups, one per CU.
+constexpr int kSplitMaxMem = 128;
+__global__ void zero_ints_kernel(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+}  // namespace fz
+
+int64_t fused_split_workspace_floats(const Dims& d) {
+  if (!fused_supported(d) || d.M > fz::kSplitMaxMem) return 0;
+  return (int64_t)d.M * (2 * fz::P2 + 32);  // exchange slots, then the pairs' counts
+}
+
 // The fused kernel sequence over sp.T tokens (a whole number of chunks).  The state moves from
 // (Wb[cur], Sb[cur]) to (Wb[1 - cur], Sb[1 - cur]) in each launch segment and `cur` flips with it;
 // Wb[0] == Wb[1] (and Sb likewise) updates the state in place, which the kernel allows: every
-// state element it writes was read earlier by the same lane, or before a workgroup barrier that
-// precedes the write.  T2: per memory 2 x 64 x 128 floats of scratch; flag: the non-finite flag.
+// state element it writes was read earlier by the same lane, or before a workgroup barrier (or a
+// wait of the workgroup pair) that precedes the write.  T2: per memory 2 x 64 x 128 floats of
+// scratch; xs: the two-workgroup form's workspace (fused_split_workspace_floats), or null for one
+// workgroup per memory; flag: the non-finite flag.
 static atlasmem_status launch_fused_bufs(const Dims& d, const void* K, const void* Q, const void* V,
                                          const float* theta, const float* eta, const float* alpha, const Span& sp,
                                          void* Y, float* const Wb[2], float* const Sb[2], int& cur, float* T2,
-                                         int* flag, hipStream_t st) {
+                                         float* xs, int* flag, hipStream_t st) {
   const bool pl = d.prec == 0;  // plain bf16 products
-  const void* kern = d.residual ? (pl ? (const void*)fz::fused_ns_kernel<true, true> : (const void*)fz::fused_ns_kernel<true, false>)
-                                : (pl ? (const void*)fz::fused_ns_kernel<false, true> : (const void*)fz::fused_ns_kernel<false, false>);
+  const void* kern = d.residual ? (pl ? (const void*)fz::fused_ns_kernel<true, true, false> : (const void*)fz::fused_ns_kernel<true, false, false>)
+                                : (pl ? (const void*)fz::fused_ns_kernel<false, true, false> : (const void*)fz::fused_ns_kernel<false, false, false>);
   if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, fz::LDS_BYTES) != hipSuccess)
     return ATLASMEM_E_DEVICE;
+  bool split = xs != nullptr && d.M <= fz::kSplitMaxMem;
+  const void* kern2 = d.residual ? (pl ? (const void*)fz::fused_ns_kernel<true, true, true> : (const void*)fz::fused_ns_kernel<true, false, true>)
+                                 : (pl ? (const void*)fz::fused_ns_kernel<false, true, true> : (const void*)fz::fused_ns_kernel<false, false, true>);
+  if (split && hipFuncSetAttribute(kern2, hipFuncAttributeMaxDynamicSharedMemorySize, fz::LDS_BYTES) != hipSuccess)
+    return ATLASMEM_E_DEVICE;
+  int* sync = split ? (int*)(xs + (int64_t)d.M * 2 * fz::P2) : nullptr;
   // one launch per segment of at most 2^22 tokens, so that per-memory byte offsets fit 32 bits
   const int64_t nchunks = sp.T / d.C;
   const int64_t seg = ((int64_t)1 << 22) / d.C;
@@ -1403,12 +1586,32 @@ static atlasmem_status launch_fused_bufs(const Dims& d, const void* K, const voi
     a.ns_c = d.ns_c;
     a.ns_eps = d.ns_eps;
     a.flag = flag;
+    a.xs = split ? xs : nullptr;
+    a.sync = sync;
+    a.M = d.M;
+    if (split) {
+      // the pairs' counts start at zero in every launch (a kernel, not a memset)
+      hipLaunchKernelGGL(fz::zero_ints_kernel, dim3((d.M * 32 + 255) / 256), dim3(256), 0, st, sync, d.M * 32);
+      AM_LAUNCH_CHECK();
+      void* args[] = {&a};
+      const unsigned nblk = 16u * (unsigned)((d.M + 7) / 8);
+      if (hipLaunchCooperativeKernel(kern2, dim3(nblk), dim3(fz::NT / 2), args, fz::LDS_BYTES, st) != hipSuccess) {
+        // not every pair can be resident at once on this device: one workgroup per memory instead
+        (void)hipGetLastError();
+        split = false;
+        a.xs = nullptr;
+        a.sync = nullptr;
+      } else {
+        cur = 1 - cur;
+        continue;
+      }
+    }
     if (d.residual) {
-      if (pl) hipLaunchKernelGGL((fz::fused_ns_kernel<true, true>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
-      else hipLaunchKernelGGL((fz::fused_ns_kernel<true, false>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+      if (pl) hipLaunchKernelGGL((fz::fused_ns_kernel<true, true, false>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+      else hipLaunchKernelGGL((fz::fused_ns_kernel<true, false, false>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
     } else {
-      if (pl) hipLaunchKernelGGL((fz::fused_ns_kernel<false, true>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
-      else hipLaunchKernelGGL((fz::fused_ns_kernel<false, false>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+      if (pl) hipLaunchKernelGGL((fz::fused_ns_kernel<false, true, false>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
+      else hipLaunchKernelGGL((fz::fused_ns_kernel<false, false, false>), dim3(d.M), dim3(fz::NT), fz::LDS_BYTES, st, a);
     }
     AM_LAUNCH_CHECK();
     cur = 1 - cur;
@@ -1480,7 +1683,7 @@ atlasmem_status launch_fused_pt(Handle* h, const Dims& d, const void* K, const v
 atlasmem_status launch_fused(Handle* h, const Dims& d, const void* K, const void* Q, const void* V,
                              const float* theta, const float* eta, const float* alpha, const Span& sp, void* Y,
                              hipStream_t st) {
-  return launch_fused_bufs(d, K, Q, V, theta, eta, alpha, sp, Y, h->W, h->S, h->cur, h->G, h->flag, st);
+  return launch_fused_bufs(d, K, Q, V, theta, eta, alpha, sp, Y, h->W, h->S, h->cur, h->G, h->fxs, h->flag, st);
 }
 
 // ---------------------------------------------------------------------------- no allocation
@@ -1544,7 +1747,7 @@ atlasmem_status launch_fused_static(const Dims& d, const void* K, const void* Q,
   float* Wb[2] = {W, W};
   float* Sb[2] = {S, S};
   int cur = 0;
-  return launch_fused_bufs(d, K, Q, V, theta, eta, alpha, sp, Y, Wb, Sb, cur, base, flag, st);
+  return launch_fused_bufs(d, K, Q, V, theta, eta, alpha, sp, Y, Wb, Sb, cur, base, nullptr, flag, st);
 }
 
 }  // namespace am

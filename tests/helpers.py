@@ -232,3 +232,36 @@ def run_gpu_states(inp, mems, calls, chunks_per_call, precision=am.PREC_AUTO, fl
     torch.cuda.synchronize()
     mem.close()
     return y_to_np(Y), states
+
+
+def handle_update_run(inp):
+    """One update_chunked call on a handle over the whole input (fp32 output): (Y, W, S) on the host."""
+    import torch
+    s = inp.spec
+    mem = am.Memory(config_for(s), to_dev(inp.W0), to_dev(inp.S0))
+    seg = segment(inp, 0, s.T)
+    Y = torch.empty((s.n_mem, s.T, s.d_value), dtype=torch.float32, device=DEV)
+    mem.update_chunked(seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"], seg["alpha"], None, s.T, Y)
+    W = torch.empty((s.n_mem, mem.P), dtype=torch.float32, device=DEV)
+    S = torch.empty_like(W)
+    assert mem.get_state(W, S) == am.OK
+    torch.cuda.synchronize()
+    mem.close()
+    return Y.cpu().numpy(), W.cpu().numpy(), S.cpu().numpy()
+
+
+def static_update_run(inp):
+    """The allocation-free update (one workgroup per memory) over the whole input: (Y, W, S)."""
+    import torch
+    s = inp.spec
+    seg = segment(inp, 0, s.T)
+    W = to_dev(inp.W0).clone()
+    S = to_dev(inp.S0).clone()
+    Y = torch.full((s.n_mem, s.T, s.d_value), float("nan"), dtype=torch.float32, device=DEV)
+    flag = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    st = am.update_chunked_static(config_for(s), seg["K"], seg["Q"], seg["V"], seg["theta"], seg["eta"],
+                                  seg["alpha"], s.T, W, S, Y, flag)
+    assert st == am.OK
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    return Y.cpu().numpy(), W.cpu().numpy(), S.cpu().numpy()

@@ -4,7 +4,7 @@ the fp64 oracle and against the general per-chunk kernel sequence, through the C
 import numpy as np
 import pytest
 
-from helpers import BF16_TOL, compare, log, maxrel, oracle_run, run_gpu
+from helpers import BF16_TOL, compare, handle_update_run, log, maxrel, oracle_run, run_gpu, static_update_run
 from test_learned_neural_amd import atlasmem as am
 from test_learned_neural_amd import synth
 
@@ -51,3 +51,23 @@ def test_fused_full_size_sampled():
     sub = (got[0][mems], got[1][mems], got[2][mems])
     errs = compare("fused_full_size_memories_5_101", inp.spec, sub, ref, BF16_TOL)
     assert all(v <= BF16_TOL for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("kind,ov", [
+    (synth.MLP2_SILU, dict(batch=8, heads=16, T=640)),                 # 128 memories: every CU a set
+    (synth.MLP2_SILU, dict(batch=1, heads=13, T=256, chunk=64)),       # pairs past the last memory exit
+    (synth.MLP2_SILU, dict(batch=1, heads=2, T=128)),                  # one chunk: no weight handoff
+    (synth.MLP2_SILU_RESIDUAL, dict(batch=2, heads=5, T=384, chunk=192)),
+], ids=["M128_C128", "M13_C64", "M2_one_chunk", "residual_M10_C192"])
+def test_two_workgroup_form_equals_one_workgroup_form(kind, ov):
+    """For up to 128 memories a handle runs each memory's two sets as two workgroups on different
+    CUs, which exchange partial gradients and new weights through global memory; the allocation-free
+    entry point runs one workgroup per memory with the same arithmetic.  The results agree bit for
+    bit, and the handle reports no failed wait (the flag that get_state checks)."""
+    inp = synth.make_inputs(4, "literal", kind=kind, **ov)
+    log(f"CASE fused two-workgroup form: kind {kind} memories {inp.spec.n_mem} T {inp.spec.T} "
+        f"chunk {inp.spec.chunk}")
+    two = handle_update_run(inp)
+    one = static_update_run(inp)
+    for name, a, b in zip(("Y", "W", "S"), two, one):
+        assert np.array_equal(a, b), (name, maxrel(a, b))
