@@ -705,7 +705,9 @@ def main():
                 frac=round(ach / PEAK_BF16_TFLOPS, 5),
                 traffic=(measured_traffic() if fused and s.T == 32768 and s.n_mem == 128 else None),
                 kernel="am::fz::fused_ns_kernel" if fused else "update_chunked launch sequence",
-                launch=(f"{s.n_mem} workgroups x 512 threads, one memory each, all {nchunks} chunks"
+                launch=((f"{16 * ((s.n_mem + 7) // 8)} workgroups x 256 threads, two per memory (one per row set, "
+                         f"on two CUs of one XCD), cooperative, all {nchunks} chunks" if s.n_mem <= 128 else
+                         f"{s.n_mem} workgroups x 512 threads, one memory each, all {nchunks} chunks")
                         if fused else "per-chunk launches"),
                 avg_launch_ms=round(upd_ms, 5),
                 algorithmic_flops_per_launch=int(step_flops))

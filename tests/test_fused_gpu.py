@@ -41,11 +41,17 @@ def test_fused_streaming_and_no_retrieval():
 
 
 def test_fused_full_size_sampled():
-    """The full workload (B=8, H=16, T=32768, chunk 128) in one call, as the benchmark runs it; the
-    oracle recomputes two sampled memories over the whole sequence."""
+    """The full workload (B=8, H=16, T=32768, chunk 128) in one call, as the benchmark runs it (the
+    two-workgroup form: 256 workgroups, 2 x 256 waits per pair); the oracle recomputes two sampled
+    memories over the whole sequence, and every memory equals the one-workgroup form (the
+    allocation-free entry point) bit for bit."""
     inp = synth.make_inputs(4, "literal")
     got = run_gpu(inp)
     assert got[3] == am.OK
+    one = static_update_run(inp)
+    for name, a, b in zip(("Y", "W", "S"), got[:3], one):
+        assert np.array_equal(a, b), (name, maxrel(a, b))
+    del one
     mems = [5, 101]
     ref = oracle_run(inp, mems=mems)
     sub = (got[0][mems], got[1][mems], got[2][mems])
