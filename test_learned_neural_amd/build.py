@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libatlasmem.so")
-SOURCES = ["api.hip", "k_scan.hip", "k_lin.hip", "k_mlp.hip", "k_ns.hip", "k_fused.hip", "k_prologue.hip", "k_features.hip", "k_backward.hip",
+SOURCES = ["api.hip", "k_scan.hip", "k_lin.hip", "k_mlp.hip", "k_ns.hip", "k_fused.hip", "k_prologue.hip", "k_features.hip", "k_backward.hip", "k_nsbwd.hip",
            "k_decode.hip", "k_calib.hip", "k_hsplit.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are kept out of the device code.

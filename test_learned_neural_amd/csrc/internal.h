@@ -223,6 +223,22 @@ atlasmem_status launch_ns_groups(const float* G, int64_t ldG_mat, int n_mat, int
                                  float a, float b, float c, float eps, int prec, const NsUpdate& upd,
                                  hipStream_t st);
 bool fused_supported(const Dims& d);
+// Newton-Schulz forward recomputation and reverse of the outer-loop backward, one workgroup per
+// 64 x 128 working slab (k_nsbwd.hip).  Slab z is matrix z / M (of nm <= 3) of memory z % M, at
+// goff in the memory's P parameters, transposed to its working orientation when tr.  Workspace per
+// slab: X [steps][128][64] (the iterates' transposes), A and B [steps][64][64], sq (|G|^2).
+struct NsSlabGeo {
+  int M, nm;
+  int64_t P;
+  int64_t goff[3];
+  int tr[3];
+};
+bool ns_slab_supported(int rows, int cols, int steps);
+atlasmem_status launch_ns_slab_forward(const NsSlabGeo& g, const float* G, float* X, float* A, float* B, float* sq,
+                                       float* N, int steps, float a, float b, float c, float eps, hipStream_t st);
+atlasmem_status launch_ns_slab_reverse(const NsSlabGeo& g, const float* G, const float* Na, const float* X,
+                                       const float* A, const float* B, const float* sq, float* Ga, int steps, float a,
+                                       float b, float c, float eps, hipStream_t st);
 int64_t fused_split_workspace_floats(const Dims& d);
 // The hidden-split chunk kernel for per-token gates (2-layer SiLU memory, Omega window, features of
 // degree <= 2): chunks [kb0, kb0 + nb) of a call, after the gate scan (and window coefficients) of

@@ -1035,11 +1035,27 @@ static unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
 // shape, else one), keeping its iterates: X_0 = G / (|G| + eps)
 // (working orientation), A_i = X_i X_i^T, B_i = b A_i + c A_i^2, X_{i+1} = a X_i + B_i X_i; the result
 // goes back to G's orientation in N (at the matrix's offset).
+// For the 64 x 128 working shape both directions run as one launch each, one workgroup per slab
+// (k_nsbwd.hip), with the iterates in the same workspace in that kernel's own layout.
+static NsSlabGeo slab_geo(const bk::NsGeo& g) {
+  NsSlabGeo s;
+  s.M = g.M;
+  s.nm = g.nm;
+  s.P = g.P;
+  for (int i = 0; i < 3; ++i) {
+    s.goff[i] = g.goff[i];
+    s.tr[i] = g.tr[i];
+  }
+  return s;
+}
+
 static atlasmem_status ns_forward(const Dims& d, float* ws, const NsLay& n, const float* G, float* N, hipStream_t st) {
   const int steps = d.ns_steps, r = n.r, c = n.c, B = n.g.nm * d.M;  // B: slabs of the batch
   const int64_t rc = (int64_t)r * c, rr = (int64_t)r * r;
   const int64_t xz = (steps + 1) * rc, az = steps * rr;
   float *X = ws + n.x, *A = ws + n.a, *Bm = ws + n.b, *sq = ws + n.sq;
+  if (ns_slab_supported(r, c, steps))
+    return launch_ns_slab_forward(slab_geo(n.g), G, X, A, Bm, sq, N, steps, d.ns_a, d.ns_b, d.ns_c, d.ns_eps, st);
   hipLaunchKernelGGL(bk::ns_gsq_kernel, dim3(B), dim3(256), 0, st, n.g, G, sq);
   hipLaunchKernelGGL(bk::ns_init_kernel, dim3(blocks_of((int64_t)B * rc)), dim3(256), 0, st, n.g, G, sq, d.ns_eps, X,
                      xz, rc);
@@ -1069,6 +1085,9 @@ static atlasmem_status ns_backward(const Dims& d, float* ws, const NsLay& n, con
   const int64_t rc = (int64_t)r * c, rr = (int64_t)r * r;
   const int64_t xz = (steps + 1) * rc, az = steps * rr;
   float *X = ws + n.x, *A = ws + n.a, *Bm = ws + n.b, *Ba = ws + n.ba, *Aa = ws + n.aa;
+  if (ns_slab_supported(r, c, steps))
+    return launch_ns_slab_reverse(slab_geo(n.g), G, Na, X, A, Bm, ws + n.sq, Ga, steps, d.ns_a, d.ns_b, d.ns_c,
+                                  d.ns_eps, st);
   float* xa = ws + n.xa0;
   float* xn = ws + n.xa1;
   hipLaunchKernelGGL(bk::ns_to_work_kernel, dim3(blocks_of((int64_t)B * rc)), dim3(256), 0, st, n.g, Na, xa, rc, rc);
