@@ -420,7 +420,7 @@ atlasmem_status atlasmem_update_chunked_static(const atlasmem_config* cfg, const
   const atlasmem_status v = validate(cfg);
   if (v != ATLASMEM_OK) return v;
   const Dims d = make_dims(cfg);
-  if (cfg->flags != 0 || d.prec != 1 || !fused_supported(d)) return ATLASMEM_E_UNSUPPORTED;
+  if (cfg->flags != 0 || d.prec != 1 || d.gated || !fused_supported(d)) return ATLASMEM_E_UNSUPPORTED;
   if (d.M > fused_static_max_memories()) return ATLASMEM_E_SHAPE;
   if (T < 0 || !W || !Sm) return ATLASMEM_E_INVALID;
   if (T % d.C != 0) return ATLASMEM_E_SHAPE;

@@ -388,8 +388,12 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
 // back from the state it has just stored (W1 from the state, W2^T from T2).  The results are those
 // of the one-workgroup form bit for bit.  The launch is cooperative, so both workgroups of a pair
 // are resident together.
-template <bool RES, bool PL, bool SPLIT>
+template <bool RES, bool PL, bool SPLIT, bool GATED = false>
 __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
+  static_assert(!GATED || (SPLIT && !RES && !PL), "the gated memory runs the two-workgroup form in split bf16");
+  // parameters per memory and the offsets of W3 (gated) and W2 in them
+  constexpr int64_t PM = GATED ? P + P1 : P, O3 = P1, O2 = GATED ? 2 * P1 : P1;
+  constexpr int NSLOT = GATED ? 3 : 2;  // exchange slots per memory (two-workgroup form)
   extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
   float* red = (float*)(sm + LDS_U16);
   const int blk = blockIdx.x;
@@ -431,16 +435,17 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
   const int ysz = a.out_bf16 ? 2 : 4;  // bytes per output element
   const rsrc_t rY = make_rsrc(a.Y ? (const char*)a.Y + (int64_t)m * a.ldT * D * ysz : nullptr,
                               a.Y ? (uint32_t)nT * D * ysz : 0u);
-  const float* Win = a.Win + (int64_t)m * P;
-  const float* Sin = a.Sin + (int64_t)m * P;
-  float* Wout = a.Wout + (int64_t)m * P;
-  float* Sout = a.Sout + (int64_t)m * P;
+  const float* Win = a.Win + (int64_t)m * PM;
+  const float* Sin = a.Sin + (int64_t)m * PM;
+  float* Wout = a.Wout + (int64_t)m * PM;
+  float* Sout = a.Sout + (int64_t)m * PM;
   const int wth = opq(WTH), wtl = opq(WTL);
   const int d2h = opq(D2H), d2l = opq(D2L), dth = opq(DTH), dtl = opq(DTL), xth = opq(XTH);
   const int rb = opq(RB);
 
-  // register slice of W1[h_own][d] (B operand of X W1^T, k = d), four k-steps of 16, hi and lo
-  u32x4 w1h[4], w1l[4];
+  // register slice of W1[h_own][d] (B operand of X W1^T, k = d), four k-steps of 16, hi and lo;
+  // the gated memory's W3 slice likewise
+  u32x4 w1h[4], w1l[4], w3h[4], w3l[4];
   {
   AM_LANE_VARS;
 #pragma unroll
@@ -451,12 +456,18 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
     v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
     v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
     pack8(v, w1h[ks], w1l[ks]);
+    if constexpr (GATED) {
+      const float4 r0 = *(const float4*)(Win + O3 + (int64_t)h_own * D + 16 * ks + 4 * hf);
+      const float4 r1 = *(const float4*)(Win + O3 + (int64_t)h_own * D + 16 * ks + 8 + 4 * hf);
+      const float u[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      pack8(u, w3h[ks], w3l[ks]);
+    }
   }
   // W2 in LDS as [h][v]: B operand of D2 W2 (direct reads) and of H W2^T (transposing reads)
   for (int e = SPLIT ? t - 256 * s : t; e < D * HD; e += (SPLIT ? NT / 2 : NT)) {
     const int vv = e / HD, hh = e % HD;
     uint32_t hi, lo;
-    split_bf16(Win[P1 + e], hi, lo);
+    split_bf16(Win[O2 + e], hi, lo);
     sm[wth + hh * LE + vv] = (uint16_t)hi;
     sm[wtl + hh * LE + vv] = (uint16_t)lo;
   }
@@ -472,7 +483,7 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
         float wv4[4], sv4[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int64_t o = P1 + (int64_t)(32 * tt + 8 * q + 4 * hf + u) * HD + h_own;
+          const int64_t o = O2 + (int64_t)(32 * tt + 8 * q + 4 * hf + u) * HD + h_own;
           wv4[u] = Win[o];
           sv4[u] = Sin[o];
         }
@@ -526,7 +537,7 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
   };
 
   bool bad = false;
-  f32x16 gr[2][2];
+  f32x16 gr[2][2], gr3[2];
   const int hq = opq(HQ);
   // One double group: Z, H and Yh of queries and keys, Y of the queries, then D2, D1 and the
   // gradient accumulation of the keys.
@@ -567,15 +578,40 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
         if constexpr (!PL) zq = mfma32(pq[ks], w1l[ks], zq);
       }
     }
+    // gated: Z3 = X W3^T of keys and queries
+    f32x16 z3k, z3q;
+    if constexpr (GATED) {
+      z3k = zero16();
+      z3q = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        z3k = mfma32(pk[ks], w3h[ks], z3k);
+        z3k = mfma32(pk[ks], w3l[ks], z3k);
+      }
+      if (withq) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          z3q = mfma32(pq[ks], w3h[ks], z3q);
+          z3q = mfma32(pq[ks], w3l[ks], z3q);
+        }
+      }
+    }
     if (g + 1 < ngroups) load_x(k, g + 1, pq, pk);
     else load_x(k + 1, 0, pq, pk);
-    // H = silu(Z) to LDS (keys: region B, queries: HQ), silu'(Z) of the keys kept for D1
-    f32x16 hz, zp;
+    // H = silu(Z) to LDS (keys: region B, queries: HQ), silu'(Z) of the keys kept for D1.  Gated:
+    // H = silu(Z1) Z3, and the keys keep Z3 silu'(Z1) (for D1) and silu(Z1) (for D3)
+    f32x16 hz, zp, a3;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float sg = sigmoidf_(zk[r]);
-      hz[r] = zk[r] * sg;
-      zp[r] = sg * (1.0f + zk[r] * (1.0f - sg));
+      if constexpr (GATED) {
+        a3[r] = zk[r] * sg;
+        hz[r] = a3[r] * z3k[r];
+        zp[r] = z3k[r] * (sg * (1.0f + zk[r] * (1.0f - sg)));
+      } else {
+        hz[r] = zk[r] * sg;
+        zp[r] = sg * (1.0f + zk[r] * (1.0f - sg));
+      }
     }
     u32x4 hph[2], hpl[2];  // hi/lo words of the keys' H, k-steps over the set's rows
 #pragma unroll
@@ -585,7 +621,10 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
     }
     if (withq) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) hz[r] = zq[r] * sigmoidf_(zq[r]);
+      for (int r = 0; r < 16; ++r) {
+        hz[r] = zq[r] * sigmoidf_(zq[r]);
+        if constexpr (GATED) hz[r] *= z3q[r];
+      }
 #pragma unroll
       for (int kl = 0; kl < 2; ++kl) {
         u32x4 qh, ql;
@@ -675,13 +714,20 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
       const u32x4 bl = cat2(lds8(sm, wtl + ob), lds8(sm, wtl + ob + 8));
       p = mmp<PL>(ah, al, bh, bl, p);
     }
+    f32x16 p3;  // gated: D3 = Pm * silu(Z1)
+    if constexpr (GATED) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p3[r] = p[r] * a3[r];
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] *= zp[r];
-    // G1^T += X^T D1 and G2 += D2^T H (k = the set's rows, B operands from registers)
+    // G1^T += X^T D1 and G2 += D2^T H (k = the set's rows, B operands from registers); gated:
+    // G3^T += X^T D3
 #pragma unroll
     for (int kl = 0; kl < 2; ++kl) {
-      u32x4 dh, dl;
+      u32x4 dh, dl, d3h, d3l;
       tile_op(p, kl, dh, dl);
+      if constexpr (GATED) tile_op(p3, kl, d3h, d3l);
       const u32x4 hh = hph[kl], hl = hpl[kl];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -689,6 +735,10 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
         const u32x4 xa = cat2(lds8(sm, xth + o0), lds8(sm, xth + o0 + 8));
         gr[0][tt] = mfma32(xa, dh, gr[0][tt]);
         if constexpr (!PL) gr[0][tt] = mfma32(xa, dl, gr[0][tt]);
+        if constexpr (GATED) {
+          gr3[tt] = mfma32(xa, d3h, gr3[tt]);
+          gr3[tt] = mfma32(xa, d3l, gr3[tt]);
+        }
         const u32x4 ah = cat2(lds8(sm, dth + o0), lds8(sm, dth + o0 + 8));
         const u32x4 al = cat2(lds8(sm, dtl + o0), lds8(sm, dtl + o0 + 8));
         gr[1][tt] = mmp<PL>(ah, al, hh, hl, gr[1][tt]);
@@ -708,15 +758,17 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) gr[i][j] = zero16();
+    if constexpr (GATED) gr3[0] = gr3[1] = zero16();
     for (int g = 0; g < ngroups; ++g) run_group(k, g, pq, pk);
 
     // Swap partial gradients: set 0 keeps G1 and passes its G2 partial, set 1 the reverse.
     // The slots were last read by the final group's H W2^T, before its second barrier.
-    f32x16 x[2];
+    f32x16 x[2], x3[2];
     if constexpr (SPLIT) {
-      // through this memory's exchange slots: slot s holds the partial this set passes on
+      // through this memory's exchange slots: slot s holds the partial this set passes on (gated:
+      // slot 2 set 1's G3 partial)
       AM_LANE_VARS;
-      const rsrc_t rx = make_rsrc(a.xs + (int64_t)m * 2 * P2, (uint32_t)(2 * P2 * 4));
+      const rsrc_t rx = make_rsrc(a.xs + (int64_t)m * NSLOT * P2, (uint32_t)(NSLOT * P2 * 4));
       const int vx = (((w * 2) * 4) * 64 + lane) * 16;  // byte offset of (tile 0, quad 0) of this lane
       if (s == 0) {
 #pragma unroll
@@ -732,6 +784,14 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
           for (int q = 0; q < 4; ++q)
             buf_st4(rx, vx + P2 * 4, ((tt * 4 + q) * 64) * 16,
                     float4{gr[0][tt][4 * q], gr[0][tt][4 * q + 1], gr[0][tt][4 * q + 2], gr[0][tt][4 * q + 3]});
+        if constexpr (GATED) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              buf_st4(rx, vx + 2 * P2 * 4, ((tt * 4 + q) * 64) * 16,
+                      float4{gr3[tt][4 * q], gr3[tt][4 * q + 1], gr3[tt][4 * q + 2], gr3[tt][4 * q + 3]});
+        }
       }
       pair_sync(pair_ctr, pair_target, stuck, pair_local);
       const int vsrc = vx + (s ? 0 : P2 * 4);
@@ -744,6 +804,19 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) x[tt][4 * q + u] = (s ? gr[1][tt][4 * q + u] : gr[0][tt][4 * q + u]) + fv[u];
         }
+      if constexpr (GATED) {
+        if (s == 0) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 f = buf_ld4(rx, vx + 2 * P2 * 4, ((tt * 4 + q) * 64) * 16);
+              const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+              for (int u = 0; u < 4; ++u) x3[tt][4 * q + u] = gr3[tt][4 * q + u] + fv[u];
+            }
+        }
+      }
     } else {
       AM_LANE_VARS;
       float* xg1 = (float*)(sm + opq(XG1));
@@ -785,8 +858,8 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
     // of G1^T (set 0: W1[h_own][d]) or of G2 (set 1: W2[v][h_own], kept transposed in T2 within
     // a launch).  Buffer accesses: one per-lane byte offset, per-register offsets are constants.
     const rsrc_t rt2 = make_rsrc(a.T2 + (int64_t)m * 2 * P2, (uint32_t)(2 * P2 * 4));
-    const rsrc_t rs = s ? rt2 : make_rsrc(Ssrc, (uint32_t)(P * 4));
-    const rsrc_t rw = s ? rt2 : make_rsrc(Wsrc, (uint32_t)(P * 4));
+    const rsrc_t rs = s ? rt2 : make_rsrc(Ssrc, (uint32_t)(PM * 4));
+    const rsrc_t rw = s ? rt2 : make_rsrc(Wsrc, (uint32_t)(PM * 4));
     float sv[2][16], wv[2][16];
     auto pre = [&](auto part) __attribute__((always_inline)) {
       constexpr int tt = decltype(part)::value >> 1, q0 = 2 * (decltype(part)::value & 1);
@@ -840,9 +913,9 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
     u32x4* ho = (u32x4*)(sm + opq(HOFF));
     {
     AM_LANE_VARS;
-    const rsrc_t rs_out = make_rsrc(Sout, (uint32_t)(P * 4)), rw_out = make_rsrc(Wout, (uint32_t)(P * 4));
+    const rsrc_t rs_out = make_rsrc(Sout, (uint32_t)(PM * 4)), rw_out = make_rsrc(Wout, (uint32_t)(PM * 4));
     const bool last = k + 1 == a.nchunks;
-    const int wo1 = (h_own * D + 4 * hf) * 4, wo2 = ((int)P1 + 4 * hf * HD + h_own) * 4;
+    const int wo1 = (h_own * D + 4 * hf) * 4, wo2 = ((int)O2 + 4 * hf * HD + h_own) * 4;
     if (s == 0 || !last) {
       const rsrc_t rs = s ? rt2 : rs_out, rw = s ? rt2 : rw_out;
       const int vs = wo1 + (s ? P2 * 4 : 0);
@@ -864,6 +937,49 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
           buf_st(rs_out, wo2, so, sv[tt][r]);
           buf_st(rw_out, wo2, so, x[tt][r]);
         }
+    }
+    if constexpr (GATED) {
+      // The gated memory's W3: set 0 orthogonalises and applies it after W1, in the same LDS
+      // buffers (the W1 pass's last B X reads only this lane's own X^T rows, which the first
+      // store of this pass overwrites; its A and B buffers are rewritten after barriers).
+      if (s == 0) {
+        const float* W3src = ((k == 0) ? Win : Wout) + O3;
+        const float* S3src = ((k == 0) ? Sin : Sout) + O3;
+        const rsrc_t rs3 = make_rsrc(S3src, (uint32_t)(P1 * 4)), rw3 = make_rsrc(W3src, (uint32_t)(P1 * 4));
+        float sv3[2][16], wv3[2][16];
+        auto pre3 = [&](auto part) __attribute__((always_inline)) {
+          constexpr int tt = decltype(part)::value >> 1, q0 = 2 * (decltype(part)::value & 1);
+          const int vo1 = (h_own * D + 4 * hf) * 4;  // W3[h_own][4hf]
+#pragma unroll
+          for (int q = q0; q < q0 + 2; ++q) {
+            const float4 so = buf_ld4(rs3, vo1, (32 * tt + 8 * q) * 4);
+            const float4 wo = buf_ld4(rw3, vo1, (32 * tt + 8 * q) * 4);
+            sv3[tt][4 * q] = so.x; sv3[tt][4 * q + 1] = so.y; sv3[tt][4 * q + 2] = so.z; sv3[tt][4 * q + 3] = so.w;
+            wv3[tt][4 * q] = wo.x; wv3[tt][4 * q + 1] = wo.y; wv3[tt][4 * q + 2] = wo.z; wv3[tt][4 * q + 3] = wo.w;
+          }
+        };
+        auto bar = [&]() __attribute__((always_inline)) { __syncthreads(); };
+        const int bxh = opq(NX), bah = opq(NA), bbh = opq(NB);
+        newton_schulz1<PL>(x3, sm, bxh, bxh + HD * 64, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red, a, lane, w, pre3,
+                           bar);
+        const rsrc_t rs3o = make_rsrc(Sout + O3, (uint32_t)(P1 * 4)), rw3o = make_rsrc(Wout + O3, (uint32_t)(P1 * 4));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float sn[4], wn[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int r = 4 * q + u;
+              sn[u] = et * sv3[tt][r] - th * x3[tt][r];
+              wn[u] = om * wv3[tt][r] + sn[u];
+              x3[tt][r] = wn[u];
+              if (last) bad |= !(isfinite(sn[u]) && isfinite(wn[u]));
+            }
+            buf_st4(rs3o, wo1, (32 * tt + 8 * q) * 4, float4{sn[0], sn[1], sn[2], sn[3]});
+            buf_st4(rw3o, wo1, (32 * tt + 8 * q) * 4, float4{wn[0], wn[1], wn[2], wn[3]});
+          }
+      }
     }
     if constexpr (!SPLIT) {
     // the handoff lies over both sets' A buffers: wait for the other set's last iteration
@@ -903,6 +1019,7 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
             tile_op(y2[ks >> 1], ks & 1, wh, wl);
             store_rows_T<PL>(sm, wth, wtl, LE, wh, wl, 16 * ks, h_own, hf);
             tile_op(x[ks >> 1], ks & 1, w1h[ks], w1l[ks]);
+            if constexpr (GATED) tile_op(x3[ks >> 1], ks & 1, w3h[ks], w3l[ks]);
           }
         } else {
 #pragma unroll
@@ -919,6 +1036,16 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
             const float4 p1 = buf_ld4(rw1, vw, (16 * ks + 8) * 4);
             const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
             pack8(v, w1h[ks], w1l[ks]);
+          }
+          if constexpr (GATED) {
+            const rsrc_t rw3 = make_rsrc(Wout + O3, (uint32_t)(P1 * 4));
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+              const float4 p0 = buf_ld4(rw3, vw, 16 * ks * 4);
+              const float4 p1 = buf_ld4(rw3, vw, (16 * ks + 8) * 4);
+              const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+              pack8(v, w3h[ks], w3l[ks]);
+            }
           }
         }
         // the next group's first LDS reads of W2^T come after its first barrier
@@ -1438,15 +1565,21 @@ __global__ void residual_output_kernel(const uint16_t* __restrict__ Q, float* __
 
 }  // namespace fz
 
-bool fused_supported(const Dims& d) {
-  return d.kind == ATLASMEM_MLP2_SILU && !d.gated && d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0 && d.dk == fz::D &&
-         d.din == fz::D && d.dv == fz::D && d.dh == fz::HD && d.c == 1 && d.C % fz::GROWS == 0 && d.in_bf16 &&
-         d.prec != 2 && !(d.residual && d.out_bf16);
-}
-
 namespace fz {
 // Memories of one launch of the two-workgroup form: 2 x 8 x ceil(M / 8) workgroups, one per CU.
 constexpr int kSplitMaxMem = 128;
+}  // namespace fz
+
+bool fused_supported(const Dims& d) {
+  const bool shape = d.kind == ATLASMEM_MLP2_SILU && d.gate_mode == ATLASMEM_PER_CHUNK && d.ns_steps > 0 &&
+                     d.dk == fz::D && d.din == fz::D && d.dv == fz::D && d.dh == fz::HD && d.c == 1 &&
+                     d.C % fz::GROWS == 0 && d.in_bf16;
+  // the gated memory: only the two-workgroup form (its registers), split bf16
+  if (d.gated) return shape && !d.residual && d.prec == 1 && d.M <= fz::kSplitMaxMem;
+  return shape && d.prec != 2 && !(d.residual && d.out_bf16);
+}
+
+namespace fz {
 __global__ void zero_ints_kernel(int* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -1455,7 +1588,7 @@ __global__ void zero_ints_kernel(int* p, int n) {
 
 int64_t fused_split_workspace_floats(const Dims& d) {
   if (!fused_supported(d) || d.M > fz::kSplitMaxMem) return 0;
-  return (int64_t)d.M * (2 * fz::P2 + 32);  // exchange slots, then the pairs' counts
+  return (int64_t)d.M * ((d.gated ? 3 : 2) * fz::P2 + 32);  // exchange slots, then the pairs' counts
 }
 
 // The fused kernel sequence over sp.T tokens (a whole number of chunks).  The state moves from
@@ -1475,11 +1608,24 @@ static atlasmem_status launch_fused_bufs(const Dims& d, const void* K, const voi
   if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, fz::LDS_BYTES) != hipSuccess)
     return ATLASMEM_E_DEVICE;
   bool split = xs != nullptr && d.M <= fz::kSplitMaxMem;
-  const void* kern2 = d.residual ? (pl ? (const void*)fz::fused_ns_kernel<true, true, true> : (const void*)fz::fused_ns_kernel<true, false, true>)
+  const void* kern2 = d.gated ? (const void*)fz::fused_ns_kernel<false, false, true, true>
+                    : d.residual ? (pl ? (const void*)fz::fused_ns_kernel<true, true, true> : (const void*)fz::fused_ns_kernel<true, false, true>)
                                  : (pl ? (const void*)fz::fused_ns_kernel<false, true, true> : (const void*)fz::fused_ns_kernel<false, false, true>);
   if (split && hipFuncSetAttribute(kern2, hipFuncAttributeMaxDynamicSharedMemorySize, fz::LDS_BYTES) != hipSuccess)
     return ATLASMEM_E_DEVICE;
-  int* sync = split ? (int*)(xs + (int64_t)d.M * 2 * fz::P2) : nullptr;
+  if (d.gated) {
+    // the gated memory has no one-workgroup form: without room for every pair at once the caller
+    // takes the general path (decided before anything runs)
+    int dev = 0, per_cu = 0, ncu = 0;
+    if (!split || hipGetDevice(&dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern2, fz::NT / 2, fz::LDS_BYTES) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        (int64_t)per_cu * ncu < 16 * ((d.M + 7) / 8)) {
+      (void)hipGetLastError();
+      return ATLASMEM_E_UNSUPPORTED;
+    }
+  }
+  int* sync = split ? (int*)(xs + (int64_t)d.M * (d.gated ? 3 : 2) * fz::P2) : nullptr;
   // one launch per segment of at most 2^22 tokens, so that per-memory byte offsets fit 32 bits
   const int64_t nchunks = sp.T / d.C;
   const int64_t seg = ((int64_t)1 << 22) / d.C;
@@ -1523,6 +1669,7 @@ static atlasmem_status launch_fused_bufs(const Dims& d, const void* K, const voi
       if (hipLaunchCooperativeKernel(kern2, dim3(nblk), dim3(fz::NT / 2), args, fz::LDS_BYTES, st) != hipSuccess) {
         // not every pair can be resident at once on this device: one workgroup per memory instead
         (void)hipGetLastError();
+        if (d.gated) return ATLASMEM_E_DEVICE;
         split = false;
         a.xs = nullptr;
         a.sync = nullptr;

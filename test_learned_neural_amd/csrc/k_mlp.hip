@@ -960,7 +960,11 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
   const int64_t zsz = (int64_t)d.Rt * dz;
   const bool per_token = d.gate_mode == ATLASMEM_PER_TOKEN;
   atlasmem_status stt;
-  if (!d.no_fused && !d.conv && fused_supported(d)) return launch_fused(h, d, K, Q, V, theta, eta, alpha, sp, Y, st);
+  if (!d.no_fused && !d.conv && fused_supported(d)) {
+    // E_UNSUPPORTED: the device cannot hold the gated memory's workgroup pairs; nothing ran
+    const atlasmem_status fs = launch_fused(h, d, K, Q, V, theta, eta, alpha, sp, Y, st);
+    if (fs != ATLASMEM_E_UNSUPPORTED) return fs;
+  }
 
   for (int64_t kb0 = 0; kb0 < nchunks; kb0 += h->ncb) {
     const int nb = (int)((nchunks - kb0) < h->ncb ? (nchunks - kb0) : h->ncb);

@@ -77,3 +77,45 @@ def test_two_workgroup_form_equals_one_workgroup_form(kind, ov):
     one = static_update_run(inp)
     for name, a, b in zip(("Y", "W", "S"), two, one):
         assert np.array_equal(a, b), (name, maxrel(a, b))
+
+
+GATED_CASES = [
+    # (name, overrides, call boundaries or None)
+    ("M3_C128", dict(batch=1, heads=3, T=512), None),
+    ("M13_C64_streamed", dict(batch=1, heads=13, T=320, chunk=64), [0, 64, 65, 192, 320]),
+    ("M2_C192_one_chunk", dict(batch=1, heads=2, T=192, chunk=192), None),
+]
+
+
+@pytest.mark.parametrize("case", GATED_CASES, ids=[c[0] for c in GATED_CASES])
+def test_gated_fused_matches_general_path_and_oracle(case):
+    """The gated memory W2 (silu(W1 x) * (W3 x)) on the two-workgroup fused form (set 0 applies W1
+    and W3, set 1 W2) against the general per-chunk sequence and the fp64 oracle."""
+    name, ov, splits = case
+    inp = synth.make_inputs(4, "literal", kind=synth.MLP2_GATED, **ov)
+    log(f"CASE fused gated {name}")
+    fused = run_gpu(inp, splits=splits)
+    general = run_gpu(inp, splits=splits, flags=am.FLAG_NO_FUSED)
+    assert fused[3] == am.OK and general[3] == am.OK
+    ref = oracle_run(inp)
+    e1 = compare(f"fused_gated_{name}", inp.spec, fused, ref, BF16_TOL)
+    e2 = compare(f"general_gated_{name}", inp.spec, general, ref, BF16_TOL)
+    assert all(v <= BF16_TOL for v in e1.values()), e1
+    assert all(v <= BF16_TOL for v in e2.values()), e2
+    d = max(maxrel(a, b) for a, b in zip(fused[:3], general[:3]))
+    log(f"PARITY fused_gated_vs_general_{name}: {d:.3e}")
+    assert d > 0.0  # different summation orders: the fused kernel ran
+
+
+def test_gated_fused_benchmark_size_sampled():
+    """128 memories x 4096 tokens of the gated memory (the benchmark's stage shape) in one call; the
+    oracle recomputes two sampled memories over the whole sequence."""
+    inp = synth.make_inputs(4, "literal", kind=synth.MLP2_GATED, T=4096)
+    log("CASE fused gated 128 x 4096")
+    got = run_gpu(inp)
+    assert got[3] == am.OK
+    mems = [3, 126]
+    ref = oracle_run(inp, mems=mems)
+    sub = (got[0][mems], got[1][mems], got[2][mems])
+    errs = compare("fused_gated_128x4096_memories_3_126", inp.spec, sub, ref, BF16_TOL)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
