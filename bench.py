@@ -111,7 +111,8 @@ def ns_flops_per_matrix(rows, cols, steps):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns5_B8H16_T32768_fused_kernel_traffic.txt")
-FUSED_SOURCES = [os.path.join(ROOT, "test_learned_neural_amd", "csrc", f) for f in ("k_fused.hip", "common.h")]
+FUSED_SOURCES = [os.path.join(ROOT, "test_learned_neural_amd", "csrc", f) for f in ("k_fused.hip", "common.h",
+                                                                                  "mfma_tiles.h")]
 
 
 def measured_traffic():

@@ -254,7 +254,9 @@ struct Part {
 // pre(Part<p>) (p = 0..3) is called before iteration p: it issues the p-th quarter of the state
 // loads, so that they stream in under the matrix work instead of stalling the vector memory path
 // all at once.
-template <bool PL, class Pre, class Bar>
+// KEEP: B X takes its X operand from the split words this lane stored for X^T (kept in registers,
+// one wave per SIMD has the room) instead of reading them back.
+template <bool PL, bool KEEP = false, class Pre, class Bar>
 __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int bxh, int bxl, int bah, int bal,
                                                int bbh, int bbl, float* red, const Args& a, int lane, int w,
                                                Pre&& pre, Bar&& set_bar) {
@@ -288,7 +290,9 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
   const int ta1 = c1 * 64 + (ra ^ swz(c1)), ta2 = c2 * 64 + (ra ^ swz(c2));
   const int tb1 = c1 * 64 + (rb ^ swz(c1)), tb2 = c2 * 64 + (rb ^ swz(c2));
   auto iteration = [&]() __attribute__((always_inline)) {
-    // X^T to LDS: tile t, quad q of this lane = rows 32t + 8q + 4hf .. +3 of column cx
+    // X^T to LDS: tile t, quad q of this lane = rows 32t + 8q + 4hf .. +3 of column cx (with KEEP
+    // also the k-step words of B X: k-step 2t + q/2, words 2(q%2) and 2(q%2) + 1)
+    u32x4 kh[4], kl[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -299,6 +303,12 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
         const int o = opv(xrow + ((32 * t + 8 * q) ^ xsw));
         *(uint2*)(sm + bxh + o) = uint2{h0, h1};
         if constexpr (!PL) *(uint2*)(sm + bxl + o) = uint2{l0, l1};
+        if constexpr (KEEP) {
+          kh[2 * t + (q >> 1)][2 * (q & 1)] = h0;
+          kh[2 * t + (q >> 1)][2 * (q & 1) + 1] = h1;
+          kl[2 * t + (q >> 1)][2 * (q & 1)] = l0;
+          kl[2 * t + (q >> 1)][2 * (q & 1) + 1] = l1;
+        }
       }
     set_bar();
     // A = X X^T, tile (rt, ct), k = the 128 columns in steps of 16 (natural order)
@@ -347,9 +357,15 @@ __device__ __forceinline__ void newton_schulz1(f32x16 (&x)[2], uint16_t* sm, int
       for (int r = 0; r < 16; ++r) x[t][r] *= a.ns_a;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const int o1 = opv(xrow + ((16 * ks) ^ xsw)), o2 = opv(xrow + ((16 * ks + 8) ^ xsw));
-      const u32x4 xh = cat2(lds8(sm, bxh + o1), lds8(sm, bxh + o2));
-      const u32x4 xl = cat2(lds8(sm, bxl + o1), lds8(sm, bxl + o2));
+      u32x4 xh, xl;
+      if constexpr (KEEP) {
+        xh = kh[ks];
+        xl = kl[ks];
+      } else {
+        const int o1 = opv(xrow + ((16 * ks) ^ xsw)), o2 = opv(xrow + ((16 * ks + 8) ^ xsw));
+        xh = cat2(lds8(sm, bxh + o1), lds8(sm, bxh + o2));
+        xl = cat2(lds8(sm, bxl + o1), lds8(sm, bxl + o2));
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int o0 = brow + 32 * t * LE + 16 * ks;
@@ -882,8 +898,8 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
         if constexpr (SPLIT) __syncthreads();
         else set_barrier(set_count, set_target, stuck, lane);
       };
-      newton_schulz1<PL>(x, sm, bxh, bxh + HD * 64, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red + 4 * s, a, lane,
-                         w, pre, set_bar);
+      newton_schulz1<PL, SPLIT>(x, sm, bxh, bxh + HD * 64, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red + 4 * s, a,
+                                lane, w, pre, set_bar);
     }
     // S = eta S - theta NS(G), W = (1 - alpha) W + S for this set's matrix
 #pragma unroll
@@ -960,8 +976,8 @@ __global__ void __launch_bounds__(SPLIT ? NT / 2 : NT) fused_ns_kernel(Args a) {
         };
         auto bar = [&]() __attribute__((always_inline)) { __syncthreads(); };
         const int bxh = opq(NX), bah = opq(NA), bbh = opq(NB);
-        newton_schulz1<PL>(x3, sm, bxh, bxh + HD * 64, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red, a, lane, w, pre3,
-                           bar);
+        newton_schulz1<PL, true>(x3, sm, bxh, bxh + HD * 64, bah, bah + 64 * LD, bbh, bbh + 64 * LE, red, a, lane, w,
+                                 pre3, bar);
         const rsrc_t rs3o = make_rsrc(Sout + O3, (uint32_t)(P1 * 4)), rw3o = make_rsrc(Wout + O3, (uint32_t)(P1 * 4));
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
