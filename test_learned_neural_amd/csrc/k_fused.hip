@@ -1623,7 +1623,10 @@ static atlasmem_status launch_fused_bufs(const Dims& d, const void* K, const voi
                                 : (pl ? (const void*)fz::fused_ns_kernel<false, true, false> : (const void*)fz::fused_ns_kernel<false, false, false>);
   if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, fz::LDS_BYTES) != hipSuccess)
     return ATLASMEM_E_DEVICE;
-  bool split = xs != nullptr && d.M <= fz::kSplitMaxMem;
+  // the two-workgroup form for calls of at least four chunks (measured: a call of one or two chunks
+  // takes longer in wall time with the cooperative launch than on one workgroup per memory); the
+  // gated memory has only that form
+  bool split = xs != nullptr && d.M <= fz::kSplitMaxMem && (sp.T / d.C >= 4 || d.gated);
   const void* kern2 = d.gated ? (const void*)fz::fused_ns_kernel<false, false, true, true>
                     : d.residual ? (pl ? (const void*)fz::fused_ns_kernel<true, true, true> : (const void*)fz::fused_ns_kernel<true, false, true>)
                                  : (pl ? (const void*)fz::fused_ns_kernel<false, true, true> : (const void*)fz::fused_ns_kernel<false, false, true>);

@@ -62,14 +62,15 @@ def test_fused_full_size_sampled():
 @pytest.mark.parametrize("kind,ov", [
     (synth.MLP2_SILU, dict(batch=8, heads=16, T=640)),                 # 128 memories: every CU a set
     (synth.MLP2_SILU, dict(batch=1, heads=13, T=256, chunk=64)),       # pairs past the last memory exit
-    (synth.MLP2_SILU, dict(batch=1, heads=2, T=128)),                  # one chunk: no weight handoff
-    (synth.MLP2_SILU_RESIDUAL, dict(batch=2, heads=5, T=384, chunk=192)),
-], ids=["M128_C128", "M13_C64", "M2_one_chunk", "residual_M10_C192"])
+    (synth.MLP2_SILU, dict(batch=1, heads=2, T=512)),                  # four chunks, the shortest call
+    (synth.MLP2_SILU_RESIDUAL, dict(batch=2, heads=5, T=768, chunk=192)),
+], ids=["M128_C128", "M13_C64", "M2_four_chunks", "residual_M10_C192"])
 def test_two_workgroup_form_equals_one_workgroup_form(kind, ov):
-    """For up to 128 memories a handle runs each memory's two sets as two workgroups on different
-    CUs, which exchange partial gradients and new weights through global memory; the allocation-free
-    entry point runs one workgroup per memory with the same arithmetic.  The results agree bit for
-    bit, and the handle reports no failed wait (the flag that get_state checks)."""
+    """For up to 128 memories and calls of at least four chunks a handle runs each memory's two
+    sets as two workgroups on different CUs, which exchange partial gradients and new weights
+    through global memory; the allocation-free entry point runs one workgroup per memory with the
+    same arithmetic.  The results agree bit for bit, and the handle reports no failed wait (the
+    flag that get_state checks)."""
     inp = synth.make_inputs(4, "literal", kind=kind, **ov)
     log(f"CASE fused two-workgroup form: kind {kind} memories {inp.spec.n_mem} T {inp.spec.T} "
         f"chunk {inp.spec.chunk}")
