@@ -172,6 +172,143 @@ __global__ void __launch_bounds__(256) feature_kernel(FeatureArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------- projection
+//
+// phi_c(X) P^T on the matrix cores, the features formed where they are used: a workgroup takes
+// 128 input rows (staged in LDS as fp32, with the monomial table of every feature) and walks the
+// features in blocks of 64; each block's P columns are split into bf16 hi / lo in LDS once for the
+// workgroup (the next block's values loaded while the current one is used), and each wave forms
+// its 32 rows' features of a k-step from the staged rows (one table read and at most three row
+// reads per feature) and multiplies them on the matrix cores (v_mfma_f32_32x32x16_bf16, hi*hi +
+// hi*lo + lo*hi, fp32 accumulation) into its 32 x d_out outputs.
+namespace fpj {
+constexpr int NT = 256;     // four waves
+constexpr int RT = 1;       // row tiles per wave: wave w takes rows 32w + 128t .. +31 (t < RT);
+                            // two tiles per wave measured slower (more registers, fewer workgroups)
+constexpr int ROWS = 128 * RT;  // input rows per workgroup
+constexpr int KB = 64;      // features per block
+constexpr int LP = KB + 8;  // P block row stride (uint16): 16-byte reads along k land on distinct banks
+constexpr int kMaxD = 64, kMaxOut = 128, kMaxF = 8192;
+
+struct Args {
+  const void* X;
+  int in_bf16;
+  int64_t n;
+  int d, F, d_out;
+  float c[4];
+  const float* P;  // [d_out][F]
+  float* out;      // [n][d_out]
+};
+
+__host__ __device__ constexpr int fpad(int F) { return (F + KB - 1) / KB * KB; }
+inline size_t lds_bytes(int d, int F, int nc) {
+  return (size_t)ROWS * (d + 1) * 4 + (size_t)fpad(F) * 4 + (size_t)nc * 32 * LP * 2 * 2;
+}
+
+template <int NC>
+__global__ void __launch_bounds__(NT) feat_proj_kernel(Args a) {
+  extern __shared__ __attribute__((aligned(16))) float fsm[];
+  const int xs = a.d + 1;  // row stride: lanes of consecutive rows on distinct banks
+  float* xr = fsm;
+  uint32_t* tab = (uint32_t*)(xr + ROWS * xs);
+  const int FP = fpad(a.F);
+  uint16_t* pbh = (uint16_t*)(tab + FP);
+  uint16_t* pbl = pbh + NC * 32 * LP;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+  const int nr = (int)((a.n - r0) < ROWS ? (a.n - r0) : ROWS);
+  for (int e = tid; e < ROWS * a.d; e += NT) {
+    const int r = e / a.d, i = e - r * a.d;
+    xr[r * xs + i] = r < nr ? load_in(a.X, (r0 + r) * a.d + i, a.in_bf16) : 0.0f;
+  }
+  {  // the monomial table: each thread decodes one run of features and steps through it
+    const int per = (FP + NT - 1) / NT;
+    const int f0 = tid * per;
+    if (f0 < a.F) {
+      Mono m = mono_of(f0, a.d);
+      for (int u = 0; u < per && f0 + u < a.F; ++u) {
+        tab[f0 + u] = mono_code(m);
+        if (f0 + u + 1 < a.F) m = mono_next(m, a.d);
+      }
+    }
+  }
+  f32x16 acc[RT][NC];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][ct][r] = 0.0f;
+  // P block: rows o < 32 NC, features fb .. fb + 63; thread element i is e = tid + 256 i.  The next
+  // block's values are loaded while the current block's products run.
+  constexpr int PE = NC * 32 * KB / NT;
+  float pv[PE];
+  auto load_p = [&](int fb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      const int e = tid + NT * i, o = e / KB, f = fb + (e - o * KB);
+      pv[i] = (o < a.d_out && f < a.F) ? a.P[(int64_t)o * a.F + f] : 0.0f;
+    }
+  };
+  load_p(0);
+  for (int fb = 0; fb < FP; fb += KB) {
+    __syncthreads();  // the staging above, or the previous block's reads of the P block
+    // the block split into bf16 hi / lo ([o][k])
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      const int e = tid + NT * i, o = e / KB, k = e - o * KB;
+      uint32_t h, l;
+      split_bf16(pv[i], h, l);
+      pbh[o * LP + k] = (uint16_t)h;
+      pbl[o * LP + k] = (uint16_t)l;
+    }
+    if (fb + KB < FP) load_p(fb + KB);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KB / 16; ++ks) {
+      const int kk = 16 * ks + 8 * hf;  // this lane's 8 features of the k-step (both operands)
+      u32x4 ah[RT], al[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const float* x = xr + (32 * w + 128 * t + l32) * xs;  // this lane's row of tile t
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int f = fb + kk + u;
+          v[u] = f < a.F ? code_value(tab[f], x, a.c) : 0.0f;
+        }
+        pack8(v, ah[t], al[t]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        const int ob = (32 * ct + l32) * LP + kk;
+        const u32x4 bh = *(const u32x4*)(pbh + ob), bl = *(const u32x4*)(pbl + ob);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          acc[t][ct] = mfma32(ah[t], bh, acc[t][ct]);
+          acc[t][ct] = mfma32(ah[t], bl, acc[t][ct]);
+          acc[t][ct] = mfma32(al[t], bh, acc[t][ct]);
+        }
+      }
+    }
+  }
+  // register r of tile t: row 32w + 128t + 8(r/4) + 4hf + r%4, column 32ct + l32
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      const int col = 32 * ct + l32;
+      if (col >= a.d_out) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * w + 128 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (row < nr) a.out[(r0 + row) * a.d_out + col] = acc[t][ct][r];
+      }
+    }
+}
+}  // namespace fpj
+
 // A operand phi_c(X) for the projection product: row = input row, k = feature.
 struct FeatMapA {
   const void* X;
@@ -265,6 +402,32 @@ atlasmem_status launch_feature_map(const void* X, bool in_bf16, int64_t n, int d
     AM_LAUNCH_CHECK();
     return ATLASMEM_OK;
   }
+  if (d <= fpj::kMaxD && F <= fpj::kMaxF && d_out <= fpj::kMaxOut) {
+    fpj::Args a;
+    a.X = X;
+    a.in_bf16 = in_bf16;
+    a.n = n;
+    a.d = d;
+    a.F = (int)F;
+    a.d_out = d_out;
+    for (int k = 0; k < 4; ++k) a.c[k] = c4[k];
+    a.P = P;
+    a.out = out;
+    const int nc = (d_out + 31) / 32;
+    const size_t lds = fpj::lds_bytes(d, (int)F, nc);
+    const int64_t blocks = (n + fpj::ROWS - 1) / fpj::ROWS;
+    if (blocks > INT32_MAX) return ATLASMEM_E_SHAPE;
+    void (*kern)(fpj::Args) = nc == 1 ? fpj::feat_proj_kernel<1>
+                              : nc == 2 ? fpj::feat_proj_kernel<2>
+                              : nc == 3 ? fpj::feat_proj_kernel<3>
+                                        : fpj::feat_proj_kernel<4>;
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return ATLASMEM_E_DEVICE;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(fpj::NT), lds, st, a);
+    AM_LAUNCH_CHECK();
+    return ATLASMEM_OK;
+  }
+  // wider rows, more features or outputs: the GEMM engine with the features formed in its loader
   FeatMapA la;
   la.X = X;
   la.in_bf16 = in_bf16;

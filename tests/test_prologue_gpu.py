@@ -223,6 +223,10 @@ FMAP_CASES = [
     ("deg2_project_d64", 300, 16, 2, am.BF16, None, 64),
     ("deg3_project_ragged_d70", 130, 6, 3, am.F32, [1.0, 1.0, 0.5, 0.2], 70),
     ("deg1_project_d5", 77, 9, 1, am.BF16, None, 5),
+    ("deg3_project_d128_four_tiles", 257, 12, 3, am.BF16, [1.0, 0.8, 0.5, 0.25], 128),
+    # beyond the matrix-core kernel's limits (d_out > 128, rows wider than 64): the GEMM engine
+    ("deg2_project_d200_engine", 70, 8, 2, am.F32, None, 200),
+    ("deg2_project_rows70_engine", 40, 70, 2, am.BF16, None, 32),
 ]
 
 
