@@ -106,7 +106,7 @@ __device__ __forceinline__ float code_value(uint32_t code, const float* x, const
 // kFeatRows input rows per block in LDS, then the monomial table (TAB, when it fits) so that each
 // feature costs one table read; the block streams the rows' contiguous features out as 16-byte
 // stores.  Without the table a thread decodes the monomial of each run of four features.
-constexpr int kFeatRows = 32;
+constexpr int kFeatRows = 8;
 constexpr int kFeatTabMax = 12288;  // table entries (48 KB)
 template <bool TAB>
 __global__ void __launch_bounds__(256) feature_kernel(FeatureArgs a) {
@@ -127,17 +127,28 @@ __global__ void __launch_bounds__(256) feature_kernel(FeatureArgs a) {
     }
   }
   __syncthreads();
-  const int64_t total = (int64_t)nr * a.F;
+  // a block's nr * F <= 32 * 2^20 elements fit 32-bit indices; the row and feature of e0 advance
+  // by a fixed step each iteration, so no division runs inside the loop
+  const int F = (int)a.F;
+  const int total = nr * F;
   float* base = a.out + r0 * a.F;
   const bool vec = ((r0 * a.F) & 3) == 0 && (((uintptr_t)a.out) & 15) == 0;
-  for (int64_t e0 = (int64_t)threadIdx.x * 4; e0 < total; e0 += (int64_t)blockDim.x * 4) {
-    int64_t r = e0 / a.F;
-    int64_t f = e0 - r * a.F;
+  const int step = blockDim.x * 4;
+  const int step_r = step / F, step_f = step - step_r * F;
+  int row_e = (threadIdx.x * 4) / F, f_e = threadIdx.x * 4 - row_e * F;
+  for (int e0 = threadIdx.x * 4; e0 < total; e0 += step) {
+    int r = row_e, f = f_e;
+    row_e += step_r;
+    f_e += step_f;
+    if (f_e >= F) {
+      f_e -= F;
+      ++row_e;
+    }
     float v[4];
     if (TAB) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (f == a.F) {
+        if (f == F) {
           ++r;
           f = 0;
         }
@@ -149,14 +160,14 @@ __global__ void __launch_bounds__(256) feature_kernel(FeatureArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (e0 + u < total) {
-          if (f == a.F) {  // the next row starts
+          if (f == F) {  // the next row starts
             ++r;
             f = 0;
             m = Mono{0, 0, 0, 0};
           }
           v[u] = mono_value(m, xr + r * a.d, a.c);
           ++f;
-          if (f < a.F) m = mono_next(m, a.d);
+          if (f < F) m = mono_next(m, a.d);
         } else {
           v[u] = 0.0f;
         }
