@@ -441,22 +441,34 @@ __global__ void __launch_bounds__(kGateWaves * 64) gates_kernel(GateArgs a) {
       if (t0 < a.T) {
         // rows past T read as zero (range-checked buffer loads), so they add nothing
         const int voff = (int)(((t0 + l32) * a.dm + 8 * hf) * 2);
-        for (int k0 = 0; k0 < ksteps; k0 += 8) {
-          u32x4 xa[8];
+        // k-steps in runs of four, double-buffered: the next run's loads are issued before the
+        // current run's products, so a wave keeps eight 16-byte loads per lane in flight throughout
+        constexpr int KR = 4;
+        auto load_run = [&](int k0, u32x4 (&x)[KR]) __attribute__((always_inline)) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) xa[i] = buf_ld16(rU, voff + (k0 + i) * 32, 0);
+          for (int i = 0; i < KR; ++i) x[i] = buf_ld16(rU, voff + (k0 + i) * 32, 0);
+        };
+        auto mul_run = [&](int k0, const u32x4 (&x)[KR]) __attribute__((always_inline)) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
+          for (int i = 0; i < KR; ++i) {
             if (k0 + i < ksteps) {
               const int ko = 16 * (k0 + i) + 8 * hf;
 #pragma unroll
               for (int j = 0; j < 2; ++j) {
                 const int o = (32 * j + l32) * ldw + ko;
-                acc[j] = mfma32(xa[i], *(const u32x4*)(wh + o), acc[j]);
-                acc[j] = mfma32(xa[i], *(const u32x4*)(wl + o), acc[j]);
+                acc[j] = mfma32(x[i], *(const u32x4*)(wh + o), acc[j]);
+                acc[j] = mfma32(x[i], *(const u32x4*)(wl + o), acc[j]);
               }
             }
           }
+        };
+        u32x4 xa[KR], xb[KR];
+        load_run(0, xa);
+        for (int k0 = 0; k0 < ksteps; k0 += 2 * KR) {
+          if (k0 + KR < ksteps) load_run(k0 + KR, xb);
+          mul_run(k0, xa);
+          if (k0 + 2 * KR < ksteps) load_run(k0 + 2 * KR, xa);
+          if (k0 + KR < ksteps) mul_run(k0 + KR, xb);
         }
       }
       if (POOL) {
