@@ -117,8 +117,9 @@ typedef struct {
 } atlasmem_config;
 
 /* Force the general per-chunk kernel sequence even where a fused whole-call kernel exists
- * (the fused kernel covers the 64 -> 128 -> 64 MLP memory with per-chunk gates and
- * Newton-Schulz, bf16 inputs, split precision).  Results agree within rounding. */
+ * (the fused kernels cover the 64 -> 128 -> 64 MLP memory, plain, residual or gated, with
+ * per-chunk gates and Newton-Schulz, bf16 inputs, split precision, and the plain or residual one
+ * with per-token gates in chunks of 64).  Results agree within rounding. */
 #define ATLASMEM_FLAG_NO_FUSED 1
 /* Per-token retrieval: Y[t] = M_{W_t}(phi(Q[t])) with W_t the state right after token t's
  * update, instead of the chunk-start weights (Atlas-Torch README, "Known deviations from the
@@ -252,8 +253,9 @@ void atlasmem_destroy(atlasmem_handle h);
  * loops, harnesses that forbid hipMalloc): atlasmem_update_chunked without a handle, for the
  * configurations the fused whole-call kernel covers (the 64 -> 128 -> 64 SiLU memory, plain or
  * residual, PER_CHUNK gates, ns_steps >= 1, window 1, poly_degree 1, bf16 inputs, AUTO / BF16X3
- * precision, chunk a multiple of 64, flags 0; E_UNSUPPORTED otherwise).  Same results as
- * update_chunked from the same state over the same tokens.
+ * precision, chunk a multiple of 64, flags 0; E_UNSUPPORTED otherwise, the gated memory
+ * included).  Same results as update_chunked from the same state over the same tokens, bit for
+ * bit (the handle may run each memory over two workgroups, this entry point one).
  *   cfg:   validated as by atlasmem_create (batch * heads <= ATLASMEM_STATIC_MAX_MEMORIES, else
  *          E_SHAPE)
  *   K, Q, V, theta, eta, alpha, Y: as in atlasmem_update_chunked, with T a multiple of the chunk
