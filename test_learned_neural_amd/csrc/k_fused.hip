@@ -1688,7 +1688,9 @@ static atlasmem_status launch_fused_bufs(const Dims& d, const void* K, const voi
       if (hipLaunchCooperativeKernel(kern2, dim3(nblk), dim3(fz::NT / 2), args, fz::LDS_BYTES, st) != hipSuccess) {
         // not every pair can be resident at once on this device: one workgroup per memory instead
         (void)hipGetLastError();
-        if (d.gated) return ATLASMEM_E_DEVICE;
+        // the gated memory has no one-workgroup form: the caller takes the general path (only the
+        // pairs' counts were cleared, and a refusal repeats for every segment, so it is the first)
+        if (d.gated) return ATLASMEM_E_UNSUPPORTED;
         split = false;
         a.xs = nullptr;
         a.sync = nullptr;

@@ -961,7 +961,8 @@ atlasmem_status mlp_update(Handle* h, const Dims& d, const void* K, const void* 
   const bool per_token = d.gate_mode == ATLASMEM_PER_TOKEN;
   atlasmem_status stt;
   if (!d.no_fused && !d.conv && fused_supported(d)) {
-    // E_UNSUPPORTED: the device cannot hold the gated memory's workgroup pairs; nothing ran
+    // E_UNSUPPORTED: the gated memory's workgroup pairs cannot all be resident (or the cooperative
+    // launch was refused); nothing ran
     const atlasmem_status fs = launch_fused(h, d, K, Q, V, theta, eta, alpha, sp, Y, st);
     if (fs != ATLASMEM_E_UNSUPPORTED) return fs;
   }
