@@ -198,15 +198,18 @@ __global__ void splitk_reduce_kernel(int M, int N, int batch, int nsplit, const 
   else ep(z, row, col, v);
 }
 
-// Slices for a product of `tiles` output tiles and nk >= 4 k-steps: enough workgroups to spread
-// over the chip (about four per CU), at least two k-steps per slice, and partials that fit the
-// scratch.
+// Slices for a product of `tiles` output tiles and nk >= 2 k-steps: enough workgroups to spread
+// over the chip (about four per CU) and partials that fit the scratch.  Up to 12 k-steps a slice
+// may be a single step (the short products of eight memories' chunks, 8-16 tiles each, are
+// latency-bound chains); longer k ranges keep at least two steps per slice, where more slices
+// only add partial-sum traffic.
 inline int splitk_slices(int M, int N, int K, int batch, int64_t scratch_floats) {
   const int64_t tiles = (int64_t)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * batch;
   const int nk = (K + GK - 1) / GK;
-  if (scratch_floats <= 0 || tiles > 256 || nk < 4) return 1;
+  if (scratch_floats <= 0 || tiles > 256 || nk < 2) return 1;
   int ns = (int)((1024 + tiles - 1) / tiles);
-  if (ns > nk / 2) ns = nk / 2;
+  const int cap = nk <= 12 ? nk : nk / 2;
+  if (ns > cap) ns = cap;
   while (ns > 1 && (int64_t)ns * batch * M * N > scratch_floats) --ns;
   return ns < 1 ? 1 : ns;
 }

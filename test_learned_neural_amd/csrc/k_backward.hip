@@ -539,7 +539,6 @@ __global__ void gate_bwd_kernel(const float* __restrict__ theta, const float* __
   float* w = gb + 2 * C;
   float* ea = gb + 3 * C;
   float* wa = gb + 4 * C;
-  float* ba = gb + 5 * C;
   float* th = gb + 6 * C;
   float* et = gb + 7 * C;
   float* al = gb + 8 * C;
@@ -737,6 +736,18 @@ __global__ void omega_adj_kernel(const float* __restrict__ oWa, const float* __r
 __global__ void fill_kernel(float* __restrict__ p, int64_t n, float v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
+}
+
+// The chunk-start state of memories m = y, y + gridDim.y, ... into the checkpoint rows:
+// ck[m][0, P) = W[m], ck[m][P, 2P) = S[m] (one launch for both, in place of two strided copies).
+__global__ void checkpoint_kernel(const float* __restrict__ W, const float* __restrict__ S, int64_t P, int64_t M,
+                                  float* __restrict__ ck) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= P) return;
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+    ck[m * 2 * P + r] = W[m * P + r];
+    ck[m * 2 * P + P + r] = S[m * P + r];
+  }
 }
 
 // Per-chunk gates: SAt = SA + WA (S_end also feeds W_end); per memory the gate adjoints
@@ -1171,13 +1182,9 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
   // ---- forward, saving the state at every chunk start
   for (int64_t k = 0; k < nch; ++k) {
     float* ck = ws + L.ck + k * M * 2 * P;
-    if (hipMemcpy2DAsync(ck, 2 * P * sizeof(float), h->W[h->cur], P * sizeof(float), P * sizeof(float), M,
-                         hipMemcpyDeviceToDevice, st) != hipSuccess ||
-        hipMemcpy2DAsync(ck + P, 2 * P * sizeof(float), h->S[h->cur], P * sizeof(float), P * sizeof(float), M,
-                         hipMemcpyDeviceToDevice, st) != hipSuccess) {
-      (void)hipGetLastError();
-      return ATLASMEM_E_DEVICE;
-    }
+    hipLaunchKernelGGL(bk::checkpoint_kernel, dim3(blocks_of(P), (unsigned)(M < 65535 ? M : 65535)), dim3(256), 0, st,
+                       (const float*)h->W[h->cur], (const float*)h->S[h->cur], (int64_t)P, (int64_t)M, ck);
+    AM_LAUNCH_CHECK();
     const int64_t s = k * C;
     const int64_t go = per_chunk ? k : s;  // this chunk's gates
     const atlasmem_status stt =
