@@ -521,7 +521,8 @@ __global__ void scalar_adj_kernel(const float* __restrict__ WA, const float* __r
 }
 
 // Reverse of the gate scan for one chunk of every memory (thread 0 of a block per memory walks the
-// chunk; e, b, w recomputed in LDS):  e_{C-1} = b_{C-1} = w_{C-1} = 1, e_r = eta_{r+1} e_{r+1},
+// chunk's two recurrences, the block's threads share out the per-step terms between them; e, b, w
+// recomputed in LDS):  e_{C-1} = b_{C-1} = w_{C-1} = 1, e_r = eta_{r+1} e_{r+1},
 // b_r = (1 - alpha_{r+1}) b_{r+1}, w_r = b_r + eta_{r+1} w_{r+1}, cS = theta e, cW = theta w,
 // PC = eta_0 e_0, beta = (1 - alpha_0) b_0, aS = eta_0 w_0.
 __global__ void gate_bwd_kernel(const float* __restrict__ theta, const float* __restrict__ eta,
@@ -571,14 +572,17 @@ __global__ void gate_bwd_kernel(const float* __restrict__ theta, const float* __
       b[r] = bc;
       w[r] = wc;
     }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < C; r += blockDim.x) {  // per-step terms: every thread
+    const float cw = cwv[r], cs = csv[r];
+    oth[r] = cs * e[r] + cw * w[r];
+    ea[r] = cs * th[r];
+    wa[r] = cw * th[r];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
     const float PCa = sca[z * 3 + 0], betaa = sca[z * 3 + 1], aSa = sca[z * 3 + 2];
-#pragma unroll 4
-    for (int r = 0; r < C; ++r) {
-      const float cw = cwv[r], cs = csv[r];
-      oth[r] = cs * e[r] + cw * w[r];
-      ea[r] = cs * th[r];
-      wa[r] = cw * th[r];
-    }
     oet[0] = PCa * e[0] + aSa * w[0];
     float ea_c = ea[0] + PCa * et[0];
     float wa_c = wa[0] + aSa * et[0];
