@@ -184,6 +184,51 @@ __global__ void __launch_bounds__(256) gemm_part_kernel(int M, int N, int K, int
                                      kb, ke);
 }
 
+// Split-K inside one workgroup, for products of at most KGROUPS k-steps: group g (256 threads)
+// forms the partial tile of k-step g, writes it over its own LDS operand buffers, and after a
+// barrier the workgroup sums the groups' partials in group order (the order of the launched
+// slices' reduction) and applies the product's epilogue.  No partial tiles in global memory and
+// no reduction launch.  Taken where the product has at least KGROUP_MIN_TILES output tiles (128
+// memories of the 64 -> 128 -> 64 memory on MI355X: per-chunk path 4.79 -> 4.15 ms, its outer
+// backward 17.9 -> 16.5 ms); with fewer, one workgroup per k-step spreads a tile's loads over more
+// CUs, which eight memories' products (8-16 tiles) need (per-token retrieval 8.1 -> 9.1 ms).
+constexpr int KGROUPS = 4;
+constexpr int KGROUP_MIN_TILES = 128;
+template <bool SPLIT, bool A_EXACT, bool B_EXACT>
+union KGroupSmem {  // a group's operand buffers, then its partial tile
+  TileSmem<SPLIT, A_EXACT, B_EXACT> tile;
+  float red[GT * GT];
+};
+
+struct EpiLdsTile {  // element (row, col) of the tile at (m0, n0) into red[(row - m0) * GT + col - n0]
+  float* red;
+  int m0, n0;
+  __device__ __forceinline__ void operator()(int, int row, int col, float v) const {
+    red[(row - m0) * GT + (col - n0)] = v;
+  }
+};
+
+template <bool SPLIT, bool A_EXACT, bool B_EXACT, class LA, class LB, class EP>
+__global__ void __launch_bounds__(256 * KGROUPS) gemm_kgroup_kernel(int M, int N, int K, LA la, LB lb, EP ep) {
+  __shared__ __attribute__((aligned(16))) KGroupSmem<SPLIT, A_EXACT, B_EXACT> sm[KGROUPS];
+  const int ng = blockDim.x >> 8;  // groups: the product's k-steps (2 .. KGROUPS)
+  const int g = threadIdx.x >> 8, t = threadIdx.x & 255;
+  const int z = blockIdx.z, m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  // gemm_tile's last k-step ends at a barrier, after which its epilogue may overwrite the
+  // group's operand buffers
+  gemm_tile<SPLIT, A_EXACT, B_EXACT>(M, N, K, la, lb, EpiLdsTile{sm[g].red, m0, n0}, z, m0, n0, t, sm[g].tile, true,
+                                     g * GK, g * GK + GK);
+  __syncthreads();
+  for (int e = threadIdx.x; e < GT * GT; e += blockDim.x) {
+    const int row = m0 + e / GT, col = n0 + e % GT;
+    if (row >= M || col >= N) continue;
+    float v = 0.0f;
+    for (int q = 0; q < ng; ++q) v += sm[q].red[e];
+    if constexpr (EpiTwoPhase<EP>::value) ep.store(z, row, col, v, ep.load(z, row, col));
+    else ep(z, row, col, v);
+  }
+}
+
 template <class EP>
 __global__ void splitk_reduce_kernel(int M, int N, int batch, int nsplit, const float* __restrict__ part, EP ep) {
   const int64_t mn = (int64_t)M * N;
@@ -219,8 +264,19 @@ inline void launch_gemm(bool split, int M, int N, int K, int batch, const LA& la
                         hipStream_t st, float* scratch = nullptr, int64_t scratch_floats = 0) {
   if (M <= 0 || N <= 0 || batch <= 0) return;
   const int ns = splitk_slices(M, N, K, batch, scratch ? scratch_floats : 0);
+  const int nk = (K + GK - 1) / GK;
+  const int64_t tiles = (int64_t)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * batch;
+  if (ns > 1 && nk <= KGROUPS && tiles >= KGROUP_MIN_TILES) {  // the slices as one workgroup's groups
+    dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch);
+    if (split)
+      hipLaunchKernelGGL((gemm_kgroup_kernel<true, A_EXACT, B_EXACT, LA, LB, EP>), grid, dim3(256 * nk), 0, st, M, N,
+                         K, la, lb, ep);
+    else
+      hipLaunchKernelGGL((gemm_kgroup_kernel<false, A_EXACT, B_EXACT, LA, LB, EP>), grid, dim3(256 * nk), 0, st, M,
+                         N, K, la, lb, ep);
+    return;
+  }
   if (ns > 1) {
-    const int nk = (K + GK - 1) / GK;
     const int kslice = ((nk + ns - 1) / ns) * GK;
     const int nsl = (K + kslice - 1) / kslice;
     dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch * nsl);
