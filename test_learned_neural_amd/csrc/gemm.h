@@ -188,10 +188,12 @@ __global__ void __launch_bounds__(256) gemm_part_kernel(int M, int N, int K, int
 // forms the partial tile of k-step g, writes it over its own LDS operand buffers, and after a
 // barrier the workgroup sums the groups' partials in group order (the order of the launched
 // slices' reduction) and applies the product's epilogue.  No partial tiles in global memory and
-// no reduction launch.  Taken where the product has at least KGROUP_MIN_TILES output tiles (128
-// memories of the 64 -> 128 -> 64 memory on MI355X: per-chunk path 4.79 -> 4.15 ms, its outer
-// backward 17.9 -> 16.5 ms); with fewer, one workgroup per k-step spreads a tile's loads over more
-// CUs, which eight memories' products (8-16 tiles) need (per-token retrieval 8.1 -> 9.1 ms).
+// no reduction launch.  Taken, where split products are allowed, for every product of 2..KGROUPS
+// k-steps with at least KGROUP_MIN_TILES output tiles, also those too wide for launched slices
+// (128 memories of the 64 -> 128 -> 64 memory on MI355X: per-chunk path 4.79 -> 4.08 ms, its
+// outer backward 17.9 -> 15.9 ms; the 384 -> 768 -> 384 memory 1.34 -> 1.24 ms); with fewer tiles,
+// one workgroup per k-step spreads a tile's loads over more CUs, which eight memories' products
+// (8-16 tiles) need (per-token retrieval 8.1 -> 9.1 ms this way).
 constexpr int KGROUPS = 4;
 constexpr int KGROUP_MIN_TILES = 128;
 template <bool SPLIT, bool A_EXACT, bool B_EXACT>
@@ -266,7 +268,7 @@ inline void launch_gemm(bool split, int M, int N, int K, int batch, const LA& la
   const int ns = splitk_slices(M, N, K, batch, scratch ? scratch_floats : 0);
   const int nk = (K + GK - 1) / GK;
   const int64_t tiles = (int64_t)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * batch;
-  if (ns > 1 && nk <= KGROUPS && tiles >= KGROUP_MIN_TILES) {  // the slices as one workgroup's groups
+  if (scratch && scratch_floats > 0 && nk >= 2 && nk <= KGROUPS && tiles >= KGROUP_MIN_TILES) {
     dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch);
     if (split)
       hipLaunchKernelGGL((gemm_kgroup_kernel<true, A_EXACT, B_EXACT, LA, LB, EP>), grid, dim3(256 * nk), 0, st, M, N,
