@@ -766,7 +766,46 @@ __global__ void chunk_gate_adj_kernel(const float* __restrict__ WA, const float*
   const float* s0 = w0 + P;
   const int64_t o = (int64_t)z * P;
   float t = 0.0f, e = 0.0f, a = 0.0f;
-  for (int64_t i = threadIdx.x; i < P; i += blockDim.x) {
+  int64_t i0 = 0;
+  if (((P & 3) == 0) && ((((uintptr_t)(WA + o)) | ((uintptr_t)(SA + o)) | ((uintptr_t)(N + o)) |
+                          ((uintptr_t)(SAt + o)) | ((uintptr_t)w0)) & 15) == 0) {
+    // 16-byte loads and stores, four iterations' loads in flight per thread (the SAt stores
+    // would otherwise keep each iteration's loads behind the previous one's store)
+    const int64_t n4 = P / 4;
+    const float4* wa4 = (const float4*)(WA + o);
+    const float4* sa4 = (const float4*)(SA + o);
+    const float4* n_4 = (const float4*)(N + o);
+    const float4* w04 = (const float4*)w0;
+    const float4* s04 = (const float4*)s0;
+    float4* st4 = (float4*)(SAt + o);
+    for (int64_t q0 = threadIdx.x; q0 < n4; q0 += 4 * (int64_t)blockDim.x) {
+      float4 u[4], v[4], nn[4], x[4], y[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t q = q0 + (int64_t)j * blockDim.x;
+        if (q < n4) {
+          u[j] = wa4[q];
+          v[j] = sa4[q];
+          nn[j] = n_4[q];
+          x[j] = w04[q];
+          y[j] = s04[q];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t q = q0 + (int64_t)j * blockDim.x;
+        if (q < n4) {
+          const float4 s = make_float4(v[j].x + u[j].x, v[j].y + u[j].y, v[j].z + u[j].z, v[j].w + u[j].w);
+          st4[q] = s;
+          t += s.x * nn[j].x + s.y * nn[j].y + s.z * nn[j].z + s.w * nn[j].w;
+          e += s.x * y[j].x + s.y * y[j].y + s.z * y[j].z + s.w * y[j].w;
+          a += u[j].x * x[j].x + u[j].y * x[j].y + u[j].z * x[j].z + u[j].w * x[j].w;
+        }
+      }
+    }
+    i0 = P;
+  }
+  for (int64_t i = i0 + threadIdx.x; i < P; i += blockDim.x) {
     const float sat = SA[o + i] + WA[o + i];
     SAt[o + i] = sat;
     t += sat * N[o + i];
