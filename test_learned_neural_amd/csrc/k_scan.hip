@@ -132,7 +132,8 @@ atlasmem_status launch_omega(const float* cW, const float* cS, int64_t ld_c, con
 // w_{l,l} = E_{l,l} = 1 and, for t > l, E_{t,l} = eta_t E_{t-1,l}, w_{t,l} = (1 - alpha_t) w_{t-1,l}
 // + E_{t,l}: each (t, l) sequence is its own scalar recurrence in t, so thread r carries the
 // w and E of its window's (at most PTR_MAXC) tokens in registers through the chunk, with no
-// barrier per token.  beta_t and a_t follow from the gates alone (thread 0).
+// barrier per token.  beta_t and a_t follow from the gates alone (the block's last thread, so
+// that this scan runs beside the key rows of the first waves).
 constexpr int PTR_MAXC = 8;
 __global__ void ptr_coeff_kernel(const float* __restrict__ theta, const float* __restrict__ eta,
                                  const float* __restrict__ alpha, const float* __restrict__ gamma, int64_t ld,
@@ -151,7 +152,7 @@ __global__ void ptr_coeff_kernel(const float* __restrict__ theta, const float* _
     al[l] = alpha[o];
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == blockDim.x - 1) {  // the last wave: the key rows start on wave 0
     float beta = 1.0f, a = 0.0f, P = 1.0f;
     for (int t = 0; t < C; ++t) {
       const float om = 1.0f - al[t], e = et[t];
@@ -175,7 +176,8 @@ __global__ void ptr_coeff_kernel(const float* __restrict__ theta, const float* _
 #pragma unroll
     for (int q = 0; q < PTR_MAXC; ++q) w[q] = E[q] = 0.0f;
     float* col = Om + (int64_t)m * C * Rk + r;
-    for (int t = 0; t < C; ++t) {
+#pragma unroll 4
+    for (int t = 0; t < C; ++t) {  // unrolled: four tokens' gate loads from LDS issued together
       const float om = 1.0f - al[t], e = et[t];
       float v = 0.0f;
 #pragma unroll
