@@ -525,29 +525,29 @@ __global__ void scalar_adj_kernel(const float* __restrict__ WA, const float* __r
 // recomputed in LDS):  e_{C-1} = b_{C-1} = w_{C-1} = 1, e_r = eta_{r+1} e_{r+1},
 // b_r = (1 - alpha_{r+1}) b_{r+1}, w_r = b_r + eta_{r+1} w_{r+1}, cS = theta e, cW = theta w,
 // PC = eta_0 e_0, beta = (1 - alpha_0) b_0, aS = eta_0 w_0.
+constexpr int kGateBwdMaxC = 1024;  // the largest chunk a configuration may ask for
 __global__ void gate_bwd_kernel(const float* __restrict__ theta, const float* __restrict__ eta,
                                 const float* __restrict__ alpha, int64_t ld, int64_t s0, int C,
                                 const float* __restrict__ cWa, const float* __restrict__ cSa,
                                 const float* __restrict__ sca, float* __restrict__ dth, float* __restrict__ det,
                                 float* __restrict__ dal) {
-  // e, b, w, ea, wa, (unused), then the chunk's gates th, et, al, the coefficient adjoints cw, cs
-  // and the outputs oth, oet, oal [C] each in LDS: the block loads and stores them in parallel,
-  // and thread 0 runs the recurrences without a global access
+  // e, b, w, ea, wa, the chunk's theta, the coefficient adjoints cw, cs and the output oth [C]
+  // each in the dynamic LDS block; eta and alpha (which the two recurrences only read) and their
+  // outputs oet, oal (which the second only writes) in arrays of their own, so that the compiler
+  // may issue a step's LDS loads ahead of the previous steps' stores.  The block loads and stores
+  // them in parallel, and thread 0 runs the recurrences without a global access.
   extern __shared__ float gb[];
+  __shared__ float et[kGateBwdMaxC], al[kGateBwdMaxC], oet[kGateBwdMaxC], oal[kGateBwdMaxC];
   const int z = blockIdx.x;
   float* e = gb;
   float* b = gb + C;
   float* w = gb + 2 * C;
   float* ea = gb + 3 * C;
   float* wa = gb + 4 * C;
-  float* th = gb + 6 * C;
-  float* et = gb + 7 * C;
-  float* al = gb + 8 * C;
-  float* cwv = gb + 9 * C;
-  float* csv = gb + 10 * C;
-  float* oth = gb + 11 * C;
-  float* oet = gb + 12 * C;
-  float* oal = gb + 13 * C;
+  float* th = gb + 5 * C;
+  float* cwv = gb + 6 * C;
+  float* csv = gb + 7 * C;
+  float* oth = gb + 8 * C;
   for (int r = threadIdx.x; r < C; r += blockDim.x) {
     const int64_t o = (int64_t)z * ld + s0 + r;
     th[r] = theta[o];
@@ -1647,7 +1647,8 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
         cWt = ws + L.cwt;
         cSt = ws + L.cst;
       }
-      hipLaunchKernelGGL(bk::gate_bwd_kernel, dim3(M), dim3(64), (size_t)14 * C * sizeof(float), st, theta, eta,
+      if (C > bk::kGateBwdMaxC) return ATLASMEM_E_UNSUPPORTED;
+      hipLaunchKernelGGL(bk::gate_bwd_kernel, dim3(M), dim3(64), (size_t)9 * C * sizeof(float), st, theta, eta,
                          alpha, T, s, C, cWt, cSt, sca, dth, det, dal);
       AM_LAUNCH_CHECK();
       hipLaunchKernelGGL(bk::state_adj_kernel, dim3(blocks_of(n)), dim3(256), 0, st, WA, SA, Wb, sc, P, M, WAn, SAn);
