@@ -611,6 +611,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the stand-alone stage rooflines")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="time the general per-product path (ATLASMEM_FLAG_NO_FUSED) for the workload")
     ap.add_argument("--only-stage", default=None,
                     help="time only this stand-alone stage (for profiling) and print its JSON object")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -651,7 +653,7 @@ def main():
     cfg = am.make_config(kind=s.kind, batch=s.batch, heads=s.heads, d_key=s.d_key, d_value=s.d_value,
                          d_hidden=s.d_hidden, poly_degree=s.poly_degree, chunk=s.chunk, omega_window=s.omega_window,
                          gate_mode=s.gate_mode, ns_steps=s.ns_steps, input_dtype=s.input_dtype,
-                         precision=args.precision)
+                         precision=args.precision, flags=am.FLAG_NO_FUSED if args.no_fused else 0)
     mem = am.Memory(cfg, W0, S0)
     Y = torch.empty((s.n_mem, s.T, s.d_value), dtype=torch.float32, device=dev)
     if args.copy_calibration:
@@ -700,7 +702,8 @@ def main():
     # dominant kernel: the update call.  On the fused path it is one launch of the whole-call
     # kernel; on the general path it is the whole per-chunk launch sequence.
     fused = (s.kind == synth.MLP2_SILU and s.gate_mode == synth.PER_CHUNK and s.ns_steps > 0 and s.d_key == 64
-             and s.d_value == 64 and s.d_hidden == 128 and s.chunk % 64 == 0 and args.precision in (am.PREC_AUTO, am.PREC_BF16X3, am.PREC_BF16))
+             and s.d_value == 64 and s.d_hidden == 128 and s.chunk % 64 == 0 and args.precision in (am.PREC_AUTO, am.PREC_BF16X3, am.PREC_BF16)
+             and not args.no_fused)
     ach = step_flops / (upd_ms * 1e-3) / 1e12
     roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                 frac=round(ach / PEAK_BF16_TFLOPS, 5),
@@ -767,7 +770,8 @@ def main():
                    "gate_mode": "per_chunk" if s.gate_mode else "per_token", "variant": args.variant,
                    "key_norm": "l2" if s.norm_k else "none", "query_norm": "l2" if s.norm_q else "none",
                    "value_norm": "l2" if s.norm_v else "none",
-                   "tokens_per_step": tokens, "parallelism": "single GPU; memories spread over workgroups"},
+                   "tokens_per_step": tokens, "parallelism": "single GPU; memories spread over workgroups",
+                   **({"path": "general (fused kernels off)"} if args.no_fused else {})},
         "path_tflops": round(path_tflops, 2),
         "path_frac_bf16_peak": round(path_tflops / PEAK_BF16_TFLOPS, 5),
         "wall_ms_per_step": round(wall_ms, 4),
