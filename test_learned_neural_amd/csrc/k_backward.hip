@@ -1261,6 +1261,13 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
   const float* rW = win ? ws + L.ow : cW;
   const float* rS = win ? ws + L.os : cS;
   const int rld = win ? R : C;
+  if (per_chunk) {
+    // per-chunk gates: the per-token products take every row's gradient adjoint G' with cW = -1,
+    // cS = 0 in place of the state adjoints; nothing in the chunk loop writes them, so once here
+    hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cW, (int64_t)M * C, -1.0f);
+    hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cS, (int64_t)M * C, 0.0f);
+    AM_LAUNCH_CHECK();
+  }
   for (int64_t k = nch - 1; k >= 0; --k) {
     const int64_t s = k * C;
     const float* ck = ws + L.ck + k * M * 2 * P;  // [M][W | S]
@@ -1394,11 +1401,6 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
         } else {
           WAg = SAg = NAb;
         }
-        hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cW, (int64_t)M * C,
-                           -1.0f);
-        hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cS, (int64_t)M * C,
-                           0.0f);
-        AM_LAUNCH_CHECK();
       }
       {  // U1 = X WAz^T, U1s = X SAz^T (dz wide), U2 = H WA2^T, U2s = H SA2^T
         bk::Cat lx = bk::cat1(bk::src(Kr, kbf, kz, din, 1, R, din));
@@ -1525,8 +1527,6 @@ atlasmem_status backward(Handle* h, const void* K, const void* Q, const void* V,
       } else {
         WAg = SAg = NAb;
       }
-      hipLaunchKernelGGL(bk::fill_kernel, dim3(blocks_of((int64_t)M * C)), dim3(256), 0, st, cW, (int64_t)M * C, -1.0f);
-      AM_LAUNCH_CHECK();
     }
     // U1 = X WA1^T, U1s = X SA1^T, U2 = H WA2^T, U2s = H SA2^T
     {
