@@ -86,6 +86,30 @@ def test_split_k_matches_whole_k(case):
     assert all(v <= BF16_TOL for v in errs.values()), errs
 
 
+def test_in_workgroup_split_matches_whole_k():
+    """Products of two to four k-steps with at least 128 output tiles split their k-steps over the
+    groups of one workgroup (reduced in LDS) where split products are allowed.  256 memories with
+    ragged widths on the per-product launches: the first-layer product over 40 key features (a
+    32-step and an 8-wide step) and the gradient pairs over 72 key rows (two full steps and an
+    8-wide one) take that form.  Against whole-k products (1e-4) and, on two memories, the oracle."""
+    log("CASE in-workgroup k-split, 256 memories, ragged widths")
+    inp = synth.make_inputs(1, "stabilised", batch=64, heads=4, T=144, chunk=72, d_key=40, d_value=20,
+                            d_hidden=36)
+    flags = am.FLAG_NO_FUSED | am.FLAG_NO_CHUNK_LOOP
+    split = run_gpu(inp, flags=flags)
+    whole = run_gpu(inp, flags=flags | am.FLAG_NO_SPLIT_K)
+    assert split[3] == am.OK and whole[3] == am.OK
+    agree = {k: maxrel(a, b) for k, a, b in zip(("Y", "W", "S"), split[:3], whole[:3])}
+    log("AGREE kgroup: " + " ".join(f"{k}={v:.2e}" for k, v in agree.items()))
+    assert all(v <= AGREE for v in agree.values()), agree
+    assert max(agree.values()) > 0.0  # different summation orders: the split form ran
+    mems = [0, 255]
+    ref = oracle_run(inp, mems=mems)
+    sub = (split[0][mems], split[1][mems], split[2][mems])
+    errs = compare("kgroup_ragged", inp.spec, sub, ref, BF16_TOL)
+    assert all(v <= BF16_TOL for v in errs.values()), errs
+
+
 def test_chunk_loop_spans_coefficient_blocks():
     """A call longer than one block of gate coefficients: 2048 memories with chunk 16 give
     blocks of 61 chunks, so a 1024-token call runs blocks of 61 and 3 chunks (an odd first
